@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the SSD scan hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the chunked scan of the 30B-shaped prefill (b=1, L=8192, H=64, P=64, N=128,
+G=8, chunk 128, bf16 x/B/C, fp32 dt/A/D and state, final state returned;
+kernels dt_cumsum, chunk_state, state_pass, chunk_output) followed by one
+decode token on the returned state (state_update).  Inputs are resident in
+HBM before timing starts; the step cycles over several copies of the inputs
+so that consecutive steps do not hit in the 256 MB MALL.
+
+Prints ONE JSON line with the throughput, a roofline entry for the dominant
+kernel (chunk_output, timed with HIP events recorded by the library on the
+stream it launches on) and the fp64 CPU oracle timed on the host cores.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD scan tokens/s (bf16, H=64,P=64,N=128) and % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+MALL_BYTES = 256 << 20
+WORKLOADS_BY_NAME = {"prefill_8k": 1, "packed_16k": 2, "long_128k": 3}
+KERNEL_NAMES = ["dt_cumsum", "chunk_state", "state_pass", "chunk_output"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    """Hash of the HIP sources; a counter summary taken on other sources is stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_ssd_selective_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per chunk_output launch from the committed rocprofv3 counter
+    summary, if it was taken on the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", "chunk_output_%s_counters.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            out[i] = e
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def cpu_baseline(p, w, budget_s):
+    """The fp64 oracle (as it stands) on the host cores, on a bounded sample of
+    the same workload: all L tokens of blocks of heads, until the budget is
+    spent; tokens/s scaled to the whole workload (all heads)."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    H = w.nheads
+    block = max(8, min(H, threads))
+    hpg = H // w.ngroups
+    done = 0
+    t0 = time.perf_counter()
+    while done < H and time.perf_counter() - t0 < budget_s:
+        heads = np.arange(done, min(H, done + block))
+        groups = heads // hpg
+        oracle.scan(p["x"][:, :, heads], p["dt_raw"][:, :, heads], p["A"][heads],
+                    p["B"][:, :, groups], p["C"][:, :, groups], dt_bias=p["dt_bias"][heads],
+                    D=p["D"][heads], h_init=None if p.get("h_init") is None else p["h_init"][:, heads],
+                    seq_idx=p.get("seq_idx"))
+        done += len(heads)
+    el = time.perf_counter() - t0
+    tokens_per_s = w.batch * w.seqlen * (done / H) / el
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s: all %d tokens x %d of %d heads (fp64 sequential recurrence, "
+                      "OpenMP over heads), %.1f s; scaled by %d/%d heads"
+                      % (w.name, w.seqlen, done, H, el, done, H)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS_BY_NAME))
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="time budget of the CPU oracle baseline (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the SSD scan's data-parallel path "
+              "on one GPU's share); --gpus %d is not supported." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    import workloads
+
+    lib = ssd.library()
+    hip = Hip()
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[WORKLOADS_BY_NAME[args.workload]]
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    log("bench: drawing %s inputs" % w.name)
+    p = workloads.make_inputs(w, seqlen=L + 1)  # last token feeds the decode update
+    bf = torch.bfloat16
+
+    def dev_t(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return t.to(dtype) if dtype is not None else t
+
+    base = dict(x=dev_t(p["x"][:, :L], bf), dt=dev_t(p["dt_raw"][:, :L]),
+                B=dev_t(p["B"][:, :L], bf), C=dev_t(p["C"][:, :L], bf),
+                xd=dev_t(p["x"][:, L], bf), dtd=dev_t(p["dt_raw"][:, L]),
+                Bd=dev_t(p["B"][:, L], bf), Cd=dev_t(p["C"][:, L], bf),
+                seq=None if p.get("seq_idx") is None else dev_t(p["seq_idx"][:, :L]),
+                h0=None if p.get("h_init") is None else dev_t(p["h_init"]))
+    A, D, bias = dev_t(p["A"]), dev_t(p["D"]), dev_t(p["dt_bias"])
+    es = 2
+    io_bytes = b * L * (2 * H * P * es + 2 * G * N * es + H * 4)
+    state_bytes = b * H * P * N * 4
+    scan_bytes = io_bytes + state_bytes + (state_bytes if base["h0"] is not None else 0) + \
+        (b * L * 4 if base["seq"] is not None else 0)
+    nsets = max(2, math.ceil(2 * MALL_BYTES / scan_bytes) + 1)
+    sets = []
+    for _ in range(nsets):
+        s = {k: (v.clone() if v is not None else None) for k, v in base.items()}
+        s["y"] = torch.empty((b, L, H, P), dtype=bf, device=dev)
+        s["fs"] = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+        s["yd"] = torch.empty((b, H, P), dtype=bf, device=dev)
+        sets.append(s)
+    ws = torch.empty(max(1, ssd.workspace_bytes(b, L, H, P, N, G, Q)), dtype=torch.uint8,
+                     device=dev)
+    nseg = ssd.segments(b, L, H, P, N, G, Q)
+    kernels = ["dt_cumsum"] + (["chunk_state", "state_pass"] if nseg > 1 else []) + \
+        ["chunk_output"]
+    nk = len(kernels) + 1  # + state_update
+    launched = ctypes.c_int(0)
+
+    vp_size = ctypes.sizeof(ctypes.c_void_p)
+
+    def ev_slice(evs, first, count):
+        return (ctypes.c_void_p * count).from_buffer(evs, first * vp_size)
+
+    def step(i, evs=None):
+        s = sets[i % nsets]
+        base_ev = 2 * nk * i
+        if evs is not None:
+            lib.ssd_set_timing_events(ev_slice(evs, base_ev, 2 * (nk - 1)), 2 * (nk - 1),
+                                      ctypes.byref(launched))
+        ssd.chunk_scan_fwd(s["x"], s["dt"], A, s["B"], s["C"], chunk_size=Q, D=D, dt_bias=bias,
+                           initial_states=s["h0"], seq_idx=s["seq"], return_final_states=True,
+                           out=s["y"], final_states_out=s["fs"], workspace=ws)
+        if evs is not None:
+            if launched.value != nk - 1:
+                raise RuntimeError("scan launched %d kernels, expected %d" % (launched.value, nk - 1))
+            lib.ssd_set_timing_events(ev_slice(evs, base_ev + 2 * (nk - 1), 2), 2,
+                                      ctypes.byref(launched))
+        ssd.state_update(s["fs"], s["xd"], s["dtd"], A, s["Bd"], s["Cd"], D=D, dt_bias=bias,
+                         out=s["yd"])
+        if evs is not None:
+            lib.ssd_set_timing_events(None, 0, None)
+
+    log("bench: %d warmup steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = hip.events(2 * nk * args.steps)
+    log("bench: %d timed steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    names = kernels + ["state_update"]
+    per_kernel = {n: [] for n in names}
+    for i in range(args.steps):
+        for k, n in enumerate(names):
+            per_kernel[n].append(hip.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1]))
+    hip.destroy(evs)
+    avg_us = {n: 1e3 * float(np.mean(v)) for n, v in per_kernel.items()}
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens_per_step = b * L + b
+    value = tokens_per_step * args.steps / elapsed
+
+    # roofline of the dominant kernel: algorithmic bytes of one chunk_output launch
+    k4_bytes = scan_bytes
+    k4_s = avg_us["chunk_output"] * 1e-6
+    achieved = k4_bytes / k4_s / 1e9
+    traffic = counter_traffic(w.name)
+    flops = b * L * H * (2 * P * N + P * Q + 2 * P * N + N * Q / (H // G))
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    step_bytes = scan_bytes + 2 * state_bytes + b * (H * P * 2 * es + 2 * G * N * es + H * 4)
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": b, "seq_len": L, "nheads": H, "headdim": P,
+                   "dstate": N, "ngroups": G, "chunk": Q, "decode_tokens_per_step": b,
+                   "segments": nseg, "input_copies": nsets},
+        "roofline": roof,
+        "kernels_us": {n: round(v, 2) for n, v in avg_us.items()},
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "chunk_output_mfma_frac": round(flops / k4_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "source_hash": source_hash(),
+    }
+    if args.cpu_seconds > 0:
+        log("bench: CPU oracle baseline (budget %.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline({k: (v[:, :L] if k in ("x", "dt_raw", "B", "C", "seq_idx") and v is not None else v)
+                                               for k, v in p.items()}, w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

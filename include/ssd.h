@@ -1,0 +1,162 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD selective-scan library
+ * (libssd.so, built from mamba_ssd_selective_amd/csrc).
+ *
+ * The operation (RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section 1, operator
+ * families 1 and 2, and section 3, Figure 2, box [F2]; "Nemotron 3 Nano - JAX
+ * Implementation", Key Components, item 1), per batch row b and head h with
+ * B/C group g = h / (H / G):
+ *
+ *   dt_t = clamp(softplus(dt_raw_t + dt_bias_h), dt_min, dt_max)
+ *   h_t  = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t (outer) B_t      state P x N, fp32
+ *   y_t  = h_t . C_t + D_h * x_t
+ *
+ * Prefill/training computes it as a chunked parallel scan (ssd_chunk_scan_fwd,
+ * chunk size chosen by the caller; the pages use 128); decode computes it one
+ * token at a time on a caller-held fp32 state (ssd_state_update).  Both use
+ * the same device functions for the per-token arithmetic (RFC section 7:
+ * train/prefill and decode share device functions).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous buffers.
+ *    The caller owns all of them; the library allocates nothing and keeps no
+ *    global buffers, so calls are re-entrant.
+ *  - Arguments are validated on the host before anything is launched.  Any
+ *    failure returns a non-zero ssd_status and leaves every output untouched
+ *    (fail closed, RFC section 4.1 and section 7 "Fail closed"); there is no
+ *    fallback path.  Validation reads no device memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  A launch error is returned as SSD_ERR_HIP; device faults
+ *    surface at the caller's next synchronisation.
+ *  - Results are deterministic: fixed reduction order, no atomics
+ *    (RFC section 4.1, WS1 rules).
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = 1,      /* a required pointer is NULL                       */
+    SSD_ERR_BAD_SHAPE = 2,     /* negative size, H % G != 0, batch*L too large ... */
+    SSD_ERR_BAD_DTYPE = 3,     /* io dtype not one of ssd_dtype                    */
+    SSD_ERR_UNSUPPORTED = 4,   /* (dtype, P, N, chunk) outside the compiled set    */
+    SSD_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required          */
+    SSD_ERR_BAD_ARG = 6,       /* dt_min > dt_max, NaN clamp bound, ...            */
+    SSD_ERR_ALIAS = 7,         /* an output overlaps an input it must not overlap  */
+    SSD_ERR_HIP = 8            /* a HIP launch returned an error                   */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype; /* dtype of x, B, C and y */
+
+typedef struct {
+    int64_t batch;      /* b >= 0                                  */
+    int64_t seqlen;     /* L >= 0 (any length; last chunk may be short) */
+    int64_t nheads;     /* H >= 1                                  */
+    int64_t headdim;    /* P                                       */
+    int64_t dstate;     /* N                                       */
+    int64_t ngroups;    /* G >= 1, H % G == 0                      */
+    int64_t chunk_size; /* Q                                       */
+} ssd_dims;
+
+/* Bytes of device workspace ssd_chunk_scan_fwd needs for these dims (0 when
+ * none).  Returns 0 as well for dims it would reject; call ssd_chunk_scan_fwd
+ * to learn why. */
+size_t ssd_chunk_scan_workspace_bytes(const ssd_dims* dims, ssd_dtype io);
+
+/* Number of sequence segments a scan of these dims is split into (1 = each
+ * row's state is carried through the whole row by one workgroup; more = the
+ * rows are cut into segments whose states are chained by an extra pass).
+ * Informational; 0 for dims the scan would reject. */
+int64_t ssd_chunk_scan_segments(const ssd_dims* dims, ssd_dtype io);
+
+/* 1 when (io, headdim, dstate, chunk_size) is in the compiled set, else 0. */
+int ssd_chunk_scan_supported(ssd_dtype io, int64_t headdim, int64_t dstate,
+                             int64_t chunk_size);
+
+/*
+ * Chunked SSD scan over a batch of sequences (prefill / training forward).
+ *
+ *   x        (b, L, H, P)  io dtype
+ *   dt       (b, L, H)     fp32, raw (before bias and softplus)
+ *   dt_bias  (H)           fp32, or NULL = 0
+ *   dt_softplus            non-zero: dt = softplus(dt + dt_bias); zero: dt = dt + dt_bias
+ *   dt_min, dt_max         clamp applied after softplus; pass 0 and +INFINITY for none
+ *   A        (H)           fp32, expected <= 0 (the caller forms -exp(A_log))
+ *   B, C     (b, L, G, N)  io dtype
+ *   D        (H)           fp32, or NULL = 0 (skip connection D * x)
+ *   initial_states (b, H, P, N) fp32, or NULL = zero state; it belongs to the
+ *                          sequence holding token 0 of each row
+ *   seq_idx  (b, L)        int32, or NULL.  Packed sequences: non-decreasing
+ *                          along each row; the state restarts from zero at every
+ *                          token whose value differs from the previous token's.
+ *                          (Non-monotone rows are a precondition violation: the
+ *                          library does not read device memory to check them.)
+ *   y        (b, L, H, P)  io dtype, output; must not overlap any input
+ *   final_states (b, H, P, N) fp32 output or NULL: the state after token L-1 of
+ *                          each row; may be the same pointer as initial_states
+ *                          (exactly equal, not partially overlapping)
+ *   workspace, workspace_bytes  device scratch of at least
+ *                          ssd_chunk_scan_workspace_bytes(dims, io) bytes, 256-byte
+ *                          aligned; contents on entry are ignored
+ *   stream                 hipStream_t
+ *
+ * Supported set: see ssd_chunk_scan_supported.  L = 0 is allowed (final_states
+ * then receives initial_states, or zeros).
+ */
+ssd_status ssd_chunk_scan_fwd(const ssd_dims* dims, ssd_dtype io, const void* x,
+                              const float* dt, const float* dt_bias, int dt_softplus,
+                              float dt_min, float dt_max, const float* A, const void* B,
+                              const void* C, const float* D, const float* initial_states,
+                              const int32_t* seq_idx, void* y, float* final_states,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode token per sequence: the per-token recurrent state update (RFC
+ * section 1, operator family 1; the state is the fixed-size fp32 SSM state of
+ * operator family 2).
+ *
+ *   state  (b, H, P, N) fp32, read and updated in place
+ *   x      (b, H, P)    io dtype
+ *   dt     (b, H)       fp32 raw;  dt_bias (H) or NULL; dt_softplus, dt_min, dt_max as above
+ *   A      (H) fp32;  B, C (b, G, N) io dtype;  D (H) fp32 or NULL
+ *   y      (b, H, P)    io dtype output, computed from the updated state
+ *
+ * Supported: io in {F32, BF16}; N in {16, 32, 64, 128, 256}; P >= 1; H % G == 0.
+ */
+ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                            int64_t ngroups, ssd_dtype io, float* state, const void* x,
+                            const float* dt, const float* dt_bias, int dt_softplus,
+                            float dt_min, float dt_max, const float* A, const void* B,
+                            const void* C, const float* D, void* y, void* stream);
+
+/* Per-kernel timing hooks (diagnostics).  After a call with events != NULL,
+ * every ssd_chunk_scan_fwd / ssd_state_update call made on the same host
+ * thread records events[2k] before and events[2k+1] after its k-th kernel
+ * launch, on the call's stream, for k < count/2, and stores the number of
+ * kernels it launched in *launched (if not NULL).  `events` are hipEvent_t
+ * handles the caller created; the library only records them.  Kernel order
+ * of the scan: dt_cumsum, [chunk_state, state_pass,] chunk_output (the two
+ * bracketed kernels run only when ssd_chunk_scan_segments(...) > 1).
+ * Pass events = NULL to turn the hooks off. */
+void ssd_set_timing_events(void* const* events, int count, int* launched);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ssd_status_string(int status);
+
+/* SSD_ABI_VERSION of the built library. */
+int ssd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

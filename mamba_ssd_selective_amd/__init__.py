@@ -1,0 +1,212 @@
+"""MI355X (gfx950) Mamba-2 SSD selective scan: Python binding of libssd.so.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libssd.so`` (built from ``csrc/`` by ``_build.build()``); PyTorch
+supplies device memory and the current stream.  There is no CPU or PyTorch
+fallback: if the library is missing or fails to load, every call raises.
+
+The operation (RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section 1 operator
+families 1 and 2, section 3 Figure 2 box [F2]; "Nemotron 3 Nano - JAX
+Implementation", Key Components item 1), per row and head:
+
+    dt_t = clamp(softplus(dt_raw_t + dt_bias), dt_min, dt_max)
+    h_t  = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t       (fp32 state, P x N)
+    y_t  = h_t . C_t + D x_t
+
+``chunk_scan_fwd`` computes it for whole sequences as a chunked parallel scan
+(prefill / training forward); ``state_update`` advances a decode state by one
+token.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = ["chunk_scan_fwd", "state_update", "workspace_bytes", "supported", "segments",
+           "SSDError", "library", "library_path", "F32", "BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssd.so")
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        msg = library().ssd_status_string(self.status).decode()
+        super().__init__("%s failed: status %d (%s)" % (where, self.status, msg))
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk_size")]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libssd.so not found at %s: build it with "
+                               "mamba_ssd_selective_amd._build.build()" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, f, i64, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_int
+        dims_p = ctypes.POINTER(_Dims)
+        lib.ssd_abi_version.restype = i
+        lib.ssd_status_string.argtypes = [i]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_chunk_scan_workspace_bytes.argtypes = [dims_p, i]
+        lib.ssd_chunk_scan_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_chunk_scan_segments.argtypes = [dims_p, i]
+        lib.ssd_chunk_scan_segments.restype = i64
+        lib.ssd_chunk_scan_supported.argtypes = [i, i64, i64, i64]
+        lib.ssd_chunk_scan_supported.restype = i
+        lib.ssd_chunk_scan_fwd.argtypes = [dims_p, i, vp, vp, vp, i, f, f, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.ssd_chunk_scan_fwd.restype = i
+        lib.ssd_state_update.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, vp, vp, i, f, f,
+                                         vp, vp, vp, vp, vp, vp]
+        lib.ssd_state_update.restype = i
+        lib.ssd_set_timing_events.argtypes = [ctypes.POINTER(vp), i, ctypes.POINTER(i)]
+        lib.ssd_set_timing_events.restype = None
+        if lib.ssd_abi_version() != 1:
+            raise RuntimeError("libssd.so ABI version %d, expected 1" % lib.ssd_abi_version())
+        _lib = lib
+    return _lib
+
+
+def _io_code(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError("x/B/C must be torch.bfloat16 or torch.float32, got %s" % dtype)
+
+
+def _dims(b, L, H, P, N, G, Q) -> _Dims:
+    return _Dims(int(b), int(L), int(H), int(P), int(N), int(G), int(Q))
+
+
+def workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, io=BF16) -> int:
+    d = _dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size)
+    return int(library().ssd_chunk_scan_workspace_bytes(ctypes.byref(d), int(io)))
+
+
+def segments(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, io=BF16) -> int:
+    d = _dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size)
+    return int(library().ssd_chunk_scan_segments(ctypes.byref(d), int(io)))
+
+
+def supported(io, headdim, dstate, chunk_size) -> bool:
+    return bool(library().ssd_chunk_scan_supported(int(io), int(headdim), int(dstate),
+                                                   int(chunk_size)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size: int, D=None, dt_bias=None,
+                   initial_states=None, seq_idx=None, dt_softplus: bool = True,
+                   dt_limit: Tuple[float, float] = (0.0, math.inf),
+                   return_final_states: bool = False, out=None, final_states_out=None,
+                   workspace=None):
+    """Chunked SSD scan.
+
+    x (b, L, H, P), B/C (b, L, G, N) in bf16 or fp32 (same dtype); dt (b, L, H),
+    A/D/dt_bias (H), initial_states (b, H, P, N) fp32; seq_idx (b, L) int32.
+    Returns y (b, L, H, P) in x's dtype, and the final fp32 states
+    (b, H, P, N) when ``return_final_states``.
+    """
+    import torch
+    lib = library()
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    io = _io_code(x.dtype)
+    f32 = torch.float32
+    _check(x, "x", (b, L, H, P), x.dtype, dev)
+    _check(B, "B", (b, L, G, N), x.dtype, dev)
+    _check(C, "C", (b, L, G, N), x.dtype, dev)
+    _check(dt, "dt", (b, L, H), f32, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    _check(initial_states, "initial_states", (b, H, P, N), f32, dev)
+    _check(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    y = out if out is not None else torch.empty((b, L, H, P), dtype=x.dtype, device=dev)
+    _check(y, "out", (b, L, H, P), x.dtype, dev)
+    fs = None
+    if return_final_states:
+        fs = final_states_out if final_states_out is not None else \
+            torch.empty((b, H, P, N), dtype=f32, device=dev)
+        _check(fs, "final_states_out", (b, H, P, N), f32, dev)
+    d = _dims(b, L, H, P, N, G, chunk_size)
+    need = int(lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d), io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_fwd(
+        ctypes.byref(d), io, _ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(initial_states), _ptr(seq_idx), _ptr(y), _ptr(fs), _ptr(workspace), ws_bytes,
+        _stream_handle(dev))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd")
+    return (y, fs) if return_final_states else y
+
+
+def state_update(state, x, dt, A, B, C, *, D=None, dt_bias=None, dt_softplus: bool = True,
+                 dt_limit: Tuple[float, float] = (0.0, math.inf), out=None):
+    """One decode token: updates ``state`` (b, H, P, N) fp32 in place and
+    returns y (b, H, P) in x's dtype.  x (b, H, P), dt (b, H), B/C (b, G, N)."""
+    import torch
+    lib = library()
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    io = _io_code(x.dtype)
+    f32 = torch.float32
+    _check(state, "state", (b, H, P, N), f32, dev)
+    _check(B, "B", (b, G, N), x.dtype, dev)
+    _check(C, "C", (b, G, N), x.dtype, dev)
+    _check(dt, "dt", (b, H), f32, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    y = out if out is not None else torch.empty((b, H, P), dtype=x.dtype, device=dev)
+    _check(y, "out", (b, H, P), x.dtype, dev)
+    st = lib.ssd_state_update(b, H, P, N, G, io, _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias),
+                              int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
+                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+                              _stream_handle(dev))
+    if st != 0:
+        raise SSDError(st, "ssd_state_update")
+    return y

@@ -1,0 +1,323 @@
+// ssd_api.hip -- the C ABI of libssd.so (declared in include/ssd.h).
+//
+// Host side only: argument validation (fail closed before any launch, RL-Kernel
+// RFC "Nemotron-3-Nano-30B-A3B" section 4.1 WS1 rules and section 7 "Fail
+// closed"), workspace sizing, and the launch sequence of the chunked scan.
+// Validation never touches the device, so it runs on machines without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+constexpr int64_t kTargetWorkgroups = 512;  // enough independent workgroups for 256 CUs
+constexpr size_t kAlign = 256;
+
+struct Plan {
+    int64_t nc = 0, Lp = 0;
+    int64_t nseg = 1, cps = 1;
+    size_t off_dtv = 0, off_cs = 0, off_seg = 0, off_mult = 0, total = 0;
+};
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+Plan make_plan(const ssd_dims& d) {
+    Plan p;
+    if (d.seqlen <= 0 || d.batch <= 0) return p;
+    p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
+    p.Lp = p.nc * d.chunk_size;
+    const int64_t bh = d.batch * d.nheads;
+    int64_t nseg = (kTargetWorkgroups + bh - 1) / bh;
+    if (nseg < 1) nseg = 1;
+    if (nseg > p.nc) nseg = p.nc;
+    p.cps = (p.nc + nseg - 1) / nseg;
+    p.nseg = (p.nc + p.cps - 1) / p.cps;
+    const size_t f = sizeof(float);
+    size_t off = 0;
+    p.off_dtv = off;
+    off = align_up(off + static_cast<size_t>(bh * p.Lp) * f);
+    p.off_cs = off;
+    off = align_up(off + static_cast<size_t>(bh * p.Lp) * f);
+    if (p.nseg > 1) {
+        p.off_seg = off;
+        off = align_up(off + static_cast<size_t>(bh * p.nseg * d.headdim * d.dstate) * f);
+        p.off_mult = off;
+        off = align_up(off + static_cast<size_t>(bh * p.nseg) * f);
+    }
+    p.total = off;
+    return p;
+}
+
+size_t io_size(ssd_dtype io) { return io == SSD_BF16 ? 2 : 4; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, size_t bytes) {
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Span{a, a + bytes};
+}
+bool overlap(Span a, Span b) {
+    if (a.lo == 0 || b.lo == 0 || a.hi == a.lo || b.hi == b.lo) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bad_clamp(float lo, float hi) { return isnan(lo) || isnan(hi) || lo > hi; }
+
+// Optional per-kernel event recording (ssd_set_timing_events), per host thread.
+struct TimingHooks {
+    void* const* events = nullptr;
+    int count = 0;
+    int* launched = nullptr;
+};
+thread_local TimingHooks g_hooks;
+
+// Runs one launch between the k-th pair of timing events (when hooks are set).
+template <typename F>
+hipError_t timed_launch(int& k, hipStream_t st, F&& launch) {
+    const bool rec = g_hooks.events && 2 * k + 1 < g_hooks.count;
+    if (rec) (void)hipEventRecord(static_cast<hipEvent_t>(g_hooks.events[2 * k]), st);
+    hipError_t e = launch();
+    if (rec) (void)hipEventRecord(static_cast<hipEvent_t>(g_hooks.events[2 * k + 1]), st);
+    ++k;
+    if (g_hooks.launched) *g_hooks.launched = k;
+    return e;
+}
+
+// Shape checks shared by the workspace query and the scan entry point.
+ssd_status check_scan_dims(const ssd_dims* d, ssd_dtype io) {
+    if (!d) return SSD_ERR_NULL_ARG;
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1 || d->chunk_size < 1)
+        return SSD_ERR_BAD_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    // index and grid limits: element offsets fit in int64, rows/heads in int
+    if (d->batch > 65535 || d->nheads > 65535 || d->seqlen > (int64_t(1) << 31))
+        return SSD_ERR_BAD_SHAPE;
+    if (!ssd::find_scan_variant(io, d->headdim, d->dstate, d->chunk_size))
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+void ssd_set_timing_events(void* const* events, int count, int* launched) {
+    g_hooks.events = events;
+    g_hooks.count = events ? count : 0;
+    g_hooks.launched = events ? launched : nullptr;
+}
+
+const char* ssd_status_string(int s) {
+    switch (s) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL_ARG: return "a required pointer argument is NULL";
+        case SSD_ERR_BAD_SHAPE: return "invalid shape (negative size, H % G != 0, or a size limit)";
+        case SSD_ERR_BAD_DTYPE: return "io dtype is not SSD_F32 or SSD_BF16";
+        case SSD_ERR_UNSUPPORTED: return "(dtype, headdim, dstate, chunk_size) is outside the compiled set";
+        case SSD_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than required";
+        case SSD_ERR_BAD_ARG: return "invalid argument (dt clamp bounds, or a buffer not 16-byte aligned)";
+        case SSD_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
+        case SSD_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown ssd_status";
+    }
+}
+
+int ssd_chunk_scan_supported(ssd_dtype io, int64_t headdim, int64_t dstate, int64_t chunk_size) {
+    return ssd::find_scan_variant(io, headdim, dstate, chunk_size) != nullptr;
+}
+
+size_t ssd_chunk_scan_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
+    if (check_scan_dims(d, io) != SSD_OK) return 0;
+    return make_plan(*d).total;
+}
+
+// Number of sequence segments the scan of these dims is split into (1 = the
+// state is carried through each whole row inside one workgroup).  Informational.
+int64_t ssd_chunk_scan_segments(const ssd_dims* d, ssd_dtype io) {
+    if (check_scan_dims(d, io) != SSD_OK) return 0;
+    return make_plan(*d).nseg;
+}
+
+ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                              const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                              const float* A, const void* B, const void* C, const float* D,
+                              const float* initial_states, const int32_t* seq_idx, void* y,
+                              float* final_states, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    ssd_status st = check_scan_dims(d, io);
+    if (st != SSD_OK) return st;
+    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim,
+                  N = d->dstate, G = d->ngroups;
+    const bool work = b > 0 && L > 0;
+    if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
+    const Plan plan = make_plan(*d);
+    if (plan.total > 0 &&
+        (!workspace || workspace_bytes < plan.total ||
+         (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+        return SSD_ERR_WORKSPACE;
+    const void* vec_bufs[] = {x, B, C, y, initial_states, final_states};
+    for (const void* p : vec_bufs)
+        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    if (initial_states && final_states && initial_states != final_states &&
+        overlap(span(initial_states, b * H * P * N * 4), span(final_states, b * H * P * N * 4)))
+        return SSD_ERR_ALIAS;
+    const size_t es = io_size(io);
+    const Span in_spans[] = {
+        span(x, b * L * H * P * es), span(dt, b * L * H * 4), span(B, b * L * G * N * es),
+        span(C, b * L * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+        span(D, D ? H * 4 : 0), span(seq_idx, seq_idx ? b * L * 4 : 0),
+    };
+    const Span ys = span(y, b * L * H * P * es);
+    const Span fs = span(final_states, final_states ? b * H * P * N * 4 : 0);
+    const Span is = span(initial_states, initial_states ? b * H * P * N * 4 : 0);
+    const Span ws = span(workspace, plan.total);
+    for (const Span& s : in_spans) {
+        if (overlap(ys, s) || overlap(fs, s) || overlap(ws, s)) return SSD_ERR_ALIAS;
+    }
+    if (overlap(ys, fs) || overlap(ys, is) || overlap(ys, ws) || overlap(fs, ws) ||
+        overlap(is, ws))
+        return SSD_ERR_ALIAS;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    if (b == 0) return SSD_OK;
+    if (L == 0) {
+        if (final_states) {
+            if (timed_launch(k, hs, [&] {
+                    return ssd::launch_copy_state(initial_states, final_states, b * H * P * N, hs);
+                }) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
+        return SSD_OK;
+    }
+    const ssd::ScanVariant* var = ssd::find_scan_variant(io, P, N, d->chunk_size);
+    char* wsb = static_cast<char*>(workspace);
+    float* dtv = reinterpret_cast<float*>(wsb + plan.off_dtv);
+    float* cs = reinterpret_cast<float*>(wsb + plan.off_cs);
+
+    ssd::DtArgs da;
+    da.dt_raw = dt;
+    da.dt_bias = dt_bias;
+    da.A = A;
+    da.seq_idx = seq_idx;
+    da.softplus = dt_softplus ? 1 : 0;
+    da.dt_min = dt_min;
+    da.dt_max = dt_max;
+    da.L = L;
+    da.Lp = plan.Lp;
+    da.H = static_cast<int>(H);
+    da.Q = static_cast<int>(d->chunk_size);
+    da.dtv = dtv;
+    da.cs = cs;
+    if (timed_launch(k, hs, [&] {
+            return ssd::launch_dt_cumsum(da, b, static_cast<int>(plan.nc), hs);
+        }) != hipSuccess)
+        return SSD_ERR_HIP;
+
+    ssd::ScanArgs sa;
+    sa.x = x;
+    sa.B = B;
+    sa.C = C;
+    sa.y = y;
+    sa.dtv = dtv;
+    sa.cs = cs;
+    sa.seq_idx = seq_idx;
+    sa.D = D;
+    sa.init = initial_states;
+    sa.final_states = final_states;
+    sa.seg_state = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_seg) : nullptr;
+    sa.seg_mult = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_mult) : nullptr;
+    sa.L = L;
+    sa.Lp = plan.Lp;
+    sa.H = static_cast<int>(H);
+    sa.G = static_cast<int>(G);
+    sa.nc = static_cast<int>(plan.nc);
+    sa.nseg = static_cast<int>(plan.nseg);
+    sa.cps = static_cast<int>(plan.cps);
+
+    if (plan.nseg > 1) {
+        if (timed_launch(k, hs, [&] {
+                return var->chunk_state(sa, b * (plan.nseg - 1) * H, hs);
+            }) != hipSuccess)
+            return SSD_ERR_HIP;
+        ssd::PassArgs pa;
+        pa.seg_state = sa.seg_state;
+        pa.seg_mult = sa.seg_mult;
+        pa.init = initial_states;
+        pa.PN = P * N;
+        pa.nseg = static_cast<int>(plan.nseg);
+        if (timed_launch(k, hs, [&] { return ssd::launch_state_pass(pa, b * H, hs); }) !=
+            hipSuccess)
+            return SSD_ERR_HIP;
+    }
+    if (timed_launch(k, hs, [&] { return var->chunk_output(sa, b * plan.nseg * H, hs); }) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                            int64_t ngroups, ssd_dtype io, float* state, const void* x,
+                            const float* dt, const float* dt_bias, int dt_softplus,
+                            float dt_min, float dt_max, const float* A, const void* B,
+                            const void* C, const float* D, void* y, void* stream) {
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
+    if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+        return SSD_ERR_BAD_SHAPE;
+    if (nheads % ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (batch * nheads > (int64_t(1) << 31) || headdim > (int64_t(1) << 20))
+        return SSD_ERR_BAD_SHAPE;
+    if (dstate != 16 && dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
+        return SSD_ERR_UNSUPPORTED;
+    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    if (batch == 0) return SSD_OK;
+    if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_ARG;
+    if (!aligned16(state)) return SSD_ERR_BAD_ARG;
+    const size_t es = io_size(io);
+    const int64_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups;
+    const Span ss = span(state, b * H * P * N * 4);
+    const Span ys = span(y, b * H * P * es);
+    const Span ins[] = {span(x, b * H * P * es), span(dt, b * H * 4), span(B, b * G * N * es),
+                        span(C, b * G * N * es), span(A, H * 4),
+                        span(dt_bias, dt_bias ? H * 4 : 0), span(D, D ? H * 4 : 0)};
+    for (const Span& s : ins)
+        if (overlap(ss, s) || overlap(ys, s)) return SSD_ERR_ALIAS;
+    if (overlap(ss, ys)) return SSD_ERR_ALIAS;
+
+    ssd::StepArgs a;
+    a.state = state;
+    a.x = x;
+    a.dt = dt;
+    a.dt_bias = dt_bias;
+    a.softplus = dt_softplus ? 1 : 0;
+    a.dt_min = dt_min;
+    a.dt_max = dt_max;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.y = y;
+    a.H = static_cast<int>(H);
+    a.P = static_cast<int>(P);
+    a.G = static_cast<int>(G);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (timed_launch(k, hs, [&] { return ssd::launch_state_update(io, N, a, b * H, hs); }) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// ssd_device.h -- device functions shared by every SSD kernel (gfx950, wave64).
+//
+// The chunked prefill path and the single-token decode path use the same
+// per-token arithmetic from here (RL-Kernel RFC "Nemotron-3-Nano-30B-A3B",
+// section 7: train/prefill and decode of the Mamba-2 mixer must share device
+// functions): the dt transform of section 3 Figure 2 box [F2]
+// (softplus(dt + dt_bias), dt_limit), the decay exp(dt * A), the bf16 <-> fp32
+// conversions and the head -> B/C group map.
+//
+// MFMA conventions (one 16x16 output tile per wave, K = 32 per step):
+//   lane l, r16 = l & 15, q = l >> 4
+//   A operand: row r16, eight k values k(q, e) = 8q + e, e = 0..7
+//   B operand: column r16, the same eight k values
+//   accumulator: rows 4q + i (i = 0..3), column r16
+// Any bijection between (q, e) and the 32 logical k indices is allowed as
+// long as A and B use the same one; the kernels use two of them (contiguous
+// runs of 8, or two runs of 4) to feed accumulators back in as operands.
+// bf16 uses one v_mfma_f32_16x16x32_bf16; fp32 uses eight v_mfma_f32_16x16x4_f32
+// (sub-step e takes element e of every lane, so the k mapping is the same).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// log(1 + e^v) without overflow.
+__device__ __forceinline__ float softplus_f32(float v) {
+    return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+}
+
+// dt_t = clamp(softplus(dt_raw + dt_bias), dt_min, dt_max)   (box [F2])
+__device__ __forceinline__ float dt_transform(float raw, float bias, int softplus,
+                                              float dt_min, float dt_max) {
+    float v = raw + bias;
+    if (softplus) v = softplus_f32(v);
+    return fminf(fmaxf(v, dt_min), dt_max);
+}
+
+// exp of a non-positive log-decay (a difference of running sums, or dt * A).
+__device__ __forceinline__ float decay_exp(float log_decay) { return __expf(log_decay); }
+
+__device__ __forceinline__ int group_of_head(int h, int heads_per_group) {
+    return h / heads_per_group;
+}
+
+// ------------------------------------------------------------ io element types
+
+template <typename T> struct Io;
+
+template <> struct Io<float> {
+    static constexpr int kVec = 4;  // elements per 16 bytes
+    __device__ static __forceinline__ float to_f32(float v) { return v; }
+    __device__ static __forceinline__ float from_f32(float v) { return v; }
+};
+
+template <> struct Io<uint16_t> {
+    static constexpr int kVec = 8;
+    __device__ static __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+    __device__ static __forceinline__ uint16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// 16-byte vector of io elements.
+template <typename T> struct Vec16 { T v[16 / sizeof(T)]; };
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16(const T* p) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(Vec16<T>, u);
+}
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const Vec16<T>& v) {
+    *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+}
+template <typename T>
+__device__ __forceinline__ Vec16<T> zero16() {
+    return __builtin_bit_cast(Vec16<T>, make_uint4(0, 0, 0, 0));
+}
+
+// Four consecutive io elements (8 bytes bf16, 16 bytes fp32).
+template <typename T> struct Vec4 { T v[4]; };
+
+template <typename T>
+__device__ __forceinline__ Vec4<T> load4(const T* p) {
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_bit_cast(Vec4<T>, *reinterpret_cast<const uint2*>(p));
+    } else {
+        return __builtin_bit_cast(Vec4<T>, *reinterpret_cast<const uint4*>(p));
+    }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const Vec4<T>& v) {
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
+    } else {
+        *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+    }
+}
+
+// ------------------------------------------------------------------ fragments
+
+template <typename T> struct Frag;
+
+template <> struct Frag<uint16_t> {
+    bf16x8_t v;
+};
+template <> struct Frag<float> {
+    float v[8];
+};
+
+// Eight consecutive elements (k = 8q + e) from LDS or global memory.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_load8(const T* p) {
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        f.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+    } else {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    }
+    return f;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_zero() {
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        f.v = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[e] = 0.0f;
+    }
+    return f;
+}
+
+// Two runs of four (elements 0..3 from p0, 4..7 from p1).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_load4x2(const T* p0, const T* p1) {
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        uint2 a = *reinterpret_cast<const uint2*>(p0);
+        uint2 b = *reinterpret_cast<const uint2*>(p1);
+        f.v = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+    } else {
+        float4 a = *reinterpret_cast<const float4*>(p0);
+        float4 b = *reinterpret_cast<const float4*>(p1);
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    }
+    return f;
+}
+
+// Eight fp32 values rounded to the operand type (one rounding, RNE).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_f32(const float (&x)[8]) {
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[e] = static_cast<__bf16>(x[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[e] = x[e];
+    }
+    return f;
+}
+
+__device__ __forceinline__ void mma(f32x4_t& acc, const Frag<uint16_t>& a,
+                                    const Frag<uint16_t>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t acc_zero() { return f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// ----------------------------------------------------------- wave primitives
+
+// Inclusive segmented scan over the 64 lanes: a set `head` flag starts a new
+// segment at that lane.  Fixed tree order (deterministic).
+__device__ __forceinline__ float wave_segmented_scan(float v, int head) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        float pv = __shfl_up(v, d, kWave);
+        int ph = __shfl_up(head, d, kWave);
+        if (lane >= d && !head) {
+            v = pv + v;
+            head = ph;
+        }
+    }
+    return v;
+}
+
+}  // namespace ssd

@@ -1,0 +1,87 @@
+// ssd_launch.h -- argument blocks and launchers shared by the C-ABI layer
+// (ssd_api.hip) and the kernels (ssd_kernels.hip).  Internal to libssd.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// K1 arguments.
+struct DtArgs {
+    const float* dt_raw;    // (b, L, H)
+    const float* dt_bias;   // (H) or null
+    const float* A;         // (H)
+    const int32_t* seq_idx; // (b, L) or null
+    int softplus;
+    float dt_min, dt_max;
+    int64_t L, Lp;          // tokens, tokens padded to whole chunks
+    int H, Q;
+    float* dtv;             // (b, H, Lp) transformed dt
+    float* cs;              // (b, H, Lp) segmented chunk cumsum of dt*A
+};
+
+// K2 / K4 arguments.
+struct ScanArgs {
+    const void* x;          // (b, L, H, P)
+    const void* B;          // (b, L, G, N)
+    const void* C;          // (b, L, G, N)
+    void* y;                // (b, L, H, P)
+    const float* dtv;       // (b, H, Lp)
+    const float* cs;        // (b, H, Lp)
+    const int32_t* seq_idx; // (b, L) or null
+    const float* D;         // (H) or null
+    const float* init;      // (b, H, P, N) or null
+    float* final_states;    // (b, H, P, N) or null
+    float* seg_state;       // (b, H, nseg, P, N) workspace
+    float* seg_mult;        // (b, H, nseg) workspace
+    int64_t L, Lp;
+    int H, G;
+    int nc, nseg, cps;      // chunks, segments, chunks per segment
+};
+
+// K3 arguments.
+struct PassArgs {
+    float* seg_state;       // (b*H, nseg, P*N)
+    const float* seg_mult;  // (b*H, nseg)
+    const float* init;      // (b*H, P*N) or null
+    int64_t PN;
+    int nseg;
+};
+
+// K5 arguments.
+struct StepArgs {
+    float* state;           // (b, H, P, N)
+    const void* x;          // (b, H, P)
+    const float* dt;        // (b, H)
+    const float* dt_bias;   // (H) or null
+    int softplus;
+    float dt_min, dt_max;
+    const float* A;         // (H)
+    const void* B;          // (b, G, N)
+    const void* C;          // (b, G, N)
+    const float* D;         // (H) or null
+    void* y;                // (b, H, P)
+    int H, P, G;
+};
+
+typedef hipError_t (*ScanLaunchFn)(const ScanArgs&, int64_t nblocks, hipStream_t);
+
+struct ScanVariant {
+    int io;  // 0 = fp32, 1 = bf16
+    int P, N, Q;
+    ScanLaunchFn chunk_state;   // K2
+    ScanLaunchFn chunk_output;  // K4
+};
+
+const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q);
+int scan_variant_count();
+const ScanVariant* scan_variant_at(int i);
+
+hipError_t launch_dt_cumsum(const DtArgs& a, int64_t batch, int nc, hipStream_t st);
+hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
+hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);
+hipError_t launch_state_update(int io, int64_t N, const StepArgs& a, int64_t nblocks,
+                               hipStream_t st);
+
+}  // namespace ssd

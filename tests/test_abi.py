@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ssd.h declares, and rejects bad arguments before launching anything
+(fail closed: RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section 4.1 WS1 rules
+and section 7 "Fail closed").  Only calls that validation rejects, or that
+return before any launch (batch = 0), are made here."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import mamba_ssd_selective_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WORKSPACE, BAD_ARG, ALIAS, HIP = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.library_path()):
+        pytest.fail("libssd.so is not built; run __graft_entry__.build()")
+    return ssd.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    names = set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text))
+    assert {"ssd_chunk_scan_fwd", "ssd_state_update", "ssd_chunk_scan_workspace_bytes",
+            "ssd_status_string", "ssd_abi_version"} <= names
+    raw = ctypes.CDLL(ssd.library_path())
+    for n in sorted(names):
+        assert hasattr(raw, n), "libssd.so does not export %s" % n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssd_abi_version() == 1
+    for s in range(9):
+        assert lib.ssd_status_string(s)
+    assert b"unknown" in lib.ssd_status_string(99)
+
+
+def test_supported_set(lib):
+    assert ssd.supported(ssd.BF16, 64, 128, 128)
+    assert ssd.supported(ssd.BF16, 64, 128, 256)
+    assert ssd.supported(ssd.F32, 16, 16, 64)
+    assert not ssd.supported(ssd.BF16, 48, 128, 128)
+    assert not ssd.supported(ssd.BF16, 64, 128, 100)
+    assert not ssd.supported(5, 64, 128, 128)
+
+
+def test_workspace_and_segments(lib):
+    # config 1: 64 heads, 64 chunks of 128 -> 8 segments of 8 chunks
+    ws = ssd.workspace_bytes(1, 8192, 64, 64, 128, 8, 128)
+    dt_cs = 2 * 64 * 8192 * 4
+    seg = 64 * 8 * 64 * 128 * 4 + 256 * math.ceil(64 * 8 * 4 / 256)
+    assert ws == dt_cs + seg
+    assert ssd.segments(1, 8192, 64, 64, 128, 8, 128) == 8
+    # enough rows x heads: one segment, no segment scratch
+    assert ssd.segments(64, 4096, 64, 64, 128, 8, 128) == 1
+    assert ssd.workspace_bytes(64, 4096, 64, 64, 128, 8, 128) == 2 * 64 * 64 * 4096 * 4
+    # ragged L pads to whole chunks
+    assert ssd.workspace_bytes(1, 300, 64, 64, 128, 8, 128) >= 2 * 64 * 384 * 4
+    assert ssd.workspace_bytes(1, 0, 64, 64, 128, 8, 128) == 0
+    assert ssd.workspace_bytes(1, 128, 64, 48, 128, 8, 128) == 0  # unsupported
+
+
+class _Buf:
+    """Fake, never-dereferenced device addresses, 256-byte aligned and far apart."""
+
+    def __init__(self):
+        self.next = 0x10000000
+
+    def __call__(self, nbytes=1 << 24):
+        a = self.next
+        self.next += (nbytes + (1 << 24)) // 256 * 256
+        return a
+
+
+def _scan_call(lib, dims=(1, 256, 4, 16, 16, 1, 64), io=ssd.F32, **over):
+    buf = _Buf()
+    args = dict(x=buf(), dt=buf(), dt_bias=None, softplus=1, lo=0.0, hi=math.inf, A=buf(),
+                B=buf(), C=buf(), D=None, init=None, seq=None, y=buf(), final=None,
+                ws=buf(), ws_bytes=1 << 30)
+    args.update(over)
+    d = ssd._Dims(*dims) if dims is not None else None
+    return lib.ssd_chunk_scan_fwd(
+        ctypes.byref(d) if d is not None else None, io, args["x"], args["dt"], args["dt_bias"],
+        args["softplus"], args["lo"], args["hi"], args["A"], args["B"], args["C"], args["D"],
+        args["init"], args["seq"], args["y"], args["final"], args["ws"], args["ws_bytes"], None)
+
+
+def test_scan_rejects_bad_arguments(lib):
+    assert _scan_call(lib, dims=None) == NULL_ARG
+    assert _scan_call(lib, io=7) == BAD_DTYPE
+    assert _scan_call(lib, dims=(1, 256, 6, 16, 16, 4, 64)) == BAD_SHAPE   # H % G
+    assert _scan_call(lib, dims=(-1, 256, 4, 16, 16, 1, 64)) == BAD_SHAPE
+    assert _scan_call(lib, dims=(1, 256, 4, 16, 16, 1, 0)) == BAD_SHAPE
+    assert _scan_call(lib, dims=(1, 256, 4, 24, 16, 1, 64)) == UNSUPPORTED
+    assert _scan_call(lib, dims=(1, 256, 4, 16, 16, 1, 256)) == UNSUPPORTED  # f32, Q=256
+    assert _scan_call(lib, x=None) == NULL_ARG
+    assert _scan_call(lib, A=None) == NULL_ARG
+    assert _scan_call(lib, y=None) == NULL_ARG
+    assert _scan_call(lib, ws=None) == WORKSPACE
+    assert _scan_call(lib, ws_bytes=16) == WORKSPACE
+    assert _scan_call(lib, ws=0x70000010) == WORKSPACE  # not 256-byte aligned
+    assert _scan_call(lib, lo=1.0, hi=0.5) == BAD_ARG
+    assert _scan_call(lib, lo=float("nan")) == BAD_ARG
+    assert _scan_call(lib, x=0x70000004) == BAD_ARG  # not 16-byte aligned
+
+
+def test_scan_rejects_aliasing(lib):
+    buf = _Buf()
+    x = buf()
+    assert _scan_call(lib, x=x, y=x + 1024) == ALIAS          # y overlaps x
+    st = buf()
+    assert _scan_call(lib, init=st, final=st + 256) == ALIAS  # partial overlap
+    w = buf()
+    assert _scan_call(lib, ws=w, y=w) == ALIAS
+    assert _scan_call(lib, final=x) == ALIAS
+
+
+def test_scan_empty_batch_launches_nothing(lib):
+    # batch = 0 passes validation and returns before any HIP call
+    assert _scan_call(lib, dims=(0, 256, 4, 16, 16, 1, 64), x=None, y=None) == OK
+
+
+def _step_call(lib, b=2, H=4, P=16, N=16, G=1, io=ssd.F32, **over):
+    buf = _Buf()
+    a = dict(state=buf(), x=buf(), dt=buf(), bias=None, sp=1, lo=0.0, hi=math.inf, A=buf(),
+             B=buf(), C=buf(), D=None, y=buf())
+    a.update(over)
+    return lib.ssd_state_update(b, H, P, N, G, io, a["state"], a["x"], a["dt"], a["bias"],
+                                a["sp"], a["lo"], a["hi"], a["A"], a["B"], a["C"], a["D"],
+                                a["y"], None)
+
+
+def test_state_update_rejects_bad_arguments(lib):
+    assert _step_call(lib, io=3) == BAD_DTYPE
+    assert _step_call(lib, H=6, G=4) == BAD_SHAPE
+    assert _step_call(lib, N=48) == UNSUPPORTED
+    assert _step_call(lib, state=None) == NULL_ARG
+    assert _step_call(lib, lo=2.0, hi=1.0) == BAD_ARG
+    assert _step_call(lib, state=0x70000008) == BAD_ARG
+    buf = _Buf()
+    s = buf()
+    assert _step_call(lib, state=s, y=s + 64) == ALIAS
+    assert _step_call(lib, b=0) == OK

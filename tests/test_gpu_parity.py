@@ -1,0 +1,246 @@
+"""GPU parity of the HIP path against the fp64 oracle at sizes the oracle
+finishes in seconds (several chunks, ragged tails, packed sequences, segment
+chaining), plus the decode update, determinism and sequence-boundary exactness.
+
+Tolerance (relative L2 over all elements): 1e-4 for fp32 inputs, 2e-2 for bf16
+inputs with fp32 state.  Because D*x dominates y for these input distributions,
+every case is also checked with D = 0, where y is the state-space part alone.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import head_subset, host, log, run_oracle, run_scan, tol, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mamba_ssd_selective_amd as ssd
+    ssd.library()
+
+
+def _packed(rng, b, L, nseq):
+    rows = []
+    for _ in range(b):
+        cuts = np.sort(rng.choice(np.arange(1, L), size=nseq - 1, replace=False))
+        lens = np.diff(np.concatenate([[0], cuts, [L]]))
+        rows.append(np.repeat(np.arange(nseq, dtype=np.int32), lens))
+    return np.stack(rows)
+
+
+def _check_case(p, io, Q, label):
+    t = to_dev(p, io)
+    for zero_D in (False, True):
+        y, fs = run_scan(t, Q, zero_D=zero_D)
+        yr, hr = run_oracle(p, zero_D=zero_D)
+        ey, eh = oracle.rel_l2(host(y), yr), oracle.rel_l2(host(fs), hr)
+        log("%s D=%s: rel_l2 y=%.3e final=%.3e" % (label, "0" if zero_D else "D", ey, eh))
+        assert ey < tol(io) and eh < tol(io), (label, zero_D, ey, eh)
+        assert np.isfinite(host(y)).all()
+
+
+def test_config0_tiny_fp32():
+    w = workloads.WORKLOADS[0]
+    p = workloads.make_inputs(w)
+    _check_case(p, "f32", w.chunk, "config0")
+
+
+FP32_CASES = [
+    # b, L, H, P, N, G, Q, init, packed
+    (2, 300, 8, 64, 128, 2, 64, True, False),
+    (1, 1000, 4, 64, 128, 1, 128, True, True),
+    (3, 77, 4, 16, 16, 2, 32, False, True),
+    (1, 1, 4, 16, 16, 1, 64, True, False),
+    (1, 64, 4, 16, 16, 1, 64, True, False),
+    (1, 65, 4, 16, 16, 1, 64, False, False),
+    (2, 500, 4, 16, 16, 4, 128, True, True),
+]
+
+
+@pytest.mark.parametrize("case", FP32_CASES, ids=lambda c: "b%dL%dH%dP%dN%dG%dQ%d_i%d_p%d" % c)
+def test_fp32_parity(case):
+    b, L, H, P, N, G, Q, init, packed = case
+    rng = np.random.default_rng(hash(case) % 2**32)
+    p = workloads.random_problem(rng, b, L, H, P, N, G, io="f32", init=init)
+    if packed:
+        p["seq_idx"] = _packed(rng, b, L, 3)
+    _check_case(p, "f32", Q, "fp32 %s" % (case,))
+
+
+BF16_CASES = [
+    (1, 4096, 64, 64, 128, 8, 128, True, False),  # 8 segments of 4 chunks
+    (2, 777, 16, 64, 128, 4, 256, True, True),
+    (4, 333, 8, 64, 128, 2, 64, False, True),
+    (1, 2000, 8, 64, 64, 2, 128, True, False),
+    (2, 150, 4, 16, 16, 1, 64, True, True),
+    (1, 129, 64, 64, 128, 8, 128, False, False),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "b%dL%dH%dP%dN%dG%dQ%d_i%d_p%d" % c)
+def test_bf16_parity(case):
+    b, L, H, P, N, G, Q, init, packed = case
+    rng = np.random.default_rng(hash(case) % 2**32)
+    p = workloads.random_problem(rng, b, L, H, P, N, G, io="bf16", init=init)
+    if packed:
+        p["seq_idx"] = _packed(rng, b, L, 4)
+    _check_case(p, "bf16", Q, "bf16 %s" % (case,))
+
+
+@pytest.mark.parametrize("Q", [64, 128, 256])
+def test_chunk_size_sweep_config1_shapes(Q):
+    """Results are independent of the chunk size (within tolerance) at the
+    30B layer shape (H=64, P=64, N=128, G=8)."""
+    w = workloads.WORKLOADS[1]
+    p = workloads.make_inputs(w, seqlen=2048)
+    t = to_dev(p, "bf16")
+    sub_heads = [0, 9, 36, 63]
+    for zero_D in (False, True):
+        y, fs = run_scan(t, Q, zero_D=zero_D)
+        sub = head_subset(p, sub_heads)
+        yr, hr = run_oracle(sub, zero_D=zero_D)
+        ey = oracle.rel_l2(host(y)[:, :, sub_heads], yr)
+        eh = oracle.rel_l2(host(fs)[:, sub_heads], hr)
+        log("chunk sweep Q=%d D=%s: y=%.3e final=%.3e" % (Q, not zero_D, ey, eh))
+        assert ey < 2e-2 and eh < 2e-2
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("PN", [(16, 16), (64, 128), (64, 256), (32, 64)])
+def test_decode_step_parity(io, PN):
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    P, N = PN
+    b, H, G = 5, 8, 2
+    rng = np.random.default_rng(P * 1000 + N)
+    p = workloads.random_problem(rng, b, 3, H, P, N, G, io=io, init=True)
+    t = to_dev(p, io)
+    state = t["h_init"].clone()
+    st_ref = p["h_init"].astype(np.float64)
+    for k in range(3):
+        y = ssd.state_update(state, t["x"][:, k].contiguous(), t["dt_raw"][:, k].contiguous(),
+                             t["A"], t["B"][:, k].contiguous(), t["C"][:, k].contiguous(),
+                             D=t["D"], dt_bias=t["dt_bias"])
+        torch.cuda.synchronize()
+        st_ref, yr = oracle.step(st_ref, p["x"][:, k], p["dt_raw"][:, k], p["A"], p["B"][:, k],
+                                 p["C"][:, k], dt_bias=p["dt_bias"], D=p["D"])
+        ey = oracle.rel_l2(host(y), yr)
+        es = oracle.rel_l2(host(state), st_ref)
+        log("decode %s P=%d N=%d step %d: y=%.3e state=%.3e" % (io, P, N, k, ey, es))
+        assert es < 1e-5
+        assert ey < (1e-5 if io == "f32" else 2e-2)
+
+
+def test_determinism_bitwise():
+    """Fixed reduction order, no atomics: two runs are bitwise equal."""
+    w = workloads.WORKLOADS[2]
+    p = workloads.make_inputs(w, seqlen=4096)
+    p["seq_idx"] = np.repeat(np.arange(5, dtype=np.int32), [700, 900, 33, 2000, 463])[None]
+    t = to_dev(p, "bf16")
+    y1, f1 = run_scan(t, 128)
+    y2, f2 = run_scan(t, 128)
+    import torch
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_other_sequence_perturbation_is_bitwise_invisible():
+    """Changing one packed sequence's (finite) inputs leaves every other
+    sequence's outputs bitwise unchanged (masks are selects)."""
+    rng = np.random.default_rng(77)
+    b, L, H, P, N, G = 1, 1500, 8, 64, 128, 2
+    p = workloads.random_problem(rng, b, L, H, P, N, G, io="bf16", init=True)
+    lens = [300, 77, 500, 623]
+    p["seq_idx"] = np.repeat(np.arange(4, dtype=np.int32), lens)[None]
+    starts = np.cumsum([0] + lens)
+    t = to_dev(p, "bf16")
+    y0, f0 = run_scan(t, 128)
+    k = 1  # perturb sequence 1 (tokens 300..376, mid-chunk on both sides)
+    q = {kk: (v.copy() if isinstance(v, np.ndarray) else v) for kk, v in p.items()}
+    a, e = starts[k], starts[k + 1]
+    q["x"][:, a:e] = workloads.round_bf16(rng.standard_normal(q["x"][:, a:e].shape).astype(np.float32) * 3)
+    q["B"][:, a:e] = workloads.round_bf16(rng.standard_normal(q["B"][:, a:e].shape).astype(np.float32))
+    q["C"][:, a:e] = workloads.round_bf16(rng.standard_normal(q["C"][:, a:e].shape).astype(np.float32))
+    q["dt_raw"][:, a:e] = rng.standard_normal(q["dt_raw"][:, a:e].shape).astype(np.float32) + 2
+    y1, f1 = run_scan(to_dev(q, "bf16"), 128)
+    Y0, Y1 = host(y0), host(y1)
+    assert not np.array_equal(Y0[:, a:e], Y1[:, a:e])
+    mask = np.ones(L, dtype=bool)
+    mask[a:e] = False
+    assert np.array_equal(Y0[:, mask], Y1[:, mask])
+    assert np.array_equal(host(f0), host(f1))
+
+
+def test_chunk_aligned_sequence_matches_standalone_run_bitwise():
+    """A sequence that starts on a chunk boundary of a packed row gives bitwise
+    the same outputs and final state as a run of that sequence alone (same
+    chunk grid, one segment per row), and the carry at the reset is exactly 0."""
+    import mamba_ssd_selective_amd as ssd
+    rng = np.random.default_rng(5)
+    b, H, P, N, G, Q = 8, 64, 64, 128, 8, 128
+    La, Lb = 256, 300
+    p = workloads.random_problem(rng, b, La + Lb, H, P, N, G, io="bf16", init=True)
+    p["seq_idx"] = np.repeat(np.array([4, 9], dtype=np.int32), [La, Lb])[None].repeat(b, 0)
+    assert ssd.segments(b, La + Lb, H, P, N, G, Q) == 1
+    assert ssd.segments(b, Lb, H, P, N, G, Q) == 1
+    y, f = run_scan(to_dev(p, "bf16"), Q)
+    alone = {k: (v[:, La:] if k in ("x", "dt_raw", "B", "C") else v) for k, v in p.items()}
+    alone["seq_idx"] = None
+    alone["h_init"] = None
+    ya, fa = run_scan(to_dev(alone, "bf16"), Q)
+    assert np.array_equal(host(y)[:, La:], host(ya))
+    assert np.array_equal(host(f), host(fa))
+
+
+def test_empty_and_tiny_lengths():
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    dev = torch.device("cuda:0")
+    b, H, P, N, G = 2, 4, 16, 16, 1
+    h0 = torch.randn(b, H, P, N, device=dev)
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, device=dev, dtype=dt)
+    A = -torch.ones(H, device=dev)
+    y, fs = ssd.chunk_scan_fwd(z(b, 0, H, P), z(b, 0, H), A, z(b, 0, G, N), z(b, 0, G, N),
+                               chunk_size=64, initial_states=h0, return_final_states=True)
+    torch.cuda.synchronize()
+    assert y.shape == (b, 0, H, P) and torch.equal(fs, h0)
+    y, fs = ssd.chunk_scan_fwd(z(b, 0, H, P), z(b, 0, H), A, z(b, 0, G, N), z(b, 0, G, N),
+                               chunk_size=64, return_final_states=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, torch.zeros_like(fs))
+    y = ssd.chunk_scan_fwd(z(0, 10, H, P), z(0, 10, H), A, z(0, 10, G, N), z(0, 10, G, N),
+                           chunk_size=64)
+    assert y.shape == (0, 10, H, P)
+
+
+def test_final_state_may_alias_initial_state():
+    import torch
+    rng = np.random.default_rng(9)
+    p = workloads.random_problem(rng, 2, 700, 8, 64, 128, 2, io="bf16", init=True)
+    t = to_dev(p, "bf16")
+    y1, f1 = run_scan(t, 128)
+    st = t["h_init"].clone()
+    t2 = dict(t)
+    t2["h_init"] = st
+    y2, f2 = run_scan(t2, 128, final_states_out=st)
+    assert f2.data_ptr() == st.data_ptr()
+    assert torch.equal(y1, y2) and torch.equal(f1, st)
+
+
+def test_rejects_unsupported_geometry_on_device():
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    dev = torch.device("cuda:0")
+    x = torch.zeros(1, 64, 4, 48, device=dev)
+    with pytest.raises(ssd.SSDError) as e:
+        ssd.chunk_scan_fwd(x, torch.zeros(1, 64, 4, device=dev), -torch.ones(4, device=dev),
+                           torch.zeros(1, 64, 1, 16, device=dev), torch.zeros(1, 64, 1, 16, device=dev),
+                           chunk_size=64)
+    assert e.value.status == 4
