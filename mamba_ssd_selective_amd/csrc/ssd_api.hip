@@ -17,9 +17,9 @@ constexpr int64_t kTargetWorkgroups = 512;  // enough independent workgroups for
 constexpr size_t kAlign = 256;
 
 struct Plan {
-    int64_t nc = 0, Lp = 0;
+    int64_t nc = 0;
     int64_t nseg = 1, cps = 1;
-    size_t off_dtv = 0, off_cs = 0, off_seg = 0, off_mult = 0, total = 0;
+    size_t off_seg = 0, off_mult = 0, total = 0;
 };
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -28,7 +28,6 @@ Plan make_plan(const ssd_dims& d) {
     Plan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
     p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
-    p.Lp = p.nc * d.chunk_size;
     const int64_t bh = d.batch * d.nheads;
     int64_t nseg = (kTargetWorkgroups + bh - 1) / bh;
     if (nseg < 1) nseg = 1;
@@ -37,10 +36,6 @@ Plan make_plan(const ssd_dims& d) {
     p.nseg = (p.nc + p.cps - 1) / p.cps;
     const size_t f = sizeof(float);
     size_t off = 0;
-    p.off_dtv = off;
-    off = align_up(off + static_cast<size_t>(bh * p.Lp) * f);
-    p.off_cs = off;
-    off = align_up(off + static_cast<size_t>(bh * p.Lp) * f);
     if (p.nseg > 1) {
         p.off_seg = off;
         off = align_up(off + static_cast<size_t>(bh * p.nseg * d.headdim * d.dstate) * f);
@@ -203,35 +198,18 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     }
     const ssd::ScanVariant* var = ssd::find_scan_variant(io, P, N, d->chunk_size);
     char* wsb = static_cast<char*>(workspace);
-    float* dtv = reinterpret_cast<float*>(wsb + plan.off_dtv);
-    float* cs = reinterpret_cast<float*>(wsb + plan.off_cs);
-
-    ssd::DtArgs da;
-    da.dt_raw = dt;
-    da.dt_bias = dt_bias;
-    da.A = A;
-    da.seq_idx = seq_idx;
-    da.softplus = dt_softplus ? 1 : 0;
-    da.dt_min = dt_min;
-    da.dt_max = dt_max;
-    da.L = L;
-    da.Lp = plan.Lp;
-    da.H = static_cast<int>(H);
-    da.Q = static_cast<int>(d->chunk_size);
-    da.dtv = dtv;
-    da.cs = cs;
-    if (timed_launch(k, hs, [&] {
-            return ssd::launch_dt_cumsum(da, b, static_cast<int>(plan.nc), hs);
-        }) != hipSuccess)
-        return SSD_ERR_HIP;
 
     ssd::ScanArgs sa;
     sa.x = x;
     sa.B = B;
     sa.C = C;
     sa.y = y;
-    sa.dtv = dtv;
-    sa.cs = cs;
+    sa.dt_raw = dt;
+    sa.dt_bias = dt_bias;
+    sa.A = A;
+    sa.softplus = dt_softplus ? 1 : 0;
+    sa.dt_min = dt_min;
+    sa.dt_max = dt_max;
     sa.seq_idx = seq_idx;
     sa.D = D;
     sa.init = initial_states;
@@ -239,7 +217,6 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     sa.seg_state = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_seg) : nullptr;
     sa.seg_mult = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_mult) : nullptr;
     sa.L = L;
-    sa.Lp = plan.Lp;
     sa.H = static_cast<int>(H);
     sa.G = static_cast<int>(G);
     sa.nc = static_cast<int>(plan.nc);

@@ -113,6 +113,72 @@ __device__ __forceinline__ void store4(T* p, const Vec4<T>& v) {
     }
 }
 
+// --------------------------------------------------------- raw 16-byte vectors
+// Global tiles are moved as raw uint4 (16 bytes) so that a load never has to
+// complete before the code that issued it moves on; elements are unpacked only
+// where they are used.
+
+__device__ __forceinline__ uint4 ld_raw16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint4 raw_keep(bool keep, const uint4& v) {
+    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+template <int I>
+__device__ __forceinline__ uint32_t u4_at(const uint4& v) {
+    static_assert(I >= 0 && I < 4, "dword index");
+    if constexpr (I == 0) return v.x;
+    else if constexpr (I == 1) return v.y;
+    else if constexpr (I == 2) return v.z;
+    else return v.w;
+}
+
+// Element E of a raw 16-byte vector of io elements, as fp32.
+template <typename T, int E>
+__device__ __forceinline__ float raw_elem_f32(const uint4& v) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t d = u4_at<E / 2>(v);
+        return __uint_as_float((E % 2 == 0) ? (d << 16) : (d & 0xFFFF0000u));
+    } else {
+        return __uint_as_float(u4_at<E>(v));
+    }
+}
+
+// Two fp32 values -> packed bf16 pair (RNE), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = static_cast<__bf16>(lo);
+    v[1] = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Store four fp32 values as four consecutive io elements (8 or 16 bytes).
+template <typename T>
+__device__ __forceinline__ void store4_f32(T* p, float a, float b, float c, float d) {
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+    } else {
+        *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+    }
+}
+
+// Column E of a 4-row x (16 bytes) block: the four elements rows[0..3][E],
+// stored as four consecutive io elements.
+template <typename T, int E>
+__device__ __forceinline__ void store_col4(T* p, const uint4 (&rows)[4]) {
+    if constexpr (sizeof(T) == 2) {
+        // v_perm_b32 byte selectors: low halves {0,1 | 4,5}, high halves {2,3 | 6,7}
+        constexpr uint32_t sel = (E % 2 == 0) ? 0x05040100u : 0x07060302u;
+        const uint32_t lo = __builtin_amdgcn_perm(u4_at<E / 2>(rows[1]), u4_at<E / 2>(rows[0]), sel);
+        const uint32_t hi = __builtin_amdgcn_perm(u4_at<E / 2>(rows[3]), u4_at<E / 2>(rows[2]), sel);
+        *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<uint4*>(p) =
+            make_uint4(u4_at<E>(rows[0]), u4_at<E>(rows[1]), u4_at<E>(rows[2]), u4_at<E>(rows[3]));
+    }
+}
+
 // ------------------------------------------------------------------ fragments
 
 template <typename T> struct Frag;
@@ -123,6 +189,33 @@ template <> struct Frag<uint16_t> {
 template <> struct Frag<float> {
     float v[8];
 };
+
+// A fragment's worth of raw bytes (16 for bf16, 32 for fp32), loaded without
+// waiting; turned into a Frag where it is used.
+template <typename T> struct RawFrag {
+    uint4 r[sizeof(T) == 2 ? 1 : 2];
+};
+template <typename T>
+__device__ __forceinline__ RawFrag<T> raw_frag_load8(const T* p) {
+    RawFrag<T> f;
+    f.r[0] = ld_raw16(p);
+    if constexpr (sizeof(T) == 4) f.r[1] = ld_raw16(p + 4);
+    return f;
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_raw(const RawFrag<T>& f, bool keep) {
+    Frag<T> out;
+    if constexpr (sizeof(T) == 2) {
+        out.v = __builtin_bit_cast(bf16x8_t, raw_keep(keep, f.r[0]));
+    } else {
+        const uint4 a = raw_keep(keep, f.r[0]), b = raw_keep(keep, f.r[1]);
+        out.v[0] = __uint_as_float(a.x); out.v[1] = __uint_as_float(a.y);
+        out.v[2] = __uint_as_float(a.z); out.v[3] = __uint_as_float(a.w);
+        out.v[4] = __uint_as_float(b.x); out.v[5] = __uint_as_float(b.y);
+        out.v[6] = __uint_as_float(b.z); out.v[7] = __uint_as_float(b.w);
+    }
+    return out;
+}
 
 // Eight consecutive elements (k = 8q + e) from LDS or global memory.
 template <typename T>

@@ -14,23 +14,27 @@
 //           + [seq_i = seq of the previous chunk's last token] exp(cs_i) h_{c-1} . C_i
 //           + D x_i
 //
-// Kernel pipeline of one ssd_chunk_scan_fwd call (one process, one GPU):
-//   K1 dt_cumsum_kernel     dt = clamp(softplus(dt_raw + dt_bias)), segmented
-//                           chunk cumsum of dt*A (wave-level segmented scan)
-//   K2 chunk_state_kernel   per (row, head, segment of chunks): chunk states on
-//                           bf16 MFMA from LDS-staged, transposed B and x tiles,
-//                           chained inside the segment in registers; writes the
-//                           segment's end state and its decay multiplier
-//   K3 state_pass_kernel    fp32 pass over segments: each segment's incoming state
-//   K4 chunk_output_kernel  per (row, head, segment): C.B^T masked-decay intra-chunk
-//                           product, C.h_prev carried-state term and D skip on
-//                           MFMA; the state is carried chunk to chunk in registers
-//                           (recomputing the chunk state with K2's device code)
-// and for decode:
-//   K5 state_update_kernel  one token: coalesced in-place fp32 state update
+// Kernels of one ssd_chunk_scan_fwd call (one process, one GPU), each
+// workgroup owning one (row, head, segment of consecutive chunks):
+//   chunk_scan_kernel<kOut = false>  "chunk state": per chunk, the dt transform
+//        and segmented chunk cumsum (wave-level scan), then S_c on bf16 MFMA from
+//        LDS-staged transposed B and x tiles, chained through the segment in
+//        registers; writes the segment's end state and decay multiplier.
+//   state_pass_kernel                fp32 pass over segments: each segment's
+//        incoming state (segment multipliers are wave-uniform scalars).
+//   chunk_scan_kernel<kOut = true>   "chunk output": the same per-chunk state
+//        chain plus the outputs: C.B^T masked-decay intra-chunk product, the
+//        C.h_prev carried-state term and the D skip, on MFMA.
+// The first two run only when the rows are cut into more than one segment
+// (few rows x heads); with one segment per row the state is carried through
+// the whole row inside one workgroup.
+// Decode:
+//   state_update_kernel              one token: coalesced in-place fp32 update.
 //
-// Segments exist only to give the GPU enough independent workgroups; with
-// batch*heads large enough there is one segment per row and K2/K3 are skipped.
+// Inside a workgroup (8 waves) the chunk loop is software-pipelined: the
+// global loads of chunk c+1 (x, B, C rows, raw dt, seq ids) are issued into
+// registers before chunk c's MFMA work, and wave 0 runs chunk c+1's dt scan
+// while the other waves finish chunk c; two barriers per chunk.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -47,77 +51,15 @@ __device__ __forceinline__ int64_t xcd_work_index(int64_t bid, int64_t nblocks) 
     return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
 }
 
-// ===========================================================================
-// K1: dt transform + segmented chunk cumsum.
-// grid (nc, ceil(H/16), batch), 256 threads.  Writes dtv and cs as (b, H, Lp)
-// with Lp = nc*Q; padded tokens (t >= L) get dt = 0 (so they contribute nothing).
-__global__ __launch_bounds__(256) void dt_cumsum_kernel(DtArgs a) {
-    constexpr int kHB = 16;
-    __shared__ float s_raw[256][kHB + 1];
-    __shared__ int s_seq[256];
-    const int c = blockIdx.x, h0 = blockIdx.y * kHB;
-    const int64_t b = blockIdx.z;
-    const int Q = a.Q;
-    const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const int tid = threadIdx.x;
-    for (int idx = tid; idx < Q * kHB; idx += 256) {
-        const int t = idx / kHB, hh = idx % kHB;
-        float v = 0.0f;
-        if (t0 + t < a.L && h0 + hh < a.H) v = a.dt_raw[(b * a.L + t0 + t) * a.H + h0 + hh];
-        s_raw[t][hh] = v;
-    }
-    for (int t = tid; t < Q; t += 256) {
-        int64_t tt = t0 + t < a.L ? t0 + t : a.L - 1;
-        s_seq[t] = a.seq_idx ? a.seq_idx[b * a.L + tt] : 0;
-    }
-    __syncthreads();
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int E = (Q + kWave - 1) / kWave;  // tokens per lane (<= 4)
-    for (int hh = wave; hh < kHB; hh += 4) {
-        const int h = h0 + hh;
-        if (h >= a.H) break;
-        const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-        const float Ah = a.A[h];
-        float dtv[4], loc[4];
-        int first_head = E;  // index of the first segment start inside this lane
-        float run = 0.0f;
-        for (int k = 0; k < E; ++k) {
-            const int t = lane * E + k;
-            float d = 0.0f;
-            bool head = false;
-            if (t < Q) {
-                if (t0 + t < a.L)
-                    d = dt_transform(s_raw[t][hh], bias, a.softplus, a.dt_min, a.dt_max);
-                head = (t == 0) || (s_seq[t] != s_seq[t - 1]);
-            }
-            dtv[k] = d;
-            const float av = d * Ah;
-            run = (k == 0 || head) ? av : run + av;
-            if (head && first_head == E) first_head = k;
-            loc[k] = run;
-        }
-        // lane aggregate: sum since its last segment start (or the whole lane)
-        const int lane_has_head = first_head < E;
-        const float incl = wave_segmented_scan(loc[E - 1], lane_has_head);
-        float excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 0.0f;
-        const int64_t base = (b * a.H + h) * a.Lp + t0;
-        for (int k = 0; k < E; ++k) {
-            const int t = lane * E + k;
-            if (t < Q) {
-                const float v = (k < first_head) ? excl + loc[k] : loc[k];
-                a.dtv[base + t] = dtv[k];
-                a.cs[base + t] = v;
-            }
-        }
-    }
-}
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kLdsBytes = 160 * 1024;
 
 // ===========================================================================
-// Shared tile configuration of K2 and K4.
+// Tile configuration.
 template <typename T, int P, int N, int Q>
 struct Cfg {
-    static_assert(P % 16 == 0 && N % 16 == 0 && Q % 32 == 0, "tile shape");
+    static_assert(P % 16 == 0 && N % 16 == 0 && Q % 32 == 0 && Q <= 256, "tile shape");
     static constexpr int kVec = Io<T>::kVec;
     static constexpr int NP = (N + 31) / 32 * 32;  // n padded to the MFMA k step
     static constexpr int PAD = kVec;               // 16 bytes of row padding in LDS
@@ -125,77 +67,238 @@ struct Cfg {
     static constexpr int SBW = Q + PAD;            // B^T*w rows       [N][SBW]
     static constexpr int SX = Q + PAD;             // x^T rows         [P][SX]
     static constexpr int SH = NP + PAD;            // h (operand) rows [P][SH]
-    static constexpr int B_ELEMS = (Q * SB > N * SBW) ? Q * SB : N * SBW;
-    static constexpr int NB = Q / 16;   // 16-row output blocks
-    static constexpr int PB = P / 16;   // 16-column blocks of P
-    static constexpr int NNB = N / 16;  // 16-row blocks of the state's n
-    static constexpr int KN = NP / 32;  // k steps over n
-    static constexpr int KQ = Q / 32;   // k steps over tokens
-    static constexpr int MT = (NNB + 3) / 4;  // state n-blocks per wave
+    static constexpr int NB = Q / 16;              // 16-row output blocks
+    static constexpr int PB = P / 16;              // 16-column blocks of P
+    static constexpr int NNB = N / 16;             // 16-row blocks of the state's n
+    static constexpr int KN = NP / 32;             // k steps over n
+    static constexpr int KQ = Q / 32;              // k steps over tokens
+    static constexpr int MT = (NNB + kWaves - 1) / kWaves;  // state n-blocks per wave
+    static constexpr int RB = NB >= 16 ? NB / 8 : 1;        // output row blocks per wave
+    // C fragments are prefetched a chunk ahead when a wave owns one row block;
+    // with two, they are loaded at the start of each row block (register budget).
+    static constexpr bool kPrefetchC = RB == 1;
+    static constexpr int RBC = kPrefetchC ? RB : 1;
+    static constexpr int CBX = P / kVec, XB = (Q / 4) * CBX;  // x staging blocks
+    static constexpr int CBB = N / kVec, BBK = (Q / 4) * CBB; // B staging blocks
+    static constexpr int XPT = (XB + kThreads - 1) / kThreads;
+    static constexpr int BPT = (BBK + kThreads - 1) / kThreads;
+    static constexpr int E = (Q + kWave - 1) / kWave;       // tokens per lane in the dt scan
+    static constexpr int META = 3 * Q * 4 + 16;
+    static constexpr int LDS_SEPARATE =
+        (Q * SB + N * SBW + P * SX + P * SH) * static_cast<int>(sizeof(T)) + 2 * META;
+    // When natural B and B^T*w do not both fit, B^T*w is written over natural B
+    // after the outputs of the chunk are done.
+    static constexpr bool kInPlace = LDS_SEPARATE > kLdsBytes;
+    static constexpr int B_ELEMS =
+        kInPlace ? (Q * SB > N * SBW ? Q * SB : N * SBW) : Q * SB;
+    // the zero padding columns [N, NP) of natural B are written once per kernel
+    static_assert(!(kInPlace && NP > N), "in-place B^T*w would overwrite B's zero padding");
 };
 
-// The fp32 state tiles a wave keeps in registers: n-block nb = wave + 4m,
+// Row block r (< RB) of wave w, chosen so that the two waves sharing a SIMD
+// (w and w+4) get equal triangular work.
+template <int NB>
+__device__ __forceinline__ int row_block(int wave, int r) {
+    if constexpr (NB >= 16) {
+        const int k = wave + 8 * (r / 2);
+        return (r % 2 == 0) ? k : NB - 1 - k;
+    } else if constexpr (NB == 8) {
+        return wave < 4 ? wave : 11 - wave;
+    } else {
+        return wave;  // valid only for wave < NB
+    }
+}
+
+// The fp32 state tiles a wave keeps in registers: n-block nb = wave + 8m,
 // p-block pb; lane (r16, q) holds h[16pb + r16][16nb + 4q + i], i = 0..3.
 template <typename T, int P, int N, int Q>
 struct StateRegs {
     f32x4_t v[Cfg<T, P, N, Q>::MT][Cfg<T, P, N, Q>::PB];
 };
 
-// Per-chunk token metadata staged in LDS.
+// Per-chunk token metadata in LDS: transformed dt, segmented cumsum of dt*A,
+// sequence ids (padded tokens repeat the last real token's id), and the id of
+// the token before the chunk (token 0 for the first chunk: the initial state
+// belongs to the sequence holding token 0).
 template <int Q>
 struct ChunkMeta {
     float cs[Q];
     float dt[Q];
     int seq[Q];
+    int seq_prev;
+    int pad_[3];
 };
 
-template <int Q>
-__device__ __forceinline__ void load_chunk_meta(ChunkMeta<Q>& m, const ScanArgs& a, int64_t b,
-                                                int h, int c) {
-    const int64_t base = (b * a.H + h) * a.Lp + static_cast<int64_t>(c) * Q;
-    const int64_t t0 = static_cast<int64_t>(c) * Q;
-    for (int i = threadIdx.x; i < Q; i += 256) {
-        m.cs[i] = a.cs[base + i];
-        m.dt[i] = a.dtv[base + i];
-        int64_t tt = t0 + i < a.L ? t0 + i : a.L - 1;
-        m.seq[i] = a.seq_idx ? a.seq_idx[b * a.L + tt] : 0;
+// Global data of one chunk, held in registers between its prefetch and its
+// staging into LDS.
+template <typename T, int P, int N, int Q, bool kOut>
+struct Prefetch {
+    using C_ = Cfg<T, P, N, Q>;
+    uint4 xr[C_::XPT][4];                      // x rows (raw)
+    uint4 br[C_::BPT][4];                      // B rows (raw)
+    RawFrag<T> cf[kOut ? C_::RBC : 1][C_::KN]; // C fragments (raw)
+    float dt[C_::E];                           // raw dt (wave 0)
+    int seq[C_::E];                            // sequence ids (wave 0)
+    int seq_prev;
+};
+
+struct WorkItem {
+    int64_t b;
+    int seg, h, g;
+};
+__device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
+    const int64_t nblocks = static_cast<int64_t>(gridDim.x);
+    int64_t w = xcd_work_index(blockIdx.x, nblocks);
+    const int hpg = a.H / a.G;
+    WorkItem it;
+    const int hh = static_cast<int>(w % hpg);
+    w /= hpg;
+    it.g = static_cast<int>(w % a.G);
+    w /= a.G;
+    it.seg = static_cast<int>(w % nseg_grid);
+    it.b = w / nseg_grid;
+    it.h = it.g * hpg + hh;
+    return it;
+}
+
+// C_i fragments of row block r of this wave (operand of C.B^T and C.h):
+// lane (r16, q) holds C[16I + r16][32s + 8q .. +7] for every k step s.  The
+// loads are unconditional (row and column clamped into the tensor); rows past
+// L and columns past N are zeroed where the fragments are used (c_frag_keep).
+template <typename T, int P, int N, int Q>
+using CRaw = RawFrag<T>[Cfg<T, P, N, Q>::KN];
+
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void load_c_frags(CRaw<T, P, N, Q>& cf, const ScanArgs& a,
+                                             const WorkItem& it, int c, int r, int wave, int lane) {
+    using C_ = Cfg<T, P, N, Q>;
+    const T* __restrict__ Cp = static_cast<const T*>(a.C);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int I = row_block<C_::NB>(wave, r);
+    int64_t ti = static_cast<int64_t>(c) * Q + 16 * I + r16;
+    ti = ti < a.L ? ti : a.L - 1;
+#pragma unroll
+    for (int s = 0; s < C_::KN; ++s) {
+        int n0 = 32 * s + 8 * q;
+        n0 = n0 < N ? n0 : N - 8;
+        cf[s] = raw_frag_load8(Cp + ((it.b * a.L + ti) * a.G + it.g) * N + n0);
     }
 }
 
-// Sequence id of the token before chunk c (token 0 for the first chunk: the
-// initial state belongs to the sequence holding token 0).
-__device__ __forceinline__ int prev_last_seq(const ScanArgs& a, int64_t b, int c, int Q) {
-    if (!a.seq_idx) return 0;
-    const int64_t t = c == 0 ? 0 : static_cast<int64_t>(c) * Q - 1;
-    return a.seq_idx[b * a.L + t];
+// Whether C fragment s of row block r holds real data (row < L, column < N).
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ bool c_frag_keep(const ScanArgs& a, int c, int r, int s, int wave,
+                                            int lane) {
+    using C_ = Cfg<T, P, N, Q>;
+    const int I = row_block<C_::NB>(wave, r);
+    const int64_t ti = static_cast<int64_t>(c) * Q + 16 * I + (lane & 15);
+    return (C_::NB >= 8 || wave < C_::NB) && ti < a.L && 32 * s + 8 * (lane >> 4) < N;
 }
 
-// x tile (Q tokens x P) of head h -> LDS transposed: sX[p][j].  Each thread
-// moves a block of 4 tokens x kVec columns and transposes it in registers.
-template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void stage_x_transposed(T* sX, const T* __restrict__ x,
-                                                   const ScanArgs& a, int64_t b, int h, int c) {
+// Issue the global loads of chunk c without waiting for them: every address
+// is clamped into its tensor (token index to L-1), and the values of tokens
+// past L are replaced by zeros at staging time.
+template <typename T, int P, int N, int Q, bool kOut>
+__device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q, kOut>& pf, const ScanArgs& a,
+                                               const WorkItem& it, int c, int wave, int lane) {
     using C_ = Cfg<T, P, N, Q>;
     constexpr int kV = C_::kVec;
-    constexpr int CB = P / kV;            // column blocks per token
-    constexpr int NBLK = (Q / 4) * CB;
+    const int tid = threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(c) * Q;
-    for (int blk = threadIdx.x; blk < NBLK; blk += 256) {
-        const int j0 = (blk / CB) * 4, p0 = (blk % CB) * kV;
-        Vec16<T> rows[4];
+    const int64_t tl = a.L - 1;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    const T* __restrict__ Bp = static_cast<const T*>(a.B);
+#pragma unroll
+    for (int k = 0; k < C_::XPT; ++k) {
+        int blk = tid + kThreads * k;
+        blk = blk < C_::XB ? blk : C_::XB - 1;
+        const int j0 = (blk / C_::CBX) * 4, p0 = (blk % C_::CBX) * kV;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + j0 + r;
-            rows[r] = (t < a.L) ? load16(x + ((b * a.L + t) * a.H + h) * P + p0) : zero16<T>();
-        }
-#pragma unroll
-        for (int e = 0; e < kV; ++e) {
-            Vec4<T> col;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) col.v[r] = rows[r].v[e];
-            store4(sX + (p0 + e) * C_::SX + j0, col);
+            int64_t t = t0 + j0 + r;
+            t = t < tl ? t : tl;
+            pf.xr[k][r] = ld_raw16(x + ((it.b * a.L + t) * a.H + it.h) * P + p0);
         }
     }
+#pragma unroll
+    for (int k = 0; k < C_::BPT; ++k) {
+        int blk = tid + kThreads * k;
+        blk = blk < C_::BBK ? blk : C_::BBK - 1;
+        const int j0 = (blk / C_::CBB) * 4, n0 = (blk % C_::CBB) * kV;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int64_t t = t0 + j0 + r;
+            t = t < tl ? t : tl;
+            pf.br[k][r] = ld_raw16(Bp + ((it.b * a.L + t) * a.G + it.g) * N + n0);
+        }
+    }
+    if constexpr (kOut && C_::kPrefetchC) load_c_frags<T, P, N, Q>(pf.cf[0], a, it, c, 0, wave, lane);
+    if (wave == 0) {
+        // without seq_idx the id loads read dt_raw (at least b*L elements of 4
+        // bytes) and the values are replaced by 0 where they are used, so that
+        // no load here depends on a branch
+        const int32_t* __restrict__ sq =
+            a.seq_idx ? a.seq_idx : reinterpret_cast<const int32_t*>(a.dt_raw);
+#pragma unroll
+        for (int k = 0; k < C_::E; ++k) {
+            int64_t t = t0 + lane * C_::E + k;
+            t = t < tl ? t : tl;
+            pf.dt[k] = a.dt_raw[(it.b * a.L + t) * a.H + it.h];
+            pf.seq[k] = sq[it.b * a.L + t];
+        }
+        pf.seq_prev = sq[it.b * a.L + (c == 0 ? 0 : t0 - 1)];
+    }
+}
+
+// Wave 0: dt transform and segmented inclusive cumsum of dt*A over the chunk
+// (restarted at the chunk start and at every sequence change), into LDS.
+template <typename T, int P, int N, int Q, bool kOut>
+__device__ __forceinline__ void chunk_meta_scan(ChunkMeta<Q>& m,
+                                                const Prefetch<T, P, N, Q, kOut>& pf,
+                                                const ScanArgs& a, int h, int c, int lane) {
+    using C_ = Cfg<T, P, N, Q>;
+    constexpr int E = C_::E;
+    const int64_t t0 = static_cast<int64_t>(c) * Q;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float Ah = a.A[h];
+    const bool has_seq = a.seq_idx != nullptr;
+    int sq[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) sq[k] = has_seq ? pf.seq[k] : 0;
+    // id of the token just before this lane's first token (within the chunk)
+    const int prev_lane_last = __shfl_up(sq[E - 1], 1, kWave);
+    float dtv[E], loc[E];
+    int first_head = E;
+    float run = 0.0f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int t = lane * E + k;
+        float d = 0.0f;
+        bool head = false;
+        if (t < Q) {
+            if (t0 + t < a.L) d = dt_transform(pf.dt[k], bias, a.softplus, a.dt_min, a.dt_max);
+            const int before = (k == 0) ? prev_lane_last : sq[k - 1];
+            head = (t == 0) || (sq[k] != before);
+        }
+        dtv[k] = d;
+        const float av = d * Ah;
+        run = (k == 0 || head) ? av : run + av;
+        if (head && first_head == E) first_head = k;
+        loc[k] = run;
+    }
+    const float incl = wave_segmented_scan(loc[E - 1], first_head < E);
+    float excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int t = lane * E + k;
+        if (t < Q) {
+            m.cs[t] = (k < first_head) ? excl + loc[k] : loc[k];
+            m.dt[t] = dtv[k];
+            m.seq[t] = sq[k];
+        }
+    }
+    if (lane == 0) m.seq_prev = has_seq ? pf.seq_prev : 0;
 }
 
 // Per-token weight of the chunk-state sum: w_j = exp(cs_last - cs_j) dt_j for
@@ -208,57 +311,110 @@ __device__ __forceinline__ float state_weight(const ChunkMeta<Q>& m, int j, floa
     return keep ? w : 0.0f;
 }
 
-// Writes one 4-token x kVec block of B, scaled by w_j, transposed into
-// sBw[n][j].  `rows` holds B[j0 + r][n0 .. n0 + kVec).
-template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void store_bw_block(T* sBw, const Vec16<T> (&rows)[4],
-                                               const ChunkMeta<Q>& m, int j0, int n0,
-                                               float cs_last, int seq_last) {
+// B^T * w: column E of one 4-token x kVec block of B, scaled by w_j and
+// stored transposed into sBw[n0 + E][j0 .. j0+3]; then the next column.
+template <typename T, int P, int N, int Q, int E = 0>
+__device__ __forceinline__ void store_bw_cols(T* sBw, const uint4 (&rows)[4], const float (&w)[4],
+                                              int j0, int n0) {
     using C_ = Cfg<T, P, N, Q>;
-    float w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = state_weight<Q>(m, j0 + r, cs_last, seq_last);
-#pragma unroll
-    for (int e = 0; e < C_::kVec; ++e) {
-        Vec4<T> col;
+    if constexpr (E < C_::kVec) {
+        float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float v = Io<T>::to_f32(rows[r].v[e]) * w[r];
-            col.v[r] = Io<T>::from_f32(w[r] != 0.0f ? v : 0.0f);
+            const float t = raw_elem_f32<T, E>(rows[r]) * w[r];
+            v[r] = w[r] != 0.0f ? t : 0.0f;
         }
-        store4(sBw + (n0 + e) * C_::SBW + j0, col);
+        store4_f32(sBw + (n0 + E) * C_::SBW + j0, v[0], v[1], v[2], v[3]);
+        store_bw_cols<T, P, N, Q, E + 1>(sBw, rows, w, j0, n0);
     }
 }
 
-// Chunk-state MFMA shared by K2 and K4:
-//   hreg.v[m][pb] (tile n-block nb = wave + 4m, p-block pb) += sum_j Bw^T[n][j] x[j][p]
 template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void chunk_state_mma(StateRegs<T, P, N, Q>& hreg,
-                                                const T* sBw, const T* sX, int wave, int lane) {
+__device__ __forceinline__ void store_bw_block(T* sBw, const uint4 (&rows)[4],
+                                               const ChunkMeta<Q>& m, int j0, int n0) {
+    const float cs_last = m.cs[Q - 1];
+    const int seq_last = m.seq[Q - 1];
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = state_weight<Q>(m, j0 + r, cs_last, seq_last);
+    store_bw_cols<T, P, N, Q>(sBw, rows, w, j0, n0);
+}
+
+// x^T: column E of one 4-token x kVec block of x into sX[p0 + E][j0 .. j0+3].
+template <typename T, int P, int N, int Q, int E = 0>
+__device__ __forceinline__ void store_x_cols(T* sX, const uint4 (&rows)[4], int j0, int p0) {
+    using C_ = Cfg<T, P, N, Q>;
+    if constexpr (E < C_::kVec) {
+        store_col4<T, E>(sX + (p0 + E) * C_::SX + j0, rows);
+        store_x_cols<T, P, N, Q, E + 1>(sX, rows, j0, p0);
+    }
+}
+
+// Stage a prefetched chunk into LDS: x^T always; natural B when outputs are
+// computed; B^T*w unless it is written later over natural B.  Tokens past L
+// are zeroed here.
+template <typename T, int P, int N, int Q, bool kOut>
+__device__ __forceinline__ void stage_chunk(const Prefetch<T, P, N, Q, kOut>& pf,
+                                            const ChunkMeta<Q>& m, T* sX, T* sB, T* sBw,
+                                            int64_t valid) {
+    using C_ = Cfg<T, P, N, Q>;
+    constexpr int kV = C_::kVec;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < C_::XPT; ++k) {
+        const int blk = tid + kThreads * k;
+        if (blk < C_::XB) {
+            const int j0 = (blk / C_::CBX) * 4, p0 = (blk % C_::CBX) * kV;
+            uint4 rows[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rows[r] = raw_keep(j0 + r < valid, pf.xr[k][r]);
+            store_x_cols<T, P, N, Q>(sX, rows, j0, p0);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < C_::BPT; ++k) {
+        const int blk = tid + kThreads * k;
+        if (blk < C_::BBK) {
+            const int j0 = (blk / C_::CBB) * 4, n0 = (blk % C_::CBB) * kV;
+            uint4 rows[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rows[r] = raw_keep(j0 + r < valid, pf.br[k][r]);
+            if constexpr (kOut) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<uint4*>(sB + (j0 + r) * C_::SB + n0) = rows[r];
+            }
+            if constexpr (!kOut || !C_::kInPlace) store_bw_block<T, P, N, Q>(sBw, rows, m, j0, n0);
+        }
+    }
+}
+
+// Chunk-state MFMA:  hreg[m][pb] += sum_j Bw^T[n][j] x[j][p]  (n-block wave + 8m)
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void chunk_state_mma(StateRegs<T, P, N, Q>& hreg, const T* sBw,
+                                                const T* sX, int wave, int lane) {
     using C_ = Cfg<T, P, N, Q>;
     const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < C_::KQ; ++s) {
-        Frag<T> xb[C_::PB];
+    for (int m = 0; m < C_::MT; ++m) {
+        const int nb = wave + kWaves * m;
+        if (nb < C_::NNB) {
 #pragma unroll
-        for (int pb = 0; pb < C_::PB; ++pb)
-            xb[pb] = frag_load8(sX + (16 * pb + r16) * C_::SX + 32 * s + 8 * q);
-#pragma unroll
-        for (int m = 0; m < C_::MT; ++m) {
-            const int nb = wave + 4 * m;
-            if (nb < C_::NNB) {
+            for (int s = 0; s < C_::KQ; ++s) {
                 const Frag<T> af = frag_load8(sBw + (16 * nb + r16) * C_::SBW + 32 * s + 8 * q);
 #pragma unroll
-                for (int pb = 0; pb < C_::PB; ++pb) mma(hreg.v[m][pb], af, xb[pb]);
+                for (int pb = 0; pb < C_::PB; ++pb) {
+                    const Frag<T> xb = frag_load8(sX + (16 * pb + r16) * C_::SX + 32 * s + 8 * q);
+                    mma(hreg.v[m][pb], af, xb);
+                }
             }
         }
     }
 }
 
-// h_c = [no reset] exp(cs_last) h_{c-1} (+ S_c, accumulated afterwards); select, not multiply.
+// h_c = [no reset] exp(cs_last) h_{c-1} (+ S_c afterwards); select, not multiply.
 template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void decay_state(StateRegs<T, P, N, Q>& hreg,
-                                            bool keep, float e) {
+__device__ __forceinline__ void decay_state(StateRegs<T, P, N, Q>& hreg, bool keep, float e) {
     using C_ = Cfg<T, P, N, Q>;
 #pragma unroll
     for (int m = 0; m < C_::MT; ++m)
@@ -279,7 +435,7 @@ __device__ __forceinline__ void state_load(StateRegs<T, P, N, Q>& hreg,
     const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int m = 0; m < C_::MT; ++m) {
-        const int nb = wave + 4 * m;
+        const int nb = wave + kWaves * m;
 #pragma unroll
         for (int pb = 0; pb < C_::PB; ++pb) {
             if (nb < C_::NNB && src) {
@@ -300,7 +456,7 @@ __device__ __forceinline__ void state_store(const StateRegs<T, P, N, Q>& hreg,
     const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int m = 0; m < C_::MT; ++m) {
-        const int nb = wave + 4 * m;
+        const int nb = wave + kWaves * m;
         if (nb < C_::NNB) {
 #pragma unroll
             for (int pb = 0; pb < C_::PB; ++pb) {
@@ -314,102 +470,270 @@ __device__ __forceinline__ void state_store(const StateRegs<T, P, N, Q>& hreg,
 
 // Register state -> operand copy in LDS, sH[p][n] in the io type.
 template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void state_to_lds(const StateRegs<T, P, N, Q>& hreg,
-                                             T* sH, int wave, int lane) {
+__device__ __forceinline__ void state_to_lds(const StateRegs<T, P, N, Q>& hreg, T* sH, int wave,
+                                             int lane) {
     using C_ = Cfg<T, P, N, Q>;
     const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int m = 0; m < C_::MT; ++m) {
-        const int nb = wave + 4 * m;
+        const int nb = wave + kWaves * m;
         if (nb < C_::NNB) {
 #pragma unroll
             for (int pb = 0; pb < C_::PB; ++pb) {
-                Vec4<T> v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v.v[i] = Io<T>::from_f32(hreg.v[m][pb][i]);
-                store4(sH + (16 * pb + r16) * C_::SH + 16 * nb + 4 * q, v);
+                const f32x4_t v = hreg.v[m][pb];
+                store4_f32(sH + (16 * pb + r16) * C_::SH + 16 * nb + 4 * q, v[0], v[1], v[2], v[3]);
             }
         }
     }
 }
 
-// Decode the (row, segment, group, head-in-group) of this workgroup.
-struct WorkItem {
-    int64_t b;
-    int seg, h, g;
-};
-__device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
-    const int64_t nblocks = static_cast<int64_t>(gridDim.x);
-    int64_t w = xcd_work_index(blockIdx.x, nblocks);
-    const int hpg = a.H / a.G;
-    WorkItem it;
-    const int hh = static_cast<int>(w % hpg);
-    w /= hpg;
-    it.g = static_cast<int>(w % a.G);
-    w /= a.G;
-    it.seg = static_cast<int>(w % nseg_grid);
-    it.b = w / nseg_grid;
-    it.h = it.g * hpg + hh;
-    return it;
-}
-
-// ===========================================================================
-// K2: chunk states of segments 0 .. nseg-2, chained inside the segment.
-// grid = batch * (nseg-1) * H, 256 threads.
+// Outputs of the wave's row blocks of one chunk:
+//   y^T[p][i] = exp(cs_i) [seq_i = seq_prev] sum_n h[p][n] C_i[n]
+//             + sum_{j <= i} x^T[p][j] G[i][j] + D x[i][p],
+//   G[i][j]   = (C_i . B_j) exp(cs_i - cs_j) dt_j [seq_j = seq_i].
+// C.B^T tiles come out of the MFMA with lane (r16, q) holding
+// C_i . B_{16J+4q+r} for i = 16I + r16, which is exactly an operand fragment
+// with k = j (two runs of four), so G never goes through LDS.
 template <typename T, int P, int N, int Q>
-__global__ __launch_bounds__(256) void chunk_state_kernel(ScanArgs a) {
+__device__ __forceinline__ void chunk_outputs(
+    const ChunkMeta<Q>& m, const RawFrag<T> (&cfp)[Cfg<T, P, N, Q>::RBC][Cfg<T, P, N, Q>::KN],
+    const T* sB, const T* sX, const T* sH, const ScanArgs& a, const WorkItem& it, int c,
+    float Dh, int wave, int lane) {
     using C_ = Cfg<T, P, N, Q>;
-    __shared__ __attribute__((aligned(16))) T sBw[N * C_::SBW];
-    __shared__ __attribute__((aligned(16))) T sX[P * C_::SX];
-    __shared__ __attribute__((aligned(16))) ChunkMeta<Q> meta;
-    const WorkItem it = decode_work(a, a.nseg - 1);
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const T* __restrict__ x = static_cast<const T*>(a.x);
-    const T* __restrict__ Bp = static_cast<const T*>(a.B);
-    StateRegs<T, P, N, Q> hreg;
-    state_load<T, P, N, Q>(hreg, nullptr, wave, lane);
-    float mult = 1.0f;
-    const int c_begin = it.seg * a.cps;
-    const int c_end = min(c_begin + a.cps, a.nc);
-    for (int c = c_begin; c < c_end; ++c) {
-        load_chunk_meta<Q>(meta, a, it.b, it.h, c);
-        const int seq_prev = prev_last_seq(a, it.b, c, Q);
-        __syncthreads();
-        const float cs_last = meta.cs[Q - 1];
-        const int seq_last = meta.seq[Q - 1];
-        stage_x_transposed<T, P, N, Q>(sX, x, a, it.b, it.h, c);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t t0 = static_cast<int64_t>(c) * Q;
+    T* __restrict__ y = static_cast<T*>(a.y);
+    const bool has_seq = a.seq_idx != nullptr;
+#pragma unroll 1
+    for (int rb = 0; rb < C_::RB; ++rb) {
+        const int I = row_block<C_::NB>(wave, rb);
+        if (C_::NB < 8 && wave >= C_::NB) continue;
+        const int i = 16 * I + r16;
+        const int64_t ti = t0 + i;
+        Frag<T> cf[C_::KN];
         {
-            constexpr int kV = C_::kVec;
-            constexpr int CB = N / kV;
-            constexpr int NBLK = (Q / 4) * CB;
-            const int64_t t0 = static_cast<int64_t>(c) * Q;
-            for (int blk = threadIdx.x; blk < NBLK; blk += 256) {
-                const int j0 = (blk / CB) * 4, n0 = (blk % CB) * kV;
-                Vec16<T> rows[4];
+            RawFrag<T> raw[C_::KN];
+            if constexpr (C_::kPrefetchC) {
+#pragma unroll
+                for (int s = 0; s < C_::KN; ++s) raw[s] = cfp[rb][s];
+            } else {
+                load_c_frags<T, P, N, Q>(raw, a, it, c, rb, wave, lane);
+            }
+#pragma unroll
+            for (int s = 0; s < C_::KN; ++s)
+                cf[s] = frag_from_raw(raw[s], c_frag_keep<T, P, N, Q>(a, c, rb, s, wave, lane));
+        }
+        f32x4_t acc[C_::PB];
+#pragma unroll
+        for (int pb = 0; pb < C_::PB; ++pb) acc[pb] = acc_zero();
+#pragma unroll
+        for (int s = 0; s < C_::KN; ++s)
+#pragma unroll
+            for (int pb = 0; pb < C_::PB; ++pb) {
+                const Frag<T> hf = frag_load8(sH + (16 * pb + r16) * C_::SH + 32 * s + 8 * q);
+                mma(acc[pb], hf, cf[s]);
+            }
+        const float cs_i = m.cs[i];
+        const int seq_i = m.seq[i];
+        {
+            const bool keep = seq_i == m.seq_prev;
+            const float e = decay_exp(cs_i);
+#pragma unroll
+            for (int pb = 0; pb < C_::PB; ++pb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t t = t0 + j0 + r;
-                    rows[r] = (t < a.L) ? load16(Bp + ((it.b * a.L + t) * a.G + it.g) * N + n0)
-                                        : zero16<T>();
+                    const float v = acc[pb][r] * e;
+                    acc[pb][r] = keep ? v : 0.0f;
                 }
-                store_bw_block<T, P, N, Q>(sBw, rows, meta, j0, n0, cs_last, seq_last);
+        }
+        for (int u = 0; u <= I / 2; ++u) {
+            float g[8];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                const int J = 2 * u + hp;
+                if (J <= I) {
+                    f32x4_t t = acc_zero();
+#pragma unroll
+                    for (int s = 0; s < C_::KN; ++s) {
+                        const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
+                        mma(t, bf, cf[s]);
+                    }
+                    const int jb = 16 * J + 4 * q;
+                    const float4 csj = *reinterpret_cast<const float4*>(&m.cs[jb]);
+                    const float4 dtj = *reinterpret_cast<const float4*>(&m.dt[jb]);
+                    const float csv[4] = {csj.x, csj.y, csj.z, csj.w};
+                    const float dtv[4] = {dtj.x, dtj.y, dtj.z, dtj.w};
+                    int sqv[4] = {seq_i, seq_i, seq_i, seq_i};
+                    if (has_seq) {
+                        const int4 sqj = *reinterpret_cast<const int4*>(&m.seq[jb]);
+                        sqv[0] = sqj.x; sqv[1] = sqj.y; sqv[2] = sqj.z; sqv[3] = sqj.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool keep = (J < I || jb + r <= i) && (sqv[r] == seq_i);
+                        const float v = t[r] * decay_exp(keep ? cs_i - csv[r] : 0.0f) * dtv[r];
+                        g[4 * hp + r] = keep ? v : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) g[4 * hp + r] = 0.0f;
+                }
+            }
+            const Frag<T> gf = frag_from_f32<T>(g);
+#pragma unroll
+            for (int pb = 0; pb < C_::PB; ++pb) {
+                const T* row = sX + (16 * pb + r16) * C_::SX;
+                const Frag<T> xf = frag_load4x2(row + 32 * u + 4 * q, row + 32 * u + 16 + 4 * q);
+                mma(acc[pb], xf, gf);
             }
         }
-        __syncthreads();
-        const bool keep = seq_last == seq_prev;
-        const float e = decay_exp(cs_last);
-        decay_state<T, P, N, Q>(hreg, keep, e);
-        mult = keep ? mult * e : 0.0f;
-        chunk_state_mma<T, P, N, Q>(hreg, sBw, sX, wave, lane);
-        __syncthreads();
+        if (ti < a.L) {
+#pragma unroll
+            for (int pb = 0; pb < C_::PB; ++pb) {
+                float o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float xv = Io<T>::to_f32(sX[(16 * pb + 4 * q + r) * C_::SX + i]);
+                    o[r] = acc[pb][r] + Dh * xv;
+                }
+                store4_f32(y + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q, o[0], o[1],
+                           o[2], o[3]);
+            }
+        }
     }
-    const int64_t slot = (it.b * a.H + it.h) * a.nseg + it.seg;
-    state_store<T, P, N, Q>(hreg, a.seg_state + slot * P * N, wave, lane);
-    if (threadIdx.x == 0) a.seg_mult[slot] = mult;
 }
 
 // ===========================================================================
-// K3: fp32 pass over segments.  grid (ceil(P*N/1024), batch*H), 256 threads,
+// The chunked scan over one (row, head, segment):
+//   kOut = false: chunk states of segments 0 .. nseg-2, written to the
+//                 workspace with each segment's decay multiplier;
+//   kOut = true:  outputs of every segment, starting from the segment's
+//                 incoming state; final states from the last segment.
+template <typename T, int P, int N, int Q, bool kOut>
+__global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
+    using C_ = Cfg<T, P, N, Q>;
+    constexpr bool kSepBw = !kOut || !C_::kInPlace;
+    __shared__ __attribute__((aligned(16))) T sB[kOut ? C_::B_ELEMS : 1];
+    __shared__ __attribute__((aligned(16))) T sBwBuf[kSepBw ? N * C_::SBW : 1];
+    __shared__ __attribute__((aligned(16))) T sX[P * C_::SX];
+    __shared__ __attribute__((aligned(16))) T sH[kOut ? P * C_::SH : 1];
+    __shared__ __attribute__((aligned(16))) ChunkMeta<Q> meta[2];
+    T* sBw = kSepBw ? sBwBuf : sB;
+
+    const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t bh = it.b * a.H + it.h;
+    const float Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
+    const int c_begin = it.seg * a.cps;
+    const int c_end = min(c_begin + a.cps, a.nc);
+    const bool last_seg = kOut && it.seg == a.nseg - 1;
+
+    StateRegs<T, P, N, Q> hreg;
+    if constexpr (kOut) {
+        if (a.nseg == 1)
+            state_load<T, P, N, Q>(hreg, a.init ? a.init + bh * P * N : nullptr, wave, lane);
+        else
+            state_load<T, P, N, Q>(hreg, a.seg_state + (bh * a.nseg + it.seg) * P * N, wave,
+                                   lane);
+        if (C_::NP > N) {  // zero the operand padding columns [N, NP) once
+            constexpr int W = C_::NP - N;
+            for (int idx = threadIdx.x; idx < P * W; idx += kThreads)
+                sH[(idx / W) * C_::SH + N + idx % W] = Io<T>::from_f32(0.0f);
+            for (int idx = threadIdx.x; idx < Q * W; idx += kThreads)
+                sB[(idx / W) * C_::SB + N + idx % W] = Io<T>::from_f32(0.0f);
+        }
+        state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
+    } else {
+        state_load<T, P, N, Q>(hreg, nullptr, wave, lane);
+    }
+    float mult = 1.0f;
+
+    Prefetch<T, P, N, Q, kOut> pf;
+    prefetch_chunk<T, P, N, Q, kOut>(pf, a, it, c_begin, wave, lane);
+    if (wave == 0) chunk_meta_scan<T, P, N, Q, kOut>(meta[0], pf, a, it.h, c_begin, lane);
+    __syncthreads();
+    stage_chunk<T, P, N, Q, kOut>(pf, meta[0], sX, sB, sBw,
+                                  a.L - static_cast<int64_t>(c_begin) * Q);
+    RawFrag<T> cf[kOut ? C_::RBC : 1][C_::KN];
+    if constexpr (kOut && C_::kPrefetchC) {
+#pragma unroll
+        for (int r = 0; r < C_::RBC; ++r)
+#pragma unroll
+            for (int s = 0; s < C_::KN; ++s) cf[r][s] = pf.cf[r][s];
+    }
+    __syncthreads();
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int cur = (c - c_begin) & 1;
+        const bool has_next = c + 1 < c_end;
+        const ChunkMeta<Q>& m = meta[cur];
+        if (has_next) prefetch_chunk<T, P, N, Q, kOut>(pf, a, it, c + 1, wave, lane);
+        const bool need_state = !kOut || has_next || (last_seg && a.final_states);
+        if constexpr (kOut) {
+            chunk_outputs<T, P, N, Q>(m, cf, sB, sX, sH, a, it, c, Dh, wave, lane);
+            if constexpr (!kSepBw) {
+                // natural B is dead after the outputs: rewrite it as B^T*w in place
+                __syncthreads();
+                if (need_state) {
+                    uint4 rows[C_::BPT][4];
+#pragma unroll
+                    for (int k = 0; k < C_::BPT; ++k) {
+                        const int blk = threadIdx.x + kThreads * k;
+                        if (blk < C_::BBK) {
+                            const int j0 = (blk / C_::CBB) * 4, n0 = (blk % C_::CBB) * C_::kVec;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                rows[k][r] = ld_raw16(sB + (j0 + r) * C_::SB + n0);
+                        }
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int k = 0; k < C_::BPT; ++k) {
+                        const int blk = threadIdx.x + kThreads * k;
+                        if (blk < C_::BBK) {
+                            const int j0 = (blk / C_::CBB) * 4, n0 = (blk % C_::CBB) * C_::kVec;
+                            store_bw_block<T, P, N, Q>(sBw, rows[k], m, j0, n0);
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (need_state) {
+            const bool keep = m.seq[Q - 1] == m.seq_prev;
+            const float e = decay_exp(m.cs[Q - 1]);
+            decay_state<T, P, N, Q>(hreg, keep, e);
+            mult = keep ? mult * e : 0.0f;
+            chunk_state_mma<T, P, N, Q>(hreg, sBw, sX, wave, lane);
+        }
+        if (has_next && wave == 0)
+            chunk_meta_scan<T, P, N, Q, kOut>(meta[cur ^ 1], pf, a, it.h, c + 1, lane);
+        __syncthreads();  // every read of this chunk's LDS tiles is done
+        if (has_next) {
+            if constexpr (kOut) state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
+            stage_chunk<T, P, N, Q, kOut>(pf, meta[cur ^ 1], sX, sB, sBw,
+                                          a.L - static_cast<int64_t>(c + 1) * Q);
+            if constexpr (kOut && C_::kPrefetchC) {
+#pragma unroll
+                for (int r = 0; r < C_::RBC; ++r)
+#pragma unroll
+                    for (int s = 0; s < C_::KN; ++s) cf[r][s] = pf.cf[r][s];
+            }
+            __syncthreads();
+        }
+    }
+    if constexpr (kOut) {
+        if (last_seg && a.final_states)
+            state_store<T, P, N, Q>(hreg, a.final_states + bh * P * N, wave, lane);
+    } else {
+        const int64_t slot = bh * a.nseg + it.seg;
+        state_store<T, P, N, Q>(hreg, a.seg_state + slot * P * N, wave, lane);
+        if (threadIdx.x == 0) a.seg_mult[slot] = mult;
+    }
+}
+
+// ===========================================================================
+// fp32 pass over segments.  grid (ceil(P*N/1024), batch*H), 256 threads,
 // four state elements per thread.  In place: slot s holds segment s's end
 // state on entry and its incoming state on exit.
 __global__ __launch_bounds__(256) void state_pass_kernel(PassArgs a) {
@@ -447,199 +771,7 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
 }
 
 // ===========================================================================
-// K4: chunk outputs with the state carried in registers.
-// grid = batch * nseg * H, 256 threads.
-template <typename T, int P, int N, int Q>
-__global__ __launch_bounds__(256) void chunk_output_kernel(ScanArgs a) {
-    using C_ = Cfg<T, P, N, Q>;
-    __shared__ __attribute__((aligned(16))) T sB[C_::B_ELEMS];  // natural B, then B^T*w
-    __shared__ __attribute__((aligned(16))) T sX[P * C_::SX];
-    __shared__ __attribute__((aligned(16))) T sH[P * C_::SH];
-    __shared__ __attribute__((aligned(16))) ChunkMeta<Q> meta;
-    const WorkItem it = decode_work(a, a.nseg);
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int r16 = lane & 15, q = lane >> 4;
-    const T* __restrict__ x = static_cast<const T*>(a.x);
-    const T* __restrict__ Bp = static_cast<const T*>(a.B);
-    const T* __restrict__ Cp = static_cast<const T*>(a.C);
-    T* __restrict__ y = static_cast<T*>(a.y);
-    const float Dh = a.D ? a.D[it.h] : 0.0f;
-    const int64_t bh = it.b * a.H + it.h;
-
-    StateRegs<T, P, N, Q> hreg;
-    if (a.nseg == 1)
-        state_load<T, P, N, Q>(hreg, a.init ? a.init + bh * P * N : nullptr, wave, lane);
-    else
-        state_load<T, P, N, Q>(hreg, a.seg_state + (bh * a.nseg + it.seg) * P * N, wave, lane);
-    if (C_::NP > N) {  // zero the operand padding columns once
-        for (int idx = threadIdx.x; idx < P * (C_::NP - N); idx += 256)
-            sH[(idx / (C_::NP - N)) * C_::SH + N + idx % (C_::NP - N)] = Io<T>::from_f32(0.0f);
-    }
-    state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
-
-    const int c_begin = it.seg * a.cps;
-    const int c_end = min(c_begin + a.cps, a.nc);
-    const bool last_seg = it.seg == a.nseg - 1;
-    for (int c = c_begin; c < c_end; ++c) {
-        const int64_t t0 = static_cast<int64_t>(c) * Q;
-        load_chunk_meta<Q>(meta, a, it.b, it.h, c);
-        const int seq_prev = prev_last_seq(a, it.b, c, Q);
-        // natural B tile -> sB[j][n] (n >= N zero-filled)
-        {
-            constexpr int kV = C_::kVec;
-            constexpr int CPR = C_::NP / kV;
-            for (int li = threadIdx.x; li < Q * CPR; li += 256) {
-                const int j = li / CPR, n0 = (li % CPR) * kV;
-                const int64_t t = t0 + j;
-                Vec16<T> v = zero16<T>();
-                if (t < a.L && n0 < N) v = load16(Bp + ((it.b * a.L + t) * a.G + it.g) * N + n0);
-                store16(sB + j * C_::SB + n0, v);
-            }
-        }
-        stage_x_transposed<T, P, N, Q>(sX, x, a, it.b, it.h, c);
-        __syncthreads();
-
-        // ---- outputs: wave owns row-block pairs (k, NB-1-k), k = wave, wave+4, ...
-        for (int pk = wave; pk < C_::NB / 2; pk += 4) {
-#pragma unroll 1
-            for (int half = 0; half < 2; ++half) {
-                const int I = half == 0 ? pk : C_::NB - 1 - pk;
-                const int i = 16 * I + r16;  // this lane's token inside the chunk
-                const int64_t ti = t0 + i;
-                // C_i fragments (operand for C.B^T and for C.h)
-                Frag<T> cf[C_::KN];
-#pragma unroll
-                for (int s = 0; s < C_::KN; ++s) {
-                    const int n0 = 32 * s + 8 * q;
-                    if (ti < a.L && n0 < N)
-                        cf[s] = frag_load8(Cp + ((it.b * a.L + ti) * a.G + it.g) * N + n0);
-                    else
-                        cf[s] = frag_zero<T>();
-                }
-                f32x4_t acc[C_::PB];
-#pragma unroll
-                for (int pb = 0; pb < C_::PB; ++pb) acc[pb] = acc_zero();
-                // carried state: y^T[p][i] = sum_n h[p][n] C_i[n]
-#pragma unroll
-                for (int s = 0; s < C_::KN; ++s)
-#pragma unroll
-                    for (int pb = 0; pb < C_::PB; ++pb) {
-                        const Frag<T> hf = frag_load8(sH + (16 * pb + r16) * C_::SH + 32 * s + 8 * q);
-                        mma(acc[pb], hf, cf[s]);
-                    }
-                const float cs_i = meta.cs[i];
-                const int seq_i = meta.seq[i];
-                {
-                    const bool keep = seq_i == seq_prev;
-                    const float e = decay_exp(cs_i);
-#pragma unroll
-                    for (int pb = 0; pb < C_::PB; ++pb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float v = acc[pb][r] * e;
-                            acc[pb][r] = keep ? v : 0.0f;
-                        }
-                }
-                // intra-chunk: y^T[p][i] += sum_{j<=i} x^T[p][j] G[i][j],
-                // G[i][j] = (C_i . B_j) exp(cs_i - cs_j) dt_j [same sequence]
-                for (int u = 0; u <= I / 2; ++u) {
-                    const int J0 = 2 * u, J1 = 2 * u + 1;
-                    float g[8];
-#pragma unroll
-                    for (int hp = 0; hp < 2; ++hp) {
-                        const int J = hp == 0 ? J0 : J1;
-                        if (J <= I) {
-                            f32x4_t t = acc_zero();  // t[r] = C_i . B_{16J+4q+r}
-#pragma unroll
-                            for (int s = 0; s < C_::KN; ++s) {
-                                const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
-                                mma(t, bf, cf[s]);
-                            }
-                            const int jb = 16 * J + 4 * q;
-                            const float4 csj = *reinterpret_cast<const float4*>(&meta.cs[jb]);
-                            const float4 dtj = *reinterpret_cast<const float4*>(&meta.dt[jb]);
-                            const int4 sqj = *reinterpret_cast<const int4*>(&meta.seq[jb]);
-                            const float csv[4] = {csj.x, csj.y, csj.z, csj.w};
-                            const float dtv[4] = {dtj.x, dtj.y, dtj.z, dtj.w};
-                            const int sqv[4] = {sqj.x, sqj.y, sqj.z, sqj.w};
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const bool keep = (jb + r <= i) && (sqv[r] == seq_i);
-                                const float v = t[r] * decay_exp(keep ? cs_i - csv[r] : 0.0f) * dtv[r];
-                                g[4 * hp + r] = keep ? v : 0.0f;
-                            }
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) g[4 * hp + r] = 0.0f;
-                        }
-                    }
-                    const Frag<T> gf = frag_from_f32<T>(g);
-#pragma unroll
-                    for (int pb = 0; pb < C_::PB; ++pb) {
-                        const T* row = sX + (16 * pb + r16) * C_::SX;
-                        const Frag<T> xf = frag_load4x2(row + 16 * J0 + 4 * q, row + 16 * J1 + 4 * q);
-                        mma(acc[pb], xf, gf);
-                    }
-                }
-                // D skip and store: lane holds y[i][16pb + 4q + r]
-                if (ti < a.L) {
-#pragma unroll
-                    for (int pb = 0; pb < C_::PB; ++pb) {
-                        Vec4<T> out;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float xv = Io<T>::to_f32(sX[(16 * pb + 4 * q + r) * C_::SX + i]);
-                            out.v[r] = Io<T>::from_f32(acc[pb][r] + Dh * xv);
-                        }
-                        store4(y + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q, out);
-                    }
-                }
-            }
-        }
-
-        const bool need_state = (c + 1 < c_end) || (last_seg && a.final_states);
-        __syncthreads();  // all reads of sB (natural) and sH are done
-        if (need_state) {
-            const float cs_last = meta.cs[Q - 1];
-            const int seq_last = meta.seq[Q - 1];
-            // natural B -> B^T * w, in place: read every block, then write
-            constexpr int kV = C_::kVec;
-            constexpr int CB = N / kV;
-            constexpr int NBLK = (Q / 4) * CB;
-            constexpr int PER = (NBLK + 255) / 256;
-            Vec16<T> rows[PER][4];
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int blk = threadIdx.x + 256 * k;
-                if (blk < NBLK) {
-                    const int j0 = (blk / CB) * 4, n0 = (blk % CB) * kV;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) rows[k][r] = load16(sB + (j0 + r) * C_::SB + n0);
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int blk = threadIdx.x + 256 * k;
-                if (blk < NBLK) {
-                    const int j0 = (blk / CB) * 4, n0 = (blk % CB) * kV;
-                    store_bw_block<T, P, N, Q>(sB, rows[k], meta, j0, n0, cs_last, seq_last);
-                }
-            }
-            __syncthreads();
-            const bool keep = seq_last == seq_prev;
-            decay_state<T, P, N, Q>(hreg, keep, decay_exp(cs_last));
-            chunk_state_mma<T, P, N, Q>(hreg, sB, sX, wave, lane);
-            state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
-        }
-        __syncthreads();
-    }
-    if (last_seg && a.final_states)
-        state_store<T, P, N, Q>(hreg, a.final_states + bh * P * N, wave, lane);
-}
-
-// ===========================================================================
-// K5: one decode token.  grid = batch*H, 256 threads; N/4 lanes per state row
+// One decode token.  grid = batch*H, 256 threads; N/4 lanes per state row
 // (one float4 each), 256/(N/4) rows per pass.  Uses the same dt transform and
 // decay functions as the chunked path.
 template <typename T, int N>
@@ -690,12 +822,6 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
 // ===========================================================================
 // Launchers.
 
-hipError_t launch_dt_cumsum(const DtArgs& a, int64_t batch, int nc, hipStream_t st) {
-    dim3 grid(nc, (a.H + 15) / 16, static_cast<unsigned>(batch));
-    hipLaunchKernelGGL(dt_cumsum_kernel, grid, dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st) {
     dim3 grid(static_cast<unsigned>((a.PN / 4 + 255) / 256), static_cast<unsigned>(bh));
     hipLaunchKernelGGL(state_pass_kernel, grid, dim3(256), 0, st, a);
@@ -709,17 +835,10 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
     return hipGetLastError();
 }
 
-template <typename T, int P, int N, int Q>
-static hipError_t launch_chunk_state_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((chunk_state_kernel<T, P, N, Q>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
-template <typename T, int P, int N, int Q>
-static hipError_t launch_chunk_output_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((chunk_output_kernel<T, P, N, Q>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(256), 0, st, a);
+template <typename T, int P, int N, int Q, bool kOut>
+static hipError_t launch_chunk_scan_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
+    hipLaunchKernelGGL((chunk_scan_kernel<T, P, N, Q, kOut>),
+                       dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -731,8 +850,9 @@ static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipS
 }
 
 // The compiled (io, P, N, Q) set of the chunked scan.
-#define SSD_SCAN_VARIANT(IO, T, P, N, Q) \
-    {IO, P, N, Q, &launch_chunk_state_t<T, P, N, Q>, &launch_chunk_output_t<T, P, N, Q>},
+#define SSD_SCAN_VARIANT(IO, T, P, N, Q)                   \
+    {IO, P, N, Q, &launch_chunk_scan_t<T, P, N, Q, false>, \
+     &launch_chunk_scan_t<T, P, N, Q, true>},
 
 static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 16, 16, 32)
@@ -753,7 +873,9 @@ const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q) {
     return nullptr;
 }
 
-int scan_variant_count() { return static_cast<int>(sizeof(kScanVariants) / sizeof(kScanVariants[0])); }
+int scan_variant_count() {
+    return static_cast<int>(sizeof(kScanVariants) / sizeof(kScanVariants[0]));
+}
 
 const ScanVariant* scan_variant_at(int i) { return &kScanVariants[i]; }
 

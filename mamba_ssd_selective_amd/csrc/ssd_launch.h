@@ -7,35 +7,24 @@
 
 namespace ssd {
 
-// K1 arguments.
-struct DtArgs {
-    const float* dt_raw;    // (b, L, H)
-    const float* dt_bias;   // (H) or null
-    const float* A;         // (H)
-    const int32_t* seq_idx; // (b, L) or null
-    int softplus;
-    float dt_min, dt_max;
-    int64_t L, Lp;          // tokens, tokens padded to whole chunks
-    int H, Q;
-    float* dtv;             // (b, H, Lp) transformed dt
-    float* cs;              // (b, H, Lp) segmented chunk cumsum of dt*A
-};
-
-// K2 / K4 arguments.
+// K2 / K4 arguments (the dt transform and chunk cumsum run inside them).
 struct ScanArgs {
     const void* x;          // (b, L, H, P)
     const void* B;          // (b, L, G, N)
     const void* C;          // (b, L, G, N)
     void* y;                // (b, L, H, P)
-    const float* dtv;       // (b, H, Lp)
-    const float* cs;        // (b, H, Lp)
+    const float* dt_raw;    // (b, L, H)
+    const float* dt_bias;   // (H) or null
+    const float* A;         // (H)
+    int softplus;
+    float dt_min, dt_max;
     const int32_t* seq_idx; // (b, L) or null
     const float* D;         // (H) or null
     const float* init;      // (b, H, P, N) or null
     float* final_states;    // (b, H, P, N) or null
     float* seg_state;       // (b, H, nseg, P, N) workspace
     float* seg_mult;        // (b, H, nseg) workspace
-    int64_t L, Lp;
+    int64_t L;
     int H, G;
     int nc, nseg, cps;      // chunks, segments, chunks per segment
 };
@@ -78,7 +67,6 @@ const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q);
 int scan_variant_count();
 const ScanVariant* scan_variant_at(int i);
 
-hipError_t launch_dt_cumsum(const DtArgs& a, int64_t batch, int nc, hipStream_t st);
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);
 hipError_t launch_state_update(int io, int64_t N, const StepArgs& a, int64_t nblocks,

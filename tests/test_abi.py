@@ -54,15 +54,15 @@ def test_supported_set(lib):
 def test_workspace_and_segments(lib):
     # config 1: 64 heads, 64 chunks of 128 -> 8 segments of 8 chunks
     ws = ssd.workspace_bytes(1, 8192, 64, 64, 128, 8, 128)
-    dt_cs = 2 * 64 * 8192 * 4
+    # segment states (fp32 P x N per row, head, segment) + segment multipliers
     seg = 64 * 8 * 64 * 128 * 4 + 256 * math.ceil(64 * 8 * 4 / 256)
-    assert ws == dt_cs + seg
+    assert ws == seg
     assert ssd.segments(1, 8192, 64, 64, 128, 8, 128) == 8
-    # enough rows x heads: one segment, no segment scratch
+    # enough rows x heads: one segment, no scratch at all
     assert ssd.segments(64, 4096, 64, 64, 128, 8, 128) == 1
-    assert ssd.workspace_bytes(64, 4096, 64, 64, 128, 8, 128) == 2 * 64 * 64 * 4096 * 4
-    # ragged L pads to whole chunks
-    assert ssd.workspace_bytes(1, 300, 64, 64, 128, 8, 128) >= 2 * 64 * 384 * 4
+    assert ssd.workspace_bytes(64, 4096, 64, 64, 128, 8, 128) == 0
+    # ragged L: 3 chunks, one segment each
+    assert ssd.segments(1, 300, 64, 64, 128, 8, 128) == 3
     assert ssd.workspace_bytes(1, 0, 64, 64, 128, 8, 128) == 0
     assert ssd.workspace_bytes(1, 128, 64, 48, 128, 8, 128) == 0  # unsupported
 
@@ -103,9 +103,10 @@ def test_scan_rejects_bad_arguments(lib):
     assert _scan_call(lib, x=None) == NULL_ARG
     assert _scan_call(lib, A=None) == NULL_ARG
     assert _scan_call(lib, y=None) == NULL_ARG
-    assert _scan_call(lib, ws=None) == WORKSPACE
-    assert _scan_call(lib, ws_bytes=16) == WORKSPACE
-    assert _scan_call(lib, ws=0x70000010) == WORKSPACE  # not 256-byte aligned
+    assert _scan_call(lib, dims=(1, 1024, 4, 16, 16, 1, 64), ws=None) == WORKSPACE
+    assert _scan_call(lib, dims=(1, 1024, 4, 16, 16, 1, 64), ws_bytes=16) == WORKSPACE
+    # not 256-byte aligned
+    assert _scan_call(lib, dims=(1, 1024, 4, 16, 16, 1, 64), ws=0x70000010) == WORKSPACE
     assert _scan_call(lib, lo=1.0, hi=0.5) == BAD_ARG
     assert _scan_call(lib, lo=float("nan")) == BAD_ARG
     assert _scan_call(lib, x=0x70000004) == BAD_ARG  # not 16-byte aligned
@@ -118,7 +119,7 @@ def test_scan_rejects_aliasing(lib):
     st = buf()
     assert _scan_call(lib, init=st, final=st + 256) == ALIAS  # partial overlap
     w = buf()
-    assert _scan_call(lib, ws=w, y=w) == ALIAS
+    assert _scan_call(lib, dims=(1, 1024, 4, 16, 16, 1, 64), ws=w, y=w) == ALIAS
     assert _scan_call(lib, final=x) == ALIAS
 
 
