@@ -4,7 +4,7 @@
 One step = one pass of the whole hot path over one batch of synthetic input:
 the chunked scan of the 30B-shaped prefill (b=1, L=8192, H=64, P=64, N=128,
 G=8, chunk 128, bf16 x/B/C, fp32 dt/A/D and state, final state returned;
-kernels chunk_state, state_pass, chunk_output) followed by one
+kernels chunk_prep, chunk_state, state_pass, chunk_output) followed by one
 decode token on the returned state (state_update).  Inputs are resident in
 HBM before timing starts; the step cycles over several copies of the inputs
 so that consecutive steps do not hit in the 256 MB MALL.
@@ -176,7 +176,7 @@ def main():
     ws = torch.empty(max(1, ssd.workspace_bytes(b, L, H, P, N, G, Q)), dtype=torch.uint8,
                      device=dev)
     nseg = ssd.segments(b, L, H, P, N, G, Q)
-    kernels = (["chunk_state", "state_pass"] if nseg > 1 else []) + ["chunk_output"]
+    kernels = ["chunk_prep"] + (["chunk_state", "state_pass"] if nseg > 1 else []) + ["chunk_output"]
     nk = len(kernels) + 1  # + state_update
     launched = ctypes.c_int(0)
 

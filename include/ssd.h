@@ -144,7 +144,7 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
  * launch, on the call's stream, for k < count/2, and stores the number of
  * kernels it launched in *launched (if not NULL).  `events` are hipEvent_t
  * handles the caller created; the library only records them.  Kernel order
- * of the scan: [chunk_state, state_pass,] chunk_output (the two bracketed
+ * of the scan: chunk_prep, [chunk_state, state_pass,] chunk_output (the two bracketed
  * kernels run only when ssd_chunk_scan_segments(...) > 1; L = 0 launches one
  * state copy).
  * Pass events = NULL to turn the hooks off. */

@@ -19,12 +19,13 @@ constexpr size_t kAlign = 256;
 struct Plan {
     int64_t nc = 0;
     int64_t nseg = 1, cps = 1;
+    size_t off_cs = 0, off_dtv = 0, off_wgt = 0, off_cbt = 0;
     size_t off_seg = 0, off_mult = 0, total = 0;
 };
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-Plan make_plan(const ssd_dims& d) {
+Plan make_plan(const ssd_dims& d, ssd_dtype io) {
     Plan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
     p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
@@ -35,7 +36,18 @@ Plan make_plan(const ssd_dims& d) {
     p.cps = (p.nc + nseg - 1) / nseg;
     p.nseg = (p.nc + p.cps - 1) / p.cps;
     const size_t f = sizeof(float);
+    const size_t es = io == SSD_BF16 ? 2 : 4;
+    const size_t meta = static_cast<size_t>(bh * p.nc * d.chunk_size) * f;
     size_t off = 0;
+    p.off_cs = off;
+    off = align_up(off + meta);
+    p.off_dtv = off;
+    off = align_up(off + meta);
+    p.off_wgt = off;
+    off = align_up(off + meta);
+    p.off_cbt = off;
+    off = align_up(off + static_cast<size_t>(d.batch * p.nc * d.ngroups) *
+                             static_cast<size_t>(ssd::cbt_elems_per_chunk_group(d.chunk_size)) * es);
     if (p.nseg > 1) {
         p.off_seg = off;
         off = align_up(off + static_cast<size_t>(bh * p.nseg * d.headdim * d.dstate) * f);
@@ -132,14 +144,14 @@ int ssd_chunk_scan_supported(ssd_dtype io, int64_t headdim, int64_t dstate, int6
 
 size_t ssd_chunk_scan_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
     if (check_scan_dims(d, io) != SSD_OK) return 0;
-    return make_plan(*d).total;
+    return make_plan(*d, io).total;
 }
 
 // Number of sequence segments the scan of these dims is split into (1 = the
 // state is carried through each whole row inside one workgroup).  Informational.
 int64_t ssd_chunk_scan_segments(const ssd_dims* d, ssd_dtype io) {
     if (check_scan_dims(d, io) != SSD_OK) return 0;
-    return make_plan(*d).nseg;
+    return make_plan(*d, io).nseg;
 }
 
 ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
@@ -155,7 +167,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
                   N = d->dstate, G = d->ngroups;
     const bool work = b > 0 && L > 0;
     if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
-    const Plan plan = make_plan(*d);
+    const Plan plan = make_plan(*d, io);
     if (plan.total > 0 &&
         (!workspace || workspace_bytes < plan.total ||
          (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
@@ -216,6 +228,10 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     sa.final_states = final_states;
     sa.seg_state = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_seg) : nullptr;
     sa.seg_mult = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_mult) : nullptr;
+    sa.cs = reinterpret_cast<float*>(wsb + plan.off_cs);
+    sa.dtv = reinterpret_cast<float*>(wsb + plan.off_dtv);
+    sa.wgt = reinterpret_cast<float*>(wsb + plan.off_wgt);
+    sa.cbt = wsb + plan.off_cbt;
     sa.L = L;
     sa.H = static_cast<int>(H);
     sa.G = static_cast<int>(G);
@@ -223,6 +239,9 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     sa.nseg = static_cast<int>(plan.nseg);
     sa.cps = static_cast<int>(plan.cps);
 
+    if (timed_launch(k, hs, [&] { return var->chunk_prep(sa, b * plan.nc * G, hs); }) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
     if (plan.nseg > 1) {
         if (timed_launch(k, hs, [&] {
                 return var->chunk_state(sa, b * (plan.nseg - 1) * H, hs);

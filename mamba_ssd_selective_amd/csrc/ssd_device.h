@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssd {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -142,6 +144,14 @@ __device__ __forceinline__ float raw_elem_f32(const uint4& v) {
     } else {
         return __uint_as_float(u4_at<E>(v));
     }
+}
+
+// Element E (< 4) of four packed bf16 values.
+template <typename T, int E>
+__device__ __forceinline__ float raw_elem_f32(const uint2& v) {
+    static_assert(sizeof(T) == 2, "uint2 holds four 16-bit elements");
+    const uint32_t d = E < 2 ? v.x : v.y;
+    return __uint_as_float((E % 2 == 0) ? (d << 16) : (d & 0xFFFF0000u));
 }
 
 // Two fp32 values -> packed bf16 pair (RNE), low half first.

@@ -14,27 +14,30 @@
 //           + [seq_i = seq of the previous chunk's last token] exp(cs_i) h_{c-1} . C_i
 //           + D x_i
 //
-// Kernels of one ssd_chunk_scan_fwd call (one process, one GPU), each
-// workgroup owning one (row, head, segment of consecutive chunks):
-//   chunk_scan_kernel<kOut = false>  "chunk state": per chunk, the dt transform
-//        and segmented chunk cumsum (wave-level scan), then S_c on bf16 MFMA from
-//        LDS-staged transposed B and x tiles, chained through the segment in
-//        registers; writes the segment's end state and decay multiplier.
-//   state_pass_kernel                fp32 pass over segments: each segment's
-//        incoming state (segment multipliers are wave-uniform scalars).
-//   chunk_scan_kernel<kOut = true>   "chunk output": the same per-chunk state
-//        chain plus the outputs: C.B^T masked-decay intra-chunk product, the
-//        C.h_prev carried-state term and the D skip, on MFMA.
-// The first two run only when the rows are cut into more than one segment
-// (few rows x heads); with one segment per row the state is carried through
-// the whole row inside one workgroup.
+// Kernels of one ssd_chunk_scan_fwd call (one process, one GPU):
+//   chunk_prep_kernel     one workgroup per (row, chunk, B/C group), all in
+//        parallel: the dt transform and segmented chunk cumsum of dt*A (wave-level
+//        scan) for the group's heads, the chunk-state weights
+//        w_j = exp(cs_last - cs_j) dt_j, and the lower-triangular C.B^T tiles of
+//        the chunk on MFMA (once per group instead of once per head), stored in
+//        the register layout the output kernel consumes them in.
+//   chunk_scan_kernel<kOut = false>  "chunk state", one workgroup per (row, head,
+//        segment of consecutive chunks) for all but the last segment: S_c on
+//        bf16 MFMA from LDS-staged transposed tiles (B^T scaled by w, x^T),
+//        chained through the segment in registers; writes the segment's end state
+//        and decay multiplier.
+//   state_pass_kernel     fp32 pass over segments: each segment's incoming state
+//        (the segment multipliers are wave-uniform scalars).
+//   chunk_scan_kernel<kOut = true>   "chunk output": the same state chain plus
+//        y = masked-decay (C.B^T) x, the C.h_prev carried-state term and D x.
+// With enough rows x heads there is one segment per row and only the prep and
+// output kernels run.
 // Decode:
-//   state_update_kernel              one token: coalesced in-place fp32 update.
+//   state_update_kernel   one token: coalesced in-place fp32 state update.
 //
-// Inside a workgroup (8 waves) the chunk loop is software-pipelined: the
-// global loads of chunk c+1 (x, B, C rows, raw dt, seq ids) are issued into
-// registers before chunk c's MFMA work, and wave 0 runs chunk c+1's dt scan
-// while the other waves finish chunk c; two barriers per chunk.
+// The chunk loop of the scan kernels (8 waves per workgroup) issues
+// the next chunk's global loads (x and B rows, chunk metadata) into registers
+// before the current chunk's MFMA work and stages them into LDS after it.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -43,8 +46,8 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 // Work-index mapping: consecutive workgroup ids are dealt round-robin to the
 // 8 XCDs of an MI355X, each with its own L2.  Remap so that one XCD receives a
-// contiguous range of work items (the heads sharing one B/C group and the same
-// chunks then share that XCD's L2).
+// contiguous range of work items (workgroups sharing B/C data then share that
+// XCD's L2).
 __device__ __forceinline__ int64_t xcd_work_index(int64_t bid, int64_t nblocks) {
     constexpr int kXcd = 8;
     if (nblocks % kXcd != 0) return bid;
@@ -53,7 +56,6 @@ __device__ __forceinline__ int64_t xcd_work_index(int64_t bid, int64_t nblocks) 
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kLdsBytes = 160 * 1024;
 
 // ===========================================================================
 // Tile configuration.
@@ -63,50 +65,41 @@ struct Cfg {
     static constexpr int kVec = Io<T>::kVec;
     static constexpr int NP = (N + 31) / 32 * 32;  // n padded to the MFMA k step
     static constexpr int PAD = kVec;               // 16 bytes of row padding in LDS
-    static constexpr int SB = NP + PAD;            // natural B rows   [Q][SB]
+    static constexpr int SB = NP + PAD;            // natural B / C rows (prep) [Q][SB]
     static constexpr int SBW = Q + PAD;            // B^T*w rows       [N][SBW]
     static constexpr int SX = Q + PAD;             // x^T rows         [P][SX]
     static constexpr int SH = NP + PAD;            // h (operand) rows [P][SH]
-    static constexpr int NB = Q / 16;              // 16-row output blocks
+    static constexpr int NB = Q / 16;              // 16-token blocks
+    static constexpr int NT = NB * (NB + 1) / 2;   // lower-triangular C.B^T tiles
     static constexpr int PB = P / 16;              // 16-column blocks of P
     static constexpr int NNB = N / 16;             // 16-row blocks of the state's n
     static constexpr int KN = NP / 32;             // k steps over n
     static constexpr int KQ = Q / 32;              // k steps over tokens
     static constexpr int MT = (NNB + kWaves - 1) / kWaves;  // state n-blocks per wave
     static constexpr int RB = NB >= 16 ? NB / 8 : 1;        // output row blocks per wave
-    // C fragments are prefetched a chunk ahead when a wave owns one row block;
-    // with two, they are loaded at the start of each row block (register budget).
-    static constexpr bool kPrefetchC = RB == 1;
-    static constexpr int RBC = kPrefetchC ? RB : 1;
     static constexpr int CBX = P / kVec, XB = (Q / 4) * CBX;  // x staging blocks
     static constexpr int CBB = N / kVec, BBK = (Q / 4) * CBB; // B staging blocks
     static constexpr int XPT = (XB + kThreads - 1) / kThreads;
     static constexpr int BPT = (BBK + kThreads - 1) / kThreads;
     static constexpr int E = (Q + kWave - 1) / kWave;       // tokens per lane in the dt scan
-    static constexpr int META = 3 * Q * 4 + 16;
-    static constexpr int LDS_SEPARATE =
-        (Q * SB + N * SBW + P * SX + P * SH) * static_cast<int>(sizeof(T)) + 2 * META;
-    // When natural B and B^T*w do not both fit, B^T*w is written over natural B
-    // after the outputs of the chunk are done.
-    static constexpr bool kInPlace = LDS_SEPARATE > kLdsBytes;
-    static constexpr int B_ELEMS =
-        kInPlace ? (Q * SB > N * SBW ? Q * SB : N * SBW) : Q * SB;
-    // the zero padding columns [N, NP) of natural B are written once per kernel
-    static_assert(!(kInPlace && NP > N), "in-place B^T*w would overwrite B's zero padding");
 };
 
 // Row block r (< RB) of wave w, chosen so that the two waves sharing a SIMD
-// (w and w+4) get equal triangular work.
+// (w and w+4) get equal triangular work: rows (k, NB-1-k) pair up.
 template <int NB>
 __device__ __forceinline__ int row_block(int wave, int r) {
     if constexpr (NB >= 16) {
-        const int k = wave + 8 * (r / 2);
+        const int k = wave + kWaves * (r / 2);
         return (r % 2 == 0) ? k : NB - 1 - k;
     } else if constexpr (NB == 8) {
         return wave < 4 ? wave : 11 - wave;
     } else {
         return wave;  // valid only for wave < NB
     }
+}
+template <int NB>
+__device__ __forceinline__ bool row_block_valid(int wave) {
+    return NB >= 8 || wave < NB;
 }
 
 // The fp32 state tiles a wave keeps in registers: n-block nb = wave + 8m,
@@ -116,36 +109,11 @@ struct StateRegs {
     f32x4_t v[Cfg<T, P, N, Q>::MT][Cfg<T, P, N, Q>::PB];
 };
 
-// Per-chunk token metadata in LDS: transformed dt, segmented cumsum of dt*A,
-// sequence ids (padded tokens repeat the last real token's id), and the id of
-// the token before the chunk (token 0 for the first chunk: the initial state
-// belongs to the sequence holding token 0).
-template <int Q>
-struct ChunkMeta {
-    float cs[Q];
-    float dt[Q];
-    int seq[Q];
-    int seq_prev;
-    int pad_[3];
-};
-
-// Global data of one chunk, held in registers between its prefetch and its
-// staging into LDS.
-template <typename T, int P, int N, int Q, bool kOut>
-struct Prefetch {
-    using C_ = Cfg<T, P, N, Q>;
-    uint4 xr[C_::XPT][4];                      // x rows (raw)
-    uint4 br[C_::BPT][4];                      // B rows (raw)
-    RawFrag<T> cf[kOut ? C_::RBC : 1][C_::KN]; // C fragments (raw)
-    float dt[C_::E];                           // raw dt (wave 0)
-    int seq[C_::E];                            // sequence ids (wave 0)
-    int seq_prev;
-};
-
 struct WorkItem {
     int64_t b;
     int seg, h, g;
 };
+// Work order (fastest first): head within its group, group, segment, row.
 __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
     const int64_t nblocks = static_cast<int64_t>(gridDim.x);
     int64_t w = xcd_work_index(blockIdx.x, nblocks);
@@ -161,47 +129,179 @@ __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid
     return it;
 }
 
-// C_i fragments of row block r of this wave (operand of C.B^T and C.h):
-// lane (r16, q) holds C[16I + r16][32s + 8q .. +7] for every k step s.  The
-// loads are unconditional (row and column clamped into the tensor); rows past
-// L and columns past N are zeroed where the fragments are used (c_frag_keep).
-template <typename T, int P, int N, int Q>
-using CRaw = RawFrag<T>[Cfg<T, P, N, Q>::KN];
+__device__ __forceinline__ int64_t meta_offset(const ScanArgs& a, int64_t b, int h, int c, int Q) {
+    return ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(Q);
+}
 
+// ===========================================================================
+// chunk_prep_kernel: one workgroup per (row, chunk, group), grid order
+// (group fastest, then chunk, then row).
+//  1. wave w handles heads w, w+8, ... of the group: dt transform, segmented
+//     inclusive cumsum of dt*A over the chunk (restarted at the chunk start and
+//     at every sequence change), weights w_j = [seq_j = seq_last]
+//     exp(cs_last - cs_j) dt_j; written to the cs / dtv / wgt workspaces.
+//  2. the chunk's B and C rows are staged in LDS; the lower-triangular tiles
+//     T(I, J)[j][i] = B_j . C_i (i in block I, j in block J <= I) are computed
+//     on MFMA and stored lane by lane: lane (r16, q) keeps C_{16I+r16} .
+//     B_{16J+4q+r}, r = 0..3, exactly the operand fragment the output kernel
+//     needs (k = j), so that kernel reads contiguous bytes per tile.
 template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void load_c_frags(CRaw<T, P, N, Q>& cf, const ScanArgs& a,
-                                             const WorkItem& it, int c, int r, int wave, int lane) {
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     using C_ = Cfg<T, P, N, Q>;
+    constexpr int kV = C_::kVec;
+    constexpr int E = C_::E;
+    __shared__ __attribute__((aligned(16))) T sB[Q * C_::SB];
+    __shared__ __attribute__((aligned(16))) T sC[Q * C_::SB];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    int64_t w = xcd_work_index(blockIdx.x, gridDim.x);
+    const int g = static_cast<int>(w % a.G);
+    w /= a.G;
+    const int c = static_cast<int>(w % a.nc);
+    const int64_t b = w / a.nc;
+    const int64_t t0 = static_cast<int64_t>(c) * Q;
+    const int64_t tl = a.L - 1;
+    const T* __restrict__ Bp = static_cast<const T*>(a.B);
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
-    const int r16 = lane & 15, q = lane >> 4;
-    const int I = row_block<C_::NB>(wave, r);
-    int64_t ti = static_cast<int64_t>(c) * Q + 16 * I + r16;
-    ti = ti < a.L ? ti : a.L - 1;
+
+    // ---- issue the B / C row loads first (they overlap the dt scan)
+    constexpr int CPR = C_::NP / kV;       // 16-byte pieces per padded row
+    constexpr int PIECES = Q * CPR;
+    constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
+    uint4 rb[PPT], rc[PPT];
 #pragma unroll
-    for (int s = 0; s < C_::KN; ++s) {
-        int n0 = 32 * s + 8 * q;
-        n0 = n0 < N ? n0 : N - 8;
-        cf[s] = raw_frag_load8(Cp + ((it.b * a.L + ti) * a.G + it.g) * N + n0);
+    for (int k = 0; k < PPT; ++k) {
+        int li = threadIdx.x + kThreads * k;
+        li = li < PIECES ? li : PIECES - 1;
+        const int j = li / CPR;
+        int n0 = (li % CPR) * kV;
+        n0 = n0 < N ? n0 : N - kV;
+        int64_t t = t0 + j;
+        t = t < tl ? t : tl;
+        rb[k] = ld_raw16(Bp + ((b * a.L + t) * a.G + g) * N + n0);
+        rc[k] = ld_raw16(Cp + ((b * a.L + t) * a.G + g) * N + n0);
+    }
+
+    // ---- per-head chunk metadata
+    const int hpg = a.H / a.G;
+    const bool has_seq = a.seq_idx != nullptr;
+    int sq[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        int64_t t = t0 + lane * E + k;
+        t = t < tl ? t : tl;
+        sq[k] = has_seq ? a.seq_idx[b * a.L + t] : 0;
+    }
+    const int prev_lane_last = __shfl_up(sq[E - 1], 1, kWave);
+    constexpr int kLastLane = (Q - 1) / E, kLastK = (Q - 1) % E;
+    for (int hh = wave; hh < hpg; hh += kWaves) {
+        const int h = g * hpg + hh;
+        const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+        const float Ah = a.A[h];
+        float dtv[E], loc[E];
+        int first_head = E;
+        float run = 0.0f;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int t = lane * E + k;
+            int64_t tt = t0 + t;
+            const bool real = t < Q && tt < a.L;
+            tt = tt < tl ? tt : tl;
+            const float raw = a.dt_raw[(b * a.L + tt) * a.H + h];
+            const float d = real ? dt_transform(raw, bias, a.softplus, a.dt_min, a.dt_max) : 0.0f;
+            const int before = (k == 0) ? prev_lane_last : sq[k - 1];
+            const bool head = t < Q && ((t == 0) || (sq[k] != before));
+            dtv[k] = d;
+            const float av = d * Ah;
+            run = (k == 0 || head) ? av : run + av;
+            if (head && first_head == E) first_head = k;
+            loc[k] = run;
+        }
+        const float incl = wave_segmented_scan(loc[E - 1], first_head < E);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 0.0f;
+        float csv[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) csv[k] = (k < first_head) ? excl + loc[k] : loc[k];
+        const float cs_last = __shfl(csv[kLastK], kLastLane, kWave);
+        const int seq_last = __shfl(sq[kLastK], kLastLane, kWave);
+        const int64_t base = ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(Q);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int t = lane * E + k;
+            if (t < Q) {
+                const float wv = decay_exp(cs_last - csv[k]) * dtv[k];
+                a.cs[base + t] = csv[k];
+                a.dtv[base + t] = dtv[k];
+                a.wgt[base + t] = (sq[k] == seq_last) ? wv : 0.0f;
+            }
+        }
+    }
+
+    // ---- stage B and C rows (tokens past L and columns past N are zero)
+    const int64_t valid = a.L - t0;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int li = threadIdx.x + kThreads * k;
+        if (li < PIECES) {
+            const int j = li / CPR, n0 = (li % CPR) * kV;
+            const bool keep = j < valid && n0 < N;
+            *reinterpret_cast<uint4*>(sB + j * C_::SB + n0) = raw_keep(keep, rb[k]);
+            *reinterpret_cast<uint4*>(sC + j * C_::SB + n0) = raw_keep(keep, rc[k]);
+        }
+    }
+    __syncthreads();
+
+    // ---- C.B^T tiles
+    T* __restrict__ out = static_cast<T*>(a.cbt) +
+                          ((b * a.nc + c) * a.G + g) * static_cast<int64_t>(C_::NT) * 64 * 4;
+    const int r16 = lane & 15, q = lane >> 4;
+    for (int tile = wave; tile < C_::NT; tile += kWaves) {
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= tile) ++I;
+        const int J = tile - I * (I + 1) / 2;
+        f32x4_t acc = acc_zero();
+#pragma unroll
+        for (int s = 0; s < C_::KN; ++s) {
+            const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
+            const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
+            mma(acc, bf, cf);
+        }
+        store4_f32(out + (static_cast<int64_t>(tile) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
     }
 }
 
-// Whether C fragment s of row block r holds real data (row < L, column < N).
-template <typename T, int P, int N, int Q>
-__device__ __forceinline__ bool c_frag_keep(const ScanArgs& a, int c, int r, int s, int wave,
-                                            int lane) {
-    using C_ = Cfg<T, P, N, Q>;
-    const int I = row_block<C_::NB>(wave, r);
-    const int64_t ti = static_cast<int64_t>(c) * Q + 16 * I + (lane & 15);
-    return (C_::NB >= 8 || wave < C_::NB) && ti < a.L && 32 * s + 8 * (lane >> 4) < N;
-}
+// ===========================================================================
+// Scan kernels: per-chunk data.
 
-// Issue the global loads of chunk c without waiting for them: every address
-// is clamped into its tensor (token index to L-1), and the values of tokens
-// past L are replaced by zeros at staging time.
-template <typename T, int P, int N, int Q, bool kOut>
-__device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q, kOut>& pf, const ScanArgs& a,
-                                               const WorkItem& it, int c, int wave, int lane) {
+// Token metadata of one chunk in LDS.
+template <int Q>
+struct ChunkMeta {
+    float cs[Q];   // segmented chunk cumsum of dt*A
+    float dt[Q];   // transformed dt (0 past L)
+    float w[Q];    // chunk-state weights
+    int seq[Q];    // sequence ids (padded tokens repeat the last real token's)
+    int seq_prev;  // id of the token before the chunk (token 0 for chunk 0)
+    int pad_[3];
+};
+
+// Global data of the next chunk, held in registers between issue and staging.
+template <typename T, int P, int N, int Q>
+struct Prefetch {
     using C_ = Cfg<T, P, N, Q>;
+    static constexpr int MP = (3 * Q / 4 + kThreads - 1) / kThreads;  // cs/dt/w pieces
+    static constexpr int SP = (Q + kThreads - 1) / kThreads;          // seq ids
+    uint4 xr[C_::XPT][4];  // x rows (raw)
+    uint4 br[C_::BPT][4];  // B rows (raw)
+    uint4 mr[MP];          // metadata, 16 bytes per piece
+    int sq[SP];
+    int seq_prev;
+};
+
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q>& pf, const ScanArgs& a,
+                                               const WorkItem& it, int c) {
+    using C_ = Cfg<T, P, N, Q>;
+    using PF = Prefetch<T, P, N, Q>;
     constexpr int kV = C_::kVec;
     const int tid = threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(c) * Q;
@@ -232,83 +332,27 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q, kOut>& pf, c
             pf.br[k][r] = ld_raw16(Bp + ((it.b * a.L + t) * a.G + it.g) * N + n0);
         }
     }
-    if constexpr (kOut && C_::kPrefetchC) load_c_frags<T, P, N, Q>(pf.cf[0], a, it, c, 0, wave, lane);
-    if (wave == 0) {
-        // without seq_idx the id loads read dt_raw (at least b*L elements of 4
-        // bytes) and the values are replaced by 0 where they are used, so that
-        // no load here depends on a branch
-        const int32_t* __restrict__ sq =
-            a.seq_idx ? a.seq_idx : reinterpret_cast<const int32_t*>(a.dt_raw);
+    const int64_t mo = meta_offset(a, it.b, it.h, c, Q);
 #pragma unroll
-        for (int k = 0; k < C_::E; ++k) {
-            int64_t t = t0 + lane * C_::E + k;
-            t = t < tl ? t : tl;
-            pf.dt[k] = a.dt_raw[(it.b * a.L + t) * a.H + it.h];
-            pf.seq[k] = sq[it.b * a.L + t];
-        }
-        pf.seq_prev = sq[it.b * a.L + (c == 0 ? 0 : t0 - 1)];
+    for (int k = 0; k < PF::MP; ++k) {
+        int piece = tid + kThreads * k;
+        piece = piece < 3 * Q / 4 ? piece : 3 * Q / 4 - 1;
+        const int arr = piece / (Q / 4), off = (piece % (Q / 4)) * 4;
+        const float* src = arr == 0 ? a.cs : (arr == 1 ? a.dtv : a.wgt);
+        pf.mr[k] = ld_raw16(src + mo + off);
     }
-}
-
-// Wave 0: dt transform and segmented inclusive cumsum of dt*A over the chunk
-// (restarted at the chunk start and at every sequence change), into LDS.
-template <typename T, int P, int N, int Q, bool kOut>
-__device__ __forceinline__ void chunk_meta_scan(ChunkMeta<Q>& m,
-                                                const Prefetch<T, P, N, Q, kOut>& pf,
-                                                const ScanArgs& a, int h, int c, int lane) {
-    using C_ = Cfg<T, P, N, Q>;
-    constexpr int E = C_::E;
-    const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    const float Ah = a.A[h];
-    const bool has_seq = a.seq_idx != nullptr;
-    int sq[E];
+    // without seq_idx the id loads read dt_raw (at least b*L elements of 4 bytes)
+    // and the values are replaced by 0 at staging, so no load here sits behind
+    // a branch
+    const int32_t* __restrict__ sqp =
+        a.seq_idx ? a.seq_idx : reinterpret_cast<const int32_t*>(a.dt_raw);
 #pragma unroll
-    for (int k = 0; k < E; ++k) sq[k] = has_seq ? pf.seq[k] : 0;
-    // id of the token just before this lane's first token (within the chunk)
-    const int prev_lane_last = __shfl_up(sq[E - 1], 1, kWave);
-    float dtv[E], loc[E];
-    int first_head = E;
-    float run = 0.0f;
-#pragma unroll
-    for (int k = 0; k < E; ++k) {
-        const int t = lane * E + k;
-        float d = 0.0f;
-        bool head = false;
-        if (t < Q) {
-            if (t0 + t < a.L) d = dt_transform(pf.dt[k], bias, a.softplus, a.dt_min, a.dt_max);
-            const int before = (k == 0) ? prev_lane_last : sq[k - 1];
-            head = (t == 0) || (sq[k] != before);
-        }
-        dtv[k] = d;
-        const float av = d * Ah;
-        run = (k == 0 || head) ? av : run + av;
-        if (head && first_head == E) first_head = k;
-        loc[k] = run;
+    for (int k = 0; k < PF::SP; ++k) {
+        int64_t t = t0 + tid + kThreads * k;
+        t = t < tl ? t : tl;
+        pf.sq[k] = sqp[it.b * a.L + t];
     }
-    const float incl = wave_segmented_scan(loc[E - 1], first_head < E);
-    float excl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) excl = 0.0f;
-#pragma unroll
-    for (int k = 0; k < E; ++k) {
-        const int t = lane * E + k;
-        if (t < Q) {
-            m.cs[t] = (k < first_head) ? excl + loc[k] : loc[k];
-            m.dt[t] = dtv[k];
-            m.seq[t] = sq[k];
-        }
-    }
-    if (lane == 0) m.seq_prev = has_seq ? pf.seq_prev : 0;
-}
-
-// Per-token weight of the chunk-state sum: w_j = exp(cs_last - cs_j) dt_j for
-// tokens of the chunk's last sequence, exactly 0 (by select) otherwise.
-template <int Q>
-__device__ __forceinline__ float state_weight(const ChunkMeta<Q>& m, int j, float cs_last,
-                                              int seq_last) {
-    const bool keep = m.seq[j] == seq_last;
-    const float w = decay_exp(cs_last - m.cs[j]) * m.dt[j];
-    return keep ? w : 0.0f;
+    pf.seq_prev = sqp[it.b * a.L + (c == 0 ? 0 : t0 - 1)];
 }
 
 // B^T * w: column E of one 4-token x kVec block of B, scaled by w_j and
@@ -329,17 +373,6 @@ __device__ __forceinline__ void store_bw_cols(T* sBw, const uint4 (&rows)[4], co
     }
 }
 
-template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void store_bw_block(T* sBw, const uint4 (&rows)[4],
-                                               const ChunkMeta<Q>& m, int j0, int n0) {
-    const float cs_last = m.cs[Q - 1];
-    const int seq_last = m.seq[Q - 1];
-    float w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = state_weight<Q>(m, j0 + r, cs_last, seq_last);
-    store_bw_cols<T, P, N, Q>(sBw, rows, w, j0, n0);
-}
-
 // x^T: column E of one 4-token x kVec block of x into sX[p0 + E][j0 .. j0+3].
 template <typename T, int P, int N, int Q, int E = 0>
 __device__ __forceinline__ void store_x_cols(T* sX, const uint4 (&rows)[4], int j0, int p0) {
@@ -350,13 +383,34 @@ __device__ __forceinline__ void store_x_cols(T* sX, const uint4 (&rows)[4], int 
     }
 }
 
-// Stage a prefetched chunk into LDS: x^T always; natural B when outputs are
-// computed; B^T*w unless it is written later over natural B.  Tokens past L
-// are zeroed here.
-template <typename T, int P, int N, int Q, bool kOut>
-__device__ __forceinline__ void stage_chunk(const Prefetch<T, P, N, Q, kOut>& pf,
-                                            const ChunkMeta<Q>& m, T* sX, T* sB, T* sBw,
-                                            int64_t valid) {
+// Stage the metadata of a prefetched chunk into LDS.
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void stage_meta(const Prefetch<T, P, N, Q>& pf, ChunkMeta<Q>& m,
+                                           bool has_seq) {
+    using PF = Prefetch<T, P, N, Q>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < PF::MP; ++k) {
+        const int piece = tid + kThreads * k;
+        if (piece < 3 * Q / 4) {
+            const int arr = piece / (Q / 4), off = (piece % (Q / 4)) * 4;
+            float* dst = arr == 0 ? m.cs : (arr == 1 ? m.dt : m.w);
+            *reinterpret_cast<uint4*>(dst + off) = pf.mr[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PF::SP; ++k) {
+        const int t = tid + kThreads * k;
+        if (t < Q) m.seq[t] = has_seq ? pf.sq[k] : 0;
+    }
+    if (tid == 0) m.seq_prev = has_seq ? pf.seq_prev : 0;
+}
+
+// Stage x^T and B^T*w of a prefetched chunk (its metadata already in LDS).
+// Tokens past L are zeroed here.
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void stage_tiles(const Prefetch<T, P, N, Q>& pf, const ChunkMeta<Q>& m,
+                                            T* sX, T* sBw, int64_t valid) {
     using C_ = Cfg<T, P, N, Q>;
     constexpr int kV = C_::kVec;
     const int tid = threadIdx.x;
@@ -379,34 +433,52 @@ __device__ __forceinline__ void stage_chunk(const Prefetch<T, P, N, Q, kOut>& pf
             uint4 rows[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) rows[r] = raw_keep(j0 + r < valid, pf.br[k][r]);
-            if constexpr (kOut) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    *reinterpret_cast<uint4*>(sB + (j0 + r) * C_::SB + n0) = rows[r];
-            }
-            if constexpr (!kOut || !C_::kInPlace) store_bw_block<T, P, N, Q>(sBw, rows, m, j0, n0);
+            const float4 w4 = *reinterpret_cast<const float4*>(&m.w[j0]);
+            const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+            store_bw_cols<T, P, N, Q>(sBw, rows, w, j0, n0);
         }
     }
 }
 
-// Chunk-state MFMA:  hreg[m][pb] += sum_j Bw^T[n][j] x[j][p]  (n-block wave + 8m)
+// Chunk-state MFMA:  hreg[m][pb] += sum_j Bw^T[n][j] x[j][p]  (n-block wave + 8m).
+// Software-pipelined: the operands of k step s+1 are read from LDS while the
+// MFMAs of step s run.
 template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void chunk_state_mma(StateRegs<T, P, N, Q>& hreg, const T* sBw,
-                                                const T* sX, int wave, int lane) {
+struct StateOps {
+    Frag<T> a[Cfg<T, P, N, Q>::MT];
+    Frag<T> b[Cfg<T, P, N, Q>::PB];
+};
+
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void load_state_ops(StateOps<T, P, N, Q>& o, const T* sBw, const T* sX,
+                                               int s, int wave, int lane) {
     using C_ = Cfg<T, P, N, Q>;
     const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int m = 0; m < C_::MT; ++m) {
-        const int nb = wave + kWaves * m;
-        if (nb < C_::NNB) {
+        int nb = wave + kWaves * m;
+        nb = nb < C_::NNB ? nb : C_::NNB - 1;
+        o.a[m] = frag_load8(sBw + (16 * nb + r16) * C_::SBW + 32 * s + 8 * q);
+    }
 #pragma unroll
-            for (int s = 0; s < C_::KQ; ++s) {
-                const Frag<T> af = frag_load8(sBw + (16 * nb + r16) * C_::SBW + 32 * s + 8 * q);
+    for (int pb = 0; pb < C_::PB; ++pb)
+        o.b[pb] = frag_load8(sX + (16 * pb + r16) * C_::SX + 32 * s + 8 * q);
+}
+
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void chunk_state_mma(StateRegs<T, P, N, Q>& hreg, const T* sBw,
+                                                const T* sX, int wave, int lane) {
+    using C_ = Cfg<T, P, N, Q>;
+    StateOps<T, P, N, Q> ops[2];
+    load_state_ops<T, P, N, Q>(ops[0], sBw, sX, 0, wave, lane);
 #pragma unroll
-                for (int pb = 0; pb < C_::PB; ++pb) {
-                    const Frag<T> xb = frag_load8(sX + (16 * pb + r16) * C_::SX + 32 * s + 8 * q);
-                    mma(hreg.v[m][pb], af, xb);
-                }
+    for (int s = 0; s < C_::KQ; ++s) {
+        if (s + 1 < C_::KQ) load_state_ops<T, P, N, Q>(ops[(s + 1) & 1], sBw, sX, s + 1, wave, lane);
+#pragma unroll
+        for (int m = 0; m < C_::MT; ++m) {
+            if (wave + kWaves * m < C_::NNB) {
+#pragma unroll
+                for (int pb = 0; pb < C_::PB; ++pb) mma(hreg.v[m][pb], ops[s & 1].a[m], ops[s & 1].b[pb]);
             }
         }
     }
@@ -487,118 +559,195 @@ __device__ __forceinline__ void state_to_lds(const StateRegs<T, P, N, Q>& hreg, 
     }
 }
 
-// Outputs of the wave's row blocks of one chunk:
+// Raw operand data of one output row block, loaded at the start of a chunk:
+// C_i fragments (lane (r16, q): C[16I + r16][32s + 8q .. +7]) and the
+// C.B^T tiles (I, J) for J <= I (lane: C_i . B_{16J+4q+r}, r = 0..3).
+template <typename T, int P, int N, int Q>
+struct RowOps {
+    using C_ = Cfg<T, P, N, Q>;
+    RawFrag<T> cf[C_::KN];
+    uint4 cb[C_::NB / 2 + 1][sizeof(T) == 2 ? 1 : 2];  // pairs of tiles (2u, 2u+1)
+    // x[i][16pb + 4q .. +3] for the D skip.
+    std::conditional_t<sizeof(T) == 2, uint2, uint4> xd[C_::PB];
+};
+
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void load_row_ops(RowOps<T, P, N, Q>& ro, const ScanArgs& a,
+                                             const WorkItem& it, int c, int I, int lane) {
+    using C_ = Cfg<T, P, N, Q>;
+    const T* __restrict__ Cp = static_cast<const T*>(a.C);
+    const int r16 = lane & 15, q = lane >> 4;
+    int64_t ti = static_cast<int64_t>(c) * Q + 16 * I + r16;
+    ti = ti < a.L ? ti : a.L - 1;
+#pragma unroll
+    for (int s = 0; s < C_::KN; ++s) {
+        int n0 = 32 * s + 8 * q;
+        n0 = n0 < N ? n0 : N - 8;
+        ro.cf[s] = raw_frag_load8(Cp + ((it.b * a.L + ti) * a.G + it.g) * N + n0);
+    }
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+#pragma unroll
+    for (int pb = 0; pb < C_::PB; ++pb) {
+        const T* px = x + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q;
+        if constexpr (sizeof(T) == 2) ro.xd[pb] = *reinterpret_cast<const uint2*>(px);
+        else ro.xd[pb] = ld_raw16(px);
+    }
+    const T* __restrict__ tiles = static_cast<const T*>(a.cbt) +
+                                  ((it.b * a.nc + c) * a.G + it.g) * static_cast<int64_t>(C_::NT) * 256;
+    const int first = I * (I + 1) / 2;  // tile (I, 0)
+#pragma unroll
+    for (int u = 0; u <= C_::NB / 2; ++u) {
+        // tiles (I, 2u) and (I, 2u+1), clamped into this row's tiles
+        int j0 = 2 * u, j1 = 2 * u + 1;
+        j0 = j0 <= I ? j0 : I;
+        j1 = j1 <= I ? j1 : I;
+        const T* p0 = tiles + (static_cast<int64_t>(first + j0) * 64 + lane) * 4;
+        const T* p1 = tiles + (static_cast<int64_t>(first + j1) * 64 + lane) * 4;
+        if constexpr (sizeof(T) == 2) {
+            const uint2 v0 = *reinterpret_cast<const uint2*>(p0);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(p1);
+            ro.cb[u][0] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        } else {
+            ro.cb[u][0] = ld_raw16(p0);
+            ro.cb[u][1] = ld_raw16(p1);
+        }
+    }
+}
+
+// Element R (0..7) of tile pair u as fp32: R < 4 from tile 2u, else 2u+1.
+template <typename T, int P, int N, int Q, int R>
+__device__ __forceinline__ float cb_elem(const RowOps<T, P, N, Q>& ro, int u) {
+    if constexpr (sizeof(T) == 2) {
+        return raw_elem_f32<T, R>(ro.cb[u][0]);
+    } else {
+        return raw_elem_f32<T, R % 4>(ro.cb[u][R / 4]);
+    }
+}
+
+// Per-k-step LDS operands of the intra-chunk product: x^T fragments of every
+// p-block for token pair (2u, 2u+1) and the metadata of those tokens.
+template <typename T, int P, int N, int Q>
+struct IntraX {
+    Frag<T> xf[Cfg<T, P, N, Q>::PB];
+};
+
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ void load_intra_x(IntraX<T, P, N, Q>& o, const T* sX, int u, int lane) {
+    using C_ = Cfg<T, P, N, Q>;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int j0 = 32 * u, j1 = 32 * u + 16 < Q ? 32 * u + 16 : 0;  // j1 masked when out of range
+#pragma unroll
+    for (int pb = 0; pb < C_::PB; ++pb) {
+        const T* row = sX + (16 * pb + r16) * C_::SX;
+        o.xf[pb] = frag_load4x2(row + j0 + 4 * q, row + j1 + 4 * q);
+    }
+}
+
+// Outputs of one row block I of one chunk (lane (r16, q): token i = 16I + r16):
 //   y^T[p][i] = exp(cs_i) [seq_i = seq_prev] sum_n h[p][n] C_i[n]
 //             + sum_{j <= i} x^T[p][j] G[i][j] + D x[i][p],
 //   G[i][j]   = (C_i . B_j) exp(cs_i - cs_j) dt_j [seq_j = seq_i].
-// C.B^T tiles come out of the MFMA with lane (r16, q) holding
-// C_i . B_{16J+4q+r} for i = 16I + r16, which is exactly an operand fragment
-// with k = j (two runs of four), so G never goes through LDS.
+// LDS operands are read one k step ahead of the MFMAs that use them.
 template <typename T, int P, int N, int Q>
-__device__ __forceinline__ void chunk_outputs(
-    const ChunkMeta<Q>& m, const RawFrag<T> (&cfp)[Cfg<T, P, N, Q>::RBC][Cfg<T, P, N, Q>::KN],
-    const T* sB, const T* sX, const T* sH, const ScanArgs& a, const WorkItem& it, int c,
-    float Dh, int wave, int lane) {
+__device__ __forceinline__ void row_block_outputs(const RowOps<T, P, N, Q>& ro, const ChunkMeta<Q>& m,
+                                                  const T* sX, const T* sH, const ScanArgs& a,
+                                                  const WorkItem& it, int c, int I, float Dh,
+                                                  bool has_seq, int lane) {
     using C_ = Cfg<T, P, N, Q>;
     const int r16 = lane & 15, q = lane >> 4;
-    const int64_t t0 = static_cast<int64_t>(c) * Q;
-    T* __restrict__ y = static_cast<T*>(a.y);
-    const bool has_seq = a.seq_idx != nullptr;
-#pragma unroll 1
-    for (int rb = 0; rb < C_::RB; ++rb) {
-        const int I = row_block<C_::NB>(wave, rb);
-        if (C_::NB < 8 && wave >= C_::NB) continue;
-        const int i = 16 * I + r16;
-        const int64_t ti = t0 + i;
-        Frag<T> cf[C_::KN];
-        {
-            RawFrag<T> raw[C_::KN];
-            if constexpr (C_::kPrefetchC) {
+    const int i = 16 * I + r16;
+    const int64_t ti = static_cast<int64_t>(c) * Q + i;
+    Frag<T> cf[C_::KN];
 #pragma unroll
-                for (int s = 0; s < C_::KN; ++s) raw[s] = cfp[rb][s];
-            } else {
-                load_c_frags<T, P, N, Q>(raw, a, it, c, rb, wave, lane);
+    for (int s = 0; s < C_::KN; ++s) cf[s] = frag_from_raw(ro.cf[s], ti < a.L && 32 * s + 8 * q < N);
+    f32x4_t acc[C_::PB];
+#pragma unroll
+    for (int pb = 0; pb < C_::PB; ++pb) acc[pb] = acc_zero();
+    {
+        Frag<T> hf[2][C_::PB];
+#pragma unroll
+        for (int pb = 0; pb < C_::PB; ++pb)
+            hf[0][pb] = frag_load8(sH + (16 * pb + r16) * C_::SH + 8 * q);
+#pragma unroll
+        for (int s = 0; s < C_::KN; ++s) {
+            if (s + 1 < C_::KN) {
+#pragma unroll
+                for (int pb = 0; pb < C_::PB; ++pb)
+                    hf[(s + 1) & 1][pb] =
+                        frag_load8(sH + (16 * pb + r16) * C_::SH + 32 * (s + 1) + 8 * q);
             }
 #pragma unroll
-            for (int s = 0; s < C_::KN; ++s)
-                cf[s] = frag_from_raw(raw[s], c_frag_keep<T, P, N, Q>(a, c, rb, s, wave, lane));
+            for (int pb = 0; pb < C_::PB; ++pb) mma(acc[pb], hf[s & 1][pb], cf[s]);
         }
-        f32x4_t acc[C_::PB];
+    }
+    const float cs_i = m.cs[i];
+    const int seq_i = m.seq[i];
+    {
+        const bool keep = seq_i == m.seq_prev;
+        const float e = decay_exp(cs_i);
 #pragma unroll
-        for (int pb = 0; pb < C_::PB; ++pb) acc[pb] = acc_zero();
+        for (int pb = 0; pb < C_::PB; ++pb)
 #pragma unroll
-        for (int s = 0; s < C_::KN; ++s)
-#pragma unroll
-            for (int pb = 0; pb < C_::PB; ++pb) {
-                const Frag<T> hf = frag_load8(sH + (16 * pb + r16) * C_::SH + 32 * s + 8 * q);
-                mma(acc[pb], hf, cf[s]);
+            for (int r = 0; r < 4; ++r) {
+                const float v = acc[pb][r] * e;
+                acc[pb][r] = keep ? v : 0.0f;
             }
-        const float cs_i = m.cs[i];
-        const int seq_i = m.seq[i];
-        {
-            const bool keep = seq_i == m.seq_prev;
-            const float e = decay_exp(cs_i);
+    }
+    IntraX<T, P, N, Q> ix[2];
+    load_intra_x<T, P, N, Q>(ix[0], sX, 0, lane);
 #pragma unroll
-            for (int pb = 0; pb < C_::PB; ++pb)
+    for (int u = 0; u <= C_::NB / 2; ++u) {
+        if (2 * u <= I) {
+            float4 csq[2], dtq[2];
+            int4 sqq[2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = acc[pb][r] * e;
-                    acc[pb][r] = keep ? v : 0.0f;
-                }
-        }
-        for (int u = 0; u <= I / 2; ++u) {
+            for (int hp = 0; hp < 2; ++hp) {
+                int jb = 16 * (2 * u + hp) + 4 * q;
+                jb = jb < Q ? jb : 0;
+                csq[hp] = *reinterpret_cast<const float4*>(&m.cs[jb]);
+                dtq[hp] = *reinterpret_cast<const float4*>(&m.dt[jb]);
+                sqq[hp] = has_seq ? *reinterpret_cast<const int4*>(&m.seq[jb]) : make_int4(0, 0, 0, 0);
+            }
+            if (2 * u + 2 <= I) load_intra_x<T, P, N, Q>(ix[(u + 1) & 1], sX, u + 1, lane);
+            const IntraX<T, P, N, Q>& cur = ix[u & 1];
             float g[8];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
                 const int J = 2 * u + hp;
-                if (J <= I) {
-                    f32x4_t t = acc_zero();
-#pragma unroll
-                    for (int s = 0; s < C_::KN; ++s) {
-                        const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
-                        mma(t, bf, cf[s]);
-                    }
-                    const int jb = 16 * J + 4 * q;
-                    const float4 csj = *reinterpret_cast<const float4*>(&m.cs[jb]);
-                    const float4 dtj = *reinterpret_cast<const float4*>(&m.dt[jb]);
-                    const float csv[4] = {csj.x, csj.y, csj.z, csj.w};
-                    const float dtv[4] = {dtj.x, dtj.y, dtj.z, dtj.w};
-                    int sqv[4] = {seq_i, seq_i, seq_i, seq_i};
-                    if (has_seq) {
-                        const int4 sqj = *reinterpret_cast<const int4*>(&m.seq[jb]);
-                        sqv[0] = sqj.x; sqv[1] = sqj.y; sqv[2] = sqj.z; sqv[3] = sqj.w;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool keep = (J < I || jb + r <= i) && (sqv[r] == seq_i);
-                        const float v = t[r] * decay_exp(keep ? cs_i - csv[r] : 0.0f) * dtv[r];
-                        g[4 * hp + r] = keep ? v : 0.0f;
-                    }
+                const int jb = 16 * J + 4 * q;
+                const float csv[4] = {csq[hp].x, csq[hp].y, csq[hp].z, csq[hp].w};
+                const float dtv[4] = {dtq[hp].x, dtq[hp].y, dtq[hp].z, dtq[hp].w};
+                const int sqv[4] = {has_seq ? sqq[hp].x : seq_i, has_seq ? sqq[hp].y : seq_i,
+                                    has_seq ? sqq[hp].z : seq_i, has_seq ? sqq[hp].w : seq_i};
+                float t[4];
+                if (hp == 0) {
+                    t[0] = cb_elem<T, P, N, Q, 0>(ro, u); t[1] = cb_elem<T, P, N, Q, 1>(ro, u);
+                    t[2] = cb_elem<T, P, N, Q, 2>(ro, u); t[3] = cb_elem<T, P, N, Q, 3>(ro, u);
                 } else {
+                    t[0] = cb_elem<T, P, N, Q, 4>(ro, u); t[1] = cb_elem<T, P, N, Q, 5>(ro, u);
+                    t[2] = cb_elem<T, P, N, Q, 6>(ro, u); t[3] = cb_elem<T, P, N, Q, 7>(ro, u);
+                }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) g[4 * hp + r] = 0.0f;
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = (J < I || (J == I && jb + r <= i)) && (sqv[r] == seq_i);
+                    const float v = t[r] * decay_exp(keep ? cs_i - csv[r] : 0.0f) * dtv[r];
+                    g[4 * hp + r] = keep ? v : 0.0f;
                 }
             }
             const Frag<T> gf = frag_from_f32<T>(g);
 #pragma unroll
-            for (int pb = 0; pb < C_::PB; ++pb) {
-                const T* row = sX + (16 * pb + r16) * C_::SX;
-                const Frag<T> xf = frag_load4x2(row + 32 * u + 4 * q, row + 32 * u + 16 + 4 * q);
-                mma(acc[pb], xf, gf);
-            }
+            for (int pb = 0; pb < C_::PB; ++pb) mma(acc[pb], cur.xf[pb], gf);
         }
-        if (ti < a.L) {
+    }
+    if (ti < a.L) {
+        T* __restrict__ y = static_cast<T*>(a.y);
 #pragma unroll
-            for (int pb = 0; pb < C_::PB; ++pb) {
-                float o[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float xv = Io<T>::to_f32(sX[(16 * pb + 4 * q + r) * C_::SX + i]);
-                    o[r] = acc[pb][r] + Dh * xv;
-                }
-                store4_f32(y + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q, o[0], o[1],
-                           o[2], o[3]);
-            }
+        for (int pb = 0; pb < C_::PB; ++pb) {
+            const float x0 = raw_elem_f32<T, 0>(ro.xd[pb]), x1 = raw_elem_f32<T, 1>(ro.xd[pb]);
+            const float x2 = raw_elem_f32<T, 2>(ro.xd[pb]), x3 = raw_elem_f32<T, 3>(ro.xd[pb]);
+            store4_f32(y + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q,
+                       acc[pb][0] + Dh * x0, acc[pb][1] + Dh * x1, acc[pb][2] + Dh * x2,
+                       acc[pb][3] + Dh * x3);
         }
     }
 }
@@ -612,13 +761,10 @@ __device__ __forceinline__ void chunk_outputs(
 template <typename T, int P, int N, int Q, bool kOut>
 __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     using C_ = Cfg<T, P, N, Q>;
-    constexpr bool kSepBw = !kOut || !C_::kInPlace;
-    __shared__ __attribute__((aligned(16))) T sB[kOut ? C_::B_ELEMS : 1];
-    __shared__ __attribute__((aligned(16))) T sBwBuf[kSepBw ? N * C_::SBW : 1];
+    __shared__ __attribute__((aligned(16))) T sBw[N * C_::SBW];
     __shared__ __attribute__((aligned(16))) T sX[P * C_::SX];
     __shared__ __attribute__((aligned(16))) T sH[kOut ? P * C_::SH : 1];
-    __shared__ __attribute__((aligned(16))) ChunkMeta<Q> meta[2];
-    T* sBw = kSepBw ? sBwBuf : sB;
+    __shared__ __attribute__((aligned(16))) ChunkMeta<Q> meta;
 
     const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -627,6 +773,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     const int c_begin = it.seg * a.cps;
     const int c_end = min(c_begin + a.cps, a.nc);
     const bool last_seg = kOut && it.seg == a.nseg - 1;
+    const bool has_seq = a.seq_idx != nullptr;
 
     StateRegs<T, P, N, Q> hreg;
     if constexpr (kOut) {
@@ -639,8 +786,6 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
             constexpr int W = C_::NP - N;
             for (int idx = threadIdx.x; idx < P * W; idx += kThreads)
                 sH[(idx / W) * C_::SH + N + idx % W] = Io<T>::from_f32(0.0f);
-            for (int idx = threadIdx.x; idx < Q * W; idx += kThreads)
-                sB[(idx / W) * C_::SB + N + idx % W] = Io<T>::from_f32(0.0f);
         }
         state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
     } else {
@@ -648,77 +793,45 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     }
     float mult = 1.0f;
 
-    Prefetch<T, P, N, Q, kOut> pf;
-    prefetch_chunk<T, P, N, Q, kOut>(pf, a, it, c_begin, wave, lane);
-    if (wave == 0) chunk_meta_scan<T, P, N, Q, kOut>(meta[0], pf, a, it.h, c_begin, lane);
+    Prefetch<T, P, N, Q> pf;
+    prefetch_chunk<T, P, N, Q>(pf, a, it, c_begin);
+    stage_meta<T, P, N, Q>(pf, meta, has_seq);
     __syncthreads();
-    stage_chunk<T, P, N, Q, kOut>(pf, meta[0], sX, sB, sBw,
-                                  a.L - static_cast<int64_t>(c_begin) * Q);
-    RawFrag<T> cf[kOut ? C_::RBC : 1][C_::KN];
-    if constexpr (kOut && C_::kPrefetchC) {
-#pragma unroll
-        for (int r = 0; r < C_::RBC; ++r)
-#pragma unroll
-            for (int s = 0; s < C_::KN; ++s) cf[r][s] = pf.cf[r][s];
-    }
+    stage_tiles<T, P, N, Q>(pf, meta, sX, sBw, a.L - static_cast<int64_t>(c_begin) * Q);
     __syncthreads();
 
     for (int c = c_begin; c < c_end; ++c) {
-        const int cur = (c - c_begin) & 1;
         const bool has_next = c + 1 < c_end;
-        const ChunkMeta<Q>& m = meta[cur];
-        if (has_next) prefetch_chunk<T, P, N, Q, kOut>(pf, a, it, c + 1, wave, lane);
         const bool need_state = !kOut || has_next || (last_seg && a.final_states);
+        // operands of this chunk's output rows first, then the next chunk's tiles
+        RowOps<T, P, N, Q> ro[kOut ? C_::RB : 1];
         if constexpr (kOut) {
-            chunk_outputs<T, P, N, Q>(m, cf, sB, sX, sH, a, it, c, Dh, wave, lane);
-            if constexpr (!kSepBw) {
-                // natural B is dead after the outputs: rewrite it as B^T*w in place
-                __syncthreads();
-                if (need_state) {
-                    uint4 rows[C_::BPT][4];
 #pragma unroll
-                    for (int k = 0; k < C_::BPT; ++k) {
-                        const int blk = threadIdx.x + kThreads * k;
-                        if (blk < C_::BBK) {
-                            const int j0 = (blk / C_::CBB) * 4, n0 = (blk % C_::CBB) * C_::kVec;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                rows[k][r] = ld_raw16(sB + (j0 + r) * C_::SB + n0);
-                        }
-                    }
-                    __syncthreads();
-#pragma unroll
-                    for (int k = 0; k < C_::BPT; ++k) {
-                        const int blk = threadIdx.x + kThreads * k;
-                        if (blk < C_::BBK) {
-                            const int j0 = (blk / C_::CBB) * 4, n0 = (blk % C_::CBB) * C_::kVec;
-                            store_bw_block<T, P, N, Q>(sBw, rows[k], m, j0, n0);
-                        }
-                    }
-                }
-                __syncthreads();
-            }
+            for (int r = 0; r < C_::RB; ++r)
+                if (row_block_valid<C_::NB>(wave))
+                    load_row_ops<T, P, N, Q>(ro[r], a, it, c, row_block<C_::NB>(wave, r), lane);
         }
+        if (has_next) prefetch_chunk<T, P, N, Q>(pf, a, it, c + 1);
         if (need_state) {
-            const bool keep = m.seq[Q - 1] == m.seq_prev;
-            const float e = decay_exp(m.cs[Q - 1]);
+            const bool keep = meta.seq[Q - 1] == meta.seq_prev;
+            const float e = decay_exp(meta.cs[Q - 1]);
             decay_state<T, P, N, Q>(hreg, keep, e);
             mult = keep ? mult * e : 0.0f;
             chunk_state_mma<T, P, N, Q>(hreg, sBw, sX, wave, lane);
         }
-        if (has_next && wave == 0)
-            chunk_meta_scan<T, P, N, Q, kOut>(meta[cur ^ 1], pf, a, it.h, c + 1, lane);
-        __syncthreads();  // every read of this chunk's LDS tiles is done
+        if constexpr (kOut) {
+#pragma unroll
+            for (int r = 0; r < C_::RB; ++r)
+                if (row_block_valid<C_::NB>(wave))
+                    row_block_outputs<T, P, N, Q>(ro[r], meta, sX, sH, a, it, c,
+                                                  row_block<C_::NB>(wave, r), Dh, has_seq, lane);
+        }
+        __syncthreads();  // every read of this chunk's LDS data is done
         if (has_next) {
             if constexpr (kOut) state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
-            stage_chunk<T, P, N, Q, kOut>(pf, meta[cur ^ 1], sX, sB, sBw,
-                                          a.L - static_cast<int64_t>(c + 1) * Q);
-            if constexpr (kOut && C_::kPrefetchC) {
-#pragma unroll
-                for (int r = 0; r < C_::RBC; ++r)
-#pragma unroll
-                    for (int s = 0; s < C_::KN; ++s) cf[r][s] = pf.cf[r][s];
-            }
+            stage_meta<T, P, N, Q>(pf, meta, has_seq);
+            __syncthreads();
+            stage_tiles<T, P, N, Q>(pf, meta, sX, sBw, a.L - static_cast<int64_t>(c + 1) * Q);
             __syncthreads();
         }
     }
@@ -835,6 +948,13 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
     return hipGetLastError();
 }
 
+template <typename T, int P, int N, int Q>
+static hipError_t launch_chunk_prep_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
+    hipLaunchKernelGGL((chunk_prep_kernel<T, P, N, Q>), dim3(static_cast<unsigned>(nblocks)),
+                       dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 template <typename T, int P, int N, int Q, bool kOut>
 static hipError_t launch_chunk_scan_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     hipLaunchKernelGGL((chunk_scan_kernel<T, P, N, Q, kOut>),
@@ -850,9 +970,9 @@ static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipS
 }
 
 // The compiled (io, P, N, Q) set of the chunked scan.
-#define SSD_SCAN_VARIANT(IO, T, P, N, Q)                   \
-    {IO, P, N, Q, &launch_chunk_scan_t<T, P, N, Q, false>, \
-     &launch_chunk_scan_t<T, P, N, Q, true>},
+#define SSD_SCAN_VARIANT(IO, T, P, N, Q)                                    \
+    {IO, P, N, Q, &launch_chunk_prep_t<T, P, N, Q>,                         \
+     &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>},
 
 static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 16, 16, 32)

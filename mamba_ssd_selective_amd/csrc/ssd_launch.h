@@ -24,6 +24,10 @@ struct ScanArgs {
     float* final_states;    // (b, H, P, N) or null
     float* seg_state;       // (b, H, nseg, P, N) workspace
     float* seg_mult;        // (b, H, nseg) workspace
+    float* cs;              // (b, H, nc, Q) workspace: segmented chunk cumsum of dt*A
+    float* dtv;             // (b, H, nc, Q) workspace: transformed dt (0 past L)
+    float* wgt;             // (b, H, nc, Q) workspace: chunk-state weights
+    void* cbt;              // (b, nc, G, tiles, 64, 4) workspace: C.B^T tiles, io type
     int64_t L;
     int H, G;
     int nc, nseg, cps;      // chunks, segments, chunks per segment
@@ -59,9 +63,16 @@ typedef hipError_t (*ScanLaunchFn)(const ScanArgs&, int64_t nblocks, hipStream_t
 struct ScanVariant {
     int io;  // 0 = fp32, 1 = bf16
     int P, N, Q;
-    ScanLaunchFn chunk_state;   // K2
-    ScanLaunchFn chunk_output;  // K4
+    ScanLaunchFn chunk_prep;    // dt transform, chunk cumsum, weights, C.B^T tiles
+    ScanLaunchFn chunk_state;   // segment states
+    ScanLaunchFn chunk_output;  // outputs with the carried state
 };
+
+// Elements of io type in the C.B^T tile buffer of one (row, chunk, group).
+inline int64_t cbt_elems_per_chunk_group(int64_t Q) {
+    const int64_t nb = Q / 16;
+    return nb * (nb + 1) / 2 * 64 * 4;
+}
 
 const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q);
 int scan_variant_count();
