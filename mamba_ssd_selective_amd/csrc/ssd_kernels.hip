@@ -40,19 +40,9 @@
 // before the current chunk's MFMA work and stages them into LDS after it.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_work.h"
 
 namespace ssd {
-
-// ---------------------------------------------------------------------------
-// Work-index mapping: consecutive workgroup ids are dealt round-robin to the
-// 8 XCDs of an MI355X, each with its own L2.  Remap so that one XCD receives a
-// contiguous range of work items (workgroups sharing B/C data then share that
-// XCD's L2).
-__device__ __forceinline__ int64_t xcd_work_index(int64_t bid, int64_t nblocks) {
-    constexpr int kXcd = 8;
-    if (nblocks % kXcd != 0) return bid;
-    return (bid % kXcd) * (nblocks / kXcd) + bid / kXcd;
-}
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
@@ -108,30 +98,6 @@ template <typename T, int P, int N, int Q>
 struct StateRegs {
     f32x4_t v[Cfg<T, P, N, Q>::MT][Cfg<T, P, N, Q>::PB];
 };
-
-struct WorkItem {
-    int64_t b;
-    int seg, h, g;
-};
-// Work order (fastest first): head within its group, group, segment, row.
-__device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
-    const int64_t nblocks = static_cast<int64_t>(gridDim.x);
-    int64_t w = xcd_work_index(blockIdx.x, nblocks);
-    const int hpg = a.H / a.G;
-    WorkItem it;
-    const int hh = static_cast<int>(w % hpg);
-    w /= hpg;
-    it.g = static_cast<int>(w % a.G);
-    w /= a.G;
-    it.seg = static_cast<int>(w % nseg_grid);
-    it.b = w / nseg_grid;
-    it.h = it.g * hpg + hh;
-    return it;
-}
-
-__device__ __forceinline__ int64_t meta_offset(const ScanArgs& a, int64_t b, int h, int c, int Q) {
-    return ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(Q);
-}
 
 // ===========================================================================
 // chunk_prep_kernel: one workgroup per (row, chunk, group), grid order
@@ -974,6 +940,11 @@ static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipS
     {IO, P, N, Q, &launch_chunk_prep_t<T, P, N, Q>,                         \
      &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>},
 
+// bf16 shapes served by the transposing-read kernels of ssd_scan_tr.hip.
+#define SSD_SCAN_VARIANT_TR(P, N, Q)                                        \
+    {1, P, N, Q, &launch_chunk_prep_t<uint16_t, P, N, Q>,                   \
+     &scan_tr_state_##P##_##N##_##Q, &scan_tr_output_##P##_##N##_##Q},
+
 static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 16, 16, 32)
     SSD_SCAN_VARIANT(0, float, 16, 16, 64)
@@ -981,9 +952,9 @@ static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 64, 128, 64)
     SSD_SCAN_VARIANT(0, float, 64, 128, 128)
     SSD_SCAN_VARIANT(1, uint16_t, 16, 16, 64)
-    SSD_SCAN_VARIANT(1, uint16_t, 64, 64, 128)
-    SSD_SCAN_VARIANT(1, uint16_t, 64, 128, 64)
-    SSD_SCAN_VARIANT(1, uint16_t, 64, 128, 128)
+    SSD_SCAN_VARIANT_TR(64, 64, 128)
+    SSD_SCAN_VARIANT_TR(64, 128, 64)
+    SSD_SCAN_VARIANT_TR(64, 128, 128)
     SSD_SCAN_VARIANT(1, uint16_t, 64, 128, 256)
 };
 

@@ -74,6 +74,15 @@ inline int64_t cbt_elems_per_chunk_group(int64_t Q) {
     return nb * (nb + 1) / 2 * 64 * 4;
 }
 
+// bf16 scan kernels built on direct-to-LDS staging and transposing LDS reads
+// (ssd_scan_tr.hip): segment states and outputs for P = 64.
+hipError_t scan_tr_state_64_64_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_output_64_64_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_state_64_128_64(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_output_64_128_64(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_state_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_output_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+
 const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q);
 int scan_variant_count();
 const ScanVariant* scan_variant_at(int i);
