@@ -37,13 +37,12 @@ Plan make_plan(const ssd_dims& d, ssd_dtype io) {
     p.nseg = (p.nc + p.cps - 1) / p.cps;
     const size_t f = sizeof(float);
     const size_t es = io == SSD_BF16 ? 2 : 4;
-    const size_t meta = static_cast<size_t>(bh * p.nc * d.chunk_size) * f;
+    // per-token metadata, one block [cs Q | dt Q | w Q] per (row, head, chunk)
+    const size_t meta = static_cast<size_t>(bh * p.nc * d.chunk_size) * 3 * f;
     size_t off = 0;
     p.off_cs = off;
-    off = align_up(off + meta);
-    p.off_dtv = off;
-    off = align_up(off + meta);
-    p.off_wgt = off;
+    p.off_dtv = off + static_cast<size_t>(d.chunk_size) * f;
+    p.off_wgt = off + 2 * static_cast<size_t>(d.chunk_size) * f;
     off = align_up(off + meta);
     p.off_cbt = off;
     off = align_up(off + static_cast<size_t>(d.batch * p.nc * d.ngroups) *

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         for (int k = 0; k < E; ++k) csv[k] = (k < first_head) ? excl + loc[k] : loc[k];
         const float cs_last = __shfl(csv[kLastK], kLastLane, kWave);
         const int seq_last = __shfl(sq[kLastK], kLastLane, kWave);
-        const int64_t base = ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(Q);
+        const int64_t base = meta_offset(a, b, h, c, Q);
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             const int t = lane * E + k;

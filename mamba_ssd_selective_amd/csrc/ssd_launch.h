@@ -24,9 +24,12 @@ struct ScanArgs {
     float* final_states;    // (b, H, P, N) or null
     float* seg_state;       // (b, H, nseg, P, N) workspace
     float* seg_mult;        // (b, H, nseg) workspace
-    float* cs;              // (b, H, nc, Q) workspace: segmented chunk cumsum of dt*A
-    float* dtv;             // (b, H, nc, Q) workspace: transformed dt (0 past L)
-    float* wgt;             // (b, H, nc, Q) workspace: chunk-state weights
+    // Per-token metadata workspace, one block [cs Q | dt Q | w Q] per (row, head,
+    // chunk); cs, dtv and wgt point at the three arrays of block 0 (chunk
+    // stride 3Q floats, see meta_offset).
+    float* cs;              // segmented chunk cumsum of dt*A
+    float* dtv;             // transformed dt (0 past L)
+    float* wgt;             // chunk-state weights
     void* cbt;              // (b, nc, G, tiles, 64, 4) workspace: C.B^T tiles, io type
     int64_t L;
     int H, G;

@@ -66,7 +66,8 @@ struct TrGeo {
     static_assert(NNB <= kTrWaves && NB <= kTrWaves, "one block per wave");
 };
 
-// Per-token metadata of one chunk (written by chunk_prep_kernel).
+// Per-token metadata of one chunk (written by chunk_prep_kernel; cs, dt, w are
+// contiguous as in the workspace block).
 template <int Q>
 struct TrMeta {
     float cs[Q];  // segmented chunk cumsum of dt*A
@@ -148,66 +149,37 @@ __device__ __forceinline__ Frag<uint16_t> frag_of(const uint4& u) {
 
 // ---------------------------------------------------------- global -> LDS
 
-// Copy `rows` token rows of ROW bytes (row r at byte r * gstride from gbase)
-// into a swizzled tile; rows at or past `rows_valid` read as zeros.
-template <int ROW, int rows>
-__device__ __forceinline__ void dma_tile(char* lds, const void* gbase, int gstride, int rows_valid,
-                                         int wave, int lane) {
+// Copy instructions kk in [k0, k1) (kk < KMAX) of this wave (instruction
+// k = wave + 8 kk covers 1024 bytes) of a swizzled [token][ROW bytes] tile; row
+// r comes from byte r * gstride of the resource, and rows past its range read
+// as zeros.  The loop unrolls fully, so constant bounds fold away.
+template <int ROW, int KMAX>
+__device__ __forceinline__ void dma_rows(char* lds, __amdgpu_buffer_rsrc_t rs, int gstride,
+                                         int k0, int k1, int wave, int lane) {
     constexpr int RPI = 1024 / ROW;  // rows per wave instruction (64 lanes x 16 bytes)
     constexpr int SPR = ROW / 16;    // 16-byte slots per row
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(gbase), 0, rows_valid * gstride, kRawBufferWord3);
-    constexpr int ninstr = rows / RPI;
-    static_assert(1024 % ROW == 0 && ninstr % kTrWaves == 0, "whole rows per wave");
+    static_assert(1024 % ROW == 0, "whole rows per instruction");
 #pragma unroll
-    for (int kk = 0; kk < ninstr / kTrWaves; ++kk) {
-        const int k = wave + kTrWaves * kk;
-        const int row = k * RPI + lane / SPR;
-        const int slot = (lane % SPR) ^ (2 * tr_swz<ROW>(row));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(lds + k * 1024), 16,
-                                                 row * gstride + slot * 16, 0, 0, 0);
+    for (int kk = 0; kk < KMAX; ++kk) {
+        if (kk >= k0 && kk < k1) {
+            const int k = wave + kTrWaves * kk;
+            const int row = k * RPI + lane / SPR;
+            const int slot = (lane % SPR) ^ (2 * tr_swz<ROW>(row));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(lds + k * 1024), 16,
+                                                     row * gstride + slot * 16, 0, 0, 0);
+        }
     }
 }
 
-// Copy chunk c's x and B tiles and its metadata (cs, dt, w from the prep
-// workspaces; sequence ids from seq_idx, zeros past L).
-template <int P, int N, int Q, bool kSeq>
-__device__ __forceinline__ void dma_chunk(char* sX, char* sB, TrMeta<Q>* sM, const ScanArgs& a,
-                                          const WorkItem& it, int c, int wave, int lane) {
-    using G_ = TrGeo<P, N, Q>;
-    const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const int64_t rem = a.L - t0;
-    const int valid = rem < Q ? static_cast<int>(rem) : Q;
-    const uint16_t* xb = static_cast<const uint16_t*>(a.x) + ((it.b * a.L + t0) * a.H + it.h) * P;
-    const uint16_t* bb = static_cast<const uint16_t*>(a.B) + ((it.b * a.L + t0) * a.G + it.g) * N;
-    dma_tile<G_::XROW, Q>(sX, xb, a.H * P * 2, valid, wave, lane);
-    dma_tile<G_::BROW, Q>(sB, bb, a.G * N * 2, valid, wave, lane);
-    constexpr int ML = Q / 4;  // lanes per metadata array (16 bytes each)
-    const int mw = kTrWaves - 1 - wave;  // metadata from the last waves (fewest tile rows)
-    if (mw < 4 && lane < ML) {
-        const int64_t mo = meta_offset(a, it.b, it.h, c, Q) + 4 * lane;
-        if (mw == 0) {
-            __builtin_amdgcn_global_load_lds((SSD_GLOBAL void*)(a.cs + mo), (SSD_LDS void*)(sM->cs),
-                                             16, 0, 0);
-        } else if (mw == 1) {
-            __builtin_amdgcn_global_load_lds((SSD_GLOBAL void*)(a.dtv + mo),
-                                             (SSD_LDS void*)(sM->dt), 16, 0, 0);
-        } else if (mw == 2) {
-            __builtin_amdgcn_global_load_lds((SSD_GLOBAL void*)(a.wgt + mo), (SSD_LDS void*)(sM->w),
-                                             16, 0, 0);
-        } else if (kSeq) {
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<int32_t*>(a.seq_idx + it.b * a.L + t0), 0, valid * 4, kRawBufferWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(sM->seq), 16, 16 * lane, 0,
-                                                     0, 0);
-        }
-    }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int stride) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, rows * stride,
+                                             kRawBufferWord3);
 }
 
 // -------------------------------------------------------------- the kernel
 
 // Output row block of an output wave; for Q = 128 the two waves sharing a
-// SIMD (w, w + 4) get rows (k, 7 - k): equal triangular work per SIMD.
+// SIMD (w, w + 4) get rows (k, 7 - k).
 template <int NB>
 __device__ __forceinline__ int tr_row_block(int wave) {
     if constexpr (NB == 8) return wave < 4 ? wave : 11 - wave;
@@ -217,66 +189,124 @@ __device__ __forceinline__ int tr_row_block(int wave) {
 template <int P, int N, int Q, bool kOut, bool kSeq>
 struct TrScan {
     using G_ = TrGeo<P, N, Q>;
+    static constexpr int XI = G_::XBYTES / 1024 / kTrWaves;  // x-tile copy instructions per wave
+    static constexpr int BI = G_::BBYTES / 1024 / kTrWaves;  // B-tile copy instructions per wave
+    static_assert(XI >= 1 && BI >= 1 && G_::XBYTES % (1024 * kTrWaves) == 0 &&
+                      G_::BBYTES % (1024 * kTrWaves) == 0, "tile copy split");
+    static constexpr int NT = G_::NB * (G_::NB + 1) / 2;     // C.B^T tiles per (chunk, group)
 
     const ScanArgs& a;
-    WorkItem it;
     int wave, lane, r16, g;
-    int c_begin, c_end;
-    bool last_seg, st_wave, out_wave;
+    int c_begin, c_end, L, nc;
+    bool last_seg, want_final;
+    bool fast_;             // factored intra-chunk decays (every dt * A <= 0 in the segment)
+    bool st_wave_, out_wave_;
+    // every wave owns a state n-block / an output row block when there are 8
+    __device__ __forceinline__ bool st() const { return G_::NNB == kTrWaves || st_wave_; }
+    __device__ __forceinline__ bool ow() const { return kOut && (G_::NB == kTrWaves || out_wave_); }
     int I;                  // output row block of this wave
-    float Dh;               // skip weight D[h]
+    float Dh, Ah;           // D[h], A[h]
     int xoff[G_::PB], boff; // transposing-read lane offsets (x per p block, B of n block `wave`)
     int seq_prev;           // sequence id of the token before the current chunk
     float mult;             // decay of the segment (chunk-state kernel)
+    // per-(row, head) / per-(row, group) bases; chunk c adds c times the chunk stride
+    const uint16_t* xg;  int xstride;   // x[b][.][h][0], token stride in bytes
+    const uint16_t* bg;  int bstride;   // B[b][.][g][0]
+    const uint16_t* cg;                 // C[b][.][g][0] (stride bstride)
+    uint16_t* yg;                       // y[b][.][h][0]
+    const float* mg;                    // metadata block (b, h, chunk 0): [cs | dt | w]
+    const int32_t* sqg;                 // seq_idx[b][0]
+    const uint16_t* cbg;                // C.B^T tiles at (b, chunk 0, g)
+    int64_t cb_cstride;                 // elements between chunks of the tile buffer
 
     f32x4_t h[G_::PB];          // state rows n = 16 wave + 4g + r, column p = 16pb + r16
-    uint4 cr[2][G_::KN];        // C rows of the current / next chunk (k over n)
-    uint4 cb[2][G_::NCB];       // C.B^T tile pairs of the current / next chunk
+    uint4 cr[G_::KN];           // C rows of a chunk (k over n), loaded a chunk ahead
+    uint4 cb[G_::NCB];          // C.B^T tile pairs of a chunk, loaded a chunk ahead
     uint2 ypk[G_::PB];          // packed outputs awaiting their store
-    int64_t ypos;               // element offset of ypk[0]
+    uint16_t* ypos;
     bool ypend;
 
     __device__ __forceinline__ TrScan(const ScanArgs& args) : a(args) {}
 
-    __device__ __forceinline__ void load_c(int k, int c) {
-        const int64_t t0 = static_cast<int64_t>(c) * Q;
-        const int64_t rem = a.L - t0;
-        const int valid = rem < Q ? static_cast<int>(rem) : Q;
-        const int stride = a.G * N * 2;
-        const uint16_t* base = static_cast<const uint16_t*>(a.C) + ((it.b * a.L + t0) * a.G + it.g) * N;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(base), 0, valid * stride, kRawBufferWord3);
+    __device__ __forceinline__ int rows_in(int c) const {
+        const int64_t rem = static_cast<int64_t>(L) - static_cast<int64_t>(c) * Q;
+        return rem < Q ? static_cast<int>(rem) : Q;
+    }
+
+    __device__ __forceinline__ void load_c(int c) {
+        const __amdgpu_buffer_rsrc_t rs =
+            rows_rsrc(cg + static_cast<int64_t>(c) * Q * (bstride / 2), rows_in(c), bstride);
 #pragma unroll
         for (int s = 0; s < G_::KN; ++s) {
             const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, (16 * I + r16) * stride + (32 * s + 8 * g) * 2, 0, 0);
-            cr[k][s] = make_uint4(v[0], v[1], v[2], v[3]);
+                rs, (16 * I + r16) * bstride + (32 * s + 8 * g) * 2, 0, 0);
+            cr[s] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
 
-    __device__ __forceinline__ void load_cb(int k, int c) {
-        constexpr int NT = G_::NB * (G_::NB + 1) / 2;
-        const uint16_t* tiles = static_cast<const uint16_t*>(a.cbt) +
-                                ((it.b * a.nc + c) * a.G + it.g) * static_cast<int64_t>(NT) * 256;
+    __device__ __forceinline__ void load_cb(int c) {
+        const uint16_t* tiles = cbg + static_cast<int64_t>(c) * cb_cstride;
         const int first = I * (I + 1) / 2;
 #pragma unroll
         for (int u = 0; u < G_::NCB; ++u) {
             if (2 * u <= I) {
                 const int j1 = 2 * u + 1 <= I ? 2 * u + 1 : I;
-                const uint2 v0 = *reinterpret_cast<const uint2*>(
-                    tiles + (static_cast<int64_t>(first + 2 * u) * 64 + lane) * 4);
-                const uint2 v1 = *reinterpret_cast<const uint2*>(
-                    tiles + (static_cast<int64_t>(first + j1) * 64 + lane) * 4);
-                cb[k][u] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+                const uint2 v0 = *reinterpret_cast<const uint2*>(tiles + ((first + 2 * u) * 64 + lane) * 4);
+                const uint2 v1 = *reinterpret_cast<const uint2*>(tiles + ((first + j1) * 64 + lane) * 4);
+                cb[u] = make_uint4(v0.x, v0.y, v1.x, v1.y);
             }
         }
     }
 
-    // G^T fragment of k step u: lane column i = 16I + r16, tokens j in the
-    // k order above; G[i][j] = (C_i . B_j) exp(cs_i - cs_j) dt_j, masked to
-    // j <= i and (with sequence ids) seq_j = seq_i.
-    __device__ __forceinline__ Frag<uint16_t> g_frag(const uint4& t, const TrMeta<Q>& m, int u,
-                                                     int i, float cs_i, int seq_i) const {
+    // Copies of chunk c+1, split so that they spread over the chunk's math.
+    __device__ __forceinline__ void dma_x(char* sX, int c) const {
+        const __amdgpu_buffer_rsrc_t rs =
+            rows_rsrc(xg + static_cast<int64_t>(c) * Q * (xstride / 2), rows_in(c), xstride);
+        dma_rows<G_::XROW, XI>(sX, rs, xstride, 0, XI, wave, lane);
+    }
+    __device__ __forceinline__ void dma_b(char* sB, int c, int k0, int k1) const {
+        if (k0 < k1) {
+            const __amdgpu_buffer_rsrc_t rs =
+                rows_rsrc(bg + static_cast<int64_t>(c) * Q * (bstride / 2), rows_in(c), bstride);
+            dma_rows<G_::BROW, BI>(sB, rs, bstride, k0, k1, wave, lane);
+        }
+    }
+    // [cs | dt | w] of a chunk is one contiguous block of 3Q floats (Q * 3/4
+    // pieces of 16 bytes) in the workspace and in TrMeta.
+    __device__ __forceinline__ void dma_meta(TrMeta<Q>* sM, int c) const {
+        constexpr int NPC = 3 * Q / 4;       // 16-byte pieces
+        const int mw = kTrWaves - 1 - wave;  // from the last waves
+        const int piece = kWave * mw + lane;
+        if (kWave * mw < NPC && piece < NPC) {
+            const float* src = mg + static_cast<int64_t>(c) * (3 * Q) + 4 * piece;
+            float* dst = reinterpret_cast<float*>(sM) + 4 * kWave * mw;  // [cs | dt | w] in order
+            __builtin_amdgcn_global_load_lds((SSD_GLOBAL void*)(src), (SSD_LDS void*)(dst), 16, 0, 0);
+        }
+        if constexpr (kSeq) {
+            if (mw == (NPC + kWave - 1) / kWave && lane < Q / 4) {
+                const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sqg + static_cast<int64_t>(c) * Q, rows_in(c), 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(sM->seq), 16, 16 * lane, 0, 0, 0);
+            }
+        }
+    }
+    __device__ __forceinline__ void dma_all(char* sX, char* sB, TrMeta<Q>* sM, int c) const {
+        dma_x(sX, c);
+        dma_b(sB, c, 0, BI);
+        dma_meta(sM, c);
+    }
+
+    // G^T fragment of k step u, exact form: lane column i = 16I + r16, tokens
+    // j in the k order above; G[i][j] = (C_i . B_j) exp(cs_i - cs_j) dt_j,
+    // masked to j <= i and (with sequence ids) seq_j = seq_i; D[h] is added on
+    // the diagonal (the D x skip rides on the same MFMA).
+    __device__ __forceinline__ Frag<uint16_t> g_exact(const uint4& t, const TrMeta<Q>& m, int u,
+                                                      float cs_i, int seq_i) const {
+        // token 16J + 4g + r of tile J is kept when r <= lim: all of a tile left
+        // of the diagonal, r <= r16 - 4g on it, none right of it
+        int tdiag = r16 - 4 * g;
+        // opaque to the optimizer: keeps the per-element compares here instead
+        // of hoisting them out of the chunk loop as 64-bit lane masks
+        asm volatile("" : "+v"(tdiag));
         float out[8];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
@@ -291,110 +321,142 @@ struct TrScan {
             const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
             const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
             const int sqv[4] = {sq4.x, sq4.y, sq4.z, sq4.w};
+            const int lim = J < I ? 3 : (J == I ? tdiag : -1);
+            const int dlim = J == I ? tdiag : -1;  // D on the diagonal element
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                bool keep = J < I || (J == I && 4 * g + r <= r16);
+                bool keep = r <= lim;
                 if constexpr (kSeq) keep = keep && sqv[r] == seq_i;
-                const float v = cbv[r] * decay_exp(keep ? cs_i - csv[r] : 0.0f) * dtv[r];
-                out[4 * hp + r] = keep ? v : 0.0f;
+                // masked elements may overflow here; the select drops them
+                const float v = cbv[r] * decay_exp(cs_i - csv[r]) * dtv[r];
+                out[4 * hp + r] = (keep ? v : 0.0f) + (r == dlim ? Dh : 0.0f);
             }
         }
         return frag_from_f32<uint16_t>(out);
     }
 
+    // Factored form for k steps strictly left of row block I (all j < 16I):
+    // G[i][j] = r_i * (C_i . B_j) c_j with c_j = [seq_j = seq_m] exp(cs_m - cs_j) dt_j
+    // (m = 16I, from this wave's scratch) and the row factor r_i applied to the
+    // accumulator later.
+    __device__ __forceinline__ Frag<uint16_t> g_factored(const uint4& t, const float* cj, int u) const {
+        const float4 c0 = *reinterpret_cast<const float4*>(&cj[32 * u + 4 * g]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&cj[32 * u + 16 + 4 * g]);
+        const float v[8] = {bf_lo(t.x) * c0.x, bf_hi(t.x) * c0.y, bf_lo(t.y) * c0.z,
+                            bf_hi(t.y) * c0.w, bf_lo(t.z) * c1.x, bf_hi(t.z) * c1.y,
+                            bf_lo(t.w) * c1.z, bf_hi(t.w) * c1.w};
+        return frag_from_f32<uint16_t>(v);
+    }
+
     __device__ __forceinline__ void store_y() {
         if (ypend) {
-            uint16_t* y = static_cast<uint16_t*>(a.y) + ypos;
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) *reinterpret_cast<uint2*>(y + 16 * pb) = ypk[pb];
+            for (int pb = 0; pb < G_::PB; ++pb) *reinterpret_cast<uint2*>(ypos + 16 * pb) = ypk[pb];
         }
         ypend = false;
     }
 
     // One chunk.  On entry chunk c's tiles and metadata are in (X, Bt, M), the
     // state before it in H (bf16 operand copy) and h (fp32, state waves), and
-    // its C rows and C.B^T tiles in cr[K], cb[K].  Issues chunk c+1's loads
-    // into the other buffers, and leaves after a barrier with them complete.
+    // its C rows and C.B^T tiles in cr, cb.  Issues chunk c+1's loads
+    // into the other buffers while it works, and leaves after a barrier with
+    // them complete.
     template <int K>
     __device__ __forceinline__ void chunk(int c, const char* X, const char* Bt, const TrMeta<Q>* M,
                                           const char* H, char* Xn, char* Bn, TrMeta<Q>* Mn,
-                                          char* Hn) {
+                                          char* Hn, float* cj) {
         const bool has_next = c + 1 < c_end;
-        const int64_t t0 = static_cast<int64_t>(c) * Q;
-        const int64_t rem = a.L - t0;
-        const int valid = rem < Q ? static_cast<int>(rem) : Q;
-        const bool need_state = !kOut || has_next || (last_seg && a.final_states != nullptr);
+        const int valid = rows_in(c);
+        const TrMeta<Q>& m = *M;
 
         if constexpr (kOut) store_y();  // previous chunk's outputs
-        if (has_next) {
-            if constexpr (kOut) {
-                if (out_wave) {
-                    load_c(K ^ 1, c + 1);
-                    load_cb(K ^ 1, c + 1);
-                }
-            }
-            dma_chunk<P, N, Q, kSeq>(Xn, Bn, Mn, a, it, c + 1, wave, lane);
-        }
-        const TrMeta<Q>& m = *M;
         const float cs_last = m.cs[Q - 1];
         const int seq_last = kSeq ? m.seq[valid - 1] : 0;
 
-        // carried-state term of the outputs: y^T[p][i] = exp(cs_i) [seq_i = seq_prev] h.C_i
+        const bool fast = kOut && fast_;
         f32x4_t y[G_::PB];
         int i = 0;
-        float cs_i = 0.0f;
+        float cs_i = 0.0f, r_i = 1.0f;
         int seq_i = 0;
         if constexpr (kOut) {
-            if (out_wave) {
+            if (ow()) {
+                // carried-state term: y^T[p][i] = exp(cs_i) [seq_i = seq_prev] h.C_i,
+                // with exp(cs_i) = r_i exp(cs_m) in the factored form
                 i = 16 * I + r16;
+                const int m0 = 16 * I;
                 cs_i = m.cs[i];
-                if constexpr (kSeq) seq_i = m.seq[i];
+                const float cs_m = m.cs[m0];
+                int seq_m = 0;
+                if constexpr (kSeq) {
+                    seq_i = m.seq[i];
+                    seq_m = m.seq[m0];
+                }
+                Frag<uint16_t> hf[2][G_::PB];
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) y[pb] = acc_zero();
+                for (int pb = 0; pb < G_::PB; ++pb) {
+                    y[pb] = acc_zero();
+                    hf[0][pb] = frag_of(*reinterpret_cast<const uint4*>(H + h_off<G_::HROW>(16 * pb + r16, g)));
+                }
 #pragma unroll
                 for (int s = 0; s < G_::KN; ++s) {
-                    const Frag<uint16_t> cf = frag_of(cr[K][s]);
+                    if (s + 1 < G_::KN) {
 #pragma unroll
-                    for (int pb = 0; pb < G_::PB; ++pb) {
-                        const Frag<uint16_t> hf = frag_of(*reinterpret_cast<const uint4*>(
-                            H + h_off<G_::HROW>(16 * pb + r16, 4 * s + g)));
-                        mma(y[pb], hf, cf);
+                        for (int pb = 0; pb < G_::PB; ++pb)
+                            hf[(s + 1) & 1][pb] = frag_of(*reinterpret_cast<const uint4*>(
+                                H + h_off<G_::HROW>(16 * pb + r16, 4 * (s + 1) + g)));
+                    }
+                    const Frag<uint16_t> cf = frag_of(cr[s]);
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], hf[s & 1][pb], cf);
+                }
+                // fast: exp(cs_i) = r_i exp(cs_m); r_i is applied at the diagonal step
+                float sc = (!kSeq || seq_i == seq_prev) ? decay_exp(cs_i) : 0.0f;
+                r_i = 1.0f;
+                if (fast) {
+                    r_i = (!kSeq || seq_i == seq_m) ? decay_exp(cs_i - cs_m) : 0.0f;
+                    sc = (!kSeq || seq_m == seq_prev) ? decay_exp(cs_m) : 0.0f;
+                    // column factors of the steps left of the row block
+#pragma unroll
+                    for (int k = 0; k < (Q + kWave - 1) / kWave; ++k) {
+                        const int j = lane + kWave * k;
+                        if (j < m0) {
+                            bool keep = true;
+                            if constexpr (kSeq) keep = m.seq[j] == seq_m;
+                            cj[j] = keep ? decay_exp(cs_m - m.cs[j]) * m.dt[j] : 0.0f;
+                        }
                     }
                 }
-                const bool keep = !kSeq || seq_i == seq_prev;
-                const float e = decay_exp(cs_i);
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = y[pb][r] * e;
-                        y[pb][r] = keep ? v : 0.0f;
-                    }
+                    for (int r = 0; r < 4; ++r) y[pb][r] *= sc;
             }
+        }
+        if (has_next) {
+            if constexpr (kOut) {
+                if (ow()) load_c(c + 1);  // this chunk's C rows are consumed
+            }
+            dma_x(Xn, c + 1);
         }
 
         // h_c = [no reset in c] exp(cs_last) h_{c-1} + S_c
         {
-            const bool keep = !kSeq || seq_last == seq_prev;
-            const float e = decay_exp(cs_last);
-            if (need_state && st_wave) {
+            const float e = (!kSeq || seq_last == seq_prev) ? decay_exp(cs_last) : 0.0f;
+            if (st()) {
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = h[pb][r] * e;
-                        h[pb][r] = keep ? v : 0.0f;
-                    }
+                    for (int r = 0; r < 4; ++r) h[pb][r] *= e;
             }
-            if constexpr (!kOut) mult = keep ? mult * e : 0.0f;
+            if constexpr (!kOut) mult *= e;
         }
 
-        // k steps over the chunk's tokens: S_c += (B w)^T x, and the
+        // k steps over the chunk's tokens: S_c += (B w)^T x and the
         // intra-chunk outputs y^T += x^T G^T, sharing the x fragments
 #pragma unroll
         for (int s = 0; s < G_::KQ; ++s) {
-            const bool do_state = need_state && st_wave;
-            const bool do_out = kOut && out_wave && 2 * s <= I;
+            const bool do_state = st();
+            const bool do_out = kOut && ow() && 2 * s <= I;
             if (do_state || do_out) {
                 Frag<uint16_t> xf[G_::PB];
 #pragma unroll
@@ -408,31 +470,45 @@ struct TrScan {
                 }
                 if constexpr (kOut) {
                     if (do_out) {
-                        const Frag<uint16_t> gf = g_frag(cb[K][s], m, s, i, cs_i, seq_i);
+                        Frag<uint16_t> gf;
+                        if (fast && 2 * s + 1 < I) {
+                            gf = g_factored(cb[s], cj, s);
+                        } else {
+                            if (2 * s + 2 > I) {
+                                // the diagonal step (last): apply the row factor first
+#pragma unroll
+                                for (int pb = 0; pb < G_::PB; ++pb)
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r) y[pb][r] *= r_i;
+                            }
+                            gf = g_exact(cb[s], m, s, cs_i, seq_i);
+                        }
 #pragma unroll
                         for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], xf[pb], gf);
                     }
                 }
             }
+            // spread the next chunk's copies over the steps
+            if (has_next) {
+                dma_b(Bn, c + 1, BI * s / G_::KQ, BI * (s + 1) / G_::KQ);
+                if (s == 0) dma_meta(Mn, c + 1);
+                if constexpr (kOut) {
+                    if (s == G_::KQ - 1 && ow()) load_cb(c + 1);  // after the last use
+                }
+            }
         }
 
         if constexpr (kOut) {
-            if (out_wave) {
-                // D x skip, then pack; the store waits for the next chunk
+            if (ow()) {
+                ypk[0] = make_uint2(0, 0);
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) {
-                    const uint2 xv = *reinterpret_cast<const uint2*>(
-                        X + tr_off<G_::XROW>(i, 32 * pb + 8 * g));
-                    const float x0 = bf_lo(xv.x), x1 = bf_hi(xv.x);
-                    const float x2 = bf_lo(xv.y), x3 = bf_hi(xv.y);
-                    ypk[pb] = make_uint2(pack_bf16x2(fmaf(Dh, x0, y[pb][0]), fmaf(Dh, x1, y[pb][1])),
-                                         pack_bf16x2(fmaf(Dh, x2, y[pb][2]), fmaf(Dh, x3, y[pb][3])));
-                }
-                ypos = ((it.b * a.L + t0 + i) * a.H + it.h) * P + 4 * g;
+                for (int pb = 0; pb < G_::PB; ++pb)
+                    ypk[pb] = make_uint2(pack_bf16x2(y[pb][0], y[pb][1]), pack_bf16x2(y[pb][2], y[pb][3]));
+                ypos = yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2) + 4 * g;
                 ypend = i < valid;
             }
             // bf16 operand copy of h_c for the next chunk's carried-state term
-            if (has_next && st_wave) {
+            if (has_next && st()) {
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb) {
                     const int p = 16 * pb + r16;
@@ -447,10 +523,19 @@ struct TrScan {
         __syncthreads();
     }
 
+    template <bool kFast>
+    __device__ __forceinline__ void loop(char* sX0, char* sB0, TrMeta<Q>* sM0, char* sH0,
+                                         char* sX1, char* sB1, TrMeta<Q>* sM1, char* sH1,
+                                         float* cj) {
+        for (int c = c_begin; c < c_end; c += 2) {
+            chunk<0, kFast>(c, sX0, sB0, sM0, sH0, sX1, sB1, sM1, sH1, cj);
+            if (c + 1 < c_end) chunk<1, kFast>(c + 1, sX1, sB1, sM1, sH1, sX0, sB0, sM0, sH0, cj);
+        }
+    }
     __device__ __forceinline__ void state_load(const float* __restrict__ src) {
 #pragma unroll
         for (int pb = 0; pb < G_::PB; ++pb) {
-            if (src && st_wave) {
+            if (src && st()) {
                 const float4 v = *reinterpret_cast<const float4*>(src + (16 * pb + r16) * N +
                                                                   16 * wave + 4 * g);
                 h[pb] = f32x4_t{v.x, v.y, v.z, v.w};
@@ -461,13 +546,115 @@ struct TrScan {
     }
 
     __device__ __forceinline__ void state_store(float* __restrict__ dst) const {
-        if (!st_wave) return;
+        if (!st()) return;
 #pragma unroll
         for (int pb = 0; pb < G_::PB; ++pb)
             *reinterpret_cast<float4*>(dst + (16 * pb + r16) * N + 16 * wave + 4 * g) =
                 make_float4(h[pb][0], h[pb][1], h[pb][2], h[pb][3]);
     }
 };
+
+// LDS of one workgroup (separate objects per buffer: the compiler then knows
+// that reads of one buffer do not wait for copies into the other).
+template <int P, int N, int Q, bool kOut>
+struct TrLds {
+    using G_ = TrGeo<P, N, Q>;
+    char* x[2];
+    char* b[2];
+    TrMeta<Q>* m[2];
+    char* h[2];
+    float* cj;
+};
+
+// One (row, head, segment) from set-up to the final stores.  fast: every
+// dt * A of the segment is <= 0 (see the kernel).
+template <int P, int N, int Q, bool kOut, bool kSeq>
+__device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s,
+                                            bool fast) {
+    using G_ = TrGeo<P, N, Q>;
+    TrScan<P, N, Q, kOut, kSeq> k(a);
+    k.fast_ = fast;
+    const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
+    k.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    k.lane = static_cast<int>(threadIdx.x) % kWave;
+    k.r16 = k.lane & 15;
+    k.g = k.lane >> 4;
+    k.L = static_cast<int>(a.L);
+    k.nc = a.nc;
+    k.c_begin = it.seg * a.cps;
+    k.c_end = min(k.c_begin + a.cps, a.nc);
+    k.last_seg = kOut && it.seg == a.nseg - 1;
+    k.want_final = k.last_seg && a.final_states != nullptr;
+    k.st_wave_ = k.wave < G_::NNB;
+    k.out_wave_ = kOut && k.wave < G_::NB;
+    k.I = tr_row_block<G_::NB>(k.wave);
+    k.Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
+    k.Ah = a.A[it.h];
+#pragma unroll
+    for (int pb = 0; pb < G_::PB; ++pb) k.xoff[pb] = tr_lane_off<G_::XROW>(pb, k.lane);
+    k.boff = tr_lane_off<G_::BROW>(k.st() ? k.wave : 0, k.lane);
+    k.mult = 1.0f;
+    k.ypend = false;
+    k.ypos = nullptr;
+    k.xstride = a.H * P * 2;
+    k.bstride = a.G * N * 2;
+    k.xg = static_cast<const uint16_t*>(a.x) + (it.b * a.L * a.H + it.h) * P;
+    k.bg = static_cast<const uint16_t*>(a.B) + (it.b * a.L * a.G + it.g) * N;
+    k.cg = static_cast<const uint16_t*>(a.C) + (it.b * a.L * a.G + it.g) * N;
+    k.yg = static_cast<uint16_t*>(a.y) + (it.b * a.L * a.H + it.h) * P;
+    k.mg = a.cs + meta_offset(a, it.b, it.h, 0, Q);
+    k.sqg = a.seq_idx ? a.seq_idx + it.b * a.L : nullptr;
+    k.cb_cstride = static_cast<int64_t>(a.G) * TrScan<P, N, Q, kOut, kSeq>::NT * 256;
+    k.cbg = static_cast<const uint16_t*>(a.cbt) + (it.b * a.nc * a.G + it.g) * (k.cb_cstride / a.G);
+    const int64_t bh = it.b * a.H + it.h;
+    if constexpr (kSeq) {
+        const int64_t tp = k.c_begin == 0 ? 0 : static_cast<int64_t>(k.c_begin) * Q - 1;
+        k.seq_prev = a.seq_idx[it.b * a.L + tp];
+    } else {
+        k.seq_prev = 0;
+    }
+    float* cj = s.cj + (kOut ? k.wave * Q : 0);
+
+    // incoming state: fp32 in registers, bf16 operand copy in h[0]
+    if constexpr (kOut) {
+        if (a.nseg == 1) k.state_load(a.init ? a.init + bh * P * N : nullptr);
+        else k.state_load(a.seg_state + (bh * a.nseg + it.seg) * P * N);
+        if (k.st()) {
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb) {
+                const int p = 16 * pb + k.r16;
+                *reinterpret_cast<uint2*>(s.h[0] + h_off<G_::HROW>(p, 2 * k.wave + (k.g >> 1)) +
+                                          8 * (k.g & 1)) =
+                    make_uint2(pack_bf16x2(k.h[pb][0], k.h[pb][1]), pack_bf16x2(k.h[pb][2], k.h[pb][3]));
+            }
+        }
+        if (k.ow()) {
+            k.load_c(k.c_begin);
+            k.load_cb(k.c_begin);
+        }
+    } else {
+        k.state_load(nullptr);
+    }
+    k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    for (int c = k.c_begin; c < k.c_end; c += 2) {
+        k.template chunk<0>(c, s.x[0], s.b[0], s.m[0], s.h[0], s.x[1], s.b[1], s.m[1], s.h[1], cj);
+        if (c + 1 < k.c_end)
+            k.template chunk<1>(c + 1, s.x[1], s.b[1], s.m[1], s.h[1], s.x[0], s.b[0], s.m[0],
+                                       s.h[0], cj);
+    }
+
+    if constexpr (kOut) {
+        k.store_y();
+        if (k.want_final) k.state_store(a.final_states + bh * P * N);
+    } else {
+        const int64_t slot = bh * a.nseg + it.seg;
+        k.state_store(a.seg_state + slot * P * N);
+        if (threadIdx.x == 0) a.seg_mult[slot] = k.mult;
+    }
+}
 
 // The chunked scan over one (row, head, segment), as chunk_scan_kernel:
 //   kOut = false: end states of segments 0 .. nseg-2 (from a zero state) and
@@ -485,70 +672,25 @@ __global__ __launch_bounds__(kTrThreads) void scan_tr_kernel(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) TrMeta<Q> sM1;
     __shared__ __attribute__((aligned(16))) char sH0[kOut ? G_::HBYTES : 16];
     __shared__ __attribute__((aligned(16))) char sH1[kOut ? G_::HBYTES : 16];
-
-    TrScan<P, N, Q, kOut, kSeq> k(a);
-    k.it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
-    k.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    k.lane = static_cast<int>(threadIdx.x) % kWave;
-    k.r16 = k.lane & 15;
-    k.g = k.lane >> 4;
-    k.c_begin = k.it.seg * a.cps;
-    k.c_end = min(k.c_begin + a.cps, a.nc);
-    k.last_seg = kOut && k.it.seg == a.nseg - 1;
-    k.st_wave = k.wave < G_::NNB;
-    k.out_wave = kOut && k.wave < G_::NB;
-    k.I = tr_row_block<G_::NB>(k.wave);
-    k.Dh = (kOut && a.D) ? a.D[k.it.h] : 0.0f;
-#pragma unroll
-    for (int pb = 0; pb < G_::PB; ++pb) k.xoff[pb] = tr_lane_off<G_::XROW>(pb, k.lane);
-    k.boff = tr_lane_off<G_::BROW>(k.st_wave ? k.wave : 0, k.lane);
-    k.mult = 1.0f;
-    k.ypend = false;
-    k.ypos = 0;
-    const int64_t bh = k.it.b * a.H + k.it.h;
-    if constexpr (kSeq) {
-        const int64_t tp = k.c_begin == 0 ? 0 : static_cast<int64_t>(k.c_begin) * Q - 1;
-        k.seq_prev = a.seq_idx[k.it.b * a.L + tp];
-    } else {
-        k.seq_prev = 0;
-    }
-
-    // incoming state: fp32 in registers, bf16 operand copy in sH0
-    if constexpr (kOut) {
-        if (a.nseg == 1) k.state_load(a.init ? a.init + bh * P * N : nullptr);
-        else k.state_load(a.seg_state + (bh * a.nseg + k.it.seg) * P * N);
-        if (k.st_wave) {
-#pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) {
-                const int p = 16 * pb + k.r16;
-                *reinterpret_cast<uint2*>(sH0 + h_off<G_::HROW>(p, 2 * k.wave + (k.g >> 1)) +
-                                          8 * (k.g & 1)) =
-                    make_uint2(pack_bf16x2(k.h[pb][0], k.h[pb][1]), pack_bf16x2(k.h[pb][2], k.h[pb][3]));
-            }
-        }
-        if (k.out_wave) {
-            k.load_c(0, k.c_begin);
-            k.load_cb(0, k.c_begin);
-        }
-    } else {
-        k.state_load(nullptr);
-    }
-    dma_chunk<P, N, Q, kSeq>(sX0, sB0, &sM0, a, k.it, k.c_begin, k.wave, k.lane);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-
-    for (int c = k.c_begin; c < k.c_end; c += 2) {
-        k.template chunk<0>(c, sX0, sB0, &sM0, sH0, sX1, sB1, &sM1, sH1);
-        if (c + 1 < k.c_end) k.template chunk<1>(c + 1, sX1, sB1, &sM1, sH1, sX0, sB0, &sM0, sH0);
-    }
+    __shared__ __attribute__((aligned(16))) float sCj[kOut ? kTrWaves * Q : 4];
+    const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1}, {&sM0, &sM1}, {sH0, sH1}, sCj};
 
     if constexpr (kOut) {
-        k.store_y();
-        if (k.last_seg && a.final_states) k.state_store(a.final_states + bh * P * N);
+        // The factored form of the intra-chunk decays needs dt_j * A <= 0 for
+        // every token of the segment (cs then never increases inside a
+        // sequence and every factor is at most 1); otherwise every k step takes
+        // the exact form.
+        const WorkItem it = decode_work(a, a.nseg);
+        const int c0 = it.seg * a.cps, c1 = min(c0 + a.cps, a.nc);
+        const float Ah = a.A[it.h];
+        const float* blk = a.cs + meta_offset(a, it.b, it.h, c0, Q);
+        const int n = (c1 - c0) * Q;
+        int up = 0;
+        for (int j = static_cast<int>(threadIdx.x); j < n; j += kTrThreads)
+            up |= blk[(j / Q) * (3 * Q) + Q + j % Q] * Ah > 0.0f;  // dt of token j
+        scan_tr_run<P, N, Q, true, kSeq>(a, lds, __syncthreads_or(up) == 0);
     } else {
-        const int64_t slot = bh * a.nseg + k.it.seg;
-        k.state_store(a.seg_state + slot * P * N);
-        if (threadIdx.x == 0) a.seg_mult[slot] = k.mult;
+        scan_tr_run<P, N, Q, false, kSeq>(a, lds, false);
     }
 }
 

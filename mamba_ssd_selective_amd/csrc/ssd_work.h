@@ -37,9 +37,10 @@ __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid
     return it;
 }
 
-// Offset of chunk c of (row b, head h) in the per-token metadata workspaces.
+// Offset of chunk c of (row b, head h) from each of the metadata pointers
+// (cs, dtv, wgt): blocks of 3Q floats.
 __device__ __forceinline__ int64_t meta_offset(const ScanArgs& a, int64_t b, int h, int c, int Q) {
-    return ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(Q);
+    return ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(3 * Q);
 }
 
 }  // namespace ssd
