@@ -31,6 +31,7 @@ METRIC = "SSD scan tokens/s (bf16, H=64,P=64,N=128) and % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20
+COPY_BYTES = 1 << 30  # calibration copy, 4x the MALL
 WORKLOADS_BY_NAME = {"prefill_8k": 1, "packed_16k": 2, "long_128k": 3}
 
 
@@ -94,30 +95,32 @@ class Hip:
 
 def cpu_baseline(p, w, budget_s):
     """The fp64 oracle (as it stands) on the host cores, on a bounded sample of
-    the same workload: all L tokens of blocks of heads, until the budget is
-    spent; tokens/s scaled to the whole workload (all heads)."""
+    the same workload: all L tokens of blocks of heads, cycling over the heads
+    until the time budget is spent; tokens/s of the whole workload (all heads)."""
     import numpy as np
     import oracle
     threads = oracle.max_threads()
     H = w.nheads
     block = max(8, min(H, threads))
     hpg = H // w.ngroups
-    done = 0
+    head_tokens = 0  # tokens x heads processed
     t0 = time.perf_counter()
-    while done < H and time.perf_counter() - t0 < budget_s:
-        heads = np.arange(done, min(H, done + block))
+    start = 0
+    while time.perf_counter() - t0 < budget_s:
+        heads = (start + np.arange(block)) % H
         groups = heads // hpg
         oracle.scan(p["x"][:, :, heads], p["dt_raw"][:, :, heads], p["A"][heads],
                     p["B"][:, :, groups], p["C"][:, :, groups], dt_bias=p["dt_bias"][heads],
                     D=p["D"][heads], h_init=None if p.get("h_init") is None else p["h_init"][:, heads],
                     seq_idx=p.get("seq_idx"))
-        done += len(heads)
+        head_tokens += w.batch * w.seqlen * len(heads)
+        start = (start + block) % H
     el = time.perf_counter() - t0
-    tokens_per_s = w.batch * w.seqlen * (done / H) / el
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%s: all %d tokens x %d of %d heads (fp64 sequential recurrence, "
-                      "OpenMP over heads), %.1f s; scaled by %d/%d heads"
-                      % (w.name, w.seqlen, done, H, el, done, H)}
+    return {"value": head_tokens / H / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s: all %d tokens of blocks of %d heads, cycling over the %d heads for "
+                      "%.1f s (%.1f passes over all heads; fp64 sequential recurrence, OpenMP "
+                      "over heads); tokens/s of the whole workload"
+                      % (w.name, w.seqlen, block, H, el, head_tokens / (w.batch * w.seqlen * H))}
 
 
 def main():
@@ -126,8 +129,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS_BY_NAME))
-    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (for scaling HBM "
+                         "byte counters) and print its size")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -137,6 +143,17 @@ def main():
 
     import numpy as np
     import torch
+    if args.calibrate_copy:
+        # a plain copy of COPY_BYTES, five times: rocprofv3 FETCH_SIZE / WRITE_SIZE of
+        # this kernel give the counter-to-bytes factor (each launch reads and writes
+        # COPY_BYTES; the buffers are larger than the 256 MB MALL)
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": COPY_BYTES, "launches": 5}), flush=True)
+        return
     import mamba_ssd_selective_amd as ssd
     import workloads
 

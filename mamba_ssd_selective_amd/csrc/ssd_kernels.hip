@@ -60,7 +60,6 @@ struct Cfg {
     static constexpr int SX = Q + PAD;             // x^T rows         [P][SX]
     static constexpr int SH = NP + PAD;            // h (operand) rows [P][SH]
     static constexpr int NB = Q / 16;              // 16-token blocks
-    static constexpr int NT = NB * (NB + 1) / 2;   // lower-triangular C.B^T tiles
     static constexpr int PB = P / 16;              // 16-column blocks of P
     static constexpr int NNB = N / 16;             // 16-row blocks of the state's n
     static constexpr int KN = NP / 32;             // k steps over n
@@ -217,22 +216,28 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     }
     __syncthreads();
 
-    // ---- C.B^T tiles
+    // ---- C.B^T tiles, in pairs (layout at cb_pair_base); half-tile k of pair
+    // p is tile (I, 2u + k), zeros when 2u + k > I
     T* __restrict__ out = static_cast<T*>(a.cbt) +
-                          ((b * a.nc + c) * a.G + g) * static_cast<int64_t>(C_::NT) * 64 * 4;
+                          ((b * a.nc + c) * a.G + g) * cbt_elems_per_chunk_group(Q);
     const int r16 = lane & 15, q = lane >> 4;
-    for (int tile = wave; tile < C_::NT; tile += kWaves) {
+    constexpr int NPAIR = C_::NB / 2 * (C_::NB / 2 + 1);
+    for (int half = wave; half < 2 * NPAIR; half += kWaves) {
+        const int pidx = half >> 1;
         int I = 0;
-        while ((I + 1) * (I + 2) / 2 <= tile) ++I;
-        const int J = tile - I * (I + 1) / 2;
+        while (cb_pair_base(I + 1) <= pidx) ++I;
+        const int J = 2 * (pidx - cb_pair_base(I)) + (half & 1);
         f32x4_t acc = acc_zero();
+        if (J <= I) {
 #pragma unroll
-        for (int s = 0; s < C_::KN; ++s) {
-            const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
-            const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
-            mma(acc, bf, cf);
+            for (int s = 0; s < C_::KN; ++s) {
+                const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
+                const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
+                mma(acc, bf, cf);
+            }
         }
-        store4_f32(out + (static_cast<int64_t>(tile) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
+        store4_f32(out + (static_cast<int64_t>(pidx) * 64 + lane) * 8 + 4 * (half & 1), acc[0],
+                   acc[1], acc[2], acc[3]);
     }
 }
 
@@ -559,24 +564,15 @@ __device__ __forceinline__ void load_row_ops(RowOps<T, P, N, Q>& ro, const ScanA
         else ro.xd[pb] = ld_raw16(px);
     }
     const T* __restrict__ tiles = static_cast<const T*>(a.cbt) +
-                                  ((it.b * a.nc + c) * a.G + it.g) * static_cast<int64_t>(C_::NT) * 256;
-    const int first = I * (I + 1) / 2;  // tile (I, 0)
+                                  ((it.b * a.nc + c) * a.G + it.g) * cbt_elems_per_chunk_group(Q);
+    const int first = cb_pair_base(I);  // pair (I, 0)
 #pragma unroll
     for (int u = 0; u <= C_::NB / 2; ++u) {
-        // tiles (I, 2u) and (I, 2u+1), clamped into this row's tiles
-        int j0 = 2 * u, j1 = 2 * u + 1;
-        j0 = j0 <= I ? j0 : I;
-        j1 = j1 <= I ? j1 : I;
-        const T* p0 = tiles + (static_cast<int64_t>(first + j0) * 64 + lane) * 4;
-        const T* p1 = tiles + (static_cast<int64_t>(first + j1) * 64 + lane) * 4;
-        if constexpr (sizeof(T) == 2) {
-            const uint2 v0 = *reinterpret_cast<const uint2*>(p0);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(p1);
-            ro.cb[u][0] = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        } else {
-            ro.cb[u][0] = ld_raw16(p0);
-            ro.cb[u][1] = ld_raw16(p1);
-        }
+        // tile pair (I, 2u), (I, 2u+1), clamped into this row's pairs
+        const int uu = u <= I / 2 ? u : I / 2;
+        const T* p0 = tiles + (static_cast<int64_t>(first + uu) * 64 + lane) * 8;
+        ro.cb[u][0] = ld_raw16(p0);
+        if constexpr (sizeof(T) == 4) ro.cb[u][1] = ld_raw16(p0 + 4);
     }
 }
 

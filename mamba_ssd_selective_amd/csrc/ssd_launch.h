@@ -71,10 +71,19 @@ struct ScanVariant {
     ScanLaunchFn chunk_output;  // outputs with the carried state
 };
 
+// C.B^T tiles of one (row, chunk, group): for every 16-token row block I and
+// u = 0 .. I/2 one tile pair (I, 2u), (I, 2u+1), stored lane by lane as
+// [pair][lane][8 elements] (elements 0..3 from tile 2u, 4..7 from tile 2u+1,
+// zeros where 2u+1 > I), so that one 16-byte (bf16) load per lane fetches a
+// whole MFMA k step.  Pairs of row block I start at pair index cb_pair_base(I).
+__host__ __device__ inline int cb_pair_base(int I) {
+    const int h = I >> 1;
+    return h * (h + 1) + ((I & 1) ? h + 1 : 0);
+}
+
 // Elements of io type in the C.B^T tile buffer of one (row, chunk, group).
-inline int64_t cbt_elems_per_chunk_group(int64_t Q) {
-    const int64_t nb = Q / 16;
-    return nb * (nb + 1) / 2 * 64 * 4;
+__host__ __device__ inline int64_t cbt_elems_per_chunk_group(int64_t Q) {
+    return static_cast<int64_t>(cb_pair_base(static_cast<int>(Q / 16))) * 64 * 8;
 }
 
 // bf16 scan kernels built on direct-to-LDS staging and transposing LDS reads

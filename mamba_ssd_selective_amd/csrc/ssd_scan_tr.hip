@@ -193,7 +193,6 @@ struct TrScan {
     static constexpr int BI = G_::BBYTES / 1024 / kTrWaves;  // B-tile copy instructions per wave
     static_assert(XI >= 1 && BI >= 1 && G_::XBYTES % (1024 * kTrWaves) == 0 &&
                       G_::BBYTES % (1024 * kTrWaves) == 0, "tile copy split");
-    static constexpr int NT = G_::NB * (G_::NB + 1) / 2;     // C.B^T tiles per (chunk, group)
 
     const ScanArgs& a;
     int wave, lane, r16, g;
@@ -246,16 +245,10 @@ struct TrScan {
 
     __device__ __forceinline__ void load_cb(int c) {
         const uint16_t* tiles = cbg + static_cast<int64_t>(c) * cb_cstride;
-        const int first = I * (I + 1) / 2;
+        const int first = cb_pair_base(I);
 #pragma unroll
-        for (int u = 0; u < G_::NCB; ++u) {
-            if (2 * u <= I) {
-                const int j1 = 2 * u + 1 <= I ? 2 * u + 1 : I;
-                const uint2 v0 = *reinterpret_cast<const uint2*>(tiles + ((first + 2 * u) * 64 + lane) * 4);
-                const uint2 v1 = *reinterpret_cast<const uint2*>(tiles + ((first + j1) * 64 + lane) * 4);
-                cb[u] = make_uint4(v0.x, v0.y, v1.x, v1.y);
-            }
-        }
+        for (int u = 0; u < G_::NCB; ++u)
+            if (2 * u <= I) cb[u] = *reinterpret_cast<const uint4*>(tiles + ((first + u) * 64 + lane) * 8);
     }
 
     // Copies of chunk c+1, split so that they spread over the chunk's math.
@@ -604,7 +597,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.yg = static_cast<uint16_t*>(a.y) + (it.b * a.L * a.H + it.h) * P;
     k.mg = a.cs + meta_offset(a, it.b, it.h, 0, Q);
     k.sqg = a.seq_idx ? a.seq_idx + it.b * a.L : nullptr;
-    k.cb_cstride = static_cast<int64_t>(a.G) * TrScan<P, N, Q, kOut, kSeq>::NT * 256;
+    k.cb_cstride = static_cast<int64_t>(a.G) * cbt_elems_per_chunk_group(Q);
     k.cbg = static_cast<const uint16_t*>(a.cbt) + (it.b * a.nc * a.G + it.g) * (k.cb_cstride / a.G);
     const int64_t bh = it.b * a.H + it.h;
     if constexpr (kSeq) {

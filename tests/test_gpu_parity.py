@@ -95,6 +95,29 @@ def test_bf16_parity(case):
     _check_case(p, "bf16", Q, "bf16 %s" % (case,))
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_mixed_sign_decay_exponent(packed):
+    """dt without softplus and of mixed sign: some dt * A > 0, so the output
+    kernel cannot factor its intra-chunk decays and every step takes the exact
+    per-element form."""
+    b, L, H, P, N, G, Q = 1, 600, 8, 64, 128, 2, 128
+    rng = np.random.default_rng(4242 + packed)
+    p = workloads.random_problem(rng, b, L, H, P, N, G, io="bf16", init=True)
+    p["dt_raw"] = (0.05 + 0.04 * rng.standard_normal((b, L, H))).astype(np.float32)
+    p["dt_bias"] = np.zeros(H, dtype=np.float32)
+    assert (p["dt_raw"] < 0).any()
+    if packed:
+        p["seq_idx"] = _packed(rng, b, L, 4)
+    t = to_dev(p, "bf16")
+    for zero_D in (False, True):
+        y, fs = run_scan(t, Q, zero_D=zero_D, dt_softplus=False)
+        yr, hr = run_oracle(p, zero_D=zero_D, dt_softplus=False)
+        ey, eh = oracle.rel_l2(host(y), yr), oracle.rel_l2(host(fs), hr)
+        log("mixed-sign dt packed=%s D=%s: rel_l2 y=%.3e final=%.3e"
+            % (packed, "0" if zero_D else "D", ey, eh))
+        assert ey < tol("bf16") and eh < tol("bf16"), (packed, zero_D, ey, eh)
+
+
 @pytest.mark.parametrize("Q", [64, 128, 256])
 def test_chunk_size_sweep_config1_shapes(Q):
     """Results are independent of the chunk size (within tolerance) at the
