@@ -146,7 +146,7 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
  * handles the caller created; the library only records them.  Kernel order
  * of the scan: chunk_prep, [chunk_state, state_pass,] chunk_output (the two bracketed
  * kernels run only when ssd_chunk_scan_segments(...) > 1; L = 0 launches one
- * state copy).
+ * state copy).  A NULL pair events[2k], events[2k+1] skips kernel k.
  * Pass events = NULL to turn the hooks off. */
 void ssd_set_timing_events(void* const* events, int count, int* launched);
 

@@ -85,7 +85,8 @@ thread_local TimingHooks g_hooks;
 // Runs one launch between the k-th pair of timing events (when hooks are set).
 template <typename F>
 hipError_t timed_launch(int& k, hipStream_t st, F&& launch) {
-    const bool rec = g_hooks.events && 2 * k + 1 < g_hooks.count;
+    const bool rec = g_hooks.events && 2 * k + 1 < g_hooks.count && g_hooks.events[2 * k] &&
+                     g_hooks.events[2 * k + 1];
     if (rec) (void)hipEventRecord(static_cast<hipEvent_t>(g_hooks.events[2 * k]), st);
     hipError_t e = launch();
     if (rec) (void)hipEventRecord(static_cast<hipEvent_t>(g_hooks.events[2 * k + 1]), st);

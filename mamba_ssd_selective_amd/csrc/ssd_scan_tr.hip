@@ -38,8 +38,19 @@
 namespace ssd {
 namespace {
 
-constexpr int kTrThreads = 512;
-constexpr int kTrWaves = kTrThreads / kWave;
+// Row blocks and state n-blocks are at most 8 per chunk.  The segment-state
+// kernel runs 8 waves, each owning one state n-block; the output kernel runs
+// 12: waves 0-7 own one output row block each, waves 8-11 two state n-blocks
+// each, so that the state chain and the output products of a chunk proceed on
+// different waves of each SIMD (three waves per SIMD).
+constexpr int kTrWaves = 8;
+template <bool kOut>
+struct TrWaves {
+    static constexpr int W = kOut ? 12 : 8;
+    static constexpr int kThreads = W * kWave;
+    static constexpr int NBW = kOut ? 2 : 1;  // state n-blocks per state wave
+    static constexpr int first_state = kOut ? 8 : 0;
+};
 // Word 3 of a raw (unswizzled, untyped) buffer resource on gfx9-family GPUs.
 constexpr int kRawBufferWord3 = 0x00020000;
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
@@ -101,9 +112,43 @@ __device__ __forceinline__ int h_off(int p, int slot) {
     return p * HROW + ((slot ^ x) << 4);
 }
 
-__device__ __forceinline__ uint2 ds_tr16(const char* p) {
-    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSD_LDS i16x4_t*)(p));
+// LDS accesses at 32-bit LDS byte addresses.  Lane-dependent addresses are
+// computed once per workgroup and kept opaque to the optimizer (lds_keep), so
+// that every access in the chunk loop is one instruction with an immediate
+// offset instead of re-deriving its address.  Each access is formed inside
+// the __shared__ object it touches (lds_at): the compiler then still knows
+// that it does not alias copies in flight into the other buffers, and inserts
+// no wait for them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<size_t>((const SSD_LDS char*)p));
+}
+__device__ __forceinline__ uint32_t lds_keep(uint32_t a) {
+    asm volatile("" : "+v"(a));
+    return a;
+}
+// Pointer into the LDS object `obj` at absolute LDS address a (inside obj).
+__device__ __forceinline__ const SSD_LDS char* lds_at(const void* obj, uint32_t a) {
+    return (const SSD_LDS char*)obj + (a - lds_addr(obj));
+}
+__device__ __forceinline__ uint2 ds_tr16(const void* obj, uint32_t a) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSD_LDS i16x4_t*)lds_at(obj, a));
     return __builtin_bit_cast(uint2, v);
+}
+// Loads and stores of 4-, 8- and 16-byte values (as plain vectors of words).
+template <int BYTES> struct LdsWords;
+template <> struct LdsWords<4> { typedef uint32_t type; };
+template <> struct LdsWords<8> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
+template <> struct LdsWords<16> { typedef unsigned int type __attribute__((ext_vector_type(4))); };
+template <typename T>
+__device__ __forceinline__ T lds_ld(const void* obj, uint32_t a) {
+    typedef typename LdsWords<sizeof(T)>::type W;
+    const W w = *(const SSD_LDS W*)lds_at(obj, a);
+    return __builtin_bit_cast(T, w);
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(void* obj, uint32_t a, const T& v) {
+    typedef typename LdsWords<sizeof(T)>::type W;
+    *(SSD_LDS W*)lds_at(obj, a) = __builtin_bit_cast(W, v);
 }
 
 // Lane byte offset of the transposing read of column block mb at k step 0.
@@ -120,9 +165,9 @@ __device__ __forceinline__ int tr_lane_off(int mb, int lane) {
 // Operand fragment of k step s from a [token][column] tile.  The swizzle of
 // rows r, r + 16 and r + 32s is the same, so steps are plain row offsets.
 template <int ROW>
-__device__ __forceinline__ Frag<uint16_t> tr_frag(const char* tile, int off, int s) {
-    const uint2 lo = ds_tr16(tile + off + 32 * s * ROW);
-    const uint2 hi = ds_tr16(tile + off + (32 * s + 16) * ROW);
+__device__ __forceinline__ Frag<uint16_t> tr_frag(const void* tile, uint32_t lane_base, int s) {
+    const uint2 lo = ds_tr16(tile, lane_base + 32 * s * ROW);
+    const uint2 hi = ds_tr16(tile, lane_base + (32 * s + 16) * ROW);
     Frag<uint16_t> f;
     f.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
     return f;
@@ -149,26 +194,25 @@ __device__ __forceinline__ Frag<uint16_t> frag_of(const uint4& u) {
 
 // ---------------------------------------------------------- global -> LDS
 
-// Copy instructions kk in [k0, k1) (kk < KMAX) of this wave (instruction
-// k = wave + 8 kk covers 1024 bytes) of a swizzled [token][ROW bytes] tile; row
-// r comes from byte r * gstride of the resource, and rows past its range read
-// as zeros.  The loop unrolls fully, so constant bounds fold away.
-template <int ROW, int KMAX>
-__device__ __forceinline__ void dma_rows(char* lds, __amdgpu_buffer_rsrc_t rs, int gstride,
-                                         int k0, int k1, int wave, int lane) {
+// Copies of a swizzled [token][ROW bytes] tile: wave instruction k = wave +
+// 8 kk writes LDS bytes [1024 k, 1024 k + 1024), 16 per lane.  dma_voff is the
+// lane's source byte offset for instruction kk (chunk independent); rows past
+// the resource's range read as zeros.
+template <int ROW, int W>
+__device__ __forceinline__ uint32_t dma_voff(int kk, int wave, int lane, int gstride) {
     constexpr int RPI = 1024 / ROW;  // rows per wave instruction (64 lanes x 16 bytes)
     constexpr int SPR = ROW / 16;    // 16-byte slots per row
     static_assert(1024 % ROW == 0, "whole rows per instruction");
-#pragma unroll
-    for (int kk = 0; kk < KMAX; ++kk) {
-        if (kk >= k0 && kk < k1) {
-            const int k = wave + kTrWaves * kk;
-            const int row = k * RPI + lane / SPR;
-            const int slot = (lane % SPR) ^ (2 * tr_swz<ROW>(row));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(lds + k * 1024), 16,
-                                                     row * gstride + slot * 16, 0, 0, 0);
-        }
-    }
+    const int k = wave + W * kk;
+    const int row = k * RPI + lane / SPR;
+    const int slot = (lane % SPR) ^ (2 * tr_swz<ROW>(row));
+    return static_cast<uint32_t>(row * gstride + slot * 16);
+}
+template <int W>
+__device__ __forceinline__ void dma_one(char* lds_tile, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                        int kk, int wave) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (SSD_LDS void*)(lds_tile + (wave + W * kk) * 1024), 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int stride) {
@@ -189,23 +233,29 @@ __device__ __forceinline__ int tr_row_block(int wave) {
 template <int P, int N, int Q, bool kOut, bool kSeq>
 struct TrScan {
     using G_ = TrGeo<P, N, Q>;
-    static constexpr int XI = G_::XBYTES / 1024 / kTrWaves;  // x-tile copy instructions per wave
-    static constexpr int BI = G_::BBYTES / 1024 / kTrWaves;  // B-tile copy instructions per wave
-    static_assert(XI >= 1 && BI >= 1 && G_::XBYTES % (1024 * kTrWaves) == 0 &&
-                      G_::BBYTES % (1024 * kTrWaves) == 0, "tile copy split");
+    static constexpr int W = TrWaves<kOut>::W;
+    static constexpr int NBW = TrWaves<kOut>::NBW;
+    static constexpr int NXI = G_::XBYTES / 1024;   // 1 KB copy instructions of an x tile
+    static constexpr int NBI = G_::BBYTES / 1024;   // ... of a B tile
+    static constexpr int XI = (NXI + W - 1) / W;    // per wave (the last round may be partial)
+    static constexpr int BI = (NBI + W - 1) / W;
+    static_assert(G_::XBYTES % 1024 == 0 && G_::BBYTES % 1024 == 0, "whole copy instructions");
+    // A row block's intra-chunk decays are factored when the decay across its
+    // 16 tokens is at most this (the column factors then stay below e^64).
+    static constexpr float kDiagSpan = 64.0f;
 
     const ScanArgs& a;
     int wave, lane, r16, g;
     int c_begin, c_end, L, nc;
-    bool last_seg, want_final;
-    bool fast_;             // factored intra-chunk decays (every dt * A <= 0 in the segment)
+    bool want_final;
+    bool fast_;             // every dt * A of the segment is <= 0
     bool st_wave_, out_wave_;
-    // every wave owns a state n-block / an output row block when there are 8
-    __device__ __forceinline__ bool st() const { return G_::NNB == kTrWaves || st_wave_; }
-    __device__ __forceinline__ bool ow() const { return kOut && (G_::NB == kTrWaves || out_wave_); }
-    int I;                  // output row block of this wave
-    float Dh, Ah;           // D[h], A[h]
-    int xoff[G_::PB], boff; // transposing-read lane offsets (x per p block, B of n block `wave`)
+    // with 8 waves and 8 n-blocks every wave owns a state n-block
+    __device__ __forceinline__ bool st() const { return (!kOut && G_::NNB == W) || st_wave_; }
+    __device__ __forceinline__ bool ow() const { return kOut && out_wave_; }
+    int I;                  // output row block of an output wave
+    int nb;                 // first state n-block of a state wave (it owns NBW)
+    float Dh;               // D[h]
     int seq_prev;           // sequence id of the token before the current chunk
     float mult;             // decay of the segment (chunk-state kernel)
     // per-(row, head) / per-(row, group) bases; chunk c adds c times the chunk stride
@@ -218,12 +268,27 @@ struct TrScan {
     const uint16_t* cbg;                // C.B^T tiles at (b, chunk 0, g)
     int64_t cb_cstride;                 // elements between chunks of the tile buffer
 
-    f32x4_t h[G_::PB];          // state rows n = 16 wave + 4g + r, column p = 16pb + r16
+    // LDS objects and lane addresses per buffer parity (opaque, see lds_keep)
+    char* xo[2];
+    char* bo[2];
+    TrMeta<Q>* mo[2];
+    char* ho[2];
+    float* cjo;
+    uint32_t xa[2];          // x tile, transposing read of p block 0, k step 0 (block pb: ^ 32 pb)
+    uint32_t ba[2][NBW];     // B tile, transposing read of this wave's n blocks
+    uint32_t ha[2];          // state operand, rows p = r16 (+16 pb), slot g (k step 0)
+    uint32_t hw[2][NBW];     // state operand, this state wave's write positions
+    uint32_t ma[2];          // metadata + 16 g (reads at tokens 32 s + 4 g)
+    uint32_t mbase[2];       // metadata
+    uint32_t cja;            // column factors of this wave + 16 g
+    uint32_t cjw;            // column factors of this wave + 4 lane
+    // chunk-independent source offsets of this wave's copies
+    uint32_t xv[XI], bv[BI];
+    uint32_t cv;             // C rows: (16 I + r16) * bstride + 16 g bytes
+
+    f32x4_t h[NBW][G_::PB];     // state rows n = 16 (nb + t) + 4g + r, column p = 16pb + r16
     uint4 cr[G_::KN];           // C rows of a chunk (k over n), loaded a chunk ahead
     uint4 cb[G_::NCB];          // C.B^T tile pairs of a chunk, loaded a chunk ahead
-    uint2 ypk[G_::PB];          // packed outputs awaiting their store
-    uint16_t* ypos;
-    bool ypend;
 
     __device__ __forceinline__ TrScan(const ScanArgs& args) : a(args) {}
 
@@ -237,43 +302,52 @@ struct TrScan {
             rows_rsrc(cg + static_cast<int64_t>(c) * Q * (bstride / 2), rows_in(c), bstride);
 #pragma unroll
         for (int s = 0; s < G_::KN; ++s) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, (16 * I + r16) * bstride + (32 * s + 8 * g) * 2, 0, 0);
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, cv + 64 * s, 0, 0);
             cr[s] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
 
+    // All NCB pairs from row block I's first (the ones past its own belong to
+    // the next row block, or for the last block are its own): one fixed count of
+    // loads, so the end-of-chunk wait can leave them in flight.
     __device__ __forceinline__ void load_cb(int c) {
-        const uint16_t* tiles = cbg + static_cast<int64_t>(c) * cb_cstride;
-        const int first = cb_pair_base(I);
+        const uint4* tiles = reinterpret_cast<const uint4*>(cbg + static_cast<int64_t>(c) * cb_cstride) +
+                             cb_pair_base(I) * 64 + lane;
 #pragma unroll
-        for (int u = 0; u < G_::NCB; ++u)
-            if (2 * u <= I) cb[u] = *reinterpret_cast<const uint4*>(tiles + ((first + u) * 64 + lane) * 8);
+        for (int u = 0; u < G_::NCB; ++u) cb[u] = tiles[64 * u];
     }
 
     // Copies of chunk c+1, split so that they spread over the chunk's math.
     __device__ __forceinline__ void dma_x(char* sX, int c) const {
         const __amdgpu_buffer_rsrc_t rs =
             rows_rsrc(xg + static_cast<int64_t>(c) * Q * (xstride / 2), rows_in(c), xstride);
-        dma_rows<G_::XROW, XI>(sX, rs, xstride, 0, XI, wave, lane);
+#pragma unroll
+        for (int kk = 0; kk < XI; ++kk)
+            if (NXI % W == 0 || wave + W * kk < NXI) dma_one<W>(sX, rs, xv[kk], kk, wave);
     }
     __device__ __forceinline__ void dma_b(char* sB, int c, int k0, int k1) const {
         if (k0 < k1) {
             const __amdgpu_buffer_rsrc_t rs =
                 rows_rsrc(bg + static_cast<int64_t>(c) * Q * (bstride / 2), rows_in(c), bstride);
-            dma_rows<G_::BROW, BI>(sB, rs, bstride, k0, k1, wave, lane);
+#pragma unroll
+            for (int kk = 0; kk < BI; ++kk)
+                if (kk >= k0 && kk < k1 && (NBI % W == 0 || wave + W * kk < NBI))
+                    dma_one<W>(sB, rs, bv[kk], kk, wave);
         }
     }
     // [cs | dt | w] of a chunk is one contiguous block of 3Q floats (Q * 3/4
     // pieces of 16 bytes) in the workspace and in TrMeta.
     __device__ __forceinline__ void dma_meta(TrMeta<Q>* sM, int c) const {
         constexpr int NPC = 3 * Q / 4;       // 16-byte pieces
-        const int mw = kTrWaves - 1 - wave;  // from the last waves
-        const int piece = kWave * mw + lane;
-        if (kWave * mw < NPC && piece < NPC) {
-            const float* src = mg + static_cast<int64_t>(c) * (3 * Q) + 4 * piece;
-            float* dst = reinterpret_cast<float*>(sM) + 4 * kWave * mw;  // [cs | dt | w] in order
-            __builtin_amdgcn_global_load_lds((SSD_GLOBAL void*)(src), (SSD_LDS void*)(dst), 16, 0, 0);
+        const int mw = W - 1 - wave;  // from the last waves
+        // a lane past the block would write LDS past [cs | dt | w] (the sequence ids)
+        if (kWave * mw + lane < NPC) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(mg + static_cast<int64_t>(c) * (3 * Q)), 0, 3 * Q * 4,
+                kRawBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (SSD_LDS void*)(reinterpret_cast<char*>(sM) + 1024 * mw), 16,
+                16 * (kWave * mw + lane), 0, 0, 0);
         }
         if constexpr (kSeq) {
             if (mw == (NPC + kWave - 1) / kWave && lane < Q / 4) {
@@ -292,8 +366,8 @@ struct TrScan {
     // j in the k order above; G[i][j] = (C_i . B_j) exp(cs_i - cs_j) dt_j,
     // masked to j <= i and (with sequence ids) seq_j = seq_i; D[h] is added on
     // the diagonal (the D x skip rides on the same MFMA).
-    __device__ __forceinline__ Frag<uint16_t> g_exact(const uint4& t, const TrMeta<Q>& m, int u,
-                                                      float cs_i, int seq_i) const {
+    __device__ __forceinline__ Frag<uint16_t> g_exact(const uint4& t, const void* mobj, uint32_t mq, int u, float cs_i,
+                                                      int seq_i) const {
         // token 16J + 4g + r of tile J is kept when r <= lim: all of a tile left
         // of the diagonal, r <= r16 - 4g on it, none right of it
         int tdiag = r16 - 4 * g;
@@ -304,11 +378,11 @@ struct TrScan {
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
             const int J = 2 * u + hp;
-            const int jb = 32 * u + 16 * hp + 4 * g;
-            const float4 cs4 = *reinterpret_cast<const float4*>(&m.cs[jb]);
-            const float4 dt4 = *reinterpret_cast<const float4*>(&m.dt[jb]);
+            const int off = 128 * u + 64 * hp;
+            const float4 cs4 = lds_ld<float4>(mobj, mq + off + offsetof(TrMeta<Q>, cs));
+            const float4 dt4 = lds_ld<float4>(mobj, mq + off + offsetof(TrMeta<Q>, dt));
             int4 sq4 = make_int4(0, 0, 0, 0);
-            if constexpr (kSeq) sq4 = *reinterpret_cast<const int4*>(&m.seq[jb]);
+            if constexpr (kSeq) sq4 = lds_ld<int4>(mobj, mq + off + offsetof(TrMeta<Q>, seq));
             const uint32_t d0 = hp ? t.z : t.x, d1 = hp ? t.w : t.y;
             const float cbv[4] = {bf_lo(d0), bf_hi(d0), bf_lo(d1), bf_hi(d1)};
             const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
@@ -328,222 +402,257 @@ struct TrScan {
         return frag_from_f32<uint16_t>(out);
     }
 
-    // Factored form for k steps strictly left of row block I (all j < 16I):
+    // Factored form, k steps strictly left of row block I (all j < 16I):
     // G[i][j] = r_i * (C_i . B_j) c_j with c_j = [seq_j = seq_m] exp(cs_m - cs_j) dt_j
-    // (m = 16I, from this wave's scratch) and the row factor r_i applied to the
-    // accumulator later.
-    __device__ __forceinline__ Frag<uint16_t> g_factored(const uint4& t, const float* cj, int u) const {
-        const float4 c0 = *reinterpret_cast<const float4*>(&cj[32 * u + 4 * g]);
-        const float4 c1 = *reinterpret_cast<const float4*>(&cj[32 * u + 16 + 4 * g]);
+    // (m = 16I; c0, c1: this wave's column factors of the step's two tiles) and
+    // the row factor r_i applied to the accumulator at the end.
+    __device__ __forceinline__ Frag<uint16_t> g_factored(const uint4& t, const float4& c0,
+                                                         const float4& c1) const {
         const float v[8] = {bf_lo(t.x) * c0.x, bf_hi(t.x) * c0.y, bf_lo(t.y) * c0.z,
                             bf_hi(t.y) * c0.w, bf_lo(t.z) * c1.x, bf_hi(t.z) * c1.y,
                             bf_lo(t.w) * c1.z, bf_hi(t.w) * c1.w};
         return frag_from_f32<uint16_t>(v);
     }
 
-    __device__ __forceinline__ void store_y() {
-        if (ypend) {
+    // Factored form of the diagonal k step u = I/2 (tiles 2u, 2u+1): the
+    // diagonal tile keeps j <= i and carries D[h] / r_i on its diagonal (the
+    // row factor r_i then restores D[h]); a tile right of the diagonal is zero.
+    __device__ __forceinline__ Frag<uint16_t> g_diag(const uint4& t, const float4& c0,
+                                                     const float4& c1, float dr) const {
+        int tdiag = r16 - 4 * g;
+        asm volatile("" : "+v"(tdiag));
+        const bool odd = I & 1;
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const uint32_t d[4] = {t.x, t.y, t.z, t.w};
+        float out[8];
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) *reinterpret_cast<uint2*>(ypos + 16 * pb) = ypk[pb];
+        for (int e = 0; e < 8; ++e) {
+            const int r = e & 3;
+            const float cbv = (e & 1) ? bf_hi(d[e >> 1]) : bf_lo(d[e >> 1]);
+            // tile 2u is the diagonal one for even I (and left of it for odd I);
+            // tile 2u+1 is the diagonal one for odd I (and right of it for even I)
+            const bool on_diag = (e < 4) ? !odd : odd;
+            const bool keep = (e < 4) ? (odd || r <= tdiag) : (odd && r <= tdiag);
+            const float v = keep ? cbv * cv[e] : 0.0f;
+            out[e] = (on_diag && r == tdiag) ? v + dr : v;
         }
-        ypend = false;
+        return frag_from_f32<uint16_t>(out);
     }
 
-    // One chunk.  On entry chunk c's tiles and metadata are in (X, Bt, M), the
-    // state before it in H (bf16 operand copy) and h (fp32, state waves), and
-    // its C rows and C.B^T tiles in cr, cb.  Issues chunk c+1's loads
-    // into the other buffers while it works, and leaves after a barrier with
-    // them complete.
+    // Copies of chunk c+1 that are this wave's share, interleaved with the k
+    // steps (s = -1: before them).
+    __device__ __forceinline__ void copies(int s, int c, char* Xn, char* Bn, TrMeta<Q>* Mn) const {
+        if (s < 0) {
+            dma_x(Xn, c + 1);
+        } else {
+            dma_b(Bn, c + 1, BI * s / G_::KQ, BI * (s + 1) / G_::KQ);
+            if (s == 0) dma_meta(Mn, c + 1);
+        }
+    }
+
+    // One chunk on an output wave (row block I).  On entry chunk c's tiles and
+    // metadata are in buffer K, the state before it in H[K] (bf16 operand
+    // copy), and its C rows and C.B^T tiles in cr, cb.  Issues this wave's
+    // share of chunk c+1's copies into buffer K^1 and leaves after the barrier
+    // that ends the chunk.
     template <int K>
-    __device__ __forceinline__ void chunk(int c, const char* X, const char* Bt, const TrMeta<Q>* M,
-                                          const char* H, char* Xn, char* Bn, TrMeta<Q>* Mn,
-                                          char* Hn, float* cj) {
+    __device__ __forceinline__ void chunk_out(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
         const bool has_next = c + 1 < c_end;
         const int valid = rows_in(c);
-        const TrMeta<Q>& m = *M;
+        const uint32_t mb = mbase[K];
+        const char* X = xo[K];
+        const TrMeta<Q>* M = mo[K];
+        const char* H = ho[K];
 
-        if constexpr (kOut) store_y();  // previous chunk's outputs
-        const float cs_last = m.cs[Q - 1];
-        const int seq_last = kSeq ? m.seq[valid - 1] : 0;
-
-        const bool fast = kOut && fast_;
+        const int i = 16 * I + r16;
+        const int m0 = 16 * I;
+        const float cs_i = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * i);
+        const float cs_m = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * m0);
+        // last real token of the row block (ids past L read as 0)
+        const int me = min(m0 + 15, max(valid - 1, m0));
+        const float cs_e = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * me);
+        int seq_i = 0, seq_m = 0, seq_e = 0;
+        if constexpr (kSeq) {
+            seq_i = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * i);
+            seq_m = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * m0);
+            seq_e = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * me);
+        }
+        // carried-state term y^T[p][i] = h . C_i, scaled below; each k step's
+        // operand reads are issued before its products
         f32x4_t y[G_::PB];
-        int i = 0;
-        float cs_i = 0.0f, r_i = 1.0f;
-        int seq_i = 0;
-        if constexpr (kOut) {
-            if (ow()) {
-                // carried-state term: y^T[p][i] = exp(cs_i) [seq_i = seq_prev] h.C_i,
-                // with exp(cs_i) = r_i exp(cs_m) in the factored form
-                i = 16 * I + r16;
-                const int m0 = 16 * I;
-                cs_i = m.cs[i];
-                const float cs_m = m.cs[m0];
-                int seq_m = 0;
-                if constexpr (kSeq) {
-                    seq_i = m.seq[i];
-                    seq_m = m.seq[m0];
-                }
-                Frag<uint16_t> hf[2][G_::PB];
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) {
-                    y[pb] = acc_zero();
-                    hf[0][pb] = frag_of(*reinterpret_cast<const uint4*>(H + h_off<G_::HROW>(16 * pb + r16, g)));
-                }
+        for (int pb = 0; pb < G_::PB; ++pb) y[pb] = acc_zero();
 #pragma unroll
-                for (int s = 0; s < G_::KN; ++s) {
-                    if (s + 1 < G_::KN) {
+        for (int s = 0; s < G_::KN; ++s) {
+            Frag<uint16_t> hf[G_::PB];
 #pragma unroll
-                        for (int pb = 0; pb < G_::PB; ++pb)
-                            hf[(s + 1) & 1][pb] = frag_of(*reinterpret_cast<const uint4*>(
-                                H + h_off<G_::HROW>(16 * pb + r16, 4 * (s + 1) + g)));
-                    }
-                    const Frag<uint16_t> cf = frag_of(cr[s]);
+            for (int pb = 0; pb < G_::PB; ++pb)
+                hf[pb] = frag_of(lds_ld<uint4>(H, (ha[K] ^ (s << 6)) + 16 * pb * G_::HROW));
+            __builtin_amdgcn_sched_barrier(0);
+            const Frag<uint16_t> cf = frag_of(cr[s]);
 #pragma unroll
-                    for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], hf[s & 1][pb], cf);
-                }
-                // fast: exp(cs_i) = r_i exp(cs_m); r_i is applied at the diagonal step
-                float sc = (!kSeq || seq_i == seq_prev) ? decay_exp(cs_i) : 0.0f;
-                r_i = 1.0f;
-                if (fast) {
-                    r_i = (!kSeq || seq_i == seq_m) ? decay_exp(cs_i - cs_m) : 0.0f;
-                    sc = (!kSeq || seq_m == seq_prev) ? decay_exp(cs_m) : 0.0f;
-                    // column factors of the steps left of the row block
-#pragma unroll
-                    for (int k = 0; k < (Q + kWave - 1) / kWave; ++k) {
-                        const int j = lane + kWave * k;
-                        if (j < m0) {
-                            bool keep = true;
-                            if constexpr (kSeq) keep = m.seq[j] == seq_m;
-                            cj[j] = keep ? decay_exp(cs_m - m.cs[j]) * m.dt[j] : 0.0f;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) y[pb][r] *= sc;
-            }
+            for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], hf[pb], cf);
         }
+        // factored: the row block holds one sequence and decays by at most
+        // kDiagSpan, so exp(cs_i - cs_j) = r_i c_j with r_i >= e^-kDiagSpan
+        const bool wfast = fast_ && (!kSeq || seq_m == seq_e) && cs_m - cs_e <= kDiagSpan;
+        float sc, fin = 1.0f, dr = 0.0f;
+        if (wfast) {
+            fin = decay_exp(cs_i - cs_m);  // r_i
+            dr = Dh / fin;
+            sc = (!kSeq || seq_m == seq_prev) ? decay_exp(cs_m) : 0.0f;
+            // column factors of tokens j < m0 + 16
+#pragma unroll
+            for (int k = 0; k < (Q + kWave - 1) / kWave; ++k) {
+                const int j = lane + kWave * k;
+                if (j < m0 + 16) {
+                    bool keep = true;
+                    if constexpr (kSeq)
+                        keep = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * j) == seq_m;
+                    const float csj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * j);
+                    const float dtj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, dt) + 4 * j);
+                    lds_st<float>(cjo, cjw + 256 * k, keep ? decay_exp(cs_m - csj) * dtj : 0.0f);
+                }
+            }
+        } else {
+            sc = (!kSeq || seq_i == seq_prev) ? decay_exp(cs_i) : 0.0f;
+        }
+#pragma unroll
+        for (int pb = 0; pb < G_::PB; ++pb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[pb][r] *= sc;
         if (has_next) {
-            if constexpr (kOut) {
-                if (ow()) load_c(c + 1);  // this chunk's C rows are consumed
-            }
-            dma_x(Xn, c + 1);
+            load_c(c + 1);  // this chunk's C rows are consumed
+            copies(-1, c, Xn, Bn, Mn);
         }
 
-        // h_c = [no reset in c] exp(cs_last) h_{c-1} + S_c
-        {
-            const float e = (!kSeq || seq_last == seq_prev) ? decay_exp(cs_last) : 0.0f;
-            if (st()) {
-#pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) h[pb][r] *= e;
-            }
-            if constexpr (!kOut) mult *= e;
-        }
-
-        // k steps over the chunk's tokens: S_c += (B w)^T x and the
-        // intra-chunk outputs y^T += x^T G^T, sharing the x fragments
+        // intra-chunk outputs y^T += x^T G^T over the k steps up to the
+        // diagonal one
+        const int sd = I >> 1;
 #pragma unroll
         for (int s = 0; s < G_::KQ; ++s) {
-            const bool do_state = st();
-            const bool do_out = kOut && ow() && 2 * s <= I;
-            if (do_state || do_out) {
+            if (s <= sd) {
                 Frag<uint16_t> xf[G_::PB];
+                float4 c0, c1;
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = tr_frag<G_::XROW>(X, xoff[pb], s);
-                if (do_state) {
-                    const float4 w0 = *reinterpret_cast<const float4*>(&m.w[32 * s + 4 * g]);
-                    const float4 w1 = *reinterpret_cast<const float4*>(&m.w[32 * s + 16 + 4 * g]);
-                    const Frag<uint16_t> bw = scale_frag(tr_frag<G_::BROW>(Bt, boff, s), w0, w1);
-#pragma unroll
-                    for (int pb = 0; pb < G_::PB; ++pb) mma(h[pb], bw, xf[pb]);
+                for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = tr_frag<G_::XROW>(X, xa[K] ^ (32 * pb), s);
+                if (wfast) {
+                    c0 = lds_ld<float4>(cjo, cja + 128 * s);
+                    c1 = lds_ld<float4>(cjo, cja + 128 * s + 64);
                 }
-                if constexpr (kOut) {
-                    if (do_out) {
-                        Frag<uint16_t> gf;
-                        if (fast && 2 * s + 1 < I) {
-                            gf = g_factored(cb[s], cj, s);
-                        } else {
-                            if (2 * s + 2 > I) {
-                                // the diagonal step (last): apply the row factor first
+                __builtin_amdgcn_sched_barrier(0);
+                Frag<uint16_t> gf;
+                if (!wfast) gf = g_exact(cb[s], M, ma[K], s, cs_i, seq_i);
+                else if (s < sd) gf = g_factored(cb[s], c0, c1);
+                else gf = g_diag(cb[s], c0, c1, dr);
 #pragma unroll
-                                for (int pb = 0; pb < G_::PB; ++pb)
-#pragma unroll
-                                    for (int r = 0; r < 4; ++r) y[pb][r] *= r_i;
-                            }
-                            gf = g_exact(cb[s], m, s, cs_i, seq_i);
-                        }
-#pragma unroll
-                        for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], xf[pb], gf);
-                    }
-                }
+                for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], xf[pb], gf);
             }
-            // spread the next chunk's copies over the steps
-            if (has_next) {
-                dma_b(Bn, c + 1, BI * s / G_::KQ, BI * (s + 1) / G_::KQ);
-                if (s == 0) dma_meta(Mn, c + 1);
-                if constexpr (kOut) {
-                    if (s == G_::KQ - 1 && ow()) load_cb(c + 1);  // after the last use
-                }
-            }
+            if (has_next) copies(s, c, Xn, Bn, Mn);
         }
+        if (has_next) load_cb(c + 1);  // after the last use
+        if (i < valid) {
+            uint16_t* yp = yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2) + 4 * g;
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb)
+                *reinterpret_cast<uint2*>(yp + 16 * pb) =
+                    make_uint2(pack_bf16x2(y[pb][0] * fin, y[pb][1] * fin),
+                               pack_bf16x2(y[pb][2] * fin, y[pb][3] * fin));
+        }
+        if constexpr (kSeq) seq_prev = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (Q - 1));
+        // this wave's copies of chunk c+1 have landed; the C rows, C.B^T tiles
+        // and y stores issued after them may still be in flight (the first use
+        // of the tiles waits for them)
+        static_assert(G_::NCB + G_::PB < 16, "vmcnt immediate");
+        if (has_next) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (G_::NCB + G_::PB));
+        __syncthreads();
+    }
 
-        if constexpr (kOut) {
-            if (ow()) {
-                ypk[0] = make_uint2(0, 0);
+    // One chunk on a state wave (n-block nb; waves owning neither an n-block
+    // nor a row block only copy): h_c = [no reset in c] exp(cs_last) h_{c-1} + S_c
+    // with S_c = (B w)^T x, then (output kernel) the bf16 operand copy of h_c in
+    // H[K^1] for the next chunk's carried-state term.
+    template <int K>
+    __device__ __forceinline__ void chunk_st(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
+        const bool has_next = c + 1 < c_end;
+        const int valid = rows_in(c);
+        const uint32_t mb = mbase[K];
+        const char* X = xo[K];
+        const char* Bt = bo[K];
+        const TrMeta<Q>* M = mo[K];
+
+        const float cs_last = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * (Q - 1));
+        const int seq_last = kSeq ? lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (valid - 1)) : 0;
+        if (has_next) copies(-1, c, Xn, Bn, Mn);
+        const float e = (!kSeq || seq_last == seq_prev) ? decay_exp(cs_last) : 0.0f;
+        if (st()) {
+#pragma unroll
+            for (int t = 0; t < NBW; ++t)
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb)
-                    ypk[pb] = make_uint2(pack_bf16x2(y[pb][0], y[pb][1]), pack_bf16x2(y[pb][2], y[pb][3]));
-                ypos = yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2) + 4 * g;
-                ypend = i < valid;
-            }
-            // bf16 operand copy of h_c for the next chunk's carried-state term
-            if (has_next && st()) {
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) {
-                    const int p = 16 * pb + r16;
-                    *reinterpret_cast<uint2*>(Hn + h_off<G_::HROW>(p, 2 * wave + (g >> 1)) +
-                                              8 * (g & 1)) =
-                        make_uint2(pack_bf16x2(h[pb][0], h[pb][1]), pack_bf16x2(h[pb][2], h[pb][3]));
+                    for (int r = 0; r < 4; ++r) h[t][pb][r] *= e;
+        }
+        if constexpr (!kOut) mult *= e;
+#pragma unroll
+        for (int s = 0; s < G_::KQ; ++s) {
+            if (st()) {
+                Frag<uint16_t> xf[G_::PB], braw[NBW];
+#pragma unroll
+                for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = tr_frag<G_::XROW>(X, xa[K] ^ (32 * pb), s);
+#pragma unroll
+                for (int t = 0; t < NBW; ++t) braw[t] = tr_frag<G_::BROW>(Bt, ba[K][t], s);
+                const float4 w0 = lds_ld<float4>(M, ma[K] + offsetof(TrMeta<Q>, w) + 128 * s);
+                const float4 w1 = lds_ld<float4>(M, ma[K] + offsetof(TrMeta<Q>, w) + 128 * s + 64);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < NBW; ++t) {
+                    const Frag<uint16_t> bw = scale_frag(braw[t], w0, w1);
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) mma(h[t][pb], bw, xf[pb]);
                 }
             }
+            if (has_next) copies(s, c, Xn, Bn, Mn);
         }
-        if constexpr (kSeq) seq_prev = m.seq[Q - 1];
+        if constexpr (kOut) {
+            if (has_next && st()) {
+#pragma unroll
+                for (int t = 0; t < NBW; ++t)
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb)
+                        lds_st<uint2>(ho[K ^ 1], hw[K ^ 1][t] + 16 * pb * G_::HROW,
+                                      make_uint2(pack_bf16x2(h[t][pb][0], h[t][pb][1]),
+                                                 pack_bf16x2(h[t][pb][2], h[t][pb][3])));
+            }
+        }
+        if constexpr (kSeq) seq_prev = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (Q - 1));
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's copies of chunk c+1 have landed
         __syncthreads();
     }
 
-    template <bool kFast>
-    __device__ __forceinline__ void loop(char* sX0, char* sB0, TrMeta<Q>* sM0, char* sH0,
-                                         char* sX1, char* sB1, TrMeta<Q>* sM1, char* sH1,
-                                         float* cj) {
-        for (int c = c_begin; c < c_end; c += 2) {
-            chunk<0, kFast>(c, sX0, sB0, sM0, sH0, sX1, sB1, sM1, sH1, cj);
-            if (c + 1 < c_end) chunk<1, kFast>(c + 1, sX1, sB1, sM1, sH1, sX0, sB0, sM0, sH0, cj);
-        }
-    }
     __device__ __forceinline__ void state_load(const float* __restrict__ src) {
 #pragma unroll
-        for (int pb = 0; pb < G_::PB; ++pb) {
-            if (src && st()) {
-                const float4 v = *reinterpret_cast<const float4*>(src + (16 * pb + r16) * N +
-                                                                  16 * wave + 4 * g);
-                h[pb] = f32x4_t{v.x, v.y, v.z, v.w};
-            } else {
-                h[pb] = acc_zero();
+        for (int t = 0; t < NBW; ++t)
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb) {
+                if (src && st()) {
+                    const float4 v = *reinterpret_cast<const float4*>(
+                        src + (16 * pb + r16) * N + 16 * (nb + t) + 4 * g);
+                    h[t][pb] = f32x4_t{v.x, v.y, v.z, v.w};
+                } else {
+                    h[t][pb] = acc_zero();
+                }
             }
-        }
     }
 
     __device__ __forceinline__ void state_store(float* __restrict__ dst) const {
         if (!st()) return;
 #pragma unroll
-        for (int pb = 0; pb < G_::PB; ++pb)
-            *reinterpret_cast<float4*>(dst + (16 * pb + r16) * N + 16 * wave + 4 * g) =
-                make_float4(h[pb][0], h[pb][1], h[pb][2], h[pb][3]);
+        for (int t = 0; t < NBW; ++t)
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb)
+                *reinterpret_cast<float4*>(dst + (16 * pb + r16) * N + 16 * (nb + t) + 4 * g) =
+                    make_float4(h[t][pb][0], h[t][pb][1], h[t][pb][2], h[t][pb][3]);
     }
 };
 
@@ -551,7 +660,6 @@ struct TrScan {
 // that reads of one buffer do not wait for copies into the other).
 template <int P, int N, int Q, bool kOut>
 struct TrLds {
-    using G_ = TrGeo<P, N, Q>;
     char* x[2];
     char* b[2];
     TrMeta<Q>* m[2];
@@ -565,7 +673,8 @@ template <int P, int N, int Q, bool kOut, bool kSeq>
 __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s,
                                             bool fast) {
     using G_ = TrGeo<P, N, Q>;
-    TrScan<P, N, Q, kOut, kSeq> k(a);
+    using S_ = TrScan<P, N, Q, kOut, kSeq>;
+    S_ k(a);
     k.fast_ = fast;
     const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
     k.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -576,19 +685,13 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.nc = a.nc;
     k.c_begin = it.seg * a.cps;
     k.c_end = min(k.c_begin + a.cps, a.nc);
-    k.last_seg = kOut && it.seg == a.nseg - 1;
-    k.want_final = k.last_seg && a.final_states != nullptr;
-    k.st_wave_ = k.wave < G_::NNB;
+    k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr;
+    k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
+    k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
     k.out_wave_ = kOut && k.wave < G_::NB;
-    k.I = tr_row_block<G_::NB>(k.wave);
+    k.I = kOut && k.wave < kTrWaves ? tr_row_block<G_::NB>(k.wave) : 0;
     k.Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
-    k.Ah = a.A[it.h];
-#pragma unroll
-    for (int pb = 0; pb < G_::PB; ++pb) k.xoff[pb] = tr_lane_off<G_::XROW>(pb, k.lane);
-    k.boff = tr_lane_off<G_::BROW>(k.st() ? k.wave : 0, k.lane);
     k.mult = 1.0f;
-    k.ypend = false;
-    k.ypos = nullptr;
     k.xstride = a.H * P * 2;
     k.bstride = a.G * N * 2;
     k.xg = static_cast<const uint16_t*>(a.x) + (it.b * a.L * a.H + it.h) * P;
@@ -606,46 +709,83 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     } else {
         k.seq_prev = 0;
     }
-    float* cj = s.cj + (kOut ? k.wave * Q : 0);
 
-    // incoming state: fp32 in registers, bf16 operand copy in h[0]
-    if constexpr (kOut) {
-        if (a.nseg == 1) k.state_load(a.init ? a.init + bh * P * N : nullptr);
-        else k.state_load(a.seg_state + (bh * a.nseg + it.seg) * P * N);
-        if (k.st()) {
+    // lane addresses and copy offsets, fixed for the whole segment
+    const int st_nb = k.st() ? k.nb : 0;
+    const int hx = G_::HROW == 256 ? k.r16 : ((k.r16 & 7) ^ ((k.r16 >> 3) & 1));  // h_off's swizzle
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) {
-                const int p = 16 * pb + k.r16;
-                *reinterpret_cast<uint2*>(s.h[0] + h_off<G_::HROW>(p, 2 * k.wave + (k.g >> 1)) +
-                                          8 * (k.g & 1)) =
-                    make_uint2(pack_bf16x2(k.h[pb][0], k.h[pb][1]), pack_bf16x2(k.h[pb][2], k.h[pb][3]));
+    for (int K = 0; K < 2; ++K) {
+        k.xo[K] = s.x[K];
+        k.bo[K] = s.b[K];
+        k.mo[K] = s.m[K];
+        k.ho[K] = s.h[K];
+        k.xa[K] = lds_keep(lds_addr(s.x[K]) + tr_lane_off<G_::XROW>(0, k.lane));
+#pragma unroll
+        for (int t = 0; t < S_::NBW; ++t) {
+            k.ba[K][t] = lds_keep(lds_addr(s.b[K]) + tr_lane_off<G_::BROW>(st_nb + t, k.lane));
+            k.hw[K][t] = lds_keep(lds_addr(s.h[K]) + k.r16 * G_::HROW +
+                                  (((2 * (st_nb + t) + (k.g >> 1)) ^ hx) << 4) + 8 * (k.g & 1));
+        }
+        k.ha[K] = lds_keep(lds_addr(s.h[K]) + k.r16 * G_::HROW + ((k.g ^ hx) << 4));
+        k.ma[K] = lds_keep(lds_addr(s.m[K]) + 16 * k.g);
+        k.mbase[K] = lds_addr(s.m[K]);
+    }
+    k.cjo = s.cj;
+    const int cw = k.ow() ? k.wave : 0;  // output waves own a column-factor row each
+    k.cja = lds_keep(lds_addr(s.cj) + 4 * Q * cw + 16 * k.g);
+    k.cjw = lds_keep(lds_addr(s.cj) + 4 * Q * cw + 4 * k.lane);
+#pragma unroll
+    for (int kk = 0; kk < S_::XI; ++kk)
+        k.xv[kk] = lds_keep(dma_voff<G_::XROW, S_::W>(kk, k.wave, k.lane, k.xstride));
+#pragma unroll
+    for (int kk = 0; kk < S_::BI; ++kk)
+        k.bv[kk] = lds_keep(dma_voff<G_::BROW, S_::W>(kk, k.wave, k.lane, k.bstride));
+    k.cv = lds_keep(static_cast<uint32_t>((16 * k.I + k.r16) * k.bstride + 16 * k.g));
+
+    // Role set-up, chunk loop and final stores per role, so that each role's
+    // registers are live only in its own code; both roles pass the same number
+    // of barriers (one after the first copies, one per chunk).
+    if (k.ow()) {
+        k.load_c(k.c_begin);
+        k.load_cb(k.c_begin);
+        k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        for (int c = k.c_begin; c < k.c_end; c += 2) {
+            k.template chunk_out<0>(c, s.x[1], s.b[1], s.m[1]);
+            if (c + 1 < k.c_end) k.template chunk_out<1>(c + 1, s.x[0], s.b[0], s.m[0]);
+        }
+    } else {
+        // incoming state: fp32 in registers, (output kernel) bf16 operand copy in H[0]
+        if constexpr (kOut) {
+            if (a.nseg == 1) k.state_load(a.init ? a.init + bh * P * N : nullptr);
+            else k.state_load(a.seg_state + (bh * a.nseg + it.seg) * P * N);
+            if (k.st()) {
+#pragma unroll
+                for (int t = 0; t < S_::NBW; ++t)
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb)
+                        lds_st<uint2>(k.ho[0], k.hw[0][t] + 16 * pb * G_::HROW,
+                                      make_uint2(pack_bf16x2(k.h[t][pb][0], k.h[t][pb][1]),
+                                                 pack_bf16x2(k.h[t][pb][2], k.h[t][pb][3])));
             }
+        } else {
+            k.state_load(nullptr);
         }
-        if (k.ow()) {
-            k.load_c(k.c_begin);
-            k.load_cb(k.c_begin);
+        k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        for (int c = k.c_begin; c < k.c_end; c += 2) {
+            k.template chunk_st<0>(c, s.x[1], s.b[1], s.m[1]);
+            if (c + 1 < k.c_end) k.template chunk_st<1>(c + 1, s.x[0], s.b[0], s.m[0]);
         }
-    } else {
-        k.state_load(nullptr);
-    }
-    k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-
-    for (int c = k.c_begin; c < k.c_end; c += 2) {
-        k.template chunk<0>(c, s.x[0], s.b[0], s.m[0], s.h[0], s.x[1], s.b[1], s.m[1], s.h[1], cj);
-        if (c + 1 < k.c_end)
-            k.template chunk<1>(c + 1, s.x[1], s.b[1], s.m[1], s.h[1], s.x[0], s.b[0], s.m[0],
-                                       s.h[0], cj);
-    }
-
-    if constexpr (kOut) {
-        k.store_y();
-        if (k.want_final) k.state_store(a.final_states + bh * P * N);
-    } else {
-        const int64_t slot = bh * a.nseg + it.seg;
-        k.state_store(a.seg_state + slot * P * N);
-        if (threadIdx.x == 0) a.seg_mult[slot] = k.mult;
+        if constexpr (kOut) {
+            if (k.want_final) k.state_store(a.final_states + bh * P * N);
+        } else {
+            const int64_t slot = bh * a.nseg + it.seg;
+            k.state_store(a.seg_state + slot * P * N);
+            if (threadIdx.x == 0) a.seg_mult[slot] = k.mult;
+        }
     }
 }
 
@@ -655,16 +795,16 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
 //   kOut = true:  outputs of every segment from its incoming state; final
 //                 states from the last segment.
 template <int P, int N, int Q, bool kOut, bool kSeq>
-__global__ __launch_bounds__(kTrThreads) void scan_tr_kernel(ScanArgs a) {
+__global__ __launch_bounds__(TrWaves<kOut>::kThreads) void scan_tr_kernel(ScanArgs a) {
     using G_ = TrGeo<P, N, Q>;
-    __shared__ __attribute__((aligned(16))) char sX0[G_::XBYTES];
-    __shared__ __attribute__((aligned(16))) char sX1[G_::XBYTES];
-    __shared__ __attribute__((aligned(16))) char sB0[G_::BBYTES];
-    __shared__ __attribute__((aligned(16))) char sB1[G_::BBYTES];
+    __shared__ __attribute__((aligned(1024))) char sX0[G_::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char sX1[G_::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char sB0[G_::BBYTES];
+    __shared__ __attribute__((aligned(1024))) char sB1[G_::BBYTES];
     __shared__ __attribute__((aligned(16))) TrMeta<Q> sM0;
     __shared__ __attribute__((aligned(16))) TrMeta<Q> sM1;
-    __shared__ __attribute__((aligned(16))) char sH0[kOut ? G_::HBYTES : 16];
-    __shared__ __attribute__((aligned(16))) char sH1[kOut ? G_::HBYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sH0[kOut ? G_::HBYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sH1[kOut ? G_::HBYTES : 16];
     __shared__ __attribute__((aligned(16))) float sCj[kOut ? kTrWaves * Q : 4];
     const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1}, {&sM0, &sM1}, {sH0, sH1}, sCj};
 
@@ -679,7 +819,7 @@ __global__ __launch_bounds__(kTrThreads) void scan_tr_kernel(ScanArgs a) {
         const float* blk = a.cs + meta_offset(a, it.b, it.h, c0, Q);
         const int n = (c1 - c0) * Q;
         int up = 0;
-        for (int j = static_cast<int>(threadIdx.x); j < n; j += kTrThreads)
+        for (int j = static_cast<int>(threadIdx.x); j < n; j += TrWaves<true>::kThreads)
             up |= blk[(j / Q) * (3 * Q) + Q + j % Q] * Ah > 0.0f;  // dt of token j
         scan_tr_run<P, N, Q, true, kSeq>(a, lds, __syncthreads_or(up) == 0);
     } else {
@@ -691,9 +831,9 @@ template <int P, int N, int Q, bool kOut>
 hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(nblocks));
     if (a.seq_idx)
-        hipLaunchKernelGGL((scan_tr_kernel<P, N, Q, kOut, true>), grid, dim3(kTrThreads), 0, st, a);
+        hipLaunchKernelGGL((scan_tr_kernel<P, N, Q, kOut, true>), grid, dim3(TrWaves<kOut>::kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((scan_tr_kernel<P, N, Q, kOut, false>), grid, dim3(kTrThreads), 0, st, a);
+        hipLaunchKernelGGL((scan_tr_kernel<P, N, Q, kOut, false>), grid, dim3(TrWaves<kOut>::kThreads), 0, st, a);
     return hipGetLastError();
 }
 

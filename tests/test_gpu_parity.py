@@ -267,3 +267,46 @@ def test_rejects_unsupported_geometry_on_device():
                            torch.zeros(1, 64, 1, 16, device=dev), torch.zeros(1, 64, 1, 16, device=dev),
                            chunk_size=64)
     assert e.value.status == 4
+
+
+def test_graph_replay_matches_eager_bitwise():
+    """The prefill scan and a decode step captured into a HIP graph give, on
+    every replay, bitwise the outputs of the same calls launched eagerly (the
+    library records no memset nodes; eager work and synchronisations run
+    between the replays)."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    rng = np.random.default_rng(31)
+    b, L, H, P, N, G, Q = 1, 2000, 16, 64, 128, 2, 128
+    p = workloads.random_problem(rng, b, L + 1, H, P, N, G, io="bf16", init=True)
+    p["seq_idx"] = _packed(rng, b, L + 1, 3)
+    t = to_dev(p, "bf16")
+    x, dt, B, C = (t[k][:, :L].contiguous() for k in ("x", "dt_raw", "B", "C"))
+    xd, dtd, Bd, Cd = (t[k][:, L].contiguous() for k in ("x", "dt_raw", "B", "C"))
+    seq = t["seq_idx"][:, :L].contiguous()
+    ws = torch.empty(max(1, ssd.workspace_bytes(b, L, H, P, N, G, Q)), dtype=torch.uint8,
+                     device=x.device)
+    y = torch.empty_like(x)
+    fs = torch.empty(b, H, P, N, device=x.device)
+    yd = torch.empty_like(xd)
+
+    def step():
+        ssd.chunk_scan_fwd(x, dt, t["A"], B, C, chunk_size=Q, D=t["D"], dt_bias=t["dt_bias"],
+                           initial_states=t["h_init"], seq_idx=seq, return_final_states=True,
+                           out=y, final_states_out=fs, workspace=ws)
+        ssd.state_update(fs, xd, dtd, t["A"], Bd, Cd, D=t["D"], dt_bias=t["dt_bias"], out=yd)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (y.clone(), fs.clone(), yd.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        for o in (y, fs, yd):
+            o.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log("graph replay %d" % r)
+        assert torch.equal(y, ref[0]) and torch.equal(fs, ref[1]) and torch.equal(yd, ref[2]), r
