@@ -13,7 +13,10 @@
 
 namespace {
 
-constexpr int64_t kTargetWorkgroups = 512;  // enough independent workgroups for 256 CUs
+// Rows x heads are cut into segments until there are about this many
+// workgroups: one per CU of an MI355X (the scan kernels hold one workgroup per
+// CU), so that every segment's workgroup runs in a single round.
+constexpr int64_t kTargetWorkgroups = 256;
 constexpr size_t kAlign = 256;
 
 struct Plan {

@@ -248,14 +248,13 @@ struct TrScan {
     int wave, lane, r16, g;
     int c_begin, c_end, L, nc;
     bool want_final;
-    bool fast_;             // every dt * A of the segment is <= 0
     bool st_wave_, out_wave_;
     // with 8 waves and 8 n-blocks every wave owns a state n-block
     __device__ __forceinline__ bool st() const { return (!kOut && G_::NNB == W) || st_wave_; }
     __device__ __forceinline__ bool ow() const { return kOut && out_wave_; }
     int I;                  // output row block of an output wave
     int nb;                 // first state n-block of a state wave (it owns NBW)
-    float Dh;               // D[h]
+    float Dh, Ah;           // D[h], A[h]
     int seq_prev;           // sequence id of the token before the current chunk
     float mult;             // decay of the segment (chunk-state kernel)
     // per-(row, head) / per-(row, group) bases; chunk c adds c times the chunk stride
@@ -493,27 +492,33 @@ struct TrScan {
 #pragma unroll
             for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], hf[pb], cf);
         }
-        // factored: the row block holds one sequence and decays by at most
-        // kDiagSpan, so exp(cs_i - cs_j) = r_i c_j with r_i >= e^-kDiagSpan
-        const bool wfast = fast_ && (!kSeq || seq_m == seq_e) && cs_m - cs_e <= kDiagSpan;
+        // column factors c_j = [seq_j = seq_m] exp(cs_m - cs_j) dt_j of the
+        // tokens j < m0 + 16, and whether any of them has dt_j * A > 0
+        bool rising = false;
+#pragma unroll
+        for (int k = 0; k < (Q + kWave - 1) / kWave; ++k) {
+            const int j = lane + kWave * k;
+            if (j < m0 + 16) {
+                bool keep = true;
+                if constexpr (kSeq)
+                    keep = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * j) == seq_m;
+                const float csj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * j);
+                const float dtj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, dt) + 4 * j);
+                rising = rising || dtj * Ah > 0.0f;
+                // overflows only where the factored form is not taken
+                lds_st<float>(cjo, cjw + 256 * k, keep ? decay_exp(cs_m - csj) * dtj : 0.0f);
+            }
+        }
+        // factored when cs never rises over these tokens (every factor is then
+        // at most dt_j, and r_i at most 1), the row block holds one sequence and
+        // decays by at most kDiagSpan (r_i >= e^-kDiagSpan); else the exact form
+        const bool wfast = !__builtin_amdgcn_ballot_w64(rising) && (!kSeq || seq_m == seq_e) &&
+                           cs_m - cs_e <= kDiagSpan;
         float sc, fin = 1.0f, dr = 0.0f;
         if (wfast) {
             fin = decay_exp(cs_i - cs_m);  // r_i
             dr = Dh / fin;
             sc = (!kSeq || seq_m == seq_prev) ? decay_exp(cs_m) : 0.0f;
-            // column factors of tokens j < m0 + 16
-#pragma unroll
-            for (int k = 0; k < (Q + kWave - 1) / kWave; ++k) {
-                const int j = lane + kWave * k;
-                if (j < m0 + 16) {
-                    bool keep = true;
-                    if constexpr (kSeq)
-                        keep = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * j) == seq_m;
-                    const float csj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * j);
-                    const float dtj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, dt) + 4 * j);
-                    lds_st<float>(cjo, cjw + 256 * k, keep ? decay_exp(cs_m - csj) * dtj : 0.0f);
-                }
-            }
         } else {
             sc = (!kSeq || seq_i == seq_prev) ? decay_exp(cs_i) : 0.0f;
         }
@@ -667,30 +672,35 @@ struct TrLds {
     float* cj;
 };
 
-// One (row, head, segment) from set-up to the final stores.  fast: every
-// dt * A of the segment is <= 0 (see the kernel).
+// One (row, head, segment) from set-up to the final stores.
 template <int P, int N, int Q, bool kOut, bool kSeq>
-__device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s,
-                                            bool fast) {
+__device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s) {
     using G_ = TrGeo<P, N, Q>;
     using S_ = TrScan<P, N, Q, kOut, kSeq>;
     S_ k(a);
-    k.fast_ = fast;
     const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
     k.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     k.lane = static_cast<int>(threadIdx.x) % kWave;
     k.r16 = k.lane & 15;
     k.g = k.lane >> 4;
+    k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
+    k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
+    const int64_t bh = it.b * a.H + it.h;
+    // the incoming state first: its load is the longest wait of the set-up
+    if (!kOut || k.st_wave_) {
+        if (kOut && a.nseg > 1) k.state_load(a.seg_state + (bh * a.nseg + it.seg) * P * N);
+        else if (kOut) k.state_load(a.init ? a.init + bh * P * N : nullptr);
+        else k.state_load(nullptr);
+    }
     k.L = static_cast<int>(a.L);
     k.nc = a.nc;
     k.c_begin = it.seg * a.cps;
     k.c_end = min(k.c_begin + a.cps, a.nc);
     k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr;
-    k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
-    k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
     k.out_wave_ = kOut && k.wave < G_::NB;
     k.I = kOut && k.wave < kTrWaves ? tr_row_block<G_::NB>(k.wave) : 0;
     k.Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
+    k.Ah = a.A[it.h];
     k.mult = 1.0f;
     k.xstride = a.H * P * 2;
     k.bstride = a.G * N * 2;
@@ -702,7 +712,6 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.sqg = a.seq_idx ? a.seq_idx + it.b * a.L : nullptr;
     k.cb_cstride = static_cast<int64_t>(a.G) * cbt_elems_per_chunk_group(Q);
     k.cbg = static_cast<const uint16_t*>(a.cbt) + (it.b * a.nc * a.G + it.g) * (k.cb_cstride / a.G);
-    const int64_t bh = it.b * a.H + it.h;
     if constexpr (kSeq) {
         const int64_t tp = k.c_begin == 0 ? 0 : static_cast<int64_t>(k.c_begin) * Q - 1;
         k.seq_prev = a.seq_idx[it.b * a.L + tp];
@@ -756,10 +765,9 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
             if (c + 1 < k.c_end) k.template chunk_out<1>(c + 1, s.x[0], s.b[0], s.m[0]);
         }
     } else {
-        // incoming state: fp32 in registers, (output kernel) bf16 operand copy in H[0]
+        // incoming state (loaded above): bf16 operand copy in H[0] (output kernel)
+        k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
         if constexpr (kOut) {
-            if (a.nseg == 1) k.state_load(a.init ? a.init + bh * P * N : nullptr);
-            else k.state_load(a.seg_state + (bh * a.nseg + it.seg) * P * N);
             if (k.st()) {
 #pragma unroll
                 for (int t = 0; t < S_::NBW; ++t)
@@ -769,10 +777,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
                                       make_uint2(pack_bf16x2(k.h[t][pb][0], k.h[t][pb][1]),
                                                  pack_bf16x2(k.h[t][pb][2], k.h[t][pb][3])));
             }
-        } else {
-            k.state_load(nullptr);
         }
-        k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         for (int c = k.c_begin; c < k.c_end; c += 2) {
@@ -808,23 +813,7 @@ __global__ __launch_bounds__(TrWaves<kOut>::kThreads) void scan_tr_kernel(ScanAr
     __shared__ __attribute__((aligned(16))) float sCj[kOut ? kTrWaves * Q : 4];
     const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1}, {&sM0, &sM1}, {sH0, sH1}, sCj};
 
-    if constexpr (kOut) {
-        // The factored form of the intra-chunk decays needs dt_j * A <= 0 for
-        // every token of the segment (cs then never increases inside a
-        // sequence and every factor is at most 1); otherwise every k step takes
-        // the exact form.
-        const WorkItem it = decode_work(a, a.nseg);
-        const int c0 = it.seg * a.cps, c1 = min(c0 + a.cps, a.nc);
-        const float Ah = a.A[it.h];
-        const float* blk = a.cs + meta_offset(a, it.b, it.h, c0, Q);
-        const int n = (c1 - c0) * Q;
-        int up = 0;
-        for (int j = static_cast<int>(threadIdx.x); j < n; j += TrWaves<true>::kThreads)
-            up |= blk[(j / Q) * (3 * Q) + Q + j % Q] * Ah > 0.0f;  // dt of token j
-        scan_tr_run<P, N, Q, true, kSeq>(a, lds, __syncthreads_or(up) == 0);
-    } else {
-        scan_tr_run<P, N, Q, false, kSeq>(a, lds, false);
-    }
+    scan_tr_run<P, N, Q, kOut, kSeq>(a, lds);
 }
 
 template <int P, int N, int Q, bool kOut>

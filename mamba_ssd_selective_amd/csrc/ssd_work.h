@@ -22,18 +22,18 @@ struct WorkItem {
 };
 
 // Work order (fastest first): head within its group, group, segment, row.
+// Grids stay below 2^31 workgroups, so the index arithmetic is 32-bit.
 __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
-    const int64_t nblocks = static_cast<int64_t>(gridDim.x);
-    int64_t w = xcd_work_index(blockIdx.x, nblocks);
-    const int hpg = a.H / a.G;
+    uint32_t w = static_cast<uint32_t>(xcd_work_index(blockIdx.x, gridDim.x));
+    const uint32_t hpg = static_cast<uint32_t>(a.H / a.G);
     WorkItem it;
     const int hh = static_cast<int>(w % hpg);
     w /= hpg;
-    it.g = static_cast<int>(w % a.G);
-    w /= a.G;
-    it.seg = static_cast<int>(w % nseg_grid);
-    it.b = w / nseg_grid;
-    it.h = it.g * hpg + hh;
+    it.g = static_cast<int>(w % static_cast<uint32_t>(a.G));
+    w /= static_cast<uint32_t>(a.G);
+    it.seg = static_cast<int>(w % static_cast<uint32_t>(nseg_grid));
+    it.b = static_cast<int64_t>(w / static_cast<uint32_t>(nseg_grid));
+    it.h = it.g * static_cast<int>(hpg) + hh;
     return it;
 }
 

@@ -52,7 +52,7 @@ def test_supported_set(lib):
 
 
 def test_workspace_and_segments(lib):
-    # config 1: 64 heads, 64 chunks of 128 -> 8 segments of 8 chunks
+    # config 1: 64 heads, 64 chunks of 128 -> 4 segments of 16 chunks (256 workgroups)
     ws = ssd.workspace_bytes(1, 8192, 64, 64, 128, 8, 128)
     # chunk metadata (cs, dt, weights: fp32 per row, head, token), C.B^T tiles
     # (lower-triangular 16x16 bf16 tiles in 20 pairs of 64 lanes x 8 elements
@@ -60,9 +60,9 @@ def test_workspace_and_segments(lib):
     # segment) and segment multipliers
     meta = 3 * 64 * 8192 * 4
     tiles = 64 * 8 * 20 * 512 * 2
-    seg = 64 * 8 * 64 * 128 * 4 + 256 * math.ceil(64 * 8 * 4 / 256)
+    seg = 64 * 4 * 64 * 128 * 4 + 256 * math.ceil(64 * 4 * 4 / 256)
     assert ws == meta + tiles + seg
-    assert ssd.segments(1, 8192, 64, 64, 128, 8, 128) == 8
+    assert ssd.segments(1, 8192, 64, 64, 128, 8, 128) == 4
     # enough rows x heads: one segment, no segment scratch
     assert ssd.segments(64, 4096, 64, 64, 128, 8, 128) == 1
     assert ssd.workspace_bytes(64, 4096, 64, 64, 128, 8, 128) == (

@@ -76,7 +76,7 @@ def test_fp32_parity(case):
 
 
 BF16_CASES = [
-    (1, 4096, 64, 64, 128, 8, 128, True, False),  # 8 segments of 4 chunks
+    (1, 4096, 64, 64, 128, 8, 128, True, False),  # 4 segments of 8 chunks
     (2, 777, 16, 64, 128, 4, 256, True, True),
     (4, 333, 8, 64, 128, 2, 64, False, True),
     (1, 2000, 8, 64, 64, 2, 128, True, False),
