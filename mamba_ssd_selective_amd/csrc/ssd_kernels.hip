@@ -128,7 +128,29 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     const T* __restrict__ Bp = static_cast<const T*>(a.B);
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
 
-    // ---- issue the B / C row loads first (they overlap the dt scan)
+    // ---- the sequence ids and the first head's dt first: loads return in
+    // order, and the dt scan should not wait behind the B / C rows
+    const int hpg = a.H / a.G;
+    const bool has_seq = a.seq_idx != nullptr;
+    int sq[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        int64_t t = t0 + lane * E + k;
+        t = t < tl ? t : tl;
+        sq[k] = has_seq ? a.seq_idx[b * a.L + t] : 0;
+    }
+    float raw0[E];
+    {
+        const int h = g * hpg + (wave < hpg ? wave : 0);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            int64_t tt = t0 + lane * E + k;
+            tt = tt < tl ? tt : tl;
+            raw0[k] = a.dt_raw[(b * a.L + tt) * a.H + h];
+        }
+    }
+
+    // ---- then the B / C row loads (they overlap the dt scan)
     constexpr int CPR = C_::NP / kV;       // 16-byte pieces per padded row
     constexpr int PIECES = Q * CPR;
     constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
@@ -147,18 +169,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     }
 
     // ---- per-head chunk metadata
-    const int hpg = a.H / a.G;
-    const bool has_seq = a.seq_idx != nullptr;
-    int sq[E];
-#pragma unroll
-    for (int k = 0; k < E; ++k) {
-        int64_t t = t0 + lane * E + k;
-        t = t < tl ? t : tl;
-        sq[k] = has_seq ? a.seq_idx[b * a.L + t] : 0;
-    }
     const int prev_lane_last = __shfl_up(sq[E - 1], 1, kWave);
     constexpr int kLastLane = (Q - 1) / E, kLastK = (Q - 1) % E;
-    for (int hh = wave; hh < hpg; hh += kWaves) {
+    // one head: dt transform, segmented cumsum, weights, written out; raw are
+    // this lane's dt_raw values of the head
+    auto head_meta = [&](int hh, const float (&raw)[E]) {
         const int h = g * hpg + hh;
         const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
         const float Ah = a.A[h];
@@ -168,11 +183,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             const int t = lane * E + k;
-            int64_t tt = t0 + t;
-            const bool real = t < Q && tt < a.L;
-            tt = tt < tl ? tt : tl;
-            const float raw = a.dt_raw[(b * a.L + tt) * a.H + h];
-            const float d = real ? dt_transform(raw, bias, a.softplus, a.dt_min, a.dt_max) : 0.0f;
+            const bool real = t < Q && t0 + t < a.L;
+            const float d = real ? dt_transform(raw[k], bias, a.softplus, a.dt_min, a.dt_max) : 0.0f;
             const int before = (k == 0) ? prev_lane_last : sq[k - 1];
             const bool head = t < Q && ((t == 0) || (sq[k] != before));
             dtv[k] = d;
@@ -200,6 +212,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
                 a.wgt[base + t] = (sq[k] == seq_last) ? wv : 0.0f;
             }
         }
+    };
+    if (wave < hpg) head_meta(wave, raw0);
+    for (int hh = wave + kWaves; hh < hpg; hh += kWaves) {
+        float raw[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            int64_t tt = t0 + lane * E + k;
+            tt = tt < tl ? tt : tl;
+            raw[k] = a.dt_raw[(b * a.L + tt) * a.H + g * hpg + hh];
+        }
+        head_meta(hh, raw);
     }
 
     // ---- stage B and C rows (tokens past L and columns past N are zero)
@@ -222,22 +245,42 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
                           ((b * a.nc + c) * a.G + g) * cbt_elems_per_chunk_group(Q);
     const int r16 = lane & 15, q = lane >> 4;
     constexpr int NPAIR = C_::NB / 2 * (C_::NB / 2 + 1);
-    for (int half = wave; half < 2 * NPAIR; half += kWaves) {
-        const int pidx = half >> 1;
-        int I = 0;
-        while (cb_pair_base(I + 1) <= pidx) ++I;
-        const int J = 2 * (pidx - cb_pair_base(I)) + (half & 1);
-        f32x4_t acc = acc_zero();
-        if (J <= I) {
+    constexpr int NHALF = 2 * NPAIR;
+    // two half-tiles per pass (independent accumulators, interleaved products);
+    // half-tile h is tile (I, J) of pair h/2: I its row block, J = 2u + h % 2
+    auto tile_of = [](int h, int& I, int& J) {
+        const int pidx = h >> 1;
+        int rbk = 0;
 #pragma unroll
-            for (int s = 0; s < C_::KN; ++s) {
-                const Frag<T> bf = frag_load8(sB + (16 * J + r16) * C_::SB + 32 * s + 8 * q);
-                const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
-                mma(acc, bf, cf);
+        for (int r = 1; r < C_::NB; ++r) rbk += cb_pair_base(r) <= pidx ? 1 : 0;
+        I = rbk;
+        J = 2 * (pidx - cb_pair_base(rbk)) + (h & 1);
+    };
+    for (int h0 = wave; h0 < NHALF; h0 += 2 * kWaves) {
+        const int h1 = h0 + kWaves;
+        int I0, J0, I1, J1;
+        tile_of(h0, I0, J0);
+        tile_of(h1, I1, J1);
+        const bool on0 = J0 <= I0, on1 = h1 < NHALF && J1 <= I1;
+        f32x4_t acc0 = acc_zero(), acc1 = acc_zero();
+#pragma unroll
+        for (int s = 0; s < C_::KN; ++s) {
+            if (on0) {
+                const Frag<T> bf = frag_load8(sB + (16 * J0 + r16) * C_::SB + 32 * s + 8 * q);
+                const Frag<T> cf = frag_load8(sC + (16 * I0 + r16) * C_::SB + 32 * s + 8 * q);
+                mma(acc0, bf, cf);
+            }
+            if (on1) {
+                const Frag<T> bf = frag_load8(sB + (16 * J1 + r16) * C_::SB + 32 * s + 8 * q);
+                const Frag<T> cf = frag_load8(sC + (16 * I1 + r16) * C_::SB + 32 * s + 8 * q);
+                mma(acc1, bf, cf);
             }
         }
-        store4_f32(out + (static_cast<int64_t>(pidx) * 64 + lane) * 8 + 4 * (half & 1), acc[0],
-                   acc[1], acc[2], acc[3]);
+        store4_f32(out + (static_cast<int64_t>(h0 >> 1) * 64 + lane) * 8 + 4 * (h0 & 1), acc0[0],
+                   acc0[1], acc0[2], acc0[3]);
+        if (h1 < NHALF)
+            store4_f32(out + (static_cast<int64_t>(h1 >> 1) * 64 + lane) * 8 + 4 * (h1 & 1),
+                       acc1[0], acc1[1], acc1[2], acc1[3]);
     }
 }
 
