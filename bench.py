@@ -193,9 +193,20 @@ def main():
     ws = torch.empty(max(1, ssd.workspace_bytes(b, L, H, P, N, G, Q)), dtype=torch.uint8,
                      device=dev)
     nseg = ssd.segments(b, L, H, P, N, G, Q)
-    kernels = ["chunk_prep"] + (["chunk_state", "state_pass"] if nseg > 1 else []) + ["chunk_output"]
-    nk = len(kernels) + 1  # + state_update
     launched = ctypes.c_int(0)
+    # the scan's kernel sequence: count its launches once (hooks with no events)
+    no_events = (ctypes.c_void_p * 16)()
+    lib.ssd_set_timing_events(no_events, 16, ctypes.byref(launched))
+    s0 = sets[0]
+    ssd.chunk_scan_fwd(s0["x"], s0["dt"], A, s0["B"], s0["C"], chunk_size=Q, D=D, dt_bias=bias,
+                       initial_states=s0["h0"], seq_idx=s0["seq"], return_final_states=True,
+                       out=s0["y"], final_states_out=s0["fs"], workspace=ws)
+    lib.ssd_set_timing_events(None, 0, None)
+    torch.cuda.synchronize()
+    kernels = {2: ["chunk_prep", "chunk_output"],
+               3: ["chunk_prep", "chunk_state", "chunk_output"],
+               4: ["chunk_prep", "chunk_state", "state_pass", "chunk_output"]}[launched.value]
+    nk = len(kernels) + 1  # + state_update
 
     vp_size = ctypes.sizeof(ctypes.c_void_p)
 

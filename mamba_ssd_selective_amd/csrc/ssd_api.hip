@@ -250,15 +250,17 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
                 return var->chunk_state(sa, b * (plan.nseg - 1) * H, hs);
             }) != hipSuccess)
             return SSD_ERR_HIP;
-        ssd::PassArgs pa;
-        pa.seg_state = sa.seg_state;
-        pa.seg_mult = sa.seg_mult;
-        pa.init = initial_states;
-        pa.PN = P * N;
-        pa.nseg = static_cast<int>(plan.nseg);
-        if (timed_launch(k, hs, [&] { return ssd::launch_state_pass(pa, b * H, hs); }) !=
-            hipSuccess)
-            return SSD_ERR_HIP;
+        if (!var->output_combines_segments) {
+            ssd::PassArgs pa;
+            pa.seg_state = sa.seg_state;
+            pa.seg_mult = sa.seg_mult;
+            pa.init = initial_states;
+            pa.PN = P * N;
+            pa.nseg = static_cast<int>(plan.nseg);
+            if (timed_launch(k, hs, [&] { return ssd::launch_state_pass(pa, b * H, hs); }) !=
+                hipSuccess)
+                return SSD_ERR_HIP;
+        }
     }
     if (timed_launch(k, hs, [&] { return var->chunk_output(sa, b * plan.nseg * H, hs); }) !=
         hipSuccess)

@@ -977,12 +977,12 @@ static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipS
 // The compiled (io, P, N, Q) set of the chunked scan.
 #define SSD_SCAN_VARIANT(IO, T, P, N, Q)                                    \
     {IO, P, N, Q, &launch_chunk_prep_t<T, P, N, Q>,                         \
-     &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>},
+     &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>, false},
 
 // bf16 shapes served by the transposing-read kernels of ssd_scan_tr.hip.
 #define SSD_SCAN_VARIANT_TR(P, N, Q)                                        \
     {1, P, N, Q, &launch_chunk_prep_t<uint16_t, P, N, Q>,                   \
-     &scan_tr_state_##P##_##N##_##Q, &scan_tr_output_##P##_##N##_##Q},
+     &scan_tr_state_##P##_##N##_##Q, &scan_tr_output_##P##_##N##_##Q, true},
 
 static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 16, 16, 32)

@@ -69,6 +69,9 @@ struct ScanVariant {
     ScanLaunchFn chunk_prep;    // dt transform, chunk cumsum, weights, C.B^T tiles
     ScanLaunchFn chunk_state;   // segment states
     ScanLaunchFn chunk_output;  // outputs with the carried state
+    // the output kernel forms each segment's incoming state from the earlier
+    // segments' end states itself (no separate state pass)
+    bool output_combines_segments;
 };
 
 // C.B^T tiles of one (row, chunk, group): for every 16-token row block I and

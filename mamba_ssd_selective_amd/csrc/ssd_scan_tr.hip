@@ -650,6 +650,20 @@ struct TrScan {
             }
     }
 
+    // h = m h + src (h = src when m = 0)
+    __device__ __forceinline__ void state_carry(float m, const float* __restrict__ src) {
+#pragma unroll
+        for (int t = 0; t < NBW; ++t)
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb) {
+                const float4 v = *reinterpret_cast<const float4*>(
+                    src + (16 * pb + r16) * N + 16 * (nb + t) + 4 * g);
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[t][pb][r] = m != 0.0f ? fmaf(m, h[t][pb][r], vv[r]) : vv[r];
+            }
+    }
+
     __device__ __forceinline__ void state_store(float* __restrict__ dst) const {
         if (!st()) return;
 #pragma unroll
@@ -686,11 +700,18 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
     k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
     const int64_t bh = it.b * a.H + it.h;
-    // the incoming state first: its load is the longest wait of the set-up
+    // the incoming state first: its loads are the longest wait of the set-up.
+    // Output kernel: the initial state (or zero) carried through the end
+    // states of the earlier segments, h = m_s h + S_s for s < seg (m_s = 0 at a
+    // sequence reset: h = S_s).
     if (!kOut || k.st_wave_) {
-        if (kOut && a.nseg > 1) k.state_load(a.seg_state + (bh * a.nseg + it.seg) * P * N);
-        else if (kOut) k.state_load(a.init ? a.init + bh * P * N : nullptr);
-        else k.state_load(nullptr);
+        k.state_load(kOut && a.init ? a.init + bh * P * N : nullptr);
+        if constexpr (kOut) {
+            for (int s2 = 0; s2 < it.seg; ++s2) {
+                const float m = a.seg_mult[bh * a.nseg + s2];
+                k.state_carry(m, a.seg_state + (bh * a.nseg + s2) * P * N);
+            }
+        }
     }
     k.L = static_cast<int>(a.L);
     k.nc = a.nc;
