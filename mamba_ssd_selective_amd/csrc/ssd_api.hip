@@ -277,7 +277,9 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
     if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
         return SSD_ERR_BAD_SHAPE;
     if (nheads % ngroups != 0) return SSD_ERR_BAD_SHAPE;
-    if (batch * nheads > (int64_t(1) << 31) || headdim > (int64_t(1) << 20))
+    // grid: one block per (row, head) (and, for few of them, per 8 or more of
+    // its state rows), below 2^31
+    if (headdim > (int64_t(1) << 20) || batch * nheads * ((headdim + 7) / 8) >= (int64_t(1) << 31))
         return SSD_ERR_BAD_SHAPE;
     if (dstate != 16 && dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
         return SSD_ERR_UNSUPPORTED;

@@ -889,14 +889,23 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
 }
 
 // ===========================================================================
-// One decode token.  grid = batch*H, 256 threads; N/4 lanes per state row
-// (one float4 each), 256/(N/4) rows per pass.  Uses the same dt transform and
-// decay functions as the chunked path.
-template <typename T, int N>
+// One decode token.  256 threads; N/4 lanes per state row (one float4 each),
+// so RP = 256/(N/4) rows per pass.  Two layouts of the grid:
+//  kSplit = false: one block per (row, head), looping over its P rows RP at a
+//    time (enough blocks in flight hide the latency: large batches);
+//  kSplit = true: one block per (row, head) and 2 RP rows, whose loads are
+//    all issued before any arithmetic (few rows x heads: the latency of one
+//    block is the time of the step).
+// Uses the same dt transform and decay functions as the chunked path.
+template <typename T, int N, bool kSplit>
 __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
     constexpr int TPR = N / 4;
     constexpr int RP = 256 / TPR;
-    const int64_t bh = blockIdx.x;
+    constexpr int U = kSplit ? 2 : 1;  // passes whose loads are issued together
+    const int pblocks = kSplit ? (a.P + RP * U - 1) / (RP * U) : 1;
+    const int64_t bh = blockIdx.x / pblocks;
+    const int p_first = kSplit ? static_cast<int>(blockIdx.x % pblocks) * RP * U : 0;
+    const int p_end = kSplit ? min(a.P, p_first + RP * U) : a.P;
     const int64_t b = bh / a.H;
     const int h = static_cast<int>(bh % a.H);
     const int g = group_of_head(h, a.H / a.G);
@@ -915,27 +924,42 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
         bv[k] = Io<T>::to_f32(Bp[(b * a.G + g) * N + 4 * cc + k]);
         cv[k] = Io<T>::to_f32(Cp[(b * a.G + g) * N + 4 * cc + k]);
     }
-    for (int p0 = 0; p0 < a.P; p0 += RP) {
-        const int p = p0 + rr;
-        float part = 0.0f;
-        float xv = 0.0f;
-        if (p < a.P) {
-            xv = Io<T>::to_f32(x[bh * a.P + p]);
-            float4* sp = reinterpret_cast<float4*>(a.state + (bh * a.P + p) * N + 4 * cc);
-            float4 s = *sp;
-            const float u = dtv * xv;
-            s.x = fmaf(dA, s.x, u * bv[0]);
-            s.y = fmaf(dA, s.y, u * bv[1]);
-            s.z = fmaf(dA, s.z, u * bv[2]);
-            s.w = fmaf(dA, s.w, u * bv[3]);
-            *sp = s;
-            part = s.x * cv[0] + s.y * cv[1] + s.z * cv[2] + s.w * cv[3];
+    for (int p0 = p_first; p0 < p_end; p0 += RP * U) {
+        float4 st[U];
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + RP * u + rr;
+            st[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            xv[u] = 0.0f;
+            if (p < p_end) {
+                st[u] = *reinterpret_cast<const float4*>(a.state + (bh * a.P + p) * N + 4 * cc);
+                xv[u] = Io<T>::to_f32(x[bh * a.P + p]);
+            }
         }
 #pragma unroll
-        for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-        if (p < a.P && cc == 0) y[bh * a.P + p] = Io<T>::from_f32(part + Dh * xv);
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + RP * u + rr;
+            float part = 0.0f;
+            if (p < p_end) {
+                float4 s = st[u];
+                const float uu = dtv * xv[u];
+                s.x = fmaf(dA, s.x, uu * bv[0]);
+                s.y = fmaf(dA, s.y, uu * bv[1]);
+                s.z = fmaf(dA, s.z, uu * bv[2]);
+                s.w = fmaf(dA, s.w, uu * bv[3]);
+                *reinterpret_cast<float4*>(a.state + (bh * a.P + p) * N + 4 * cc) = s;
+                part = s.x * cv[0] + s.y * cv[1] + s.z * cv[2] + s.w * cv[3];
+            }
+#pragma unroll
+            for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+            if (p < p_end && cc == 0) y[bh * a.P + p] = Io<T>::from_f32(part + Dh * xv[u]);
+        }
     }
 }
+
+// Rows x heads below which a decode step splits each head's rows over blocks.
+constexpr int64_t kDecodeSplitBelow = 1024;
 
 // ===========================================================================
 // Launchers.
@@ -969,8 +993,15 @@ static hipError_t launch_chunk_scan_t(const ScanArgs& a, int64_t nblocks, hipStr
 
 template <typename T, int N>
 static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((state_update_kernel<T, N>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(256), 0, st, a);
+    if (nblocks < kDecodeSplitBelow) {
+        const int64_t rows = 2 * (256 / (N / 4));
+        hipLaunchKernelGGL((state_update_kernel<T, N, true>),
+                           dim3(static_cast<unsigned>(nblocks * ((a.P + rows - 1) / rows))),
+                           dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((state_update_kernel<T, N, false>), dim3(static_cast<unsigned>(nblocks)),
+                           dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 

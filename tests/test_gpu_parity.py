@@ -137,12 +137,15 @@ def test_chunk_size_sweep_config1_shapes(Q):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("PN", [(16, 16), (64, 128), (64, 256), (32, 64)])
-def test_decode_step_parity(io, PN):
+@pytest.mark.parametrize("PN", [(16, 16), (64, 128), (64, 256), (32, 64), (24, 32), (80, 16)])
+@pytest.mark.parametrize("bH", [(5, 8), (16, 64)], ids=["few_heads", "many_heads"])
+def test_decode_step_parity(io, PN, bH):
+    """One decode token three times; both grid layouts of the update (few rows x
+    heads split each head's rows over blocks, many loop over them)."""
     import torch
     import mamba_ssd_selective_amd as ssd
     P, N = PN
-    b, H, G = 5, 8, 2
+    (b, H), G = bH, 2
     rng = np.random.default_rng(P * 1000 + N)
     p = workloads.random_problem(rng, b, 3, H, P, N, G, io=io, init=True)
     t = to_dev(p, io)
