@@ -463,6 +463,9 @@ struct TrScan {
         const TrMeta<Q>* M = mo[K];
         const char* H = ho[K];
 
+        // chunk c+1's x copy first (its source is the one input no earlier
+        // kernel has read, so it may come from HBM)
+        if (has_next) copies(-1, c, Xn, Bn, Mn);
         const int i = 16 * I + r16;
         const int m0 = 16 * I;
         const float cs_i = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * i);
@@ -526,10 +529,7 @@ struct TrScan {
         for (int pb = 0; pb < G_::PB; ++pb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[pb][r] *= sc;
-        if (has_next) {
-            load_c(c + 1);  // this chunk's C rows are consumed
-            copies(-1, c, Xn, Bn, Mn);
-        }
+        if (has_next) load_c(c + 1);  // this chunk's C rows are consumed
 
         // intra-chunk outputs y^T += x^T G^T over the k steps up to the
         // diagonal one
@@ -650,18 +650,44 @@ struct TrScan {
             }
     }
 
-    // h = m h + src (h = src when m = 0)
-    __device__ __forceinline__ void state_carry(float m, const float* __restrict__ src) {
+    // h = m_s h + S_s over the segments s < count in order (m_s = 0 at a
+    // sequence reset: h = S_s); mult[s] and the P x N states[s] as written by
+    // the segment-state kernel.  The loads of kCarryBatch segments are issued
+    // before any of them is combined.
+    static constexpr int kCarryBatch = 3;
+    __device__ __forceinline__ void state_carry(const float* __restrict__ mult,
+                                                const float* __restrict__ states, int count) {
+        for (int s0 = 0; s0 < count; s0 += kCarryBatch) {
+            float4 v[kCarryBatch][NBW][G_::PB];
+            float m[kCarryBatch];
 #pragma unroll
-        for (int t = 0; t < NBW; ++t)
+            for (int u = 0; u < kCarryBatch; ++u) {
+                if (s0 + u < count) {
+                    m[u] = mult[s0 + u];
+                    const float* src = states + static_cast<int64_t>(s0 + u) * P * N;
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) {
-                const float4 v = *reinterpret_cast<const float4*>(
-                    src + (16 * pb + r16) * N + 16 * (nb + t) + 4 * g);
-                const float vv[4] = {v.x, v.y, v.z, v.w};
+                    for (int t = 0; t < NBW; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) h[t][pb][r] = m != 0.0f ? fmaf(m, h[t][pb][r], vv[r]) : vv[r];
+                        for (int pb = 0; pb < G_::PB; ++pb)
+                            v[u][t][pb] = *reinterpret_cast<const float4*>(
+                                src + (16 * pb + r16) * N + 16 * (nb + t) + 4 * g);
+                }
             }
+#pragma unroll
+            for (int u = 0; u < kCarryBatch; ++u) {
+                if (s0 + u < count) {
+#pragma unroll
+                    for (int t = 0; t < NBW; ++t)
+#pragma unroll
+                        for (int pb = 0; pb < G_::PB; ++pb) {
+                            const float vv[4] = {v[u][t][pb].x, v[u][t][pb].y, v[u][t][pb].z, v[u][t][pb].w};
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                h[t][pb][r] = m[u] != 0.0f ? fmaf(m[u], h[t][pb][r], vv[r]) : vv[r];
+                        }
+                }
+            }
+        }
     }
 
     __device__ __forceinline__ void state_store(float* __restrict__ dst) const {
@@ -700,19 +726,6 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
     k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
     const int64_t bh = it.b * a.H + it.h;
-    // the incoming state first: its loads are the longest wait of the set-up.
-    // Output kernel: the initial state (or zero) carried through the end
-    // states of the earlier segments, h = m_s h + S_s for s < seg (m_s = 0 at a
-    // sequence reset: h = S_s).
-    if (!kOut || k.st_wave_) {
-        k.state_load(kOut && a.init ? a.init + bh * P * N : nullptr);
-        if constexpr (kOut) {
-            for (int s2 = 0; s2 < it.seg; ++s2) {
-                const float m = a.seg_mult[bh * a.nseg + s2];
-                k.state_carry(m, a.seg_state + (bh * a.nseg + s2) * P * N);
-            }
-        }
-    }
     k.L = static_cast<int>(a.L);
     k.nc = a.nc;
     k.c_begin = it.seg * a.cps;
@@ -786,9 +799,14 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
             if (c + 1 < k.c_end) k.template chunk_out<1>(c + 1, s.x[0], s.b[0], s.m[0]);
         }
     } else {
-        // incoming state (loaded above): bf16 operand copy in H[0] (output kernel)
+        // the first chunk's copies, then (in flight together with them) the
+        // incoming state.  Output kernel: the initial state (or zero) carried
+        // through the end states of the earlier segments, and its bf16 operand
+        // copy in H[0].
         k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+        k.state_load(kOut && a.init ? a.init + bh * P * N : nullptr);
         if constexpr (kOut) {
+            if (k.st()) k.state_carry(a.seg_mult + bh * a.nseg, a.seg_state + bh * a.nseg * P * N, it.seg);
             if (k.st()) {
 #pragma unroll
                 for (int t = 0; t < S_::NBW; ++t)
