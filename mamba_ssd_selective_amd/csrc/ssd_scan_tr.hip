@@ -126,6 +126,13 @@ __device__ __forceinline__ uint32_t lds_keep(uint32_t a) {
     asm volatile("" : "+v"(a));
     return a;
 }
+// A wave-uniform value made opaque at its point of use: what is derived from
+// it there (copy destinations, guards) is recomputed by a scalar instruction
+// or two instead of being held in scalar registers across the chunk loop.
+__device__ __forceinline__ int s_opaque(int v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
 // Pointer into the LDS object `obj` at absolute LDS address a (inside obj).
 __device__ __forceinline__ const SSD_LDS char* lds_at(const void* obj, uint32_t a) {
     return (const SSD_LDS char*)obj + (a - lds_addr(obj));
@@ -212,7 +219,7 @@ template <int W>
 __device__ __forceinline__ void dma_one(char* lds_tile, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                         int kk, int wave) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (SSD_LDS void*)(lds_tile + (wave + W * kk) * 1024), 16, voff, 0, 0, 0);
+        rs, (SSD_LDS void*)(lds_tile + (s_opaque(wave) + W * kk) * 1024), 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int stride) {
@@ -291,9 +298,10 @@ struct TrScan {
 
     __device__ __forceinline__ TrScan(const ScanArgs& args) : a(args) {}
 
+    // rows of chunk c inside the sequence (c * Q < L < 2^31)
     __device__ __forceinline__ int rows_in(int c) const {
-        const int64_t rem = static_cast<int64_t>(L) - static_cast<int64_t>(c) * Q;
-        return rem < Q ? static_cast<int>(rem) : Q;
+        const int rem = L - c * Q;
+        return rem < Q ? rem : Q;
     }
 
     __device__ __forceinline__ void load_c(int c) {
@@ -322,7 +330,7 @@ struct TrScan {
             rows_rsrc(xg + static_cast<int64_t>(c) * Q * (xstride / 2), rows_in(c), xstride);
 #pragma unroll
         for (int kk = 0; kk < XI; ++kk)
-            if (NXI % W == 0 || wave + W * kk < NXI) dma_one<W>(sX, rs, xv[kk], kk, wave);
+            if (NXI % W == 0 || s_opaque(wave) + W * kk < NXI) dma_one<W>(sX, rs, xv[kk], kk, wave);
     }
     __device__ __forceinline__ void dma_b(char* sB, int c, int k0, int k1) const {
         if (k0 < k1) {
@@ -330,7 +338,7 @@ struct TrScan {
                 rows_rsrc(bg + static_cast<int64_t>(c) * Q * (bstride / 2), rows_in(c), bstride);
 #pragma unroll
             for (int kk = 0; kk < BI; ++kk)
-                if (kk >= k0 && kk < k1 && (NBI % W == 0 || wave + W * kk < NBI))
+                if (kk >= k0 && kk < k1 && (NBI % W == 0 || s_opaque(wave) + W * kk < NBI))
                     dma_one<W>(sB, rs, bv[kk], kk, wave);
         }
     }
@@ -351,7 +359,10 @@ struct TrScan {
         if constexpr (kSeq) {
             if (mw == (NPC + kWave - 1) / kWave && lane < Q / 4) {
                 const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sqg + static_cast<int64_t>(c) * Q, rows_in(c), 4);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(sM->seq), 16, 16 * lane, 0, 0, 0);
+                // destination formed from its 32-bit LDS address (a generic-pointer
+                // form of it can hit an instruction-selection fault)
+                const uint32_t dst = lds_addr(sM) + static_cast<uint32_t>(offsetof(TrMeta<Q>, seq));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (SSD_LDS void*)(uintptr_t)dst, 16, 16 * lane, 0, 0, 0);
             }
         }
     }
@@ -370,9 +381,10 @@ struct TrScan {
         // token 16J + 4g + r of tile J is kept when r <= lim: all of a tile left
         // of the diagonal, r <= r16 - 4g on it, none right of it
         int tdiag = r16 - 4 * g;
+        int Iv = I;
         // opaque to the optimizer: keeps the per-element compares here instead
         // of hoisting them out of the chunk loop as 64-bit lane masks
-        asm volatile("" : "+v"(tdiag));
+        asm volatile("" : "+v"(tdiag), "+v"(Iv));
         float out[8];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
@@ -387,8 +399,8 @@ struct TrScan {
             const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
             const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
             const int sqv[4] = {sq4.x, sq4.y, sq4.z, sq4.w};
-            const int lim = J < I ? 3 : (J == I ? tdiag : -1);
-            const int dlim = J == I ? tdiag : -1;  // D on the diagonal element
+            const int lim = J < Iv ? 3 : (J == Iv ? tdiag : -1);
+            const int dlim = J == Iv ? tdiag : -1;  // D on the diagonal element
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 bool keep = r <= lim;
