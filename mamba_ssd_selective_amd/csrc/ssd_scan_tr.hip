@@ -372,12 +372,12 @@ struct TrScan {
         dma_meta(sM, c);
     }
 
-    // G^T fragment of k step u, exact form: lane column i = 16I + r16, tokens
-    // j in the k order above; G[i][j] = (C_i . B_j) exp(cs_i - cs_j) dt_j,
-    // masked to j <= i and (with sequence ids) seq_j = seq_i; D[h] is added on
-    // the diagonal (the D x skip rides on the same MFMA).
-    __device__ __forceinline__ Frag<uint16_t> g_exact(const uint4& t, const void* mobj, uint32_t mq, int u, float cs_i,
-                                                      int seq_i) const {
+    // Factors of the G^T fragment of k step u (tiles J = 2u, 2u+1; element e
+    // is token j_e in the k order above) for lane column i = 16I + r16, in
+    // the exact form: f_e = [j_e <= i] [seq_j = seq_i] exp(cs_i - cs_j) dt_j,
+    // so that G[i][j_e] = (C_i . B_j) f_e.
+    __device__ __forceinline__ void exact_factors(float (&f)[8], const void* mobj, uint32_t mq, int u,
+                                                  float cs_i, int seq_i) const {
         // token 16J + 4g + r of tile J is kept when r <= lim: all of a tile left
         // of the diagonal, r <= r16 - 4g on it, none right of it
         int tdiag = r16 - 4 * g;
@@ -385,7 +385,6 @@ struct TrScan {
         // opaque to the optimizer: keeps the per-element compares here instead
         // of hoisting them out of the chunk loop as 64-bit lane masks
         asm volatile("" : "+v"(tdiag), "+v"(Iv));
-        float out[8];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
             const int J = 2 * u + hp;
@@ -394,58 +393,50 @@ struct TrScan {
             const float4 dt4 = lds_ld<float4>(mobj, mq + off + offsetof(TrMeta<Q>, dt));
             int4 sq4 = make_int4(0, 0, 0, 0);
             if constexpr (kSeq) sq4 = lds_ld<int4>(mobj, mq + off + offsetof(TrMeta<Q>, seq));
-            const uint32_t d0 = hp ? t.z : t.x, d1 = hp ? t.w : t.y;
-            const float cbv[4] = {bf_lo(d0), bf_hi(d0), bf_lo(d1), bf_hi(d1)};
             const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
             const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
             const int sqv[4] = {sq4.x, sq4.y, sq4.z, sq4.w};
             const int lim = J < Iv ? 3 : (J == Iv ? tdiag : -1);
-            const int dlim = J == Iv ? tdiag : -1;  // D on the diagonal element
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 bool keep = r <= lim;
                 if constexpr (kSeq) keep = keep && sqv[r] == seq_i;
                 // masked elements may overflow here; the select drops them
-                const float v = cbv[r] * decay_exp(cs_i - csv[r]) * dtv[r];
-                out[4 * hp + r] = (keep ? v : 0.0f) + (r == dlim ? Dh : 0.0f);
+                f[4 * hp + r] = keep ? decay_exp(cs_i - csv[r]) * dtv[r] : 0.0f;
             }
         }
-        return frag_from_f32<uint16_t>(out);
     }
 
-    // Factored form, k steps strictly left of row block I (all j < 16I):
-    // G[i][j] = r_i * (C_i . B_j) c_j with c_j = [seq_j = seq_m] exp(cs_m - cs_j) dt_j
-    // (m = 16I; c0, c1: this wave's column factors of the step's two tiles) and
-    // the row factor r_i applied to the accumulator at the end.
-    __device__ __forceinline__ Frag<uint16_t> g_factored(const uint4& t, const float4& c0,
-                                                         const float4& c1) const {
-        const float v[8] = {bf_lo(t.x) * c0.x, bf_hi(t.x) * c0.y, bf_lo(t.y) * c0.z,
-                            bf_hi(t.y) * c0.w, bf_lo(t.z) * c1.x, bf_hi(t.z) * c1.y,
-                            bf_lo(t.w) * c1.z, bf_hi(t.w) * c1.w};
-        return frag_from_f32<uint16_t>(v);
-    }
-
-    // Factored form of the diagonal k step u = I/2 (tiles 2u, 2u+1): the
-    // diagonal tile keeps j <= i and carries D[h] / r_i on its diagonal (the
-    // row factor r_i then restores D[h]); a tile right of the diagonal is zero.
-    __device__ __forceinline__ Frag<uint16_t> g_diag(const uint4& t, const float4& c0,
-                                                     const float4& c1, float dr) const {
-        int tdiag = r16 - 4 * g;
-        asm volatile("" : "+v"(tdiag));
-        const bool odd = I & 1;
-        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    // G^T fragment from a C.B^T tile pair and per-element factors f (both
+    // forms).  Factored form, k steps left of the diagonal one:
+    // G[i][j] = r_i (C_i . B_j) c_j with c_j = [seq_j = seq_m] exp(cs_m - cs_j) dt_j
+    // (m = 16I) and the row factor r_i applied to the accumulator at the end.
+    // On the diagonal step (u = I/2) the tile right of the diagonal is zero,
+    // the diagonal tile keeps j <= i, and dd is added on the diagonal element:
+    // D[h] / r_i in the factored form (r_i then restores D[h]), D[h] in the
+    // exact form (whose factors already hold the masks).
+    __device__ __forceinline__ Frag<uint16_t> g_apply(const uint4& t, const float (&f)[8], bool diag,
+                                                      float dd) const {
         const uint32_t d[4] = {t.x, t.y, t.z, t.w};
         float out[8];
+        if (!diag) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int r = e & 3;
-            const float cbv = (e & 1) ? bf_hi(d[e >> 1]) : bf_lo(d[e >> 1]);
-            // tile 2u is the diagonal one for even I (and left of it for odd I);
-            // tile 2u+1 is the diagonal one for odd I (and right of it for even I)
-            const bool on_diag = (e < 4) ? !odd : odd;
-            const bool keep = (e < 4) ? (odd || r <= tdiag) : (odd && r <= tdiag);
-            const float v = keep ? cbv * cv[e] : 0.0f;
-            out[e] = (on_diag && r == tdiag) ? v + dr : v;
+            for (int e = 0; e < 8; ++e) out[e] = ((e & 1) ? bf_hi(d[e >> 1]) : bf_lo(d[e >> 1])) * f[e];
+        } else {
+            int tdiag = r16 - 4 * g;
+            asm volatile("" : "+v"(tdiag));
+            const bool odd = I & 1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = e & 3;
+                const float cbv = (e & 1) ? bf_hi(d[e >> 1]) : bf_lo(d[e >> 1]);
+                // tile 2u is the diagonal one for even I (and left of it for odd I);
+                // tile 2u+1 is the diagonal one for odd I (and right of it for even I)
+                const bool on_diag = (e < 4) ? !odd : odd;
+                const bool keep = (e < 4) ? (odd || r <= tdiag) : (odd && r <= tdiag);
+                const float v = keep ? cbv * f[e] : 0.0f;
+                out[e] = (on_diag && r == tdiag) ? v + dd : v;
+            }
         }
         return frag_from_f32<uint16_t>(out);
     }
@@ -458,6 +449,41 @@ struct TrScan {
         } else {
             dma_b(Bn, c + 1, BI * s / G_::KQ, BI * (s + 1) / G_::KQ);
             if (s == 0) dma_meta(Mn, c + 1);
+        }
+    }
+
+    // Row i of y (lane column i, p = 16 pb + 4 g + r in the accumulators) as
+    // bf16, scaled by fin.  Lanes of 16-lane rows g and g ^ 1 swap p blocks
+    // (q, q + 1) so that each lane holds 8 consecutive p: p0 = 16 (g & 1) +
+    // 8 (g >> 1) and p0 + 32; a store then writes 64 contiguous bytes of each
+    // of 16 rows.  y is not read again, so the stores are non-temporal.  All
+    // lanes take part in the swap; only rows inside the sequence are stored.
+    static constexpr int kYStores = G_::PB / 2;  // store instructions per row block
+    __device__ __forceinline__ void store_y(const f32x4_t (&y)[G_::PB], float fin, int c, int i, int valid) const {
+        static_assert(G_::PB == 4, "two swapped block pairs");
+        typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+        uint32_t yw[G_::PB][2];
+#pragma unroll
+        for (int pb = 0; pb < G_::PB; ++pb) {
+            yw[pb][0] = pack_bf16x2(y[pb][0] * fin, y[pb][1] * fin);
+            yw[pb][1] = pack_bf16x2(y[pb][2] * fin, y[pb][3] * fin);
+        }
+        // odd rows of the first operand trade places with even rows of the second
+#pragma unroll
+        for (int q = 0; q < G_::PB; q += 2)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const auto r = __builtin_amdgcn_permlane16_swap(yw[q][w], yw[q + 1][w], false, false);
+                yw[q][w] = r[0];
+                yw[q + 1][w] = r[1];
+            }
+        if (i < valid) {
+            uint16_t* yp = yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2) + 16 * (g & 1) + 8 * (g >> 1);
+#pragma unroll
+            for (int q = 0; q < G_::PB; q += 2) {
+                const u4 v = {yw[q][0], yw[q][1], yw[q + 1][0], yw[q + 1][1]};
+                __builtin_nontemporal_store(v, reinterpret_cast<u4*>(yp + 16 * q));
+            }
         }
     }
 
@@ -529,7 +555,7 @@ struct TrScan {
         // decays by at most kDiagSpan (r_i >= e^-kDiagSpan); else the exact form
         const bool wfast = !__builtin_amdgcn_ballot_w64(rising) && (!kSeq || seq_m == seq_e) &&
                            cs_m - cs_e <= kDiagSpan;
-        float sc, fin = 1.0f, dr = 0.0f;
+        float sc, fin = 1.0f, dr = Dh;
         if (wfast) {
             fin = decay_exp(cs_i - cs_m);  // r_i
             dr = Dh / fin;
@@ -550,38 +576,33 @@ struct TrScan {
         for (int s = 0; s < G_::KQ; ++s) {
             if (s <= sd) {
                 Frag<uint16_t> xf[G_::PB];
-                float4 c0, c1;
+                float f[8];
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = tr_frag<G_::XROW>(X, xa[K] ^ (32 * pb), s);
                 if (wfast) {
-                    c0 = lds_ld<float4>(cjo, cja + 128 * s);
-                    c1 = lds_ld<float4>(cjo, cja + 128 * s + 64);
+                    const float4 c0 = lds_ld<float4>(cjo, cja + 128 * s);
+                    const float4 c1 = lds_ld<float4>(cjo, cja + 128 * s + 64);
+                    f[0] = c0.x; f[1] = c0.y; f[2] = c0.z; f[3] = c0.w;
+                    f[4] = c1.x; f[5] = c1.y; f[6] = c1.z; f[7] = c1.w;
+                } else {
+                    exact_factors(f, M, ma[K], s, cs_i, seq_i);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                Frag<uint16_t> gf;
-                if (!wfast) gf = g_exact(cb[s], M, ma[K], s, cs_i, seq_i);
-                else if (s < sd) gf = g_factored(cb[s], c0, c1);
-                else gf = g_diag(cb[s], c0, c1, dr);
+                const Frag<uint16_t> gf = g_apply(cb[s], f, s == sd, dr);
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], xf[pb], gf);
             }
             if (has_next) copies(s, c, Xn, Bn, Mn);
         }
         if (has_next) load_cb(c + 1);  // after the last use
-        if (i < valid) {
-            uint16_t* yp = yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2) + 4 * g;
-#pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb)
-                *reinterpret_cast<uint2*>(yp + 16 * pb) =
-                    make_uint2(pack_bf16x2(y[pb][0] * fin, y[pb][1] * fin),
-                               pack_bf16x2(y[pb][2] * fin, y[pb][3] * fin));
-        }
+        store_y(y, fin, c, i, valid);
         if constexpr (kSeq) seq_prev = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (Q - 1));
-        // this wave's copies of chunk c+1 have landed; the C rows, C.B^T tiles
-        // and y stores issued after them may still be in flight (the first use
-        // of the tiles waits for them)
-        static_assert(G_::NCB + G_::PB < 16, "vmcnt immediate");
-        if (has_next) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (G_::NCB + G_::PB));
+        // this wave's copies of chunk c+1 have landed; the C.B^T tiles and y
+        // stores issued after them may still be in flight (the first use of the
+        // tiles waits for them)
+        constexpr int kLeft = G_::NCB + kYStores;
+        static_assert(kLeft < 16, "vmcnt immediate");
+        if (has_next) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | kLeft);
         __syncthreads();
     }
 
@@ -666,7 +687,7 @@ struct TrScan {
     // sequence reset: h = S_s); mult[s] and the P x N states[s] as written by
     // the segment-state kernel.  The loads of kCarryBatch segments are issued
     // before any of them is combined.
-    static constexpr int kCarryBatch = 3;
+    static constexpr int kCarryBatch = 2;
     __device__ __forceinline__ void state_carry(const float* __restrict__ mult,
                                                 const float* __restrict__ states, int count) {
         for (int s0 = 0; s0 < count; s0 += kCarryBatch) {
