@@ -55,6 +55,11 @@ struct TrWaves {
 constexpr int kRawBufferWord3 = 0x00020000;
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | N);
+}
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -314,14 +319,13 @@ struct TrScan {
         }
     }
 
-    // All NCB pairs from row block I's first (the ones past its own belong to
-    // the next row block, or for the last block are its own): one fixed count of
-    // loads, so the end-of-chunk wait can leave them in flight.
+    // The (I >> 1) + 1 tile pairs of row block I.
     __device__ __forceinline__ void load_cb(int c) {
         const uint4* tiles = reinterpret_cast<const uint4*>(cbg + static_cast<int64_t>(c) * cb_cstride) +
                              cb_pair_base(I) * 64 + lane;
 #pragma unroll
-        for (int u = 0; u < G_::NCB; ++u) cb[u] = tiles[64 * u];
+        for (int u = 0; u < G_::NCB; ++u)
+            if (u <= (I >> 1)) cb[u] = tiles[64 * u];
     }
 
     // Copies of chunk c+1, split so that they spread over the chunk's math.
@@ -600,9 +604,14 @@ struct TrScan {
         // this wave's copies of chunk c+1 have landed; the C.B^T tiles and y
         // stores issued after them may still be in flight (the first use of the
         // tiles waits for them)
-        constexpr int kLeft = G_::NCB + kYStores;
-        static_assert(kLeft < 16, "vmcnt immediate");
-        if (has_next) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | kLeft);
+        static_assert(G_::NCB + kYStores < 16, "vmcnt immediate");
+        if (has_next) {
+            const int nt = (I >> 1) + 1;  // tile loads of this row block
+            if (nt == 1) wait_vmcnt<1 + kYStores>();
+            else if (G_::NCB > 2 && nt == 2) wait_vmcnt<2 + kYStores>();
+            else if (G_::NCB > 3 && nt == 3) wait_vmcnt<3 + kYStores>();
+            else wait_vmcnt<G_::NCB + kYStores>();
+        }
         __syncthreads();
     }
 
