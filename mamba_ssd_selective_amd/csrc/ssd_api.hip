@@ -22,7 +22,8 @@ constexpr size_t kAlign = 256;
 struct Plan {
     int64_t nc = 0;
     int64_t nseg = 1, cps = 1;
-    size_t off_cs = 0, off_dtv = 0, off_wgt = 0, off_cbt = 0;
+    size_t off_cs = 0, off_dtv = 0, off_wgt = 0, off_cbt = 0, off_cmf = 0;
+    bool has_cmf = false;
     size_t off_seg = 0, off_mult = 0, total = 0;
 };
 
@@ -50,6 +51,13 @@ Plan make_plan(const ssd_dims& d, ssd_dtype io) {
     p.off_cbt = off;
     off = align_up(off + static_cast<size_t>(d.batch * p.nc * d.ngroups) *
                              static_cast<size_t>(ssd::cbt_elems_per_chunk_group(d.chunk_size)) * es);
+    const ssd::ScanVariant* var = ssd::find_scan_variant(io, d.headdim, d.dstate, d.chunk_size);
+    if (var != nullptr && var->output_reads_c_copy) {
+        p.has_cmf = true;
+        p.off_cmf = off;
+        off = align_up(off + static_cast<size_t>(d.batch * p.nc * d.ngroups) *
+                                 static_cast<size_t>(d.chunk_size * d.dstate) * es);
+    }
     if (p.nseg > 1) {
         p.off_seg = off;
         off = align_up(off + static_cast<size_t>(bh * p.nseg * d.headdim * d.dstate) * f);
@@ -214,7 +222,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     const ssd::ScanVariant* var = ssd::find_scan_variant(io, P, N, d->chunk_size);
     char* wsb = static_cast<char*>(workspace);
 
-    ssd::ScanArgs sa;
+    ssd::ScanArgs sa{};
     sa.x = x;
     sa.B = B;
     sa.C = C;
@@ -235,6 +243,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     sa.dtv = reinterpret_cast<float*>(wsb + plan.off_dtv);
     sa.wgt = reinterpret_cast<float*>(wsb + plan.off_wgt);
     sa.cbt = wsb + plan.off_cbt;
+    sa.cmf = plan.has_cmf ? wsb + plan.off_cmf : nullptr;
     sa.L = L;
     sa.H = static_cast<int>(H);
     sa.G = static_cast<int>(G);

@@ -239,11 +239,25 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     }
     __syncthreads();
 
+    const int r16 = lane & 15, q = lane >> 4;
+    // ---- the chunk's C rows in the output kernel's operand order: piece
+    // (I, s) holds, lane (r16, q), C[16I + r16][32s + 8q .. +7] (16 bytes)
+    if constexpr (sizeof(T) == 2 && N % 32 == 0) {
+        if (a.cmf != nullptr) {
+            constexpr int KS = N / 32;
+            T* __restrict__ cm = static_cast<T*>(a.cmf) + ((b * a.nc + c) * a.G + g) * static_cast<int64_t>(Q * N);
+            for (int pc = wave; pc < C_::NB * KS; pc += kWaves) {
+                const int I = pc / KS, s = pc % KS;
+                const uint4 v = *reinterpret_cast<const uint4*>(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
+                *reinterpret_cast<uint4*>(cm + (static_cast<int64_t>(pc) * 64 + lane) * 8) = v;
+            }
+        }
+    }
+
     // ---- C.B^T tiles, in pairs (layout at cb_pair_base); half-tile k of pair
     // p is tile (I, 2u + k), zeros when 2u + k > I
     T* __restrict__ out = static_cast<T*>(a.cbt) +
                           ((b * a.nc + c) * a.G + g) * cbt_elems_per_chunk_group(Q);
-    const int r16 = lane & 15, q = lane >> 4;
     constexpr int NPAIR = C_::NB / 2 * (C_::NB / 2 + 1);
     constexpr int NHALF = 2 * NPAIR;
     // two half-tiles per pass (independent accumulators, interleaved products);
@@ -1008,12 +1022,12 @@ static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipS
 // The compiled (io, P, N, Q) set of the chunked scan.
 #define SSD_SCAN_VARIANT(IO, T, P, N, Q)                                    \
     {IO, P, N, Q, &launch_chunk_prep_t<T, P, N, Q>,                         \
-     &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>, false},
+     &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>, false, false},
 
 // bf16 shapes served by the transposing-read kernels of ssd_scan_tr.hip.
 #define SSD_SCAN_VARIANT_TR(P, N, Q)                                        \
     {1, P, N, Q, &launch_chunk_prep_t<uint16_t, P, N, Q>,                   \
-     &scan_tr_state_##P##_##N##_##Q, &scan_tr_output_##P##_##N##_##Q, true},
+     &scan_tr_state_##P##_##N##_##Q, &scan_tr_output_##P##_##N##_##Q, true, true},
 
 static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 16, 16, 32)

@@ -31,6 +31,10 @@ struct ScanArgs {
     float* dtv;             // transformed dt (0 past L)
     float* wgt;             // chunk-state weights
     void* cbt;              // (b, nc, G, tiles, 64, 4) workspace: C.B^T tiles, io type
+    // (b, nc, G, Q/16, N/32, 64, 8) workspace or null: the C rows of each chunk
+    // in the output kernel's operand order (piece (I, s): lane (r16, q) holds
+    // C[16I + r16][32s + 8q .. +7]), io type; written by chunk_prep when set.
+    void* cmf;
     int64_t L;
     int H, G;
     int nc, nseg, cps;      // chunks, segments, chunks per segment
@@ -72,6 +76,8 @@ struct ScanVariant {
     // the output kernel forms each segment's incoming state from the earlier
     // segments' end states itself (no separate state pass)
     bool output_combines_segments;
+    // the output kernel reads the C rows from chunk_prep's operand-order copy
+    bool output_reads_c_copy;
 };
 
 // C.B^T tiles of one (row, chunk, group): for every 16-token row block I and

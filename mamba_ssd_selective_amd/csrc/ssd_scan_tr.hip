@@ -272,7 +272,8 @@ struct TrScan {
     // per-(row, head) / per-(row, group) bases; chunk c adds c times the chunk stride
     const uint16_t* xg;  int xstride;   // x[b][.][h][0], token stride in bytes
     const uint16_t* bg;  int bstride;   // B[b][.][g][0]
-    const uint16_t* cg;                 // C[b][.][g][0] (stride bstride)
+    const uint16_t* cmg;                // C rows in operand order at (b, chunk 0, g)
+    int64_t cm_cstride;                 // elements between chunks of that copy
     uint16_t* yg;                       // y[b][.][h][0]
     const float* mg;                    // metadata block (b, h, chunk 0): [cs | dt | w]
     const int32_t* sqg;                 // seq_idx[b][0]
@@ -295,7 +296,7 @@ struct TrScan {
     uint32_t cjw;            // column factors of this wave + 4 lane
     // chunk-independent source offsets of this wave's copies
     uint32_t xv[XI], bv[BI];
-    uint32_t cv;             // C rows: (16 I + r16) * bstride + 16 g bytes
+    uint32_t cv;             // C rows: byte offset of piece (I, 0), lane's 16 bytes
 
     f32x4_t h[NBW][G_::PB];     // state rows n = 16 (nb + t) + 4g + r, column p = 16pb + r16
     uint4 cr[G_::KN];           // C rows of a chunk (k over n), loaded a chunk ahead
@@ -309,12 +310,14 @@ struct TrScan {
         return rem < Q ? rem : Q;
     }
 
+    // C rows of row block I (k over n) from chunk_prep's operand-order copy:
+    // 1 KB contiguous per k step
     __device__ __forceinline__ void load_c(int c) {
-        const __amdgpu_buffer_rsrc_t rs =
-            rows_rsrc(cg + static_cast<int64_t>(c) * Q * (bstride / 2), rows_in(c), bstride);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(cmg + static_cast<int64_t>(c) * cm_cstride), 0, Q * N * 2, kRawBufferWord3);
 #pragma unroll
         for (int s = 0; s < G_::KN; ++s) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, cv + 64 * s, 0, 0);
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, cv + 1024 * s, 0, 0);
             cr[s] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
@@ -408,6 +411,8 @@ struct TrScan {
                 // masked elements may overflow here; the select drops them
                 f[4 * hp + r] = keep ? decay_exp(cs_i - csv[r]) * dtv[r] : 0.0f;
             }
+            // one half at a time (bounds the registers of this rarely taken path)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -782,7 +787,8 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.bstride = a.G * N * 2;
     k.xg = static_cast<const uint16_t*>(a.x) + (it.b * a.L * a.H + it.h) * P;
     k.bg = static_cast<const uint16_t*>(a.B) + (it.b * a.L * a.G + it.g) * N;
-    k.cg = static_cast<const uint16_t*>(a.C) + (it.b * a.L * a.G + it.g) * N;
+    k.cm_cstride = static_cast<int64_t>(a.G) * Q * N;
+    k.cmg = static_cast<const uint16_t*>(a.cmf) + (it.b * a.nc * a.G + it.g) * static_cast<int64_t>(Q) * N;
     k.yg = static_cast<uint16_t*>(a.y) + (it.b * a.L * a.H + it.h) * P;
     k.mg = a.cs + meta_offset(a, it.b, it.h, 0, Q);
     k.sqg = a.seq_idx ? a.seq_idx + it.b * a.L : nullptr;
@@ -825,7 +831,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
 #pragma unroll
     for (int kk = 0; kk < S_::BI; ++kk)
         k.bv[kk] = lds_keep(dma_voff<G_::BROW, S_::W>(kk, k.wave, k.lane, k.bstride));
-    k.cv = lds_keep(static_cast<uint32_t>((16 * k.I + k.r16) * k.bstride + 16 * k.g));
+    k.cv = lds_keep(static_cast<uint32_t>(k.I * G_::KN * 1024 + 16 * k.lane));
 
     // Role set-up, chunk loop and final stores per role, so that each role's
     // registers are live only in its own code; both roles pass the same number

@@ -56,17 +56,19 @@ def test_workspace_and_segments(lib):
     ws = ssd.workspace_bytes(1, 8192, 64, 64, 128, 8, 128)
     # chunk metadata (cs, dt, weights: fp32 per row, head, token), C.B^T tiles
     # (lower-triangular 16x16 bf16 tiles in 20 pairs of 64 lanes x 8 elements
-    # per row, chunk, group), segment states (fp32 P x N per row, head,
-    # segment) and segment multipliers
+    # per row, chunk, group), the C rows in the output kernel's operand order
+    # (bf16 Q x N per row, chunk, group), segment states (fp32 P x N per row,
+    # head, segment) and segment multipliers
     meta = 3 * 64 * 8192 * 4
     tiles = 64 * 8 * 20 * 512 * 2
+    cops = 64 * 8 * 128 * 128 * 2
     seg = 64 * 4 * 64 * 128 * 4 + 256 * math.ceil(64 * 4 * 4 / 256)
-    assert ws == meta + tiles + seg
+    assert ws == meta + tiles + cops + seg
     assert ssd.segments(1, 8192, 64, 64, 128, 8, 128) == 4
     # enough rows x heads: one segment, no segment scratch
     assert ssd.segments(64, 4096, 64, 64, 128, 8, 128) == 1
     assert ssd.workspace_bytes(64, 4096, 64, 64, 128, 8, 128) == (
-        3 * 64 * 64 * 4096 * 4 + 64 * 32 * 8 * 20 * 512 * 2)
+        3 * 64 * 64 * 4096 * 4 + 64 * 32 * 8 * 20 * 512 * 2 + 64 * 32 * 8 * 128 * 128 * 2)
     # ragged L: 3 chunks, one segment each
     assert ssd.segments(1, 300, 64, 64, 128, 8, 128) == 3
     assert ssd.workspace_bytes(1, 0, 64, 64, 128, 8, 128) == 0
