@@ -22,7 +22,10 @@ struct ScanArgs {
     const float* D;         // (H) or null
     const float* init;      // (b, H, P, N) or null
     float* final_states;    // (b, H, P, N) or null
-    float* seg_state;       // (b, H, nseg, P, N) workspace
+    // (b, H, nseg, P*N) workspace: [P][N] for the generic kernels; for the
+    // transposing-read kernels in register order, blocks [n-block][p-block]
+    // of 64 lanes x 4 floats (the MFMA accumulator layout of both kernels)
+    float* seg_state;
     float* seg_mult;        // (b, H, nseg) workspace
     // Per-token metadata workspace, one block [cs Q | dt Q | w Q] per (row, head,
     // chunk); cs, dtv and wgt point at the three arrays of block 0 (chunk

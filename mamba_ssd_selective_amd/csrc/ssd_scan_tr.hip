@@ -697,9 +697,16 @@ struct TrScan {
             }
     }
 
+    // Offset of this lane's four values of state block (n-block nb, p-block
+    // pb) in the register-order layout of the segment states: blocks
+    // [nb][pb] of 64 lanes x 4 floats, so that a wave moves 1 KB contiguous.
+    __device__ __forceinline__ int reg_order(int nbk, int pb) const {
+        return ((nbk * G_::PB + pb) * kWave + lane) * 4;
+    }
+
     // h = m_s h + S_s over the segments s < count in order (m_s = 0 at a
-    // sequence reset: h = S_s); mult[s] and the P x N states[s] as written by
-    // the segment-state kernel.  The loads of kCarryBatch segments are issued
+    // sequence reset: h = S_s); mult[s] and the P x N states[s] (register
+    // order) as written by the segment-state kernel.  The loads of kCarryBatch segments are issued
     // before any of them is combined.
     static constexpr int kCarryBatch = 2;
     __device__ __forceinline__ void state_carry(const float* __restrict__ mult,
@@ -716,8 +723,7 @@ struct TrScan {
                     for (int t = 0; t < NBW; ++t)
 #pragma unroll
                         for (int pb = 0; pb < G_::PB; ++pb)
-                            v[u][t][pb] = *reinterpret_cast<const float4*>(
-                                src + (16 * pb + r16) * N + 16 * (nb + t) + 4 * g);
+                            v[u][t][pb] = *reinterpret_cast<const float4*>(src + reg_order(nb + t, pb));
                 }
             }
 #pragma unroll
@@ -737,6 +743,18 @@ struct TrScan {
         }
     }
 
+    // the state in register order (segment states)
+    __device__ __forceinline__ void state_store_reg(float* __restrict__ dst) const {
+        if (!st()) return;
+#pragma unroll
+        for (int t = 0; t < NBW; ++t)
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb)
+                *reinterpret_cast<float4*>(dst + reg_order(nb + t, pb)) =
+                    make_float4(h[t][pb][0], h[t][pb][1], h[t][pb][2], h[t][pb][3]);
+    }
+
+    // the state as [p][n] (final states)
     __device__ __forceinline__ void state_store(float* __restrict__ dst) const {
         if (!st()) return;
 #pragma unroll
@@ -875,7 +893,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
             if (k.want_final) k.state_store(a.final_states + bh * P * N);
         } else {
             const int64_t slot = bh * a.nseg + it.seg;
-            k.state_store(a.seg_state + slot * P * N);
+            k.state_store_reg(a.seg_state + slot * P * N);
             if (threadIdx.x == 0) a.seg_mult[slot] = k.mult;
         }
     }
