@@ -259,42 +259,39 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     T* __restrict__ out = static_cast<T*>(a.cbt) +
                           ((b * a.nc + c) * a.G + g) * cbt_elems_per_chunk_group(Q);
     constexpr int NPAIR = C_::NB / 2 * (C_::NB / 2 + 1);
-    constexpr int NHALF = 2 * NPAIR;
-    // two half-tiles per pass (independent accumulators, interleaved products);
-    // half-tile h is tile (I, J) of pair h/2: I its row block, J = 2u + h % 2
-    auto tile_of = [](int h, int& I, int& J) {
-        const int pidx = h >> 1;
+    // one pair per pass: both tiles share row block I (and its C rows), and
+    // the pair's 8 elements per lane are stored contiguously
+    auto tile_of = [](int pidx, int& I, int& J) {
         int rbk = 0;
 #pragma unroll
         for (int r = 1; r < C_::NB; ++r) rbk += cb_pair_base(r) <= pidx ? 1 : 0;
         I = rbk;
-        J = 2 * (pidx - cb_pair_base(rbk)) + (h & 1);
+        J = 2 * (pidx - cb_pair_base(rbk));
     };
-    for (int h0 = wave; h0 < NHALF; h0 += 2 * kWaves) {
-        const int h1 = h0 + kWaves;
-        int I0, J0, I1, J1;
-        tile_of(h0, I0, J0);
-        tile_of(h1, I1, J1);
-        const bool on0 = J0 <= I0, on1 = h1 < NHALF && J1 <= I1;
+    for (int pidx = wave; pidx < NPAIR; pidx += kWaves) {
+        int I, J0;
+        tile_of(pidx, I, J0);
+        const bool on1 = J0 + 1 <= I;  // the pair's second tile is left of or on the diagonal
         f32x4_t acc0 = acc_zero(), acc1 = acc_zero();
 #pragma unroll
         for (int s = 0; s < C_::KN; ++s) {
-            if (on0) {
-                const Frag<T> bf = frag_load8(sB + (16 * J0 + r16) * C_::SB + 32 * s + 8 * q);
-                const Frag<T> cf = frag_load8(sC + (16 * I0 + r16) * C_::SB + 32 * s + 8 * q);
-                mma(acc0, bf, cf);
-            }
+            const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
+            const Frag<T> bf0 = frag_load8(sB + (16 * J0 + r16) * C_::SB + 32 * s + 8 * q);
+            mma(acc0, bf0, cf);
             if (on1) {
-                const Frag<T> bf = frag_load8(sB + (16 * J1 + r16) * C_::SB + 32 * s + 8 * q);
-                const Frag<T> cf = frag_load8(sC + (16 * I1 + r16) * C_::SB + 32 * s + 8 * q);
-                mma(acc1, bf, cf);
+                const Frag<T> bf1 = frag_load8(sB + (16 * (J0 + 1) + r16) * C_::SB + 32 * s + 8 * q);
+                mma(acc1, bf1, cf);
             }
         }
-        store4_f32(out + (static_cast<int64_t>(h0 >> 1) * 64 + lane) * 8 + 4 * (h0 & 1), acc0[0],
-                   acc0[1], acc0[2], acc0[3]);
-        if (h1 < NHALF)
-            store4_f32(out + (static_cast<int64_t>(h1 >> 1) * 64 + lane) * 8 + 4 * (h1 & 1),
-                       acc1[0], acc1[1], acc1[2], acc1[3]);
+        T* o = out + (static_cast<int64_t>(pidx) * 64 + lane) * 8;
+        if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<uint4*>(o) =
+                make_uint4(pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                           pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3]));
+        } else {
+            store4_f32(o, acc0[0], acc0[1], acc0[2], acc0[3]);
+            store4_f32(o + 4, acc1[0], acc1[1], acc1[2], acc1[3]);
+        }
     }
 }
 
