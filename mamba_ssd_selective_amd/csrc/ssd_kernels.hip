@@ -202,14 +202,26 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         const float cs_last = __shfl(csv[kLastK], kLastLane, kWave);
         const int seq_last = __shfl(sq[kLastK], kLastLane, kWave);
         const int64_t base = meta_offset(a, b, h, c, Q);
+        float wgv[E];
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            const int t = lane * E + k;
-            if (t < Q) {
-                const float wv = decay_exp(cs_last - csv[k]) * dtv[k];
-                a.cs[base + t] = csv[k];
-                a.dtv[base + t] = dtv[k];
-                a.wgt[base + t] = (sq[k] == seq_last) ? wv : 0.0f;
+        for (int k = 0; k < E; ++k)
+            wgv[k] = (sq[k] == seq_last) ? decay_exp(cs_last - csv[k]) * dtv[k] : 0.0f;
+        if constexpr (E == 2) {
+            // this lane's two tokens are adjacent: one 8-byte store per array
+            if (lane * E < Q) {
+                *reinterpret_cast<float2*>(a.cs + base + lane * E) = make_float2(csv[0], csv[1]);
+                *reinterpret_cast<float2*>(a.dtv + base + lane * E) = make_float2(dtv[0], dtv[1]);
+                *reinterpret_cast<float2*>(a.wgt + base + lane * E) = make_float2(wgv[0], wgv[1]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int t = lane * E + k;
+                if (t < Q) {
+                    a.cs[base + t] = csv[k];
+                    a.dtv[base + t] = dtv[k];
+                    a.wgt[base + t] = wgv[k];
+                }
             }
         }
     };
