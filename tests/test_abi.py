@@ -52,7 +52,7 @@ def test_supported_set(lib):
 
 
 def test_workspace_and_segments(lib):
-    # config 1: 64 heads, 64 chunks of 128 -> 4 segments of 16 chunks (256 workgroups)
+    # one 8192-token row, 64 heads: 64 chunks of 128 -> 4 segments of 16 chunks (256 workgroups)
     ws = ssd.workspace_bytes(1, 8192, 64, 64, 128, 8, 128)
     # chunk metadata (cs, dt, weights: fp32 per row, head, token), C.B^T tiles
     # (lower-triangular 16x16 bf16 tiles in 20 pairs of 64 lanes x 8 elements
