@@ -17,10 +17,10 @@ xBC 6144 and dt 64, so H*P = 4096 and 2*G*N = 2048; SSD chunk 128):
   4 prefill_decode b=64 rows of 4352 tokens: 4096-token prefill (Q=128)
                    then 256 single-token state updates
 
-Recipe (seeded by 1000 + config id):
+Recipe (seeded by 1000 + the workload's index in the table above):
   per-head parameters from the parent generator, in order:
     dt_bias ~ U[-4,-2], A = -exp(U[0, ln 16]), D ~ N(0,1)
-  packed lengths (config 2) next: u_i ~ U[ln 64, ln 4096], l_i = e^{u_i}
+  packed lengths (packed_16k) next: u_i ~ U[ln 64, ln 4096], l_i = e^{u_i}
     rescaled to sum to L, floored, remainder given to the largest fractional
     parts (ties to the lower index), each length >= 1;
   per batch row, from SeedSequence(1000+k).spawn(b)[row], in order:
@@ -54,7 +54,7 @@ class Workload:
     init_states: bool = False
     final_states: bool = True
     packed: int = 0         # number of packed sequences (0 = no seq_idx)
-    prefill: Optional[int] = None   # config 4: tokens scanned before decode
+    prefill: Optional[int] = None   # prefill_decode: tokens scanned before decode
     decode_steps: int = 0
 
     @property
