@@ -10,8 +10,12 @@ HBM before timing starts; the step cycles over several copies of the inputs
 so that consecutive steps do not hit in the 256 MB MALL.
 
 Prints ONE JSON line with the throughput, a roofline entry for the dominant
-kernel (chunk_output, timed with HIP events recorded by the library on the
-stream it launches on) and the fp64 CPU oracle timed on the host cores.
+kernel (chunk_output, timed with HIP events that the library binds to its
+dispatch on the stream it launches on, so that they take the dispatch's own
+start and end timestamps) and the fp64 CPU oracle timed on the host cores.
+
+The defaults warm up for about 30 ms (the clocks settle within about 20 ms of
+sustained work) and time about 0.1 s of steps.
 """
 import argparse
 import ctypes
@@ -126,8 +130,8 @@ def cpu_baseline(p, w, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS_BY_NAME))
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 = skip)")
@@ -217,8 +221,8 @@ def main():
 
     def step(i, evs=None, only_output=False):
         """One step.  With evs: records the library's per-kernel events of step i
-        (all kernels, or only chunk_output's pair: every event record is a
-        timestamp packet on the stream, so the timed steps carry just that pair)."""
+        (all kernels, or only chunk_output's pair: every event bound to a dispatch
+        adds work around it, so the timed steps carry just that pair)."""
         s = sets[i % nsets]
         base_ev = 2 * nk * i
         if evs is not None:

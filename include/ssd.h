@@ -140,14 +140,18 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
 
 /* Per-kernel timing hooks (diagnostics).  After a call with events != NULL,
  * every ssd_chunk_scan_fwd / ssd_state_update call made on the same host
- * thread records events[2k] before and events[2k+1] after its k-th kernel
- * launch, on the call's stream, for k < count/2, and stores the number of
- * kernels it launched in *launched (if not NULL).  `events` are hipEvent_t
- * handles the caller created; the library only records them.  Kernel order
- * of the scan: chunk_prep, [chunk_state, state_pass,] chunk_output (the two bracketed
- * kernels run only when ssd_chunk_scan_segments(...) > 1; L = 0 launches one
- * state copy).  A NULL pair events[2k], events[2k+1] skips kernel k.
- * Pass events = NULL to turn the hooks off. */
+ * thread binds events[2k] and events[2k+1] to its k-th kernel dispatch, on
+ * the call's stream, for k < count/2 (hipExtLaunchKernel's start and stop
+ * events): they take that dispatch's own start and end timestamps, so
+ * hipEventElapsedTime of the pair is the kernel's execution time.  The call
+ * stores the number of kernels it launched in *launched (if not NULL).
+ * `events` are hipEvent_t handles the caller created; the library only binds
+ * them.  Kernel order of the scan: chunk_prep, [chunk_state, [state_pass,]]
+ * chunk_output (chunk_state runs only when ssd_chunk_scan_segments(...) > 1,
+ * state_pass only then and for kernels whose output pass does not combine the
+ * segment states itself; L = 0 launches one state copy).  A NULL pair
+ * events[2k], events[2k+1] skips kernel k.  Pass events = NULL to turn the
+ * hooks off. */
 void ssd_set_timing_events(void* const* events, int count, int* launched);
 
 /* Static, human-readable text for a status code (never NULL). */

@@ -92,15 +92,21 @@ struct TimingHooks {
     int* launched = nullptr;
 };
 thread_local TimingHooks g_hooks;
+thread_local ssd::DispatchEvents g_dispatch_events;
 
-// Runs one launch between the k-th pair of timing events (when hooks are set).
+// Runs one launch (one kernel dispatch) with the k-th pair of timing events
+// bound to it (when hooks are set).
 template <typename F>
-hipError_t timed_launch(int& k, hipStream_t st, F&& launch) {
+hipError_t timed_launch(int& k, hipStream_t, F&& launch) {
     const bool rec = g_hooks.events && 2 * k + 1 < g_hooks.count && g_hooks.events[2 * k] &&
                      g_hooks.events[2 * k + 1];
-    if (rec) (void)hipEventRecord(static_cast<hipEvent_t>(g_hooks.events[2 * k]), st);
+    ssd::DispatchEvents& ev = ssd::dispatch_events();
+    if (rec) {
+        ev.start = static_cast<hipEvent_t>(g_hooks.events[2 * k]);
+        ev.stop = static_cast<hipEvent_t>(g_hooks.events[2 * k + 1]);
+    }
     hipError_t e = launch();
-    if (rec) (void)hipEventRecord(static_cast<hipEvent_t>(g_hooks.events[2 * k + 1]), st);
+    ev = ssd::DispatchEvents{};
     ++k;
     if (g_hooks.launched) *g_hooks.launched = k;
     return e;
@@ -123,6 +129,8 @@ ssd_status check_scan_dims(const ssd_dims* d, ssd_dtype io) {
 }
 
 }  // namespace
+
+ssd::DispatchEvents& ssd::dispatch_events() { return g_dispatch_events; }
 
 extern "C" {
 

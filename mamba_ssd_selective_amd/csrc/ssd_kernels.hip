@@ -989,43 +989,37 @@ constexpr int64_t kDecodeSplitBelow = 1024;
 
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st) {
     dim3 grid(static_cast<unsigned>((a.PN / 4 + 255) / 256), static_cast<unsigned>(bh));
-    hipLaunchKernelGGL(state_pass_kernel, grid, dim3(256), 0, st, a);
-    return hipGetLastError();
+    return dispatch(state_pass_kernel, grid, dim3(256), st, a);
 }
 
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, st, src, dst, n);
-    return hipGetLastError();
+    return dispatch(copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                    st, src, dst, n);
 }
 
 template <typename T, int P, int N, int Q>
 static hipError_t launch_chunk_prep_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((chunk_prep_kernel<T, P, N, Q>), dim3(static_cast<unsigned>(nblocks)),
-                       dim3(kThreads), 0, st, a);
-    return hipGetLastError();
+    return dispatch(chunk_prep_kernel<T, P, N, Q>, dim3(static_cast<unsigned>(nblocks)),
+                    dim3(kThreads), st, a);
 }
 
 template <typename T, int P, int N, int Q, bool kOut>
 static hipError_t launch_chunk_scan_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((chunk_scan_kernel<T, P, N, Q, kOut>),
-                       dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st, a);
-    return hipGetLastError();
+    return dispatch(chunk_scan_kernel<T, P, N, Q, kOut>, dim3(static_cast<unsigned>(nblocks)),
+                    dim3(kThreads), st, a);
 }
 
 template <typename T, int N>
 static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipStream_t st) {
     if (nblocks < kDecodeSplitBelow) {
         const int64_t rows = 2 * (256 / (N / 4));
-        hipLaunchKernelGGL((state_update_kernel<T, N, true>),
-                           dim3(static_cast<unsigned>(nblocks * ((a.P + rows - 1) / rows))),
-                           dim3(256), 0, st, a);
-    } else {
-        hipLaunchKernelGGL((state_update_kernel<T, N, false>), dim3(static_cast<unsigned>(nblocks)),
-                           dim3(256), 0, st, a);
+        return dispatch(state_update_kernel<T, N, true>,
+                        dim3(static_cast<unsigned>(nblocks * ((a.P + rows - 1) / rows))),
+                        dim3(256), st, a);
     }
-    return hipGetLastError();
+    return dispatch(state_update_kernel<T, N, false>, dim3(static_cast<unsigned>(nblocks)),
+                    dim3(256), st, a);
 }
 
 // The compiled (io, P, N, Q) set of the chunked scan.

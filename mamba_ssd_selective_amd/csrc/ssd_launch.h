@@ -2,6 +2,7 @@
 // (ssd_api.hip) and the kernels (ssd_kernels.hip).  Internal to libssd.so.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -110,6 +111,25 @@ hipError_t scan_tr_output_64_128_128(const ScanArgs& a, int64_t nblocks, hipStre
 const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q);
 int scan_variant_count();
 const ScanVariant* scan_variant_at(int i);
+
+// Events to bind to this host thread's next kernel dispatch (both null: none).
+// Bound events take the dispatch's own start and end timestamps, so their
+// elapsed time is the kernel's execution alone, without the launch gap and
+// queue packets that separate event records on the stream would include.
+struct DispatchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+DispatchEvents& dispatch_events();
+
+// Every kernel of the library is launched through here.
+template <typename... KArgs, typename... Args>
+inline hipError_t dispatch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                           Args... args) {
+    const DispatchEvents& ev = dispatch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+    return hipGetLastError();
+}
 
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);

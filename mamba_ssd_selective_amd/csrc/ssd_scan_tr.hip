@@ -924,11 +924,9 @@ __global__ __launch_bounds__(TrWaves<kOut>::kThreads) void scan_tr_kernel(ScanAr
 template <int P, int N, int Q, bool kOut>
 hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(nblocks));
-    if (a.seq_idx)
-        hipLaunchKernelGGL((scan_tr_kernel<P, N, Q, kOut, true>), grid, dim3(TrWaves<kOut>::kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((scan_tr_kernel<P, N, Q, kOut, false>), grid, dim3(TrWaves<kOut>::kThreads), 0, st, a);
-    return hipGetLastError();
+    const dim3 block(TrWaves<kOut>::kThreads);
+    if (a.seq_idx) return dispatch(scan_tr_kernel<P, N, Q, kOut, true>, grid, block, st, a);
+    return dispatch(scan_tr_kernel<P, N, Q, kOut, false>, grid, block, st, a);
 }
 
 }  // namespace
