@@ -10,6 +10,7 @@ Three independent formulations of the same operation live here:
 
 * ``scan`` / ``step`` -- the plain sequential recurrence in C (``ssd_oracle.c``),
   the authority every GPU result is compared against;
+* ``scan_bwd`` -- its gradients, by reverse mode of the same recurrence in C;
 * ``dual.quadratic_scan`` -- the brute-force matrix ("dual") form with explicit
   products of per-step decays, for tiny inputs;
 * ``chunked.chunked_scan`` -- the chunk decomposition (chunk states, state
@@ -72,6 +73,11 @@ def _bind(lib):
                                     ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                     dp, dp, dp, dp, dp]
     lib.oracle_ssd_step.restype = ctypes.c_int
+    lib.oracle_ssd_scan_bwd.argtypes = [i64, i64, i64, i64, i64, i64,
+                                        dp, dp, dp, ctypes.c_int, ctypes.c_double,
+                                        ctypes.c_double, dp, dp, dp, dp, dp, ip,
+                                        dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_ssd_scan_bwd.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -137,6 +143,44 @@ def scan(x, dt_raw, A, B, C, *, dt_bias=None, D=None, h_init=None, seq_idx=None,
     if rc != 0:
         raise RuntimeError("oracle_ssd_scan failed with code %d" % rc)
     return y, hf
+
+
+def scan_bwd(x, dt_raw, A, B, C, dy, *, dh_final=None, dt_bias=None, D=None, h_init=None,
+             seq_idx=None, dt_softplus=True, dt_min=0.0, dt_max=float("inf"), nthreads=0,
+             lib=None):
+    """Gradients of the sequential recurrence (reverse mode, fp64) for a loss
+    with gradients dy (b,L,H,P) with respect to y and dh_final (b,H,P,N, or
+    None = 0) with respect to the final state.
+
+    Returns a dict of float64 arrays: dx (b,L,H,P), ddt_raw (b,L,H), dA (H),
+    dB, dC (b,L,G,N), dD (H), ddt_bias (H), dh_init (b,H,P,N).
+    """
+    x, dt_raw, A, B, C, dy = map(_f64, (x, dt_raw, A, B, C, dy))
+    dt_bias, D, h_init, dh_final = map(_f64, (dt_bias, D, h_init, dh_final))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt_raw.shape == (b, L, H) and B.shape == (b, L, G, N) and C.shape == B.shape
+    assert dy.shape == x.shape and A.shape == (H,)
+    for st in (h_init, dh_final):
+        if st is not None:
+            assert st.shape == (b, H, P, N)
+    sp = None
+    if seq_idx is not None:
+        seq_idx = np.ascontiguousarray(np.asarray(seq_idx, dtype=np.int32))
+        assert seq_idx.shape == (b, L)
+        sp = seq_idx.ctypes.data_as(ctypes.c_void_p)
+    out = {"dx": np.empty((b, L, H, P)), "ddt_raw": np.empty((b, L, H)), "dA": np.empty(H),
+           "dB": np.empty((b, L, G, N)), "dC": np.empty((b, L, G, N)), "dD": np.empty(H),
+           "ddt_bias": np.empty(H), "dh_init": np.empty((b, H, P, N))}
+    rc = (lib or _load()).oracle_ssd_scan_bwd(
+        b, L, H, P, N, G, _ptr(x), _ptr(dt_raw), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_min), float(dt_max), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h_init),
+        sp, _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt_raw"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["ddt_bias"]),
+        _ptr(out["dh_init"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_ssd_scan_bwd failed with code %d" % rc)
+    return out
 
 
 def step(state, x, dt_raw, A, B, C, *, dt_bias=None, D=None, dt_softplus=True,
