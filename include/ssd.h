@@ -119,6 +119,50 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* dims, ssd_dtype io, const void* x,
                               const int32_t* seq_idx, void* y, float* final_states,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace ssd_chunk_scan_bwd needs for these dims (0 when
+ * none, and for dims it would reject). */
+size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* dims, ssd_dtype io);
+
+/*
+ * Gradients of ssd_chunk_scan_fwd: the backward pass of the chunked scan that
+ * training runs (RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section 1, operator
+ * family 1: the chunked parallel scan serves training).  Given the forward
+ * inputs and the gradients of a loss with respect to y and to the final
+ * states, writes the gradients with respect to every input.
+ *
+ *   x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D, initial_states,
+ *   seq_idx          the forward call's inputs, same layouts and meaning
+ *   dy       (b, L, H, P)  io dtype: gradient with respect to y
+ *   d_final_states (b, H, P, N) fp32, or NULL = zero: gradient with respect
+ *                          to final_states
+ *   dx       (b, L, H, P)  io dtype output
+ *   ddt      (b, L, H)     fp32 output: gradient with respect to the raw dt
+ *                          (zero where the clamp binds)
+ *   dA       (H)           fp32 output
+ *   dB, dC   (b, L, G, N)  io dtype outputs (summed over each group's heads)
+ *   dD, ddt_bias (H)       fp32 outputs, or NULL to skip
+ *   d_initial_states (b, H, P, N) fp32 output, or NULL to skip
+ *   workspace, workspace_bytes  device scratch of at least
+ *                          ssd_chunk_scan_bwd_workspace_bytes(dims, io) bytes,
+ *                          256-byte aligned; contents on entry are ignored
+ *   stream                 hipStream_t
+ *
+ * No output may overlap an input, another output or the workspace
+ * (SSD_ERR_ALIAS).  Supported set: io = SSD_BF16, headdim 64, dstate 128,
+ * chunk_size 128 (else SSD_ERR_UNSUPPORTED); any b, L (L = 0 gives zero sums
+ * and d_initial_states = d_final_states), H % G == 0.  Deterministic: every
+ * sum is taken in a fixed order, without atomics.
+ */
+ssd_status ssd_chunk_scan_bwd(const ssd_dims* dims, ssd_dtype io, const void* x,
+                              const float* dt, const float* dt_bias, int dt_softplus,
+                              float dt_min, float dt_max, const float* A, const void* B,
+                              const void* C, const float* D, const float* initial_states,
+                              const int32_t* seq_idx, const void* dy,
+                              const float* d_final_states, void* dx, float* ddt, float* dA,
+                              void* dB, void* dC, float* dD, float* ddt_bias,
+                              float* d_initial_states, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /*
  * One decode token per sequence: the per-token recurrent state update (RFC
  * section 1, operator family 1; the state is the fixed-size fp32 SSM state of

@@ -72,6 +72,12 @@ def library():
         lib.ssd_chunk_scan_fwd.argtypes = [dims_p, i, vp, vp, vp, i, f, f, vp, vp, vp, vp, vp,
                                            vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_scan_fwd.restype = i
+        lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [dims_p, i]
+        lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_chunk_scan_bwd.argtypes = [dims_p, i, vp, vp, vp, i, f, f, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_size_t, vp]
+        lib.ssd_chunk_scan_bwd.restype = i
         lib.ssd_state_update.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, vp, vp, i, f, f,
                                          vp, vp, vp, vp, vp, vp]
         lib.ssd_state_update.restype = i
@@ -181,6 +187,67 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size: int, D=None, dt_bias=None,
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd")
     return (y, fs) if return_final_states else y
+
+
+def bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
+                        io=BF16) -> int:
+    d = _dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size)
+    return int(library().ssd_chunk_scan_bwd_workspace_bytes(ctypes.byref(d), io))
+
+
+def chunk_scan_bwd(x, dt, A, B, C, dy, *, chunk_size: int, D=None, dt_bias=None,
+                   initial_states=None, seq_idx=None, d_final_states=None,
+                   dt_softplus: bool = True, dt_limit: Tuple[float, float] = (0.0, math.inf),
+                   workspace=None):
+    """Gradients of ``chunk_scan_fwd`` for a loss with gradients ``dy``
+    (b, L, H, P, x's dtype) with respect to y and ``d_final_states``
+    (b, H, P, N fp32, or None) with respect to the final states.
+
+    Returns a dict: dx (b, L, H, P) and dB, dC (b, L, G, N) in x's dtype;
+    ddt (b, L, H), dA, dD, ddt_bias (H), d_initial_states (b, H, P, N) fp32
+    (dD only when D is given, ddt_bias only when dt_bias is given).
+    """
+    import torch
+    lib = library()
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    io = _io_code(x.dtype)
+    f32 = torch.float32
+    _check(x, "x", (b, L, H, P), x.dtype, dev)
+    _check(B, "B", (b, L, G, N), x.dtype, dev)
+    _check(C, "C", (b, L, G, N), x.dtype, dev)
+    _check(dy, "dy", (b, L, H, P), x.dtype, dev)
+    _check(dt, "dt", (b, L, H), f32, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    _check(initial_states, "initial_states", (b, H, P, N), f32, dev)
+    _check(d_final_states, "d_final_states", (b, H, P, N), f32, dev)
+    _check(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    g = {"dx": torch.empty((b, L, H, P), dtype=x.dtype, device=dev),
+         "ddt": torch.empty((b, L, H), dtype=f32, device=dev),
+         "dA": torch.empty((H,), dtype=f32, device=dev),
+         "dB": torch.empty((b, L, G, N), dtype=x.dtype, device=dev),
+         "dC": torch.empty((b, L, G, N), dtype=x.dtype, device=dev),
+         "dD": torch.empty((H,), dtype=f32, device=dev) if D is not None else None,
+         "ddt_bias": torch.empty((H,), dtype=f32, device=dev) if dt_bias is not None else None,
+         "d_initial_states": torch.empty((b, H, P, N), dtype=f32, device=dev)}
+    d = _dims(b, L, H, P, N, G, chunk_size)
+    need = int(lib.ssd_chunk_scan_bwd_workspace_bytes(ctypes.byref(d), io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_bwd(
+        ctypes.byref(d), io, _ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(initial_states), _ptr(seq_idx), _ptr(dy), _ptr(d_final_states), _ptr(g["dx"]),
+        _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+        _ptr(g["ddt_bias"]), _ptr(g["d_initial_states"]), _ptr(workspace), ws_bytes,
+        _stream_handle(dev))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_bwd")
+    return g
 
 
 def state_update(state, x, dt, A, B, C, *, D=None, dt_bias=None, dt_softplus: bool = True,

@@ -128,6 +128,50 @@ ssd_status check_scan_dims(const ssd_dims* d, ssd_dtype io) {
     return SSD_OK;
 }
 
+// The gradient path's compiled set: bf16, P = 64, N = 128, chunk 128.
+ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
+    if (!d) return SSD_ERR_NULL_ARG;
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1 || d->chunk_size < 1)
+        return SSD_ERR_BAD_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (d->batch > 65535 || d->nheads > 65535 || d->seqlen > (int64_t(1) << 31))
+        return SSD_ERR_BAD_SHAPE;
+    if (io != SSD_BF16 || d->headdim != 64 || d->dstate != 128 || d->chunk_size != 128)
+        return SSD_ERR_UNSUPPORTED;
+    // grids: (row, chunk, group) and (row, head) workgroups below 2^31
+    const int64_t nc = (d->seqlen + d->chunk_size - 1) / d->chunk_size;
+    if (d->batch * nc * d->ngroups >= (int64_t(1) << 31) || d->batch * d->nheads >= (int64_t(1) << 31))
+        return SSD_ERR_BAD_SHAPE;
+    return SSD_OK;
+}
+
+struct BwdPlan {
+    int64_t nc = 0;
+    size_t off_meta = 0, off_states = 0, off_gstates = 0, off_partials = 0, total = 0;
+};
+
+// Workspace of the gradient path: the metadata blocks of chunk_prep_kernel,
+// the fp32 state before and the gradient after every chunk, per-chunk sums.
+BwdPlan make_bwd_plan(const ssd_dims& d) {
+    BwdPlan p;
+    if (d.seqlen <= 0 || d.batch <= 0) return p;
+    p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
+    const size_t bhc = static_cast<size_t>(d.batch * d.nheads * p.nc);
+    size_t off = 0;
+    p.off_meta = off;
+    off = align_up(off + bhc * static_cast<size_t>(d.chunk_size) * 3 * sizeof(float));
+    p.off_states = off;
+    off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(float));
+    p.off_gstates = off;
+    off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(float));
+    p.off_partials = off;
+    off = align_up(off + bhc * 3 * sizeof(float));
+    p.total = off;
+    return p;
+}
+
 }  // namespace
 
 ssd::DispatchEvents& ssd::dispatch_events() { return g_dispatch_events; }
@@ -281,6 +325,136 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     }
     if (timed_launch(k, hs, [&] { return var->chunk_output(sa, b * plan.nseg * H, hs); }) !=
         hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
+    if (check_bwd_dims(d, io) != SSD_OK) return 0;
+    return make_bwd_plan(*d).total;
+}
+
+ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                              const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                              const float* A, const void* B, const void* C, const float* D,
+                              const float* initial_states, const int32_t* seq_idx, const void* dy,
+                              const float* d_final_states, void* dx, float* ddt, float* dA,
+                              void* dB, void* dC, float* dD, float* ddt_bias,
+                              float* d_initial_states, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    ssd_status st = check_bwd_dims(d, io);
+    if (st != SSD_OK) return st;
+    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim,
+                  N = d->dstate, G = d->ngroups;
+    const bool work = b > 0 && L > 0;
+    if (!A || !dA) return SSD_ERR_NULL_ARG;
+    if (work && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_NULL_ARG;
+    const BwdPlan plan = make_bwd_plan(*d);
+    if (plan.total > 0 &&
+        (!workspace || workspace_bytes < plan.total ||
+         (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+        return SSD_ERR_WORKSPACE;
+    const void* vec_bufs[] = {x, B, C, dy, dx, dB, dC, initial_states, d_final_states,
+                              d_initial_states};
+    for (const void* p : vec_bufs)
+        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    const size_t es = io_size(io);
+    const int64_t sbytes = b * H * P * N * 4;
+    const Span ins[] = {
+        span(x, b * L * H * P * es), span(dt, b * L * H * 4), span(B, b * L * G * N * es),
+        span(C, b * L * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+        span(D, D ? H * 4 : 0), span(seq_idx, seq_idx ? b * L * 4 : 0),
+        span(initial_states, initial_states ? sbytes : 0), span(dy, b * L * H * P * es),
+        span(d_final_states, d_final_states ? sbytes : 0),
+    };
+    const Span outs[] = {
+        span(dx, b * L * H * P * es), span(ddt, b * L * H * 4), span(dA, H * 4),
+        span(dB, b * L * G * N * es), span(dC, b * L * G * N * es), span(dD, dD ? H * 4 : 0),
+        span(ddt_bias, ddt_bias ? H * 4 : 0), span(d_initial_states, d_initial_states ? sbytes : 0),
+        span(workspace, plan.total),
+    };
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span& s : ins)
+            if (overlap(outs[i], s)) return SSD_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
+    }
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    ssd::BwdArgs ba{};
+    ba.x = x;
+    ba.B = B;
+    ba.C = C;
+    ba.dy = dy;
+    ba.dt_raw = dt;
+    ba.dt_bias = dt_bias;
+    ba.A = A;
+    ba.D = D;
+    ba.softplus = dt_softplus ? 1 : 0;
+    ba.dt_min = dt_min;
+    ba.dt_max = dt_max;
+    ba.seq_idx = seq_idx;
+    ba.h_init = initial_states;
+    ba.dh_final = d_final_states;
+    ba.dx = dx;
+    ba.ddt = ddt;
+    ba.dA = dA;
+    ba.dB = dB;
+    ba.dC = dC;
+    ba.dD = dD;
+    ba.ddt_bias = ddt_bias;
+    ba.dh_init = d_initial_states;
+    ba.L = L;
+    ba.batch = static_cast<int>(b);
+    ba.H = static_cast<int>(H);
+    ba.G = static_cast<int>(G);
+    ba.nc = static_cast<int>(plan.nc);
+    if (!work) {
+        if (timed_launch(k, hs, [&] { return ssd::launch_bwd_empty(ba, b * H * P * N, hs); }) !=
+            hipSuccess)
+            return SSD_ERR_HIP;
+        return SSD_OK;
+    }
+    char* wsb = static_cast<char*>(workspace);
+    float* meta = reinterpret_cast<float*>(wsb + plan.off_meta);
+    ba.cs = meta;
+    ba.states = reinterpret_cast<float*>(wsb + plan.off_states);
+    ba.gstates = reinterpret_cast<float*>(wsb + plan.off_gstates);
+    ba.partials = reinterpret_cast<float*>(wsb + plan.off_partials);
+
+    // the per-token metadata of the forward pass (chunk_prep_kernel, no tiles)
+    ssd::ScanArgs sa{};
+    sa.B = B;
+    sa.C = C;
+    sa.dt_raw = dt;
+    sa.dt_bias = dt_bias;
+    sa.A = A;
+    sa.softplus = ba.softplus;
+    sa.dt_min = dt_min;
+    sa.dt_max = dt_max;
+    sa.seq_idx = seq_idx;
+    sa.cs = meta;
+    sa.dtv = meta + d->chunk_size;
+    sa.wgt = meta + 2 * d->chunk_size;
+    sa.L = L;
+    sa.H = ba.H;
+    sa.G = ba.G;
+    sa.nc = ba.nc;
+    sa.nseg = 1;
+    sa.cps = ba.nc;
+    if (timed_launch(k, hs, [&] { return ssd::launch_chunk_meta_bf16_64_128_128(sa, b * plan.nc * G, hs); }) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
+    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_states(ba, false, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_states(ba, true, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_chunk(ba, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_reduce(ba, hs); }) != hipSuccess)
         return SSD_ERR_HIP;
     return SSD_OK;
 }

@@ -1,0 +1,679 @@
+// ssd_bwd.hip -- gradients of the chunked SSD scan on gfx950 (bf16 x, B, C and
+// dy; fp32 dt, A, D and states; P = 64, N = 128, chunk Q = 128).
+//
+// Operation: the scan of ssd_kernels.hip (RL-Kernel RFC "Nemotron-3-Nano-30B-A3B",
+// section 1 operator families 1-2 and section 3 Figure 2 box [F2]: the chunked
+// scan serves training, which needs its backward pass).  For chunk c of one
+// (row, head), with cs the segmented chunk cumsum of a = dt*A, V the tokens of
+// the chunk inside the sequence, seq_prev the sequence id of the token before
+// the chunk and seq_last that of its last token:
+//   kappa_i = [seq_i = seq_prev] exp(cs_i)             decay carried into token i
+//   omega_j = [seq_j = seq_last] exp(cs_last - cs_j)   decay from token j to the end
+//   e_c     = [seq_last = seq_prev] exp(cs_last)
+//   L_ij    = [j <= i][seq_i = seq_j] exp(cs_i - cs_j)
+// the forward pass is
+//   y_i   = sum_j (C_i.B_j) L_ij dt_j x_j + kappa_i h_in C_i + D x_i
+//   h_out = e_c h_in + sum_j omega_j dt_j x_j (outer) B_j.
+// With g_out the gradient of the loss with respect to h_out (from later chunks,
+// or the final-state gradient) and dy the gradient with respect to y:
+//   g_in    = e_c g_out + sum_i kappa_i dy_i (outer) C_i            (into h_in)
+//   u_j     = sum_i (C_i.B_j) L_ij dy_i + omega_j g_out B_j          (= g_j B_j)
+//   dx_j    = dt_j u_j + D dy_j
+//   dB_j    = sum over the group's heads of dt_j [sum_i L_ij (dy_i.x_j) C_i + omega_j g_out^T x_j]
+//   dC_i    = sum over the group's heads of sum_j L_ij dt_j (dy_i.x_j) B_j + kappa_i h_in^T dy_i
+//   d(dt_j) = x_j.u_j + A d(a_j),  d(a_k) = sum of dcs_i over i >= k in k's sequence run
+//   dcs_i   = sum_j M_ij - sum_j M_ji + kappa_i dy_i.(h_in C_i) - T_i
+//             (+ sum_j T_j + e_c <g_out, h_in> at the last token of the chunk)
+//   with M_ij = (C_i.B_j) L_ij dt_j (dy_i.x_j) and T_j = omega_j dt_j x_j.(g_out B_j);
+//   dA = sum dt_k d(a_k), dD = sum dy.x, d(h_init) = g_in of chunk 0, and
+//   d(dt_raw) = d(dt) [not clamped] (sigmoid(dt_raw + dt_bias) with softplus).
+// Every term is local to its chunk once h_in and g_out are known.
+//
+// Kernels (one backward call):
+//   bwd_states_kernel<false>  one workgroup per (row, head): the states h_in of
+//        every chunk, in chunk order (h <- e_c h + sum_j omega_j dt_j x_j B_j^T);
+//   bwd_states_kernel<true>   the same walk backwards for g_out of every chunk
+//        (g <- e_c g + sum_i kappa_i dy_i C_i^T); its last state is d(h_init);
+//   bwd_chunk_kernel          one workgroup per (row, chunk, group), the group's
+//        heads in turn: every gradient above on bf16 MFMA, dB and dC summed over
+//        the heads in registers (no atomics: deterministic);
+//   bwd_reduce_kernel         dA, dD, d(dt_bias) from per-chunk partial sums in a
+//        fixed order.
+// The per-token metadata (cs, dt, weights) comes from chunk_prep_kernel.
+//
+// Operand conventions are those of ssd_scan_tr.hip: MFMA 16x16x32 bf16, lane
+// (r16, g = lane / 16); k over tokens (transposing reads) in the order element
+// e < 4: token 32s + 4g + e, e >= 4: token 32s + 16 + 4g + (e - 4); k over a
+// contiguous dimension read plainly: element e is 32s + 8g + e.  Products whose
+// operands are both read with k over tokens use the token order on both sides.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+#include "ssd_lds.h"
+#include "ssd_work.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kBP = 64, kBN = 128, kBQ = 128;  // compiled shape
+constexpr int kBWaves = 8;
+constexpr int kBThreads = kBWaves * kWave;
+constexpr int kRowX = 2 * kBP;   // bytes of a token row of an x / dy tile
+constexpr int kRowB = 2 * kBN;   // bytes of a token row of a B / C tile, of a state row
+constexpr int kRowT = 2 * kBQ;   // bytes of a row of a Q x Q matrix
+
+// ------------------------------------------------------------------ helpers
+
+// 16-byte pieces of a [rows][ROW bytes] bf16 tile from global rows (stride
+// gstride bytes, `valid` rows inside the sequence, the rest zero) into LDS in
+// the swizzled layout of tr_off; all threads of the workgroup take part.
+template <int ROW, int ROWS>
+__device__ __forceinline__ void stage_rows(char* lds, const char* src, int64_t gstride, int valid) {
+    constexpr int SPR = ROW / 16;
+    constexpr int PIECES = ROWS * SPR;
+#pragma unroll
+    for (int k = 0; k < (PIECES + kBThreads - 1) / kBThreads; ++k) {
+        const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+        if (q < PIECES) {
+            const int r = q / SPR, slot = q % SPR;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (r < valid) v = *reinterpret_cast<const uint4*>(src + r * gstride + slot * 16);
+            lds_st<uint4>(lds, lds_addr(lds) + tr_off<ROW>(r, slot * 16), v);
+        }
+    }
+}
+
+// Plain fragment: row R of a tile, k = 32s + 8g + e (16 contiguous bytes).
+// `base` is the tile's LDS address; the chunk kernel passes it opaque (formed
+// again for every head), so that no lane address is hoisted out of its loop.
+template <int ROW>
+__device__ __forceinline__ Frag<uint16_t> row_frag(const char* tile, uint32_t base, int R, int s, int g) {
+    return frag_of(lds_ld<uint4>(tile, base + tr_off<ROW>(R, 64 * s + 16 * g)));
+}
+// Row R of a tile with k over its columns in the token order (two 8-byte reads).
+template <int ROW>
+__device__ __forceinline__ Frag<uint16_t> row_frag_tk(const char* tile, uint32_t base, int R, int s, int g) {
+    const uint2 lo = lds_ld<uint2>(tile, base + tr_off<ROW>(R, 64 * s + 8 * g));
+    const uint2 hi = lds_ld<uint2>(tile, base + tr_off<ROW>(R, 64 * s + 32 + 8 * g));
+    return frag_of(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// Column block mb of a tile whose rows are the k index (token order).
+template <int ROW>
+__device__ __forceinline__ Frag<uint16_t> col_frag(const char* tile, uint32_t base, int mb, int s, int lane) {
+    return tr_frag<ROW>(tile, base + tr_lane_off<ROW>(mb, lane), s);
+}
+// Token-order fragment elements scaled by per-token factors f[32s + ...].
+__device__ __forceinline__ Frag<uint16_t> scale_tk(const Frag<uint16_t>& f, const float* fv, int s, int g) {
+    const float4 w0 = *reinterpret_cast<const float4*>(fv + 32 * s + 4 * g);
+    const float4 w1 = *reinterpret_cast<const float4*>(fv + 32 * s + 16 + 4 * g);
+    return scale_frag(f, w0, w1);
+}
+
+// Four bf16 values (one accumulator) as 8 bytes.
+__device__ __forceinline__ uint2 pack4(const f32x4_t& v) {
+    return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
+// Metadata block [cs Q | dt Q | w Q] of (row b, head h, chunk c) from a.cs.
+__device__ __forceinline__ int64_t meta_offset_bwd(const BwdArgs& a, int64_t b, int h, int c) {
+    return ((b * a.H + h) * a.nc + c) * static_cast<int64_t>(3 * kBQ);
+}
+
+__device__ __forceinline__ int seq_at(const int32_t* seq, int64_t row_base, int64_t t, int64_t L) {
+    return seq ? seq[row_base + (t < L ? t : L - 1)] : 0;
+}
+
+// ------------------------------------------------------------ chain of states
+
+// The state before every chunk (forward: h_in, chunk order) or the gradient
+// after every chunk (backward: g_out, reverse chunk order), fp32 [p][n] in
+// `states` at (row, head, chunk).  Wave w owns state rows n = 16w + 4g + r,
+// column p = 16pb + r16 (the MFMA accumulator layout).
+template <bool kRev>
+__global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];   // x or dy rows
+    __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];   // B or C rows
+    __shared__ __attribute__((aligned(16))) float sW[kBQ];            // per-token weights
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / a.H;
+    const int h = static_cast<int>(bh % a.H);
+    const int grp = h / (a.H / a.G);
+    const int64_t L = a.L;
+    const int64_t srow = b * L;
+
+    f32x4_t st[kBP / 16];
+    const float* init = kRev ? a.dh_final : a.h_init;
+#pragma unroll
+    for (int pb = 0; pb < kBP / 16; ++pb) {
+        st[pb] = acc_zero();
+        if (init) {
+            const float4 v = *reinterpret_cast<const float4*>(init + bh * kBP * kBN + (16 * pb + r16) * kBN +
+                                                              16 * wave + 4 * g);
+            st[pb] = f32x4_t{v.x, v.y, v.z, v.w};
+        }
+    }
+    const char* vsrc = static_cast<const char*>(kRev ? a.dy : a.x);
+    const char* ksrc = static_cast<const char*>(kRev ? a.C : a.B);
+    const int64_t vstride = static_cast<int64_t>(a.H) * kRowX;
+    const int64_t kstride = static_cast<int64_t>(a.G) * kRowB;
+    for (int k = 0; k < a.nc; ++k) {
+        const int c = kRev ? a.nc - 1 - k : k;
+        const int64_t t0 = static_cast<int64_t>(c) * kBQ;
+        const int valid = static_cast<int>(L - t0 < kBQ ? L - t0 : kBQ);
+        // the state before this chunk's update
+        float* dst = (kRev ? a.gstates : a.states) + (bh * a.nc + c) * kBP * kBN;
+#pragma unroll
+        for (int pb = 0; pb < kBP / 16; ++pb)
+            *reinterpret_cast<float4*>(dst + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
+                make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
+        const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
+        const int seq_prev = seq_at(a.seq_idx, srow, t0 == 0 ? 0 : t0 - 1, L);
+        const int seq_last = seq_at(a.seq_idx, srow, t0 + valid - 1, L);
+        const float cs_last = meta[valid - 1];
+        const float e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
+        stage_rows<kRowX, kBQ>(sV, vsrc + ((srow + t0) * a.H + h) * kRowX, vstride, valid);
+        stage_rows<kRowB, kBQ>(sK, ksrc + ((srow + t0) * a.G + grp) * kRowB, kstride, valid);
+        for (int t = static_cast<int>(threadIdx.x); t < kBQ; t += kBThreads) {
+            float w = 0.0f;
+            if (t < valid) {
+                if (kRev) {
+                    w = seq_at(a.seq_idx, srow, t0 + t, L) == seq_prev ? decay_exp(meta[t]) : 0.0f;
+                } else {
+                    w = meta[2 * kBQ + t];  // omega_t dt_t from chunk_prep_kernel
+                }
+            }
+            sW[t] = w;
+        }
+        __syncthreads();
+        const uint32_t bsK = lds_keep(lds_addr(sK)), bsV = lds_keep(lds_addr(sV));
+#pragma unroll
+        for (int pb = 0; pb < kBP / 16; ++pb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[pb][r] *= e;
+#pragma unroll
+        for (int s = 0; s < kBQ / 32; ++s) {
+            const Frag<uint16_t> kf = scale_tk(col_frag<kRowB>(sK, bsK, wave, s, lane), sW, s, g);
+#pragma unroll
+            for (int pb = 0; pb < kBP / 16; ++pb) mma(st[pb], kf, col_frag<kRowX>(sV, bsV, pb, s, lane));
+        }
+        __syncthreads();
+    }
+    if (kRev && a.dh_init) {
+#pragma unroll
+        for (int pb = 0; pb < kBP / 16; ++pb)
+            *reinterpret_cast<float4*>(a.dh_init + bh * kBP * kBN + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
+                make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
+    }
+}
+
+// --------------------------------------------------------- per-chunk gradients
+
+// Sum over the 16 lanes of a 16-lane row (same g).
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+// Sum over the 4 lane groups g with the same r16.
+__device__ __forceinline__ float sum_g(float v) {
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+__device__ __forceinline__ float sum64(float v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+// Workgroup sum (fixed order); every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = sum64(v);
+    const int wave = static_cast<int>(threadIdx.x) / kWave;
+    if ((threadIdx.x % kWave) == 0) red[wave] = v;
+    __syncthreads();
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kBWaves; ++w) t += red[w];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char sB[kBQ * kRowB];
+    __shared__ __attribute__((aligned(1024))) char sC[kBQ * kRowB];
+    __shared__ __attribute__((aligned(1024))) char sX[kBQ * kRowX];
+    __shared__ __attribute__((aligned(1024))) char sDY[kBQ * kRowX];
+    __shared__ __attribute__((aligned(1024))) char sT[kBQ * kRowT];
+    __shared__ __attribute__((aligned(1024))) char sH[kBP * kRowB];
+    // per-token values of the current head: chunk cumsum, dt, omega, kappa,
+    // row sums of M (then dcs), per-row-block column sums of M, x.u, T_j,
+    // kappa_i dy_i.(h_in C_i); sequence ids; block reductions
+    __shared__ __attribute__((aligned(16))) float sCs[kBQ];
+    __shared__ __attribute__((aligned(16))) float sDt[kBQ];
+    __shared__ __attribute__((aligned(16))) float sOm[kBQ];
+    __shared__ __attribute__((aligned(16))) float sKa[kBQ];
+    __shared__ __attribute__((aligned(16))) float sRows[kBQ];
+    __shared__ __attribute__((aligned(16))) float sCols[kBWaves * kBQ];
+    __shared__ __attribute__((aligned(16))) float sDin[kBQ];
+    __shared__ __attribute__((aligned(16))) float sTj[kBQ];
+    __shared__ __attribute__((aligned(16))) float sCar[kBQ];
+    __shared__ __attribute__((aligned(16))) int sSeq[kBQ];
+    __shared__ float sRed[kBWaves];
+
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const int r16 = lane & 15, g = lane >> 4;
+    // work item: group fastest, then chunk, then row
+    int64_t w = blockIdx.x;
+    const int grp = static_cast<int>(w % a.G);
+    w /= a.G;
+    const int c = static_cast<int>(w % a.nc);
+    const int64_t b = w / a.nc;
+    const int hpg = a.H / a.G;
+    const int64_t L = a.L;
+    const int64_t srow = b * L;
+    const int64_t t0 = static_cast<int64_t>(c) * kBQ;
+    const int valid = static_cast<int>(L - t0 < kBQ ? L - t0 : kBQ);
+    const int seq_prev = seq_at(a.seq_idx, srow, t0 == 0 ? 0 : t0 - 1, L);
+    const int seq_last = seq_at(a.seq_idx, srow, t0 + valid - 1, L);
+    const int I = wave;  // row block (P1, P4) / column block (P2, P3) of this wave
+
+    // ---- the group's B and C rows, and C.B^T (tiles (I, J <= I) of this wave)
+    const int64_t bcstride = static_cast<int64_t>(a.G) * kRowB;
+    stage_rows<kRowB, kBQ>(sB, static_cast<const char*>(a.B) + ((srow + t0) * a.G + grp) * kRowB, bcstride, valid);
+    stage_rows<kRowB, kBQ>(sC, static_cast<const char*>(a.C) + ((srow + t0) * a.G + grp) * kRowB, bcstride, valid);
+    for (int t = static_cast<int>(threadIdx.x); t < kBQ; t += kBThreads)
+        sSeq[t] = seq_at(a.seq_idx, srow, t0 + t, L);
+    __syncthreads();
+    f32x4_t dBacc[8], dCacc[8];  // dB^T tiles (nb, J = wave), dC^T tiles (nb, I = wave)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+        dBacc[nb] = acc_zero();
+        dCacc[nb] = acc_zero();
+    }
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const uint32_t bsB = lds_keep(lds_addr(sB)), bsC = lds_keep(lds_addr(sC));
+        const uint32_t bsX = lds_keep(lds_addr(sX)), bsDY = lds_keep(lds_addr(sDY));
+        const uint32_t bsT = lds_keep(lds_addr(sT)), bsH = lds_keep(lds_addr(sH));
+        const int h = grp * hpg + hh;
+        const int64_t bh = b * a.H + h;
+        const float Ah = a.A[h];
+        const float Dh = a.D ? a.D[h] : 0.0f;
+        const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
+        const float cs_last = meta[valid - 1];
+        const float e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
+        // ---- head inputs
+        const int64_t xstride = static_cast<int64_t>(a.H) * kRowX;
+        stage_rows<kRowX, kBQ>(sX, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
+        stage_rows<kRowX, kBQ>(sDY, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
+        for (int t = static_cast<int>(threadIdx.x); t < kBQ; t += kBThreads) {
+            const float cst = meta[t];
+            sCs[t] = cst;
+            sDt[t] = meta[kBQ + t];
+            const bool in = t < valid;
+            sOm[t] = in && sSeq[t] == seq_last ? decay_exp(cs_last - cst) : 0.0f;
+            sKa[t] = in && sSeq[t] == seq_prev ? decay_exp(cst) : 0.0f;
+        }
+        // g_out as the bf16 operand copy; its fp32 values stay for <g_out, h_in>
+        const float* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
+        const float* hsrc = a.states + (bh * a.nc + c) * kBP * kBN;
+        float gv[16];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;  // 16-byte bf16 piece
+            const int p = q / 16, slot = q % 16;
+            const float4 v0 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot);
+            const float4 v1 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot + 4);
+            gv[8 * k + 0] = v0.x; gv[8 * k + 1] = v0.y; gv[8 * k + 2] = v0.z; gv[8 * k + 3] = v0.w;
+            gv[8 * k + 4] = v1.x; gv[8 * k + 5] = v1.y; gv[8 * k + 6] = v1.z; gv[8 * k + 7] = v1.w;
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot),
+                          make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
+                                     pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)));
+        }
+        __syncthreads();
+
+        // ---- P1: tiles (I, J <= I) of M1 = dY X^T and C.B^T (rows i of block I);
+        // S = CB L, M = S dt_j M1; row sums of M, column-sum partials, S^T to LDS
+        float rsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float cs_i[4];
+        int sq_i[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            cs_i[r] = sCs[16 * I + 4 * g + r];
+            sq_i[r] = sSeq[16 * I + 4 * g + r];
+        }
+        // L_ij of this lane's rows and column j
+        auto decay_l = [&](int J, int r) {
+            const int i = 16 * I + 4 * g + r, j = 16 * J + r16;
+            return (j <= i && sq_i[r] == sSeq[j]) ? decay_exp(cs_i[r] - sCs[j]) : 0.0f;
+        };
+        auto m1_tile = [&](int J) {
+            f32x4_t m1 = acc_zero();
+#pragma unroll
+            for (int ks = 0; ks < kBP / 32; ++ks)
+                mma(m1, row_frag<kRowX>(sDY, bsDY, 16 * I + r16, ks, g), row_frag<kRowX>(sX, bsX, 16 * J + r16, ks, g));
+            return m1;
+        };
+        for (int J = 0; J < 8; ++J) {
+            f32x4_t sv = acc_zero();
+            float csum = 0.0f;
+            if (J <= I) {
+                const f32x4_t m1 = m1_tile(J);
+                f32x4_t cbt = acc_zero();
+#pragma unroll
+                for (int ks = 0; ks < kBN / 32; ++ks)
+                    mma(cbt, row_frag<kRowB>(sC, bsC, 16 * I + r16, ks, g), row_frag<kRowB>(sB, bsB, 16 * J + r16, ks, g));
+                const float dt_j = sDt[16 * J + r16];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sv[r] = cbt[r] * decay_l(J, r);
+                    const float mv = sv[r] * dt_j * m1[r];
+                    rsum[r] += mv;
+                    csum += mv;
+                }
+            }
+            // S^T row j, columns i = 16I + 4g .. +3 (zeros right of the diagonal block)
+            lds_st<uint2>(sT, bsT + tr_off<kRowT>(16 * J + r16, 32 * I + 8 * g), pack4(sv));
+            csum = sum_g(csum);
+            if (g == 0) sCols[I * kBQ + 16 * J + r16] = csum;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = sum16(rsum[r]);
+            if (r16 == 0) sRows[16 * I + 4 * g + r] = v;
+        }
+        __syncthreads();
+
+        // ---- P2: u^T = (S^T dY)^T + omega (g_out B^T), columns j of block J = wave
+        {
+            const int J = wave;
+            const int j = 16 * J + r16;
+            f32x4_t ut[4], vt[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                ut[pb] = acc_zero();
+                vt[pb] = acc_zero();
+            }
+#pragma unroll
+            for (int ks = 0; ks < kBQ / 32; ++ks) {
+                if (2 * ks + 1 >= J) {
+                    const Frag<uint16_t> sf = row_frag_tk<kRowT>(sT, bsT, j, ks, g);
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) mma(ut[pb], col_frag<kRowX>(sDY, bsDY, pb, ks, lane), sf);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < kBN / 32; ++ks) {
+                const Frag<uint16_t> bf = row_frag<kRowB>(sB, bsB, j, ks, g);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) mma(vt[pb], row_frag<kRowB>(sH, bsH, 16 * pb + r16, ks, g), bf);
+            }
+            const float om_j = sOm[j], dt_j = sDt[j];
+            float din = 0.0f, tsum = 0.0f, dd = 0.0f;
+            uint2 dxw[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                // row j, p = 16pb + 4g .. +3
+                const uint2 xr = lds_ld<uint2>(sX, bsX + tr_off<kRowX>(j, 32 * pb + 8 * g));
+                const uint2 yr = lds_ld<uint2>(sDY, bsDY + tr_off<kRowX>(j, 32 * pb + 8 * g));
+                const float xv[4] = {bf_lo(xr.x), bf_hi(xr.x), bf_lo(xr.y), bf_hi(xr.y)};
+                const float yv[4] = {bf_lo(yr.x), bf_hi(yr.x), bf_lo(yr.y), bf_hi(yr.y)};
+                float dxv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float u = ut[pb][r] + om_j * vt[pb][r];
+                    dxv[r] = dt_j * u + Dh * yv[r];
+                    din += xv[r] * u;
+                    tsum += xv[r] * vt[pb][r];
+                    dd += xv[r] * yv[r];
+                }
+                dxw[pb] = make_uint2(pack_bf16x2(dxv[0], dxv[1]), pack_bf16x2(dxv[2], dxv[3]));
+            }
+            if (j < valid) {
+                uint16_t* dxp = static_cast<uint16_t*>(a.dx) + ((srow + t0 + j) * a.H + h) * kBP + 4 * g;
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) *reinterpret_cast<uint2*>(dxp + 16 * pb) = dxw[pb];
+            }
+            din = sum_g(din);
+            tsum = sum_g(tsum);
+            if (g == 0) {
+                sDin[j] = din;
+                sTj[j] = om_j * dt_j * tsum;
+            }
+            dd = sum64(dd);
+            if (lane == 0) sRed[wave] = dd;
+        }
+        __syncthreads();
+        float dD_part = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kBWaves; ++q) dD_part += sRed[q];
+
+        // ---- W^T over S^T (W = M1 L, M1 formed again)
+        for (int J = 0; J < 8; ++J) {
+            f32x4_t wv = acc_zero();
+            if (J <= I) {
+                const f32x4_t m1 = m1_tile(J);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wv[r] = m1[r] * decay_l(J, r);
+            }
+            lds_st<uint2>(sT, bsT + tr_off<kRowT>(16 * J + r16, 32 * I + 8 * g), pack4(wv));
+        }
+        __syncthreads();
+
+        // ---- P3: dB^T += dt_j [(C^T W) + omega_j g_out^T X^T], columns j of block J = wave
+        {
+            const int J = wave;
+            const int j = 16 * J + r16;
+            const float dt_j = sDt[j], om_j = sOm[j];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                f32x4_t a1 = acc_zero(), a2 = acc_zero();
+#pragma unroll
+                for (int ks = 0; ks < kBQ / 32; ++ks)
+                    if (2 * ks + 1 >= J) mma(a1, col_frag<kRowB>(sC, bsC, nb, ks, lane), row_frag_tk<kRowT>(sT, bsT, j, ks, g));
+#pragma unroll
+                for (int ks = 0; ks < kBP / 32; ++ks)
+                    mma(a2, col_frag<kRowB>(sH, bsH, nb, ks, lane), row_frag_tk<kRowX>(sX, bsX, j, ks, g));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dBacc[nb][r] += dt_j * (a1[r] + om_j * a2[r]);
+                __builtin_amdgcn_sched_barrier(0);  // one n block's operands live at a time
+            }
+        }
+        // <g_out, h_in> (fp32); then h_in replaces g_out as the bf16 operand
+        float ghp = 0.0f;
+        float hv[16];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+            const int p = q / 16, slot = q % 16;
+            const float4 v0 = *reinterpret_cast<const float4*>(hsrc + p * kBN + 8 * slot);
+            const float4 v1 = *reinterpret_cast<const float4*>(hsrc + p * kBN + 8 * slot + 4);
+            hv[8 * k + 0] = v0.x; hv[8 * k + 1] = v0.y; hv[8 * k + 2] = v0.z; hv[8 * k + 3] = v0.w;
+            hv[8 * k + 4] = v1.x; hv[8 * k + 5] = v1.y; hv[8 * k + 6] = v1.z; hv[8 * k + 7] = v1.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) ghp += gv[q] * hv[q];
+        const float gh = block_sum(ghp, sRed);  // its barriers also end P3's reads of g_out
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+            const int p = q / 16, slot = q % 16;
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot),
+                          make_uint4(pack_bf16x2(hv[8 * k], hv[8 * k + 1]), pack_bf16x2(hv[8 * k + 2], hv[8 * k + 3]),
+                                     pack_bf16x2(hv[8 * k + 4], hv[8 * k + 5]), pack_bf16x2(hv[8 * k + 6], hv[8 * k + 7])));
+        }
+        __syncthreads();
+
+        // ---- P4: dC^T += (B^T dt) W^T + kappa_i h_in^T dY^T, columns i of block I = wave
+        {
+            const int i = 16 * I + r16;
+            const float ka_i = sKa[i];
+            float car = 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                f32x4_t cw = acc_zero(), cc = acc_zero();
+#pragma unroll
+                for (int ks = 0; ks < kBQ / 32; ++ks)
+                    if (2 * ks <= I)
+                        mma(cw, scale_tk(col_frag<kRowB>(sB, bsB, nb, ks, lane), sDt, ks, g),
+                            col_frag<kRowT>(sT, bsT, I, ks, lane));
+#pragma unroll
+                for (int ks = 0; ks < kBP / 32; ++ks)
+                    mma(cc, col_frag<kRowB>(sH, bsH, nb, ks, lane), row_frag_tk<kRowX>(sDY, bsDY, i, ks, g));
+                const uint2 cr = lds_ld<uint2>(sC, bsC + tr_off<kRowB>(i, 32 * nb + 8 * g));
+                const float cv[4] = {bf_lo(cr.x), bf_hi(cr.x), bf_lo(cr.y), bf_hi(cr.y)};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    dCacc[nb][r] += cw[r] + ka_i * cc[r];
+                    car += cv[r] * cc[r];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            car = sum_g(car);
+            if (g == 0) sCar[i] = ka_i * car;
+        }
+        __syncthreads();
+
+        // ---- dcs, d(a) by a reverse segmented sum over each sequence run, d(dt)
+        if (wave == 0) {
+            // column sums of M over the row blocks
+            float tsum = 0.0f;
+            for (int t = lane; t < kBQ; t += kWave) tsum += sTj[t];
+            tsum = sum64(tsum);
+            // lane q holds tokens t1 = 2(63 - q) + 1 then t0 = 2(63 - q) (reverse order)
+            const int tA = 2 * (kWave - 1 - lane) + 1, tB = tA - 1;
+            auto dcs_of = [&](int t) {
+                if (t >= valid) return 0.0f;
+                float cols = 0.0f;
+#pragma unroll
+                for (int q = 0; q < kBWaves; ++q) cols += (t < 16 * q + 16) ? sCols[q * kBQ + t] : 0.0f;
+                float v = sRows[t] - cols + sCar[t] - sTj[t];
+                if (t == valid - 1) v += tsum + e * gh;
+                return v;
+            };
+            // a token ends its run (starts a segment in reverse order) at the
+            // last real token or before a sequence change
+            auto run_end = [&](int t) {
+                return t >= valid - 1 || sSeq[t + 1] != sSeq[t];
+            };
+            const float dA0 = dcs_of(tA), dB0 = dcs_of(tB);
+            const bool hA = run_end(tA), hB = run_end(tB);
+            const float agg = hB ? dB0 : dA0 + dB0;
+            const float incl = wave_segmented_scan(agg, (hA || hB) ? 1 : 0);
+            float carry = __shfl_up(incl, 1, kWave);
+            if (lane == 0) carry = 0.0f;
+            const float rA = hA ? dA0 : carry + dA0;
+            const float rB = hB ? dB0 : rA + dB0;
+            // d(dt), d(dt_raw), the per-chunk sums
+            float dA_part = 0.0f, dbias_part = 0.0f;
+            const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = u == 0 ? tA : tB;
+                const float da = u == 0 ? rA : rB;
+                if (t < valid) {
+                    const float dtv = sDt[t];
+                    dA_part += dtv * da;
+                    const float ddt = sDin[t] + Ah * da;
+                    const int64_t ti = (srow + t0 + t) * a.H + h;
+                    const float v = a.dt_raw[ti] + bias;
+                    const float sp = a.softplus ? softplus_f32(v) : v;
+                    float draw = 0.0f;
+                    if (sp >= a.dt_min && sp <= a.dt_max) draw = a.softplus ? ddt / (1.0f + __expf(-v)) : ddt;
+                    a.ddt[ti] = draw;
+                    dbias_part += draw;
+                }
+            }
+            dA_part = sum64(dA_part);
+            dbias_part = sum64(dbias_part);
+            if (lane == 0) {
+                float* part = a.partials + ((b * a.nc + c) * a.H + h) * 3;
+                part[0] = dA_part;
+                part[1] = dD_part;
+                part[2] = dbias_part;
+            }
+        }
+        __syncthreads();  // LDS is reused by the next head
+    }
+
+    // ---- dB, dC of the group: lane holds n = 16nb + 4g .. +3 of row 16 * wave + r16
+    const int jr = 16 * wave + r16;
+    if (jr < valid) {
+        uint16_t* dbp = static_cast<uint16_t*>(a.dB) + ((srow + t0 + jr) * a.G + grp) * kBN + 4 * g;
+        uint16_t* dcp = static_cast<uint16_t*>(a.dC) + ((srow + t0 + jr) * a.G + grp) * kBN + 4 * g;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            *reinterpret_cast<uint2*>(dbp + 16 * nb) = pack4(dBacc[nb]);
+            *reinterpret_cast<uint2*>(dcp + 16 * nb) = pack4(dCacc[nb]);
+        }
+    }
+}
+
+// dA, dD, d(dt_bias) of head blockIdx.x: sums of the per-(row, chunk) partials
+// in a fixed order.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int64_t rows_chunks) {
+    __shared__ float red[3][256];
+    const int h = blockIdx.x;
+    float acc[3] = {0.0f, 0.0f, 0.0f};
+    for (int64_t k = threadIdx.x; k < rows_chunks; k += 256) {
+        const float* part = a.partials + (k * a.H + h) * 3;
+        acc[0] += part[0];
+        acc[1] += part[1];
+        acc[2] += part[2];
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) red[q][threadIdx.x] = acc[q];
+    __syncthreads();
+    for (int d = 128; d > 0; d >>= 1) {
+        if (static_cast<int>(threadIdx.x) < d)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + d];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        a.dA[h] = red[0][0];
+        if (a.dD) a.dD[h] = red[1][0];
+        if (a.ddt_bias) a.ddt_bias[h] = red[2][0];
+    }
+}
+
+// Gradients when there are no tokens: d(h_init) = dh_final (or zero) and
+// zero dA, dD, d(dt_bias).
+__global__ __launch_bounds__(256) void bwd_empty_kernel(BwdArgs a, int64_t nstate) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (a.dh_init && i < nstate) a.dh_init[i] = a.dh_final ? a.dh_final[i] : 0.0f;
+    if (i < a.H) {
+        a.dA[i] = 0.0f;
+        if (a.dD) a.dD[i] = 0.0f;
+        if (a.ddt_bias) a.ddt_bias[i] = 0.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st) {
+    const int64_t n = nstate > a.H ? nstate : a.H;
+    return dispatch(bwd_empty_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), st, a,
+                    nstate);
+}
+
+hipError_t launch_bwd_states(const BwdArgs& a, bool reverse, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.H));
+    if (reverse) return dispatch(bwd_states_kernel<true>, grid, dim3(kBThreads), st, a);
+    return dispatch(bwd_states_kernel<false>, grid, dim3(kBThreads), st, a);
+}
+
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.nc * a.G));
+    return dispatch(bwd_chunk_kernel, grid, dim3(kBThreads), st, a);
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st) {
+    return dispatch(bwd_reduce_kernel, dim3(static_cast<unsigned>(a.H)), dim3(256), st, a,
+                    static_cast<int64_t>(a.batch) * a.nc);
+}
+
+}  // namespace ssd

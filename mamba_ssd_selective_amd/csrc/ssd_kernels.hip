@@ -110,13 +110,14 @@ struct StateRegs {
 //     on MFMA and stored lane by lane: lane (r16, q) keeps C_{16I+r16} .
 //     B_{16J+4q+r}, r = 0..3, exactly the operand fragment the output kernel
 //     needs (k = j), so that kernel reads contiguous bytes per tile.
-template <typename T, int P, int N, int Q>
+// kTiles = false: step 1 only (the gradient kernels need the metadata alone).
+template <typename T, int P, int N, int Q, bool kTiles>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     using C_ = Cfg<T, P, N, Q>;
     constexpr int kV = C_::kVec;
     constexpr int E = C_::E;
-    __shared__ __attribute__((aligned(16))) T sB[Q * C_::SB];
-    __shared__ __attribute__((aligned(16))) T sC[Q * C_::SB];
+    __shared__ __attribute__((aligned(16))) T sB[kTiles ? Q * C_::SB : kV];
+    __shared__ __attribute__((aligned(16))) T sC[kTiles ? Q * C_::SB : kV];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     int64_t w = xcd_work_index(blockIdx.x, gridDim.x);
     const int g = static_cast<int>(w % a.G);
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
     uint4 rb[PPT], rc[PPT];
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
+    for (int k = 0; k < (kTiles ? PPT : 0); ++k) {
         int li = threadIdx.x + kThreads * k;
         li = li < PIECES ? li : PIECES - 1;
         const int j = li / CPR;
@@ -237,72 +238,74 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         head_meta(hh, raw);
     }
 
-    // ---- stage B and C rows (tokens past L and columns past N are zero)
-    const int64_t valid = a.L - t0;
+    if constexpr (kTiles) {
+        // ---- stage B and C rows (tokens past L and columns past N are zero)
+        const int64_t valid = a.L - t0;
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-        const int li = threadIdx.x + kThreads * k;
-        if (li < PIECES) {
-            const int j = li / CPR, n0 = (li % CPR) * kV;
-            const bool keep = j < valid && n0 < N;
-            *reinterpret_cast<uint4*>(sB + j * C_::SB + n0) = raw_keep(keep, rb[k]);
-            *reinterpret_cast<uint4*>(sC + j * C_::SB + n0) = raw_keep(keep, rc[k]);
-        }
-    }
-    __syncthreads();
-
-    const int r16 = lane & 15, q = lane >> 4;
-    // ---- the chunk's C rows in the output kernel's operand order: piece
-    // (I, s) holds, lane (r16, q), C[16I + r16][32s + 8q .. +7] (16 bytes)
-    if constexpr (sizeof(T) == 2 && N % 32 == 0) {
-        if (a.cmf != nullptr) {
-            constexpr int KS = N / 32;
-            T* __restrict__ cm = static_cast<T*>(a.cmf) + ((b * a.nc + c) * a.G + g) * static_cast<int64_t>(Q * N);
-            for (int pc = wave; pc < C_::NB * KS; pc += kWaves) {
-                const int I = pc / KS, s = pc % KS;
-                const uint4 v = *reinterpret_cast<const uint4*>(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
-                *reinterpret_cast<uint4*>(cm + (static_cast<int64_t>(pc) * 64 + lane) * 8) = v;
+        for (int k = 0; k < PPT; ++k) {
+            const int li = threadIdx.x + kThreads * k;
+            if (li < PIECES) {
+                const int j = li / CPR, n0 = (li % CPR) * kV;
+                const bool keep = j < valid && n0 < N;
+                *reinterpret_cast<uint4*>(sB + j * C_::SB + n0) = raw_keep(keep, rb[k]);
+                *reinterpret_cast<uint4*>(sC + j * C_::SB + n0) = raw_keep(keep, rc[k]);
             }
         }
-    }
+        __syncthreads();
 
-    // ---- C.B^T tiles, in pairs (layout at cb_pair_base); half-tile k of pair
-    // p is tile (I, 2u + k), zeros when 2u + k > I
-    T* __restrict__ out = static_cast<T*>(a.cbt) +
-                          ((b * a.nc + c) * a.G + g) * cbt_elems_per_chunk_group(Q);
-    constexpr int NPAIR = C_::NB / 2 * (C_::NB / 2 + 1);
-    // one pair per pass: both tiles share row block I (and its C rows), and
-    // the pair's 8 elements per lane are stored contiguously
-    auto tile_of = [](int pidx, int& I, int& J) {
-        int rbk = 0;
-#pragma unroll
-        for (int r = 1; r < C_::NB; ++r) rbk += cb_pair_base(r) <= pidx ? 1 : 0;
-        I = rbk;
-        J = 2 * (pidx - cb_pair_base(rbk));
-    };
-    for (int pidx = wave; pidx < NPAIR; pidx += kWaves) {
-        int I, J0;
-        tile_of(pidx, I, J0);
-        const bool on1 = J0 + 1 <= I;  // the pair's second tile is left of or on the diagonal
-        f32x4_t acc0 = acc_zero(), acc1 = acc_zero();
-#pragma unroll
-        for (int s = 0; s < C_::KN; ++s) {
-            const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
-            const Frag<T> bf0 = frag_load8(sB + (16 * J0 + r16) * C_::SB + 32 * s + 8 * q);
-            mma(acc0, bf0, cf);
-            if (on1) {
-                const Frag<T> bf1 = frag_load8(sB + (16 * (J0 + 1) + r16) * C_::SB + 32 * s + 8 * q);
-                mma(acc1, bf1, cf);
+        const int r16 = lane & 15, q = lane >> 4;
+        // ---- the chunk's C rows in the output kernel's operand order: piece
+        // (I, s) holds, lane (r16, q), C[16I + r16][32s + 8q .. +7] (16 bytes)
+        if constexpr (sizeof(T) == 2 && N % 32 == 0) {
+            if (a.cmf != nullptr) {
+                constexpr int KS = N / 32;
+                T* __restrict__ cm = static_cast<T*>(a.cmf) + ((b * a.nc + c) * a.G + g) * static_cast<int64_t>(Q * N);
+                for (int pc = wave; pc < C_::NB * KS; pc += kWaves) {
+                    const int I = pc / KS, s = pc % KS;
+                    const uint4 v = *reinterpret_cast<const uint4*>(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
+                    *reinterpret_cast<uint4*>(cm + (static_cast<int64_t>(pc) * 64 + lane) * 8) = v;
+                }
             }
         }
-        T* o = out + (static_cast<int64_t>(pidx) * 64 + lane) * 8;
-        if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<uint4*>(o) =
-                make_uint4(pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
-                           pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3]));
-        } else {
-            store4_f32(o, acc0[0], acc0[1], acc0[2], acc0[3]);
-            store4_f32(o + 4, acc1[0], acc1[1], acc1[2], acc1[3]);
+
+        // ---- C.B^T tiles, in pairs (layout at cb_pair_base); half-tile k of pair
+        // p is tile (I, 2u + k), zeros when 2u + k > I
+        T* __restrict__ out = static_cast<T*>(a.cbt) +
+                              ((b * a.nc + c) * a.G + g) * cbt_elems_per_chunk_group(Q);
+        constexpr int NPAIR = C_::NB / 2 * (C_::NB / 2 + 1);
+        // one pair per pass: both tiles share row block I (and its C rows), and
+        // the pair's 8 elements per lane are stored contiguously
+        auto tile_of = [](int pidx, int& I, int& J) {
+            int rbk = 0;
+#pragma unroll
+            for (int r = 1; r < C_::NB; ++r) rbk += cb_pair_base(r) <= pidx ? 1 : 0;
+            I = rbk;
+            J = 2 * (pidx - cb_pair_base(rbk));
+        };
+        for (int pidx = wave; pidx < NPAIR; pidx += kWaves) {
+            int I, J0;
+            tile_of(pidx, I, J0);
+            const bool on1 = J0 + 1 <= I;  // the pair's second tile is left of or on the diagonal
+            f32x4_t acc0 = acc_zero(), acc1 = acc_zero();
+#pragma unroll
+            for (int s = 0; s < C_::KN; ++s) {
+                const Frag<T> cf = frag_load8(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
+                const Frag<T> bf0 = frag_load8(sB + (16 * J0 + r16) * C_::SB + 32 * s + 8 * q);
+                mma(acc0, bf0, cf);
+                if (on1) {
+                    const Frag<T> bf1 = frag_load8(sB + (16 * (J0 + 1) + r16) * C_::SB + 32 * s + 8 * q);
+                    mma(acc1, bf1, cf);
+                }
+            }
+            T* o = out + (static_cast<int64_t>(pidx) * 64 + lane) * 8;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint4*>(o) =
+                    make_uint4(pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                               pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3]));
+            } else {
+                store4_f32(o, acc0[0], acc0[1], acc0[2], acc0[3]);
+                store4_f32(o + 4, acc1[0], acc1[1], acc1[2], acc1[3]);
+            }
         }
     }
 }
@@ -998,9 +1001,9 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
                     st, src, dst, n);
 }
 
-template <typename T, int P, int N, int Q>
+template <typename T, int P, int N, int Q, bool kTiles = true>
 static hipError_t launch_chunk_prep_t(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
-    return dispatch(chunk_prep_kernel<T, P, N, Q>, dim3(static_cast<unsigned>(nblocks)),
+    return dispatch(chunk_prep_kernel<T, P, N, Q, kTiles>, dim3(static_cast<unsigned>(nblocks)),
                     dim3(kThreads), st, a);
 }
 
@@ -1056,6 +1059,10 @@ int scan_variant_count() {
 }
 
 const ScanVariant* scan_variant_at(int i) { return &kScanVariants[i]; }
+
+hipError_t launch_chunk_meta_bf16_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
+    return launch_chunk_prep_t<uint16_t, 64, 128, 128, false>(a, nblocks, st);
+}
 
 hipError_t launch_state_update(int io, int64_t N, const StepArgs& a, int64_t nblocks,
                                hipStream_t st) {

@@ -69,6 +69,37 @@ struct StepArgs {
     int H, P, G;
 };
 
+// Gradient kernels' arguments (ssd_bwd.hip; bf16 x, B, C, dy, dx, dB, dC).
+struct BwdArgs {
+    const void* x;          // (b, L, H, P)
+    const void* B;          // (b, L, G, N)
+    const void* C;          // (b, L, G, N)
+    const void* dy;         // (b, L, H, P)
+    const float* dt_raw;    // (b, L, H)
+    const float* dt_bias;   // (H) or null
+    const float* A;         // (H)
+    const float* D;         // (H) or null
+    int softplus;
+    float dt_min, dt_max;
+    const int32_t* seq_idx; // (b, L) or null
+    const float* h_init;    // (b, H, P, N) or null
+    const float* dh_final;  // (b, H, P, N) or null (zero)
+    const float* cs;        // chunk_prep_kernel's metadata blocks (as ScanArgs::cs)
+    float* states;          // (b, H, nc, P, N) workspace: state before each chunk
+    float* gstates;         // (b, H, nc, P, N) workspace: gradient after each chunk
+    float* partials;        // (b, nc, H, 3) workspace: dA, dD, d(dt_bias) per chunk
+    void* dx;               // (b, L, H, P)
+    float* ddt;             // (b, L, H): gradient with respect to dt_raw
+    float* dA;              // (H)
+    void* dB;               // (b, L, G, N)
+    void* dC;               // (b, L, G, N)
+    float* dD;              // (H) or null
+    float* ddt_bias;        // (H) or null
+    float* dh_init;         // (b, H, P, N) or null
+    int64_t L;
+    int batch, H, G, nc;
+};
+
 typedef hipError_t (*ScanLaunchFn)(const ScanArgs&, int64_t nblocks, hipStream_t);
 
 struct ScanVariant {
@@ -130,6 +161,18 @@ inline hipError_t dispatch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipS
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
     return hipGetLastError();
 }
+
+// chunk_prep_kernel's per-token metadata alone (cs, dt, weights; no C.B^T
+// tiles), bf16, P = 64, N = 128, Q = 128: one workgroup per (row, chunk, group).
+hipError_t launch_chunk_meta_bf16_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+
+// Gradient kernels (bf16, P = 64, N = 128, Q = 128): the chain of states
+// (forward: before each chunk; reverse: gradient after each chunk, then
+// d(h_init)), the per-(row, chunk, group) gradients, the per-head sums.
+hipError_t launch_bwd_states(const BwdArgs& a, bool reverse, hipStream_t st);
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st);
 
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);

@@ -370,6 +370,7 @@ def test_pins_catch_planted_mistakes(tmp_path):
     assert _pin_suite(oracle._load()) == []
     for name, (old, new) in MUTATIONS.items():
         assert old in src, name
-        path = oracle.compile_variant(src.replace(old, new), str(tmp_path / ("m_%s.so" % name)))
+        # planted in the forward recurrence (the first occurrence in the source)
+        path = oracle.compile_variant(src.replace(old, new, 1), str(tmp_path / ("m_%s.so" % name)))
         lib = oracle._load(path)
         assert _pin_suite(lib), "mutation %s went undetected" % name
