@@ -448,9 +448,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     if (timed_launch(k, hs, [&] { return ssd::launch_chunk_meta_bf16_64_128_128(sa, b * plan.nc * G, hs); }) !=
         hipSuccess)
         return SSD_ERR_HIP;
-    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_states(ba, false, hs); }) != hipSuccess)
-        return SSD_ERR_HIP;
-    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_states(ba, true, hs); }) != hipSuccess)
+    if (timed_launch(k, hs, [&] { return ssd::launch_bwd_states(ba, hs); }) != hipSuccess)
         return SSD_ERR_HIP;
     if (timed_launch(k, hs, [&] { return ssd::launch_bwd_chunk(ba, hs); }) != hipSuccess)
         return SSD_ERR_HIP;

@@ -30,10 +30,11 @@
 // Every term is local to its chunk once h_in and g_out are known.
 //
 // Kernels (one backward call):
-//   bwd_states_kernel<false>  one workgroup per (row, head): the states h_in of
-//        every chunk, in chunk order (h <- e_c h + sum_j omega_j dt_j x_j B_j^T);
-//   bwd_states_kernel<true>   the same walk backwards for g_out of every chunk
-//        (g <- e_c g + sum_i kappa_i dy_i C_i^T); its last state is d(h_init);
+//   bwd_states_kernel   one workgroup per (row, head) and direction, both
+//        directions in one launch: forward, the states h_in of every chunk in
+//        chunk order (h <- e_c h + sum_j omega_j dt_j x_j B_j^T); backward, g_out
+//        of every chunk (g <- e_c g + sum_i kappa_i dy_i C_i^T), whose last state
+//        is d(h_init); each walk loads the next chunk during the current one;
 //   bwd_chunk_kernel          one workgroup per (row, chunk, group), the group's
 //        heads in turn: every gradient above on bf16 MFMA, dB and dC summed over
 //        the heads in registers (no atomics: deterministic);
@@ -82,6 +83,37 @@ __device__ __forceinline__ void stage_rows(char* lds, const char* src, int64_t g
     }
 }
 
+// The same in two steps, so that several tiles' loads are in flight together:
+// the 16-byte pieces of this thread (zeros past `valid` rows), then their LDS
+// stores.
+template <int ROW, int ROWS>
+struct RowPieces {
+    static constexpr int SPR = ROW / 16;
+    static constexpr int K = ROWS * SPR / kBThreads;
+    static_assert(ROWS * SPR % kBThreads == 0, "whole rounds");
+    uint4 v[K];
+};
+template <int ROW, int ROWS>
+__device__ __forceinline__ void load_rows(RowPieces<ROW, ROWS>& rp, const char* src, int64_t gstride,
+                                          int valid) {
+#pragma unroll
+    for (int k = 0; k < RowPieces<ROW, ROWS>::K; ++k) {
+        const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+        const int r = q / RowPieces<ROW, ROWS>::SPR, slot = q % RowPieces<ROW, ROWS>::SPR;
+        rp.v[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < valid) rp.v[k] = *reinterpret_cast<const uint4*>(src + r * gstride + slot * 16);
+    }
+}
+template <int ROW, int ROWS>
+__device__ __forceinline__ void store_rows(char* lds, const RowPieces<ROW, ROWS>& rp) {
+#pragma unroll
+    for (int k = 0; k < RowPieces<ROW, ROWS>::K; ++k) {
+        const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+        const int r = q / RowPieces<ROW, ROWS>::SPR, slot = q % RowPieces<ROW, ROWS>::SPR;
+        lds_st<uint4>(lds, lds_addr(lds) + tr_off<ROW>(r, slot * 16), rp.v[k]);
+    }
+}
+
 // Plain fragment: row R of a tile, k = 32s + 8g + e (16 contiguous bytes).
 // `base` is the tile's LDS address; the chunk kernel passes it opaque (formed
 // again for every head), so that no lane address is hoisted out of its loop.
@@ -101,6 +133,39 @@ template <int ROW>
 __device__ __forceinline__ Frag<uint16_t> col_frag(const char* tile, uint32_t base, int mb, int s, int lane) {
     return tr_frag<ROW>(tile, base + tr_lane_off<ROW>(mb, lane), s);
 }
+// Lane bases for the read patterns above, so that a block or k step costs one
+// XOR and an immediate offset (the swizzle of rows r, r + 16 and r + 32 is the
+// same, and tile bases are 1 KB aligned):
+//   col_base: transposing read of column block mb -> base ^ (mb << 5);
+//   row_base: row 16 blk + r16, k step s -> (base ^ (s << 6)) + 16 blk ROW;
+//   tk_base:  row R in token order, k step s -> halves base ^ (2s << 5) and
+//             base ^ ((2s + 1) << 5); 8 bytes at column 32 m + 8g -> base ^ (m << 5).
+template <int ROW>
+__device__ __forceinline__ uint32_t col_base(uint32_t tile, int lane) {
+    return tile + static_cast<uint32_t>(tr_lane_off<ROW>(0, lane));
+}
+template <int ROW>
+__device__ __forceinline__ uint32_t row_base(uint32_t tile, int r16, int g) {
+    return tile + static_cast<uint32_t>(tr_off<ROW>(r16, 16 * g));
+}
+template <int ROW>
+__device__ __forceinline__ uint32_t tk_base(uint32_t tile, int R, int g) {
+    return tile + static_cast<uint32_t>(tr_off<ROW>(R, 8 * g));
+}
+template <int ROW>
+__device__ __forceinline__ Frag<uint16_t> col_at(const char* tile, uint32_t cb, int mb, int s) {
+    return tr_frag<ROW>(tile, cb ^ static_cast<uint32_t>(mb << 5), s);
+}
+template <int ROW>
+__device__ __forceinline__ Frag<uint16_t> row_at(const char* tile, uint32_t rb, int blk, int s) {
+    return frag_of(lds_ld<uint4>(tile, (rb ^ static_cast<uint32_t>(s << 6)) + 16 * blk * ROW));
+}
+__device__ __forceinline__ Frag<uint16_t> tk_at(const char* tile, uint32_t tb, int s) {
+    const uint2 lo = lds_ld<uint2>(tile, tb ^ static_cast<uint32_t>(s << 6));
+    const uint2 hi = lds_ld<uint2>(tile, tb ^ static_cast<uint32_t>((2 * s + 1) << 5));
+    return frag_of(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // Token-order fragment elements scaled by per-token factors f[32s + ...].
 __device__ __forceinline__ Frag<uint16_t> scale_tk(const Frag<uint16_t>& f, const float* fv, int s, int g) {
     const float4 w0 = *reinterpret_cast<const float4*>(fv + 32 * s + 4 * g);
@@ -129,14 +194,11 @@ __device__ __forceinline__ int seq_at(const int32_t* seq, int64_t row_base, int6
 // `states` at (row, head, chunk).  Wave w owns state rows n = 16w + 4g + r,
 // column p = 16pb + r16 (the MFMA accumulator layout).
 template <bool kRev>
-__global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];   // x or dy rows
-    __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];   // B or C rows
-    __shared__ __attribute__((aligned(16))) float sW[kBQ];            // per-token weights
+__device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, char* sV, char* sK,
+                                                float* sW) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
     const int r16 = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.H;
     const int h = static_cast<int>(bh % a.H);
     const int grp = h / (a.H / a.G);
@@ -158,35 +220,50 @@ __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
     const char* ksrc = static_cast<const char*>(kRev ? a.C : a.B);
     const int64_t vstride = static_cast<int64_t>(a.H) * kRowX;
     const int64_t kstride = static_cast<int64_t>(a.G) * kRowB;
-    for (int k = 0; k < a.nc; ++k) {
+    // chunk k of the walk: its tiles, this thread's token weight and the decay
+    // e_c, all loaded into registers one chunk ahead
+    struct Next {
+        RowPieces<kRowX, kBQ> v;
+        RowPieces<kRowB, kBQ> kr;
+        float w, e;
+    };
+    auto fetch = [&](int k, Next& nx) {
         const int c = kRev ? a.nc - 1 - k : k;
         const int64_t t0 = static_cast<int64_t>(c) * kBQ;
         const int valid = static_cast<int>(L - t0 < kBQ ? L - t0 : kBQ);
+        const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
+        const int seq_prev = seq_at(a.seq_idx, srow, t0 == 0 ? 0 : t0 - 1, L);
+        const int seq_last = seq_at(a.seq_idx, srow, t0 + valid - 1, L);
+        load_rows(nx.v, vsrc + ((srow + t0) * a.H + h) * kRowX, vstride, valid);
+        load_rows(nx.kr, ksrc + ((srow + t0) * a.G + grp) * kRowB, kstride, valid);
+        const int t = static_cast<int>(threadIdx.x);
+        nx.w = 0.0f;
+        if (t < valid) {
+            if (kRev) {
+                nx.w = seq_at(a.seq_idx, srow, t0 + t, L) == seq_prev ? decay_exp(meta[t]) : 0.0f;
+            } else {
+                nx.w = meta[2 * kBQ + t];  // omega_t dt_t from chunk_prep_kernel
+            }
+        }
+        const float cs_last = meta[valid - 1];
+        nx.e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
+    };
+    Next nx;
+    fetch(0, nx);
+    for (int k = 0; k < a.nc; ++k) {
+        const int c = kRev ? a.nc - 1 - k : k;
         // the state before this chunk's update
         float* dst = (kRev ? a.gstates : a.states) + (bh * a.nc + c) * kBP * kBN;
 #pragma unroll
         for (int pb = 0; pb < kBP / 16; ++pb)
             *reinterpret_cast<float4*>(dst + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
                 make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
-        const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
-        const int seq_prev = seq_at(a.seq_idx, srow, t0 == 0 ? 0 : t0 - 1, L);
-        const int seq_last = seq_at(a.seq_idx, srow, t0 + valid - 1, L);
-        const float cs_last = meta[valid - 1];
-        const float e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
-        stage_rows<kRowX, kBQ>(sV, vsrc + ((srow + t0) * a.H + h) * kRowX, vstride, valid);
-        stage_rows<kRowB, kBQ>(sK, ksrc + ((srow + t0) * a.G + grp) * kRowB, kstride, valid);
-        for (int t = static_cast<int>(threadIdx.x); t < kBQ; t += kBThreads) {
-            float w = 0.0f;
-            if (t < valid) {
-                if (kRev) {
-                    w = seq_at(a.seq_idx, srow, t0 + t, L) == seq_prev ? decay_exp(meta[t]) : 0.0f;
-                } else {
-                    w = meta[2 * kBQ + t];  // omega_t dt_t from chunk_prep_kernel
-                }
-            }
-            sW[t] = w;
-        }
+        store_rows(sV, nx.v);
+        store_rows(sK, nx.kr);
+        if (threadIdx.x < kBQ) sW[threadIdx.x] = nx.w;
+        const float e = nx.e;
         __syncthreads();
+        if (k + 1 < a.nc) fetch(k + 1, nx);  // in flight during this chunk's products
         const uint32_t bsK = lds_keep(lds_addr(sK)), bsV = lds_keep(lds_addr(sV));
 #pragma unroll
         for (int pb = 0; pb < kBP / 16; ++pb)
@@ -206,6 +283,18 @@ __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
             *reinterpret_cast<float4*>(a.dh_init + bh * kBP * kBN + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
                 make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
     }
+}
+
+// Both walks in one launch (they are independent): workgroups [0, b*H) walk
+// forward over (row, head) = blockIdx.x, the next b*H walk backwards.
+__global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];   // x or dy rows
+    __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];   // B or C rows
+    __shared__ __attribute__((aligned(16))) float sW[kBQ];            // per-token weights
+    const int64_t nbh = static_cast<int64_t>(a.batch) * a.H;
+    const int64_t w = blockIdx.x;
+    if (w < nbh) bwd_states_walk<false>(a, w, sV, sK, sW);
+    else bwd_states_walk<true>(a, w - nbh, sV, sK, sW);
 }
 
 // --------------------------------------------------------- per-chunk gradients
@@ -259,6 +348,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sDin[kBQ];
     __shared__ __attribute__((aligned(16))) float sTj[kBQ];
     __shared__ __attribute__((aligned(16))) float sCar[kBQ];
+    __shared__ __attribute__((aligned(16))) float sRaw[kBQ];  // dt_raw of the head's tokens
     __shared__ __attribute__((aligned(16))) int sSeq[kBQ];
     __shared__ float sRed[kBWaves];
 
@@ -295,9 +385,26 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
 
     for (int hh = 0; hh < hpg; ++hh) {
-        const uint32_t bsB = lds_keep(lds_addr(sB)), bsC = lds_keep(lds_addr(sC));
-        const uint32_t bsX = lds_keep(lds_addr(sX)), bsDY = lds_keep(lds_addr(sDY));
+        // lane bases of this head's accesses (opaque: formed again per head)
         const uint32_t bsT = lds_keep(lds_addr(sT)), bsH = lds_keep(lds_addr(sH));
+        const uint32_t rbX = lds_keep(row_base<kRowX>(lds_addr(sX), r16, g));
+        const uint32_t rbDY = lds_keep(row_base<kRowX>(lds_addr(sDY), r16, g));
+        const uint32_t rbB = lds_keep(row_base<kRowB>(lds_addr(sB), r16, g));
+        const uint32_t rbC = lds_keep(row_base<kRowB>(lds_addr(sC), r16, g));
+        const uint32_t rbH = lds_keep(row_base<kRowB>(lds_addr(sH), r16, g));
+        const uint32_t cbDY = lds_keep(col_base<kRowX>(lds_addr(sDY), lane));
+        const uint32_t cbB = lds_keep(col_base<kRowB>(lds_addr(sB), lane));
+        const uint32_t cbC = lds_keep(col_base<kRowB>(lds_addr(sC), lane));
+        const uint32_t cbH = lds_keep(col_base<kRowB>(lds_addr(sH), lane));
+        const uint32_t cbT = lds_keep(col_base<kRowT>(lds_addr(sT), lane));
+        // row 16 * wave + r16 (the j of P2, P3 and the i of P4) in token order
+        const int rw = 16 * wave + r16;
+        const uint32_t tkT = lds_keep(tk_base<kRowT>(lds_addr(sT), rw, g));
+        const uint32_t tkX = lds_keep(tk_base<kRowX>(lds_addr(sX), rw, g));
+        const uint32_t tkDY = lds_keep(tk_base<kRowX>(lds_addr(sDY), rw, g));
+        const uint32_t tkC = lds_keep(tk_base<kRowB>(lds_addr(sC), rw, g));
+        // S^T / W^T writes: row 16 J + r16, columns 16 I + 4g .. +3
+        const uint32_t wT = lds_keep(tk_base<kRowT>(lds_addr(sT), r16, g) ^ static_cast<uint32_t>(I << 5));
         const int h = grp * hpg + hh;
         const int64_t bh = b * a.H + h;
         const float Ah = a.A[h];
@@ -305,31 +412,43 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
         const float cs_last = meta[valid - 1];
         const float e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
-        // ---- head inputs
+        // ---- head inputs: every load issued before any is used (one round trip)
         const int64_t xstride = static_cast<int64_t>(a.H) * kRowX;
-        stage_rows<kRowX, kBQ>(sX, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
-        stage_rows<kRowX, kBQ>(sDY, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
-        for (int t = static_cast<int>(threadIdx.x); t < kBQ; t += kBThreads) {
-            const float cst = meta[t];
-            sCs[t] = cst;
-            sDt[t] = meta[kBQ + t];
-            const bool in = t < valid;
-            sOm[t] = in && sSeq[t] == seq_last ? decay_exp(cs_last - cst) : 0.0f;
-            sKa[t] = in && sSeq[t] == seq_prev ? decay_exp(cst) : 0.0f;
-        }
-        // g_out as the bf16 operand copy; its fp32 values stay for <g_out, h_in>
+        RowPieces<kRowX, kBQ> px, pdy;
+        load_rows(px, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
+        load_rows(pdy, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
         const float* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
         const float* hsrc = a.states + (bh * a.nc + c) * kBP * kBN;
-        float gv[16];
+        float4 gq[4];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;  // 16-byte bf16 piece
-            const int p = q / 16, slot = q % 16;
-            const float4 v0 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot);
-            const float4 v1 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot + 4);
-            gv[8 * k + 0] = v0.x; gv[8 * k + 1] = v0.y; gv[8 * k + 2] = v0.z; gv[8 * k + 3] = v0.w;
-            gv[8 * k + 4] = v1.x; gv[8 * k + 5] = v1.y; gv[8 * k + 6] = v1.z; gv[8 * k + 7] = v1.w;
-            lds_st<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot),
+            gq[2 * k] = *reinterpret_cast<const float4*>(gsrc + (q / 16) * kBN + 8 * (q % 16));
+            gq[2 * k + 1] = *reinterpret_cast<const float4*>(gsrc + (q / 16) * kBN + 8 * (q % 16) + 4);
+        }
+        const int tt = static_cast<int>(threadIdx.x);
+        float m_cs = 0.0f, m_dt = 0.0f, m_raw = 0.0f;
+        if (tt < kBQ) {
+            m_cs = meta[tt];
+            m_dt = meta[kBQ + tt];
+            if (tt < valid) m_raw = a.dt_raw[(srow + t0 + tt) * a.H + h];
+        }
+        store_rows(sX, px);
+        store_rows(sDY, pdy);
+        if (tt < kBQ) {
+            sCs[tt] = m_cs;
+            sDt[tt] = m_dt;
+            sRaw[tt] = m_raw;
+            const bool in = tt < valid;
+            sOm[tt] = in && sSeq[tt] == seq_last ? decay_exp(cs_last - m_cs) : 0.0f;
+            sKa[tt] = in && sSeq[tt] == seq_prev ? decay_exp(m_cs) : 0.0f;
+        }
+        // g_out as the bf16 operand copy
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+            const float4 v0 = gq[2 * k], v1 = gq[2 * k + 1];
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)),
                           make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
                                      pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)));
         }
@@ -354,7 +473,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
             f32x4_t m1 = acc_zero();
 #pragma unroll
             for (int ks = 0; ks < kBP / 32; ++ks)
-                mma(m1, row_frag<kRowX>(sDY, bsDY, 16 * I + r16, ks, g), row_frag<kRowX>(sX, bsX, 16 * J + r16, ks, g));
+                mma(m1, row_at<kRowX>(sDY, rbDY, I, ks), row_at<kRowX>(sX, rbX, J, ks));
             return m1;
         };
         for (int J = 0; J < 8; ++J) {
@@ -365,7 +484,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                 f32x4_t cbt = acc_zero();
 #pragma unroll
                 for (int ks = 0; ks < kBN / 32; ++ks)
-                    mma(cbt, row_frag<kRowB>(sC, bsC, 16 * I + r16, ks, g), row_frag<kRowB>(sB, bsB, 16 * J + r16, ks, g));
+                    mma(cbt, row_at<kRowB>(sC, rbC, I, ks), row_at<kRowB>(sB, rbB, J, ks));
                 const float dt_j = sDt[16 * J + r16];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -376,7 +495,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                 }
             }
             // S^T row j, columns i = 16I + 4g .. +3 (zeros right of the diagonal block)
-            lds_st<uint2>(sT, bsT + tr_off<kRowT>(16 * J + r16, 32 * I + 8 * g), pack4(sv));
+            lds_st<uint2>(sT, wT + 16 * J * kRowT, pack4(sv));
             csum = sum_g(csum);
             if (g == 0) sCols[I * kBQ + 16 * J + r16] = csum;
         }
@@ -400,16 +519,16 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int ks = 0; ks < kBQ / 32; ++ks) {
                 if (2 * ks + 1 >= J) {
-                    const Frag<uint16_t> sf = row_frag_tk<kRowT>(sT, bsT, j, ks, g);
+                    const Frag<uint16_t> sf = tk_at(sT, tkT, ks);
 #pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) mma(ut[pb], col_frag<kRowX>(sDY, bsDY, pb, ks, lane), sf);
+                    for (int pb = 0; pb < 4; ++pb) mma(ut[pb], col_at<kRowX>(sDY, cbDY, pb, ks), sf);
                 }
             }
 #pragma unroll
             for (int ks = 0; ks < kBN / 32; ++ks) {
-                const Frag<uint16_t> bf = row_frag<kRowB>(sB, bsB, j, ks, g);
+                const Frag<uint16_t> bf = row_at<kRowB>(sB, rbB, J, ks);
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) mma(vt[pb], row_frag<kRowB>(sH, bsH, 16 * pb + r16, ks, g), bf);
+                for (int pb = 0; pb < 4; ++pb) mma(vt[pb], row_at<kRowB>(sH, rbH, pb, ks), bf);
             }
             const float om_j = sOm[j], dt_j = sDt[j];
             float din = 0.0f, tsum = 0.0f, dd = 0.0f;
@@ -417,8 +536,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) {
                 // row j, p = 16pb + 4g .. +3
-                const uint2 xr = lds_ld<uint2>(sX, bsX + tr_off<kRowX>(j, 32 * pb + 8 * g));
-                const uint2 yr = lds_ld<uint2>(sDY, bsDY + tr_off<kRowX>(j, 32 * pb + 8 * g));
+                const uint2 xr = lds_ld<uint2>(sX, tkX ^ static_cast<uint32_t>(pb << 5));
+                const uint2 yr = lds_ld<uint2>(sDY, tkDY ^ static_cast<uint32_t>(pb << 5));
                 const float xv[4] = {bf_lo(xr.x), bf_hi(xr.x), bf_lo(xr.y), bf_hi(xr.y)};
                 const float yv[4] = {bf_lo(yr.x), bf_hi(yr.x), bf_lo(yr.y), bf_hi(yr.y)};
                 float dxv[4];
@@ -451,19 +570,21 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int q = 0; q < kBWaves; ++q) dD_part += sRed[q];
 
-        // ---- W^T over S^T (W = M1 L, M1 formed again)
+        // ---- W'^T over S^T: W'_ij = M1_ij L_ij dt_j (M1 formed again); both of
+        // its products need W scaled by dt of its column
         for (int J = 0; J < 8; ++J) {
             f32x4_t wv = acc_zero();
             if (J <= I) {
                 const f32x4_t m1 = m1_tile(J);
+                const float dt_j = sDt[16 * J + r16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) wv[r] = m1[r] * decay_l(J, r);
+                for (int r = 0; r < 4; ++r) wv[r] = m1[r] * decay_l(J, r) * dt_j;
             }
-            lds_st<uint2>(sT, bsT + tr_off<kRowT>(16 * J + r16, 32 * I + 8 * g), pack4(wv));
+            lds_st<uint2>(sT, wT + 16 * J * kRowT, pack4(wv));
         }
         __syncthreads();
 
-        // ---- P3: dB^T += dt_j [(C^T W) + omega_j g_out^T X^T], columns j of block J = wave
+        // ---- P3: dB^T += C^T W' + dt_j omega_j g_out^T X^T, columns j of block J = wave
         {
             const int J = wave;
             const int j = 16 * J + r16;
@@ -473,16 +594,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                 f32x4_t a1 = acc_zero(), a2 = acc_zero();
 #pragma unroll
                 for (int ks = 0; ks < kBQ / 32; ++ks)
-                    if (2 * ks + 1 >= J) mma(a1, col_frag<kRowB>(sC, bsC, nb, ks, lane), row_frag_tk<kRowT>(sT, bsT, j, ks, g));
+                    if (2 * ks + 1 >= J) mma(a1, col_at<kRowB>(sC, cbC, nb, ks), tk_at(sT, tkT, ks));
 #pragma unroll
                 for (int ks = 0; ks < kBP / 32; ++ks)
-                    mma(a2, col_frag<kRowB>(sH, bsH, nb, ks, lane), row_frag_tk<kRowX>(sX, bsX, j, ks, g));
+                    mma(a2, col_at<kRowB>(sH, cbH, nb, ks), tk_at(sX, tkX, ks));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dBacc[nb][r] += dt_j * (a1[r] + om_j * a2[r]);
+                for (int r = 0; r < 4; ++r) dBacc[nb][r] += a1[r] + dt_j * om_j * a2[r];
                 __builtin_amdgcn_sched_barrier(0);  // one n block's operands live at a time
             }
         }
-        // <g_out, h_in> (fp32); then h_in replaces g_out as the bf16 operand
+        // <g_out, h_in> (fp32, g_out read again); then h_in replaces g_out as
+        // the bf16 operand
         float ghp = 0.0f;
         float hv[16];
 #pragma unroll
@@ -491,11 +613,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
             const int p = q / 16, slot = q % 16;
             const float4 v0 = *reinterpret_cast<const float4*>(hsrc + p * kBN + 8 * slot);
             const float4 v1 = *reinterpret_cast<const float4*>(hsrc + p * kBN + 8 * slot + 4);
+            const float4 g0 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot);
+            const float4 g1 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot + 4);
             hv[8 * k + 0] = v0.x; hv[8 * k + 1] = v0.y; hv[8 * k + 2] = v0.z; hv[8 * k + 3] = v0.w;
             hv[8 * k + 4] = v1.x; hv[8 * k + 5] = v1.y; hv[8 * k + 6] = v1.z; hv[8 * k + 7] = v1.w;
+            ghp += g0.x * v0.x + g0.y * v0.y + g0.z * v0.z + g0.w * v0.w;
+            ghp += g1.x * v1.x + g1.y * v1.y + g1.z * v1.z + g1.w * v1.w;
         }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) ghp += gv[q] * hv[q];
         const float gh = block_sum(ghp, sRed);  // its barriers also end P3's reads of g_out
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -507,7 +631,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         }
         __syncthreads();
 
-        // ---- P4: dC^T += (B^T dt) W^T + kappa_i h_in^T dY^T, columns i of block I = wave
+        // ---- P4: dC^T += B^T W'^T + kappa_i h_in^T dY^T, columns i of block I = wave
         {
             const int i = 16 * I + r16;
             const float ka_i = sKa[i];
@@ -518,12 +642,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < kBQ / 32; ++ks)
                     if (2 * ks <= I)
-                        mma(cw, scale_tk(col_frag<kRowB>(sB, bsB, nb, ks, lane), sDt, ks, g),
-                            col_frag<kRowT>(sT, bsT, I, ks, lane));
+                        mma(cw, col_at<kRowB>(sB, cbB, nb, ks), col_at<kRowT>(sT, cbT, I, ks));
 #pragma unroll
                 for (int ks = 0; ks < kBP / 32; ++ks)
-                    mma(cc, col_frag<kRowB>(sH, bsH, nb, ks, lane), row_frag_tk<kRowX>(sDY, bsDY, i, ks, g));
-                const uint2 cr = lds_ld<uint2>(sC, bsC + tr_off<kRowB>(i, 32 * nb + 8 * g));
+                    mma(cc, col_at<kRowB>(sH, cbH, nb, ks), tk_at(sDY, tkDY, ks));
+                const uint2 cr = lds_ld<uint2>(sC, tkC ^ static_cast<uint32_t>(nb << 5));
                 const float cv[4] = {bf_lo(cr.x), bf_hi(cr.x), bf_lo(cr.y), bf_hi(cr.y)};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -579,7 +702,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                     dA_part += dtv * da;
                     const float ddt = sDin[t] + Ah * da;
                     const int64_t ti = (srow + t0 + t) * a.H + h;
-                    const float v = a.dt_raw[ti] + bias;
+                    const float v = sRaw[t] + bias;
                     const float sp = a.softplus ? softplus_f32(v) : v;
                     float draw = 0.0f;
                     if (sp >= a.dt_min && sp <= a.dt_max) draw = a.softplus ? ddt / (1.0f + __expf(-v)) : ddt;
@@ -660,10 +783,9 @@ hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st) {
                     nstate);
 }
 
-hipError_t launch_bwd_states(const BwdArgs& a, bool reverse, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.H));
-    if (reverse) return dispatch(bwd_states_kernel<true>, grid, dim3(kBThreads), st, a);
-    return dispatch(bwd_states_kernel<false>, grid, dim3(kBThreads), st, a);
+hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(2 * static_cast<int64_t>(a.batch) * a.H));
+    return dispatch(bwd_states_kernel, grid, dim3(kBThreads), st, a);
 }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st) {

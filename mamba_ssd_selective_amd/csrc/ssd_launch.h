@@ -166,10 +166,11 @@ inline hipError_t dispatch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipS
 // tiles), bf16, P = 64, N = 128, Q = 128: one workgroup per (row, chunk, group).
 hipError_t launch_chunk_meta_bf16_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
 
-// Gradient kernels (bf16, P = 64, N = 128, Q = 128): the chain of states
+// Gradient kernels (bf16, P = 64, N = 128, Q = 128): the chains of states
 // (forward: before each chunk; reverse: gradient after each chunk, then
-// d(h_init)), the per-(row, chunk, group) gradients, the per-head sums.
-hipError_t launch_bwd_states(const BwdArgs& a, bool reverse, hipStream_t st);
+// d(h_init); one launch), the per-(row, chunk, group) gradients, the per-head
+// sums.
+hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st);
