@@ -16,6 +16,12 @@ start and end timestamps) and the fp64 CPU oracle timed on the host cores.
 
 The defaults warm up for about 30 ms (the clocks settle within about 20 ms of
 sustained work) and time about 0.1 s of steps.
+
+The line also carries a "backward" object for the gradients of the same scan
+(ssd_chunk_scan_bwd on the same inputs, seeded dy and final-state gradient):
+its tokens/s, per-kernel times, a roofline entry for its per-chunk gradient
+kernel against the compulsory bytes of the whole backward pass, and the fp64
+oracle's gradients timed on the heads of one group.
 """
 import argparse
 import ctypes
@@ -127,12 +133,110 @@ def cpu_baseline(p, w, budget_s):
                       % (w.name, w.seqlen, block, H, el, head_tokens / (w.batch * w.seqlen * H))}
 
 
+def backward_measure(ssd, lib, hip, torch, base, A, D, bias, w, steps, cpu_seconds, p):
+    """The backward pass (ssd_chunk_scan_bwd) on the same workload: tokens/s
+    over `steps` timed calls, the gradient kernel's duration from events bound
+    to its dispatch, its roofline against the compulsory bytes of the whole
+    backward, and the oracle's gradients timed on one group of heads."""
+    import numpy as np
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    if not (P == 64 and N == 128 and Q == 128):
+        return None
+    dev = base["x"].device
+    gen = torch.Generator(device="cpu").manual_seed(2024)
+    dy = torch.randn((b, L, H, P), generator=gen).to(torch.bfloat16).to(dev)
+    dfin = torch.randn((b, H, P, N), generator=gen).to(dev)
+    ws = torch.empty(ssd.bwd_workspace_bytes(b, L, H, P, N, G, Q), dtype=torch.uint8, device=dev)
+
+    def call():
+        return ssd.chunk_scan_bwd(base["x"], base["dt"], A, base["B"], base["C"], dy, chunk_size=Q,
+                                  D=D, dt_bias=bias, initial_states=base["h0"], seq_idx=base["seq"],
+                                  d_final_states=dfin, workspace=ws)
+
+    launched = ctypes.c_int(0)
+    no_events = (ctypes.c_void_p * 16)()
+    lib.ssd_set_timing_events(no_events, 16, ctypes.byref(launched))
+    call()
+    lib.ssd_set_timing_events(None, 0, None)
+    nk = launched.value
+    names = ["chunk_meta", "chunk_states", "chunk_grad", "grad_sums"][:nk]
+    kg = names.index("chunk_grad")
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    vp = ctypes.sizeof(ctypes.c_void_p)
+    evs = hip.events(2 * nk * steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sl = (ctypes.c_void_p * (2 * nk))()
+        sl[2 * kg] = evs[2 * nk * i + 2 * kg]
+        sl[2 * kg + 1] = evs[2 * nk * i + 2 * kg + 1]
+        lib.ssd_set_timing_events(sl, 2 * nk, ctypes.byref(launched))
+        call()
+    lib.ssd_set_timing_events(None, 0, None)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    grad_us = 1e3 * float(np.mean([hip.elapsed_ms(evs[2 * nk * i + 2 * kg], evs[2 * nk * i + 2 * kg + 1])
+                                   for i in range(steps)]))
+    diag = min(steps, 10)
+    for i in range(diag):
+        lib.ssd_set_timing_events(ev_slice_of(evs, 2 * nk * i, 2 * nk, vp), 2 * nk, ctypes.byref(launched))
+        call()
+    lib.ssd_set_timing_events(None, 0, None)
+    torch.cuda.synchronize()
+    kus = {n: round(1e3 * float(np.mean([hip.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
+                                        for i in range(diag)])), 2) for k, n in enumerate(names)}
+    hip.destroy(evs)
+    # compulsory bytes: x, dy, B, C, dt in; dx, dB, dC, d(dt) out; the states in and out
+    per_token = 2 * (2 * H * P * 2 + 2 * G * N * 2 + H * 4)
+    state_bytes = b * H * P * N * 4
+    bwd_bytes = b * L * per_token + 3 * state_bytes + (b * L * 4 if base["seq"] is not None else 0)
+    achieved = bwd_bytes / (grad_us * 1e-6) / 1e9
+    out = {"value": round(b * L * steps / el, 1), "unit": "tokens/s", "steps": steps,
+           "ms_per_step": round(1e3 * el / steps, 5), "dtype": "bf16",
+           "grad_kernel_us": round(grad_us, 2), "kernels_us": kus,
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+           "cpu_baseline": None}
+    if cpu_seconds > 0:
+        import oracle
+        grp = 0
+        hs = slice(0, H // G)
+        pin = {k: (None if v is None else v) for k, v in p.items()}
+        dy_np = dy.float().cpu().numpy()
+        df_np = dfin.cpu().numpy()
+        t0 = time.perf_counter()
+        runs = 0
+        while runs == 0 or time.perf_counter() - t0 < cpu_seconds:
+            oracle.scan_bwd(pin["x"][:, :L, hs], pin["dt_raw"][:, :L, hs], pin["A"][hs],
+                            pin["B"][:, :L, grp:grp + 1], pin["C"][:, :L, grp:grp + 1], dy_np[:, :, hs],
+                            dh_final=df_np[:, hs], dt_bias=pin["dt_bias"][hs], D=pin["D"][hs],
+                            h_init=None if pin.get("h_init") is None else pin["h_init"][:, hs],
+                            seq_idx=None if pin.get("seq_idx") is None else pin["seq_idx"][:, :L])
+            runs += 1
+        cel = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(b * L * runs * (H // G) / H / cel, 1), "unit": "tokens/s",
+            "cores": min(oracle.max_threads(), b * (H // G)), "kind": "oracle",
+            "sample": "%s: gradients of all %d tokens for the %d heads of group 0, %d run(s) in "
+                      "%.1f s (fp64 reverse-mode recurrence, OpenMP over heads); tokens/s of the "
+                      "whole workload" % (w.name, L, H // G, runs, cel)}
+    return out
+
+
+def ev_slice_of(evs, first, count, vp):
+    return (ctypes.c_void_p * count).from_buffer(evs, first * vp)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS_BY_NAME))
+    ap.add_argument("--backward-steps", type=int, default=30,
+                    help="timed calls of the backward pass (reported under \"backward\")")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -302,6 +406,9 @@ def main():
         "chunk_output_mfma_frac": round(flops / k4_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "source_hash": source_hash(),
     }
+    log("bench: backward pass")
+    result["backward"] = backward_measure(ssd, lib, hip, torch, sets[0], A, D, bias, w,
+                                          args.backward_steps, min(args.cpu_seconds, 5.0), p)
     if args.cpu_seconds > 0:
         log("bench: CPU oracle baseline (budget %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline({k: (v[:, :L] if k in ("x", "dt_raw", "B", "C", "seq_idx") and v is not None else v)
