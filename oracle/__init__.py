@@ -11,6 +11,8 @@ Three independent formulations of the same operation live here:
 * ``scan`` / ``step`` -- the plain sequential recurrence in C (``ssd_oracle.c``),
   the authority every GPU result is compared against;
 * ``scan_bwd`` -- its gradients, by reverse mode of the same recurrence in C;
+* ``mixer`` -- the steps beside the scan (causal conv1d + bias + SiLU with its
+  conv state, the split into x/B/C, gated group RMSNorm), numpy fp64;
 * ``dual.quadratic_scan`` -- the brute-force matrix ("dual") form with explicit
   products of per-step decays, for tiny inputs;
 * ``chunked.chunked_scan`` -- the chunk decomposition (chunk states, state
