@@ -164,6 +164,49 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* dims, ssd_dtype io, const void* x,
                               void* stream);
 
 /*
+ * The steps beside the scan in the Mamba-2 mixer (RL-Kernel RFC
+ * "Nemotron-3-Nano-30B-A3B", section 3, Figure 2, box [F2]).
+ *
+ * ssd_conv1d_fwd: causal depthwise conv1d of width 4 + bias + SiLU over the
+ * xBC channels (prefill), written straight into the scan's inputs:
+ *   out_t[c] = silu(bias[c] + sum_{k<4} weight[c][k] * in_{t-3+k}[c]),
+ * inputs before token 0 taken from conv_state_in (oldest first) or zero; with
+ * seq_idx, an input of another sequence counts as zero (the state belongs to
+ * the sequence of token 0).
+ *   xbc      (b, L, dim)  io dtype, dim = nx + 2 * nb
+ *   weight   (dim, 4) fp32;  width must be 4;  bias (dim) fp32 or NULL
+ *   conv_state_in  (b, dim, 3) io dtype or NULL (zero)
+ *   seq_idx  (b, L) int32 or NULL (as for ssd_chunk_scan_fwd)
+ *   x_out    (b, L, nx) io: channels [0, nx)   (the scan's x as (b, L, H, P))
+ *   b_out, c_out (b, L, nb) io: channels [nx, nx + nb) and [nx + nb, dim)
+ *                          (the scan's B and C as (b, L, G, N))
+ *   conv_state_out (b, dim, 3) io or NULL: the last three inputs (zero where
+ *                          they belong to another sequence than the last
+ *                          token's); may be exactly conv_state_in (in place)
+ * Supported: io F32 or BF16; dim, nx, nb multiples of 8.
+ */
+ssd_status ssd_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t nx, int64_t nb,
+                          ssd_dtype io, const void* xbc, const float* weight, int64_t width,
+                          const float* bias, const void* conv_state_in, const int32_t* seq_idx,
+                          void* x_out, void* b_out, void* c_out, void* conv_state_out,
+                          void* stream);
+
+/* One decode token of the conv: xbc (b, dim), conv_state (b, dim, 3) read and
+ * updated in place (shifted by the new input); outputs x_out (b, nx), b_out,
+ * c_out (b, nb).  Same supported set as ssd_conv1d_fwd. */
+ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb, ssd_dtype io,
+                             const void* xbc, const float* weight, int64_t width, const float* bias,
+                             void* conv_state, void* x_out, void* b_out, void* c_out, void* stream);
+
+/* Gated group RMSNorm of the scan's output: per row and group of `group`
+ * consecutive channels, v = y * silu(z) and out = v / sqrt(mean(v^2) + eps) *
+ * weight.  y, z, out (rows, dim) io dtype; weight (dim) fp32; eps >= 0 (the
+ * pages' RMSNorm epsilon is 1e-6).  Supported: group a multiple of 8, at most
+ * 4096, dividing dim. */
+ssd_status ssd_gated_rmsnorm(int64_t rows, int64_t dim, int64_t group, ssd_dtype io, const void* y,
+                             const void* z, const float* weight, float eps, void* out, void* stream);
+
+/*
  * One decode token per sequence: the per-token recurrent state update (RFC
  * section 1, operator family 1; the state is the fixed-size fp32 SSM state of
  * operator family 2).

@@ -78,6 +78,13 @@ def library():
                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_size_t, vp]
         lib.ssd_chunk_scan_bwd.restype = i
+        lib.ssd_conv1d_fwd.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp, vp, vp,
+                                       vp, vp, vp]
+        lib.ssd_conv1d_fwd.restype = i
+        lib.ssd_conv1d_update.argtypes = [i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp, vp, vp, vp]
+        lib.ssd_conv1d_update.restype = i
+        lib.ssd_gated_rmsnorm.argtypes = [i64, i64, i64, i, vp, vp, vp, f, vp, vp]
+        lib.ssd_gated_rmsnorm.restype = i
         lib.ssd_state_update.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, vp, vp, i, f, f,
                                          vp, vp, vp, vp, vp, vp]
         lib.ssd_state_update.restype = i
@@ -248,6 +255,85 @@ def chunk_scan_bwd(x, dt, A, B, C, dy, *, chunk_size: int, D=None, dt_bias=None,
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_bwd")
     return g
+
+
+def conv1d_fwd(xbc, weight, *, nheads: int, headdim: int, ngroups: int, dstate: int, bias=None,
+               conv_state=None, seq_idx=None, return_conv_state: bool = False,
+               conv_state_out=None):
+    """Causal conv1d (width 4) + bias + SiLU over xbc (b, L, H*P + 2*G*N),
+    written as the scan's inputs: returns x (b, L, H, P), B, C (b, L, G, N) in
+    xbc's dtype, and the new conv state (b, dim, 3) when ``return_conv_state``
+    (``conv_state_out`` may be ``conv_state`` itself: updated in place)."""
+    import torch
+    lib = library()
+    b, L, dim = xbc.shape
+    nx, nb = nheads * headdim, ngroups * dstate
+    dev = xbc.device
+    io = _io_code(xbc.dtype)
+    _check(xbc, "xbc", (b, L, dim), xbc.dtype, dev)
+    _check(weight, "weight", (dim, 4), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev)
+    _check(conv_state, "conv_state", (b, dim, 3), xbc.dtype, dev)
+    _check(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    x = torch.empty((b, L, nheads, headdim), dtype=xbc.dtype, device=dev)
+    Bm = torch.empty((b, L, ngroups, dstate), dtype=xbc.dtype, device=dev)
+    Cm = torch.empty((b, L, ngroups, dstate), dtype=xbc.dtype, device=dev)
+    st = None
+    if return_conv_state:
+        st = conv_state_out if conv_state_out is not None else \
+            torch.empty((b, dim, 3), dtype=xbc.dtype, device=dev)
+        _check(st, "conv_state_out", (b, dim, 3), xbc.dtype, dev)
+    rc = lib.ssd_conv1d_fwd(b, L, dim, nx, nb, io, _ptr(xbc), _ptr(weight), 4, _ptr(bias),
+                            _ptr(conv_state), _ptr(seq_idx), _ptr(x), _ptr(Bm), _ptr(Cm), _ptr(st),
+                            _stream_handle(dev))
+    if rc != 0:
+        raise SSDError(rc, "ssd_conv1d_fwd")
+    return (x, Bm, Cm, st) if return_conv_state else (x, Bm, Cm)
+
+
+def conv1d_update(xbc, conv_state, weight, *, nheads: int, headdim: int, ngroups: int,
+                  dstate: int, bias=None):
+    """One decode token of the conv: xbc (b, dim); conv_state (b, dim, 3) is
+    updated in place.  Returns x (b, H, P), B, C (b, G, N)."""
+    import torch
+    lib = library()
+    b, dim = xbc.shape
+    nx, nb = nheads * headdim, ngroups * dstate
+    dev = xbc.device
+    io = _io_code(xbc.dtype)
+    _check(xbc, "xbc", (b, dim), xbc.dtype, dev)
+    _check(conv_state, "conv_state", (b, dim, 3), xbc.dtype, dev)
+    _check(weight, "weight", (dim, 4), torch.float32, dev)
+    _check(bias, "bias", (dim,), torch.float32, dev)
+    x = torch.empty((b, nheads, headdim), dtype=xbc.dtype, device=dev)
+    Bm = torch.empty((b, ngroups, dstate), dtype=xbc.dtype, device=dev)
+    Cm = torch.empty((b, ngroups, dstate), dtype=xbc.dtype, device=dev)
+    rc = lib.ssd_conv1d_update(b, dim, nx, nb, io, _ptr(xbc), _ptr(weight), 4, _ptr(bias),
+                               _ptr(conv_state), _ptr(x), _ptr(Bm), _ptr(Cm), _stream_handle(dev))
+    if rc != 0:
+        raise SSDError(rc, "ssd_conv1d_update")
+    return x, Bm, Cm
+
+
+def gated_rmsnorm(y, z, weight, *, group: int, eps: float = 1e-6, out=None):
+    """norm(y * silu(z)) over groups of ``group`` channels of the last axis,
+    times weight (fp32, last-axis size).  y, z of the same shape and dtype."""
+    import torch
+    lib = library()
+    dim = y.shape[-1]
+    rows = y.numel() // dim if dim else 0
+    dev = y.device
+    io = _io_code(y.dtype)
+    _check(y, "y", tuple(y.shape), y.dtype, dev)
+    _check(z, "z", tuple(y.shape), y.dtype, dev)
+    _check(weight, "weight", (dim,), torch.float32, dev)
+    o = out if out is not None else torch.empty_like(y)
+    _check(o, "out", tuple(y.shape), y.dtype, dev)
+    rc = lib.ssd_gated_rmsnorm(rows, dim, group, io, _ptr(y), _ptr(z), _ptr(weight), float(eps),
+                               _ptr(o), _stream_handle(dev))
+    if rc != 0:
+        raise SSDError(rc, "ssd_gated_rmsnorm")
+    return o
 
 
 def state_update(state, x, dt, A, B, C, *, D=None, dt_bias=None, dt_softplus: bool = True,

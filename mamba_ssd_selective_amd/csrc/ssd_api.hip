@@ -457,6 +457,142 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     return SSD_OK;
 }
 
+ssd_status ssd_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t nx, int64_t nb,
+                          ssd_dtype io, const void* xbc, const float* weight, int64_t width,
+                          const float* bias, const void* conv_state_in, const int32_t* seq_idx,
+                          void* x_out, void* b_out, void* c_out, void* conv_state_out,
+                          void* stream) {
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
+    if (batch < 0 || seqlen < 0 || nx < 0 || nb < 0 || dim != nx + 2 * nb || dim < 8)
+        return SSD_ERR_BAD_SHAPE;
+    if (width != 4 || dim % 8 != 0 || nx % 8 != 0 || nb % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (batch > 65535 || seqlen > int64_t(65535) * 32 || dim > (int64_t(1) << 30)) return SSD_ERR_BAD_SHAPE;
+    const bool work = batch > 0 && seqlen > 0;
+    if (!weight) return SSD_ERR_NULL_ARG;
+    if (work && (!xbc || !x_out || (nb > 0 && (!b_out || !c_out)))) return SSD_ERR_NULL_ARG;
+    const void* vec_bufs[] = {xbc, weight, x_out, b_out, c_out};
+    for (const void* p : vec_bufs)
+        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    const size_t es = io_size(io);
+    const int64_t rows = batch * seqlen;
+    const Span ins[] = {span(xbc, rows * dim * es), span(weight, dim * 16), span(bias, bias ? dim * 4 : 0),
+                        span(seq_idx, seq_idx ? rows * 4 : 0)};
+    const Span sin = span(conv_state_in, conv_state_in ? batch * dim * 3 * es : 0);
+    const Span outs[] = {span(x_out, rows * nx * es), span(b_out, rows * nb * es), span(c_out, rows * nb * es),
+                         span(conv_state_out, conv_state_out ? batch * dim * 3 * es : 0)};
+    for (size_t i = 0; i < 4; ++i) {
+        for (const Span& s : ins)
+            if (overlap(outs[i], s)) return SSD_ERR_ALIAS;
+        // the state may be updated in place (exactly the same buffer), the
+        // outputs may not overlap the old state otherwise
+        if (overlap(outs[i], sin) && !(i == 3 && conv_state_out == conv_state_in)) return SSD_ERR_ALIAS;
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
+    }
+    if (!work) return SSD_OK;
+    ssd::ConvArgs ca{};
+    ca.xbc = xbc;
+    ca.weight = weight;
+    ca.bias = bias;
+    ca.state_in = conv_state_in;
+    ca.seq_idx = seq_idx;
+    ca.x_out = x_out;
+    ca.b_out = b_out;
+    ca.c_out = c_out;
+    ca.state_out = conv_state_out;
+    ca.L = seqlen;
+    ca.batch = static_cast<int>(batch);
+    ca.dim = static_cast<int>(dim);
+    ca.nx = static_cast<int>(nx);
+    ca.nb = static_cast<int>(nb);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    if (timed_launch(k, hs, [&] { return ssd::launch_conv1d_fwd(io, ca, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb, ssd_dtype io,
+                             const void* xbc, const float* weight, int64_t width, const float* bias,
+                             void* conv_state, void* x_out, void* b_out, void* c_out, void* stream) {
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
+    if (batch < 0 || nx < 0 || nb < 0 || dim != nx + 2 * nb || dim < 8) return SSD_ERR_BAD_SHAPE;
+    if (width != 4 || dim % 8 != 0 || nx % 8 != 0 || nb % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (batch > 65535 || dim > (int64_t(1) << 30)) return SSD_ERR_BAD_SHAPE;
+    if (!weight) return SSD_ERR_NULL_ARG;
+    if (batch > 0 && (!xbc || !conv_state || !x_out || (nb > 0 && (!b_out || !c_out))))
+        return SSD_ERR_NULL_ARG;
+    const void* vec_bufs[] = {xbc, weight, x_out, b_out, c_out};
+    for (const void* p : vec_bufs)
+        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    const size_t es = io_size(io);
+    const Span ins[] = {span(xbc, batch * dim * es), span(weight, dim * 16), span(bias, bias ? dim * 4 : 0)};
+    const Span outs[] = {span(x_out, batch * nx * es), span(b_out, batch * nb * es), span(c_out, batch * nb * es),
+                         span(conv_state, batch * dim * 3 * es)};
+    for (size_t i = 0; i < 4; ++i) {
+        for (const Span& s : ins)
+            if (overlap(outs[i], s)) return SSD_ERR_ALIAS;
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
+    }
+    if (batch == 0) return SSD_OK;
+    ssd::ConvArgs ca{};
+    ca.xbc = xbc;
+    ca.weight = weight;
+    ca.bias = bias;
+    ca.x_out = x_out;
+    ca.b_out = b_out;
+    ca.c_out = c_out;
+    ca.state_out = conv_state;
+    ca.L = 1;
+    ca.batch = static_cast<int>(batch);
+    ca.dim = static_cast<int>(dim);
+    ca.nx = static_cast<int>(nx);
+    ca.nb = static_cast<int>(nb);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    if (timed_launch(k, hs, [&] { return ssd::launch_conv1d_update(io, ca, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status ssd_gated_rmsnorm(int64_t rows, int64_t dim, int64_t group, ssd_dtype io, const void* y,
+                             const void* z, const float* weight, float eps, void* out, void* stream) {
+    if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
+    if (rows < 0 || dim < 1 || group < 1 || dim % group != 0) return SSD_ERR_BAD_SHAPE;
+    if (group % 8 != 0 || group > 4096) return SSD_ERR_UNSUPPORTED;
+    if (rows > (int64_t(1) << 31) / (dim / group + 1) || dim > (int64_t(1) << 30)) return SSD_ERR_BAD_SHAPE;
+    if (!(eps >= 0.0f) || isinf(eps)) return SSD_ERR_BAD_ARG;
+    if (!weight) return SSD_ERR_NULL_ARG;
+    if (rows > 0 && (!y || !z || !out)) return SSD_ERR_NULL_ARG;
+    const void* vec_bufs[] = {y, z, weight, out};
+    for (const void* p : vec_bufs)
+        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    const size_t es = io_size(io);
+    const Span os = span(out, rows * dim * es);
+    if (overlap(os, span(y, rows * dim * es)) || overlap(os, span(z, rows * dim * es)) ||
+        overlap(os, span(weight, dim * 4)))
+        return SSD_ERR_ALIAS;
+    if (rows == 0) return SSD_OK;
+    ssd::NormArgs na{};
+    na.y = y;
+    na.z = z;
+    na.weight = weight;
+    na.out = out;
+    na.rows = rows;
+    na.dim = static_cast<int>(dim);
+    na.group = static_cast<int>(group);
+    na.eps = eps;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    if (timed_launch(k, hs, [&] { return ssd::launch_gated_rmsnorm(io, na, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
                             int64_t ngroups, ssd_dtype io, float* state, const void* x,
                             const float* dt, const float* dt_bias, int dt_softplus,

@@ -100,6 +100,30 @@ struct BwdArgs {
     int batch, H, G, nc;
 };
 
+// Mixer steps beside the scan (ssd_mixer.hip).
+struct ConvArgs {
+    const void* xbc;         // (b, L, dim) io; decode: (b, dim)
+    const float* weight;     // (dim, 4)
+    const float* bias;       // (dim) or null
+    const void* state_in;    // (b, dim, 3) io or null (prefill)
+    const int32_t* seq_idx;  // (b, L) or null (prefill)
+    void* x_out;             // (b, L, nx): channels [0, nx)
+    void* b_out;             // (b, L, nb): channels [nx, nx + nb)
+    void* c_out;             // (b, L, nb): channels [nx + nb, dim)
+    void* state_out;         // (b, dim, 3) io or null; decode: the state, updated in place
+    int64_t L;
+    int batch, dim, nx, nb;
+};
+struct NormArgs {
+    const void* y;           // (rows, dim) io
+    const void* z;           // (rows, dim) io
+    const float* weight;     // (dim)
+    void* out;               // (rows, dim) io
+    int64_t rows;
+    int dim, group;
+    float eps;
+};
+
 typedef hipError_t (*ScanLaunchFn)(const ScanArgs&, int64_t nblocks, hipStream_t);
 
 struct ScanVariant {
@@ -174,6 +198,11 @@ hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st);
+
+// Mixer steps (io 0 = fp32, 1 = bf16).
+hipError_t launch_conv1d_fwd(int io, const ConvArgs& a, hipStream_t st);
+hipError_t launch_conv1d_update(int io, const ConvArgs& a, hipStream_t st);
+hipError_t launch_gated_rmsnorm(int io, const NormArgs& a, hipStream_t st);
 
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);
