@@ -21,7 +21,9 @@ The line also carries a "backward" object for the gradients of the same scan
 (ssd_chunk_scan_bwd on the same inputs, seeded dy and final-state gradient):
 its tokens/s, per-kernel times, a roofline entry for its per-chunk gradient
 kernel against the compulsory bytes of the whole backward pass, and the fp64
-oracle's gradients timed on the heads of one group.
+oracle's gradients timed on the heads of one group; and a "mixer" object for
+the steps beside the scan (causal conv1d into the scan's x/B/C, gated group
+RMSNorm of its output) at the same shape.
 """
 import argparse
 import ctypes
@@ -225,6 +227,86 @@ def backward_measure(ssd, lib, hip, torch, base, A, D, bias, w, steps, cpu_secon
     return out
 
 
+def mixer_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
+    """The mixer steps beside the scan at the workload's shape: the causal conv1d
+    over the xBC channels (written as the scan's x, B, C) and the gated group
+    RMSNorm of the scan's output (group 512).  Dispatch-timed durations, HBM
+    rooflines against each kernel's compulsory bytes, and the oracle timed on
+    a sample of tokens."""
+    import numpy as np
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    dev = torch.device("cuda:0")
+    nx, nb = H * P, G * N
+    dim = nx + 2 * nb
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    bf = torch.bfloat16
+    xbc = torch.randn((b, L, dim), generator=gen).to(bf).to(dev)
+    cw = (0.5 * torch.randn((dim, 4), generator=gen)).to(dev)
+    cb = torch.randn((dim,), generator=gen).to(dev)
+    cst = torch.randn((b, dim, 3), generator=gen).to(bf).to(dev)
+    y = torch.randn((b, L, nx), generator=gen).to(bf).to(dev)
+    z = torch.randn((b, L, nx), generator=gen).to(bf).to(dev)
+    nw = torch.randn((nx,), generator=gen).to(dev)
+    xo = torch.empty((b, L, H, P), dtype=bf, device=dev)
+    bo = torch.empty((b, L, G, N), dtype=bf, device=dev)
+    co = torch.empty((b, L, G, N), dtype=bf, device=dev)
+    so = torch.empty((b, dim, 3), dtype=bf, device=dev)
+    out = torch.empty_like(y)
+    calls = {
+        "conv1d": lambda: lib.ssd_conv1d_fwd(b, L, dim, nx, nb, 1, xbc.data_ptr(), cw.data_ptr(), 4,
+                                             cb.data_ptr(), cst.data_ptr(), None, xo.data_ptr(),
+                                             bo.data_ptr(), co.data_ptr(), so.data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream),
+        "gated_norm": lambda: lib.ssd_gated_rmsnorm(b * L, nx, 512, 1, y.data_ptr(), z.data_ptr(),
+                                                    nw.data_ptr(), 1e-6, out.data_ptr(),
+                                                    torch.cuda.current_stream().cuda_stream),
+    }
+    nbytes = {"conv1d": 2 * b * L * dim * 2 + 2 * b * dim * 3 * 2 + dim * 5 * 4,
+              "gated_norm": 3 * b * L * nx * 2 + nx * 4}
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(5):
+            if fn() != 0:
+                raise RuntimeError("%s failed" % name)
+        torch.cuda.synchronize()
+        evs = hip.events(2 * steps)
+        launched = ctypes.c_int(0)
+        for i in range(steps):
+            lib.ssd_set_timing_events(ev_slice_of(evs, 2 * i, 2, ctypes.sizeof(ctypes.c_void_p)), 2,
+                                      ctypes.byref(launched))
+            fn()
+        lib.ssd_set_timing_events(None, 0, None)
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]))
+        hip.destroy(evs)
+        ach = nbytes[name] / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "tokens_per_s": round(b * L / (us * 1e-6), 1),
+                     "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                  "traffic": None}}
+    res["shape"] = {"tokens": b * L, "xbc_channels": dim, "norm_channels": nx, "norm_group": 512,
+                    "dtype": "bf16"}
+    res["cpu_baseline"] = None
+    if cpu_seconds > 0:
+        from oracle import mixer
+        T = min(L, 1024)
+        xs = xbc[:, :T].float().cpu().numpy(); ys = y[:, :T].float().cpu().numpy()
+        zs = z[:, :T].float().cpu().numpy()
+        cwn, cbn, csn, nwn = cw.cpu().numpy(), cb.cpu().numpy(), cst.float().cpu().numpy(), nw.cpu().numpy()
+        t0 = time.perf_counter()
+        runs = 0
+        while runs == 0 or time.perf_counter() - t0 < cpu_seconds:
+            mixer.conv1d(xs, cwn, cbn, csn)
+            mixer.gated_rmsnorm(ys, zs, nwn, 512)
+            runs += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(b * T * runs / el, 1), "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "conv1d + gated norm of the first %d tokens, %d run(s) in %.1f s "
+                                         "(numpy fp64, one thread)" % (T, runs, el)}
+    return res
+
+
 def ev_slice_of(evs, first, count, vp):
     return (ctypes.c_void_p * count).from_buffer(evs, first * vp)
 
@@ -409,6 +491,8 @@ def main():
     log("bench: backward pass")
     result["backward"] = backward_measure(ssd, lib, hip, torch, sets[0], A, D, bias, w,
                                           args.backward_steps, min(args.cpu_seconds, 5.0), p)
+    log("bench: mixer steps")
+    result["mixer"] = mixer_measure(ssd, lib, hip, torch, w, 50, min(args.cpu_seconds, 3.0))
     if args.cpu_seconds > 0:
         log("bench: CPU oracle baseline (budget %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline({k: (v[:, :L] if k in ("x", "dt_raw", "B", "C", "seq_idx") and v is not None else v)

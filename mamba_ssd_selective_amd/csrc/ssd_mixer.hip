@@ -22,7 +22,8 @@ namespace ssd {
 namespace {
 
 constexpr int kConvW = 4;        // taps (the pages' mamba_d_conv)
-constexpr int kConvTile = 32;    // tokens per thread of the prefill kernel
+constexpr int kConvTile = 16;    // tokens per thread of the prefill kernel
+constexpr int kConvStep = 4;     // tokens whose loads are in flight together
 constexpr int kMixThreads = 256;
 
 template <typename T> struct V8;
@@ -59,7 +60,9 @@ template <> struct V8<float> {
     }
 };
 
-__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
+// v * sigmoid(v) with the reciprocal instruction (these kernels are bound by
+// their VALU work, and an IEEE divide costs several times more)
+__device__ __forceinline__ float silu_f32(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // Destination of channels c0 .. c0+7 of token row `row` (row = b * L + t).
 template <typename T>
@@ -69,8 +72,9 @@ __device__ __forceinline__ T* conv_dst(const ConvArgs& a, int64_t row, int c0) {
     return static_cast<T*>(a.c_out) + row * a.nb + (c0 - a.nx - a.nb);
 }
 
-// One thread: 8 channels, kConvTile consecutive tokens of one row.
-template <typename T>
+// One thread: 8 channels, kConvTile consecutive tokens of one row.  kSeq: the
+// row packs sequences (the masks are compiled only into that form).
+template <typename T, bool kSeq>
 __global__ __launch_bounds__(kMixThreads) void conv1d_fwd_kernel(ConvArgs a) {
     const int cg = static_cast<int>(blockIdx.x) * kMixThreads + static_cast<int>(threadIdx.x);
     const int c0 = 8 * cg;
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(kMixThreads) void conv1d_fwd_kernel(ConvArgs a) {
     const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kConvTile;
     const T* src = static_cast<const T*>(a.xbc);
     const int64_t rowb = b * L;
-    const int32_t* seq = a.seq_idx ? a.seq_idx + rowb : nullptr;
+    const int32_t* seq = kSeq ? a.seq_idx + rowb : nullptr;
     float w[8][kConvW], bias[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -162,33 +166,49 @@ __global__ __launch_bounds__(kMixThreads) void conv1d_fwd_kernel(ConvArgs a) {
             }
     }
     const int64_t tend = t0 + kConvTile < L ? t0 + kConvTile : L;
-    for (int64_t t = t0; t < tend; ++t) {
-        V8<T> cur;
-        cur.load(src + (rowb + t) * a.dim + c0);
-        const int st = seq ? seq[t] : 0;
-        float o[8];
+    T* const dst0 = conv_dst<T>(a, rowb, c0);
+    const int64_t dstride = c0 < a.nx ? a.nx : a.nb;  // elements between token rows of the output
+    // kConvStep tokens at a time: their loads are issued together
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // the same fused order as the decode update: bias, current token,
-            // then the three earlier inputs oldest first (another sequence's: 0)
-            float acc = fmaf(w[e][3], cur.get(e), bias[e]);
+    for (int64_t tb = t0; tb < t0 + kConvTile; tb += kConvStep) {
+        V8<T> cur[kConvStep];
+        int sq[kConvStep];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) acc = fmaf(w[e][k], wseq[k] == st ? win[k][e] : 0.0f, acc);
-            o[e] = silu_f32(acc);
+        for (int u = 0; u < kConvStep; ++u) {
+            const int64_t t = tb + u < tend ? tb + u : tend - 1;
+            cur[u].load(src + (rowb + t) * a.dim + c0);
+            sq[u] = seq ? seq[t] : 0;
         }
-        V8<T> ov;
-        ov.set(o);
-        ov.store(conv_dst<T>(a, rowb + t, c0));
-        // slide the window
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            win[0][e] = win[1][e];
-            win[1][e] = win[2][e];
-            win[2][e] = cur.get(e);
+        for (int u = 0; u < kConvStep; ++u) {
+            if (tb + u < tend) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // the same fused order as the decode update: bias, current
+                    // token, then the three earlier inputs oldest first
+                    // (another sequence's count as 0)
+                    float acc = fmaf(w[e][3], cur[u].get(e), bias[e]);
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        acc = fmaf(w[e][k], (!kSeq || wseq[k] == sq[u]) ? win[k][e] : 0.0f, acc);
+                    o[e] = silu_f32(acc);
+                }
+                V8<T> ov;
+                ov.set(o);
+                ov.store(dst0 + (tb + u) * dstride);
+            }
+            // slide the window
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                win[0][e] = win[1][e];
+                win[1][e] = win[2][e];
+                win[2][e] = cur[u].get(e);
+            }
+            wseq[0] = wseq[1];
+            wseq[1] = wseq[2];
+            wseq[2] = sq[u];
         }
-        wseq[0] = wseq[1];
-        wseq[1] = wseq[2];
-        wseq[2] = st;
     }
 }
 
@@ -285,8 +305,12 @@ __global__ __launch_bounds__(kMixThreads) void gated_rmsnorm_kernel(NormArgs a) 
 hipError_t launch_conv1d_fwd(int io, const ConvArgs& a, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>((a.dim / 8 + kMixThreads - 1) / kMixThreads),
                     static_cast<unsigned>((a.L + kConvTile - 1) / kConvTile), static_cast<unsigned>(a.batch));
-    if (io == 1) return dispatch(conv1d_fwd_kernel<uint16_t>, grid, dim3(kMixThreads), st, a);
-    return dispatch(conv1d_fwd_kernel<float>, grid, dim3(kMixThreads), st, a);
+    if (io == 1) {
+        if (a.seq_idx) return dispatch(conv1d_fwd_kernel<uint16_t, true>, grid, dim3(kMixThreads), st, a);
+        return dispatch(conv1d_fwd_kernel<uint16_t, false>, grid, dim3(kMixThreads), st, a);
+    }
+    if (a.seq_idx) return dispatch(conv1d_fwd_kernel<float, true>, grid, dim3(kMixThreads), st, a);
+    return dispatch(conv1d_fwd_kernel<float, false>, grid, dim3(kMixThreads), st, a);
 }
 
 hipError_t launch_conv1d_update(int io, const ConvArgs& a, hipStream_t st) {
