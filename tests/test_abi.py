@@ -157,3 +157,100 @@ def test_state_update_rejects_bad_arguments(lib):
     s = buf()
     assert _step_call(lib, state=s, y=s + 64) == ALIAS
     assert _step_call(lib, b=0) == OK
+
+
+# ---------------------------------------------------------- gradients, mixer
+
+
+def test_bwd_workspace_bytes(lib):
+    # metadata (3 x Q fp32 per row, head, chunk), the state before and the
+    # gradient after every chunk (fp32 P x N each), per-chunk sums (3 fp32)
+    b, L, H, G = 1, 8192, 64, 8
+    nc = 64
+    meta = b * H * nc * 128 * 3 * 4
+    states = b * H * nc * 64 * 128 * 4
+    parts = 256 * math.ceil(b * H * nc * 3 * 4 / 256)
+    assert ssd.bwd_workspace_bytes(b, L, H, 64, 128, G, 128) == meta + 2 * states + parts
+    assert ssd.bwd_workspace_bytes(1, 0, H, 64, 128, G, 128) == 0
+    assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 64, io=ssd.BF16) == 0   # Q 64: not built
+    assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 128, io=ssd.F32) == 0   # fp32: not built
+
+
+def _bwd_call(lib, dims=(1, 256, 4, 64, 128, 1, 128), io=ssd.BF16, **over):
+    buf = _Buf()
+    args = dict(x=buf(), dt=buf(), dt_bias=None, softplus=1, lo=0.0, hi=math.inf, A=buf(), B=buf(),
+                C=buf(), D=None, init=None, seq=None, dy=buf(), dfin=None, dx=buf(), ddt=buf(),
+                dA=buf(), dB=buf(), dC=buf(), dD=None, dbias=None, dinit=None, ws=buf(1 << 28),
+                ws_bytes=1 << 28)
+    args.update(over)
+    d = ssd._Dims(*dims)
+    return lib.ssd_chunk_scan_bwd(
+        ctypes.byref(d), io, args["x"], args["dt"], args["dt_bias"], args["softplus"], args["lo"],
+        args["hi"], args["A"], args["B"], args["C"], args["D"], args["init"], args["seq"], args["dy"],
+        args["dfin"], args["dx"], args["ddt"], args["dA"], args["dB"], args["dC"], args["dD"],
+        args["dbias"], args["dinit"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    assert _bwd_call(lib, io=ssd.F32) == UNSUPPORTED
+    assert _bwd_call(lib, dims=(1, 256, 4, 64, 64, 1, 128)) == UNSUPPORTED
+    assert _bwd_call(lib, dims=(1, 256, 6, 64, 128, 4, 128)) == BAD_SHAPE   # H % G
+    assert _bwd_call(lib, dy=None) == NULL_ARG
+    assert _bwd_call(lib, dA=None) == NULL_ARG
+    assert _bwd_call(lib, ws=None) == WORKSPACE
+    assert _bwd_call(lib, ws_bytes=16) == WORKSPACE
+    assert _bwd_call(lib, lo=1.0, hi=0.5) == BAD_ARG
+    assert _bwd_call(lib, dx=0x70000008) == BAD_ARG   # not 16-byte aligned
+    buf = _Buf()
+    x = buf()
+    assert _bwd_call(lib, x=x, dx=x + 4096) == ALIAS   # an output over an input
+    o = buf()
+    assert _bwd_call(lib, dB=o, dC=o + 64) == ALIAS    # two outputs overlap
+    w = buf(1 << 28)
+    assert _bwd_call(lib, ws=w, ddt=w + 4096) == ALIAS  # an output over the workspace
+
+
+def _conv_call(lib, b=1, L=64, nx=64, nb=32, io=ssd.BF16, width=4, dim=None, **over):
+    """Every call here fails validation (or has nothing to do) before any launch."""
+    buf = _Buf()
+    args = dict(xbc=buf(), w=buf(), bias=None, sin=None, seq=None, xo=buf(), bo=buf(), co=buf(),
+                sout=None)
+    args.update(over)
+    return lib.ssd_conv1d_fwd(b, L, nx + 2 * nb if dim is None else dim, nx, nb, io, args["xbc"],
+                              args["w"], width, args["bias"], args["sin"], args["seq"], args["xo"],
+                              args["bo"], args["co"], args["sout"], None)
+
+
+def test_conv_rejects_bad_arguments(lib):
+    assert _conv_call(lib, width=3) == UNSUPPORTED
+    assert _conv_call(lib, nx=60, nb=34) == UNSUPPORTED          # not multiples of 8
+    assert _conv_call(lib, io=7) == BAD_DTYPE
+    assert _conv_call(lib, dim=100) == BAD_SHAPE                  # dim != nx + 2 nb
+    assert _conv_call(lib, w=None) == NULL_ARG
+    assert _conv_call(lib, xo=None) == NULL_ARG
+    assert _conv_call(lib, xbc=0x70000002) == BAD_ARG
+    buf = _Buf()
+    x = buf()
+    assert _conv_call(lib, xbc=x, co=x + 512) == ALIAS
+    s = buf()
+    assert _conv_call(lib, sin=s, sout=s + 2) == ALIAS            # partial overlap (in place is allowed)
+    assert _conv_call(lib, b=0) == OK                             # nothing to launch
+
+
+def test_gated_norm_rejects_bad_arguments(lib):
+    buf = _Buf()
+
+    def call(rows=8, dim=1024, group=512, io=ssd.BF16, eps=1e-6, **over):
+        a = dict(y=buf(), z=buf(), w=buf(), out=buf())
+        a.update(over)
+        return lib.ssd_gated_rmsnorm(rows, dim, group, io, a["y"], a["z"], a["w"], eps, a["out"], None)
+
+    assert call(dim=1200, group=12) == UNSUPPORTED      # divides dim, but not a multiple of 8
+    assert call(group=8192, dim=8192) == UNSUPPORTED
+    assert call(dim=1000, group=512) == BAD_SHAPE
+    assert call(eps=-1.0) == BAD_ARG
+    assert call(eps=float("inf")) == BAD_ARG
+    assert call(w=None) == NULL_ARG
+    y = buf()
+    assert call(y=y, out=y) == ALIAS
+    assert call(rows=0) == OK
