@@ -198,6 +198,22 @@ ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb,
                              const void* xbc, const float* weight, int64_t width, const float* bias,
                              void* conv_state, void* x_out, void* b_out, void* c_out, void* stream);
 
+/* ssd_conv1d_update on a conv-state cache (continuous batching; the
+ * per-sequence conv state of RFC section 1, operator family 2): row r of
+ * the batch reads and updates row state_indices[r] of conv_state_cache
+ * (cache_rows, dim, 3) io dtype in place.  state_indices (batch) int32 on the
+ * device.  An index outside [0, cache_rows) marks a padding row: its cache
+ * row is not touched and its outputs are not written.  The indices of the
+ * other rows must be distinct (two rows naming one cache row race); the
+ * library does not read device memory to check.  Otherwise as
+ * ssd_conv1d_update; cache_rows = batch with indices 0..batch-1 is the same
+ * call. */
+ssd_status ssd_conv1d_update_cached(int64_t batch, int64_t cache_rows, int64_t dim, int64_t nx,
+                                    int64_t nb, ssd_dtype io, const void* xbc, const float* weight,
+                                    int64_t width, const float* bias, void* conv_state_cache,
+                                    const int32_t* state_indices, void* x_out, void* b_out,
+                                    void* c_out, void* stream);
+
 /* Gated group RMSNorm of the scan's output: per row and group of `group`
  * consecutive channels, v = y * silu(z) and out = v / sqrt(mean(v^2) + eps) *
  * weight.  y, z, out (rows, dim) io dtype; weight (dim) fp32; eps >= 0 (the
@@ -224,6 +240,25 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
                             const float* dt, const float* dt_bias, int dt_softplus,
                             float dt_min, float dt_max, const float* A, const void* B,
                             const void* C, const float* D, void* y, void* stream);
+
+/* ssd_state_update on a state cache (continuous batching; the per-sequence
+ * fp32 SSM state of RFC section 1, operator family 2, held in slots of one
+ * buffer that outlives the batch): row
+ * r of the batch reads and updates slot state_indices[r] of state_cache
+ * (cache_rows, H, P, N) fp32 in place; x, dt, B, C, y keep the batch's rows.
+ * state_indices (batch) int32 on the device.  An index outside
+ * [0, cache_rows) marks a padding row: its slot is not touched and its y
+ * rows are not written.  The indices of the other rows must be distinct (two
+ * rows naming one slot race); the library does not read device memory to
+ * check.  Otherwise as ssd_state_update; cache_rows = batch with indices
+ * 0..batch-1 is the same call. */
+ssd_status ssd_state_update_cached(int64_t batch, int64_t cache_rows, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype io,
+                                   float* state_cache, const int32_t* state_indices,
+                                   const void* x, const float* dt, const float* dt_bias,
+                                   int dt_softplus, float dt_min, float dt_max, const float* A,
+                                   const void* B, const void* C, const float* D, void* y,
+                                   void* stream);
 
 /* Per-kernel timing hooks (diagnostics).  After a call with events != NULL,
  * every ssd_chunk_scan_fwd / ssd_state_update call made on the same host

@@ -83,11 +83,17 @@ def library():
         lib.ssd_conv1d_fwd.restype = i
         lib.ssd_conv1d_update.argtypes = [i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         lib.ssd_conv1d_update.restype = i
+        lib.ssd_conv1d_update_cached.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp,
+                                                 vp, vp, vp, vp]
+        lib.ssd_conv1d_update_cached.restype = i
         lib.ssd_gated_rmsnorm.argtypes = [i64, i64, i64, i, vp, vp, vp, f, vp, vp]
         lib.ssd_gated_rmsnorm.restype = i
         lib.ssd_state_update.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, vp, vp, i, f, f,
                                          vp, vp, vp, vp, vp, vp]
         lib.ssd_state_update.restype = i
+        lib.ssd_state_update_cached.argtypes = [i64, i64, i64, i64, i64, i64, i, vp, vp, vp, vp, vp,
+                                                i, f, f, vp, vp, vp, vp, vp, vp]
+        lib.ssd_state_update_cached.restype = i
         lib.ssd_set_timing_events.argtypes = [ctypes.POINTER(vp), i, ctypes.POINTER(i)]
         lib.ssd_set_timing_events.restype = None
         if lib.ssd_abi_version() != 1:
@@ -292,9 +298,14 @@ def conv1d_fwd(xbc, weight, *, nheads: int, headdim: int, ngroups: int, dstate: 
 
 
 def conv1d_update(xbc, conv_state, weight, *, nheads: int, headdim: int, ngroups: int,
-                  dstate: int, bias=None):
+                  dstate: int, bias=None, state_indices=None, out=None):
     """One decode token of the conv: xbc (b, dim); conv_state (b, dim, 3) is
-    updated in place.  Returns x (b, H, P), B, C (b, G, N)."""
+    updated in place.  Returns x (b, H, P), B, C (b, G, N).
+
+    With ``state_indices`` (b,) int32, conv_state is a cache (rows, dim, 3):
+    row r reads and updates cache row state_indices[r]; an index outside the
+    cache marks a padding row (cache untouched, outputs not written).  ``out``
+    optionally gives the (x, B, C) tensors to write."""
     import torch
     lib = library()
     b, dim = xbc.shape
@@ -302,16 +313,31 @@ def conv1d_update(xbc, conv_state, weight, *, nheads: int, headdim: int, ngroups
     dev = xbc.device
     io = _io_code(xbc.dtype)
     _check(xbc, "xbc", (b, dim), xbc.dtype, dev)
-    _check(conv_state, "conv_state", (b, dim, 3), xbc.dtype, dev)
+    rows = conv_state.shape[0] if state_indices is not None else b
+    _check(conv_state, "conv_state", (rows, dim, 3), xbc.dtype, dev)
+    _check(state_indices, "state_indices", (b,), torch.int32, dev)
     _check(weight, "weight", (dim, 4), torch.float32, dev)
     _check(bias, "bias", (dim,), torch.float32, dev)
-    x = torch.empty((b, nheads, headdim), dtype=xbc.dtype, device=dev)
-    Bm = torch.empty((b, ngroups, dstate), dtype=xbc.dtype, device=dev)
-    Cm = torch.empty((b, ngroups, dstate), dtype=xbc.dtype, device=dev)
-    rc = lib.ssd_conv1d_update(b, dim, nx, nb, io, _ptr(xbc), _ptr(weight), 4, _ptr(bias),
-                               _ptr(conv_state), _ptr(x), _ptr(Bm), _ptr(Cm), _stream_handle(dev))
+    if out is None:
+        out = (torch.empty((b, nheads, headdim), dtype=xbc.dtype, device=dev),
+               torch.empty((b, ngroups, dstate), dtype=xbc.dtype, device=dev),
+               torch.empty((b, ngroups, dstate), dtype=xbc.dtype, device=dev))
+    x, Bm, Cm = out
+    _check(x, "x", (b, nheads, headdim), xbc.dtype, dev)
+    _check(Bm, "B", (b, ngroups, dstate), xbc.dtype, dev)
+    _check(Cm, "C", (b, ngroups, dstate), xbc.dtype, dev)
+    if state_indices is None:
+        rc = lib.ssd_conv1d_update(b, dim, nx, nb, io, _ptr(xbc), _ptr(weight), 4, _ptr(bias),
+                                   _ptr(conv_state), _ptr(x), _ptr(Bm), _ptr(Cm),
+                                   _stream_handle(dev))
+        name = "ssd_conv1d_update"
+    else:
+        rc = lib.ssd_conv1d_update_cached(b, rows, dim, nx, nb, io, _ptr(xbc), _ptr(weight), 4,
+                                          _ptr(bias), _ptr(conv_state), _ptr(state_indices),
+                                          _ptr(x), _ptr(Bm), _ptr(Cm), _stream_handle(dev))
+        name = "ssd_conv1d_update_cached"
     if rc != 0:
-        raise SSDError(rc, "ssd_conv1d_update")
+        raise SSDError(rc, name)
     return x, Bm, Cm
 
 
@@ -337,9 +363,13 @@ def gated_rmsnorm(y, z, weight, *, group: int, eps: float = 1e-6, out=None):
 
 
 def state_update(state, x, dt, A, B, C, *, D=None, dt_bias=None, dt_softplus: bool = True,
-                 dt_limit: Tuple[float, float] = (0.0, math.inf), out=None):
+                 dt_limit: Tuple[float, float] = (0.0, math.inf), out=None, state_indices=None):
     """One decode token: updates ``state`` (b, H, P, N) fp32 in place and
-    returns y (b, H, P) in x's dtype.  x (b, H, P), dt (b, H), B/C (b, G, N)."""
+    returns y (b, H, P) in x's dtype.  x (b, H, P), dt (b, H), B/C (b, G, N).
+
+    With ``state_indices`` (b,) int32, state is a cache (slots, H, P, N): row
+    r reads and updates slot state_indices[r]; an index outside the cache
+    marks a padding row (slot untouched, its y rows not written)."""
     import torch
     lib = library()
     b, H, P = x.shape
@@ -347,7 +377,9 @@ def state_update(state, x, dt, A, B, C, *, D=None, dt_bias=None, dt_softplus: bo
     dev = x.device
     io = _io_code(x.dtype)
     f32 = torch.float32
-    _check(state, "state", (b, H, P, N), f32, dev)
+    rows = state.shape[0] if state_indices is not None else b
+    _check(state, "state", (rows, H, P, N), f32, dev)
+    _check(state_indices, "state_indices", (b,), torch.int32, dev)
     _check(B, "B", (b, G, N), x.dtype, dev)
     _check(C, "C", (b, G, N), x.dtype, dev)
     _check(dt, "dt", (b, H), f32, dev)
@@ -356,10 +388,19 @@ def state_update(state, x, dt, A, B, C, *, D=None, dt_bias=None, dt_softplus: bo
     _check(dt_bias, "dt_bias", (H,), f32, dev)
     y = out if out is not None else torch.empty((b, H, P), dtype=x.dtype, device=dev)
     _check(y, "out", (b, H, P), x.dtype, dev)
-    st = lib.ssd_state_update(b, H, P, N, G, io, _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias),
-                              int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
-                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
-                              _stream_handle(dev))
+    if state_indices is None:
+        st = lib.ssd_state_update(b, H, P, N, G, io, _ptr(state), _ptr(x), _ptr(dt),
+                                  _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]),
+                                  float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+                                  _stream_handle(dev))
+        name = "ssd_state_update"
+    else:
+        st = lib.ssd_state_update_cached(b, rows, H, P, N, G, io, _ptr(state),
+                                         _ptr(state_indices), _ptr(x), _ptr(dt), _ptr(dt_bias),
+                                         int(bool(dt_softplus)), float(dt_limit[0]),
+                                         float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                         _ptr(y), _stream_handle(dev))
+        name = "ssd_state_update_cached"
     if st != 0:
-        raise SSDError(st, "ssd_state_update")
+        raise SSDError(st, name)
     return y

@@ -513,13 +513,24 @@ ssd_status ssd_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t nx
     return SSD_OK;
 }
 
-ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb, ssd_dtype io,
-                             const void* xbc, const float* weight, int64_t width, const float* bias,
-                             void* conv_state, void* x_out, void* b_out, void* c_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode token of the conv with the conv states taken from a cache of
+// cache_rows rows (state_idx[r] picks row r's; null: row r, cache_rows =
+// batch).
+ssd_status conv1d_update_impl(int64_t batch, int64_t cache_rows, int64_t dim, int64_t nx,
+                              int64_t nb, ssd_dtype io, const void* xbc, const float* weight,
+                              int64_t width, const float* bias, void* conv_state,
+                              const int32_t* state_idx, void* x_out, void* b_out, void* c_out,
+                              void* stream) {
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
     if (batch < 0 || nx < 0 || nb < 0 || dim != nx + 2 * nb || dim < 8) return SSD_ERR_BAD_SHAPE;
     if (width != 4 || dim % 8 != 0 || nx % 8 != 0 || nb % 8 != 0) return SSD_ERR_UNSUPPORTED;
     if (batch > 65535 || dim > (int64_t(1) << 30)) return SSD_ERR_BAD_SHAPE;
+    if (cache_rows < 0 || cache_rows > (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
+    if (cache_rows > 0 && dim > (int64_t(1) << 52) / cache_rows) return SSD_ERR_BAD_SHAPE;
     if (!weight) return SSD_ERR_NULL_ARG;
     if (batch > 0 && (!xbc || !conv_state || !x_out || (nb > 0 && (!b_out || !c_out))))
         return SSD_ERR_NULL_ARG;
@@ -527,9 +538,10 @@ ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb,
     for (const void* p : vec_bufs)
         if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
     const size_t es = io_size(io);
-    const Span ins[] = {span(xbc, batch * dim * es), span(weight, dim * 16), span(bias, bias ? dim * 4 : 0)};
+    const Span ins[] = {span(xbc, batch * dim * es), span(weight, dim * 16), span(bias, bias ? dim * 4 : 0),
+                        span(state_idx, state_idx ? batch * 4 : 0)};
     const Span outs[] = {span(x_out, batch * nx * es), span(b_out, batch * nb * es), span(c_out, batch * nb * es),
-                         span(conv_state, batch * dim * 3 * es)};
+                         span(conv_state, cache_rows * dim * 3 * es)};
     for (size_t i = 0; i < 4; ++i) {
         for (const Span& s : ins)
             if (overlap(outs[i], s)) return SSD_ERR_ALIAS;
@@ -545,6 +557,8 @@ ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb,
     ca.b_out = b_out;
     ca.c_out = c_out;
     ca.state_out = conv_state;
+    ca.state_idx = state_idx;
+    ca.cache_rows = cache_rows;
     ca.L = 1;
     ca.batch = static_cast<int>(batch);
     ca.dim = static_cast<int>(dim);
@@ -556,6 +570,27 @@ ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb,
     if (timed_launch(k, hs, [&] { return ssd::launch_conv1d_update(io, ca, hs); }) != hipSuccess)
         return SSD_ERR_HIP;
     return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_conv1d_update(int64_t batch, int64_t dim, int64_t nx, int64_t nb, ssd_dtype io,
+                             const void* xbc, const float* weight, int64_t width, const float* bias,
+                             void* conv_state, void* x_out, void* b_out, void* c_out, void* stream) {
+    return conv1d_update_impl(batch, batch, dim, nx, nb, io, xbc, weight, width, bias, conv_state,
+                              nullptr, x_out, b_out, c_out, stream);
+}
+
+ssd_status ssd_conv1d_update_cached(int64_t batch, int64_t cache_rows, int64_t dim, int64_t nx,
+                                    int64_t nb, ssd_dtype io, const void* xbc, const float* weight,
+                                    int64_t width, const float* bias, void* conv_state_cache,
+                                    const int32_t* state_indices, void* x_out, void* b_out,
+                                    void* c_out, void* stream) {
+    if (batch > 0 && !state_indices) return SSD_ERR_NULL_ARG;
+    return conv1d_update_impl(batch, cache_rows, dim, nx, nb, io, xbc, weight, width, bias,
+                              conv_state_cache, state_indices, x_out, b_out, c_out, stream);
 }
 
 ssd_status ssd_gated_rmsnorm(int64_t rows, int64_t dim, int64_t group, ssd_dtype io, const void* y,
@@ -593,18 +628,31 @@ ssd_status ssd_gated_rmsnorm(int64_t rows, int64_t dim, int64_t group, ssd_dtype
     return SSD_OK;
 }
 
-ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
-                            int64_t ngroups, ssd_dtype io, float* state, const void* x,
-                            const float* dt, const float* dt_bias, int dt_softplus,
-                            float dt_min, float dt_max, const float* A, const void* B,
-                            const void* C, const float* D, void* y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step with the state rows taken from a cache of cache_rows rows
+// (state_idx[r] picks row r's; null: row r uses state row r, cache_rows =
+// batch).
+ssd_status state_update_impl(int64_t batch, int64_t cache_rows, int64_t nheads, int64_t headdim,
+                             int64_t dstate, int64_t ngroups, ssd_dtype io, float* state,
+                             const int32_t* state_idx, const void* x, const float* dt,
+                             const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                             const float* A, const void* B, const void* C, const float* D, void* y,
+                             void* stream) {
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
-    if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+    if (batch < 0 || cache_rows < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
         return SSD_ERR_BAD_SHAPE;
     if (nheads % ngroups != 0) return SSD_ERR_BAD_SHAPE;
     // grid: one block per (row, head) (and, for few of them, per 8 or more of
-    // its state rows), below 2^31
-    if (headdim > (int64_t(1) << 20) || batch * nheads * ((headdim + 7) / 8) >= (int64_t(1) << 31))
+    // its state rows), below 2^31; the cache's byte offsets below 2^62
+    const int64_t k31 = int64_t(1) << 31;
+    if (headdim > (int64_t(1) << 20) || nheads >= k31 || batch >= k31 || cache_rows >= k31)
+        return SSD_ERR_BAD_SHAPE;
+    if (batch * nheads >= k31 || batch * nheads * ((headdim + 7) / 8) >= k31)
+        return SSD_ERR_BAD_SHAPE;
+    if (cache_rows > 0 && nheads * headdim > (int64_t(1) << 52) / cache_rows)
         return SSD_ERR_BAD_SHAPE;
     if (dstate != 16 && dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
         return SSD_ERR_UNSUPPORTED;
@@ -615,17 +663,20 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
     if (!aligned16(state)) return SSD_ERR_BAD_ARG;
     const size_t es = io_size(io);
     const int64_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups;
-    const Span ss = span(state, b * H * P * N * 4);
+    const Span ss = span(state, cache_rows * H * P * N * 4);
     const Span ys = span(y, b * H * P * es);
     const Span ins[] = {span(x, b * H * P * es), span(dt, b * H * 4), span(B, b * G * N * es),
                         span(C, b * G * N * es), span(A, H * 4),
-                        span(dt_bias, dt_bias ? H * 4 : 0), span(D, D ? H * 4 : 0)};
-    for (const Span& s : ins)
-        if (overlap(ss, s) || overlap(ys, s)) return SSD_ERR_ALIAS;
+                        span(dt_bias, dt_bias ? H * 4 : 0), span(D, D ? H * 4 : 0),
+                        span(state_idx, state_idx ? b * 4 : 0)};
+    for (const Span& sp : ins)
+        if (overlap(ss, sp) || overlap(ys, sp)) return SSD_ERR_ALIAS;
     if (overlap(ss, ys)) return SSD_ERR_ALIAS;
 
     ssd::StepArgs a;
     a.state = state;
+    a.state_idx = state_idx;
+    a.cache_rows = cache_rows;
     a.x = x;
     a.dt = dt;
     a.dt_bias = dt_bias;
@@ -646,6 +697,32 @@ ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int6
         hipSuccess)
         return SSD_ERR_HIP;
     return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_state_update(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                            int64_t ngroups, ssd_dtype io, float* state, const void* x,
+                            const float* dt, const float* dt_bias, int dt_softplus,
+                            float dt_min, float dt_max, const float* A, const void* B,
+                            const void* C, const float* D, void* y, void* stream) {
+    return state_update_impl(batch, batch, nheads, headdim, dstate, ngroups, io, state, nullptr, x,
+                             dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D, y, stream);
+}
+
+ssd_status ssd_state_update_cached(int64_t batch, int64_t cache_rows, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype io,
+                                   float* state_cache, const int32_t* state_indices,
+                                   const void* x, const float* dt, const float* dt_bias,
+                                   int dt_softplus, float dt_min, float dt_max, const float* A,
+                                   const void* B, const void* C, const float* D, void* y,
+                                   void* stream) {
+    if (batch > 0 && !state_indices) return SSD_ERR_NULL_ARG;
+    return state_update_impl(batch, cache_rows, nheads, headdim, dstate, ngroups, io, state_cache,
+                             state_indices, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C,
+                             D, y, stream);
 }
 
 }  // extern "C"

@@ -935,6 +935,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
     const int64_t b = bh / a.H;
     const int h = static_cast<int>(bh % a.H);
     const int g = group_of_head(h, a.H / a.G);
+    // the state row of batch row b in the cache (a padding row touches nothing)
+    int64_t sb = b;
+    if (a.state_idx) {
+        sb = a.state_idx[b];
+        if (sb < 0 || sb >= a.cache_rows) return;
+    }
+    float* __restrict__ state = a.state + (sb * a.H + h) * static_cast<int64_t>(a.P) * N;
     const T* __restrict__ x = static_cast<const T*>(a.x);
     const T* __restrict__ Bp = static_cast<const T*>(a.B);
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
@@ -959,7 +966,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
             st[u] = make_float4(0.f, 0.f, 0.f, 0.f);
             xv[u] = 0.0f;
             if (p < p_end) {
-                st[u] = *reinterpret_cast<const float4*>(a.state + (bh * a.P + p) * N + 4 * cc);
+                st[u] = *reinterpret_cast<const float4*>(state + static_cast<int64_t>(p) * N + 4 * cc);
                 xv[u] = Io<T>::to_f32(x[bh * a.P + p]);
             }
         }
@@ -974,7 +981,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
                 s.y = fmaf(dA, s.y, uu * bv[1]);
                 s.z = fmaf(dA, s.z, uu * bv[2]);
                 s.w = fmaf(dA, s.w, uu * bv[3]);
-                *reinterpret_cast<float4*>(a.state + (bh * a.P + p) * N + 4 * cc) = s;
+                *reinterpret_cast<float4*>(state + static_cast<int64_t>(p) * N + 4 * cc) = s;
                 part = s.x * cv[0] + s.y * cv[1] + s.z * cv[2] + s.w * cv[3];
             }
 #pragma unroll

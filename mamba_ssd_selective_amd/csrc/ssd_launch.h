@@ -66,6 +66,10 @@ struct StepArgs {
     const void* C;          // (b, G, N)
     const float* D;         // (H) or null
     void* y;                // (b, H, P)
+    // state cache rows of the batch rows, or null (row b uses state row b);
+    // an index outside [0, cache_rows) marks a padding row (skipped)
+    const int32_t* state_idx;
+    int64_t cache_rows;
     int H, P, G;
 };
 
@@ -111,6 +115,9 @@ struct ConvArgs {
     void* b_out;             // (b, L, nb): channels [nx, nx + nb)
     void* c_out;             // (b, L, nb): channels [nx + nb, dim)
     void* state_out;         // (b, dim, 3) io or null; decode: the state, updated in place
+    // decode: conv-state cache rows of the batch rows, or null (as StepArgs)
+    const int32_t* state_idx;
+    int64_t cache_rows;
     int64_t L;
     int batch, dim, nx, nb;
 };

@@ -219,14 +219,19 @@ __global__ __launch_bounds__(kMixThreads) void conv1d_update_kernel(ConvArgs a) 
     const int c0 = 8 * cg;
     if (c0 >= a.dim) return;
     const int64_t b = blockIdx.y;
+    int64_t sb = b;  // the conv-state cache row of batch row b (padding rows: skipped)
+    if (a.state_idx) {
+        sb = a.state_idx[b];
+        if (sb < 0 || sb >= a.cache_rows) return;
+    }
     V8<T> cur;
     cur.load(static_cast<const T*>(a.xbc) + b * a.dim + c0);
-    T* st = static_cast<T*>(a.state_out);
+    T* st = static_cast<T*>(a.state_out) + sb * a.dim * 3;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float4 wv = *reinterpret_cast<const float4*>(a.weight + (c0 + e) * kConvW);
-        T* sp = st + (b * a.dim + c0 + e) * 3;
+        T* sp = st + (c0 + e) * 3;
         float s[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) {

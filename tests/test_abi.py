@@ -159,6 +159,54 @@ def test_state_update_rejects_bad_arguments(lib):
     assert _step_call(lib, b=0) == OK
 
 
+def _cached_step_call(lib, b=2, rows=1000, H=4, P=16, N=16, G=1, io=ssd.F32, **over):
+    buf = _Buf()
+    a = dict(state=buf(), idx=buf(), x=buf(), dt=buf(), bias=None, sp=1, lo=0.0, hi=math.inf,
+             A=buf(), B=buf(), C=buf(), D=None, y=buf())
+    a.update(over)
+    return lib.ssd_state_update_cached(b, rows, H, P, N, G, io, a["state"], a["idx"], a["x"],
+                                       a["dt"], a["bias"], a["sp"], a["lo"], a["hi"], a["A"],
+                                       a["B"], a["C"], a["D"], a["y"], None)
+
+
+def test_cached_state_update_rejects_bad_arguments(lib):
+    assert _cached_step_call(lib, idx=None) == NULL_ARG
+    assert _cached_step_call(lib, rows=-1) == BAD_SHAPE
+    assert _cached_step_call(lib, rows=1 << 31) == BAD_SHAPE
+    assert _cached_step_call(lib, rows=(1 << 30), H=1 << 16, P=1 << 10) == BAD_SHAPE  # bytes > 2^62
+    assert _cached_step_call(lib, N=48) == UNSUPPORTED
+    buf = _Buf()
+    s = buf()
+    # the cache spans all its rows (1000 x 4 KiB), not the batch's two
+    assert _cached_step_call(lib, state=s, y=s + 2 * 1024 * 1024) == ALIAS
+    assert _cached_step_call(lib, state=s, idx=s + 4096) == ALIAS
+    y = buf()
+    assert _cached_step_call(lib, idx=y, y=y) == ALIAS
+    assert _cached_step_call(lib, b=0, idx=None) == OK
+
+
+def _cached_conv_call(lib, b=2, rows=1000, nx=64, nb=32, io=ssd.BF16, **over):
+    buf = _Buf()
+    a = dict(xbc=buf(), w=buf(), bias=None, st=buf(), idx=buf(), xo=buf(), bo=buf(), co=buf())
+    a.update(over)
+    return lib.ssd_conv1d_update_cached(b, rows, nx + 2 * nb, nx, nb, io, a["xbc"], a["w"], 4,
+                                        a["bias"], a["st"], a["idx"], a["xo"], a["bo"], a["co"],
+                                        None)
+
+
+def test_cached_conv_update_rejects_bad_arguments(lib):
+    assert _cached_conv_call(lib, idx=None) == NULL_ARG
+    assert _cached_conv_call(lib, rows=-1) == BAD_SHAPE
+    assert _cached_conv_call(lib, rows=(1 << 31) + 1) == BAD_SHAPE
+    assert _cached_conv_call(lib, nx=60, nb=34) == UNSUPPORTED
+    buf = _Buf()
+    s = buf()
+    # 1000 rows x 128 channels x 3 bf16 = 768 KB of cache
+    assert _cached_conv_call(lib, st=s, xo=s + 512 * 1024) == ALIAS
+    assert _cached_conv_call(lib, st=s, idx=s + 256) == ALIAS
+    assert _cached_conv_call(lib, b=0, idx=None) == OK
+
+
 # ---------------------------------------------------------- gradients, mixer
 
 
