@@ -119,6 +119,36 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* dims, ssd_dtype io, const void* x,
                               const int32_t* seq_idx, void* y, float* final_states,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The forward scan of a batch of prompts whose states live in a state cache
+ * (continuous batching: the per-sequence fp32 SSM state of RFC section 1,
+ * operator family 2, kept in slots across prefill and decode).  Row r of the
+ * batch is one sequence: its real tokens are [0, seq_lens[r]) of the row
+ * (seq_lens NULL: all L; values are clamped to [0, L]); later tokens are
+ * padding and leave the state as it is (they enter with dt = 0).  The
+ * row starts from slot state_indices[r] of state_cache (cache_rows, H, P, N)
+ * fp32 when init_from_cache != 0, else from zeros, and its state after its
+ * last real token is written back to that slot.  An index outside
+ * [0, cache_rows) marks a padding row: it is scanned from zeros and its state
+ * is dropped.  The indices of the other rows must be distinct (two rows
+ * naming one slot race); the library does not read device memory to check.
+ * y (b, L, H, P): rows past a row's length are not meaningful.  x, B and C
+ * must hold finite values at padding positions too (zeros are the natural
+ * fill): padding enters the sums with weight zero.  Other arguments as
+ * ssd_chunk_scan_fwd (no seq_idx: a row is one sequence).  The workspace
+ * (ssd_chunk_scan_cached_workspace_bytes, 256-byte aligned) holds the scan's
+ * and the gathered states.  Dispatch order: slot gather, the scan's kernels,
+ * slot scatter.
+ */
+size_t ssd_chunk_scan_cached_workspace_bytes(const ssd_dims* d, ssd_dtype io);
+ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void* x,
+                                     const float* dt, const float* dt_bias, int dt_softplus,
+                                     float dt_min, float dt_max, const float* A, const void* B,
+                                     const void* C, const float* D, const int32_t* seq_lens,
+                                     float* state_cache, int64_t cache_rows,
+                                     const int32_t* state_indices, int init_from_cache, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace ssd_chunk_scan_bwd needs for these dims (0 when
  * none, and for dims it would reject). */
 size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* dims, ssd_dtype io);

@@ -83,6 +83,12 @@ def library():
         lib.ssd_conv1d_fwd.restype = i
         lib.ssd_conv1d_update.argtypes = [i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         lib.ssd_conv1d_update.restype = i
+        lib.ssd_chunk_scan_cached_workspace_bytes.argtypes = [ctypes.POINTER(_Dims), i]
+        lib.ssd_chunk_scan_cached_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_chunk_scan_fwd_cached.argtypes = [ctypes.POINTER(_Dims), i, vp, vp, vp, i, f, f,
+                                                  vp, vp, vp, vp, vp, vp, i64, vp, i, vp, vp,
+                                                  ctypes.c_size_t, vp]
+        lib.ssd_chunk_scan_fwd_cached.restype = i
         lib.ssd_conv1d_update_cached.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp,
                                                  vp, vp, vp, vp]
         lib.ssd_conv1d_update_cached.restype = i
@@ -200,6 +206,59 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size: int, D=None, dt_bias=None,
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd")
     return (y, fs) if return_final_states else y
+
+
+def cached_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
+                           io=BF16) -> int:
+    d = _dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size)
+    return int(library().ssd_chunk_scan_cached_workspace_bytes(ctypes.byref(d), io))
+
+
+def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_size: int,
+                          seq_lens=None, init_from_cache: bool = True, D=None, dt_bias=None,
+                          dt_softplus: bool = True,
+                          dt_limit: Tuple[float, float] = (0.0, math.inf), out=None,
+                          workspace=None):
+    """Chunked SSD scan of a batch of prompts on a state cache: row r is one
+    sequence of seq_lens[r] real tokens (None: all L; later tokens are
+    padding), starting from slot state_indices[r] of ``state_cache``
+    (slots, H, P, N) fp32 (zeros unless ``init_from_cache``) and writing its
+    final state back to that slot.  An index outside the cache marks a
+    padding row.  Returns y (b, L, H, P); rows past a row's length are not
+    meaningful."""
+    import torch
+    lib = library()
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    io = _io_code(x.dtype)
+    f32 = torch.float32
+    _check(x, "x", (b, L, H, P), x.dtype, dev)
+    _check(B, "B", (b, L, G, N), x.dtype, dev)
+    _check(C, "C", (b, L, G, N), x.dtype, dev)
+    _check(dt, "dt", (b, L, H), f32, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    rows = state_cache.shape[0]
+    _check(state_cache, "state_cache", (rows, H, P, N), f32, dev)
+    _check(state_indices, "state_indices", (b,), torch.int32, dev)
+    _check(seq_lens, "seq_lens", (b,), torch.int32, dev)
+    y = out if out is not None else torch.empty((b, L, H, P), dtype=x.dtype, device=dev)
+    _check(y, "out", (b, L, H, P), x.dtype, dev)
+    d = _dims(b, L, H, P, N, G, chunk_size)
+    need = int(lib.ssd_chunk_scan_cached_workspace_bytes(ctypes.byref(d), io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_fwd_cached(
+        ctypes.byref(d), io, _ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(seq_lens), _ptr(state_cache), rows, _ptr(state_indices), int(bool(init_from_cache)),
+        _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_cached")
+    return y
 
 
 def bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,

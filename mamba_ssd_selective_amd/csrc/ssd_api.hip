@@ -217,12 +217,20 @@ int64_t ssd_chunk_scan_segments(const ssd_dims* d, ssd_dtype io) {
     return make_plan(*d, io).nseg;
 }
 
-ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
-                              const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
-                              const float* A, const void* B, const void* C, const float* D,
-                              const float* initial_states, const int32_t* seq_idx, void* y,
-                              float* final_states, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward scan.  row_len (b) or null: row r's tokens from row_len[r] on
+// are padding.  k counts the dispatches of the calling entry point; before()
+// runs once the arguments are validated, ahead of the scan's first launch.
+template <typename F>
+ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                         const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                         const float* A, const void* B, const void* C, const float* D,
+                         const float* initial_states, const int32_t* seq_idx,
+                         const int32_t* row_len, void* y, float* final_states, void* workspace,
+                         size_t workspace_bytes, hipStream_t hs, int& k, F&& before) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
     if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
@@ -246,6 +254,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
         span(x, b * L * H * P * es), span(dt, b * L * H * 4), span(B, b * L * G * N * es),
         span(C, b * L * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
         span(D, D ? H * 4 : 0), span(seq_idx, seq_idx ? b * L * 4 : 0),
+        span(row_len, row_len ? b * 4 : 0),
     };
     const Span ys = span(y, b * L * H * P * es);
     const Span fs = span(final_states, final_states ? b * H * P * N * 4 : 0);
@@ -258,10 +267,8 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
         overlap(is, ws))
         return SSD_ERR_ALIAS;
 
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    int k = 0;
-    if (g_hooks.launched) *g_hooks.launched = 0;
     if (b == 0) return SSD_OK;
+    if (before() != hipSuccess) return SSD_ERR_HIP;
     if (L == 0) {
         if (final_states) {
             if (timed_launch(k, hs, [&] {
@@ -286,6 +293,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     sa.dt_min = dt_min;
     sa.dt_max = dt_max;
     sa.seq_idx = seq_idx;
+    sa.row_len = row_len;
     sa.D = D;
     sa.init = initial_states;
     sa.final_states = final_states;
@@ -325,6 +333,93 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     }
     if (timed_launch(k, hs, [&] { return var->chunk_output(sa, b * plan.nseg * H, hs); }) !=
         hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                              const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                              const float* A, const void* B, const void* C, const float* D,
+                              const float* initial_states, const int32_t* seq_idx, void* y,
+                              float* final_states, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    return scan_fwd_impl(d, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D,
+                         initial_states, seq_idx, nullptr, y, final_states, workspace,
+                         workspace_bytes, static_cast<hipStream_t>(stream), k,
+                         [] { return hipSuccess; });
+}
+
+size_t ssd_chunk_scan_cached_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
+    if (check_scan_dims(d, io) != SSD_OK) return 0;
+    if (d->batch == 0 || d->seqlen == 0) return 0;
+    return align_up(make_plan(*d, io).total) +
+           align_up(static_cast<size_t>(d->batch * d->nheads * d->headdim * d->dstate) * 4);
+}
+
+ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void* x,
+                                     const float* dt, const float* dt_bias, int dt_softplus,
+                                     float dt_min, float dt_max, const float* A, const void* B,
+                                     const void* C, const float* D, const int32_t* seq_lens,
+                                     float* state_cache, int64_t cache_rows,
+                                     const int32_t* state_indices, int init_from_cache, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    ssd_status st = check_scan_dims(d, io);
+    if (st != SSD_OK) return st;
+    const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
+    const int64_t k31 = int64_t(1) << 31;
+    if (cache_rows < 0 || cache_rows >= k31) return SSD_ERR_BAD_SHAPE;
+    if (cache_rows > 0 && H * P * N > (int64_t(1) << 60) / 4 / cache_rows) return SSD_ERR_BAD_SHAPE;
+    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
+    if (b > 0 && (!state_cache || !state_indices)) return SSD_ERR_NULL_ARG;
+    if (state_cache && !aligned16(state_cache)) return SSD_ERR_BAD_ARG;
+    const size_t need = ssd_chunk_scan_cached_workspace_bytes(d, io);
+    if (need > 0 && (!workspace || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+        return SSD_ERR_WORKSPACE;
+    const size_t es = io_size(io);
+    const int64_t G = d->ngroups;
+    const Span cs = span(state_cache, cache_rows * H * P * N * 4);
+    const Span others[] = {
+        span(x, b * L * H * P * es), span(dt, b * L * H * 4), span(B, b * L * G * N * es),
+        span(C, b * L * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+        span(D, D ? H * 4 : 0), span(seq_lens, seq_lens ? b * 4 : 0),
+        span(state_indices, state_indices ? b * 4 : 0), span(y, b * L * H * P * es),
+        span(workspace, need)};
+    for (const Span& o : others)
+        if (overlap(cs, o)) return SSD_ERR_ALIAS;
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    if (b == 0 || L == 0) {
+        // nothing to scan: every state stays as it is
+        if (b > 0 && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
+        return SSD_OK;
+    }
+    const Plan plan = make_plan(*d, io);
+    const size_t scan_bytes = align_up(plan.total);
+    float* states = reinterpret_cast<float*>(static_cast<char*>(workspace) + scan_bytes);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int64_t per_row = H * P * N;
+    // the initial states gathered from their slots (zeros without them), the
+    // scan's final states over them in place, then scattered back
+    st = scan_fwd_impl(d, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D, states,
+                       nullptr, seq_lens, y, states, workspace, scan_bytes, hs, k, [&] {
+                           return timed_launch(k, hs, [&] {
+                               return ssd::launch_gather_slots(
+                                   init_from_cache ? state_cache : nullptr, state_indices,
+                                   cache_rows, states, b, per_row, hs);
+                           });
+                       });
+    if (st != SSD_OK) return st;
+    if (timed_launch(k, hs, [&] {
+            return ssd::launch_scatter_slots(states, state_indices, cache_rows, state_cache, b,
+                                             per_row, hs);
+        }) != hipSuccess)
         return SSD_ERR_HIP;
     return SSD_OK;
 }

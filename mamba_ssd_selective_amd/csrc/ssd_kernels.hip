@@ -126,6 +126,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     const int64_t b = w / a.nc;
     const int64_t t0 = static_cast<int64_t>(c) * Q;
     const int64_t tl = a.L - 1;
+    // tokens from here on carry no state (dt 0): the row's end, or its length
+    int64_t t_end = a.L;
+    if (a.row_len) {
+        const int64_t rl = a.row_len[b];
+        t_end = rl < 0 ? 0 : (rl < a.L ? rl : a.L);
+    }
     const T* __restrict__ Bp = static_cast<const T*>(a.B);
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
 
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             const int t = lane * E + k;
-            const bool real = t < Q && t0 + t < a.L;
+            const bool real = t < Q && t0 + t < t_end;
             const float d = real ? dt_transform(raw[k], bias, a.softplus, a.dt_min, a.dt_max) : 0.0f;
             const int before = (k == 0) ? prev_lane_last : sq[k - 1];
             const bool head = t < Q && ((t == 0) || (sq[k] != before));
@@ -914,6 +920,31 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
     if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
+__global__ __launch_bounds__(256) void gather_slots_kernel(const float* __restrict__ cache,
+                                                          const int32_t* __restrict__ idx,
+                                                          int64_t rows, float* __restrict__ dst,
+                                                          int64_t per_row) {
+    const int64_t r = blockIdx.y;
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i >= per_row) return;
+    const int64_t s = idx[r];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cache && s >= 0 && s < rows) v = *reinterpret_cast<const float4*>(cache + s * per_row + i);
+    *reinterpret_cast<float4*>(dst + r * per_row + i) = v;
+}
+
+__global__ __launch_bounds__(256) void scatter_slots_kernel(const float* __restrict__ src,
+                                                           const int32_t* __restrict__ idx,
+                                                           int64_t rows, float* __restrict__ cache,
+                                                           int64_t per_row) {
+    const int64_t r = blockIdx.y;
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    const int64_t s = idx[r];
+    if (i >= per_row || s < 0 || s >= rows) return;
+    *reinterpret_cast<float4*>(cache + s * per_row + i) =
+        *reinterpret_cast<const float4*>(src + r * per_row + i);
+}
+
 // ===========================================================================
 // One decode token.  256 threads; N/4 lanes per state row (one float4 each),
 // so RP = 256/(N/4) rows per pass.  Two layouts of the grid:
@@ -1006,6 +1037,20 @@ hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_
     if (n == 0) return hipSuccess;
     return dispatch(copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                     st, src, dst, n);
+}
+
+hipError_t launch_gather_slots(const float* cache, const int32_t* idx, int64_t rows, float* dst,
+                               int64_t b, int64_t per_row, hipStream_t st) {
+    if (b == 0 || per_row == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((per_row / 4 + 255) / 256), static_cast<unsigned>(b));
+    return dispatch(gather_slots_kernel, grid, dim3(256), st, cache, idx, rows, dst, per_row);
+}
+
+hipError_t launch_scatter_slots(const float* src, const int32_t* idx, int64_t rows, float* cache,
+                                int64_t b, int64_t per_row, hipStream_t st) {
+    if (b == 0 || per_row == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((per_row / 4 + 255) / 256), static_cast<unsigned>(b));
+    return dispatch(scatter_slots_kernel, grid, dim3(256), st, src, idx, rows, cache, per_row);
 }
 
 template <typename T, int P, int N, int Q, bool kTiles = true>

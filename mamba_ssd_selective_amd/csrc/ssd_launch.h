@@ -20,6 +20,9 @@ struct ScanArgs {
     int softplus;
     float dt_min, dt_max;
     const int32_t* seq_idx; // (b, L) or null
+    // (b) or null: row b's tokens from row_len[b] on are padding (dt 0: they
+    // leave the state as it is; their y rows are not meaningful)
+    const int32_t* row_len;
     const float* D;         // (H) or null
     const float* init;      // (b, H, P, N) or null
     float* final_states;    // (b, H, P, N) or null
@@ -213,6 +216,13 @@ hipError_t launch_gated_rmsnorm(int io, const NormArgs& a, hipStream_t st);
 
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);
+// Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros
+// for an index outside [0, rows) or when cache is null); scatter row r to slot
+// idx[r] (rows whose index is outside are skipped).  per_row % 4 == 0.
+hipError_t launch_gather_slots(const float* cache, const int32_t* idx, int64_t rows, float* dst,
+                               int64_t b, int64_t per_row, hipStream_t st);
+hipError_t launch_scatter_slots(const float* src, const int32_t* idx, int64_t rows, float* cache,
+                                int64_t b, int64_t per_row, hipStream_t st);
 hipError_t launch_state_update(int io, int64_t N, const StepArgs& a, int64_t nblocks,
                                hipStream_t st);
 

@@ -207,6 +207,41 @@ def test_cached_conv_update_rejects_bad_arguments(lib):
     assert _cached_conv_call(lib, b=0, idx=None) == OK
 
 
+def test_cached_prefill_workspace_and_rejections(lib):
+    # the scan's workspace, then the gathered states (fp32 P x N per row, head)
+    plain = ssd.workspace_bytes(2, 300, 8, 64, 128, 2, 128)
+    assert ssd.cached_workspace_bytes(2, 300, 8, 64, 128, 2, 128) == plain + 2 * 8 * 64 * 128 * 4
+    assert ssd.cached_workspace_bytes(2, 0, 8, 64, 128, 2, 128) == 0
+    buf = _Buf()
+
+    def call(dims=(2, 300, 8, 64, 128, 2, 128), rows=16, **over):
+        a = dict(x=buf(), dt=buf(), A=buf(), B=buf(), C=buf(), lens=None, cache=buf(1 << 26),
+                 idx=buf(), y=buf(), ws=buf(1 << 23), ws_bytes=1 << 23, lo=0.0, hi=math.inf)
+        a.update(over)
+        d = ssd._Dims(*dims)
+        return lib.ssd_chunk_scan_fwd_cached(
+            ctypes.byref(d), ssd.BF16, a["x"], a["dt"], None, 1, a["lo"], a["hi"], a["A"], a["B"],
+            a["C"], None, a["lens"], a["cache"], rows, a["idx"], 1, a["y"], a["ws"], a["ws_bytes"],
+            None)
+
+    assert call(idx=None) == NULL_ARG
+    assert call(cache=None) == NULL_ARG
+    assert call(rows=-1) == BAD_SHAPE
+    assert call(rows=1 << 31) == BAD_SHAPE
+    assert call(cache=0x70000008) == BAD_ARG
+    assert call(lo=1.0, hi=0.0) == BAD_ARG
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=1 << 20) == WORKSPACE
+    assert call(dims=(2, 300, 8, 64, 96, 2, 128)) == UNSUPPORTED
+    c = buf(1 << 26)
+    assert call(cache=c, y=c + 4096) == ALIAS              # y over the cache
+    assert call(cache=c, idx=c + (4 << 20) - 64) == ALIAS   # indices inside the last slot (16 x 256 KiB)
+    w = buf(1 << 23)
+    assert call(ws=w, y=w + 4096) == ALIAS                 # y over the workspace
+    assert call(dims=(0, 300, 8, 64, 128, 2, 128), idx=None, cache=None) == OK
+    assert call(dims=(2, 0, 8, 64, 128, 2, 128), ws=None) == OK   # nothing to scan
+
+
 # ---------------------------------------------------------- gradients, mixer
 
 

@@ -166,3 +166,136 @@ def test_continuous_batching_decode():
         assert oracle.rel_l2(np.stack(ys[s]), np.stack(yr)) < 2e-2
     # the slots no sequence holds stayed zero
     assert not got[[1, 3]].any()
+
+
+def _prefill_case(seed, b, L, H, G, io, rows):
+    rng = np.random.default_rng(seed)
+    p = workloads.random_problem(rng, b, L, H, 64, 128, G, io=io, init=False)
+    p["cache"] = rng.standard_normal((rows, H, 64, 128)).astype(np.float32)
+    return rng, p
+
+
+def _run_prefill(p, idx, lens, io, Q, init_from_cache=True):
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    t = torch.bfloat16 if io == "bf16" else torch.float32
+    c = _dev(p["cache"])
+    y = ssd.chunk_scan_fwd_cached(_dev(p["x"], t), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], t),
+                                  _dev(p["C"], t), c, _dev(idx), chunk_size=Q,
+                                  seq_lens=None if lens is None else _dev(lens),
+                                  init_from_cache=init_from_cache, D=_dev(p["D"]),
+                                  dt_bias=_dev(p["dt_bias"]))
+    torch.cuda.synchronize()
+    return _host(y), _host(c)
+
+
+def _oracle_row(p, r, n, h0, heads=None, grp=None):
+    hs = slice(None) if heads is None else heads
+    gs = slice(None) if grp is None else grp
+    return oracle.scan(p["x"][r:r + 1, :n, hs], p["dt_raw"][r:r + 1, :n, hs], p["A"][hs],
+                       p["B"][r:r + 1, :n, gs], p["C"][r:r + 1, :n, gs],
+                       dt_bias=p["dt_bias"][hs], D=p["D"][hs],
+                       h_init=None if h0 is None else h0[None])
+
+
+@pytest.mark.parametrize("io,Q", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("init_from_cache", [True, False])
+def test_prefill_cached_rows(io, Q, init_from_cache):
+    """Rows of lengths 300 (all), 0, 1, one chunk, a ragged 200 and a padding
+    row: each row's y up to its length and its slot equal the oracle's scan of
+    that row's real tokens from the slot's state; other slots are untouched."""
+    b, L, H, G, rows = 6, 300, 8, 2, 9
+    rng, p = _prefill_case(3, b, L, H, G, io, rows)
+    idx = np.array([7, 2, 0, 5, -1, 3], dtype=np.int32)
+    lens = np.array([300, 0, 1, Q, 137, 200], dtype=np.int32)
+    print("case io=%s Q=%d init=%s" % (io, Q, init_from_cache), flush=True)
+    y, c = _run_prefill(p, idx, lens, io, Q, init_from_cache)
+    tol = 1e-4 if io == "f32" else 2e-2
+    for r in range(b):
+        s, n = idx[r], lens[r]
+        if not 0 <= s < rows:
+            continue
+        h0 = p["cache"][s] if init_from_cache else None
+        if n == 0:
+            want = p["cache"][s] if init_from_cache else np.zeros_like(p["cache"][s])
+            assert np.array_equal(c[s], want)
+            continue
+        yr, hr = _oracle_row(p, r, n, h0)
+        assert oracle.rel_l2(y[r, :n], yr[0]) < tol, r
+        assert oracle.rel_l2(c[s], hr[0]) < tol, r
+    untouched = [s for s in range(rows) if s not in idx]
+    assert np.array_equal(c[untouched], p["cache"][untouched])
+
+
+def test_prefill_cached_matches_plain_scan():
+    """All rows full and slots 0..b-1 in order: the same y and final states
+    as the plain scan with those initial states, bit for bit."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    b, L, H, G = 3, 700, 8, 2
+    rng, p = _prefill_case(8, b, L, H, G, "bf16", b)
+    bf = torch.bfloat16
+    y0, fs = ssd.chunk_scan_fwd(_dev(p["x"], bf), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], bf),
+                                _dev(p["C"], bf), chunk_size=128, D=_dev(p["D"]),
+                                dt_bias=_dev(p["dt_bias"]), initial_states=_dev(p["cache"]),
+                                return_final_states=True)
+    y, c = _run_prefill(p, np.arange(b, dtype=np.int32), None, "bf16", 128)
+    assert np.array_equal(y, _host(y0))
+    assert np.array_equal(c, _host(fs))
+
+
+def test_prefill_cached_8k_shape():
+    """The 8K-token shape (H 64, G 8) as a two-row batch of lengths 8192 and
+    5000 on an 8-slot cache; the oracle runs the heads of group 5."""
+    b, L, H, G, rows = 2, 8192, 64, 8, 8
+    rng, p = _prefill_case(12, b, L, H, G, "bf16", rows)
+    idx = np.array([6, 1], dtype=np.int32)
+    lens = np.array([8192, 5000], dtype=np.int32)
+    y, c = _run_prefill(p, idx, lens, "bf16", 128)
+    grp = 5
+    hs = slice(8 * grp, 8 * grp + 8)
+    for r in range(b):
+        s, n = idx[r], lens[r]
+        yr, hr = _oracle_row(p, r, n, p["cache"][s][hs], heads=hs, grp=slice(grp, grp + 1))
+        ey, eh = oracle.rel_l2(y[r, :n, hs], yr[0]), oracle.rel_l2(c[s][hs], hr[0])
+        print("row %d: y %.3e state %.3e" % (r, ey, eh), flush=True)
+        assert ey < 2e-2 and eh < 2e-2
+
+
+def test_prefill_then_decode_on_cache():
+    """Prompts of different lengths prefilled into their slots, then three
+    decode tokens each on the same slots: every sequence's decode outputs and
+    final slot equal the oracle's scan of its prompt plus the three tokens."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    b, L, H, G, rows = 4, 260, 8, 2, 6
+    T = 3
+    rng, p = _prefill_case(21, b, L + T, H, G, "bf16", rows)
+    idx = np.array([4, 0, 5, 2], dtype=np.int32)
+    lens = np.array([260, 77, 128, 1], dtype=np.int32)
+    # the prompts: each row's first lens[r] tokens, zeros after
+    q = {k: p[k].copy() for k in ("x", "dt_raw", "B", "C")}
+    for k in q:
+        q[k] = q[k][:, :L].copy()
+        for r in range(b):
+            q[k][r, lens[r]:] = 0
+    q.update({k: p[k] for k in ("A", "D", "dt_bias", "cache")})
+    _, c = _run_prefill(q, idx, lens, "bf16", 128)
+    cd = _dev(c)
+    bf = torch.bfloat16
+    ys = []
+    for k in range(T):
+        # decode token k of row r is the row's token lens[r] + k
+        pick = lambda a: np.stack([a[r, lens[r] + k] for r in range(b)])
+        ys.append(_host(ssd.state_update(cd, _dev(pick(p["x"]), bf), _dev(pick(p["dt_raw"])),
+                                         _dev(p["A"]), _dev(pick(p["B"]), bf), _dev(pick(p["C"]), bf),
+                                         D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]),
+                                         state_indices=_dev(idx))))
+    torch.cuda.synchronize()
+    got = _host(cd)
+    for r in range(b):
+        n = lens[r] + T
+        yr, hr = _oracle_row(p, r, n, p["cache"][idx[r]])
+        dec = np.stack([ys[k][r] for k in range(T)])
+        assert oracle.rel_l2(dec, yr[0, lens[r]:n]) < 2e-2, r
+        assert oracle.rel_l2(got[idx[r]], hr[0]) < 2e-2, r
