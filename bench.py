@@ -23,7 +23,10 @@ its tokens/s, per-kernel times, a roofline entry for its per-chunk gradient
 kernel against the compulsory bytes of the whole backward pass, and the fp64
 oracle's gradients timed on the heads of one group; and a "mixer" object for
 the steps beside the scan (causal conv1d into the scan's x/B/C, gated group
-RMSNorm of its output) at the same shape.
+RMSNorm of its output) at the same shape; and a "cache" object for continuous
+batching on state caches (a 256-row decode step on slots of a 512-slot cache
+with its HBM roofline, and the prefill of 8 prompts of different lengths from
+and back into cache slots).
 """
 import argparse
 import ctypes
@@ -307,6 +310,125 @@ def mixer_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
     return res
 
 
+def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
+    """Continuous batching on state caches at the workload's head shape: one
+    decode token for 256 rows whose fp32 states sit in slots of a 512-slot
+    cache (the state update; HBM roofline against its compulsory bytes), and
+    the prefill of 8 prompts of seeded lengths 512..2048 (rows of 2048 tokens)
+    from and back into the slots of a 16-slot cache (every dispatch timed).
+    The oracle's decode step is timed on 16 of the rows."""
+    import numpy as np
+    H, P, N, G, Q = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(91)
+    bf = torch.bfloat16
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+    A = (-torch.rand((H,), generator=gen) * 3 - 0.5).to(dev)
+    D = torch.randn((H,), generator=gen).to(dev)
+    bias = (torch.rand((H,), generator=gen) - 4.0).to(dev)
+    res = {}
+    vp = ctypes.sizeof(ctypes.c_void_p)
+
+    def timed(fn, nk, n):
+        for _ in range(5):
+            if fn() != 0:
+                raise RuntimeError("cache call failed")
+        torch.cuda.synchronize()
+        evs = hip.events(2 * nk * n)
+        launched = ctypes.c_int(0)
+        t0 = time.perf_counter()
+        for i in range(n):
+            lib.ssd_set_timing_events(ev_slice_of(evs, 2 * nk * i, 2 * nk, vp), 2 * nk,
+                                      ctypes.byref(launched))
+            fn()
+        lib.ssd_set_timing_events(None, 0, None)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n
+        if launched.value != nk:
+            raise RuntimeError("expected %d dispatches, got %d" % (nk, launched.value))
+        us = [1e3 * float(np.mean([hip.elapsed_ms(evs[2 * (nk * i + k)], evs[2 * (nk * i + k) + 1])
+                                   for i in range(n)])) for k in range(nk)]
+        hip.destroy(evs)
+        return us, wall
+
+    # ---- decode: 256 rows, 512 slots
+    rows, slots = 256, 512
+    cache = torch.randn((slots, H, P, N), generator=gen).to(dev)
+    idx = torch.randperm(slots, generator=gen)[:rows].to(torch.int32).to(dev)
+    x = torch.randn((rows, H, P), generator=gen).to(bf).to(dev)
+    dt = torch.randn((rows, H), generator=gen).to(dev)
+    Bm = torch.randn((rows, G, N), generator=gen).to(bf).to(dev)
+    Cm = torch.randn((rows, G, N), generator=gen).to(bf).to(dev)
+    y = torch.empty((rows, H, P), dtype=bf, device=dev)
+    dec = lambda: lib.ssd_state_update_cached(rows, slots, H, P, N, G, 1, cache.data_ptr(),
+                                              idx.data_ptr(), x.data_ptr(), dt.data_ptr(),
+                                              bias.data_ptr(), 1, 0.0, math.inf, A.data_ptr(),
+                                              Bm.data_ptr(), Cm.data_ptr(), D.data_ptr(),
+                                              y.data_ptr(), stream())
+    (us,), _ = timed(dec, 1, steps)
+    nbytes = rows * (2 * H * P * N * 4 + 2 * H * P * 2 + 2 * G * N * 2 + H * 4 + 4) + 3 * H * 4
+    ach = nbytes / (us * 1e-6) / 1e9
+    res["decode"] = {"rows": rows, "slots": slots, "us": round(us, 2),
+                     "tokens_per_s": round(rows / (us * 1e-6), 1),
+                     "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                  "traffic": None}}
+
+    # ---- prefill: 8 prompts of 512..2048 tokens into a 16-slot cache
+    b, L, pslots = 8, 2048, 16
+    lens = torch.randint(512, L + 1, (b,), generator=gen, dtype=torch.int32)
+    px = torch.randn((b, L, H, P), generator=gen).to(bf)
+    pB = torch.randn((b, L, G, N), generator=gen).to(bf)
+    pC = torch.randn((b, L, G, N), generator=gen).to(bf)
+    pdt = torch.randn((b, L, H), generator=gen)
+    for r in range(b):  # padding positions hold zeros
+        n = int(lens[r])
+        px[r, n:] = 0
+        pB[r, n:] = 0
+        pC[r, n:] = 0
+    px, pB, pC, pdt = px.to(dev), pB.to(dev), pC.to(dev), pdt.to(dev)
+    pcache = torch.randn((pslots, H, P, N), generator=gen).to(dev)
+    pidx = torch.randperm(pslots, generator=gen)[:b].to(torch.int32).to(dev)
+    plens = lens.to(dev)
+    py = torch.empty((b, L, H, P), dtype=bf, device=dev)
+    d = ssd._dims(b, L, H, P, N, G, Q)
+    need = int(lib.ssd_chunk_scan_cached_workspace_bytes(ctypes.byref(d), 1))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    nseg = ssd.segments(b, L, H, P, N, G, Q)
+    names = ["gather", "chunk_prep"] + (["chunk_state"] if nseg > 1 else []) + ["chunk_output",
+                                                                                  "scatter"]
+    pre = lambda: lib.ssd_chunk_scan_fwd_cached(
+        ctypes.byref(d), 1, px.data_ptr(), pdt.data_ptr(), bias.data_ptr(), 1, 0.0, math.inf,
+        A.data_ptr(), pB.data_ptr(), pC.data_ptr(), D.data_ptr(), plens.data_ptr(),
+        pcache.data_ptr(), pslots, pidx.data_ptr(), 1, py.data_ptr(), ws.data_ptr(), need, stream())
+    us_k, wall = timed(pre, len(names), max(steps // 2, 10))
+    real = int(lens.sum())
+    res["prefill"] = {"rows": b, "row_capacity": L, "real_tokens": real,
+                      "lengths": [int(v) for v in lens], "slots": pslots,
+                      "kernels_us": {n: round(u, 2) for n, u in zip(names, us_k)},
+                      "kernels_total_us": round(sum(us_k), 2),
+                      "ms_per_call": round(1e3 * wall, 4),
+                      "real_tokens_per_s": round(real / wall, 1)}
+    res["cpu_baseline"] = None
+    if cpu_seconds > 0:
+        import oracle
+        k = 16
+        st0 = cache[idx[:k].long()].double().cpu().numpy()
+        args = (x[:k].float().cpu().numpy(), dt[:k].cpu().numpy(), A.cpu().numpy(),
+                Bm[:k].float().cpu().numpy(), Cm[:k].float().cpu().numpy())
+        t0 = time.perf_counter()
+        runs = 0
+        while runs == 0 or time.perf_counter() - t0 < cpu_seconds:
+            oracle.step(st0, *args, dt_bias=bias.cpu().numpy(), D=D.cpu().numpy())
+            runs += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(k * runs / el, 1), "unit": "decode tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "decode step of %d of the %d rows, %d run(s) in %.1f s "
+                                         "(fp64, one thread)" % (k, rows, runs, el)}
+    return res
+
+
 def ev_slice_of(evs, first, count, vp):
     return (ctypes.c_void_p * count).from_buffer(evs, first * vp)
 
@@ -493,6 +615,8 @@ def main():
                                           args.backward_steps, min(args.cpu_seconds, 5.0), p)
     log("bench: mixer steps")
     result["mixer"] = mixer_measure(ssd, lib, hip, torch, w, 50, min(args.cpu_seconds, 3.0))
+    log("bench: state caches")
+    result["cache"] = cache_measure(ssd, lib, hip, torch, w, 50, min(args.cpu_seconds, 2.0))
     if args.cpu_seconds > 0:
         log("bench: CPU oracle baseline (budget %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline({k: (v[:, :L] if k in ("x", "dt_raw", "B", "C", "seq_idx") and v is not None else v)
