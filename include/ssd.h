@@ -149,6 +149,43 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
                                      const int32_t* state_indices, int init_from_cache, void* y,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Chunk-emulating decode (RFC section 1, operator family 1: "batch invariant"
+ * covers how a sequence is split into prefill and decode steps; section 3,
+ * Figure 2, box [F2]: the SSD scan's "chunk-emulating decode").  One token per
+ * batch row; row r works on slot state_indices[r], whose new token sits at
+ * offset positions[r] (0..Q-1) of its current chunk.  Per slot the caller
+ * keeps:
+ *   state_cache (slots, H, P, N) fp32: the state at the start of the slot's
+ *                current chunk (for example from ssd_chunk_scan_fwd_cached
+ *                over a prompt whose length is a multiple of Q);
+ *   x_chunks (slots, Q, H, P) io, dt_chunks (slots, Q, H) fp32 (raw dt),
+ *   b_chunks, c_chunks (slots, Q, G, N) io: the tokens of the current chunk so
+ *                far (offsets below positions[r]; their contents past that
+ *                are never read).
+ * The call writes the new token into offset positions[r] of the slot's chunk
+ * buffers, runs the chunked scan over offsets 0..positions[r] from the
+ * chunk-start state, and writes y (b, H, P) io: the value the chunked prefill
+ * gives that token.  When positions[r] = Q - 1 the chunk is complete and its
+ * final state replaces the slot's chunk-start state.  An index outside
+ * [0, cache_rows) or a position outside [0, Q) marks a padding row: its slot
+ * and its y row are not touched.  Live rows must name distinct slots.
+ * dims: batch b, seqlen = chunk_size = Q (one chunk), H, P, N, G as for the
+ * scan and in its compiled set.  The workspace
+ * (ssd_decode_emulated_workspace_bytes, 256-byte aligned) holds the chunk's
+ * scan.  Each step costs a scan of one chunk per row: this is the strict
+ * decode, not the fast one (ssd_state_update).  Dispatch order: staging copy,
+ * slot gather, the scan's kernels, output copy and state commit.
+ */
+size_t ssd_decode_emulated_workspace_bytes(const ssd_dims* d, ssd_dtype io);
+ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                               const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                               const float* A, const void* B, const void* C, const float* D,
+                               float* state_cache, void* x_chunks, float* dt_chunks,
+                               void* b_chunks, void* c_chunks, int64_t cache_rows,
+                               const int32_t* state_indices, const int32_t* positions, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace ssd_chunk_scan_bwd needs for these dims (0 when
  * none, and for dims it would reject). */
 size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* dims, ssd_dtype io);

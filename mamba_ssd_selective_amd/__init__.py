@@ -89,6 +89,12 @@ def library():
                                                   vp, vp, vp, vp, vp, vp, i64, vp, i, vp, vp,
                                                   ctypes.c_size_t, vp]
         lib.ssd_chunk_scan_fwd_cached.restype = i
+        lib.ssd_decode_emulated_workspace_bytes.argtypes = [ctypes.POINTER(_Dims), i]
+        lib.ssd_decode_emulated_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_decode_emulated.argtypes = [ctypes.POINTER(_Dims), i, vp, vp, vp, i, f, f, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp,
+                                            ctypes.c_size_t, vp]
+        lib.ssd_decode_emulated.restype = i
         lib.ssd_conv1d_update_cached.argtypes = [i64, i64, i64, i64, i64, i, vp, vp, i64, vp, vp, vp,
                                                  vp, vp, vp, vp]
         lib.ssd_conv1d_update_cached.restype = i
@@ -258,6 +264,57 @@ def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_s
         _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_cached")
+    return y
+
+
+def decode_emulated(x, dt, A, B, C, state_cache, chunks, state_indices, positions, *,
+                    chunk_size: int, D=None, dt_bias=None, dt_softplus: bool = True,
+                    dt_limit: Tuple[float, float] = (0.0, math.inf), out=None, workspace=None):
+    """Chunk-emulating decode: one token per row (x (b, H, P), dt (b, H),
+    B/C (b, G, N)) at offset positions[r] of the current chunk of slot
+    state_indices[r].  ``state_cache`` (slots, H, P, N) fp32 holds each slot's
+    chunk-start state and ``chunks`` = (x_chunks (slots, Q, H, P),
+    dt_chunks (slots, Q, H), B_chunks, C_chunks (slots, Q, G, N)) the chunk's
+    tokens so far; both are updated in place.  Returns y (b, H, P), bitwise
+    the chunked prefill's value for each token."""
+    import torch
+    lib = library()
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    Q = int(chunk_size)
+    dev = x.device
+    io = _io_code(x.dtype)
+    f32 = torch.float32
+    xc, dtc, bc, cc = chunks
+    rows = state_cache.shape[0]
+    _check(x, "x", (b, H, P), x.dtype, dev)
+    _check(dt, "dt", (b, H), f32, dev)
+    _check(B, "B", (b, G, N), x.dtype, dev)
+    _check(C, "C", (b, G, N), x.dtype, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    _check(state_cache, "state_cache", (rows, H, P, N), f32, dev)
+    _check(xc, "x_chunks", (rows, Q, H, P), x.dtype, dev)
+    _check(dtc, "dt_chunks", (rows, Q, H), f32, dev)
+    _check(bc, "B_chunks", (rows, Q, G, N), x.dtype, dev)
+    _check(cc, "C_chunks", (rows, Q, G, N), x.dtype, dev)
+    _check(state_indices, "state_indices", (b,), torch.int32, dev)
+    _check(positions, "positions", (b,), torch.int32, dev)
+    y = out if out is not None else torch.empty((b, H, P), dtype=x.dtype, device=dev)
+    _check(y, "out", (b, H, P), x.dtype, dev)
+    d = _dims(b, Q, H, P, N, G, Q)
+    need = int(lib.ssd_decode_emulated_workspace_bytes(ctypes.byref(d), io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_decode_emulated(
+        ctypes.byref(d), io, _ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(state_cache), _ptr(xc), _ptr(dtc), _ptr(bc), _ptr(cc), rows, _ptr(state_indices),
+        _ptr(positions), _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
+    if st != 0:
+        raise SSDError(st, "ssd_decode_emulated")
     return y
 
 

@@ -424,6 +424,165 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
     return SSD_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the chunk-emulating decode: the scan's (rows of one chunk), the
+// gathered states, then the batch-ordered inputs, output and row lengths.
+struct EmulPlan {
+    size_t scan = 0, states = 0, xw = 0, dtw = 0, bw = 0, cw = 0, yw = 0, rl = 0, total = 0;
+};
+
+EmulPlan make_emul_plan(const ssd_dims& d, ssd_dtype io) {
+    EmulPlan e;
+    const size_t es = io_size(io);
+    const size_t b = static_cast<size_t>(d.batch), Q = static_cast<size_t>(d.chunk_size);
+    const size_t HP = static_cast<size_t>(d.nheads * d.headdim);
+    const size_t GN = static_cast<size_t>(d.ngroups * d.dstate);
+    size_t off = align_up(make_plan(d, io).total);
+    e.scan = 0;
+    e.states = off;
+    off = align_up(off + b * HP * static_cast<size_t>(d.dstate) * 4);
+    e.xw = off;
+    off = align_up(off + b * Q * HP * es);
+    e.dtw = off;
+    off = align_up(off + b * Q * static_cast<size_t>(d.nheads) * 4);
+    e.bw = off;
+    off = align_up(off + b * Q * GN * es);
+    e.cw = off;
+    off = align_up(off + b * Q * GN * es);
+    e.yw = off;
+    off = align_up(off + b * Q * HP * es);
+    e.rl = off;
+    off = align_up(off + b * 4);
+    e.total = off;
+    return e;
+}
+
+ssd_status check_emul_dims(const ssd_dims* d, ssd_dtype io) {
+    ssd_status st = check_scan_dims(d, io);
+    if (st != SSD_OK) return st;
+    if (d->seqlen != d->chunk_size) return SSD_ERR_BAD_SHAPE;  // the buffers hold one chunk
+    const int64_t es = static_cast<int64_t>(io_size(io));
+    if ((d->nheads * d->headdim * es) % 4 != 0 || (d->ngroups * d->dstate * es) % 4 != 0)
+        return SSD_ERR_UNSUPPORTED;
+    if (d->batch > 65535) return SSD_ERR_BAD_SHAPE;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_decode_emulated_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
+    if (check_emul_dims(d, io) != SSD_OK || d->batch == 0) return 0;
+    return make_emul_plan(*d, io).total;
+}
+
+ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                               const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                               const float* A, const void* B, const void* C, const float* D,
+                               float* state_cache, void* x_chunks, float* dt_chunks,
+                               void* b_chunks, void* c_chunks, int64_t cache_rows,
+                               const int32_t* state_indices, const int32_t* positions, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    ssd_status st = check_emul_dims(d, io);
+    if (st != SSD_OK) return st;
+    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
+    const int64_t b = d->batch, Q = d->chunk_size, H = d->nheads, P = d->headdim, N = d->dstate,
+                  G = d->ngroups;
+    if (cache_rows < 0 || cache_rows >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
+    if (cache_rows > 0 && Q * (H * P * N + H * P + 2 * G * N + H) > (int64_t(1) << 58) / cache_rows)
+        return SSD_ERR_BAD_SHAPE;
+    if (b == 0) return SSD_OK;
+    if (!x || !dt || !A || !B || !C || !y || !state_cache || !x_chunks || !dt_chunks ||
+        !b_chunks || !c_chunks || !state_indices || !positions)
+        return SSD_ERR_NULL_ARG;
+    if (!aligned16(state_cache)) return SSD_ERR_BAD_ARG;
+    const void* word_bufs[] = {x, dt, B, C, y, x_chunks, dt_chunks, b_chunks, c_chunks};
+    for (const void* p : word_bufs)
+        if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return SSD_ERR_BAD_ARG;
+    const EmulPlan e = make_emul_plan(*d, io);
+    if (!workspace || workspace_bytes < e.total ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return SSD_ERR_WORKSPACE;
+    const size_t es = io_size(io);
+    // the caches (updated in place) against everything else and each other
+    const Span caches[] = {span(state_cache, cache_rows * H * P * N * 4),
+                           span(x_chunks, cache_rows * Q * H * P * es),
+                           span(dt_chunks, cache_rows * Q * H * 4),
+                           span(b_chunks, cache_rows * Q * G * N * es),
+                           span(c_chunks, cache_rows * Q * G * N * es)};
+    const Span others[] = {span(x, b * H * P * es), span(dt, b * H * 4), span(B, b * G * N * es),
+                           span(C, b * G * N * es), span(A, H * 4),
+                           span(dt_bias, dt_bias ? H * 4 : 0), span(D, D ? H * 4 : 0),
+                           span(state_indices, b * 4), span(positions, b * 4),
+                           span(y, b * H * P * es), span(workspace, e.total)};
+    for (size_t i = 0; i < 5; ++i) {
+        for (const Span& o : others)
+            if (overlap(caches[i], o)) return SSD_ERR_ALIAS;
+        for (size_t j = i + 1; j < 5; ++j)
+            if (overlap(caches[i], caches[j])) return SSD_ERR_ALIAS;
+    }
+    const Span ys = span(y, b * H * P * es);
+    const Span ins[] = {span(x, b * H * P * es), span(dt, b * H * 4), span(B, b * G * N * es),
+                        span(C, b * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+                        span(D, D ? H * 4 : 0), span(state_indices, b * 4), span(positions, b * 4),
+                        span(workspace, e.total)};
+    for (const Span& o : ins)
+        if (overlap(ys, o)) return SSD_ERR_ALIAS;
+
+    char* wsb = static_cast<char*>(workspace);
+    ssd::EmulArgs ea{};
+    ea.x = x;
+    ea.dt = dt;
+    ea.B = B;
+    ea.C = C;
+    ea.x_buf = x_chunks;
+    ea.dt_buf = dt_chunks;
+    ea.b_buf = b_chunks;
+    ea.c_buf = c_chunks;
+    ea.state_idx = state_indices;
+    ea.pos = positions;
+    ea.cache_rows = cache_rows;
+    ea.xw = wsb + e.xw;
+    ea.dtw = reinterpret_cast<float*>(wsb + e.dtw);
+    ea.bw = wsb + e.bw;
+    ea.cw = wsb + e.cw;
+    ea.row_len = reinterpret_cast<int32_t*>(wsb + e.rl);
+    ea.yw = wsb + e.yw;
+    float* states = reinterpret_cast<float*>(wsb + e.states);
+    ea.states = states;
+    ea.state_cache = state_cache;
+    ea.y = y;
+    ea.Q = static_cast<int>(Q);
+    ea.wx = H * P * static_cast<int64_t>(es) / 4;
+    ea.wd = H;
+    ea.wb = G * N * static_cast<int64_t>(es) / 4;
+    ea.hpn = H * P * N;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int k = 0;
+    if (g_hooks.launched) *g_hooks.launched = 0;
+    st = scan_fwd_impl(d, io, ea.xw, ea.dtw, dt_bias, dt_softplus, dt_min, dt_max, A, ea.bw, ea.cw,
+                       D, states, nullptr, ea.row_len, wsb + e.yw, states, wsb,
+                       align_up(make_plan(*d, io).total), hs, k, [&] {
+                           hipError_t he = timed_launch(k, hs, [&] {
+                               return ssd::launch_emul_stage(ea, b, hs);
+                           });
+                           if (he != hipSuccess) return he;
+                           return timed_launch(k, hs, [&] {
+                               return ssd::launch_gather_slots(state_cache, state_indices,
+                                                               cache_rows, states, b, H * P * N,
+                                                               hs);
+                           });
+                       });
+    if (st != SSD_OK) return st;
+    if (timed_launch(k, hs, [&] { return ssd::launch_emul_finish(ea, b, hs); }) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
     if (check_bwd_dims(d, io) != SSD_OK) return 0;
     return make_bwd_plan(*d).total;

@@ -216,6 +216,35 @@ hipError_t launch_gated_rmsnorm(int io, const NormArgs& a, hipStream_t st);
 
 hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);
+// Chunk-emulating decode: the copies around the scan (widths in 4-byte words:
+// wx = H*P*io/4, wd = H, wb = G*N*io/4; hpn = H*P*N).
+struct EmulArgs {
+    const void* x;            // (b, H, P) io: the new tokens
+    const float* dt;          // (b, H)
+    const void* B;            // (b, G, N) io
+    const void* C;            // (b, G, N) io
+    void* x_buf;              // (slots, Q, H, P) io: each slot's current chunk
+    float* dt_buf;            // (slots, Q, H)
+    void* b_buf;              // (slots, Q, G, N) io
+    void* c_buf;              // (slots, Q, G, N) io
+    const int32_t* state_idx; // (b) slot of each row
+    const int32_t* pos;       // (b) offset of the new token in its chunk
+    int64_t cache_rows;
+    void* xw;                 // (b, Q, H, P) io: the scan's inputs
+    float* dtw;               // (b, Q, H)
+    void* bw;                 // (b, Q, G, N) io
+    void* cw;                 // (b, Q, G, N) io
+    int32_t* row_len;         // (b)
+    const void* yw;           // (b, Q, H, P) io: the scan's output
+    const float* states;      // (b, H, P, N): the scan's final states
+    float* state_cache;       // (slots, H, P, N): chunk-start states
+    void* y;                  // (b, H, P) io
+    int Q;
+    int64_t wx, wd, wb, hpn;
+};
+hipError_t launch_emul_stage(const EmulArgs& a, int64_t b, hipStream_t st);
+hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st);
+
 // Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros
 // for an index outside [0, rows) or when cache is null); scatter row r to slot
 // idx[r] (rows whose index is outside are skipped).  per_row % 4 == 0.

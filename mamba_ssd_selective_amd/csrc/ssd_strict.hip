@@ -1,0 +1,120 @@
+// ssd_strict.hip -- chunk-emulating decode on gfx950 (RL-Kernel RFC
+// "Nemotron-3-Nano-30B-A3B", section 1, operator family 1, and section 3,
+// Figure 2, box [F2]: the SSD scan runs train, prefill and "chunk-emulating
+// decode" with one arithmetic, so that how a sequence is split into prefill
+// and decode steps does not change a bit of its outputs).
+//
+// A decode token at offset i of its chunk is not folded into a running state.
+// Each slot keeps the state at its current chunk's start and that chunk's
+// tokens so far; a step appends the new token and runs the chunked scan over
+// the chunk (offsets 0..i real, the rest padding with dt 0) from the
+// chunk-start state, and returns y at offset i: the value the chunked prefill
+// computes for that token.  When the chunk is complete (i = Q - 1) the scan's
+// final state becomes the slot's new chunk-start state.
+//
+// Two small copy kernels around the scan:
+//   emul_stage_kernel   writes the new token into its slot's chunk buffers and
+//                       copies the slot's chunk (new token included, zeros past
+//                       it) into batch-ordered scan inputs; row lengths i + 1;
+//   emul_finish_kernel  copies y at offset i out, and commits the final state
+//                       of a completed chunk to the slot.
+// Both move 4-byte words (bf16 pairs or fp32); widths are checked on the host.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kEmulThreads = 256;
+
+__device__ __forceinline__ bool emul_row(const EmulArgs& a, int64_t r, int64_t& s, int& i) {
+    s = a.state_idx[r];
+    i = a.pos[r];
+    return s >= 0 && s < a.cache_rows && i >= 0 && i < a.Q;
+}
+
+__global__ __launch_bounds__(kEmulThreads) void emul_stage_kernel(EmulArgs a) {
+    const int64_t r = blockIdx.y;
+    int64_t s;
+    int i;
+    const bool live = emul_row(a, r, s, i);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.row_len[r] = live ? i + 1 : 0;
+    // per token: x words, dt words, B words, C words
+    const int64_t wx = a.wx, wd = a.wd, wb = a.wb;
+    const int64_t W = wx + wd + 2 * wb;
+    const int64_t total = static_cast<int64_t>(a.Q) * W;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kEmulThreads;
+    for (int64_t w = static_cast<int64_t>(blockIdx.x) * kEmulThreads + threadIdx.x; w < total;
+         w += stride) {
+        const int64_t j = w / W;
+        int64_t o = w % W;
+        const uint32_t* tok;   // the new token's row
+        uint32_t* buf;         // the slot's chunk buffer, token 0
+        uint32_t* ws;          // the batch-ordered scan input, token 0
+        int64_t width;
+        if (o < wx) {
+            tok = static_cast<const uint32_t*>(a.x) + r * wx;
+            buf = static_cast<uint32_t*>(a.x_buf);
+            ws = static_cast<uint32_t*>(a.xw);
+            width = wx;
+        } else if ((o -= wx) < wd) {
+            tok = reinterpret_cast<const uint32_t*>(a.dt) + r * wd;
+            buf = reinterpret_cast<uint32_t*>(a.dt_buf);
+            ws = reinterpret_cast<uint32_t*>(a.dtw);
+            width = wd;
+        } else if ((o -= wd) < wb) {
+            tok = static_cast<const uint32_t*>(a.B) + r * wb;
+            buf = static_cast<uint32_t*>(a.b_buf);
+            ws = static_cast<uint32_t*>(a.bw);
+            width = wb;
+        } else {
+            o -= wb;
+            tok = static_cast<const uint32_t*>(a.C) + r * wb;
+            buf = static_cast<uint32_t*>(a.c_buf);
+            ws = static_cast<uint32_t*>(a.cw);
+            width = wb;
+        }
+        uint32_t v = 0u;
+        if (live) {
+            uint32_t* slot = buf + (s * a.Q + j) * width + o;
+            if (j == i) {
+                v = tok[o];
+                *slot = v;
+            } else if (j < i) {
+                v = *slot;
+            }
+        }
+        ws[(r * a.Q + j) * width + o] = v;
+    }
+}
+
+__global__ __launch_bounds__(kEmulThreads) void emul_finish_kernel(EmulArgs a) {
+    const int64_t r = blockIdx.y;
+    int64_t s;
+    int i;
+    if (!emul_row(a, r, s, i)) return;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kEmulThreads;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kEmulThreads + threadIdx.x;
+    const uint32_t* yw = static_cast<const uint32_t*>(a.yw) + (r * a.Q + i) * a.wx;
+    uint32_t* y = static_cast<uint32_t*>(a.y) + r * a.wx;
+    for (int64_t w = t0; w < a.wx; w += stride) y[w] = yw[w];
+    if (i == a.Q - 1) {
+        const float4* src = reinterpret_cast<const float4*>(a.states + r * a.hpn);
+        float4* dst = reinterpret_cast<float4*>(a.state_cache + s * a.hpn);
+        for (int64_t w = t0; w < a.hpn / 4; w += stride) dst[w] = src[w];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_emul_stage(const EmulArgs& a, int64_t b, hipStream_t st) {
+    if (b == 0) return hipSuccess;
+    return dispatch(emul_stage_kernel, dim3(64, static_cast<unsigned>(b)), dim3(kEmulThreads), st, a);
+}
+
+hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st) {
+    if (b == 0) return hipSuccess;
+    return dispatch(emul_finish_kernel, dim3(64, static_cast<unsigned>(b)), dim3(kEmulThreads), st, a);
+}
+
+}  // namespace ssd

@@ -242,6 +242,44 @@ def test_cached_prefill_workspace_and_rejections(lib):
     assert call(dims=(2, 0, 8, 64, 128, 2, 128), ws=None) == OK   # nothing to scan
 
 
+def test_emulated_decode_workspace_and_rejections(lib):
+    d = (4, 128, 64, 64, 128, 8, 128)
+    need = ssd.library().ssd_decode_emulated_workspace_bytes(ctypes.byref(ssd._Dims(*d)), ssd.BF16)
+    # the one-chunk scan's workspace, states, then x/dt/B/C/y copies and row lengths
+    scan = ssd.workspace_bytes(*d)
+    al = lambda v: (v + 255) // 256 * 256
+    parts = [4 * 64 * 64 * 128 * 4, 4 * 128 * 4096 * 2, 4 * 128 * 64 * 4, 4 * 128 * 1024 * 2,
+             4 * 128 * 1024 * 2, 4 * 128 * 4096 * 2, 4 * 4]
+    assert need == al(scan) + sum(al(v) for v in parts)
+    buf = _Buf()
+
+    def call(dims=d, rows=8, **over):
+        a = dict(x=buf(), dt=buf(), A=buf(), B=buf(), C=buf(), st=buf(1 << 26), xc=buf(1 << 28),
+                 dtc=buf(), bc=buf(1 << 26), cc=buf(1 << 26), idx=buf(), pos=buf(), y=buf(),
+                 ws=buf(1 << 26), ws_bytes=1 << 26)
+        a.update(over)
+        return lib.ssd_decode_emulated(
+            ctypes.byref(ssd._Dims(*dims)), ssd.BF16, a["x"], a["dt"], None, 1, 0.0, math.inf, a["A"],
+            a["B"], a["C"], None, a["st"], a["xc"], a["dtc"], a["bc"], a["cc"], rows, a["idx"],
+            a["pos"], a["y"], a["ws"], a["ws_bytes"], None)
+
+    assert call(dims=(4, 256, 64, 64, 128, 8, 128)) == BAD_SHAPE   # seqlen must be one chunk
+    assert call(dims=(4, 128, 64, 64, 96, 8, 128)) == UNSUPPORTED
+    assert call(rows=-1) == BAD_SHAPE
+    assert call(xc=None) == NULL_ARG
+    assert call(pos=None) == NULL_ARG
+    assert call(st=0x70000008) == BAD_ARG
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=1 << 20) == WORKSPACE
+    s = buf(1 << 26)
+    assert call(st=s, y=s + 4096) == ALIAS                   # y inside the state cache
+    x = buf(1 << 28)
+    assert call(xc=x, bc=x + (1 << 20)) == ALIAS            # two caches overlap
+    w = buf(1 << 26)
+    assert call(ws=w, y=w + 1024) == ALIAS                   # y over the workspace
+    assert call(dims=(0, 128, 64, 64, 128, 8, 128), x=None, xc=None) == OK
+
+
 # ---------------------------------------------------------- gradients, mixer
 
 
