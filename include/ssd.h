@@ -138,7 +138,13 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* dims, ssd_dtype io, const void* x,
  * ssd_chunk_scan_fwd (no seq_idx: a row is one sequence).  The workspace
  * (ssd_chunk_scan_cached_workspace_bytes, 256-byte aligned) holds the scan's
  * and the gathered states.  Dispatch order: slot gather, the scan's kernels,
- * slot scatter.
+ * slot scatter.  strict != 0 runs every row as one segment of chunks whatever
+ * the batch, and forms every intra-chunk decay exp(cs_i - cs_j) per element
+ * (RFC section 4.1: batch-invariant arithmetic): a row's outputs and state
+ * are then bitwise the same in any batch, and the chunk-emulating decode
+ * (ssd_decode_emulated, always strict) continues them bit for bit.  strict = 0 lets the
+ * library cut rows into segments to fill the GPU (faster for few rows; the
+ * bits then depend on the number of rows x heads).
  */
 size_t ssd_chunk_scan_cached_workspace_bytes(const ssd_dims* d, ssd_dtype io);
 ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void* x,
@@ -146,8 +152,9 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
                                      float dt_min, float dt_max, const float* A, const void* B,
                                      const void* C, const float* D, const int32_t* seq_lens,
                                      float* state_cache, int64_t cache_rows,
-                                     const int32_t* state_indices, int init_from_cache, void* y,
-                                     void* workspace, size_t workspace_bytes, void* stream);
+                                     const int32_t* state_indices, int init_from_cache, int strict,
+                                     void* y, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * Chunk-emulating decode (RFC section 1, operator family 1: "batch invariant"

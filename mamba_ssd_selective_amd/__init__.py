@@ -86,7 +86,7 @@ def library():
         lib.ssd_chunk_scan_cached_workspace_bytes.argtypes = [ctypes.POINTER(_Dims), i]
         lib.ssd_chunk_scan_cached_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_chunk_scan_fwd_cached.argtypes = [ctypes.POINTER(_Dims), i, vp, vp, vp, i, f, f,
-                                                  vp, vp, vp, vp, vp, vp, i64, vp, i, vp, vp,
+                                                  vp, vp, vp, vp, vp, vp, i64, vp, i, i, vp, vp,
                                                   ctypes.c_size_t, vp]
         lib.ssd_chunk_scan_fwd_cached.restype = i
         lib.ssd_decode_emulated_workspace_bytes.argtypes = [ctypes.POINTER(_Dims), i]
@@ -221,7 +221,8 @@ def cached_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chun
 
 
 def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_size: int,
-                          seq_lens=None, init_from_cache: bool = True, D=None, dt_bias=None,
+                          seq_lens=None, init_from_cache: bool = True, strict: bool = False,
+                          D=None, dt_bias=None,
                           dt_softplus: bool = True,
                           dt_limit: Tuple[float, float] = (0.0, math.inf), out=None,
                           workspace=None):
@@ -230,8 +231,9 @@ def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_s
     padding), starting from slot state_indices[r] of ``state_cache``
     (slots, H, P, N) fp32 (zeros unless ``init_from_cache``) and writing its
     final state back to that slot.  An index outside the cache marks a
-    padding row.  Returns y (b, L, H, P); rows past a row's length are not
-    meaningful."""
+    padding row.  ``strict`` runs each row as one segment (bitwise the same
+    in any batch, continued bit for bit by ``decode_emulated``).  Returns
+    y (b, L, H, P); rows past a row's length are not meaningful."""
     import torch
     lib = library()
     b, L, H, P = x.shape
@@ -261,7 +263,7 @@ def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_s
         ctypes.byref(d), io, _ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)),
         float(dt_limit[0]), float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
         _ptr(seq_lens), _ptr(state_cache), rows, _ptr(state_indices), int(bool(init_from_cache)),
-        _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
+        int(bool(strict)), _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_cached")
     return y

@@ -29,12 +29,15 @@ struct Plan {
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-Plan make_plan(const ssd_dims& d, ssd_dtype io) {
+// one_segment: every row in one segment whatever the batch, so that a row's
+// bits do not depend on the batch it is in (the strict mode's split; the scan
+// then also takes the exact intra-chunk decay form in every chunk).
+Plan make_plan(const ssd_dims& d, ssd_dtype io, bool one_segment = false) {
     Plan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
     p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
     const int64_t bh = d.batch * d.nheads;
-    int64_t nseg = (kTargetWorkgroups + bh - 1) / bh;
+    int64_t nseg = one_segment ? 1 : (kTargetWorkgroups + bh - 1) / bh;
     if (nseg < 1) nseg = 1;
     if (nseg > p.nc) nseg = p.nc;
     p.cps = (p.nc + nseg - 1) / nseg;
@@ -230,7 +233,8 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
                          const float* A, const void* B, const void* C, const float* D,
                          const float* initial_states, const int32_t* seq_idx,
                          const int32_t* row_len, void* y, float* final_states, void* workspace,
-                         size_t workspace_bytes, hipStream_t hs, int& k, F&& before) {
+                         size_t workspace_bytes, hipStream_t hs, int& k, F&& before,
+                         bool one_segment = false) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
     if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
@@ -238,7 +242,7 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
                   N = d->dstate, G = d->ngroups;
     const bool work = b > 0 && L > 0;
     if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
-    const Plan plan = make_plan(*d, io);
+    const Plan plan = make_plan(*d, io, one_segment);
     if (plan.total > 0 &&
         (!workspace || workspace_bytes < plan.total ||
          (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
@@ -294,6 +298,7 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     sa.dt_max = dt_max;
     sa.seq_idx = seq_idx;
     sa.row_len = row_len;
+    sa.exact_decay = one_segment ? 1 : 0;
     sa.D = D;
     sa.init = initial_states;
     sa.final_states = final_states;
@@ -367,8 +372,9 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
                                      float dt_min, float dt_max, const float* A, const void* B,
                                      const void* C, const float* D, const int32_t* seq_lens,
                                      float* state_cache, int64_t cache_rows,
-                                     const int32_t* state_indices, int init_from_cache, void* y,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     const int32_t* state_indices, int init_from_cache, int strict,
+                                     void* y, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
@@ -400,8 +406,7 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
         if (b > 0 && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
         return SSD_OK;
     }
-    const Plan plan = make_plan(*d, io);
-    const size_t scan_bytes = align_up(plan.total);
+    const size_t scan_bytes = align_up(make_plan(*d, io).total);
     float* states = reinterpret_cast<float*>(static_cast<char*>(workspace) + scan_bytes);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int64_t per_row = H * P * N;
@@ -414,7 +419,7 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
                                    init_from_cache ? state_cache : nullptr, state_indices,
                                    cache_rows, states, b, per_row, hs);
                            });
-                       });
+                       }, strict != 0);
     if (st != SSD_OK) return st;
     if (timed_launch(k, hs, [&] {
             return ssd::launch_scatter_slots(states, state_indices, cache_rows, state_cache, b,
@@ -576,7 +581,7 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
                                                                cache_rows, states, b, H * P * N,
                                                                hs);
                            });
-                       });
+                       }, true);
     if (st != SSD_OK) return st;
     if (timed_launch(k, hs, [&] { return ssd::launch_emul_finish(ea, b, hs); }) != hipSuccess)
         return SSD_ERR_HIP;

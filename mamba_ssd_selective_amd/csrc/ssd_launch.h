@@ -23,6 +23,10 @@ struct ScanArgs {
     // (b) or null: row b's tokens from row_len[b] on are padding (dt 0: they
     // leave the state as it is; their y rows are not meaningful)
     const int32_t* row_len;
+    // 1: every chunk takes the per-element exp(cs_i - cs_j) form of the
+    // intra-chunk decay (no factoring), so that a token's output does not
+    // depend on the tokens after it in its chunk (the strict mode)
+    int exact_decay;
     const float* D;         // (H) or null
     const float* init;      // (b, H, P, N) or null
     float* final_states;    // (b, H, P, N) or null

@@ -443,9 +443,11 @@ struct TrScan {
         }
         // factored when cs never rises over these tokens (every factor is then
         // at most dt_j, and r_i at most 1), the row block holds one sequence and
-        // decays by at most kDiagSpan (r_i >= e^-kDiagSpan); else the exact form
+        // decays by at most kDiagSpan (r_i >= e^-kDiagSpan), and the strict
+        // mode is off (the choice depends on the row block's later tokens);
+        // else the exact form
         const bool wfast = !__builtin_amdgcn_ballot_w64(rising) && (!kSeq || seq_m == seq_e) &&
-                           cs_m - cs_e <= kDiagSpan;
+                           cs_m - cs_e <= kDiagSpan && !a.exact_decay;
         float sc, fin = 1.0f, dr = Dh;
         if (wfast) {
             fin = decay_exp(cs_i - cs_m);  // r_i

@@ -221,8 +221,8 @@ def test_cached_prefill_workspace_and_rejections(lib):
         d = ssd._Dims(*dims)
         return lib.ssd_chunk_scan_fwd_cached(
             ctypes.byref(d), ssd.BF16, a["x"], a["dt"], None, 1, a["lo"], a["hi"], a["A"], a["B"],
-            a["C"], None, a["lens"], a["cache"], rows, a["idx"], 1, a["y"], a["ws"], a["ws_bytes"],
-            None)
+            a["C"], None, a["lens"], a["cache"], rows, a["idx"], 1, 0, a["y"], a["ws"],
+            a["ws_bytes"], None)
 
     assert call(idx=None) == NULL_ARG
     assert call(cache=None) == NULL_ARG

@@ -1,10 +1,10 @@
 """Chunk-emulating decode (ssd_decode_emulated through the C-ABI): decode
-tokens give bitwise the chunked prefill's outputs and chunk-start states, so
-the split of a sequence into prefill and decode steps changes no bit (RL-Kernel
-RFC "Nemotron-3-Nano-30B-A3B", section 1, operator family 1, and section 3,
-Figure 2, box [F2]).  The reference prefill runs one segment per row (rows x
-heads = 256), the split under which the chained state is the same
-computation; and the oracle checks the values."""
+tokens give bitwise the strict chunked prefill's outputs and chunk-start
+states, so the split of a sequence into prefill and decode steps changes no bit
+(RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section 1, operator family 1, and
+section 3, Figure 2, box [F2]).  The strict prefill runs each row as one
+segment and forms every intra-chunk decay per element; the oracle checks the
+values."""
 import numpy as np
 import pytest
 
@@ -38,16 +38,11 @@ class _Slots:
 
 
 def _full_prefill(p, L):
-    import torch
-    import mamba_ssd_selective_amd as ssd
+    """The strict prefill of every row's first L tokens: (y, final states)."""
     b = p["x"].shape[0]
-    assert ssd.segments(b, L, H, P, N, G, Q) == 1
-    bf = torch.bfloat16
-    y, fs = ssd.chunk_scan_fwd(_dev(p["x"][:, :L], bf), _dev(p["dt_raw"][:, :L]), _dev(p["A"]),
-                               _dev(p["B"][:, :L], bf), _dev(p["C"][:, :L], bf), chunk_size=Q,
-                               D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]), return_final_states=True)
-    torch.cuda.synchronize()
-    return _host(y), _host(fs)
+    s = _Slots(b)
+    y = _cached(p, list(range(b)), L, s, list(range(b)), True)
+    return y, _host(s.state)
 
 
 def _step(p, slots, toks, idx, pos):
@@ -83,7 +78,8 @@ def test_emulated_decode_bitwise_equals_prefill():
     ssd.chunk_scan_fwd_cached(_dev(p["x"][:, :L0], bf), _dev(p["dt_raw"][:, :L0]), _dev(p["A"]),
                               _dev(p["B"][:, :L0], bf), _dev(p["C"][:, :L0], bf), slots.state,
                               _dev(np.asarray(idx, dtype=np.int32)), chunk_size=Q,
-                              init_from_cache=False, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
+                              init_from_cache=False, strict=True, D=_dev(p["D"]),
+                              dt_bias=_dev(p["dt_bias"]))
     ys = []
     for t in range(L0, T):
         ys.append(_host(_step(p, slots, [t] * b, idx, [t % Q] * b)))
@@ -125,7 +121,7 @@ def test_emulated_decode_staggered_rows_and_padding():
     ssd.chunk_scan_fwd_cached(_dev(q["x"], bf), _dev(q["dt_raw"]), _dev(p["A"]), _dev(q["B"], bf),
                               _dev(q["C"], bf), slots.state, _dev(np.asarray(idx, dtype=np.int32)),
                               chunk_size=Q, seq_lens=_dev(lens), init_from_cache=False,
-                              D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
+                              strict=True, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
     got = {r: [] for r in range(b)}
     for k in range(steps):
         toks, ii, pp = [], [], []
@@ -146,3 +142,42 @@ def test_emulated_decode_staggered_rows_and_padding():
         assert got[r]
         for t, yv in got[r]:
             assert np.array_equal(yv, y_full[r, t]), (r, t)
+
+
+def _cached(p, rows_sel, L, slots, idx, strict, lens=None):
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    bf = torch.bfloat16
+    sel = lambda k: p[k][rows_sel, :L]
+    y = ssd.chunk_scan_fwd_cached(_dev(sel("x"), bf), _dev(sel("dt_raw")), _dev(p["A"]),
+                                  _dev(sel("B"), bf), _dev(sel("C"), bf), slots.state,
+                                  _dev(np.asarray(idx, dtype=np.int32)), chunk_size=Q,
+                                  seq_lens=None if lens is None else _dev(lens),
+                                  init_from_cache=False, strict=strict, D=_dev(p["D"]),
+                                  dt_bias=_dev(p["dt_bias"]))
+    torch.cuda.synchronize()
+    return _host(y)
+
+
+def test_strict_prefill_is_batch_invariant_and_decode_continues_it():
+    """Strict mode: a row alone and the same row inside a batch of three give
+    the same bits (the row is one segment either way), and one row's strict
+    prefill of 256 tokens continued by 40 emulated decode tokens equals its
+    strict prefill of 296 tokens bit for bit."""
+    import mamba_ssd_selective_amd as ssd
+    rng = np.random.default_rng(13)
+    T = 2 * Q + 40
+    p = workloads.random_problem(rng, 3, T, H, P, N, G, io="bf16", init=False)
+    assert ssd.segments(1, T, H, P, N, G, Q) > 1   # the default split of one row differs
+    s1, s3 = _Slots(1), _Slots(3)
+    y1 = _cached(p, [1], T, s1, [0], True)
+    y3 = _cached(p, [0, 1, 2], T, s3, [2, 0, 1], True)
+    assert np.array_equal(y1[0], y3[1])
+    assert np.array_equal(_host(s1.state)[0], _host(s3.state)[0])
+    # one row: prefill 256 tokens, then decode 40
+    s = _Slots(1)
+    _cached(p, [1], 2 * Q, s, [0], True)
+    for t in range(2 * Q, T):
+        yd = _host(_step({k: (p[k][1:2] if k in ("x", "dt_raw", "B", "C") else p[k]) for k in p},
+                         s, [t], [0], [t % Q]))
+        assert np.array_equal(yd[0], y1[0, t]), t
