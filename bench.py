@@ -25,8 +25,8 @@ oracle's gradients timed on the heads of one group; and a "mixer" object for
 the steps beside the scan (causal conv1d into the scan's x/B/C, gated group
 RMSNorm of its output) at the same shape; and a "cache" object for continuous
 batching on state caches (a 256-row decode step on slots of a 512-slot cache
-with its HBM roofline, and the prefill of 8 prompts of different lengths from
-and back into cache slots).
+with its HBM roofline, the prefill of 8 prompts of different lengths from and
+back into cache slots, and the strict chunk-emulating decode of 64 rows).
 """
 import argparse
 import ctypes
@@ -315,7 +315,8 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
     decode token for 256 rows whose fp32 states sit in slots of a 512-slot
     cache (the state update; HBM roofline against its compulsory bytes), and
     the prefill of 8 prompts of seeded lengths 512..2048 (rows of 2048 tokens)
-    from and back into the slots of a 16-slot cache (every dispatch timed).
+    from and back into the slots of a 16-slot cache (every dispatch timed); and
+    the strict chunk-emulating decode of 64 rows at offset 63 of their chunks.
     The oracle's decode step is timed on 16 of the rows."""
     import numpy as np
     H, P, N, G, Q = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
@@ -400,7 +401,8 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
     pre = lambda: lib.ssd_chunk_scan_fwd_cached(
         ctypes.byref(d), 1, px.data_ptr(), pdt.data_ptr(), bias.data_ptr(), 1, 0.0, math.inf,
         A.data_ptr(), pB.data_ptr(), pC.data_ptr(), D.data_ptr(), plens.data_ptr(),
-        pcache.data_ptr(), pslots, pidx.data_ptr(), 1, py.data_ptr(), ws.data_ptr(), need, stream())
+        pcache.data_ptr(), pslots, pidx.data_ptr(), 1, 0, py.data_ptr(), ws.data_ptr(), need,
+        stream())
     us_k, wall = timed(pre, len(names), max(steps // 2, 10))
     real = int(lens.sum())
     res["prefill"] = {"rows": b, "row_capacity": L, "real_tokens": real,
@@ -409,6 +411,32 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
                       "kernels_total_us": round(sum(us_k), 2),
                       "ms_per_call": round(1e3 * wall, 4),
                       "real_tokens_per_s": round(real / wall, 1)}
+    # ---- strict decode (chunk-emulating): 64 rows at offset 63 of their chunks
+    er, eslots, epos = 64, 64, 63
+    ecache = torch.randn((eslots, H, P, N), generator=gen).to(dev)
+    ech = (torch.randn((eslots, Q, H, P), generator=gen).to(bf).to(dev),
+           torch.randn((eslots, Q, H), generator=gen).to(dev),
+           torch.randn((eslots, Q, G, N), generator=gen).to(bf).to(dev),
+           torch.randn((eslots, Q, G, N), generator=gen).to(bf).to(dev))
+    eidx = torch.randperm(eslots, generator=gen).to(torch.int32).to(dev)
+    eposd = torch.full((er,), epos, dtype=torch.int32, device=dev)
+    ey = torch.empty((er, H, P), dtype=bf, device=dev)
+    ed = ssd._dims(er, Q, H, P, N, G, Q)
+    eneed = int(lib.ssd_decode_emulated_workspace_bytes(ctypes.byref(ed), 1))
+    ews = torch.empty(eneed, dtype=torch.uint8, device=dev)
+    ex, edt, eB, eC = x[:er], dt[:er], Bm[:er], Cm[:er]
+    emu = lambda: lib.ssd_decode_emulated(
+        ctypes.byref(ed), 1, ex.data_ptr(), edt.data_ptr(), bias.data_ptr(), 1, 0.0, math.inf,
+        A.data_ptr(), eB.data_ptr(), eC.data_ptr(), D.data_ptr(), ecache.data_ptr(),
+        ech[0].data_ptr(), ech[1].data_ptr(), ech[2].data_ptr(), ech[3].data_ptr(), eslots,
+        eidx.data_ptr(), eposd.data_ptr(), ey.data_ptr(), ews.data_ptr(), eneed, stream())
+    enames = ["stage", "gather", "chunk_prep", "chunk_output", "finish"]
+    eus, ewall = timed(emu, len(enames), max(steps // 2, 10))
+    res["strict_decode"] = {"rows": er, "slots": eslots, "offset_in_chunk": epos,
+                            "kernels_us": {n: round(u, 2) for n, u in zip(enames, eus)},
+                            "kernels_total_us": round(sum(eus), 2),
+                            "ms_per_call": round(1e3 * ewall, 4),
+                            "tokens_per_s": round(er / ewall, 1)}
     res["cpu_baseline"] = None
     if cpu_seconds > 0:
         import oracle

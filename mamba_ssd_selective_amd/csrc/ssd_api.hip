@@ -566,6 +566,17 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
     ea.wd = H;
     ea.wb = G * N * static_cast<int64_t>(es) / 4;
     ea.hpn = H * P * N;
+    // the staging copy in 16-byte words when every width and buffer allows
+    const int64_t xb = H * P * static_cast<int64_t>(es), gb = G * N * static_cast<int64_t>(es);
+    const void* stage_bufs[] = {x, dt, B, C, x_chunks, dt_chunks, b_chunks, c_chunks};
+    bool wide = xb % 16 == 0 && gb % 16 == 0 && (H * 4) % 16 == 0;
+    for (const void* p : stage_bufs) wide = wide && aligned16(p);
+    ssd::EmulArgs sa_stage = ea;
+    if (wide) {
+        sa_stage.wx = xb / 16;
+        sa_stage.wd = H * 4 / 16;
+        sa_stage.wb = gb / 16;
+    }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int k = 0;
     if (g_hooks.launched) *g_hooks.launched = 0;
@@ -573,7 +584,7 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
                        D, states, nullptr, ea.row_len, wsb + e.yw, states, wsb,
                        align_up(make_plan(*d, io).total), hs, k, [&] {
                            hipError_t he = timed_launch(k, hs, [&] {
-                               return ssd::launch_emul_stage(ea, b, hs);
+                               return ssd::launch_emul_stage(sa_stage, wide, b, hs);
                            });
                            if (he != hipSuccess) return he;
                            return timed_launch(k, hs, [&] {

@@ -246,7 +246,8 @@ struct EmulArgs {
     int Q;
     int64_t wx, wd, wb, hpn;
 };
-hipError_t launch_emul_stage(const EmulArgs& a, int64_t b, hipStream_t st);
+// wide: the stage copies 16-byte words (widths wx, wd, wb given in them)
+hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st);
 hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st);
 
 // Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros

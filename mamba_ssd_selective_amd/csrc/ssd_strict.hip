@@ -18,7 +18,7 @@
 //                       it) into batch-ordered scan inputs; row lengths i + 1;
 //   emul_finish_kernel  copies y at offset i out, and commits the final state
 //                       of a completed chunk to the slot.
-// Both move 4-byte words (bf16 pairs or fp32); widths are checked on the host.
+// They move 16-byte words where every width allows (else 4-byte words).
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -33,6 +33,9 @@ __device__ __forceinline__ bool emul_row(const EmulArgs& a, int64_t r, int64_t& 
     return s >= 0 && s < a.cache_rows && i >= 0 && i < a.Q;
 }
 
+// Word = uint4 when every width is a multiple of 16 bytes (the host then
+// passes the widths in 16-byte words), else uint32_t.
+template <typename Word>
 __global__ __launch_bounds__(kEmulThreads) void emul_stage_kernel(EmulArgs a) {
     const int64_t r = blockIdx.y;
     int64_t s;
@@ -48,35 +51,35 @@ __global__ __launch_bounds__(kEmulThreads) void emul_stage_kernel(EmulArgs a) {
          w += stride) {
         const int64_t j = w / W;
         int64_t o = w % W;
-        const uint32_t* tok;   // the new token's row
-        uint32_t* buf;         // the slot's chunk buffer, token 0
-        uint32_t* ws;          // the batch-ordered scan input, token 0
+        const Word* tok;   // the new token's row
+        Word* buf;         // the slot's chunk buffer, token 0
+        Word* ws;          // the batch-ordered scan input, token 0
         int64_t width;
         if (o < wx) {
-            tok = static_cast<const uint32_t*>(a.x) + r * wx;
-            buf = static_cast<uint32_t*>(a.x_buf);
-            ws = static_cast<uint32_t*>(a.xw);
+            tok = static_cast<const Word*>(a.x) + r * wx;
+            buf = static_cast<Word*>(a.x_buf);
+            ws = static_cast<Word*>(a.xw);
             width = wx;
         } else if ((o -= wx) < wd) {
-            tok = reinterpret_cast<const uint32_t*>(a.dt) + r * wd;
-            buf = reinterpret_cast<uint32_t*>(a.dt_buf);
-            ws = reinterpret_cast<uint32_t*>(a.dtw);
+            tok = reinterpret_cast<const Word*>(a.dt) + r * wd;
+            buf = reinterpret_cast<Word*>(a.dt_buf);
+            ws = reinterpret_cast<Word*>(a.dtw);
             width = wd;
         } else if ((o -= wd) < wb) {
-            tok = static_cast<const uint32_t*>(a.B) + r * wb;
-            buf = static_cast<uint32_t*>(a.b_buf);
-            ws = static_cast<uint32_t*>(a.bw);
+            tok = static_cast<const Word*>(a.B) + r * wb;
+            buf = static_cast<Word*>(a.b_buf);
+            ws = static_cast<Word*>(a.bw);
             width = wb;
         } else {
             o -= wb;
-            tok = static_cast<const uint32_t*>(a.C) + r * wb;
-            buf = static_cast<uint32_t*>(a.c_buf);
-            ws = static_cast<uint32_t*>(a.cw);
+            tok = static_cast<const Word*>(a.C) + r * wb;
+            buf = static_cast<Word*>(a.c_buf);
+            ws = static_cast<Word*>(a.cw);
             width = wb;
         }
-        uint32_t v = 0u;
+        Word v = Word{};
         if (live) {
-            uint32_t* slot = buf + (s * a.Q + j) * width + o;
+            Word* slot = buf + (s * a.Q + j) * width + o;
             if (j == i) {
                 v = tok[o];
                 *slot = v;
@@ -107,9 +110,11 @@ __global__ __launch_bounds__(kEmulThreads) void emul_finish_kernel(EmulArgs a) {
 
 }  // namespace
 
-hipError_t launch_emul_stage(const EmulArgs& a, int64_t b, hipStream_t st) {
+hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st) {
     if (b == 0) return hipSuccess;
-    return dispatch(emul_stage_kernel, dim3(64, static_cast<unsigned>(b)), dim3(kEmulThreads), st, a);
+    const dim3 grid(64, static_cast<unsigned>(b));
+    if (wide) return dispatch(emul_stage_kernel<uint4>, grid, dim3(kEmulThreads), st, a);
+    return dispatch(emul_stage_kernel<uint32_t>, grid, dim3(kEmulThreads), st, a);
 }
 
 hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st) {
