@@ -193,6 +193,33 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
                                const int32_t* state_indices, const int32_t* positions, void* y,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Packed variable-length prefill (RFC section 8, open question 4: cu_seqlens-
+ * aware chunking).  x (T, H, P), dt (T, H), B, C (T, G, N) hold nseq
+ * sequences back to back, sequence r at tokens [cu_seqlens[r],
+ * cu_seqlens[r+1]) (int32 on the device, nseq + 1 entries, non-decreasing
+ * from 0 to T).  Each sequence is chunked from its own first token and runs
+ * as one row of the cached prefill (ssd_chunk_scan_fwd_cached): it starts
+ * from slot state_indices[r] of state_cache (or zeros) and its final state is
+ * written back to that slot; strict as there.  y (T, H, P) receives every
+ * sequence's outputs in the packed layout.  dims: batch = nseq, seqlen =
+ * max_seqlen (no sequence longer; longer ones are cut to it, and offsets
+ * outside [0, T] are clamped, so that no access leaves the buffers).  The
+ * sequences are copied into rows of max_seqlen tokens in the workspace
+ * (ssd_chunk_scan_varlen_workspace_bytes), so the scan's work grows with
+ * nseq x max_seqlen.  Timing hooks see the cached prefill's dispatches; the
+ * packing copies around them are not bound to events.
+ */
+size_t ssd_chunk_scan_varlen_workspace_bytes(const ssd_dims* d, ssd_dtype io);
+ssd_status ssd_chunk_scan_fwd_varlen(const ssd_dims* d, int64_t total_tokens, ssd_dtype io,
+                                     const void* x, const float* dt, const float* dt_bias,
+                                     int dt_softplus, float dt_min, float dt_max, const float* A,
+                                     const void* B, const void* C, const float* D,
+                                     const int32_t* cu_seqlens, float* state_cache,
+                                     int64_t cache_rows, const int32_t* state_indices,
+                                     int init_from_cache, int strict, void* y, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace ssd_chunk_scan_bwd needs for these dims (0 when
  * none, and for dims it would reject). */
 size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* dims, ssd_dtype io);

@@ -89,6 +89,12 @@ def library():
                                                   vp, vp, vp, vp, vp, vp, i64, vp, i, i, vp, vp,
                                                   ctypes.c_size_t, vp]
         lib.ssd_chunk_scan_fwd_cached.restype = i
+        lib.ssd_chunk_scan_varlen_workspace_bytes.argtypes = [ctypes.POINTER(_Dims), i]
+        lib.ssd_chunk_scan_varlen_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_chunk_scan_fwd_varlen.argtypes = [ctypes.POINTER(_Dims), i64, i, vp, vp, vp, i, f,
+                                                  f, vp, vp, vp, vp, vp, vp, i64, vp, i, i, vp, vp,
+                                                  ctypes.c_size_t, vp]
+        lib.ssd_chunk_scan_fwd_varlen.restype = i
         lib.ssd_decode_emulated_workspace_bytes.argtypes = [ctypes.POINTER(_Dims), i]
         lib.ssd_decode_emulated_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_decode_emulated.argtypes = [ctypes.POINTER(_Dims), i, vp, vp, vp, i, f, f, vp, vp,
@@ -266,6 +272,52 @@ def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_s
         int(bool(strict)), _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_cached")
+    return y
+
+
+def chunk_scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, state_cache, state_indices, *,
+                          max_seqlen: int, chunk_size: int, init_from_cache: bool = True,
+                          strict: bool = False, D=None, dt_bias=None, dt_softplus: bool = True,
+                          dt_limit: Tuple[float, float] = (0.0, math.inf), out=None,
+                          workspace=None):
+    """Packed variable-length prefill: x (T, H, P), dt (T, H), B/C (T, G, N)
+    hold the sequences back to back at offsets ``cu_seqlens`` (nseq + 1,
+    int32); sequence r is chunked from its own start, begins at slot
+    state_indices[r] of ``state_cache`` (zeros unless ``init_from_cache``) and
+    leaves its final state there.  Returns y (T, H, P)."""
+    import torch
+    lib = library()
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    S = cu_seqlens.shape[0] - 1
+    dev = x.device
+    io = _io_code(x.dtype)
+    f32 = torch.float32
+    _check(x, "x", (T, H, P), x.dtype, dev)
+    _check(dt, "dt", (T, H), f32, dev)
+    _check(B, "B", (T, G, N), x.dtype, dev)
+    _check(C, "C", (T, G, N), x.dtype, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    rows = state_cache.shape[0]
+    _check(state_cache, "state_cache", (rows, H, P, N), f32, dev)
+    _check(state_indices, "state_indices", (S,), torch.int32, dev)
+    y = out if out is not None else torch.empty((T, H, P), dtype=x.dtype, device=dev)
+    _check(y, "out", (T, H, P), x.dtype, dev)
+    d = _dims(S, max_seqlen, H, P, N, G, chunk_size)
+    need = int(lib.ssd_chunk_scan_varlen_workspace_bytes(ctypes.byref(d), io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_fwd_varlen(
+        ctypes.byref(d), T, io, _ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(cu_seqlens), _ptr(state_cache), rows, _ptr(state_indices), int(bool(init_from_cache)),
+        int(bool(strict)), _ptr(y), _ptr(workspace), ws_bytes, _stream_handle(dev))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_varlen")
     return y
 
 

@@ -599,6 +599,99 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
     return SSD_OK;
 }
 
+size_t ssd_chunk_scan_varlen_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
+    if (check_scan_dims(d, io) != SSD_OK || d->batch == 0 || d->seqlen == 0) return 0;
+    const size_t es = io_size(io);
+    const size_t rows = static_cast<size_t>(d->batch * d->seqlen);
+    const size_t hp = static_cast<size_t>(d->nheads * d->headdim);
+    const size_t gn = static_cast<size_t>(d->ngroups * d->dstate);
+    return ssd_chunk_scan_cached_workspace_bytes(d, io) + align_up(rows * hp * es) +
+           align_up(rows * static_cast<size_t>(d->nheads) * 4) + 2 * align_up(rows * gn * es) +
+           align_up(rows * hp * es) + align_up(static_cast<size_t>(d->batch) * 4);
+}
+
+ssd_status ssd_chunk_scan_fwd_varlen(const ssd_dims* d, int64_t total_tokens, ssd_dtype io,
+                                     const void* x, const float* dt, const float* dt_bias,
+                                     int dt_softplus, float dt_min, float dt_max, const float* A,
+                                     const void* B, const void* C, const float* D,
+                                     const int32_t* cu_seqlens, float* state_cache,
+                                     int64_t cache_rows, const int32_t* state_indices,
+                                     int init_from_cache, int strict, void* y, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    ssd_status st = check_scan_dims(d, io);
+    if (st != SSD_OK) return st;
+    const int64_t S = d->batch, Lmax = d->seqlen, T = total_tokens, H = d->nheads,
+                  P = d->headdim, N = d->dstate, G = d->ngroups;
+    if (T < 0 || T > (int64_t(1) << 40) || S > 65535) return SSD_ERR_BAD_SHAPE;
+    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
+    if (S == 0 || Lmax == 0) return SSD_OK;
+    if (!cu_seqlens || !y || (T > 0 && (!x || !dt || !B || !C))) return SSD_ERR_NULL_ARG;
+    const size_t es = io_size(io);
+    const size_t need = ssd_chunk_scan_varlen_workspace_bytes(d, io);
+    if (!workspace || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return SSD_ERR_WORKSPACE;
+    const void* word_bufs[] = {x, dt, B, C, y};
+    for (const void* p : word_bufs)
+        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    const Span ys = span(y, T * H * P * es);
+    const Span ins[] = {span(x, T * H * P * es), span(dt, T * H * 4), span(B, T * G * N * es),
+                        span(C, T * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+                        span(D, D ? H * 4 : 0), span(cu_seqlens, (S + 1) * 4),
+                        span(state_indices, state_indices ? S * 4 : 0),
+                        span(state_cache, state_cache ? cache_rows * H * P * N * 4 : 0),
+                        span(workspace, need)};
+    for (const Span& o : ins)
+        if (overlap(ys, o)) return SSD_ERR_ALIAS;
+    const Span cs = span(state_cache, state_cache ? cache_rows * H * P * N * 4 : 0);
+    for (size_t i = 0; i + 2 < sizeof(ins) / sizeof(ins[0]); ++i)
+        if (overlap(cs, ins[i])) return SSD_ERR_ALIAS;
+    if (overlap(cs, span(workspace, need))) return SSD_ERR_ALIAS;
+    // the rows and the cached prefill's workspace
+    const size_t rows = static_cast<size_t>(S * Lmax);
+    char* wsb = static_cast<char*>(workspace);
+    const size_t cws = ssd_chunk_scan_cached_workspace_bytes(d, io);
+    size_t off = cws;
+    ssd::VarlenArgs va{};
+    va.x = x;
+    va.dt = dt;
+    va.B = B;
+    va.C = C;
+    va.cu = cu_seqlens;
+    va.xw = wsb + off;
+    off += align_up(rows * H * P * es);
+    va.dtw = reinterpret_cast<float*>(wsb + off);
+    off += align_up(rows * H * 4);
+    va.bw = wsb + off;
+    off += align_up(rows * G * N * es);
+    va.cw = wsb + off;
+    off += align_up(rows * G * N * es);
+    void* yw = wsb + off;
+    va.yw = yw;
+    off += align_up(rows * H * P * es);
+    va.row_len = reinterpret_cast<int32_t*>(wsb + off);
+    va.y = y;
+    va.nseq = S;
+    va.T = T;
+    va.Lmax = Lmax;
+    const int64_t xb = H * P * static_cast<int64_t>(es), gb = G * N * static_cast<int64_t>(es);
+    const bool wide = xb % 16 == 0 && gb % 16 == 0 && (H * 4) % 16 == 0;
+    const int64_t word = wide ? 16 : 4;
+    if (xb % 4 != 0 || gb % 4 != 0) return SSD_ERR_UNSUPPORTED;
+    va.wx = xb / word;
+    va.wd = H * 4 / word;
+    va.wb = gb / word;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (ssd::launch_varlen_pack(va, wide, hs) != hipSuccess) return SSD_ERR_HIP;
+    st = ssd_chunk_scan_fwd_cached(d, io, va.xw, va.dtw, dt_bias, dt_softplus, dt_min, dt_max, A,
+                                   va.bw, va.cw, D, va.row_len, state_cache, cache_rows,
+                                   state_indices, init_from_cache, strict, yw, workspace, cws,
+                                   stream);
+    if (st != SSD_OK) return st;
+    if (ssd::launch_varlen_unpack(va, wide, hs) != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
     if (check_bwd_dims(d, io) != SSD_OK) return 0;
     return make_bwd_plan(*d).total;

@@ -250,6 +250,28 @@ struct EmulArgs {
 hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st);
 hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st);
 
+// Packed variable-length prefill: packed tokens (T of them, cu_seqlens
+// offsets) <-> one row of Lmax tokens per sequence.  Widths in words (4 or 16
+// bytes): wx = H*P*io, wd = H*4, wb = G*N*io bytes per token.
+struct VarlenArgs {
+    const void* x;            // (T, H, P) io
+    const float* dt;          // (T, H)
+    const void* B;            // (T, G, N) io
+    const void* C;            // (T, G, N) io
+    const int32_t* cu;        // (nseq + 1)
+    void* xw;                 // (nseq, Lmax, H, P) io
+    float* dtw;               // (nseq, Lmax, H)
+    void* bw;                 // (nseq, Lmax, G, N) io
+    void* cw;                 // (nseq, Lmax, G, N) io
+    int32_t* row_len;         // (nseq)
+    const void* yw;           // (nseq, Lmax, H, P) io
+    void* y;                  // (T, H, P) io
+    int64_t nseq, T, Lmax;
+    int64_t wx, wd, wb;
+};
+hipError_t launch_varlen_pack(const VarlenArgs& a, bool wide, hipStream_t st);
+hipError_t launch_varlen_unpack(const VarlenArgs& a, bool wide, hipStream_t st);
+
 // Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros
 // for an index outside [0, rows) or when cache is null); scatter row r to slot
 // idx[r] (rows whose index is outside are skipped).  per_row % 4 == 0.

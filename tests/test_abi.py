@@ -280,6 +280,37 @@ def test_emulated_decode_workspace_and_rejections(lib):
     assert call(dims=(0, 128, 64, 64, 128, 8, 128), x=None, xc=None) == OK
 
 
+def test_varlen_prefill_workspace_and_rejections(lib):
+    d = ssd._Dims(3, 300, 8, 64, 128, 2, 128)
+    need = lib.ssd_chunk_scan_varlen_workspace_bytes(ctypes.byref(d), ssd.BF16)
+    rows = 3 * 300
+    al = lambda v: (v + 255) // 256 * 256
+    extra = al(rows * 512 * 2) + al(rows * 8 * 4) + 2 * al(rows * 256 * 2) + al(rows * 512 * 2) + al(12)
+    assert need == ssd.cached_workspace_bytes(3, 300, 8, 64, 128, 2, 128) + extra
+    buf = _Buf()
+
+    def call(dims=(3, 300, 8, 64, 128, 2, 128), T=500, **over):
+        a = dict(x=buf(), dt=buf(), A=buf(), B=buf(), C=buf(), cu=buf(), st=buf(1 << 26), idx=buf(),
+                 y=buf(), ws=buf(1 << 26), ws_bytes=1 << 26)
+        a.update(over)
+        return lib.ssd_chunk_scan_fwd_varlen(
+            ctypes.byref(ssd._Dims(*dims)), T, ssd.BF16, a["x"], a["dt"], None, 1, 0.0, math.inf,
+            a["A"], a["B"], a["C"], None, a["cu"], a["st"], 16, a["idx"], 1, 0, a["y"], a["ws"],
+            a["ws_bytes"], None)
+
+    assert call(T=-1) == BAD_SHAPE
+    assert call(cu=None) == NULL_ARG
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=1 << 20) == WORKSPACE
+    assert call(x=0x70000008) == BAD_ARG
+    assert call(dims=(3, 300, 8, 64, 96, 2, 128)) == UNSUPPORTED
+    x = buf()
+    assert call(x=x, y=x + 4096) == ALIAS
+    s = buf(1 << 26)
+    assert call(st=s, dt=s + 64) == ALIAS
+    assert call(dims=(0, 300, 8, 64, 128, 2, 128)) == OK
+
+
 # ---------------------------------------------------------- gradients, mixer
 
 

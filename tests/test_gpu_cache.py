@@ -299,3 +299,81 @@ def test_prefill_then_decode_on_cache():
         dec = np.stack([ys[k][r] for k in range(T)])
         assert oracle.rel_l2(dec, yr[0, lens[r]:n]) < 2e-2, r
         assert oracle.rel_l2(got[idx[r]], hr[0]) < 2e-2, r
+
+
+def _varlen_case(seed, lens, H, G, io, rows):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    p = workloads.random_problem(rng, 1, T, H, 64, 128, G, io=io, init=False)
+    p = {k: (v[0] if k in ("x", "dt_raw", "B", "C") else v) for k, v in p.items()}
+    p["cache"] = rng.standard_normal((rows, H, 64, 128)).astype(np.float32)
+    p["cu"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return p
+
+
+@pytest.mark.parametrize("io,Q", [("bf16", 128), ("f32", 64)])
+def test_varlen_packed_sequences(io, Q):
+    """Five packed sequences of 300, 1, 128, 0 and 77 tokens: each one's y
+    and final slot equal the oracle's scan of that sequence from its slot's
+    state; the slots of no sequence are untouched."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    lens = [300, 1, 128, 0, 77]
+    H, G, rows = 8, 2, 9
+    p = _varlen_case(17, lens, H, G, io, rows)
+    idx = np.array([6, 0, 3, 8, 1], dtype=np.int32)
+    t = torch.bfloat16 if io == "bf16" else torch.float32
+    c = _dev(p["cache"])
+    y = ssd.chunk_scan_fwd_varlen(_dev(p["x"], t), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], t),
+                                  _dev(p["C"], t), _dev(p["cu"]), c, _dev(idx), max_seqlen=max(lens),
+                                  chunk_size=Q, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
+    torch.cuda.synchronize()
+    y, c = _host(y), _host(c)
+    tol = 1e-4 if io == "f32" else 2e-2
+    for r, n in enumerate(lens):
+        s, a = idx[r], p["cu"][r]
+        if n == 0:
+            assert np.array_equal(c[s], p["cache"][s])
+            continue
+        yr, hr = oracle.scan(p["x"][None, a:a + n], p["dt_raw"][None, a:a + n], p["A"],
+                             p["B"][None, a:a + n], p["C"][None, a:a + n], dt_bias=p["dt_bias"],
+                             D=p["D"], h_init=p["cache"][s][None])
+        assert oracle.rel_l2(y[a:a + n], yr[0]) < tol, r
+        assert oracle.rel_l2(c[s], hr[0]) < tol, r
+    untouched = [s for s in range(rows) if s not in idx]
+    assert np.array_equal(c[untouched], p["cache"][untouched])
+
+
+def test_varlen_equals_cached_rows_bitwise():
+    """The packed prefill gives the bits of the cached prefill on the same
+    sequences laid out as padded rows (strict mode, so that the split is the
+    same)."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    lens = [700, 129, 1000, 64]
+    H, G, rows = 16, 2, 4
+    p = _varlen_case(23, lens, H, G, "bf16", rows)
+    idx = np.array([2, 3, 0, 1], dtype=np.int32)
+    bf = torch.bfloat16
+    Lm = max(lens)
+    c1 = _dev(p["cache"])
+    y = ssd.chunk_scan_fwd_varlen(_dev(p["x"], bf), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], bf),
+                                  _dev(p["C"], bf), _dev(p["cu"]), c1, _dev(idx), max_seqlen=Lm,
+                                  chunk_size=128, strict=True, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
+    rowsd = {}
+    for k in ("x", "dt_raw", "B", "C"):
+        a = np.zeros((len(lens), Lm) + p[k].shape[1:], dtype=p[k].dtype)
+        for r, n in enumerate(lens):
+            a[r, :n] = p[k][p["cu"][r]:p["cu"][r] + n]
+        rowsd[k] = a
+    c2 = _dev(p["cache"])
+    y2 = ssd.chunk_scan_fwd_cached(_dev(rowsd["x"], bf), _dev(rowsd["dt_raw"]), _dev(p["A"]),
+                                   _dev(rowsd["B"], bf), _dev(rowsd["C"], bf), c2, _dev(idx),
+                                   chunk_size=128, seq_lens=_dev(np.array(lens, dtype=np.int32)),
+                                   strict=True, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
+    torch.cuda.synchronize()
+    y, y2 = _host(y), _host(y2)
+    for r, n in enumerate(lens):
+        a = p["cu"][r]
+        assert np.array_equal(y[a:a + n], y2[r, :n]), r
+    assert np.array_equal(_host(c1), _host(c2))
