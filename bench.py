@@ -26,7 +26,8 @@ the steps beside the scan (causal conv1d into the scan's x/B/C, gated group
 RMSNorm of its output) at the same shape; and a "cache" object for continuous
 batching on state caches (a 256-row decode step on slots of a 512-slot cache
 with its HBM roofline, the prefill of 8 prompts of different lengths from and
-back into cache slots, and the strict chunk-emulating decode of 64 rows).
+back into cache slots, the same prompts packed back to back (cu_seqlens), and the
+strict chunk-emulating decode of 64 rows).
 """
 import argparse
 import ctypes
@@ -405,6 +406,34 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
         stream())
     us_k, wall = timed(pre, len(names), max(steps // 2, 10))
     real = int(lens.sum())
+    # the same prompts packed back to back (cu_seqlens)
+    cu = torch.zeros(b + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0)
+    vx = torch.cat([px[r, :int(lens[r])] for r in range(b)])
+    vdt = torch.cat([pdt[r, :int(lens[r])] for r in range(b)])
+    vB = torch.cat([pB[r, :int(lens[r])] for r in range(b)])
+    vC = torch.cat([pC[r, :int(lens[r])] for r in range(b)])
+    vy = torch.empty_like(vx)
+    cud = cu.to(dev)
+    vneed = int(lib.ssd_chunk_scan_varlen_workspace_bytes(ctypes.byref(d), 1))
+    vws = torch.empty(vneed, dtype=torch.uint8, device=dev)
+    var = lambda: lib.ssd_chunk_scan_fwd_varlen(
+        ctypes.byref(d), real, 1, vx.data_ptr(), vdt.data_ptr(), bias.data_ptr(), 1, 0.0, math.inf,
+        A.data_ptr(), vB.data_ptr(), vC.data_ptr(), D.data_ptr(), cud.data_ptr(), pcache.data_ptr(),
+        pslots, pidx.data_ptr(), 1, 0, vy.data_ptr(), vws.data_ptr(), vneed, stream())
+    for _ in range(5):
+        if var() != 0:
+            raise RuntimeError("varlen prefill failed")
+    torch.cuda.synchronize()
+    nv = max(steps // 2, 10)
+    t0 = time.perf_counter()
+    for _ in range(nv):
+        var()
+    torch.cuda.synchronize()
+    vwall = (time.perf_counter() - t0) / nv
+    res["packed_prefill"] = {"sequences": b, "real_tokens": real, "max_seqlen": L,
+                             "ms_per_call": round(1e3 * vwall, 4),
+                             "real_tokens_per_s": round(real / vwall, 1)}
     res["prefill"] = {"rows": b, "row_capacity": L, "real_tokens": real,
                       "lengths": [int(v) for v in lens], "slots": pslots,
                       "kernels_us": {n: round(u, 2) for n, u in zip(names, us_k)},

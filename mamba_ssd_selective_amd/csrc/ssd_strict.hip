@@ -42,52 +42,49 @@ __global__ __launch_bounds__(kEmulThreads) void emul_stage_kernel(EmulArgs a) {
     int i;
     const bool live = emul_row(a, r, s, i);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.row_len[r] = live ? i + 1 : 0;
-    // per token: x words, dt words, B words, C words
-    const int64_t wx = a.wx, wd = a.wd, wb = a.wb;
-    const int64_t W = wx + wd + 2 * wb;
-    const int64_t total = static_cast<int64_t>(a.Q) * W;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kEmulThreads;
-    for (int64_t w = static_cast<int64_t>(blockIdx.x) * kEmulThreads + threadIdx.x; w < total;
-         w += stride) {
-        const int64_t j = w / W;
-        int64_t o = w % W;
-        const Word* tok;   // the new token's row
-        Word* buf;         // the slot's chunk buffer, token 0
-        Word* ws;          // the batch-ordered scan input, token 0
-        int64_t width;
-        if (o < wx) {
-            tok = static_cast<const Word*>(a.x) + r * wx;
-            buf = static_cast<Word*>(a.x_buf);
-            ws = static_cast<Word*>(a.xw);
-            width = wx;
-        } else if ((o -= wx) < wd) {
-            tok = reinterpret_cast<const Word*>(a.dt) + r * wd;
-            buf = reinterpret_cast<Word*>(a.dt_buf);
-            ws = reinterpret_cast<Word*>(a.dtw);
-            width = wd;
-        } else if ((o -= wd) < wb) {
-            tok = static_cast<const Word*>(a.B) + r * wb;
-            buf = static_cast<Word*>(a.b_buf);
-            ws = static_cast<Word*>(a.bw);
-            width = wb;
-        } else {
-            o -= wb;
-            tok = static_cast<const Word*>(a.C) + r * wb;
-            buf = static_cast<Word*>(a.c_buf);
-            ws = static_cast<Word*>(a.cw);
-            width = wb;
-        }
-        Word v = Word{};
-        if (live) {
-            Word* slot = buf + (s * a.Q + j) * width + o;
-            if (j == i) {
-                v = tok[o];
-                *slot = v;
-            } else if (j < i) {
-                v = *slot;
+    // one token per block step, its words (x, dt, B, C) over the threads
+    const int wx = static_cast<int>(a.wx), wd = static_cast<int>(a.wd), wb = static_cast<int>(a.wb);
+    const int W = wx + wd + 2 * wb;
+    for (int j = blockIdx.x; j < a.Q; j += gridDim.x) {
+        for (int o = threadIdx.x; o < W; o += kEmulThreads) {
+            const Word* tok;   // the new token's row
+            Word* buf;         // the slot's chunk buffer, token 0
+            Word* ws;          // the batch-ordered scan input, token 0
+            int e = o, width;
+            if (e < wx) {
+                tok = static_cast<const Word*>(a.x) + r * wx;
+                buf = static_cast<Word*>(a.x_buf);
+                ws = static_cast<Word*>(a.xw);
+                width = wx;
+            } else if ((e -= wx) < wd) {
+                tok = reinterpret_cast<const Word*>(a.dt) + r * wd;
+                buf = reinterpret_cast<Word*>(a.dt_buf);
+                ws = reinterpret_cast<Word*>(a.dtw);
+                width = wd;
+            } else if ((e -= wd) < wb) {
+                tok = static_cast<const Word*>(a.B) + r * wb;
+                buf = static_cast<Word*>(a.b_buf);
+                ws = static_cast<Word*>(a.bw);
+                width = wb;
+            } else {
+                e -= wb;
+                tok = static_cast<const Word*>(a.C) + r * wb;
+                buf = static_cast<Word*>(a.c_buf);
+                ws = static_cast<Word*>(a.cw);
+                width = wb;
             }
+            Word v = Word{};
+            if (live) {
+                Word* slot = buf + (s * a.Q + j) * width + e;
+                if (j == i) {
+                    v = tok[e];
+                    *slot = v;
+                } else if (j < i) {
+                    v = *slot;
+                }
+            }
+            ws[(r * a.Q + j) * width + e] = v;
         }
-        ws[(r * a.Q + j) * width + o] = v;
     }
 }
 
@@ -112,7 +109,7 @@ __global__ __launch_bounds__(kEmulThreads) void emul_finish_kernel(EmulArgs a) {
 
 hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st) {
     if (b == 0) return hipSuccess;
-    const dim3 grid(64, static_cast<unsigned>(b));
+    const dim3 grid(static_cast<unsigned>(a.Q), static_cast<unsigned>(b));
     if (wide) return dispatch(emul_stage_kernel<uint4>, grid, dim3(kEmulThreads), st, a);
     return dispatch(emul_stage_kernel<uint32_t>, grid, dim3(kEmulThreads), st, a);
 }

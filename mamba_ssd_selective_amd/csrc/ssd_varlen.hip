@@ -36,38 +36,38 @@ __global__ __launch_bounds__(kVarThreads) void varlen_pack_kernel(VarlenArgs a) 
     int64_t off, len;
     varlen_row(a, r, off, len);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.row_len[r] = static_cast<int32_t>(len);
-    const int64_t wx = a.wx, wd = a.wd, wb = a.wb;
-    const int64_t W = wx + wd + 2 * wb;
-    const int64_t total = a.Lmax * W;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kVarThreads;
-    for (int64_t w = static_cast<int64_t>(blockIdx.x) * kVarThreads + threadIdx.x; w < total;
-         w += stride) {
-        const int64_t j = w / W;
-        int64_t o = w % W;
-        const Word* src;
-        Word* dst;
-        int64_t width;
-        if (o < wx) {
-            src = static_cast<const Word*>(a.x);
-            dst = static_cast<Word*>(a.xw);
-            width = wx;
-        } else if ((o -= wx) < wd) {
-            src = reinterpret_cast<const Word*>(a.dt);
-            dst = reinterpret_cast<Word*>(a.dtw);
-            width = wd;
-        } else if ((o -= wd) < wb) {
-            src = static_cast<const Word*>(a.B);
-            dst = static_cast<Word*>(a.bw);
-            width = wb;
-        } else {
-            o -= wb;
-            src = static_cast<const Word*>(a.C);
-            dst = static_cast<Word*>(a.cw);
-            width = wb;
+    // one token per block step, its words over the threads (no division)
+    const int wx = static_cast<int>(a.wx), wd = static_cast<int>(a.wd), wb = static_cast<int>(a.wb);
+    const int W = wx + wd + 2 * wb;
+    for (int64_t j = blockIdx.x; j < a.Lmax; j += gridDim.x) {
+        const bool real = j < len;
+        const int64_t src_t = off + j, dst_t = r * a.Lmax + j;
+        for (int o = threadIdx.x; o < W; o += kVarThreads) {
+            const Word* src;
+            Word* dst;
+            int e = o, width;
+            if (e < wx) {
+                src = static_cast<const Word*>(a.x);
+                dst = static_cast<Word*>(a.xw);
+                width = wx;
+            } else if ((e -= wx) < wd) {
+                src = reinterpret_cast<const Word*>(a.dt);
+                dst = reinterpret_cast<Word*>(a.dtw);
+                width = wd;
+            } else if ((e -= wd) < wb) {
+                src = static_cast<const Word*>(a.B);
+                dst = static_cast<Word*>(a.bw);
+                width = wb;
+            } else {
+                e -= wb;
+                src = static_cast<const Word*>(a.C);
+                dst = static_cast<Word*>(a.cw);
+                width = wb;
+            }
+            Word v = Word{};
+            if (real) v = src[src_t * width + e];
+            dst[dst_t * width + e] = v;
         }
-        Word v = Word{};
-        if (j < len) v = src[(off + j) * width + o];
-        dst[(r * a.Lmax + j) * width + o] = v;
     }
 }
 
@@ -76,27 +76,26 @@ __global__ __launch_bounds__(kVarThreads) void varlen_unpack_kernel(VarlenArgs a
     const int64_t r = blockIdx.y;
     int64_t off, len;
     varlen_row(a, r, off, len);
-    const int64_t total = len * a.wx;
-    const Word* src = static_cast<const Word*>(a.yw) + r * a.Lmax * a.wx;
-    Word* dst = static_cast<Word*>(a.y) + off * a.wx;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kVarThreads;
-    for (int64_t w = static_cast<int64_t>(blockIdx.x) * kVarThreads + threadIdx.x; w < total;
-         w += stride)
-        dst[w] = src[w];
+    const int wx = static_cast<int>(a.wx);
+    for (int64_t j = blockIdx.x; j < len; j += gridDim.x) {
+        const Word* src = static_cast<const Word*>(a.yw) + (r * a.Lmax + j) * wx;
+        Word* dst = static_cast<Word*>(a.y) + (off + j) * wx;
+        for (int o = threadIdx.x; o < wx; o += kVarThreads) dst[o] = src[o];
+    }
 }
 
 }  // namespace
 
 hipError_t launch_varlen_pack(const VarlenArgs& a, bool wide, hipStream_t st) {
     if (a.nseq == 0) return hipSuccess;
-    const dim3 grid(64, static_cast<unsigned>(a.nseq));
+    const dim3 grid(static_cast<unsigned>(a.Lmax < 512 ? a.Lmax : 512), static_cast<unsigned>(a.nseq));
     if (wide) return dispatch(varlen_pack_kernel<uint4>, grid, dim3(kVarThreads), st, a);
     return dispatch(varlen_pack_kernel<uint32_t>, grid, dim3(kVarThreads), st, a);
 }
 
 hipError_t launch_varlen_unpack(const VarlenArgs& a, bool wide, hipStream_t st) {
     if (a.nseq == 0) return hipSuccess;
-    const dim3 grid(64, static_cast<unsigned>(a.nseq));
+    const dim3 grid(static_cast<unsigned>(a.Lmax < 512 ? a.Lmax : 512), static_cast<unsigned>(a.nseq));
     if (wide) return dispatch(varlen_unpack_kernel<uint4>, grid, dim3(kVarThreads), st, a);
     return dispatch(varlen_unpack_kernel<uint32_t>, grid, dim3(kVarThreads), st, a);
 }
