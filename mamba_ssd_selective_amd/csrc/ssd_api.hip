@@ -626,6 +626,12 @@ ssd_status ssd_chunk_scan_fwd_varlen(const ssd_dims* d, int64_t total_tokens, ss
     if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
     if (S == 0 || Lmax == 0) return SSD_OK;
     if (!cu_seqlens || !y || (T > 0 && (!x || !dt || !B || !C))) return SSD_ERR_NULL_ARG;
+    // the cached prefill's own checks that do not involve the rows, before the
+    // packing copy runs
+    if (!state_cache || !state_indices || !A) return SSD_ERR_NULL_ARG;
+    if (cache_rows < 0 || cache_rows >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
+    if (cache_rows > 0 && H * P * N > (int64_t(1) << 60) / 4 / cache_rows) return SSD_ERR_BAD_SHAPE;
+    if (!aligned16(state_cache)) return SSD_ERR_BAD_ARG;
     const size_t es = io_size(io);
     const size_t need = ssd_chunk_scan_varlen_workspace_bytes(d, io);
     if (!workspace || workspace_bytes < need ||

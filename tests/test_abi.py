@@ -300,6 +300,9 @@ def test_varlen_prefill_workspace_and_rejections(lib):
 
     assert call(T=-1) == BAD_SHAPE
     assert call(cu=None) == NULL_ARG
+    assert call(st=None) == NULL_ARG        # before the packing copy is launched
+    assert call(idx=None) == NULL_ARG
+    assert call(st=0x70000008) == BAD_ARG
     assert call(ws=None) == WORKSPACE
     assert call(ws_bytes=1 << 20) == WORKSPACE
     assert call(x=0x70000008) == BAD_ARG
