@@ -997,7 +997,14 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
             st[u] = make_float4(0.f, 0.f, 0.f, 0.f);
             xv[u] = 0.0f;
             if (p < p_end) {
-                st[u] = *reinterpret_cast<const float4*>(state + static_cast<int64_t>(p) * N + 4 * cc);
+                const float* sp = state + static_cast<int64_t>(p) * N + 4 * cc;
+                if constexpr (kSplit) {
+                    st[u] = *reinterpret_cast<const float4*>(sp);
+                } else {
+                    // large batches stream each state once: keep it out of the caches
+                    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(sp));
+                    st[u] = make_float4(v[0], v[1], v[2], v[3]);
+                }
                 xv[u] = Io<T>::to_f32(x[bh * a.P + p]);
             }
         }
@@ -1012,7 +1019,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
                 s.y = fmaf(dA, s.y, uu * bv[1]);
                 s.z = fmaf(dA, s.z, uu * bv[2]);
                 s.w = fmaf(dA, s.w, uu * bv[3]);
-                *reinterpret_cast<float4*>(state + static_cast<int64_t>(p) * N + 4 * cc) = s;
+                float* sp = state + static_cast<int64_t>(p) * N + 4 * cc;
+                if constexpr (kSplit) {
+                    *reinterpret_cast<float4*>(sp) = s;
+                } else {
+                    const f32x4_t v = {s.x, s.y, s.z, s.w};
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(sp));
+                }
                 part = s.x * cv[0] + s.y * cv[1] + s.z * cv[2] + s.w * cv[3];
             }
 #pragma unroll
