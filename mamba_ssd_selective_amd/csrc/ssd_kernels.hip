@@ -948,8 +948,9 @@ __global__ __launch_bounds__(256) void scatter_slots_kernel(const float* __restr
 // ===========================================================================
 // One decode token.  256 threads; N/4 lanes per state row (one float4 each),
 // so RP = 256/(N/4) rows per pass.  Two layouts of the grid:
-//  kSplit = false: one block per (row, head), looping over its P rows RP at a
-//    time (enough blocks in flight hide the latency: large batches);
+//  kSplit = false: one block per (row, head), looping over its P rows 4 RP at
+//    a time with the four passes' loads issued together, the state streamed
+//    with nontemporal loads and stores (large batches);
 //  kSplit = true: one block per (row, head) and 2 RP rows, whose loads are
 //    all issued before any arithmetic (few rows x heads: the latency of one
 //    block is the time of the step).
@@ -958,7 +959,7 @@ template <typename T, int N, bool kSplit>
 __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
     constexpr int TPR = N / 4;
     constexpr int RP = 256 / TPR;
-    constexpr int U = kSplit ? 2 : 1;  // passes whose loads are issued together
+    constexpr int U = kSplit ? 2 : 4;  // passes whose loads are issued together
     const int pblocks = kSplit ? (a.P + RP * U - 1) / (RP * U) : 1;
     const int64_t bh = blockIdx.x / pblocks;
     const int p_first = kSplit ? static_cast<int>(blockIdx.x % pblocks) * RP * U : 0;
