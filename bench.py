@@ -506,7 +506,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the SSD scan's data-parallel path "
+        print("bench.py: the library runs on one GPU only (the SSD scan's data-parallel path "
               "on one GPU's share); --gpus %d is not supported." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
