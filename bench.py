@@ -194,8 +194,9 @@ def backward_measure(ssd, lib, hip, torch, base, A, D, bias, w, steps, cpu_secon
     kus = {n: round(1e3 * float(np.mean([hip.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
                                         for i in range(diag)])), 2) for k, n in enumerate(names)}
     hip.destroy(evs)
-    # compulsory bytes: x, dy, B, C, dt in; dx, dB, dC, d(dt) out; the states in and out
-    per_token = 2 * (2 * H * P * 2 + 2 * G * N * 2 + H * 4)
+    # compulsory bytes: x, dy, B, C, dt in; dx, dB, dC, d(dt) out (three (b,L,H,P)
+    # bf16 tensors, four (b,L,G,N) ones, two fp32 dt-shaped ones); the states in and out
+    per_token = 3 * H * P * 2 + 4 * G * N * 2 + 2 * H * 4
     state_bytes = b * H * P * N * 4
     bwd_bytes = b * L * per_token + 3 * state_bytes + (b * L * 4 if base["seq"] is not None else 0)
     achieved = bwd_bytes / (grad_us * 1e-6) / 1e9

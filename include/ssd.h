@@ -138,7 +138,9 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* dims, ssd_dtype io, const void* x,
  * ssd_chunk_scan_fwd (no seq_idx: a row is one sequence).  The workspace
  * (ssd_chunk_scan_cached_workspace_bytes, 256-byte aligned) holds the scan's
  * and the gathered states.  Dispatch order: slot gather, the scan's kernels,
- * slot scatter.  strict != 0 runs every row as one segment of chunks whatever
+ * slot scatter.  L = 0 reads no input (x, dt, A, B, C and y may be NULL): a
+ * live row's slot is left as it is when init_from_cache != 0 and cleared to
+ * zeros otherwise (one scatter launch).  strict != 0 runs every row as one segment of chunks whatever
  * the batch, and forms every intra-chunk decay exp(cs_i - cs_j) per element
  * (RFC section 4.1: batch-invariant arithmetic): a row's outputs and state
  * are then bitwise the same in any batch, and the chunk-emulating decode

@@ -24,7 +24,7 @@ struct Plan {
     int64_t nseg = 1, cps = 1;
     size_t off_cs = 0, off_dtv = 0, off_wgt = 0, off_cbt = 0, off_cmf = 0;
     bool has_cmf = false;
-    size_t off_seg = 0, off_mult = 0, total = 0;
+    size_t off_seg = 0, off_mult = 0, off_final = 0, total = 0;
 };
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -66,6 +66,13 @@ Plan make_plan(const ssd_dims& d, ssd_dtype io, bool one_segment = false) {
         off = align_up(off + static_cast<size_t>(bh * p.nseg * d.headdim * d.dstate) * f);
         p.off_mult = off;
         off = align_up(off + static_cast<size_t>(bh * p.nseg) * f);
+        // where the final states go when the caller's final states are its
+        // initial states: every segment's workgroup reads the initial state,
+        // while the last segment's writes the final one, and with more
+        // workgroups than fit at once the two can meet.  bh < 256 here, so
+        // this area is below 256 states.
+        p.off_final = off;
+        off = align_up(off + static_cast<size_t>(bh * d.headdim * d.dstate) * f);
     }
     p.total = off;
     return p;
@@ -302,6 +309,10 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     sa.D = D;
     sa.init = initial_states;
     sa.final_states = final_states;
+    // final states written over the initial states they start from: to the
+    // workspace first, copied over the initial states once the scan is done
+    const bool final_in_ws = final_states && final_states == initial_states && plan.nseg > 1;
+    if (final_in_ws) sa.final_states = reinterpret_cast<float*>(wsb + plan.off_final);
     sa.seg_state = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_seg) : nullptr;
     sa.seg_mult = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_mult) : nullptr;
     sa.cs = reinterpret_cast<float*>(wsb + plan.off_cs);
@@ -339,6 +350,12 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     if (timed_launch(k, hs, [&] { return var->chunk_output(sa, b * plan.nseg * H, hs); }) !=
         hipSuccess)
         return SSD_ERR_HIP;
+    if (final_in_ws) {
+        if (timed_launch(k, hs, [&] {
+                return ssd::launch_copy_state(sa.final_states, final_states, b * H * P * N, hs);
+            }) != hipSuccess)
+            return SSD_ERR_HIP;
+    }
     return SSD_OK;
 }
 
@@ -402,8 +419,17 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
     int k = 0;
     if (g_hooks.launched) *g_hooks.launched = 0;
     if (b == 0 || L == 0) {
-        // nothing to scan: every state stays as it is
-        if (b > 0 && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
+        // nothing to scan (no input is read): a row that starts from its slot
+        // keeps it as it is; one that starts from zeros ends in zeros, written
+        // to its slot
+        if (b > 0 && !init_from_cache) {
+            hipStream_t hs0 = static_cast<hipStream_t>(stream);
+            if (timed_launch(k, hs0, [&] {
+                    return ssd::launch_scatter_slots(nullptr, state_indices, cache_rows, state_cache,
+                                                     b, H * P * N, hs0);
+                }) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
         return SSD_OK;
     }
     const size_t scan_bytes = align_up(make_plan(*d, io).total);

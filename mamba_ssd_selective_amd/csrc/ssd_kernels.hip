@@ -941,8 +941,9 @@ __global__ __launch_bounds__(256) void scatter_slots_kernel(const float* __restr
     const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
     const int64_t s = idx[r];
     if (i >= per_row || s < 0 || s >= rows) return;
+    // no source: the slot is cleared (a row of no tokens that starts from zeros)
     *reinterpret_cast<float4*>(cache + s * per_row + i) =
-        *reinterpret_cast<const float4*>(src + r * per_row + i);
+        src ? *reinterpret_cast<const float4*>(src + r * per_row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ===========================================================================

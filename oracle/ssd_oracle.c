@@ -20,9 +20,9 @@
  *
  * Sources (the pages that define the operation):
  *  - RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section 1, operator family 1:
- *    the Mamba-2 layer is a linear recurrence, computed as a chunked parallel
- *    scan in training and as a per-token recurrent state update in decode;
- *    operator family 2: a fixed-size FP32 SSM state per sequence.
+ *    the Mamba-2 layer's recurrence, evaluated chunk-parallel for prefill and
+ *    training and one token at a time for decode; operator family 2: each
+ *    sequence keeps an FP32 state of fixed size.
  *  - same RFC, section 3, Figure 2, box [F2]: softplus(dt + dt_bias),
  *    dt_limit, A = -exp(A_log) feed the SSD scan.
  *  - "Nemotron 3 Nano - JAX Implementation", Key Components, item 1
@@ -30,8 +30,9 @@
  *    groups of B/C shared by several heads, like GQA (Configuration,
  *    mamba_ngroups).
  *  - same RFC, section 2, "Reference-implementation hazards": the naive SSD
- *    path is checked by allclose against an FP64 re-run; section 7,
- *    "Oracles": never test a kernel against an oracle that shares its code.
+ *    path is compared, within a tolerance, with a double-precision rerun;
+ *    section 7, "Oracles": the reference a kernel is checked against must be
+ *    written separately from it.
  *
  * Layouts (row-major, contiguous):
  *   x (b,L,H,P)  dt_raw (b,L,H)  B,C (b,L,G,N)  y (b,L,H,P)

@@ -58,12 +58,15 @@ def test_workspace_and_segments(lib):
     # (lower-triangular 16x16 bf16 tiles in 20 pairs of 64 lanes x 8 elements
     # per row, chunk, group), the C rows in the output kernel's operand order
     # (bf16 Q x N per row, chunk, group), segment states (fp32 P x N per row,
-    # head, segment) and segment multipliers
+    # head, segment) and segment multipliers, and room for the final states
+    # (fp32 P x N per row, head) for calls whose final states overwrite their
+    # initial states
     meta = 3 * 64 * 8192 * 4
     tiles = 64 * 8 * 20 * 512 * 2
     cops = 64 * 8 * 128 * 128 * 2
     seg = 64 * 4 * 64 * 128 * 4 + 256 * math.ceil(64 * 4 * 4 / 256)
-    assert ws == meta + tiles + cops + seg
+    fin = 64 * 64 * 128 * 4
+    assert ws == meta + tiles + cops + seg + fin
     assert ssd.segments(1, 8192, 64, 64, 128, 8, 128) == 4
     # enough rows x heads: one segment, no segment scratch
     assert ssd.segments(64, 4096, 64, 64, 128, 8, 128) == 1

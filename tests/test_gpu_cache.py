@@ -377,3 +377,29 @@ def test_varlen_equals_cached_rows_bitwise():
         a = p["cu"][r]
         assert np.array_equal(y[a:a + n], y2[r, :n]), r
     assert np.array_equal(_host(c1), _host(c2))
+
+
+@pytest.mark.parametrize("init_from_cache", [False, True])
+def test_cached_prefill_of_no_tokens(init_from_cache):
+    """L = 0: a row that starts from zeros ends in zeros, written to its slot;
+    a row that starts from its slot leaves it as it is; padding rows and
+    other slots are untouched either way."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    b, H, P, N, G, Q, slots = 3, 4, 64, 128, 2, 128, 6
+    rng = np.random.default_rng(31)
+    cache = rng.standard_normal((slots, H, P, N)).astype(np.float32)
+    idx = np.array([4, -1, 1], dtype=np.int32)  # the middle row is padding
+    c = _dev(cache)
+    bf = torch.bfloat16
+    z = lambda *s: torch.zeros(s, dtype=bf, device="cuda:0")
+    f = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda:0")
+    ssd.chunk_scan_fwd_cached(z(b, 0, H, P), f(b, 0, H), f(H), z(b, 0, G, N), z(b, 0, G, N), c,
+                              _dev(idx), chunk_size=Q, init_from_cache=init_from_cache)
+    torch.cuda.synchronize()
+    got = c.cpu().numpy()
+    live = np.array([4, 1])
+    want = cache[live] if init_from_cache else np.zeros_like(cache[live])
+    assert np.array_equal(got[live], want)
+    others = np.setdiff1d(np.arange(slots), live)
+    assert np.array_equal(got[others], cache[others])
