@@ -20,7 +20,8 @@
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers to row-major, contiguous buffers.
  *    The caller owns all of them; the library allocates nothing and keeps no
- *    global buffers, so calls are re-entrant.
+ *    global buffers, so calls are re-entrant.  (One exception, on purpose:
+ *    ssd_chunk_scan_fwd_noalloc takes its scratch from a static device array.)
  *  - Arguments are validated on the host before anything is launched.  Any
  *    failure returns a non-zero ssd_status and leaves every output untouched
  *    (fail closed, RFC section 4.1 and section 7 "Fail closed"); there is no
@@ -52,7 +53,9 @@ typedef enum {
     SSD_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required          */
     SSD_ERR_BAD_ARG = 6,       /* dt_min > dt_max, NaN clamp bound, ...            */
     SSD_ERR_ALIAS = 7,         /* an output overlaps an input it must not overlap  */
-    SSD_ERR_HIP = 8            /* a HIP launch returned an error                   */
+    SSD_ERR_HIP = 8,           /* a HIP launch returned an error                   */
+    SSD_ERR_TOO_LARGE = 9      /* needs more scratch than the library's static
+                                  buffer holds (allocation-free entry point)       */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype; /* dtype of x, B, C and y */
@@ -118,6 +121,35 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* dims, ssd_dtype io, const void* x,
                               const void* C, const float* D, const float* initial_states,
                               const int32_t* seq_idx, void* y, float* final_states,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssd_chunk_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it).  Same arguments, same
+ * kernels and bitwise the same results as ssd_chunk_scan_fwd; the scratch
+ * the scan needs comes from a static device array of the library
+ * (SSD_NOALLOC_SCRATCH_BYTES per GPU, held by every GPU the library runs on
+ * until the process ends).  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.
+ *  - Dims whose workspace (ssd_chunk_scan_workspace_bytes) exceeds
+ *    SSD_NOALLOC_SCRATCH_BYTES are rejected with SSD_ERR_TOO_LARGE before any
+ *    launch.
+ *  - The array's device address is looked up once per device, on the first
+ *    call made with that device current; `stream` must belong to the current
+ *    device.  A failed lookup returns SSD_ERR_HIP.
+ *  - Every call on one GPU shares that GPU's array, and the scan writes each
+ *    scratch word before reading it (nothing needs to start at zero).  Calls
+ *    that overlap in time on one GPU (different streams, or host threads
+ *    without ordering between them) race on the array and give wrong
+ *    results: serialise them, for example on one stream.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_dims* dims, ssd_dtype io, const void* x,
+                                      const float* dt, const float* dt_bias, int dt_softplus,
+                                      float dt_min, float dt_max, const float* A,
+                                      const void* B, const void* C, const float* D,
+                                      const float* initial_states, const int32_t* seq_idx,
+                                      void* y, float* final_states, void* stream);
 
 /*
  * The forward scan of a batch of prompts whose states live in a state cache

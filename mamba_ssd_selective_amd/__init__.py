@@ -72,6 +72,9 @@ def library():
         lib.ssd_chunk_scan_fwd.argtypes = [dims_p, i, vp, vp, vp, i, f, f, vp, vp, vp, vp, vp,
                                            vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.ssd_chunk_scan_fwd.restype = i
+        lib.ssd_chunk_scan_fwd_noalloc.argtypes = [dims_p, i, vp, vp, vp, i, f, f, vp, vp, vp, vp,
+                                                   vp, vp, vp, vp, vp]
+        lib.ssd_chunk_scan_fwd_noalloc.restype = i
         lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [dims_p, i]
         lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_chunk_scan_bwd.argtypes = [dims_p, i, vp, vp, vp, i, f, f, vp, vp, vp, vp, vp, vp,

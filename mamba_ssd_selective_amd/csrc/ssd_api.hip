@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ssd.h"
 #include "ssd_launch.h"
 
@@ -207,6 +209,7 @@ const char* ssd_status_string(int s) {
         case SSD_ERR_BAD_ARG: return "invalid argument (dt clamp bounds, or a buffer not 16-byte aligned)";
         case SSD_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
         case SSD_ERR_HIP: return "a HIP kernel launch failed";
+        case SSD_ERR_TOO_LARGE: return "needs more scratch than the allocation-free entry point's static buffer holds";
         default: return "unknown ssd_status";
     }
 }
@@ -375,6 +378,58 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
                          initial_states, seq_idx, nullptr, y, final_states, workspace,
                          workspace_bytes, static_cast<hipStream_t>(stream), k,
                          [] { return hipSuccess; });
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of ssd_chunk_scan_fwd_noalloc: one copy per GPU, for the life of
+// the process.  In host code `noalloc_scratch` names a host-side stand-in, not
+// device memory: only the address that hipGetSymbolAddress returns for the
+// current device is ever passed to a kernel.
+__device__ __align__(256) char noalloc_scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of noalloc_scratch (looked up on its first
+// use, with that device current), or null on failure.
+void* noalloc_scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_dims* d, ssd_dtype io, const void* x,
+                                      const float* dt, const float* dt_bias, int dt_softplus,
+                                      float dt_min, float dt_max, const float* A, const void* B,
+                                      const void* C, const float* D, const float* initial_states,
+                                      const int32_t* seq_idx, void* y, float* final_states,
+                                      void* stream) {
+    ssd_status st = check_scan_dims(d, io);
+    if (st != SSD_OK) return st;
+    const size_t need = make_plan(*d, io).total;
+    if (need > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = noalloc_scratch_ptr();
+        if (!ws) return SSD_ERR_HIP;
+    }
+    return ssd_chunk_scan_fwd(d, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D,
+                              initial_states, seq_idx, y, final_states, ws,
+                              need > 0 ? SSD_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t ssd_chunk_scan_cached_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
