@@ -22,6 +22,7 @@ constexpr int64_t kTargetWorkgroups = 256;
 constexpr size_t kAlign = 256;
 
 struct Plan {
+    int64_t Qk = 0;  // chunk size the kernels run with
     int64_t nc = 0;
     int64_t nseg = 1, cps = 1;
     size_t off_cs = 0, off_dtv = 0, off_wgt = 0, off_cbt = 0, off_cmf = 0;
@@ -34,10 +35,17 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // one_segment: every row in one segment whatever the batch, so that a row's
 // bits do not depend on the batch it is in (the strict mode's split; the scan
 // then also takes the exact intra-chunk decay form in every chunk).
+// The plan follows the variant that serves the call (strict calls: one that
+// runs the caller's chunk size; others may run a divisor of it), and is laid
+// out for the chunk size its kernels run with (Qk).
 Plan make_plan(const ssd_dims& d, ssd_dtype io, bool one_segment = false) {
     Plan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
-    p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
+    const ssd::ScanVariant* var =
+        ssd::find_scan_variant(io, d.headdim, d.dstate, d.chunk_size, one_segment);
+    const int64_t Qk = var ? var->kernel_Q : d.chunk_size;
+    p.Qk = Qk;
+    p.nc = (d.seqlen + Qk - 1) / Qk;
     const int64_t bh = d.batch * d.nheads;
     int64_t nseg = one_segment ? 1 : (kTargetWorkgroups + bh - 1) / bh;
     if (nseg < 1) nseg = 1;
@@ -47,21 +55,20 @@ Plan make_plan(const ssd_dims& d, ssd_dtype io, bool one_segment = false) {
     const size_t f = sizeof(float);
     const size_t es = io == SSD_BF16 ? 2 : 4;
     // per-token metadata, one block [cs Q | dt Q | w Q] per (row, head, chunk)
-    const size_t meta = static_cast<size_t>(bh * p.nc * d.chunk_size) * 3 * f;
+    const size_t meta = static_cast<size_t>(bh * p.nc * Qk) * 3 * f;
     size_t off = 0;
     p.off_cs = off;
-    p.off_dtv = off + static_cast<size_t>(d.chunk_size) * f;
-    p.off_wgt = off + 2 * static_cast<size_t>(d.chunk_size) * f;
+    p.off_dtv = off + static_cast<size_t>(Qk) * f;
+    p.off_wgt = off + 2 * static_cast<size_t>(Qk) * f;
     off = align_up(off + meta);
     p.off_cbt = off;
     off = align_up(off + static_cast<size_t>(d.batch * p.nc * d.ngroups) *
-                             static_cast<size_t>(ssd::cbt_elems_per_chunk_group(d.chunk_size)) * es);
-    const ssd::ScanVariant* var = ssd::find_scan_variant(io, d.headdim, d.dstate, d.chunk_size);
+                             static_cast<size_t>(ssd::cbt_elems_per_chunk_group(Qk)) * es);
     if (var != nullptr && var->output_reads_c_copy) {
         p.has_cmf = true;
         p.off_cmf = off;
         off = align_up(off + static_cast<size_t>(d.batch * p.nc * d.ngroups) *
-                                 static_cast<size_t>(d.chunk_size * d.dstate) * es);
+                                 static_cast<size_t>(Qk * d.dstate) * es);
     }
     if (p.nseg > 1) {
         p.off_seg = off;
@@ -81,6 +88,13 @@ Plan make_plan(const ssd_dims& d, ssd_dtype io, bool one_segment = false) {
 }
 
 size_t io_size(ssd_dtype io) { return io == SSD_BF16 ? 2 : 4; }
+
+// Workspace of a scan that may run in either mode (the strict flag is a
+// call argument): the larger of the two plans.
+size_t plan_bytes_any_mode(const ssd_dims& d, ssd_dtype io) {
+    const size_t a = make_plan(d, io, false).total, b = make_plan(d, io, true).total;
+    return a > b ? a : b;
+}
 
 struct Span {
     uintptr_t lo, hi;  // [lo, hi)
@@ -247,6 +261,8 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
                          bool one_segment = false) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
+    if (one_segment && !ssd::find_scan_variant(io, d->headdim, d->dstate, d->chunk_size, true))
+        return SSD_ERR_UNSUPPORTED;
     if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim,
                   N = d->dstate, G = d->ngroups;
@@ -292,7 +308,7 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
         }
         return SSD_OK;
     }
-    const ssd::ScanVariant* var = ssd::find_scan_variant(io, P, N, d->chunk_size);
+    const ssd::ScanVariant* var = ssd::find_scan_variant(io, P, N, d->chunk_size, one_segment);
     char* wsb = static_cast<char*>(workspace);
 
     ssd::ScanArgs sa{};
@@ -435,7 +451,7 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_dims* d, ssd_dtype io, const voi
 size_t ssd_chunk_scan_cached_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
     if (check_scan_dims(d, io) != SSD_OK) return 0;
     if (d->batch == 0 || d->seqlen == 0) return 0;
-    return align_up(make_plan(*d, io).total) +
+    return align_up(plan_bytes_any_mode(*d, io)) +
            align_up(static_cast<size_t>(d->batch * d->nheads * d->headdim * d->dstate) * 4);
 }
 
@@ -487,7 +503,7 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
         }
         return SSD_OK;
     }
-    const size_t scan_bytes = align_up(make_plan(*d, io).total);
+    const size_t scan_bytes = align_up(plan_bytes_any_mode(*d, io));
     float* states = reinterpret_cast<float*>(static_cast<char*>(workspace) + scan_bytes);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int64_t per_row = H * P * N;
@@ -526,7 +542,7 @@ EmulPlan make_emul_plan(const ssd_dims& d, ssd_dtype io) {
     const size_t b = static_cast<size_t>(d.batch), Q = static_cast<size_t>(d.chunk_size);
     const size_t HP = static_cast<size_t>(d.nheads * d.headdim);
     const size_t GN = static_cast<size_t>(d.ngroups * d.dstate);
-    size_t off = align_up(make_plan(d, io).total);
+    size_t off = align_up(make_plan(d, io, true).total);  // always strict
     e.scan = 0;
     e.states = off;
     off = align_up(off + b * HP * static_cast<size_t>(d.dstate) * 4);
@@ -663,7 +679,7 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
     if (g_hooks.launched) *g_hooks.launched = 0;
     st = scan_fwd_impl(d, io, ea.xw, ea.dtw, dt_bias, dt_softplus, dt_min, dt_max, A, ea.bw, ea.cw,
                        D, states, nullptr, ea.row_len, wsb + e.yw, states, wsb,
-                       align_up(make_plan(*d, io).total), hs, k, [&] {
+                       align_up(make_plan(*d, io, true).total), hs, k, [&] {
                            hipError_t he = timed_launch(k, hs, [&] {
                                return ssd::launch_emul_stage(sa_stage, wide, b, hs);
                            });

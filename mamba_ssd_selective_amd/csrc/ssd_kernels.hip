@@ -1094,30 +1094,46 @@ static hipError_t launch_state_update_t(const StepArgs& a, int64_t nblocks, hipS
 
 // The compiled (io, P, N, Q) set of the chunked scan.
 #define SSD_SCAN_VARIANT(IO, T, P, N, Q)                                    \
-    {IO, P, N, Q, &launch_chunk_prep_t<T, P, N, Q>,                         \
+    {IO, P, N, Q, Q, &launch_chunk_prep_t<T, P, N, Q>,                      \
      &launch_chunk_scan_t<T, P, N, Q, false>, &launch_chunk_scan_t<T, P, N, Q, true>, false, false},
+// the same kernels run at chunk QK < Q for a caller chunk of Q
+#define SSD_SCAN_VARIANT_BLOCKED(IO, T, P, N, Q, QK)                        \
+    {IO, P, N, Q, QK, &launch_chunk_prep_t<T, P, N, QK>,                    \
+     &launch_chunk_scan_t<T, P, N, QK, false>, &launch_chunk_scan_t<T, P, N, QK, true>, false, false},
 
 // bf16 shapes served by the transposing-read kernels of ssd_scan_tr.hip.
 #define SSD_SCAN_VARIANT_TR(P, N, Q)                                        \
-    {1, P, N, Q, &launch_chunk_prep_t<uint16_t, P, N, Q>,                   \
+    {1, P, N, Q, Q, &launch_chunk_prep_t<uint16_t, P, N, Q>,                \
      &scan_tr_state_##P##_##N##_##Q, &scan_tr_output_##P##_##N##_##Q, true, true},
+// ... at chunk QK < Q: their double-buffered tiles of a 256-token chunk
+// (x 32 KiB and B 64 KiB per buffer at N = 128) do not fit the 160 KiB of LDS
+#define SSD_SCAN_VARIANT_TR_BLOCKED(P, N, Q, QK)                            \
+    {1, P, N, Q, QK, &launch_chunk_prep_t<uint16_t, P, N, QK>,              \
+     &scan_tr_state_##P##_##N##_##QK, &scan_tr_output_##P##_##N##_##QK, true, true},
 
+// Non-strict lookups take the first match, strict ones the first with
+// kernel_Q == Q: blocked entries come before the native ones they stand in for.
 static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT(0, float, 16, 16, 32)
     SSD_SCAN_VARIANT(0, float, 16, 16, 64)
     SSD_SCAN_VARIANT(0, float, 16, 16, 128)
     SSD_SCAN_VARIANT(0, float, 64, 128, 64)
     SSD_SCAN_VARIANT(0, float, 64, 128, 128)
+    SSD_SCAN_VARIANT_BLOCKED(0, float, 64, 128, 256, 128)
     SSD_SCAN_VARIANT(1, uint16_t, 16, 16, 64)
+    SSD_SCAN_VARIANT_TR(64, 64, 64)
     SSD_SCAN_VARIANT_TR(64, 64, 128)
+    SSD_SCAN_VARIANT_TR_BLOCKED(64, 64, 256, 128)
     SSD_SCAN_VARIANT_TR(64, 128, 64)
     SSD_SCAN_VARIANT_TR(64, 128, 128)
+    SSD_SCAN_VARIANT_TR_BLOCKED(64, 128, 256, 128)
     SSD_SCAN_VARIANT(1, uint16_t, 64, 128, 256)
 };
 
-const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q) {
+const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q, bool strict) {
     for (const ScanVariant& v : kScanVariants)
-        if (v.io == io && v.P == P && v.N == N && v.Q == Q) return &v;
+        if (v.io == io && v.P == P && v.N == N && v.Q == Q && (!strict || v.kernel_Q == v.Q))
+            return &v;
     return nullptr;
 }
 

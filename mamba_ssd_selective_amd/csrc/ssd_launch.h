@@ -143,6 +143,12 @@ typedef hipError_t (*ScanLaunchFn)(const ScanArgs&, int64_t nblocks, hipStream_t
 struct ScanVariant {
     int io;  // 0 = fp32, 1 = bf16
     int P, N, Q;
+    // chunk size the kernels run with: Q itself, or a divisor of it whose
+    // kernels serve the caller's chunk grid (the chunked form is the same
+    // recurrence for any chunk size; only the rounding order differs).  Strict
+    // calls, whose bits are defined on the caller's chunk grid, take only
+    // variants with kernel_Q == Q.
+    int kernel_Q;
     ScanLaunchFn chunk_prep;    // dt transform, chunk cumsum, weights, C.B^T tiles
     ScanLaunchFn chunk_state;   // segment states
     ScanLaunchFn chunk_output;  // outputs with the carried state
@@ -174,10 +180,14 @@ hipError_t scan_tr_state_64_64_128(const ScanArgs& a, int64_t nblocks, hipStream
 hipError_t scan_tr_output_64_64_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
 hipError_t scan_tr_state_64_128_64(const ScanArgs& a, int64_t nblocks, hipStream_t st);
 hipError_t scan_tr_output_64_128_64(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_state_64_64_64(const ScanArgs& a, int64_t nblocks, hipStream_t st);
+hipError_t scan_tr_output_64_64_64(const ScanArgs& a, int64_t nblocks, hipStream_t st);
 hipError_t scan_tr_state_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
 hipError_t scan_tr_output_64_128_128(const ScanArgs& a, int64_t nblocks, hipStream_t st);
 
-const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q);
+// The variant serving (io, P, N, Q); strict: only one that runs the caller's
+// chunk size itself.  Null when there is none.
+const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q, bool strict = false);
 int scan_variant_count();
 const ScanVariant* scan_variant_at(int i);
 

@@ -823,6 +823,7 @@ hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
         return launch_scan_tr<P, N, Q, true>(a, nb, st);                                      \
     }
 
+SSD_SCAN_TR(64, 64, 64)
 SSD_SCAN_TR(64, 64, 128)
 SSD_SCAN_TR(64, 128, 64)
 SSD_SCAN_TR(64, 128, 128)

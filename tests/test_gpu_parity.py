@@ -62,6 +62,8 @@ FP32_CASES = [
     (1, 64, 4, 16, 16, 1, 64, True, False),
     (1, 65, 4, 16, 16, 1, 64, False, False),
     (2, 500, 4, 16, 16, 4, 128, True, True),
+    # chunk 256 run as two 128-token blocks by the chunk-128 kernels
+    (1, 700, 4, 64, 128, 2, 256, True, True),
 ]
 
 
@@ -82,6 +84,11 @@ BF16_CASES = [
     (1, 2000, 8, 64, 64, 2, 128, True, False),
     (2, 150, 4, 16, 16, 1, 64, True, True),
     (1, 129, 64, 64, 128, 8, 128, False, False),
+    # the JAX page's Configuration defaults (d_state 64, head dim 64, chunk 64)
+    (2, 333, 8, 64, 64, 2, 64, True, True),
+    (1, 1000, 64, 64, 64, 8, 64, True, False),
+    # chunk 256 at N = 64, run as two 128-token blocks
+    (1, 900, 8, 64, 64, 2, 256, True, True),
 ]
 
 
