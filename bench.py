@@ -4,15 +4,21 @@
 One step = one pass of the whole hot path over one batch of synthetic input:
 the chunked scan of the 30B-shaped prefill (b=1, L=8192, H=64, P=64, N=128,
 G=8, chunk 128, bf16 x/B/C, fp32 dt/A/D and state, final state returned;
-kernels chunk_prep, chunk_state, state_pass, chunk_output) followed by one
-decode token on the returned state (state_update).  Inputs are resident in
-HBM before timing starts; the step cycles over several copies of the inputs
-so that consecutive steps do not hit in the 256 MB MALL.
+kernels chunk_prep, chunk_state, chunk_output) followed by one decode token on
+the returned state (state_update).  Inputs are resident in HBM before timing
+starts; the step cycles over several copies of the inputs so that consecutive
+steps do not hit in the 256 MB MALL.
 
-Prints ONE JSON line with the throughput, a roofline entry for the dominant
-kernel (chunk_output, timed with HIP events that the library binds to its
-dispatch on the stream it launches on, so that they take the dispatch's own
-start and end timestamps) and the fp64 CPU oracle timed on the host cores.
+Prints ONE JSON line with the throughput (host clock over the timed steps),
+a roofline entry for the whole scan call (its compulsory bytes over the sum of
+its dispatches' durations, each timed by HIP events that the library binds to
+the dispatch on the stream it launches on, over the same number of steps right
+after the timed ones; the GPU time of the whole call between plain stream
+events, launch gaps included, is reported beside it), and the fp64 CPU oracle
+timed on the host cores.  A "workloads" object measures the other workloads
+the same way: 16 packed sequences of 16K tokens in all, a 128K-token row from
+an initial state (chunk 256), and a 64 x 4096 prefill with its batch-64 decode
+step.
 
 The defaults warm up for about 30 ms (the clocks settle within about 20 ms of
 sustained work) and time about 0.1 s of steps.
@@ -49,6 +55,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20
 COPY_BYTES = 1 << 30  # calibration copy, 4x the MALL
 WORKLOADS_BY_NAME = {"prefill_8k": 1, "packed_16k": 2, "long_128k": 3}
+WORKLOADS_BY_NAME_ALL = dict(WORKLOADS_BY_NAME, prefill_decode=4)
 
 
 def log(msg):
@@ -66,17 +73,79 @@ def source_hash():
 
 
 def counter_traffic(workload):
-    """HBM bytes per chunk_output launch from the committed rocprofv3 counter
-    summary, if it was taken on the current sources; else None."""
-    path = os.path.join(ROOT, "profiles", "chunk_output_%s_counters.md" % workload)
+    """HBM bytes per ssd_chunk_scan_fwd call (all its dispatches) from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", "scan_%s_counters.md" % workload)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def compulsory_bytes(b, L, H, P, N, G, *, es=2, seq_idx=False, init=False, final=True):
+    """Each input read once and each output written once: x, dt, B, C in, y
+    out (plus seq_idx), the fp32 final states (and initial states)."""
+    per_token = 2 * H * P * es + 2 * G * N * es + H * 4 + (4 if seq_idx else 0)
+    state = b * H * P * N * 4
+    return b * L * per_token + (state if final else 0) + (state if init else 0)
+
+
+def scan_flops(b, L, H, P, N, G, Q):
+    """MFMA work of the chunked form on the lower triangle: chunk states and
+    the carried-state term (2PN each), the intra-chunk product (PQ) and the
+    group's C.B^T (NQ, shared by H/G heads), per token and head."""
+    return b * L * H * (2 * P * N + P * Q + 2 * P * N + N * Q / (H // G))
+
+
+def bound_pass(lib, hip, fn, nk, reps):
+    """Every dispatch of `reps` rounds of library calls timed by HIP events
+    bound to it (the library passes them to the launch, on the stream it
+    launches on).  fn is one call, or a list of calls made in turn each round;
+    nk is its number of dispatches (or the list of them).  Returns the mean
+    duration of each dispatch of a round, in order, in us."""
+    import numpy as np
+    fns = fn if isinstance(fn, (list, tuple)) else [fn]
+    nks = nk if isinstance(nk, (list, tuple)) else [nk]
+    tot = sum(nks)
+    evs = hip.events(2 * tot * reps)
+    launched = ctypes.c_int(0)
+    vp = ctypes.sizeof(ctypes.c_void_p)
+    for i in range(reps):
+        first = tot * i
+        for f, n in zip(fns, nks):
+            lib.ssd_set_timing_events(ev_slice_of(evs, 2 * first, 2 * n, vp), 2 * n,
+                                      ctypes.byref(launched))
+            f(i)
+            if launched.value != n:
+                raise RuntimeError("expected %d dispatches, got %d" % (n, launched.value))
+            first += n
+    lib.ssd_set_timing_events(None, 0, None)
+    import torch
+    torch.cuda.synchronize()
+    us = [1e3 * float(np.mean([hip.elapsed_ms(evs[2 * (tot * i + k)], evs[2 * (tot * i + k) + 1])
+                               for i in range(reps)])) for k in range(tot)]
+    hip.destroy(evs)
+    return us
+
+
+def count_dispatches(lib, fn):
+    launched = ctypes.c_int(0)
+    no_events = (ctypes.c_void_p * 32)()
+    lib.ssd_set_timing_events(no_events, 32, ctypes.byref(launched))
+    fn(0)
+    lib.ssd_set_timing_events(None, 0, None)
+    return launched.value
+
+
+def roofline_entry(nbytes, us, traffic=None):
+    ach = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
 class Hip:
@@ -199,12 +268,14 @@ def backward_measure(ssd, lib, hip, torch, base, A, D, bias, w, steps, cpu_secon
     per_token = 3 * H * P * 2 + 4 * G * N * 2 + 2 * H * 4
     state_bytes = b * H * P * N * 4
     bwd_bytes = b * L * per_token + 3 * state_bytes + (b * L * 4 if base["seq"] is not None else 0)
-    achieved = bwd_bytes / (grad_us * 1e-6) / 1e9
+    call_us = sum(kus.values())
     out = {"value": round(b * L * steps / el, 1), "unit": "tokens/s", "steps": steps,
            "ms_per_step": round(1e3 * el / steps, 5), "dtype": "bf16",
            "grad_kernel_us": round(grad_us, 2), "kernels_us": kus,
-           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+           "call_kernel_us": round(call_us, 2), "compulsory_bytes": bwd_bytes,
+           # the whole backward call: its compulsory bytes over the sum of its dispatches
+           "roofline": roofline_entry(bwd_bytes, call_us),
+           "grad_kernel_roofline_frac": round(bwd_bytes / (grad_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "cpu_baseline": None}
     if cpu_seconds > 0:
         import oracle
@@ -487,6 +558,85 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
     return res
 
 
+def scan_workload_measure(ssd, lib, hip, torch, w, reps):
+    """One ssd_chunk_scan_fwd call over workload w (inputs drawn on the device,
+    resident in HBM): tokens/s from the host clock over `reps` calls, every
+    dispatch's duration from events bound to it over another `reps` calls, and
+    the whole call's HBM roofline against its compulsory bytes.  For the
+    prefill+decode workload, also its batch decode step (ssd_state_update on
+    the rows' final states, one token per row, cycling over the decode tokens)."""
+    import workloads
+    dev = torch.device("cuda:0")
+    b, H, P, N, G, Q = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    Lp = w.prefill or w.seqlen
+    inp = workloads.make_inputs_device(w, dev)
+    x, dt, B, C = (inp[k][:, :Lp].contiguous() for k in ("x", "dt_raw", "B", "C"))
+    seq = inp["seq_idx"]
+    h0 = inp["h_init"]
+    y = torch.empty_like(x)
+    fs = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, ssd.workspace_bytes(b, Lp, H, P, N, G, Q)), dtype=torch.uint8, device=dev)
+    A, D, bias = inp["A"], inp["D"], inp["dt_bias"]
+
+    def scan(i):
+        ssd.chunk_scan_fwd(x, dt, A, B, C, chunk_size=Q, D=D, dt_bias=bias, initial_states=h0,
+                           seq_idx=seq, return_final_states=True, out=y, final_states_out=fs,
+                           workspace=ws)
+
+    for i in range(3):
+        scan(i)
+    torch.cuda.synchronize()
+    nk = count_dispatches(lib, scan)
+    t0 = time.perf_counter()
+    for i in range(reps):
+        scan(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    kus = bound_pass(lib, hip, scan, nk, reps)
+    nbytes = compulsory_bytes(b, Lp, H, P, N, G, seq_idx=seq is not None, init=h0 is not None)
+    ksum = sum(kus)
+    res = {"workload": w.name, "batch": b, "seq_len": Lp, "chunk": Q,
+           "segments": ssd.segments(b, Lp, H, P, N, G, Q),
+           "packed_sequences": w.packed or None, "initial_states": h0 is not None,
+           "value": round(b * Lp / wall, 1), "unit": "tokens/s", "calls": reps,
+           "ms_per_call": round(1e3 * wall, 4), "kernels_us": [round(u, 2) for u in kus],
+           "call_kernel_us": round(ksum, 2), "compulsory_bytes": nbytes,
+           "roofline": roofline_entry(nbytes, ksum),
+           "mfma_frac": round(scan_flops(b, Lp, H, P, N, G, Q) / (ksum * 1e-6) / 1e12
+                              / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if w.decode_steps:
+        steps = w.decode_steps
+        xs, dts = inp["x"][:, Lp:], inp["dt_raw"][:, Lp:]
+        Bs, Cs = inp["B"][:, Lp:], inp["C"][:, Lp:]
+        xd = [xs[:, t].contiguous() for t in range(steps)]
+        dtd = [dts[:, t].contiguous() for t in range(steps)]
+        Bd = [Bs[:, t].contiguous() for t in range(steps)]
+        Cd = [Cs[:, t].contiguous() for t in range(steps)]
+        yd = torch.empty((b, H, P), dtype=x.dtype, device=dev)
+
+        def step(i):
+            t = i % steps
+            ssd.state_update(fs, xd[t], dtd[t], A, Bd[t], Cd[t], D=D, dt_bias=bias, out=yd)
+
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        dwall = (time.perf_counter() - t0) / steps
+        (dus,) = bound_pass(lib, hip, step, 1, steps)
+        dbytes = b * (2 * H * P * N * 4 + 2 * H * P * 2 + 2 * G * N * 2 + H * 4)
+        res["decode"] = {"rows": b, "steps": steps, "value": round(b / dwall, 1),
+                         "unit": "decode tokens/s", "ms_per_step": round(1e3 * dwall, 4),
+                         "kernel_us": round(dus, 2), "compulsory_bytes": dbytes,
+                         "roofline": roofline_entry(dbytes, dus)}
+    del inp, x, dt, B, C, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def ev_slice_of(evs, first, count, vp):
     return (ctypes.c_void_p * count).from_buffer(evs, first * vp)
 
@@ -501,6 +651,9 @@ def main():
                     help="timed calls of the backward pass (reported under \"backward\")")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--skip-workloads", action="store_true",
+                    help="measure only the headline workload (no packed_16k, long_128k, "
+                         "prefill_decode objects)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (for scaling HBM "
                          "byte counters) and print its size")
@@ -548,10 +701,9 @@ def main():
                 h0=None if p.get("h_init") is None else dev_t(p["h_init"]))
     A, D, bias = dev_t(p["A"]), dev_t(p["D"]), dev_t(p["dt_bias"])
     es = 2
-    io_bytes = b * L * (2 * H * P * es + 2 * G * N * es + H * 4)
     state_bytes = b * H * P * N * 4
-    scan_bytes = io_bytes + state_bytes + (state_bytes if base["h0"] is not None else 0) + \
-        (b * L * 4 if base["seq"] is not None else 0)
+    scan_bytes = compulsory_bytes(b, L, H, P, N, G, seq_idx=base["seq"] is not None,
+                                  init=base["h0"] is not None)
     nsets = max(2, math.ceil(2 * MALL_BYTES / scan_bytes) + 1)
     sets = []
     for _ in range(nsets):
@@ -563,95 +715,58 @@ def main():
     ws = torch.empty(max(1, ssd.workspace_bytes(b, L, H, P, N, G, Q)), dtype=torch.uint8,
                      device=dev)
     nseg = ssd.segments(b, L, H, P, N, G, Q)
-    launched = ctypes.c_int(0)
-    # the scan's kernel sequence: count its launches once (hooks with no events)
-    no_events = (ctypes.c_void_p * 16)()
-    lib.ssd_set_timing_events(no_events, 16, ctypes.byref(launched))
-    s0 = sets[0]
-    ssd.chunk_scan_fwd(s0["x"], s0["dt"], A, s0["B"], s0["C"], chunk_size=Q, D=D, dt_bias=bias,
-                       initial_states=s0["h0"], seq_idx=s0["seq"], return_final_states=True,
-                       out=s0["y"], final_states_out=s0["fs"], workspace=ws)
-    lib.ssd_set_timing_events(None, 0, None)
-    torch.cuda.synchronize()
-    kernels = {2: ["chunk_prep", "chunk_output"],
-               3: ["chunk_prep", "chunk_state", "chunk_output"],
-               4: ["chunk_prep", "chunk_state", "state_pass", "chunk_output"]}[launched.value]
-    nk = len(kernels) + 1  # + state_update
 
-    vp_size = ctypes.sizeof(ctypes.c_void_p)
-
-    def ev_slice(evs, first, count):
-        return (ctypes.c_void_p * count).from_buffer(evs, first * vp_size)
-
-    k_out = kernels.index("chunk_output")
-
-    def step(i, evs=None, only_output=False):
-        """One step.  With evs: records the library's per-kernel events of step i
-        (all kernels, or only chunk_output's pair: every event bound to a dispatch
-        adds work around it, so the timed steps carry just that pair)."""
+    def scan(i):
         s = sets[i % nsets]
-        base_ev = 2 * nk * i
-        if evs is not None:
-            scan_ev = ev_slice(evs, base_ev, 2 * (nk - 1))
-            if only_output:
-                scan_ev = (ctypes.c_void_p * (2 * (nk - 1)))()
-                scan_ev[2 * k_out] = evs[base_ev + 2 * k_out]
-                scan_ev[2 * k_out + 1] = evs[base_ev + 2 * k_out + 1]
-            lib.ssd_set_timing_events(scan_ev, 2 * (nk - 1), ctypes.byref(launched))
         ssd.chunk_scan_fwd(s["x"], s["dt"], A, s["B"], s["C"], chunk_size=Q, D=D, dt_bias=bias,
                            initial_states=s["h0"], seq_idx=s["seq"], return_final_states=True,
                            out=s["y"], final_states_out=s["fs"], workspace=ws)
-        if evs is not None:
-            if launched.value != nk - 1:
-                raise RuntimeError("scan launched %d kernels, expected %d" % (launched.value, nk - 1))
-            if only_output:
-                lib.ssd_set_timing_events(None, 0, None)
-            else:
-                lib.ssd_set_timing_events(ev_slice(evs, base_ev + 2 * (nk - 1), 2), 2,
-                                          ctypes.byref(launched))
+
+    def decode(i):
+        s = sets[i % nsets]
         ssd.state_update(s["fs"], s["xd"], s["dtd"], A, s["Bd"], s["Cd"], D=D, dt_bias=bias,
                          out=s["yd"])
-        if evs is not None:
-            lib.ssd_set_timing_events(None, 0, None)
 
-    def kernel_ms(evs, i, k):
-        return hip.elapsed_ms(evs[2 * nk * i + 2 * k], evs[2 * nk * i + 2 * k + 1])
+    nk = count_dispatches(lib, scan)
+    kernels = {2: ["chunk_prep", "chunk_output"],
+               3: ["chunk_prep", "chunk_state", "chunk_output"],
+               4: ["chunk_prep", "chunk_state", "state_pass", "chunk_output"]}[nk]
 
     log("bench: %d warmup steps" % args.warmup)
     for i in range(args.warmup):
-        step(i)
+        scan(i)
+        decode(i)
     torch.cuda.synchronize()
-    evs = hip.events(2 * nk * args.steps)
+    # the timed steps: a plain stream event on each side of the scan (GPU time
+    # of the whole call, launch gaps included)
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     log("bench: %d timed steps" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs, only_output=True)
+        e0[i].record()
+        scan(i)
+        e1[i].record()
+        decode(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    out_ms = [kernel_ms(evs, i, k_out) for i in range(args.steps)]
-    # diagnostics outside the timed region: every kernel's events, same steps
-    diag_steps = min(args.steps, 20)
-    for i in range(diag_steps):
-        step(i, evs)
-    torch.cuda.synchronize()
-    names = kernels + ["state_update"]
-    per_kernel = {n: [kernel_ms(evs, i, k) for i in range(diag_steps)] for k, n in enumerate(names)}
-    hip.destroy(evs)
-    avg_us = {n: 1e3 * float(np.mean(v)) for n, v in per_kernel.items()}
-    out_us = 1e3 * float(np.mean(out_ms))
+    call_us = 1e3 * float(np.mean([e0[i].elapsed_time(e1[i]) for i in range(args.steps)]))
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_step = b * L + b
     value = tokens_per_step * args.steps / elapsed
+    # the same steps again with HIP events bound to every dispatch of the scan
+    # and of the decode update (each pair on the stream its kernel runs on)
+    log("bench: %d steps with events bound to every dispatch" % args.steps)
 
-    # roofline of the dominant kernel: algorithmic bytes of one chunk_output launch
-    k4_bytes = scan_bytes
-    k4_s = out_us * 1e-6
-    achieved = k4_bytes / k4_s / 1e9
-    traffic = counter_traffic(w.name)
-    flops = b * L * H * (2 * P * N + P * Q + 2 * P * N + N * Q / (H // G))
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    kus = bound_pass(lib, hip, [scan, decode], [nk, 1], args.steps)
+    names = kernels + ["state_update"]
+    avg_us = dict(zip(names, kus))
+    kernel_sum = sum(kus[:nk])
+
+    # roofline of the whole scan call: its compulsory bytes over the sum of
+    # its dispatches' durations
+    roof = roofline_entry(scan_bytes, kernel_sum, counter_traffic(w.name))
     step_bytes = scan_bytes + 2 * state_bytes + b * (H * P * 2 * es + 2 * G * N * es + H * 4)
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -662,12 +777,23 @@ def main():
                    "dstate": N, "ngroups": G, "chunk": Q, "decode_tokens_per_step": b,
                    "segments": nseg, "input_copies": nsets},
         "roofline": roof,
-        "chunk_output_us": round(out_us, 2),
+        "scan_kernel_us": round(kernel_sum, 2),
+        "scan_call_us": round(call_us, 2),
         "kernels_us": {n: round(v, 2) for n, v in avg_us.items()},
+        "kernel_roofline_frac": {n: round(scan_bytes / (avg_us[n] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                 for n in kernels},
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "chunk_output_mfma_frac": round(flops / k4_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "scan_mfma_frac": round(scan_flops(b, L, H, P, N, G, Q) / (kernel_sum * 1e-6) / 1e12
+                                / MFMA_BF16_PEAK_TFLOPS, 4),
         "source_hash": source_hash(),
     }
+    if not args.skip_workloads:
+        result["workloads"] = {}
+        for name in ("packed_16k", "long_128k", "prefill_decode"):
+            log("bench: workload %s" % name)
+            ww = workloads.WORKLOADS[WORKLOADS_BY_NAME_ALL[name]]
+            result["workloads"][name] = scan_workload_measure(
+                ssd, lib, hip, torch, ww, 20 if name != "packed_16k" else 50)
     log("bench: backward pass")
     result["backward"] = backward_measure(ssd, lib, hip, torch, sets[0], A, D, bias, w,
                                           args.backward_steps, min(args.cpu_seconds, 5.0), p)

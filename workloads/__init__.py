@@ -181,3 +181,44 @@ def random_problem(rng: np.random.Generator, b, L, H, P, N, G, *, io="f32",
                 if init else None),
         seq_idx=None,
     )
+
+
+def make_inputs_device(w: Workload, device, *, seed: Optional[int] = None,
+                       seqlen: Optional[int] = None):
+    """The inputs of workload ``w`` drawn directly on ``device`` with torch's
+    seeded generator: the same distributions and shapes as ``make_inputs``
+    (dt_bias ~ U[-4,-2], A = -exp(U[0, ln 16]), D ~ N(0,1); x, dt_raw ~ N(0,1);
+    B, C ~ N(0,1)/sqrt(N); h_init ~ 0.1 N(0,1); packed lengths by the same
+    recipe), from a different random stream.  For throughput measurement of
+    the large workloads, whose host-side generation takes tens of seconds;
+    nothing compares these values with the oracle.  x, B and C come back in
+    bfloat16 for the bf16 workloads (torch's conversion rounds to nearest
+    even), everything else in float32.  Returns a dict of torch tensors."""
+    import torch
+    k = w.cid if seed is None else seed
+    L = w.seqlen if seqlen is None else int(seqlen)
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    gen = torch.Generator(device=device)
+    gen.manual_seed(2000 + k)
+    f32 = torch.float32
+    io = torch.bfloat16 if w.io == "bf16" else f32
+
+    def u(shape, lo, hi):
+        return torch.rand(shape, generator=gen, device=device, dtype=f32) * (hi - lo) + lo
+
+    def n(shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=f32)
+
+    out = dict(dt_bias=u((H,), -4.0, -2.0), A=-torch.exp(u((H,), 0.0, math.log(16.0))), D=n((H,)))
+    out["x"] = n((b, L, H, P)).to(io)
+    out["dt_raw"] = n((b, L, H))
+    out["B"] = (n((b, L, G, N)) / math.sqrt(N)).to(io)
+    out["C"] = (n((b, L, G, N)) / math.sqrt(N)).to(io)
+    out["h_init"] = 0.1 * n((b, H, P, N)) if w.init_states else None
+    out["seq_idx"] = None
+    if w.packed:
+        lengths = packed_lengths(np.random.default_rng(2000 + k), w.packed, L)
+        sid = np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)
+        out["seq_idx"] = torch.from_numpy(np.broadcast_to(sid, (b, L)).copy()).to(device)
+        out["lengths"] = lengths
+    return out
