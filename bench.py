@@ -780,8 +780,11 @@ def main():
         "scan_kernel_us": round(kernel_sum, 2),
         "scan_call_us": round(call_us, 2),
         "kernels_us": {n: round(v, 2) for n, v in avg_us.items()},
-        "kernel_roofline_frac": {n: round(scan_bytes / (avg_us[n] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-                                 for n in kernels},
+        # share of the call's kernel time per dispatch, and the call's bytes
+        # over the output kernel's time alone (the figure earlier lines reported)
+        "kernel_time_share": {n: round(avg_us[n] / kernel_sum, 4) for n in kernels},
+        "chunk_output_frac_of_call_bytes": round(
+            scan_bytes / (avg_us["chunk_output"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "scan_mfma_frac": round(scan_flops(b, L, H, P, N, G, Q) / (kernel_sum * 1e-6) / 1e12
                                 / MFMA_BF16_PEAK_TFLOPS, 4),
