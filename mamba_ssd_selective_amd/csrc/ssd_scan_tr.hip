@@ -265,8 +265,10 @@ struct TrScan {
     // is token j_e in the k order above) for lane column i = 16I + r16, in
     // the exact form: f_e = [j_e <= i] [seq_j = seq_i] exp(cs_i - cs_j) dt_j,
     // so that G[i][j_e] = (C_i . B_j) f_e.
+    // sigma: the sequence a pass serves (rows of other sequences get zero
+    // factors; callers without one pass seq_i).
     __device__ __forceinline__ void exact_factors(float (&f)[8], const void* mobj, uint32_t mq, int u,
-                                                  float cs_i, int seq_i) const {
+                                                  float cs_i, int seq_i, int sigma) const {
         // token 16J + 4g + r of tile J is kept when r <= lim: all of a tile left
         // of the diagonal, r <= r16 - 4g on it, none right of it
         int tdiag = r16 - 4 * g;
@@ -289,13 +291,34 @@ struct TrScan {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 bool keep = r <= lim;
-                if constexpr (kSeq) keep = keep && sqv[r] == seq_i;
+                if constexpr (kSeq) keep = keep && sqv[r] == seq_i && seq_i == sigma;
                 // masked elements may overflow here; the select drops them
                 f[4 * hp + r] = keep ? decay_exp(cs_i - csv[r]) * dtv[r] : 0.0f;
             }
             // one half at a time (bounds the registers of this rarely taken path)
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+
+    // Packed sequences: 16-bit masks of k step s's tokens (the fragment
+    // element order above) that belong to sequence sigma, one word per bf16
+    // pair.  ANDing a fragment with them zeroes every other sequence's values
+    // (NaN and Inf included), where a product with a zero weight would not.
+    __device__ __forceinline__ uint4 seq_keep_mask(const void* mobj, uint32_t mq, int s,
+                                                   int sigma) const {
+        const int4 q0 = lds_ld<int4>(mobj, mq + 128 * s + offsetof(TrMeta<Q>, seq));
+        const int4 q1 = lds_ld<int4>(mobj, mq + 128 * s + 64 + offsetof(TrMeta<Q>, seq));
+        auto m2 = [](bool lo, bool hi) { return (lo ? 0x0000FFFFu : 0u) | (hi ? 0xFFFF0000u : 0u); };
+        return make_uint4(m2(q0.x == sigma, q0.y == sigma), m2(q0.z == sigma, q0.w == sigma),
+                          m2(q1.x == sigma, q1.y == sigma), m2(q1.z == sigma, q1.w == sigma));
+    }
+    static __device__ __forceinline__ Frag<uint16_t> frag_and(const Frag<uint16_t>& f, const uint4& m) {
+        uint4 u = __builtin_bit_cast(uint4, f.v);
+        u.x &= m.x;
+        u.y &= m.y;
+        u.z &= m.z;
+        u.w &= m.w;
+        return frag_of(u);
     }
 
     // G^T fragment from a C.B^T tile pair and per-element factors f (both
@@ -306,13 +329,19 @@ struct TrScan {
     // the diagonal tile keeps j <= i, and dd is added on the diagonal element:
     // D[h] / r_i in the factored form (r_i then restores D[h]), D[h] in the
     // exact form (whose factors already hold the masks).
+    // kMasked: zero factors mark another sequence's pairs, kept zero by a
+    // select whatever the tile holds.
     __device__ __forceinline__ Frag<uint16_t> g_apply(const uint4& t, const float (&f)[8], bool diag,
-                                                      float dd) const {
+                                                      float dd, bool kMasked) const {
         const uint32_t d[4] = {t.x, t.y, t.z, t.w};
         float out[8];
         if (!diag) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] = ((e & 1) ? bf_hi(d[e >> 1]) : bf_lo(d[e >> 1])) * f[e];
+            for (int e = 0; e < 8; ++e) {
+                const float v = ((e & 1) ? bf_hi(d[e >> 1]) : bf_lo(d[e >> 1])) * f[e];
+                // a masked pair (zero factor) stays zero whatever its tile value
+                out[e] = (kSeq && kMasked && f[e] == 0.0f) ? 0.0f : v;
+            }
         } else {
             int tdiag = r16 - 4 * g;
             asm volatile("" : "+v"(tdiag));
@@ -324,7 +353,8 @@ struct TrScan {
                 // tile 2u is the diagonal one for even I (and left of it for odd I);
                 // tile 2u+1 is the diagonal one for odd I (and right of it for even I)
                 const bool on_diag = (e < 4) ? !odd : odd;
-                const bool keep = (e < 4) ? (odd || r <= tdiag) : (odd && r <= tdiag);
+                bool keep = (e < 4) ? (odd || r <= tdiag) : (odd && r <= tdiag);
+                if (kSeq && kMasked) keep = keep && f[e] != 0.0f;  // another sequence's pair
                 const float v = keep ? cbv * f[e] : 0.0f;
                 out[e] = (on_diag && r == tdiag) ? v + dd : v;
             }
@@ -383,6 +413,69 @@ struct TrScan {
     // copy), and its C rows and C.B^T tiles in cr, cb.  Issues this wave's
     // share of chunk c+1's copies into buffer K^1 and leaves after the barrier
     // that ends the chunk.
+    // Whether chunk c (in buffer K) holds more than one packed sequence among
+    // its tokens.  Such chunks take the kMixed code (masks and passes), which
+    // the others never execute.
+    template <int K>
+    __device__ __forceinline__ bool chunk_mixed(int c) const {
+        if constexpr (!kSeq) {
+            return false;
+        } else {
+            const TrMeta<Q>* M = mo[K];
+            const uint32_t mb = mbase[K];
+            return lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq)) !=
+                   lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (rows_in(c) - 1));
+        }
+    }
+    // A row block that holds more than one packed sequence: the main k-step
+    // loop served its first sequence (seq_m).  Rows of later sequences have no
+    // carried-state term (their sequence starts inside this chunk), so they
+    // restart from zero and take one pass per sequence: x masked to the
+    // sequence, exact factors for its rows only, and each k step's product
+    // added to its rows with a select.  Rare: only where a sequence boundary
+    // falls inside a 16-row block.
+    template <int K>
+    __device__ __forceinline__ void span_passes(f32x4_t (&y)[G_::PB], int c, int valid, int i,
+                                                         int sd, float cs_i, int seq_i, int seq_m,
+                                                         float dr) const {
+        const TrMeta<Q>* M = mo[K];
+        const char* X = xo[K];
+#pragma unroll
+        for (int pb = 0; pb < G_::PB; ++pb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[pb][r] = seq_i == seq_m ? y[pb][r] : 0.0f;
+        int sigma = seq_m;
+        for (int pass = 0; pass < 16; ++pass) {
+            // the next sequence among this block's rows (the ids rise along
+            // lanes 0..15; at most 16 passes whatever the ids)
+            const uint64_t nxt = __builtin_amdgcn_ballot_w64(g == 0 && i < valid && seq_i > sigma);
+            if (nxt == 0) break;
+            sigma = __builtin_amdgcn_readlane(seq_i, static_cast<int>(__builtin_ctzll(nxt)));
+            const bool mine = seq_i == sigma;
+#pragma unroll
+            for (int s = 0; s < G_::KQ; ++s) {
+                if (s <= sd) {
+                    Frag<uint16_t> xf[G_::PB];
+                    float f[8];
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = tr_frag<G_::XROW>(X, xa[K] ^ (32 * pb), s);
+                    exact_factors(f, M, ma[K], s, cs_i, seq_i, sigma);
+                    const uint4 km = seq_keep_mask(M, ma[K], s, sigma);
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = frag_and(xf[pb], km);
+                    const Frag<uint16_t> gf = g_apply(cb[s], f, s == sd, dr, true);
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) {
+                        f32x4_t t = acc_zero();
+                        mma(t, xf[pb], gf);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) y[pb][r] += mine ? t[r] : 0.0f;
+                    }
+                }
+            }
+        }
+    }
+
     template <int K>
     __device__ __forceinline__ void chunk_out(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
         const bool has_next = c + 1 < c_end;
@@ -403,10 +496,15 @@ struct TrScan {
         const int me = min(m0 + 15, max(valid - 1, m0));
         const float cs_e = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * me);
         int seq_i = 0, seq_m = 0, seq_e = 0;
+        // packed sequences: the chunk holds more than one of them ("mixed"),
+        // and this row block does ("spanning")
+        bool mixed = false, spanning = false;
         if constexpr (kSeq) {
             seq_i = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * i);
             seq_m = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * m0);
             seq_e = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * me);
+            mixed = chunk_mixed<K>(c);
+            spanning = mixed && seq_m != seq_e;
         }
         // carried-state term y^T[p][i] = h . C_i, scaled below; each k step's
         // operand reads are issued before its products
@@ -436,7 +534,8 @@ struct TrScan {
                     keep = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * j) == seq_m;
                 const float csj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * j);
                 const float dtj = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, dt) + 4 * j);
-                rising = rising || dtj * Ah > 0.0f;
+                // (other sequences' tokens have no say in the form this block takes)
+                rising = rising || (keep && dtj * Ah > 0.0f);
                 // overflows only where the factored form is not taken
                 lds_st<float>(cjo, cjw + 256 * k, keep ? decay_exp(cs_m - csj) * dtj : 0.0f);
             }
@@ -449,21 +548,27 @@ struct TrScan {
         const bool wfast = !__builtin_amdgcn_ballot_w64(rising) && (!kSeq || seq_m == seq_e) &&
                            cs_m - cs_e <= kDiagSpan && !a.exact_decay;
         float sc, fin = 1.0f, dr = Dh;
+        bool carry = true;  // the carried state reaches this row (select, not a product)
         if (wfast) {
             fin = decay_exp(cs_i - cs_m);  // r_i
             dr = Dh / fin;
-            sc = (!kSeq || seq_m == seq_prev) ? decay_exp(cs_m) : 0.0f;
+            sc = decay_exp(cs_m);
+            if constexpr (kSeq) carry = seq_m == seq_prev;
         } else {
-            sc = (!kSeq || seq_i == seq_prev) ? decay_exp(cs_i) : 0.0f;
+            sc = decay_exp(cs_i);
+            if constexpr (kSeq) carry = seq_i == seq_prev;
         }
 #pragma unroll
         for (int pb = 0; pb < G_::PB; ++pb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[pb][r] *= sc;
+            for (int r = 0; r < 4; ++r) y[pb][r] = carry ? y[pb][r] * sc : 0.0f;
         if (has_next) load_c(c + 1);  // this chunk's C rows are consumed
 
         // intra-chunk outputs y^T += x^T G^T over the k steps up to the
-        // diagonal one
+        // diagonal one.  In a chunk that holds several sequences the x
+        // operand is masked to the row block's first sequence with a select
+        // and masked pairs of G stay zero whatever their tile holds, so a
+        // non-finite value of another sequence never meets a zero weight.
         const int sd = I >> 1;
 #pragma unroll
         for (int s = 0; s < G_::KQ; ++s) {
@@ -478,15 +583,21 @@ struct TrScan {
                     f[0] = c0.x; f[1] = c0.y; f[2] = c0.z; f[3] = c0.w;
                     f[4] = c1.x; f[5] = c1.y; f[6] = c1.z; f[7] = c1.w;
                 } else {
-                    exact_factors(f, M, ma[K], s, cs_i, seq_i);
+                    exact_factors(f, M, ma[K], s, cs_i, seq_i, kSeq ? seq_m : seq_i);
+                }
+                if (kSeq && mixed) {
+                    const uint4 km = seq_keep_mask(M, ma[K], s, seq_m);
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = frag_and(xf[pb], km);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                const Frag<uint16_t> gf = g_apply(cb[s], f, s == sd, dr);
+                const Frag<uint16_t> gf = g_apply(cb[s], f, s == sd, dr, kSeq && mixed);
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], xf[pb], gf);
             }
             if (has_next) copies(s, c, Xn, Bn, Mn);
         }
+        if (kSeq && spanning) span_passes<K>(y, c, valid, i, sd, cs_i, seq_i, seq_m, dr);
         if (has_next) load_cb(c + 1);  // after the last use
         store_y(y, fin, c, i, valid);
         if constexpr (kSeq) seq_prev = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (Q - 1));
@@ -510,6 +621,11 @@ struct TrScan {
     // H[K^1] for the next chunk's carried-state term.
     template <int K>
     __device__ __forceinline__ void chunk_st(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
+        if (chunk_mixed<K>(c)) chunk_st_t<K, true>(c, Xn, Bn, Mn);
+        else chunk_st_t<K, false>(c, Xn, Bn, Mn);
+    }
+    template <int K, bool kMixed>
+    __device__ __forceinline__ void chunk_st_t(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
         const bool has_next = c + 1 < c_end;
         const int valid = rows_in(c);
         const uint32_t mb = mbase[K];
@@ -520,16 +636,20 @@ struct TrScan {
         const float cs_last = lds_ld<float>(M, mb + offsetof(TrMeta<Q>, cs) + 4 * (Q - 1));
         const int seq_last = kSeq ? lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (valid - 1)) : 0;
         if (has_next) copies(-1, c, Xn, Bn, Mn);
-        const float e = (!kSeq || seq_last == seq_prev) ? decay_exp(cs_last) : 0.0f;
+        // at a sequence change the state restarts: selects, so that a
+        // non-finite state of the previous sequence does not survive a zero
+        // factor
+        const bool keep_h = !kSeq || seq_last == seq_prev;
+        const float e = decay_exp(cs_last);
         if (st()) {
 #pragma unroll
             for (int t = 0; t < NBW; ++t)
 #pragma unroll
                 for (int pb = 0; pb < G_::PB; ++pb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) h[t][pb][r] *= e;
+                    for (int r = 0; r < 4; ++r) h[t][pb][r] = keep_h ? h[t][pb][r] * e : 0.0f;
         }
-        if constexpr (!kOut) mult *= e;
+        if constexpr (!kOut) mult = keep_h ? mult * e : 0.0f;
 #pragma unroll
         for (int s = 0; s < G_::KQ; ++s) {
             if (st()) {
@@ -540,6 +660,14 @@ struct TrScan {
                 for (int t = 0; t < NBW; ++t) braw[t] = tr_frag<G_::BROW>(Bt, ba[K][t], s);
                 const float4 w0 = lds_ld<float4>(M, ma[K] + offsetof(TrMeta<Q>, w) + 128 * s);
                 const float4 w1 = lds_ld<float4>(M, ma[K] + offsetof(TrMeta<Q>, w) + 128 * s + 64);
+                if constexpr (kMixed) {
+                    // only the last sequence's tokens enter the chunk's state
+                    const uint4 km = seq_keep_mask(M, ma[K], s, seq_last);
+#pragma unroll
+                    for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = frag_and(xf[pb], km);
+#pragma unroll
+                    for (int t = 0; t < NBW; ++t) braw[t] = frag_and(braw[t], km);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < NBW; ++t) {

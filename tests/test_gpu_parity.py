@@ -320,3 +320,78 @@ def test_graph_replay_matches_eager_bitwise():
         torch.cuda.synchronize()
         log("graph replay %d" % r)
         assert torch.equal(y, ref[0]) and torch.equal(fs, ref[1]) and torch.equal(yd, ref[2]), r
+
+
+def _report_diff(Y0, Y1, mask):
+    """Log the tokens (outside the poisoned sequence) whose outputs differ."""
+    d = (Y0 != Y1) & mask[None, :, None, None]
+    if d.any():
+        toks = np.unique(np.nonzero(d)[1])
+        heads = np.unique(np.nonzero(d)[2])
+        log("differing tokens %s (%d), heads %s, non-finite %d"
+            % (toks[:40].tolist(), len(toks), heads.tolist(), int((~np.isfinite(Y1) & d).sum())))
+
+
+def _poison(q, a, e, kind, rng):
+    """Non-finite values in tokens [a, e) of one packed sequence: at its first
+    and last token and at a few tokens between (so that chunks it shares with
+    its neighbours are hit)."""
+    toks = sorted({a, e - 1, (a + e) // 2} | set(rng.integers(a, e, size=3).tolist()))
+    bad = {"nan": np.float32("nan"), "inf": np.float32("inf"), "-inf": np.float32("-inf")}[kind]
+    for t in toks:
+        q["x"][:, t, :, ::7] = bad
+        q["B"][:, t, :, 3] = bad
+        q["C"][:, t, :, 5] = -bad
+        q["dt_raw"][:, t, 1] = bad
+    return toks
+
+
+@pytest.mark.parametrize("kind", ["nan", "inf", "-inf"])
+@pytest.mark.parametrize("victim", [1, 3])
+def test_nonfinite_inputs_stay_inside_their_sequence(kind, victim):
+    """NaN or +-Inf in one packed sequence's x, B, C and dt leave every other
+    sequence's y bitwise unchanged, and the final state too unless the poisoned
+    sequence is the row's last (masks are selects).  12
+    segments of one chunk each, so the segment-state pass and the carry between
+    segments are on the path."""
+    rng = np.random.default_rng(99)
+    b, L, H, P, N, G = 1, 1500, 8, 64, 128, 2
+    p = workloads.random_problem(rng, b, L, H, P, N, G, io="bf16", init=True)
+    lens = [300, 77, 500, 623]
+    p["seq_idx"] = np.repeat(np.arange(4, dtype=np.int32), lens)[None]
+    starts = np.cumsum([0] + lens)
+    y0, f0 = run_scan(to_dev(p, "bf16"), 128)
+    q = {kk: (v.copy() if isinstance(v, np.ndarray) else v) for kk, v in p.items()}
+    a, e = starts[victim], starts[victim + 1]
+    toks = _poison(q, a, e, kind, rng)
+    log("nonfinite %s in sequence %d (tokens %s)" % (kind, victim, toks))
+    y1, f1 = run_scan(to_dev(q, "bf16"), 128)
+    Y0, Y1 = host(y0), host(y1)
+    mask = np.ones(L, dtype=bool)
+    mask[a:e] = False
+    _report_diff(Y0, Y1, mask)
+    assert np.array_equal(Y0[:, mask], Y1[:, mask])
+    assert not np.isfinite(Y1[:, a:e]).all()
+    if victim != 3:
+        assert np.array_equal(host(f0), host(f1))
+
+
+def test_nonfinite_inputs_stay_inside_their_sequence_packed_16k():
+    """The same at the packed 16K workload's shape (64 heads, 16 sequences,
+    most starting mid-chunk), for one sequence in the middle."""
+    w = workloads.WORKLOADS[2]
+    p = workloads.make_inputs(w)
+    lens = p["lengths"]
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    victim = 6
+    a, e = int(starts[victim]), int(starts[victim + 1])
+    y0, f0 = run_scan(to_dev(p, "bf16"), w.chunk)
+    q = {kk: (v.copy() if isinstance(v, np.ndarray) else v) for kk, v in p.items()}
+    toks = _poison(q, a, e, "nan", np.random.default_rng(3))
+    log("nonfinite nan in packed_16k sequence %d [%d, %d) tokens %s" % (victim, a, e, toks))
+    y1, f1 = run_scan(to_dev(q, "bf16"), w.chunk)
+    Y0, Y1 = host(y0), host(y1)
+    mask = np.ones(w.seqlen, dtype=bool)
+    mask[a:e] = False
+    assert np.array_equal(Y0[:, mask], Y1[:, mask])
+    assert np.array_equal(host(f0), host(f1))
