@@ -175,26 +175,28 @@ def _prefill_case(seed, b, L, H, G, io, rows):
     return rng, p
 
 
-def _run_prefill(p, idx, lens, io, Q, init_from_cache=True):
+def _run_prefill(p, idx, lens, io, Q, init_from_cache=True, zero_D=False):
     import torch
     import mamba_ssd_selective_amd as ssd
     t = torch.bfloat16 if io == "bf16" else torch.float32
     c = _dev(p["cache"])
+    D = np.zeros_like(p["D"]) if zero_D else p["D"]
     y = ssd.chunk_scan_fwd_cached(_dev(p["x"], t), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], t),
                                   _dev(p["C"], t), c, _dev(idx), chunk_size=Q,
                                   seq_lens=None if lens is None else _dev(lens),
-                                  init_from_cache=init_from_cache, D=_dev(p["D"]),
+                                  init_from_cache=init_from_cache, D=_dev(D),
                                   dt_bias=_dev(p["dt_bias"]))
     torch.cuda.synchronize()
     return _host(y), _host(c)
 
 
-def _oracle_row(p, r, n, h0, heads=None, grp=None):
+def _oracle_row(p, r, n, h0, heads=None, grp=None, zero_D=False):
     hs = slice(None) if heads is None else heads
     gs = slice(None) if grp is None else grp
+    D = np.zeros_like(p["D"]) if zero_D else p["D"]
     return oracle.scan(p["x"][r:r + 1, :n, hs], p["dt_raw"][r:r + 1, :n, hs], p["A"][hs],
                        p["B"][r:r + 1, :n, gs], p["C"][r:r + 1, :n, gs],
-                       dt_bias=p["dt_bias"][hs], D=p["D"][hs],
+                       dt_bias=p["dt_bias"][hs], D=D[hs],
                        h_init=None if h0 is None else h0[None])
 
 
@@ -208,23 +210,26 @@ def test_prefill_cached_rows(io, Q, init_from_cache):
     rng, p = _prefill_case(3, b, L, H, G, io, rows)
     idx = np.array([7, 2, 0, 5, -1, 3], dtype=np.int32)
     lens = np.array([300, 0, 1, Q, 137, 200], dtype=np.int32)
-    print("case io=%s Q=%d init=%s" % (io, Q, init_from_cache), flush=True)
-    y, c = _run_prefill(p, idx, lens, io, Q, init_from_cache)
     tol = 1e-4 if io == "f32" else 2e-2
-    for r in range(b):
-        s, n = idx[r], lens[r]
-        if not 0 <= s < rows:
-            continue
-        h0 = p["cache"][s] if init_from_cache else None
-        if n == 0:
-            want = p["cache"][s] if init_from_cache else np.zeros_like(p["cache"][s])
-            assert np.array_equal(c[s], want)
-            continue
-        yr, hr = _oracle_row(p, r, n, h0)
-        assert oracle.rel_l2(y[r, :n], yr[0]) < tol, r
-        assert oracle.rel_l2(c[s], hr[0]) < tol, r
-    untouched = [s for s in range(rows) if s not in idx]
-    assert np.array_equal(c[untouched], p["cache"][untouched])
+    # with D, and with D = 0 (D x dominates y, which would hide the scan terms)
+    for zero_D in (False, True):
+        print("case io=%s Q=%d init=%s D=%s" % (io, Q, init_from_cache, "0" if zero_D else "D"),
+              flush=True)
+        y, c = _run_prefill(p, idx, lens, io, Q, init_from_cache, zero_D=zero_D)
+        for r in range(b):
+            s, n = idx[r], lens[r]
+            if not 0 <= s < rows:
+                continue
+            h0 = p["cache"][s] if init_from_cache else None
+            if n == 0:
+                want = p["cache"][s] if init_from_cache else np.zeros_like(p["cache"][s])
+                assert np.array_equal(c[s], want)
+                continue
+            yr, hr = _oracle_row(p, r, n, h0, zero_D=zero_D)
+            assert oracle.rel_l2(y[r, :n], yr[0]) < tol, (r, zero_D)
+            assert oracle.rel_l2(c[s], hr[0]) < tol, (r, zero_D)
+        untouched = [s for s in range(rows) if s not in idx]
+        assert np.array_equal(c[untouched], p["cache"][untouched])
 
 
 def test_prefill_cached_matches_plain_scan():
@@ -251,15 +256,17 @@ def test_prefill_cached_8k_shape():
     rng, p = _prefill_case(12, b, L, H, G, "bf16", rows)
     idx = np.array([6, 1], dtype=np.int32)
     lens = np.array([8192, 5000], dtype=np.int32)
-    y, c = _run_prefill(p, idx, lens, "bf16", 128)
     grp = 5
     hs = slice(8 * grp, 8 * grp + 8)
-    for r in range(b):
-        s, n = idx[r], lens[r]
-        yr, hr = _oracle_row(p, r, n, p["cache"][s][hs], heads=hs, grp=slice(grp, grp + 1))
-        ey, eh = oracle.rel_l2(y[r, :n, hs], yr[0]), oracle.rel_l2(c[s][hs], hr[0])
-        print("row %d: y %.3e state %.3e" % (r, ey, eh), flush=True)
-        assert ey < 2e-2 and eh < 2e-2
+    for zero_D in (False, True):
+        y, c = _run_prefill(p, idx, lens, "bf16", 128, zero_D=zero_D)
+        for r in range(b):
+            s, n = idx[r], lens[r]
+            yr, hr = _oracle_row(p, r, n, p["cache"][s][hs], heads=hs, grp=slice(grp, grp + 1),
+                                 zero_D=zero_D)
+            ey, eh = oracle.rel_l2(y[r, :n, hs], yr[0]), oracle.rel_l2(c[s][hs], hr[0])
+            print("row %d D=%s: y %.3e state %.3e" % (r, "0" if zero_D else "D", ey, eh), flush=True)
+            assert ey < 2e-2 and eh < 2e-2
 
 
 def test_prefill_then_decode_on_cache():
@@ -323,25 +330,27 @@ def test_varlen_packed_sequences(io, Q):
     p = _varlen_case(17, lens, H, G, io, rows)
     idx = np.array([6, 0, 3, 8, 1], dtype=np.int32)
     t = torch.bfloat16 if io == "bf16" else torch.float32
-    c = _dev(p["cache"])
-    y = ssd.chunk_scan_fwd_varlen(_dev(p["x"], t), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], t),
-                                  _dev(p["C"], t), _dev(p["cu"]), c, _dev(idx), max_seqlen=max(lens),
-                                  chunk_size=Q, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]))
-    torch.cuda.synchronize()
-    y, c = _host(y), _host(c)
     tol = 1e-4 if io == "f32" else 2e-2
-    for r, n in enumerate(lens):
-        s, a = idx[r], p["cu"][r]
-        if n == 0:
-            assert np.array_equal(c[s], p["cache"][s])
-            continue
-        yr, hr = oracle.scan(p["x"][None, a:a + n], p["dt_raw"][None, a:a + n], p["A"],
-                             p["B"][None, a:a + n], p["C"][None, a:a + n], dt_bias=p["dt_bias"],
-                             D=p["D"], h_init=p["cache"][s][None])
-        assert oracle.rel_l2(y[a:a + n], yr[0]) < tol, r
-        assert oracle.rel_l2(c[s], hr[0]) < tol, r
-    untouched = [s for s in range(rows) if s not in idx]
-    assert np.array_equal(c[untouched], p["cache"][untouched])
+    for zero_D in (False, True):
+        D = np.zeros_like(p["D"]) if zero_D else p["D"]
+        c = _dev(p["cache"])
+        y = ssd.chunk_scan_fwd_varlen(_dev(p["x"], t), _dev(p["dt_raw"]), _dev(p["A"]), _dev(p["B"], t),
+                                      _dev(p["C"], t), _dev(p["cu"]), c, _dev(idx), max_seqlen=max(lens),
+                                      chunk_size=Q, D=_dev(D), dt_bias=_dev(p["dt_bias"]))
+        torch.cuda.synchronize()
+        y, c = _host(y), _host(c)
+        for r, n in enumerate(lens):
+            s, a = idx[r], p["cu"][r]
+            if n == 0:
+                assert np.array_equal(c[s], p["cache"][s])
+                continue
+            yr, hr = oracle.scan(p["x"][None, a:a + n], p["dt_raw"][None, a:a + n], p["A"],
+                                 p["B"][None, a:a + n], p["C"][None, a:a + n], dt_bias=p["dt_bias"],
+                                 D=D, h_init=p["cache"][s][None])
+            assert oracle.rel_l2(y[a:a + n], yr[0]) < tol, (r, zero_D)
+            assert oracle.rel_l2(c[s], hr[0]) < tol, (r, zero_D)
+        untouched = [s for s in range(rows) if s not in idx]
+        assert np.array_equal(c[untouched], p["cache"][untouched])
 
 
 def test_varlen_equals_cached_rows_bitwise():

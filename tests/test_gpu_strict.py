@@ -181,3 +181,43 @@ def test_strict_prefill_is_batch_invariant_and_decode_continues_it():
         yd = _host(_step({k: (p[k][1:2] if k in ("x", "dt_raw", "B", "C") else p[k]) for k in p},
                          s, [t], [0], [t % Q]))
         assert np.array_equal(yd[0], y1[0, t]), t
+
+
+def test_strict_states_and_outputs_against_the_oracle():
+    """The strict path's values against the fp64 oracle (its bitwise tests
+    above compare GPU with GPU): the strict prefill's y with D and with D = 0
+    (D x dominates y), its final states, and the chunk-start states the
+    emulated decode commits to the slots as it crosses chunk boundaries."""
+    import torch
+    rng = np.random.default_rng(31)
+    b, L0, T = 2, Q + 37, 3 * Q
+    p = workloads.random_problem(rng, b, T, H, P, N, G, io="bf16", init=False)
+    for zero_D in (False, True):
+        q = dict(p, D=np.zeros_like(p["D"]) if zero_D else p["D"])
+        s = _Slots(b)
+        y = _cached(q, list(range(b)), L0, s, list(range(b)), True)
+        yr, hr = oracle.scan(q["x"][:, :L0], q["dt_raw"][:, :L0], q["A"], q["B"][:, :L0],
+                             q["C"][:, :L0], dt_bias=q["dt_bias"], D=q["D"])
+        ey, eh = oracle.rel_l2(y, yr), oracle.rel_l2(_host(s.state), hr)
+        print("strict prefill D=%s: y %.3e final %.3e" % ("0" if zero_D else "D", ey, eh), flush=True)
+        assert ey < 2e-2 and eh < 2e-2
+    # the emulated decode from a chunk-aligned prompt of Q tokens: after the
+    # boundary at 2Q each slot holds the oracle's state after 2Q tokens, and
+    # the decode outputs with D = 0 match the oracle's
+    q = dict(p, D=np.zeros_like(p["D"]))
+    s = _Slots(b)
+    _cached(q, list(range(b)), Q, s, list(range(b)), True)
+    ys = []
+    for t in range(Q, T):
+        ys.append(_host(_step(q, s, [t] * b, list(range(b)), [t % Q] * b)))
+        if t == 2 * Q - 1:
+            torch.cuda.synchronize()
+            committed = _host(s.state)
+    torch.cuda.synchronize()
+    yr, _ = oracle.scan(q["x"], q["dt_raw"], q["A"], q["B"], q["C"], dt_bias=q["dt_bias"], D=q["D"])
+    _, h2 = oracle.scan(q["x"][:, :2 * Q], q["dt_raw"][:, :2 * Q], q["A"], q["B"][:, :2 * Q],
+                        q["C"][:, :2 * Q], dt_bias=q["dt_bias"], D=q["D"])
+    ed = oracle.rel_l2(np.stack(ys, axis=1), yr[:, Q:])
+    ec = oracle.rel_l2(committed, h2)
+    print("emulated decode D=0: y %.3e, committed chunk-start state %.3e" % (ed, ec), flush=True)
+    assert ed < 2e-2 and ec < 2e-2
