@@ -54,11 +54,19 @@ typedef enum {
     SSD_ERR_BAD_ARG = 6,       /* dt_min > dt_max, NaN clamp bound, ...            */
     SSD_ERR_ALIAS = 7,         /* an output overlaps an input it must not overlap  */
     SSD_ERR_HIP = 8,           /* a HIP launch returned an error                   */
-    SSD_ERR_TOO_LARGE = 9      /* needs more scratch than the library's static
+    SSD_ERR_TOO_LARGE = 9,     /* needs more scratch than the library's static
                                   buffer holds (allocation-free entry point)       */
+    SSD_ERR_BAD_SEQ_IDX = 10   /* seq_idx decreases along a row (opt-in check)     */
 } ssd_status;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype; /* dtype of x, B, C and y */
+/* dtype of x, B, C and y.  A C caller may pass any int here (others are
+ * rejected with SSD_ERR_BAD_DTYPE); in C++ the enum has int32_t as its fixed
+ * underlying type so that every such value is a valid one, as in C. */
+#ifdef __cplusplus
+typedef enum : int32_t { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+#else
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+#endif
 
 typedef struct {
     int64_t batch;      /* b >= 0                                  */
@@ -80,6 +88,23 @@ size_t ssd_chunk_scan_workspace_bytes(const ssd_dims* dims, ssd_dtype io);
  * rows are cut into segments whose states are chained by an extra pass).
  * Informational; 0 for dims the scan would reject. */
 int64_t ssd_chunk_scan_segments(const ssd_dims* dims, ssd_dtype io);
+
+/*
+ * Opt-in checks of the seq_idx precondition of ssd_chunk_scan_fwd (every row
+ * non-decreasing).  The scan itself never reads seq_idx on the host, so a
+ * violation is not detected there; these calls are for debugging and for
+ * callers that build seq_idx themselves.
+ *   ssd_check_seq_idx_host: seq_idx is a HOST pointer (b, L) int32; pure host
+ *     code.  Returns SSD_OK, SSD_ERR_BAD_SEQ_IDX at the first decrease,
+ *     SSD_ERR_NULL_ARG (NULL with b * L > 0) or SSD_ERR_BAD_SHAPE (b or L < 0,
+ *     or b * L values too many to address).
+ *   ssd_check_seq_idx: seq_idx is a DEVICE pointer; the call copies it to the
+ *     host on `stream`, waits for that copy (it synchronises the stream) and
+ *     checks it as above.  SSD_ERR_BAD_SHAPE as well when b * L > 2^31 (the
+ *     size of the host copy); SSD_ERR_HIP when the copy fails.
+ */
+ssd_status ssd_check_seq_idx_host(const int32_t* seq_idx, int64_t b, int64_t L);
+ssd_status ssd_check_seq_idx(const int32_t* seq_idx, int64_t b, int64_t L, void* stream);
 
 /* 1 when (io, headdim, dstate, chunk_size) is in the compiled set, else 0. */
 int ssd_chunk_scan_supported(ssd_dtype io, int64_t headdim, int64_t dstate,

@@ -115,6 +115,10 @@ def library():
         lib.ssd_state_update_cached.argtypes = [i64, i64, i64, i64, i64, i64, i, vp, vp, vp, vp, vp,
                                                 i, f, f, vp, vp, vp, vp, vp, vp]
         lib.ssd_state_update_cached.restype = i
+        lib.ssd_check_seq_idx_host.argtypes = [vp, i64, i64]
+        lib.ssd_check_seq_idx_host.restype = i
+        lib.ssd_check_seq_idx.argtypes = [vp, i64, i64, vp]
+        lib.ssd_check_seq_idx.restype = i
         lib.ssd_set_timing_events.argtypes = [ctypes.POINTER(vp), i, ctypes.POINTER(i)]
         lib.ssd_set_timing_events.restype = None
         if lib.ssd_abi_version() != 1:
@@ -173,20 +177,41 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def check_seq_idx(seq_idx):
+    """Raise SSDError (SSD_ERR_BAD_SEQ_IDX) if a row of seq_idx (b, L) int32
+    decreases.  A host tensor is checked in place; a device tensor is copied
+    to the host on the current stream first (which synchronises it)."""
+    import torch
+    lib = library()
+    if seq_idx.dtype != torch.int32 or seq_idx.dim() != 2 or not seq_idx.is_contiguous():
+        raise ValueError("seq_idx must be a contiguous (b, L) int32 tensor")
+    b, L = seq_idx.shape
+    if seq_idx.is_cuda:
+        st = lib.ssd_check_seq_idx(_ptr(seq_idx), b, L, _stream_handle(seq_idx.device))
+    else:
+        st = lib.ssd_check_seq_idx_host(seq_idx.data_ptr() if seq_idx.numel() else None, b, L)
+    if st != 0:
+        raise SSDError(st, "ssd_check_seq_idx")
+
+
 def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size: int, D=None, dt_bias=None,
                    initial_states=None, seq_idx=None, dt_softplus: bool = True,
                    dt_limit: Tuple[float, float] = (0.0, math.inf),
                    return_final_states: bool = False, out=None, final_states_out=None,
-                   workspace=None):
+                   workspace=None, check_seq_idx_order: bool = False):
     """Chunked SSD scan.
 
     x (b, L, H, P), B/C (b, L, G, N) in bf16 or fp32 (same dtype); dt (b, L, H),
     A/D/dt_bias (H), initial_states (b, H, P, N) fp32; seq_idx (b, L) int32.
     Returns y (b, L, H, P) in x's dtype, and the final fp32 states
-    (b, H, P, N) when ``return_final_states``.
+    (b, H, P, N) when ``return_final_states``.  ``check_seq_idx_order``: first
+    verify that seq_idx never decreases along a row (a device-to-host copy
+    and a stream synchronisation; off by default).
     """
     import torch
     lib = library()
+    if check_seq_idx_order and seq_idx is not None:
+        check_seq_idx(seq_idx)
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     dev = x.device

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/ssd.h"
 #include "ssd_launch.h"
@@ -224,8 +225,37 @@ const char* ssd_status_string(int s) {
         case SSD_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
         case SSD_ERR_HIP: return "a HIP kernel launch failed";
         case SSD_ERR_TOO_LARGE: return "needs more scratch than the allocation-free entry point's static buffer holds";
+        case SSD_ERR_BAD_SEQ_IDX: return "seq_idx decreases along a row";
         default: return "unknown ssd_status";
     }
+}
+
+ssd_status ssd_check_seq_idx_host(const int32_t* seq_idx, int64_t b, int64_t L) {
+    if (b < 0 || L < 0) return SSD_ERR_BAD_SHAPE;
+    if (b == 0 || L == 0) return SSD_OK;
+    if (!seq_idx) return SSD_ERR_NULL_ARG;
+    // b * L int32 values must fit in the address space
+    if (b > INT64_MAX / int64_t(sizeof(int32_t)) / L) return SSD_ERR_BAD_SHAPE;
+    for (int64_t r = 0; r < b; ++r) {
+        const int32_t* row = seq_idx + r * L;
+        for (int64_t t = 1; t < L; ++t)
+            if (row[t] < row[t - 1]) return SSD_ERR_BAD_SEQ_IDX;
+    }
+    return SSD_OK;
+}
+
+ssd_status ssd_check_seq_idx(const int32_t* seq_idx, int64_t b, int64_t L, void* stream) {
+    if (b < 0 || L < 0) return SSD_ERR_BAD_SHAPE;
+    if (b == 0 || L == 0) return SSD_OK;
+    if (!seq_idx) return SSD_ERR_NULL_ARG;
+    if (L > (int64_t(1) << 31) || b > (int64_t(1) << 31) / L) return SSD_ERR_BAD_SHAPE;
+    std::vector<int32_t> host(static_cast<size_t>(b * L));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(host.data(), seq_idx, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       hs) != hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess)
+        return SSD_ERR_HIP;
+    return ssd_check_seq_idx_host(host.data(), b, L);
 }
 
 int ssd_chunk_scan_supported(ssd_dtype io, int64_t headdim, int64_t dstate, int64_t chunk_size) {

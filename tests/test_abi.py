@@ -37,8 +37,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.ssd_abi_version() == 1
-    for s in range(9):
-        assert lib.ssd_status_string(s)
+    for s in range(11):
+        assert lib.ssd_status_string(s) and b"unknown" not in lib.ssd_status_string(s)
     assert b"unknown" in lib.ssd_status_string(99)
 
 
@@ -412,3 +412,22 @@ def test_gated_norm_rejects_bad_arguments(lib):
     y = buf()
     assert call(y=y, out=y) == ALIAS
     assert call(rows=0) == OK
+
+
+def test_seq_idx_order_check_on_the_host(lib):
+    import numpy as np
+    ok = np.array([[0, 0, 1, 1, 5], [2, 2, 2, 3, 3]], dtype=np.int32)
+    bad = ok.copy()
+    bad[1, 3] = 1  # decreases inside row 1
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.ssd_check_seq_idx_host(ptr(ok), 2, 5) == OK
+    assert lib.ssd_check_seq_idx_host(ptr(bad), 2, 5) == 10  # SSD_ERR_BAD_SEQ_IDX
+    # a decrease across rows is allowed (rows are independent)
+    assert lib.ssd_check_seq_idx_host(ptr(np.array([[4, 5], [0, 1]], dtype=np.int32)), 2, 2) == OK
+    assert lib.ssd_check_seq_idx_host(None, 2, 5) == NULL_ARG
+    assert lib.ssd_check_seq_idx_host(None, 0, 5) == OK
+    assert lib.ssd_check_seq_idx_host(ptr(ok), -1, 5) == BAD_SHAPE
+    import torch
+    ssd.check_seq_idx(torch.from_numpy(ok))
+    with pytest.raises(ssd.SSDError):
+        ssd.check_seq_idx(torch.from_numpy(bad))

@@ -395,3 +395,23 @@ def test_nonfinite_inputs_stay_inside_their_sequence_packed_16k():
     mask[a:e] = False
     assert np.array_equal(Y0[:, mask], Y1[:, mask])
     assert np.array_equal(host(f0), host(f1))
+
+
+def test_seq_idx_order_check_on_the_device():
+    """The opt-in check reads a device seq_idx and rejects a decreasing row;
+    the scan entry point runs it first when asked."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    dev = torch.device("cuda:0")
+    good = torch.tensor([[0, 0, 1, 2, 2, 7]] * 2, dtype=torch.int32, device=dev)
+    bad = good.clone()
+    bad[1, 4] = 1
+    ssd.check_seq_idx(good)
+    with pytest.raises(ssd.SSDError) as e:
+        ssd.check_seq_idx(bad)
+    assert e.value.status == 10
+    b, L, H, P, N, G = 2, 6, 4, 16, 16, 1
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, device=dev, dtype=dt)
+    with pytest.raises(ssd.SSDError):
+        ssd.chunk_scan_fwd(z(b, L, H, P), z(b, L, H), -torch.ones(H, device=dev), z(b, L, G, N),
+                           z(b, L, G, N), chunk_size=64, seq_idx=bad, check_seq_idx_order=True)
