@@ -493,17 +493,11 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
         ctypes.byref(d), real, 1, vx.data_ptr(), vdt.data_ptr(), bias.data_ptr(), 1, 0.0, math.inf,
         A.data_ptr(), vB.data_ptr(), vC.data_ptr(), D.data_ptr(), cud.data_ptr(), pcache.data_ptr(),
         pslots, pidx.data_ptr(), 1, 0, vy.data_ptr(), vws.data_ptr(), vneed, stream())
-    for _ in range(5):
-        if var() != 0:
-            raise RuntimeError("varlen prefill failed")
-    torch.cuda.synchronize()
-    nv = max(steps // 2, 10)
-    t0 = time.perf_counter()
-    for _ in range(nv):
-        var()
-    torch.cuda.synchronize()
-    vwall = (time.perf_counter() - t0) / nv
+    # the same dispatches as the cached prefill, on the packed layout in place
+    vus, vwall = timed(var, len(names), max(steps // 2, 10))
     res["packed_prefill"] = {"sequences": b, "real_tokens": real, "max_seqlen": L,
+                             "kernels_us": {n: round(u, 2) for n, u in zip(names, vus)},
+                             "kernels_total_us": round(sum(vus), 2),
                              "ms_per_call": round(1e3 * vwall, 4),
                              "real_tokens_per_s": round(real / vwall, 1)}
     res["prefill"] = {"rows": b, "row_capacity": L, "real_tokens": real,

@@ -182,16 +182,15 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const ssd_dims* dims, ssd_dtype io, const 
  * operator family 2, kept in slots across prefill and decode).  Row r of the
  * batch is one sequence: its real tokens are [0, seq_lens[r]) of the row
  * (seq_lens NULL: all L; values are clamped to [0, L]); later tokens are
- * padding and leave the state as it is (they enter with dt = 0).  The
+ * padding: they are not read, cost no work past the row's last chunk, and
+ * leave the state as it is.  The
  * row starts from slot state_indices[r] of state_cache (cache_rows, H, P, N)
  * fp32 when init_from_cache != 0, else from zeros, and its state after its
  * last real token is written back to that slot.  An index outside
  * [0, cache_rows) marks a padding row: it is scanned from zeros and its state
  * is dropped.  The indices of the other rows must be distinct (two rows
  * naming one slot race); the library does not read device memory to check.
- * y (b, L, H, P): rows past a row's length are not meaningful.  x, B and C
- * must hold finite values at padding positions too (zeros are the natural
- * fill): padding enters the sums with weight zero.  Other arguments as
+ * y (b, L, H, P): rows past a row's length are not written.  Other arguments as
  * ssd_chunk_scan_fwd (no seq_idx: a row is one sequence).  The workspace
  * (ssd_chunk_scan_cached_workspace_bytes, 256-byte aligned) holds the scan's
  * and the gathered states.  Dispatch order: slot gather, the scan's kernels,
@@ -258,16 +257,17 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
  * sequences back to back, sequence r at tokens [cu_seqlens[r],
  * cu_seqlens[r+1]) (int32 on the device, nseq + 1 entries, non-decreasing
  * from 0 to T).  Each sequence is chunked from its own first token and runs
- * as one row of the cached prefill (ssd_chunk_scan_fwd_cached): it starts
- * from slot state_indices[r] of state_cache (or zeros) and its final state is
- * written back to that slot; strict as there.  y (T, H, P) receives every
- * sequence's outputs in the packed layout.  dims: batch = nseq, seqlen =
- * max_seqlen (no sequence longer; longer ones are cut to it, and offsets
- * outside [0, T] are clamped, so that no access leaves the buffers).  The
- * sequences are copied into rows of max_seqlen tokens in the workspace
- * (ssd_chunk_scan_varlen_workspace_bytes), so the scan's work grows with
- * nseq x max_seqlen.  Timing hooks see the cached prefill's dispatches; the
- * packing copies around them are not bound to events.
+ * as one row of the cached prefill (ssd_chunk_scan_fwd_cached), read and
+ * written in place in the packed layout (no copies, no padding work): it
+ * starts from slot state_indices[r] of state_cache (or zeros) and its final
+ * state is written back to that slot; strict as there.  y (T, H, P) receives
+ * every sequence's outputs.  Its results are bitwise those of the cached
+ * prefill over the same sequences as rows of one batch.  dims: batch = nseq,
+ * seqlen = max_seqlen (no sequence longer: a longer one is cut to it, its
+ * later tokens' y not written; offsets outside [0, T] are clamped, so that no
+ * access leaves the buffers).  Workspace:
+ * ssd_chunk_scan_varlen_workspace_bytes (the cached prefill's).  T = 0 reads
+ * no token (x, dt, B, C, y may be NULL) and treats every sequence as empty.
  */
 size_t ssd_chunk_scan_varlen_workspace_bytes(const ssd_dims* d, ssd_dtype io);
 ssd_status ssd_chunk_scan_fwd_varlen(const ssd_dims* d, int64_t total_tokens, ssd_dtype io,

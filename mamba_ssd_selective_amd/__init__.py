@@ -304,17 +304,37 @@ def chunk_scan_fwd_cached(x, dt, A, B, C, state_cache, state_indices, *, chunk_s
 
 
 def chunk_scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, state_cache, state_indices, *,
-                          max_seqlen: int, chunk_size: int, init_from_cache: bool = True,
-                          strict: bool = False, D=None, dt_bias=None, dt_softplus: bool = True,
+                          chunk_size: int, max_seqlen: Optional[int] = None,
+                          init_from_cache: bool = True, strict: bool = False, D=None,
+                          dt_bias=None, dt_softplus: bool = True,
                           dt_limit: Tuple[float, float] = (0.0, math.inf), out=None,
-                          workspace=None):
+                          workspace=None, check_seqlens: bool = False):
     """Packed variable-length prefill: x (T, H, P), dt (T, H), B/C (T, G, N)
     hold the sequences back to back at offsets ``cu_seqlens`` (nseq + 1,
     int32); sequence r is chunked from its own start, begins at slot
     state_indices[r] of ``state_cache`` (zeros unless ``init_from_cache``) and
-    leaves its final state there.  Returns y (T, H, P)."""
+    leaves its final state there.  Returns y (T, H, P).
+
+    ``max_seqlen`` bounds every sequence's length (the library cuts longer
+    ones to it).  None: it is computed from cu_seqlens, which reads the
+    offsets back to the host (a synchronisation).  ``check_seqlens``: read
+    them back and raise ValueError unless they run from 0 to T without
+    decreasing and no sequence is longer than max_seqlen."""
     import torch
     lib = library()
+    if max_seqlen is None or check_seqlens:
+        cu = cu_seqlens.detach().to("cpu", torch.int64)
+        lens = cu[1:] - cu[:-1]
+        longest = int(lens.max()) if lens.numel() else 0
+        if check_seqlens:
+            if cu.numel() == 0 or int(cu[0]) != 0 or int(cu[-1]) != x.shape[0] or \
+                    (lens.numel() and int(lens.min()) < 0):
+                raise ValueError("cu_seqlens must rise from 0 to the packed token count")
+            if max_seqlen is not None and longest > max_seqlen:
+                raise ValueError("a sequence of %d tokens is longer than max_seqlen %d"
+                                 % (longest, max_seqlen))
+        if max_seqlen is None:
+            max_seqlen = longest
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     S = cu_seqlens.shape[0] - 1

@@ -148,7 +148,7 @@ ssd_status check_scan_dims(const ssd_dims* d, ssd_dtype io) {
         return SSD_ERR_BAD_SHAPE;
     if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
     // index and grid limits: element offsets fit in int64, rows/heads in int
-    if (d->batch > 65535 || d->nheads > 65535 || d->seqlen > (int64_t(1) << 31))
+    if (d->batch > 65535 || d->nheads > 65535 || d->seqlen >= (int64_t(1) << 31))
         return SSD_ERR_BAD_SHAPE;
     if (!ssd::find_scan_variant(io, d->headdim, d->dstate, d->chunk_size))
         return SSD_ERR_UNSUPPORTED;
@@ -163,7 +163,7 @@ ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
         d->ngroups < 1 || d->chunk_size < 1)
         return SSD_ERR_BAD_SHAPE;
     if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
-    if (d->batch > 65535 || d->nheads > 65535 || d->seqlen > (int64_t(1) << 31))
+    if (d->batch > 65535 || d->nheads > 65535 || d->seqlen >= (int64_t(1) << 31))
         return SSD_ERR_BAD_SHAPE;
     if (io != SSD_BF16 || d->headdim != 64 || d->dstate != 128 || d->chunk_size != 128)
         return SSD_ERR_UNSUPPORTED;
@@ -278,9 +278,11 @@ int64_t ssd_chunk_scan_segments(const ssd_dims* d, ssd_dtype io) {
 
 namespace {
 
-// The forward scan.  row_len (b) or null: row r's tokens from row_len[r] on
-// are padding.  k counts the dispatches of the calling entry point; before()
-// runs once the arguments are validated, ahead of the scan's first launch.
+// The forward scan.  row_len (b) or null: row r ends after row_len[r]
+// tokens.  cu (b + 1) or null: packed rows, row r is tokens [cu[r], cu[r+1])
+// of the T tokens of x, dt, B, C and y (no seq_idx then).  k counts the
+// dispatches of the calling entry point; before() runs once the arguments are
+// validated, ahead of the scan's first launch.
 template <typename F>
 ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
                          const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
@@ -288,7 +290,7 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
                          const float* initial_states, const int32_t* seq_idx,
                          const int32_t* row_len, void* y, float* final_states, void* workspace,
                          size_t workspace_bytes, hipStream_t hs, int& k, F&& before,
-                         bool one_segment = false) {
+                         bool one_segment = false, const int32_t* cu = nullptr, int64_t T = 0) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
     if (one_segment && !ssd::find_scan_variant(io, d->headdim, d->dstate, d->chunk_size, true))
@@ -296,6 +298,9 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim,
                   N = d->dstate, G = d->ngroups;
+    if (cu && (seq_idx || row_len || T < 0)) return SSD_ERR_BAD_ARG;
+    // tokens of x, dt, B, C and y
+    const int64_t toks = cu ? T : b * L;
     const bool work = b > 0 && L > 0;
     if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
     const Plan plan = make_plan(*d, io, one_segment);
@@ -311,12 +316,12 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
         return SSD_ERR_ALIAS;
     const size_t es = io_size(io);
     const Span in_spans[] = {
-        span(x, b * L * H * P * es), span(dt, b * L * H * 4), span(B, b * L * G * N * es),
-        span(C, b * L * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+        span(x, toks * H * P * es), span(dt, toks * H * 4), span(B, toks * G * N * es),
+        span(C, toks * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
         span(D, D ? H * 4 : 0), span(seq_idx, seq_idx ? b * L * 4 : 0),
-        span(row_len, row_len ? b * 4 : 0),
+        span(row_len, row_len ? b * 4 : 0), span(cu, cu ? (b + 1) * 4 : 0),
     };
-    const Span ys = span(y, b * L * H * P * es);
+    const Span ys = span(y, toks * H * P * es);
     const Span fs = span(final_states, final_states ? b * H * P * N * 4 : 0);
     const Span is = span(initial_states, initial_states ? b * H * P * N * 4 : 0);
     const Span ws = span(workspace, plan.total);
@@ -354,6 +359,8 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     sa.dt_max = dt_max;
     sa.seq_idx = seq_idx;
     sa.row_len = row_len;
+    sa.cu = cu;
+    sa.T = T;
     sa.exact_decay = one_segment ? 1 : 0;
     sa.D = D;
     sa.init = initial_states;
@@ -485,14 +492,16 @@ size_t ssd_chunk_scan_cached_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
            align_up(static_cast<size_t>(d->batch * d->nheads * d->headdim * d->dstate) * 4);
 }
 
-ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void* x,
-                                     const float* dt, const float* dt_bias, int dt_softplus,
-                                     float dt_min, float dt_max, const float* A, const void* B,
-                                     const void* C, const float* D, const int32_t* seq_lens,
-                                     float* state_cache, int64_t cache_rows,
-                                     const int32_t* state_indices, int init_from_cache, int strict,
-                                     void* y, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+// The prefill of rows whose states live in cache slots: the rows are
+// row_len-limited rows of L tokens (cu null) or packed rows at offsets cu
+// into T tokens.
+static ssd_status cached_prefill(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
+                                 const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
+                                 const float* A, const void* B, const void* C, const float* D,
+                                 const int32_t* seq_lens, const int32_t* cu, int64_t T,
+                                 float* state_cache, int64_t cache_rows,
+                                 const int32_t* state_indices, int init_from_cache, int strict,
+                                 void* y, void* workspace, size_t workspace_bytes, void* stream) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
@@ -508,13 +517,14 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
         return SSD_ERR_WORKSPACE;
     const size_t es = io_size(io);
     const int64_t G = d->ngroups;
+    const int64_t toks = cu ? T : b * L;
     const Span cs = span(state_cache, cache_rows * H * P * N * 4);
     const Span others[] = {
-        span(x, b * L * H * P * es), span(dt, b * L * H * 4), span(B, b * L * G * N * es),
-        span(C, b * L * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
+        span(x, toks * H * P * es), span(dt, toks * H * 4), span(B, toks * G * N * es),
+        span(C, toks * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
         span(D, D ? H * 4 : 0), span(seq_lens, seq_lens ? b * 4 : 0),
-        span(state_indices, state_indices ? b * 4 : 0), span(y, b * L * H * P * es),
-        span(workspace, need)};
+        span(cu, cu ? (b + 1) * 4 : 0), span(state_indices, state_indices ? b * 4 : 0),
+        span(y, toks * H * P * es), span(workspace, need)};
     for (const Span& o : others)
         if (overlap(cs, o)) return SSD_ERR_ALIAS;
     int k = 0;
@@ -546,7 +556,7 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
                                    init_from_cache ? state_cache : nullptr, state_indices,
                                    cache_rows, states, b, per_row, hs);
                            });
-                       }, strict != 0);
+                       }, strict != 0, cu, T);
     if (st != SSD_OK) return st;
     if (timed_launch(k, hs, [&] {
             return ssd::launch_scatter_slots(states, state_indices, cache_rows, state_cache, b,
@@ -554,6 +564,19 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
         }) != hipSuccess)
         return SSD_ERR_HIP;
     return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void* x,
+                                     const float* dt, const float* dt_bias, int dt_softplus,
+                                     float dt_min, float dt_max, const float* A, const void* B,
+                                     const void* C, const float* D, const int32_t* seq_lens,
+                                     float* state_cache, int64_t cache_rows,
+                                     const int32_t* state_indices, int init_from_cache, int strict,
+                                     void* y, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    return cached_prefill(d, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D, seq_lens,
+                          nullptr, 0, state_cache, cache_rows, state_indices, init_from_cache,
+                          strict, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -727,14 +750,7 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
 }
 
 size_t ssd_chunk_scan_varlen_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
-    if (check_scan_dims(d, io) != SSD_OK || d->batch == 0 || d->seqlen == 0) return 0;
-    const size_t es = io_size(io);
-    const size_t rows = static_cast<size_t>(d->batch * d->seqlen);
-    const size_t hp = static_cast<size_t>(d->nheads * d->headdim);
-    const size_t gn = static_cast<size_t>(d->ngroups * d->dstate);
-    return ssd_chunk_scan_cached_workspace_bytes(d, io) + align_up(rows * hp * es) +
-           align_up(rows * static_cast<size_t>(d->nheads) * 4) + 2 * align_up(rows * gn * es) +
-           align_up(rows * hp * es) + align_up(static_cast<size_t>(d->batch) * 4);
+    return ssd_chunk_scan_cached_workspace_bytes(d, io);
 }
 
 ssd_status ssd_chunk_scan_fwd_varlen(const ssd_dims* d, int64_t total_tokens, ssd_dtype io,
@@ -747,82 +763,18 @@ ssd_status ssd_chunk_scan_fwd_varlen(const ssd_dims* d, int64_t total_tokens, ss
                                      size_t workspace_bytes, void* stream) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
-    const int64_t S = d->batch, Lmax = d->seqlen, T = total_tokens, H = d->nheads,
-                  P = d->headdim, N = d->dstate, G = d->ngroups;
-    if (T < 0 || T > (int64_t(1) << 40) || S > 65535) return SSD_ERR_BAD_SHAPE;
-    if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
-    if (S == 0 || Lmax == 0) return SSD_OK;
-    if (!cu_seqlens || !y || (T > 0 && (!x || !dt || !B || !C))) return SSD_ERR_NULL_ARG;
-    // the cached prefill's own checks that do not involve the rows, before the
-    // packing copy runs
-    if (!state_cache || !state_indices || !A) return SSD_ERR_NULL_ARG;
-    if (cache_rows < 0 || cache_rows >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
-    if (cache_rows > 0 && H * P * N > (int64_t(1) << 60) / 4 / cache_rows) return SSD_ERR_BAD_SHAPE;
-    if (!aligned16(state_cache)) return SSD_ERR_BAD_ARG;
-    const size_t es = io_size(io);
-    const size_t need = ssd_chunk_scan_varlen_workspace_bytes(d, io);
-    if (!workspace || workspace_bytes < need ||
-        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
-        return SSD_ERR_WORKSPACE;
-    const void* word_bufs[] = {x, dt, B, C, y};
-    for (const void* p : word_bufs)
-        if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
-    const Span ys = span(y, T * H * P * es);
-    const Span ins[] = {span(x, T * H * P * es), span(dt, T * H * 4), span(B, T * G * N * es),
-                        span(C, T * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
-                        span(D, D ? H * 4 : 0), span(cu_seqlens, (S + 1) * 4),
-                        span(state_indices, state_indices ? S * 4 : 0),
-                        span(state_cache, state_cache ? cache_rows * H * P * N * 4 : 0),
-                        span(workspace, need)};
-    for (const Span& o : ins)
-        if (overlap(ys, o)) return SSD_ERR_ALIAS;
-    const Span cs = span(state_cache, state_cache ? cache_rows * H * P * N * 4 : 0);
-    for (size_t i = 0; i + 2 < sizeof(ins) / sizeof(ins[0]); ++i)
-        if (overlap(cs, ins[i])) return SSD_ERR_ALIAS;
-    if (overlap(cs, span(workspace, need))) return SSD_ERR_ALIAS;
-    // the rows and the cached prefill's workspace
-    const size_t rows = static_cast<size_t>(S * Lmax);
-    char* wsb = static_cast<char*>(workspace);
-    const size_t cws = ssd_chunk_scan_cached_workspace_bytes(d, io);
-    size_t off = cws;
-    ssd::VarlenArgs va{};
-    va.x = x;
-    va.dt = dt;
-    va.B = B;
-    va.C = C;
-    va.cu = cu_seqlens;
-    va.xw = wsb + off;
-    off += align_up(rows * H * P * es);
-    va.dtw = reinterpret_cast<float*>(wsb + off);
-    off += align_up(rows * H * 4);
-    va.bw = wsb + off;
-    off += align_up(rows * G * N * es);
-    va.cw = wsb + off;
-    off += align_up(rows * G * N * es);
-    void* yw = wsb + off;
-    va.yw = yw;
-    off += align_up(rows * H * P * es);
-    va.row_len = reinterpret_cast<int32_t*>(wsb + off);
-    va.y = y;
-    va.nseq = S;
-    va.T = T;
-    va.Lmax = Lmax;
-    const int64_t xb = H * P * static_cast<int64_t>(es), gb = G * N * static_cast<int64_t>(es);
-    const bool wide = xb % 16 == 0 && gb % 16 == 0 && (H * 4) % 16 == 0;
-    const int64_t word = wide ? 16 : 4;
-    if (xb % 4 != 0 || gb % 4 != 0) return SSD_ERR_UNSUPPORTED;
-    va.wx = xb / word;
-    va.wd = H * 4 / word;
-    va.wb = gb / word;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (ssd::launch_varlen_pack(va, wide, hs) != hipSuccess) return SSD_ERR_HIP;
-    st = ssd_chunk_scan_fwd_cached(d, io, va.xw, va.dtw, dt_bias, dt_softplus, dt_min, dt_max, A,
-                                   va.bw, va.cw, D, va.row_len, state_cache, cache_rows,
-                                   state_indices, init_from_cache, strict, yw, workspace, cws,
-                                   stream);
-    if (st != SSD_OK) return st;
-    if (ssd::launch_varlen_unpack(va, wide, hs) != hipSuccess) return SSD_ERR_HIP;
-    return SSD_OK;
+    const int64_t T = total_tokens;
+    if (T < 0 || T > (int64_t(1) << 40)) return SSD_ERR_BAD_SHAPE;
+    if (d->batch > 0 && !cu_seqlens) return SSD_ERR_NULL_ARG;
+    // an empty packed batch reads no token
+    if (d->batch > 0 && d->seqlen > 0 && T > 0 && (!x || !dt || !B || !C || !y))
+        return SSD_ERR_NULL_ARG;
+    // no tokens at all: as for rows of no tokens (nothing is read)
+    ssd_dims dd = *d;
+    if (T == 0) dd.seqlen = 0;
+    return cached_prefill(&dd, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D,
+                          nullptr, cu_seqlens, T, state_cache, cache_rows, state_indices,
+                          init_from_cache, strict, y, workspace, workspace_bytes, stream);
 }
 
 size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* d, ssd_dtype io) {

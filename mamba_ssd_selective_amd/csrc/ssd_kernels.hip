@@ -125,13 +125,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     const int c = static_cast<int>(w % a.nc);
     const int64_t b = w / a.nc;
     const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const int64_t tl = a.L - 1;
-    // tokens from here on carry no state (dt 0): the row's end, or its length
-    int64_t t_end = a.L;
-    if (a.row_len) {
-        const int64_t rl = a.row_len[b];
-        t_end = rl < 0 ? 0 : (rl < a.L ? rl : a.L);
-    }
+    const RowSpan rs = row_span(a, b);
+    // a chunk past the row's end: the scan kernels never read its data
+    if (t0 >= rs.len) return;
+    const int64_t tl = rs.len - 1;  // loads past it are clamped to it (and masked)
+    const int64_t t_end = rs.len;
+    const int64_t r0 = rs.t0;
     const T* __restrict__ Bp = static_cast<const T*>(a.B);
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
 
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     for (int k = 0; k < E; ++k) {
         int64_t t = t0 + lane * E + k;
         t = t < tl ? t : tl;
-        sq[k] = has_seq ? a.seq_idx[b * a.L + t] : 0;
+        sq[k] = has_seq ? a.seq_idx[r0 + t] : 0;
     }
     float raw0[E];
     {
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         for (int k = 0; k < E; ++k) {
             int64_t tt = t0 + lane * E + k;
             tt = tt < tl ? tt : tl;
-            raw0[k] = a.dt_raw[(b * a.L + tt) * a.H + h];
+            raw0[k] = a.dt_raw[(r0 + tt) * a.H + h];
         }
     }
 
@@ -171,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         n0 = n0 < N ? n0 : N - kV;
         int64_t t = t0 + j;
         t = t < tl ? t : tl;
-        rb[k] = ld_raw16(Bp + ((b * a.L + t) * a.G + g) * N + n0);
-        rc[k] = ld_raw16(Cp + ((b * a.L + t) * a.G + g) * N + n0);
+        rb[k] = ld_raw16(Bp + ((r0 + t) * a.G + g) * N + n0);
+        rc[k] = ld_raw16(Cp + ((r0 + t) * a.G + g) * N + n0);
     }
 
     // ---- per-head chunk metadata
@@ -239,14 +238,14 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         for (int k = 0; k < E; ++k) {
             int64_t tt = t0 + lane * E + k;
             tt = tt < tl ? tt : tl;
-            raw[k] = a.dt_raw[(b * a.L + tt) * a.H + g * hpg + hh];
+            raw[k] = a.dt_raw[(r0 + tt) * a.H + g * hpg + hh];
         }
         head_meta(hh, raw);
     }
 
     if constexpr (kTiles) {
         // ---- stage B and C rows (tokens past L and columns past N are zero)
-        const int64_t valid = a.L - t0;
+        const int64_t valid = rs.len - t0;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const int li = threadIdx.x + kThreads * k;
@@ -345,13 +344,13 @@ struct Prefetch {
 
 template <typename T, int P, int N, int Q>
 __device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q>& pf, const ScanArgs& a,
-                                               const WorkItem& it, int c) {
+                                               const WorkItem& it, const RowSpan& rs, int c) {
     using C_ = Cfg<T, P, N, Q>;
     using PF = Prefetch<T, P, N, Q>;
     constexpr int kV = C_::kVec;
     const int tid = threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const int64_t tl = a.L - 1;
+    const int64_t tl = rs.len - 1;  // c < the row's chunks: tl >= t0
     const T* __restrict__ x = static_cast<const T*>(a.x);
     const T* __restrict__ Bp = static_cast<const T*>(a.B);
 #pragma unroll
@@ -363,7 +362,7 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q>& pf, const S
         for (int r = 0; r < 4; ++r) {
             int64_t t = t0 + j0 + r;
             t = t < tl ? t : tl;
-            pf.xr[k][r] = ld_raw16(x + ((it.b * a.L + t) * a.H + it.h) * P + p0);
+            pf.xr[k][r] = ld_raw16(x + ((rs.t0 + t) * a.H + it.h) * P + p0);
         }
     }
 #pragma unroll
@@ -375,7 +374,7 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q>& pf, const S
         for (int r = 0; r < 4; ++r) {
             int64_t t = t0 + j0 + r;
             t = t < tl ? t : tl;
-            pf.br[k][r] = ld_raw16(Bp + ((it.b * a.L + t) * a.G + it.g) * N + n0);
+            pf.br[k][r] = ld_raw16(Bp + ((rs.t0 + t) * a.G + it.g) * N + n0);
         }
     }
     const int64_t mo = meta_offset(a, it.b, it.h, c, Q);
@@ -387,7 +386,7 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q>& pf, const S
         const float* src = arr == 0 ? a.cs : (arr == 1 ? a.dtv : a.wgt);
         pf.mr[k] = ld_raw16(src + mo + off);
     }
-    // without seq_idx the id loads read dt_raw (at least b*L elements of 4 bytes)
+    // without seq_idx the id loads read dt_raw (H >= 1 values per token)
     // and the values are replaced by 0 at staging, so no load here sits behind
     // a branch
     const int32_t* __restrict__ sqp =
@@ -396,9 +395,9 @@ __device__ __forceinline__ void prefetch_chunk(Prefetch<T, P, N, Q>& pf, const S
     for (int k = 0; k < PF::SP; ++k) {
         int64_t t = t0 + tid + kThreads * k;
         t = t < tl ? t : tl;
-        pf.sq[k] = sqp[it.b * a.L + t];
+        pf.sq[k] = sqp[rs.t0 + t];
     }
-    pf.seq_prev = sqp[it.b * a.L + (c == 0 ? 0 : t0 - 1)];
+    pf.seq_prev = sqp[rs.t0 + (c == 0 ? 0 : t0 - 1)];
 }
 
 // B^T * w: column E of one 4-token x kVec block of B, scaled by w_j and
@@ -619,22 +618,23 @@ struct RowOps {
 
 template <typename T, int P, int N, int Q>
 __device__ __forceinline__ void load_row_ops(RowOps<T, P, N, Q>& ro, const ScanArgs& a,
-                                             const WorkItem& it, int c, int I, int lane) {
+                                             const WorkItem& it, const RowSpan& rs, int c, int I,
+                                             int lane) {
     using C_ = Cfg<T, P, N, Q>;
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
     const int r16 = lane & 15, q = lane >> 4;
     int64_t ti = static_cast<int64_t>(c) * Q + 16 * I + r16;
-    ti = ti < a.L ? ti : a.L - 1;
+    ti = ti < rs.len ? ti : rs.len - 1;
 #pragma unroll
     for (int s = 0; s < C_::KN; ++s) {
         int n0 = 32 * s + 8 * q;
         n0 = n0 < N ? n0 : N - 8;
-        ro.cf[s] = raw_frag_load8(Cp + ((it.b * a.L + ti) * a.G + it.g) * N + n0);
+        ro.cf[s] = raw_frag_load8(Cp + ((rs.t0 + ti) * a.G + it.g) * N + n0);
     }
     const T* __restrict__ x = static_cast<const T*>(a.x);
 #pragma unroll
     for (int pb = 0; pb < C_::PB; ++pb) {
-        const T* px = x + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q;
+        const T* px = x + ((rs.t0 + ti) * a.H + it.h) * P + 16 * pb + 4 * q;
         if constexpr (sizeof(T) == 2) ro.xd[pb] = *reinterpret_cast<const uint2*>(px);
         else ro.xd[pb] = ld_raw16(px);
     }
@@ -688,15 +688,15 @@ __device__ __forceinline__ void load_intra_x(IntraX<T, P, N, Q>& o, const T* sX,
 template <typename T, int P, int N, int Q>
 __device__ __forceinline__ void row_block_outputs(const RowOps<T, P, N, Q>& ro, const ChunkMeta<Q>& m,
                                                   const T* sX, const T* sH, const ScanArgs& a,
-                                                  const WorkItem& it, int c, int I, float Dh,
-                                                  bool has_seq, int lane) {
+                                                  const WorkItem& it, const RowSpan& rs, int c,
+                                                  int I, float Dh, bool has_seq, int lane) {
     using C_ = Cfg<T, P, N, Q>;
     const int r16 = lane & 15, q = lane >> 4;
     const int i = 16 * I + r16;
     const int64_t ti = static_cast<int64_t>(c) * Q + i;
     Frag<T> cf[C_::KN];
 #pragma unroll
-    for (int s = 0; s < C_::KN; ++s) cf[s] = frag_from_raw(ro.cf[s], ti < a.L && 32 * s + 8 * q < N);
+    for (int s = 0; s < C_::KN; ++s) cf[s] = frag_from_raw(ro.cf[s], ti < rs.len && 32 * s + 8 * q < N);
     f32x4_t acc[C_::PB];
 #pragma unroll
     for (int pb = 0; pb < C_::PB; ++pb) acc[pb] = acc_zero();
@@ -776,13 +776,13 @@ __device__ __forceinline__ void row_block_outputs(const RowOps<T, P, N, Q>& ro, 
             for (int pb = 0; pb < C_::PB; ++pb) mma(acc[pb], cur.xf[pb], gf);
         }
     }
-    if (ti < a.L) {
+    if (ti < rs.len) {
         T* __restrict__ y = static_cast<T*>(a.y);
 #pragma unroll
         for (int pb = 0; pb < C_::PB; ++pb) {
             const float x0 = raw_elem_f32<T, 0>(ro.xd[pb]), x1 = raw_elem_f32<T, 1>(ro.xd[pb]);
             const float x2 = raw_elem_f32<T, 2>(ro.xd[pb]), x3 = raw_elem_f32<T, 3>(ro.xd[pb]);
-            store4_f32(y + ((it.b * a.L + ti) * a.H + it.h) * P + 16 * pb + 4 * q,
+            store4_f32(y + ((rs.t0 + ti) * a.H + it.h) * P + 16 * pb + 4 * q,
                        acc[pb][0] + Dh * x0, acc[pb][1] + Dh * x1, acc[pb][2] + Dh * x2,
                        acc[pb][3] + Dh * x3);
         }
@@ -807,8 +807,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t bh = it.b * a.H + it.h;
     const float Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
+    const RowSpan rs = row_span(a, it.b);
+    const int nc_row = static_cast<int>((rs.len + Q - 1) / Q);
     const int c_begin = it.seg * a.cps;
-    const int c_end = min(c_begin + a.cps, a.nc);
+    const int c_end = min(c_begin + a.cps, nc_row);  // none when the row ends earlier
     const bool last_seg = kOut && it.seg == a.nseg - 1;
     const bool has_seq = a.seq_idx != nullptr;
 
@@ -831,11 +833,13 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     float mult = 1.0f;
 
     Prefetch<T, P, N, Q> pf;
-    prefetch_chunk<T, P, N, Q>(pf, a, it, c_begin);
-    stage_meta<T, P, N, Q>(pf, meta, has_seq);
-    __syncthreads();
-    stage_tiles<T, P, N, Q>(pf, meta, sX, sBw, a.L - static_cast<int64_t>(c_begin) * Q);
-    __syncthreads();
+    if (c_begin < c_end) {
+        prefetch_chunk<T, P, N, Q>(pf, a, it, rs, c_begin);
+        stage_meta<T, P, N, Q>(pf, meta, has_seq);
+        __syncthreads();
+        stage_tiles<T, P, N, Q>(pf, meta, sX, sBw, rs.len - static_cast<int64_t>(c_begin) * Q);
+        __syncthreads();
+    }
 
     for (int c = c_begin; c < c_end; ++c) {
         const bool has_next = c + 1 < c_end;
@@ -846,9 +850,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int r = 0; r < C_::RB; ++r)
                 if (row_block_valid<C_::NB>(wave))
-                    load_row_ops<T, P, N, Q>(ro[r], a, it, c, row_block<C_::NB>(wave, r), lane);
+                    load_row_ops<T, P, N, Q>(ro[r], a, it, rs, c, row_block<C_::NB>(wave, r), lane);
         }
-        if (has_next) prefetch_chunk<T, P, N, Q>(pf, a, it, c + 1);
+        if (has_next) prefetch_chunk<T, P, N, Q>(pf, a, it, rs, c + 1);
         if (need_state) {
             const bool keep = meta.seq[Q - 1] == meta.seq_prev;
             const float e = decay_exp(meta.cs[Q - 1]);
@@ -860,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int r = 0; r < C_::RB; ++r)
                 if (row_block_valid<C_::NB>(wave))
-                    row_block_outputs<T, P, N, Q>(ro[r], meta, sX, sH, a, it, c,
+                    row_block_outputs<T, P, N, Q>(ro[r], meta, sX, sH, a, it, rs, c,
                                                   row_block<C_::NB>(wave, r), Dh, has_seq, lane);
         }
         __syncthreads();  // every read of this chunk's LDS data is done
@@ -868,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
             if constexpr (kOut) state_to_lds<T, P, N, Q>(hreg, sH, wave, lane);
             stage_meta<T, P, N, Q>(pf, meta, has_seq);
             __syncthreads();
-            stage_tiles<T, P, N, Q>(pf, meta, sX, sBw, a.L - static_cast<int64_t>(c + 1) * Q);
+            stage_tiles<T, P, N, Q>(pf, meta, sX, sBw, rs.len - static_cast<int64_t>(c + 1) * Q);
             __syncthreads();
         }
     }

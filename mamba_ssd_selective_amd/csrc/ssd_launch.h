@@ -20,9 +20,14 @@ struct ScanArgs {
     int softplus;
     float dt_min, dt_max;
     const int32_t* seq_idx; // (b, L) or null
-    // (b) or null: row b's tokens from row_len[b] on are padding (dt 0: they
-    // leave the state as it is; their y rows are not meaningful)
+    // Where each row's tokens are (see row_span): by default row b is tokens
+    // [b L, b L + L) of x, dt, B, C and y.  row_len (b) or null: row b ends
+    // after row_len[b] tokens (clamped to [0, L]); its later tokens are
+    // neither read nor written.  cu (b + 1) or null: packed rows, row b is
+    // tokens [cu[b], cu[b+1]) of T (offsets clamped into [0, T], lengths to L).
     const int32_t* row_len;
+    const int32_t* cu;
+    int64_t T;
     // 1: every chunk takes the per-element exp(cs_i - cs_j) form of the
     // intra-chunk decay (no factoring), so that a token's output does not
     // depend on the tokens after it in its chunk (the strict mode)
@@ -259,28 +264,6 @@ struct EmulArgs {
 // wide: the stage copies 16-byte words (widths wx, wd, wb given in them)
 hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st);
 hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st);
-
-// Packed variable-length prefill: packed tokens (T of them, cu_seqlens
-// offsets) <-> one row of Lmax tokens per sequence.  Widths in words (4 or 16
-// bytes): wx = H*P*io, wd = H*4, wb = G*N*io bytes per token.
-struct VarlenArgs {
-    const void* x;            // (T, H, P) io
-    const float* dt;          // (T, H)
-    const void* B;            // (T, G, N) io
-    const void* C;            // (T, G, N) io
-    const int32_t* cu;        // (nseq + 1)
-    void* xw;                 // (nseq, Lmax, H, P) io
-    float* dtw;               // (nseq, Lmax, H)
-    void* bw;                 // (nseq, Lmax, G, N) io
-    void* cw;                 // (nseq, Lmax, G, N) io
-    int32_t* row_len;         // (nseq)
-    const void* yw;           // (nseq, Lmax, H, P) io
-    void* y;                  // (T, H, P) io
-    int64_t nseq, T, Lmax;
-    int64_t wx, wd, wb;
-};
-hipError_t launch_varlen_pack(const VarlenArgs& a, bool wide, hipStream_t st);
-hipError_t launch_varlen_unpack(const VarlenArgs& a, bool wide, hipStream_t st);
 
 // Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros
 // for an index outside [0, rows) or when cache is null); scatter row r to slot

@@ -803,10 +803,13 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
     k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
     const int64_t bh = it.b * a.H + it.h;
-    k.L = static_cast<int>(a.L);
+    const RowSpan rs = row_span(a, it.b);
+    k.L = static_cast<int>(rs.len);
     k.nc = a.nc;
     k.c_begin = it.seg * a.cps;
-    k.c_end = min(k.c_begin + a.cps, a.nc);
+    // no chunks when the row ends before this segment
+    k.c_end = min(k.c_begin + a.cps, static_cast<int>((rs.len + Q - 1) / Q));
+    const bool any = k.c_begin < k.c_end;
     k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr;
     k.out_wave_ = kOut && k.wave < G_::NB;
     k.I = kOut && k.wave < kTrWaves ? tr_row_block<G_::NB>(k.wave) : 0;
@@ -815,20 +818,19 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.mult = 1.0f;
     k.xstride = a.H * P * 2;
     k.bstride = a.G * N * 2;
-    k.xg = static_cast<const uint16_t*>(a.x) + (it.b * a.L * a.H + it.h) * P;
-    k.bg = static_cast<const uint16_t*>(a.B) + (it.b * a.L * a.G + it.g) * N;
+    k.xg = static_cast<const uint16_t*>(a.x) + (rs.t0 * a.H + it.h) * P;
+    k.bg = static_cast<const uint16_t*>(a.B) + (rs.t0 * a.G + it.g) * N;
     k.cm_cstride = static_cast<int64_t>(a.G) * Q * N;
     k.cmg = static_cast<const uint16_t*>(a.cmf) + (it.b * a.nc * a.G + it.g) * static_cast<int64_t>(Q) * N;
-    k.yg = static_cast<uint16_t*>(a.y) + (it.b * a.L * a.H + it.h) * P;
+    k.yg = static_cast<uint16_t*>(a.y) + (rs.t0 * a.H + it.h) * P;
     k.mg = a.cs + meta_offset(a, it.b, it.h, 0, Q);
-    k.sqg = a.seq_idx ? a.seq_idx + it.b * a.L : nullptr;
+    k.sqg = a.seq_idx ? a.seq_idx + rs.t0 : nullptr;
     k.cb_cstride = static_cast<int64_t>(a.G) * cbt_elems_per_chunk_group(Q);
     k.cbg = static_cast<const uint16_t*>(a.cbt) + (it.b * a.nc * a.G + it.g) * (k.cb_cstride / a.G);
+    k.seq_prev = 0;
     if constexpr (kSeq) {
         const int64_t tp = k.c_begin == 0 ? 0 : static_cast<int64_t>(k.c_begin) * Q - 1;
-        k.seq_prev = a.seq_idx[it.b * a.L + tp];
-    } else {
-        k.seq_prev = 0;
+        if (any) k.seq_prev = a.seq_idx[rs.t0 + tp];
     }
 
     // lane addresses and copy offsets, fixed for the whole segment
@@ -867,9 +869,11 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     // registers are live only in its own code; both roles pass the same number
     // of barriers (one after the first copies, one per chunk).
     if (k.ow()) {
-        k.load_c(k.c_begin);
-        k.load_cb(k.c_begin);
-        k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+        if (any) {
+            k.load_c(k.c_begin);
+            k.load_cb(k.c_begin);
+            k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         for (int c = k.c_begin; c < k.c_end; c += 2) {
@@ -881,7 +885,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
         // incoming state.  Output kernel: the initial state (or zero) carried
         // through the end states of the earlier segments, and its bf16 operand
         // copy in H[0].
-        k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
+        if (any) k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
         k.state_load(kOut && a.init ? a.init + bh * P * N : nullptr);
         if constexpr (kOut) {
             if (k.st()) k.state_carry(a.seg_mult + bh * a.nseg, a.seg_state + bh * a.nseg * P * N, it.seg);

@@ -37,6 +37,33 @@ __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid
     return it;
 }
 
+// The tokens of row b: the first one's index in x, dt, B, C, y and seq_idx
+// (counted in tokens) and how many there are.  Chunk c of the row is tokens
+// [c Q, min(c Q + Q, len)) from there; chunks at or past len are not part of
+// it (no kernel reads or writes their data).
+struct RowSpan {
+    int64_t t0;
+    int64_t len;  // <= L
+};
+__device__ __forceinline__ RowSpan row_span(const ScanArgs& a, int64_t b) {
+    RowSpan r;
+    if (a.cu) {
+        int64_t lo = a.cu[b], hi = a.cu[b + 1];
+        lo = lo < 0 ? 0 : (lo > a.T ? a.T : lo);
+        hi = hi < lo ? lo : (hi > a.T ? a.T : hi);
+        r.t0 = lo;
+        r.len = hi - lo < a.L ? hi - lo : a.L;
+    } else {
+        r.t0 = b * a.L;
+        r.len = a.L;
+        if (a.row_len) {
+            const int64_t rl = a.row_len[b];
+            r.len = rl < 0 ? 0 : (rl < a.L ? rl : a.L);
+        }
+    }
+    return r;
+}
+
 // Offset of chunk c of (row b, head h) from each of the metadata pointers
 // (cs, dtv, wgt): blocks of 3Q floats.
 __device__ __forceinline__ int64_t meta_offset(const ScanArgs& a, int64_t b, int h, int c, int Q) {
