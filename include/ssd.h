@@ -236,11 +236,14 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
  * [0, cache_rows) or a position outside [0, Q) marks a padding row: its slot
  * and its y row are not touched.  Live rows must name distinct slots.
  * dims: batch b, seqlen = chunk_size = Q (one chunk), H, P, N, G as for the
- * scan and in its compiled set.  The workspace
+ * scan and in its compiled set.  The scan reads each slot's chunk buffers and
+ * chunk-start state in place (x_chunks, b_chunks, c_chunks, state_cache and y
+ * 16-byte aligned) and computes only the 16-token row block that holds the
+ * new token (the chunk's state only when it completes).  The workspace
  * (ssd_decode_emulated_workspace_bytes, 256-byte aligned) holds the chunk's
- * scan.  Each step costs a scan of one chunk per row: this is the strict
- * decode, not the fast one (ssd_state_update).  Dispatch order: staging copy,
- * slot gather, the scan's kernels, output copy and state commit.
+ * scan data and the rows' lengths.  This is the strict decode, not the fast
+ * one (ssd_state_update).  Dispatch order: the new tokens' copy into their
+ * slots, then the scan's kernels (chunk_prep, chunk_output).
  */
 size_t ssd_decode_emulated_workspace_bytes(const ssd_dims* d, ssd_dtype io);
 ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,

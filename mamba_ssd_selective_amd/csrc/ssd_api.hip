@@ -278,19 +278,34 @@ int64_t ssd_chunk_scan_segments(const ssd_dims* d, ssd_dtype io) {
 
 namespace {
 
-// The forward scan.  row_len (b) or null: row r ends after row_len[r]
-// tokens.  cu (b + 1) or null: packed rows, row r is tokens [cu[r], cu[r+1])
-// of the T tokens of x, dt, B, C and y (no seq_idx then).  k counts the
-// dispatches of the calling entry point; before() runs once the arguments are
-// validated, ahead of the scan's first launch.
+// Where the scan's rows are (ScanArgs has the same fields):
+//  row_len (b) or null: row r ends after row_len[r] tokens;
+//  cu (b + 1) or null: packed rows, row r is tokens [cu[r], cu[r+1]) of the T
+//    tokens of x, dt, B, C and y (no seq_idx then);
+//  slot (b) or null: row r is slot slot[r] of buffers of `slots` rows of L
+//    tokens, its initial and final states those of the slot;
+//  y_last (b, H, P) or null: decode output (each row's last token only; a
+//    row's final state is written only when it holds L tokens).
+struct RowLayout {
+    const int32_t* row_len = nullptr;
+    const int32_t* cu = nullptr;
+    int64_t T = 0;
+    const int32_t* slot = nullptr;
+    int64_t slots = 0;
+    void* y_last = nullptr;
+};
+
+// The forward scan over rows laid out as `rl` says.  k counts the dispatches
+// of the calling entry point; before() runs once the arguments are validated,
+// ahead of the scan's first launch.
 template <typename F>
 ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
                          const float* dt_bias, int dt_softplus, float dt_min, float dt_max,
                          const float* A, const void* B, const void* C, const float* D,
                          const float* initial_states, const int32_t* seq_idx,
-                         const int32_t* row_len, void* y, float* final_states, void* workspace,
+                         const RowLayout& rl, void* y, float* final_states, void* workspace,
                          size_t workspace_bytes, hipStream_t hs, int& k, F&& before,
-                         bool one_segment = false, const int32_t* cu = nullptr, int64_t T = 0) {
+                         bool one_segment = false) {
     ssd_status st = check_scan_dims(d, io);
     if (st != SSD_OK) return st;
     if (one_segment && !ssd::find_scan_variant(io, d->headdim, d->dstate, d->chunk_size, true))
@@ -298,32 +313,39 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     if (bad_clamp(dt_min, dt_max)) return SSD_ERR_BAD_ARG;
     const int64_t b = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim,
                   N = d->dstate, G = d->ngroups;
-    if (cu && (seq_idx || row_len || T < 0)) return SSD_ERR_BAD_ARG;
-    // tokens of x, dt, B, C and y
-    const int64_t toks = cu ? T : b * L;
+    if (rl.cu && (seq_idx || rl.row_len || rl.slot || rl.T < 0)) return SSD_ERR_BAD_ARG;
+    // slots and the decode output: single-segment scans of rows of one chunk
+    if ((rl.slot || rl.y_last) && (!one_segment || seq_idx || rl.slots < 0 || L != d->chunk_size))
+        return SSD_ERR_BAD_ARG;
+    // tokens of x, dt, B, C (and y), and rows of states
+    const int64_t toks = rl.cu ? rl.T : (rl.slot ? rl.slots * L : b * L);
+    const int64_t srows = rl.slot ? rl.slots : b;
     const bool work = b > 0 && L > 0;
-    if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_NULL_ARG;
+    if (work && (!x || !dt || !A || !B || !C || !(rl.y_last ? rl.y_last : y)))
+        return SSD_ERR_NULL_ARG;
     const Plan plan = make_plan(*d, io, one_segment);
     if (plan.total > 0 &&
         (!workspace || workspace_bytes < plan.total ||
          (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
         return SSD_ERR_WORKSPACE;
-    const void* vec_bufs[] = {x, B, C, y, initial_states, final_states};
+    const void* vec_bufs[] = {x, B, C, y, rl.y_last, initial_states, final_states};
     for (const void* p : vec_bufs)
         if (p && !aligned16(p)) return SSD_ERR_BAD_ARG;
+    const int64_t sbytes = srows * H * P * N * 4;
     if (initial_states && final_states && initial_states != final_states &&
-        overlap(span(initial_states, b * H * P * N * 4), span(final_states, b * H * P * N * 4)))
+        overlap(span(initial_states, sbytes), span(final_states, sbytes)))
         return SSD_ERR_ALIAS;
     const size_t es = io_size(io);
     const Span in_spans[] = {
         span(x, toks * H * P * es), span(dt, toks * H * 4), span(B, toks * G * N * es),
         span(C, toks * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
         span(D, D ? H * 4 : 0), span(seq_idx, seq_idx ? b * L * 4 : 0),
-        span(row_len, row_len ? b * 4 : 0), span(cu, cu ? (b + 1) * 4 : 0),
+        span(rl.row_len, rl.row_len ? b * 4 : 0), span(rl.cu, rl.cu ? (b + 1) * 4 : 0),
+        span(rl.slot, rl.slot ? b * 4 : 0),
     };
-    const Span ys = span(y, toks * H * P * es);
-    const Span fs = span(final_states, final_states ? b * H * P * N * 4 : 0);
-    const Span is = span(initial_states, initial_states ? b * H * P * N * 4 : 0);
+    const Span ys = rl.y_last ? span(rl.y_last, b * H * P * es) : span(y, toks * H * P * es);
+    const Span fs = span(final_states, final_states ? sbytes : 0);
+    const Span is = span(initial_states, initial_states ? sbytes : 0);
     const Span ws = span(workspace, plan.total);
     for (const Span& s : in_spans) {
         if (overlap(ys, s) || overlap(fs, s) || overlap(ws, s)) return SSD_ERR_ALIAS;
@@ -358,9 +380,12 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     sa.dt_min = dt_min;
     sa.dt_max = dt_max;
     sa.seq_idx = seq_idx;
-    sa.row_len = row_len;
-    sa.cu = cu;
-    sa.T = T;
+    sa.row_len = rl.row_len;
+    sa.cu = rl.cu;
+    sa.T = rl.T;
+    sa.slot = rl.slot;
+    sa.slots = rl.slots;
+    sa.y_last = rl.y_last;
     sa.exact_decay = one_segment ? 1 : 0;
     sa.D = D;
     sa.init = initial_states;
@@ -428,7 +453,7 @@ ssd_status ssd_chunk_scan_fwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     int k = 0;
     if (g_hooks.launched) *g_hooks.launched = 0;
     return scan_fwd_impl(d, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D,
-                         initial_states, seq_idx, nullptr, y, final_states, workspace,
+                         initial_states, seq_idx, RowLayout{}, y, final_states, workspace,
                          workspace_bytes, static_cast<hipStream_t>(stream), k,
                          [] { return hipSuccess; });
 }
@@ -549,14 +574,18 @@ static ssd_status cached_prefill(const ssd_dims* d, ssd_dtype io, const void* x,
     const int64_t per_row = H * P * N;
     // the initial states gathered from their slots (zeros without them), the
     // scan's final states over them in place, then scattered back
+    RowLayout rl;
+    rl.row_len = seq_lens;
+    rl.cu = cu;
+    rl.T = T;
     st = scan_fwd_impl(d, io, x, dt, dt_bias, dt_softplus, dt_min, dt_max, A, B, C, D, states,
-                       nullptr, seq_lens, y, states, workspace, scan_bytes, hs, k, [&] {
+                       nullptr, rl, y, states, workspace, scan_bytes, hs, k, [&] {
                            return timed_launch(k, hs, [&] {
                                return ssd::launch_gather_slots(
                                    init_from_cache ? state_cache : nullptr, state_indices,
                                    cache_rows, states, b, per_row, hs);
                            });
-                       }, strict != 0, cu, T);
+                       }, strict != 0);
     if (st != SSD_OK) return st;
     if (timed_launch(k, hs, [&] {
             return ssd::launch_scatter_slots(states, state_indices, cache_rows, state_cache, b,
@@ -583,35 +612,16 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
 
 namespace {
 
-// Workspace of the chunk-emulating decode: the scan's (rows of one chunk), the
-// gathered states, then the batch-ordered inputs, output and row lengths.
+// Workspace of the chunk-emulating decode: the scan's (rows of one chunk,
+// strict), then the rows' lengths.
 struct EmulPlan {
-    size_t scan = 0, states = 0, xw = 0, dtw = 0, bw = 0, cw = 0, yw = 0, rl = 0, total = 0;
+    size_t rl = 0, total = 0;
 };
 
 EmulPlan make_emul_plan(const ssd_dims& d, ssd_dtype io) {
     EmulPlan e;
-    const size_t es = io_size(io);
-    const size_t b = static_cast<size_t>(d.batch), Q = static_cast<size_t>(d.chunk_size);
-    const size_t HP = static_cast<size_t>(d.nheads * d.headdim);
-    const size_t GN = static_cast<size_t>(d.ngroups * d.dstate);
-    size_t off = align_up(make_plan(d, io, true).total);  // always strict
-    e.scan = 0;
-    e.states = off;
-    off = align_up(off + b * HP * static_cast<size_t>(d.dstate) * 4);
-    e.xw = off;
-    off = align_up(off + b * Q * HP * es);
-    e.dtw = off;
-    off = align_up(off + b * Q * static_cast<size_t>(d.nheads) * 4);
-    e.bw = off;
-    off = align_up(off + b * Q * GN * es);
-    e.cw = off;
-    off = align_up(off + b * Q * GN * es);
-    e.yw = off;
-    off = align_up(off + b * Q * HP * es);
-    e.rl = off;
-    off = align_up(off + b * 4);
-    e.total = off;
+    e.rl = align_up(make_plan(d, io, true).total);
+    e.total = align_up(e.rl + static_cast<size_t>(d.batch) * 4);
     return e;
 }
 
@@ -701,52 +711,39 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
     ea.state_idx = state_indices;
     ea.pos = positions;
     ea.cache_rows = cache_rows;
-    ea.xw = wsb + e.xw;
-    ea.dtw = reinterpret_cast<float*>(wsb + e.dtw);
-    ea.bw = wsb + e.bw;
-    ea.cw = wsb + e.cw;
     ea.row_len = reinterpret_cast<int32_t*>(wsb + e.rl);
-    ea.yw = wsb + e.yw;
-    float* states = reinterpret_cast<float*>(wsb + e.states);
-    ea.states = states;
-    ea.state_cache = state_cache;
-    ea.y = y;
     ea.Q = static_cast<int>(Q);
     ea.wx = H * P * static_cast<int64_t>(es) / 4;
     ea.wd = H;
     ea.wb = G * N * static_cast<int64_t>(es) / 4;
-    ea.hpn = H * P * N;
-    // the staging copy in 16-byte words when every width and buffer allows
+    // the new tokens in 16-byte words when every width and buffer allows
     const int64_t xb = H * P * static_cast<int64_t>(es), gb = G * N * static_cast<int64_t>(es);
     const void* stage_bufs[] = {x, dt, B, C, x_chunks, dt_chunks, b_chunks, c_chunks};
     bool wide = xb % 16 == 0 && gb % 16 == 0 && (H * 4) % 16 == 0;
     for (const void* p : stage_bufs) wide = wide && aligned16(p);
-    ssd::EmulArgs sa_stage = ea;
     if (wide) {
-        sa_stage.wx = xb / 16;
-        sa_stage.wd = H * 4 / 16;
-        sa_stage.wb = gb / 16;
+        ea.wx = xb / 16;
+        ea.wd = H * 4 / 16;
+        ea.wb = gb / 16;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int k = 0;
     if (g_hooks.launched) *g_hooks.launched = 0;
-    st = scan_fwd_impl(d, io, ea.xw, ea.dtw, dt_bias, dt_softplus, dt_min, dt_max, A, ea.bw, ea.cw,
-                       D, states, nullptr, ea.row_len, wsb + e.yw, states, wsb,
-                       align_up(make_plan(*d, io, true).total), hs, k, [&] {
-                           hipError_t he = timed_launch(k, hs, [&] {
-                               return ssd::launch_emul_stage(sa_stage, wide, b, hs);
-                           });
-                           if (he != hipSuccess) return he;
-                           return timed_launch(k, hs, [&] {
-                               return ssd::launch_gather_slots(state_cache, state_indices,
-                                                               cache_rows, states, b, H * P * N,
-                                                               hs);
-                           });
-                       }, true);
-    if (st != SSD_OK) return st;
-    if (timed_launch(k, hs, [&] { return ssd::launch_emul_finish(ea, b, hs); }) != hipSuccess)
-        return SSD_ERR_HIP;
-    return SSD_OK;
+    // the scan of each slot's chunk in place: its chunk buffers and its
+    // chunk-start state, decode output (y of the new token; the slot's state
+    // replaced only when the chunk is complete)
+    RowLayout rl;
+    rl.row_len = ea.row_len;
+    rl.slot = state_indices;
+    rl.slots = cache_rows;
+    rl.y_last = y;
+    return scan_fwd_impl(d, io, x_chunks, dt_chunks, dt_bias, dt_softplus, dt_min, dt_max, A,
+                         b_chunks, c_chunks, D, state_cache, nullptr, rl, nullptr, state_cache,
+                         wsb, e.rl, hs, k, [&] {
+                             return timed_launch(k, hs, [&] {
+                                 return ssd::launch_emul_stage(ea, wide, b, hs);
+                             });
+                         }, true);
 }
 
 size_t ssd_chunk_scan_varlen_workspace_bytes(const ssd_dims* d, ssd_dtype io) {

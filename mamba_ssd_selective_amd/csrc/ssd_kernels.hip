@@ -244,6 +244,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     }
 
     if constexpr (kTiles) {
+        // decode output: the output kernels read the tiles and C rows of the
+        // row block of the row's last token only
+        const int I_only = a.y_last ? static_cast<int>((rs.len - 1 - t0) >> 4) : -1;
         // ---- stage B and C rows (tokens past L and columns past N are zero)
         const int64_t valid = rs.len - t0;
 #pragma unroll
@@ -267,6 +270,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
                 T* __restrict__ cm = static_cast<T*>(a.cmf) + ((b * a.nc + c) * a.G + g) * static_cast<int64_t>(Q * N);
                 for (int pc = wave; pc < C_::NB * KS; pc += kWaves) {
                     const int I = pc / KS, s = pc % KS;
+                    if (I_only >= 0 && I != I_only) continue;
                     const uint4 v = *reinterpret_cast<const uint4*>(sC + (16 * I + r16) * C_::SB + 32 * s + 8 * q);
                     *reinterpret_cast<uint4*>(cm + (static_cast<int64_t>(pc) * 64 + lane) * 8) = v;
                 }
@@ -290,6 +294,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         for (int pidx = wave; pidx < NPAIR; pidx += kWaves) {
             int I, J0;
             tile_of(pidx, I, J0);
+            if (I_only >= 0 && I != I_only) continue;
             const bool on1 = J0 + 1 <= I;  // the pair's second tile is left of or on the diagonal
             f32x4_t acc0 = acc_zero(), acc1 = acc_zero();
 #pragma unroll
@@ -776,13 +781,15 @@ __device__ __forceinline__ void row_block_outputs(const RowOps<T, P, N, Q>& ro, 
             for (int pb = 0; pb < C_::PB; ++pb) mma(acc[pb], cur.xf[pb], gf);
         }
     }
-    if (ti < rs.len) {
-        T* __restrict__ y = static_cast<T*>(a.y);
+    // decode output: the row's last token alone, into y_last[b]
+    if (a.y_last ? ti == rs.len - 1 : ti < rs.len) {
+        T* __restrict__ y = a.y_last ? static_cast<T*>(a.y_last) + (it.b * a.H + it.h) * P
+                                     : static_cast<T*>(a.y) + ((rs.t0 + ti) * a.H + it.h) * P;
 #pragma unroll
         for (int pb = 0; pb < C_::PB; ++pb) {
             const float x0 = raw_elem_f32<T, 0>(ro.xd[pb]), x1 = raw_elem_f32<T, 1>(ro.xd[pb]);
             const float x2 = raw_elem_f32<T, 2>(ro.xd[pb]), x3 = raw_elem_f32<T, 3>(ro.xd[pb]);
-            store4_f32(y + ((rs.t0 + ti) * a.H + it.h) * P + 16 * pb + 4 * q,
+            store4_f32(y + 16 * pb + 4 * q,
                        acc[pb][0] + Dh * x0, acc[pb][1] + Dh * x1, acc[pb][2] + Dh * x2,
                        acc[pb][3] + Dh * x3);
         }
@@ -811,13 +818,21 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     const int nc_row = static_cast<int>((rs.len + Q - 1) / Q);
     const int c_begin = it.seg * a.cps;
     const int c_end = min(c_begin + a.cps, nc_row);  // none when the row ends earlier
-    const bool last_seg = kOut && it.seg == a.nseg - 1;
+    // the final state is written by the last segment; decode output: only for
+    // rows that hold a whole chunk (a slot's state moves on at chunk ends)
+    const bool last_seg = kOut && it.seg == a.nseg - 1 && rs.live &&
+                          (a.y_last == nullptr || rs.len == a.L);
+    // the row's initial / final state (its own, or its slot's)
+    const int64_t sh = rs.state * a.H + it.h;
+    // decode output: only the row block of the row's last token is computed
+    const int I_last = a.y_last ? static_cast<int>(((rs.len - 1) % Q) / 16) : -1;
     const bool has_seq = a.seq_idx != nullptr;
 
     StateRegs<T, P, N, Q> hreg;
     if constexpr (kOut) {
         if (a.nseg == 1)
-            state_load<T, P, N, Q>(hreg, a.init ? a.init + bh * P * N : nullptr, wave, lane);
+            state_load<T, P, N, Q>(hreg, a.init && rs.live ? a.init + sh * P * N : nullptr, wave,
+                                   lane);
         else
             state_load<T, P, N, Q>(hreg, a.seg_state + (bh * a.nseg + it.seg) * P * N, wave,
                                    lane);
@@ -849,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
         if constexpr (kOut) {
 #pragma unroll
             for (int r = 0; r < C_::RB; ++r)
-                if (row_block_valid<C_::NB>(wave))
+                if (row_block_valid<C_::NB>(wave) && (I_last < 0 || row_block<C_::NB>(wave, r) == I_last))
                     load_row_ops<T, P, N, Q>(ro[r], a, it, rs, c, row_block<C_::NB>(wave, r), lane);
         }
         if (has_next) prefetch_chunk<T, P, N, Q>(pf, a, it, rs, c + 1);
@@ -863,7 +878,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
         if constexpr (kOut) {
 #pragma unroll
             for (int r = 0; r < C_::RB; ++r)
-                if (row_block_valid<C_::NB>(wave))
+                if (row_block_valid<C_::NB>(wave) && (I_last < 0 || row_block<C_::NB>(wave, r) == I_last))
                     row_block_outputs<T, P, N, Q>(ro[r], meta, sX, sH, a, it, rs, c,
                                                   row_block<C_::NB>(wave, r), Dh, has_seq, lane);
         }
@@ -878,7 +893,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanArgs a) {
     }
     if constexpr (kOut) {
         if (last_seg && a.final_states)
-            state_store<T, P, N, Q>(hreg, a.final_states + bh * P * N, wave, lane);
+            state_store<T, P, N, Q>(hreg, a.final_states + sh * P * N, wave, lane);
     } else {
         const int64_t slot = bh * a.nseg + it.seg;
         state_store<T, P, N, Q>(hreg, a.seg_state + slot * P * N, wave, lane);

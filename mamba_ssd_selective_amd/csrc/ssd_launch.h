@@ -28,6 +28,18 @@ struct ScanArgs {
     const int32_t* row_len;
     const int32_t* cu;
     int64_t T;
+    // (b) or null: row b lives in slot slot[b] of buffers of `slots` rows of L
+    // tokens each (its tokens at slot[b] L + t of x, dt, B and C), and its
+    // initial and final states are those of the slot (init / final_states +
+    // slot[b] H P N).  A slot outside [0, slots) marks a row that is not
+    // computed: nothing of it is read or written.  Single-segment calls only.
+    const int32_t* slot;
+    int64_t slots;
+    // (b, H, P) or null: decode output.  Only each row's last token (token
+    // len - 1) is output, into y_last[b], and y is not written; a row writes
+    // its final state only when it holds a whole chunk (len = L), so that its
+    // slot's state moves on at chunk ends only.  Single-segment calls only.
+    void* y_last;
     // 1: every chunk takes the per-element exp(cs_i - cs_j) form of the
     // intra-chunk decay (no factoring), so that a token's output does not
     // depend on the tokens after it in its chunk (the strict mode)
@@ -249,21 +261,12 @@ struct EmulArgs {
     const int32_t* state_idx; // (b) slot of each row
     const int32_t* pos;       // (b) offset of the new token in its chunk
     int64_t cache_rows;
-    void* xw;                 // (b, Q, H, P) io: the scan's inputs
-    float* dtw;               // (b, Q, H)
-    void* bw;                 // (b, Q, G, N) io
-    void* cw;                 // (b, Q, G, N) io
-    int32_t* row_len;         // (b)
-    const void* yw;           // (b, Q, H, P) io: the scan's output
-    const float* states;      // (b, H, P, N): the scan's final states
-    float* state_cache;       // (slots, H, P, N): chunk-start states
-    void* y;                  // (b, H, P) io
+    int32_t* row_len;         // (b): tokens of the row's chunk so far (0: padding row)
     int Q;
-    int64_t wx, wd, wb, hpn;
+    int64_t wx, wd, wb;
 };
 // wide: the stage copies 16-byte words (widths wx, wd, wb given in them)
 hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st);
-hipError_t launch_emul_finish(const EmulArgs& a, int64_t b, hipStream_t st);
 
 // Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros
 // for an index outside [0, rows) or when cache is null); scatter row r to slot

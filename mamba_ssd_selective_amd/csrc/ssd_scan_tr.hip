@@ -157,6 +157,7 @@ struct TrScan {
     const uint16_t* cmg;                // C rows in operand order at (b, chunk 0, g)
     int64_t cm_cstride;                 // elements between chunks of that copy
     uint16_t* yg;                       // y[b][.][h][0]
+    uint16_t* ylg;                      // decode output y_last[b][h][0], or null
     const float* mg;                    // metadata block (b, h, chunk 0): [cs | dt | w]
     const int32_t* sqg;                 // seq_idx[b][0]
     const uint16_t* cbg;                // C.B^T tiles at (b, chunk 0, g)
@@ -398,8 +399,11 @@ struct TrScan {
                 yw[q][w] = r[0];
                 yw[q + 1][w] = r[1];
             }
-        if (i < valid) {
-            uint16_t* yp = yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2) + 16 * (g & 1) + 8 * (g >> 1);
+        // decode output: the row's last token alone
+        const bool keep = ylg ? i == valid - 1 : i < valid;
+        if (keep) {
+            uint16_t* yp = (ylg ? ylg : yg + (static_cast<int64_t>(c) * Q + i) * (xstride / 2)) +
+                           16 * (g & 1) + 8 * (g >> 1);
 #pragma unroll
             for (int q = 0; q < G_::PB; q += 2) {
                 const u4 v = {yw[q][0], yw[q][1], yw[q + 1][0], yw[q + 1][1]};
@@ -480,6 +484,11 @@ struct TrScan {
     __device__ __forceinline__ void chunk_out(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
         const bool has_next = c + 1 < c_end;
         const int valid = rows_in(c);
+        // decode output (rows of one chunk): only the row block of the last token
+        if (ylg && I != ((valid - 1) >> 4)) {
+            __syncthreads();
+            return;
+        }
         const uint32_t mb = mbase[K];
         const char* X = xo[K];
         const TrMeta<Q>* M = mo[K];
@@ -628,6 +637,11 @@ struct TrScan {
     __device__ __forceinline__ void chunk_st_t(int c, char* Xn, char* Bn, TrMeta<Q>* Mn) {
         const bool has_next = c + 1 < c_end;
         const int valid = rows_in(c);
+        // decode output (rows of one chunk): the state is needed at the chunk's end only
+        if (kOut && a.y_last && valid != Q) {
+            __syncthreads();
+            return;
+        }
         const uint32_t mb = mbase[K];
         const char* X = xo[K];
         const char* Bt = bo[K];
@@ -810,7 +824,9 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     // no chunks when the row ends before this segment
     k.c_end = min(k.c_begin + a.cps, static_cast<int>((rs.len + Q - 1) / Q));
     const bool any = k.c_begin < k.c_end;
-    k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr;
+    // (decode output: a slot's state moves on at chunk ends only)
+    k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr && rs.live &&
+                   (a.y_last == nullptr || rs.len == a.L);
     k.out_wave_ = kOut && k.wave < G_::NB;
     k.I = kOut && k.wave < kTrWaves ? tr_row_block<G_::NB>(k.wave) : 0;
     k.Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
@@ -823,6 +839,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     k.cm_cstride = static_cast<int64_t>(a.G) * Q * N;
     k.cmg = static_cast<const uint16_t*>(a.cmf) + (it.b * a.nc * a.G + it.g) * static_cast<int64_t>(Q) * N;
     k.yg = static_cast<uint16_t*>(a.y) + (rs.t0 * a.H + it.h) * P;
+    k.ylg = kOut && a.y_last ? static_cast<uint16_t*>(a.y_last) + bh * P : nullptr;
     k.mg = a.cs + meta_offset(a, it.b, it.h, 0, Q);
     k.sqg = a.seq_idx ? a.seq_idx + rs.t0 : nullptr;
     k.cb_cstride = static_cast<int64_t>(a.G) * cbt_elems_per_chunk_group(Q);
@@ -886,7 +903,9 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
         // through the end states of the earlier segments, and its bf16 operand
         // copy in H[0].
         if (any) k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
-        k.state_load(kOut && a.init ? a.init + bh * P * N : nullptr);
+        // the initial state of the row (or of its slot)
+        const int64_t sh = rs.state * a.H + it.h;
+        k.state_load(kOut && a.init && rs.live ? a.init + sh * P * N : nullptr);
         if constexpr (kOut) {
             if (k.st()) k.state_carry(a.seg_mult + bh * a.nseg, a.seg_state + bh * a.nseg * P * N, it.seg);
             if (k.st()) {
@@ -906,7 +925,7 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
             if (c + 1 < k.c_end) k.template chunk_st<1>(c + 1, s.x[0], s.b[0], s.m[0]);
         }
         if constexpr (kOut) {
-            if (k.want_final) k.state_store(a.final_states + bh * P * N);
+            if (k.want_final) k.state_store(a.final_states + sh * P * N);
         } else {
             const int64_t slot = bh * a.nseg + it.seg;
             k.state_store_reg(a.seg_state + slot * P * N);

@@ -43,11 +43,28 @@ __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid
 // it (no kernel reads or writes their data).
 struct RowSpan {
     int64_t t0;
-    int64_t len;  // <= L
+    int64_t len;    // <= L
+    int64_t state;  // the row's initial / final state: row b, or its slot
+    bool live;      // false: a row of no slot (nothing of it is read or written)
 };
 __device__ __forceinline__ RowSpan row_span(const ScanArgs& a, int64_t b) {
     RowSpan r;
-    if (a.cu) {
+    r.state = b;
+    r.live = true;
+    if (a.slot) {
+        const int64_t s = a.slot[b];
+        r.live = s >= 0 && s < a.slots;
+        r.state = r.live ? s : 0;
+        r.t0 = r.state * a.L;
+        r.len = 0;
+        if (r.live) {
+            r.len = a.L;
+            if (a.row_len) {
+                const int64_t rl = a.row_len[b];
+                r.len = rl < 0 ? 0 : (rl < a.L ? rl : a.L);
+            }
+        }
+    } else if (a.cu) {
         int64_t lo = a.cu[b], hi = a.cu[b + 1];
         lo = lo < 0 ? 0 : (lo > a.T ? a.T : lo);
         hi = hi < lo ? lo : (hi > a.T ? a.T : hi);

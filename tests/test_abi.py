@@ -248,12 +248,10 @@ def test_cached_prefill_workspace_and_rejections(lib):
 def test_emulated_decode_workspace_and_rejections(lib):
     d = (4, 128, 64, 64, 128, 8, 128)
     need = ssd.library().ssd_decode_emulated_workspace_bytes(ctypes.byref(ssd._Dims(*d)), ssd.BF16)
-    # the one-chunk scan's workspace, states, then x/dt/B/C/y copies and row lengths
+    # the one-chunk scan's workspace, then the row lengths (the slots are read in place)
     scan = ssd.workspace_bytes(*d)
     al = lambda v: (v + 255) // 256 * 256
-    parts = [4 * 64 * 64 * 128 * 4, 4 * 128 * 4096 * 2, 4 * 128 * 64 * 4, 4 * 128 * 1024 * 2,
-             4 * 128 * 1024 * 2, 4 * 128 * 4096 * 2, 4 * 4]
-    assert need == al(scan) + sum(al(v) for v in parts)
+    assert need == al(scan) + al(4 * 4)
     buf = _Buf()
 
     def call(dims=d, rows=8, **over):
@@ -272,6 +270,7 @@ def test_emulated_decode_workspace_and_rejections(lib):
     assert call(xc=None) == NULL_ARG
     assert call(pos=None) == NULL_ARG
     assert call(st=0x70000008) == BAD_ARG
+    assert call(xc=buf(1 << 28) + 8) == BAD_ARG   # the scan reads the chunk buffers: 16-byte aligned
     assert call(ws=None) == WORKSPACE
     assert call(ws_bytes=1 << 20) == WORKSPACE
     s = buf(1 << 26)
