@@ -41,13 +41,17 @@ namespace {
 // 12: waves 0-7 own one output row block each, waves 8-11 two state n-blocks
 // each, so that the state chain and the output products of a chunk proceed on
 // different waves of each SIMD (three waves per SIMD).
+// The decode-output form (kDec: rows of one chunk, one output row block per
+// row) runs 5: wave 0 computes the row block of the row's last token, waves
+// 1-4 own two state n-blocks each; with single buffers its LDS and waves
+// leave room for two workgroups per CU.
 constexpr int kTrWaves = 8;
-template <bool kOut>
+template <bool kOut, bool kDec = false>
 struct TrWaves {
-    static constexpr int W = kOut ? 12 : 8;
+    static constexpr int W = kDec ? 5 : (kOut ? 12 : 8);
     static constexpr int kThreads = W * kWave;
     static constexpr int NBW = kOut ? 2 : 1;  // state n-blocks per state wave
-    static constexpr int first_state = kOut ? 8 : 0;
+    static constexpr int first_state = kDec ? 1 : (kOut ? 8 : 0);
 };
 template <int P, int N, int Q>
 struct TrGeo {
@@ -124,11 +128,11 @@ __device__ __forceinline__ int tr_row_block(int wave) {
     else return wave;
 }
 
-template <int P, int N, int Q, bool kOut, bool kSeq>
+template <int P, int N, int Q, bool kOut, bool kSeq, bool kDec = false>
 struct TrScan {
     using G_ = TrGeo<P, N, Q>;
-    static constexpr int W = TrWaves<kOut>::W;
-    static constexpr int NBW = TrWaves<kOut>::NBW;
+    static constexpr int W = TrWaves<kOut, kDec>::W;
+    static constexpr int NBW = TrWaves<kOut, kDec>::NBW;
     static constexpr int NXI = G_::XBYTES / 1024;   // 1 KB copy instructions of an x tile
     static constexpr int NBI = G_::BBYTES / 1024;   // ... of a B tile
     static constexpr int XI = (NXI + W - 1) / W;    // per wave (the last round may be partial)
@@ -804,17 +808,17 @@ struct TrLds {
 };
 
 // One (row, head, segment) from set-up to the final stores.
-template <int P, int N, int Q, bool kOut, bool kSeq>
+template <int P, int N, int Q, bool kOut, bool kSeq, bool kDec>
 __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s) {
     using G_ = TrGeo<P, N, Q>;
-    using S_ = TrScan<P, N, Q, kOut, kSeq>;
+    using S_ = TrScan<P, N, Q, kOut, kSeq, kDec>;
     S_ k(a);
     const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
     k.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     k.lane = static_cast<int>(threadIdx.x) % kWave;
     k.r16 = k.lane & 15;
     k.g = k.lane >> 4;
-    k.nb = (k.wave - TrWaves<kOut>::first_state) * S_::NBW;
+    k.nb = (k.wave - TrWaves<kOut, kDec>::first_state) * S_::NBW;
     k.st_wave_ = k.nb >= 0 && k.nb < G_::NNB;
     const int64_t bh = it.b * a.H + it.h;
     const RowSpan rs = row_span(a, it.b);
@@ -827,8 +831,13 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     // (decode output: a slot's state moves on at chunk ends only)
     k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr && rs.live &&
                    (a.y_last == nullptr || rs.len == a.L);
-    k.out_wave_ = kOut && k.wave < G_::NB;
-    k.I = kOut && k.wave < kTrWaves ? tr_row_block<G_::NB>(k.wave) : 0;
+    k.out_wave_ = kDec ? k.wave == 0 : kOut && k.wave < G_::NB;
+    if constexpr (kDec) {
+        // the row block of the row's last token (rows of one chunk)
+        k.I = rs.len > 0 ? static_cast<int>((rs.len - 1) >> 4) : 0;
+    } else {
+        k.I = kOut && k.wave < kTrWaves ? tr_row_block<G_::NB>(k.wave) : 0;
+    }
     k.Dh = (kOut && a.D) ? a.D[it.h] : 0.0f;
     k.Ah = a.A[it.h];
     k.mult = 1.0f;
@@ -939,29 +948,39 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
 //                 their decay multipliers, written to the workspace;
 //   kOut = true:  outputs of every segment from its incoming state; final
 //                 states from the last segment.
-template <int P, int N, int Q, bool kOut, bool kSeq>
-__global__ __launch_bounds__(TrWaves<kOut>::kThreads) void scan_tr_kernel(ScanArgs a) {
+// kDec: the decode-output form (one chunk per row, so the second buffers are
+// never used and take no LDS; one column-factor row).
+template <int P, int N, int Q, bool kOut, bool kSeq, bool kDec>
+__global__ __launch_bounds__((TrWaves<kOut, kDec>::kThreads)) void scan_tr_kernel(ScanArgs a) {
     using G_ = TrGeo<P, N, Q>;
+    constexpr int kSecond = kDec ? 16 : 1;  // bytes of a second buffer: all, or a stub
     __shared__ __attribute__((aligned(1024))) char sX0[G_::XBYTES];
-    __shared__ __attribute__((aligned(1024))) char sX1[G_::XBYTES];
+    __shared__ __attribute__((aligned(1024))) char sX1[kDec ? kSecond : G_::XBYTES];
     __shared__ __attribute__((aligned(1024))) char sB0[G_::BBYTES];
-    __shared__ __attribute__((aligned(1024))) char sB1[G_::BBYTES];
+    __shared__ __attribute__((aligned(1024))) char sB1[kDec ? kSecond : G_::BBYTES];
     __shared__ __attribute__((aligned(16))) TrMeta<Q> sM0;
-    __shared__ __attribute__((aligned(16))) TrMeta<Q> sM1;
+    __shared__ __attribute__((aligned(16))) char sM1[kDec ? kSecond : sizeof(TrMeta<Q>)];
     __shared__ __attribute__((aligned(1024))) char sH0[kOut ? G_::HBYTES : 16];
-    __shared__ __attribute__((aligned(1024))) char sH1[kOut ? G_::HBYTES : 16];
-    __shared__ __attribute__((aligned(16))) float sCj[kOut ? kTrWaves * Q : 4];
-    const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1}, {&sM0, &sM1}, {sH0, sH1}, sCj};
+    __shared__ __attribute__((aligned(1024))) char sH1[kOut && !kDec ? G_::HBYTES : 16];
+    __shared__ __attribute__((aligned(16))) float sCj[kDec ? Q : (kOut ? kTrWaves * Q : 4)];
+    const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1},
+                                   {&sM0, reinterpret_cast<TrMeta<Q>*>(sM1)}, {sH0, sH1}, sCj};
 
-    scan_tr_run<P, N, Q, kOut, kSeq>(a, lds);
+    scan_tr_run<P, N, Q, kOut, kSeq, kDec>(a, lds);
 }
 
 template <int P, int N, int Q, bool kOut>
 hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(nblocks));
+    if constexpr (kOut) {
+        // decode output (rows of one chunk, no seq_idx): the 5-wave form
+        if (a.y_last && !a.seq_idx)
+            return dispatch(scan_tr_kernel<P, N, Q, true, false, true>, grid,
+                            dim3(TrWaves<true, true>::kThreads), st, a);
+    }
     const dim3 block(TrWaves<kOut>::kThreads);
-    if (a.seq_idx) return dispatch(scan_tr_kernel<P, N, Q, kOut, true>, grid, block, st, a);
-    return dispatch(scan_tr_kernel<P, N, Q, kOut, false>, grid, block, st, a);
+    if (a.seq_idx) return dispatch(scan_tr_kernel<P, N, Q, kOut, true, false>, grid, block, st, a);
+    return dispatch(scan_tr_kernel<P, N, Q, kOut, false, false>, grid, block, st, a);
 }
 
 }  // namespace
