@@ -234,7 +234,9 @@ def backward_measure(ssd, lib, hip, torch, base, A, D, bias, w, steps, cpu_secon
     call()
     lib.ssd_set_timing_events(None, 0, None)
     nk = launched.value
-    names = ["chunk_meta", "chunk_states", "chunk_grad", "grad_sums"][:nk]
+    # segmented state walks add the segment ends and a pass per direction
+    names = (["chunk_meta", "seg_ends", "seg_pass_fwd", "seg_pass_bwd", "chunk_states", "chunk_grad",
+              "grad_sums"] if nk == 7 else ["chunk_meta", "chunk_states", "chunk_grad", "grad_sums"][:nk])
     kg = names.index("chunk_grad")
     for _ in range(5):
         call()

@@ -175,26 +175,45 @@ ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
 }
 
 struct BwdPlan {
-    int64_t nc = 0;
-    size_t off_meta = 0, off_states = 0, off_gstates = 0, off_partials = 0, total = 0;
+    int64_t nc = 0, nseg = 1, cps = 0;
+    size_t off_meta = 0, off_states = 0, off_gstates = 0, off_partials = 0, off_seg = 0,
+           off_mult = 0, total = 0;
 };
 
+// Workgroups the gradient path's state walks aim for (two per CU: both
+// directions of every row x head, cut into segments when there are few).
+constexpr int64_t kBwdWalkWorkgroups = 512;
+
 // Workspace of the gradient path: the metadata blocks of chunk_prep_kernel,
-// the fp32 state before and the gradient after every chunk, per-chunk sums.
+// the bf16 state before and the gradient after every chunk, per-chunk sums,
+// and (segmented walks) the segments' end states and decay products.
 BwdPlan make_bwd_plan(const ssd_dims& d) {
     BwdPlan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
     p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
+    const int64_t walks = 2 * d.batch * d.nheads;
+    int64_t nseg = (kBwdWalkWorkgroups + walks - 1) / walks;
+    if (nseg > p.nc) nseg = p.nc;
+    if (nseg < 1) nseg = 1;
+    p.cps = (p.nc + nseg - 1) / nseg;
+    p.nseg = (p.nc + p.cps - 1) / p.cps;
     const size_t bhc = static_cast<size_t>(d.batch * d.nheads * p.nc);
     size_t off = 0;
     p.off_meta = off;
     off = align_up(off + bhc * static_cast<size_t>(d.chunk_size) * 3 * sizeof(float));
     p.off_states = off;
-    off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(float));
+    off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(uint16_t));
     p.off_gstates = off;
-    off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(float));
+    off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(uint16_t));
     p.off_partials = off;
     off = align_up(off + bhc * 3 * sizeof(float));
+    if (p.nseg > 1) {
+        const size_t segs = static_cast<size_t>(2 * d.batch * d.nheads * p.nseg);
+        p.off_seg = off;
+        off = align_up(off + segs * static_cast<size_t>(d.headdim * d.dstate) * sizeof(float));
+        p.off_mult = off;
+        off = align_up(off + segs * sizeof(float));
+    }
     p.total = off;
     return p;
 }
@@ -857,6 +876,8 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     ba.H = static_cast<int>(H);
     ba.G = static_cast<int>(G);
     ba.nc = static_cast<int>(plan.nc);
+    ba.nseg = static_cast<int>(plan.nseg);
+    ba.cps = static_cast<int>(plan.cps);
     if (!work) {
         if (timed_launch(k, hs, [&] { return ssd::launch_bwd_empty(ba, b * H * P * N, hs); }) !=
             hipSuccess)
@@ -866,9 +887,11 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     char* wsb = static_cast<char*>(workspace);
     float* meta = reinterpret_cast<float*>(wsb + plan.off_meta);
     ba.cs = meta;
-    ba.states = reinterpret_cast<float*>(wsb + plan.off_states);
-    ba.gstates = reinterpret_cast<float*>(wsb + plan.off_gstates);
+    ba.states = reinterpret_cast<uint16_t*>(wsb + plan.off_states);
+    ba.gstates = reinterpret_cast<uint16_t*>(wsb + plan.off_gstates);
     ba.partials = reinterpret_cast<float*>(wsb + plan.off_partials);
+    ba.seg_end = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_seg) : nullptr;
+    ba.seg_mult = plan.nseg > 1 ? reinterpret_cast<float*>(wsb + plan.off_mult) : nullptr;
 
     // the per-token metadata of the forward pass (chunk_prep_kernel, no tiles)
     ssd::ScanArgs sa{};
@@ -893,6 +916,23 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     if (timed_launch(k, hs, [&] { return ssd::launch_chunk_meta_bf16_64_128_128(sa, b * plan.nc * G, hs); }) !=
         hipSuccess)
         return SSD_ERR_HIP;
+    if (plan.nseg > 1) {
+        // segment ends from zero, then each segment's incoming state (one pass
+        // per direction: from h_init forwards, from d(final states) backwards)
+        if (timed_launch(k, hs, [&] { return ssd::launch_bwd_seg_ends(ba, hs); }) != hipSuccess)
+            return SSD_ERR_HIP;
+        for (int dir = 0; dir < 2; ++dir) {
+            ssd::PassArgs pa;
+            pa.seg_state = ba.seg_end + dir * b * H * plan.nseg * P * N;
+            pa.seg_mult = ba.seg_mult + dir * b * H * plan.nseg;
+            pa.init = dir == 0 ? initial_states : d_final_states;
+            pa.PN = P * N;
+            pa.nseg = static_cast<int>(plan.nseg);
+            if (timed_launch(k, hs, [&] { return ssd::launch_state_pass(pa, b * H, hs); }) !=
+                hipSuccess)
+                return SSD_ERR_HIP;
+        }
+    }
     if (timed_launch(k, hs, [&] { return ssd::launch_bwd_states(ba, hs); }) != hipSuccess)
         return SSD_ERR_HIP;
     if (timed_launch(k, hs, [&] { return ssd::launch_bwd_chunk(ba, hs); }) != hipSuccess)

@@ -30,11 +30,17 @@
 // Every term is local to its chunk once h_in and g_out are known.
 //
 // Kernels (one backward call):
-//   bwd_states_kernel   one workgroup per (row, head) and direction, both
-//        directions in one launch: forward, the states h_in of every chunk in
-//        chunk order (h <- e_c h + sum_j omega_j dt_j x_j B_j^T); backward, g_out
-//        of every chunk (g <- e_c g + sum_i kappa_i dy_i C_i^T), whose last state
-//        is d(h_init); each walk loads the next chunk during the current one;
+//   bwd_states_kernel   the two chains of states, both directions in one
+//        launch: forward, the states h_in of every chunk in chunk order
+//        (h <- e_c h + sum_j omega_j dt_j x_j B_j^T); backward, g_out of every
+//        chunk (g <- e_c g + sum_i kappa_i dy_i C_i^T), whose last state is
+//        d(h_init); each walk loads the next chunk during the current one.
+//        With few rows x heads the walks are cut into segments, as the
+//        forward scan's: bwd_seg_ends_kernel walks every segment but the last
+//        from zero to its end state, a pass over segments (state_pass_kernel)
+//        turns those into each segment's incoming state, and
+//        bwd_states_kernel walks the segments from there, one workgroup per
+//        (direction, row, head, segment);
 //   bwd_chunk_kernel          one workgroup per (row, chunk, group), the group's
 //        heads in turn: every gradient above on bf16 MFMA, dB and dC summed over
 //        the heads in registers (no atomics: deterministic);
@@ -193,9 +199,17 @@ __device__ __forceinline__ int seq_at(const int32_t* seq, int64_t row_base, int6
 // after every chunk (backward: g_out, reverse chunk order), fp32 [p][n] in
 // `states` at (row, head, chunk).  Wave w owns state rows n = 16w + 4g + r,
 // column p = 16pb + r16 (the MFMA accumulator layout).
-template <bool kRev>
-__device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, char* sV, char* sK,
-                                                float* sW) {
+// One walk covers the chunks k in [k_begin, k_end) of the walk order (chunk
+// k, or nc - 1 - k backwards), starting from `init` (P x N, or zero):
+//  kChunks = true:  the state before each of them is written to `states`;
+//                   the walk that ends the chain writes d(h_init);
+//  kChunks = false: only the state at the end is written, to `end`, and the
+//                   product of the chunks' decays to *mult (a segment's part
+//                   of the chain, for a pass over segments).
+template <bool kRev, bool kChunks>
+__device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, int k_begin, int k_end,
+                                                const float* init, float* end, float* mult,
+                                                char* sV, char* sK, float* sW) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
     const int r16 = lane & 15, g = lane >> 4;
@@ -206,16 +220,16 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, ch
     const int64_t srow = b * L;
 
     f32x4_t st[kBP / 16];
-    const float* init = kRev ? a.dh_final : a.h_init;
 #pragma unroll
     for (int pb = 0; pb < kBP / 16; ++pb) {
         st[pb] = acc_zero();
         if (init) {
-            const float4 v = *reinterpret_cast<const float4*>(init + bh * kBP * kBN + (16 * pb + r16) * kBN +
+            const float4 v = *reinterpret_cast<const float4*>(init + (16 * pb + r16) * kBN +
                                                               16 * wave + 4 * g);
             st[pb] = f32x4_t{v.x, v.y, v.z, v.w};
         }
     }
+    float prod = 1.0f;  // product of the decays (kChunks = false)
     const char* vsrc = static_cast<const char*>(kRev ? a.dy : a.x);
     const char* ksrc = static_cast<const char*>(kRev ? a.C : a.B);
     const int64_t vstride = static_cast<int64_t>(a.H) * kRowX;
@@ -249,21 +263,24 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, ch
         nx.e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
     };
     Next nx;
-    fetch(0, nx);
-    for (int k = 0; k < a.nc; ++k) {
+    if (k_begin < k_end) fetch(k_begin, nx);
+    for (int k = k_begin; k < k_end; ++k) {
         const int c = kRev ? a.nc - 1 - k : k;
-        // the state before this chunk's update
-        float* dst = (kRev ? a.gstates : a.states) + (bh * a.nc + c) * kBP * kBN;
+        if constexpr (kChunks) {
+            // the state before this chunk's update, as bf16 [p][n]
+            uint16_t* dst = (kRev ? a.gstates : a.states) + (bh * a.nc + c) * kBP * kBN;
 #pragma unroll
-        for (int pb = 0; pb < kBP / 16; ++pb)
-            *reinterpret_cast<float4*>(dst + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
-                make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
+            for (int pb = 0; pb < kBP / 16; ++pb)
+                *reinterpret_cast<uint2*>(dst + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
+                    make_uint2(pack_bf16x2(st[pb][0], st[pb][1]), pack_bf16x2(st[pb][2], st[pb][3]));
+        }
         store_rows(sV, nx.v);
         store_rows(sK, nx.kr);
         if (threadIdx.x < kBQ) sW[threadIdx.x] = nx.w;
         const float e = nx.e;
+        prod *= e;
         __syncthreads();
-        if (k + 1 < a.nc) fetch(k + 1, nx);  // in flight during this chunk's products
+        if (k + 1 < k_end) fetch(k + 1, nx);  // in flight during this chunk's products
         const uint32_t bsK = lds_keep(lds_addr(sK)), bsV = lds_keep(lds_addr(sV));
 #pragma unroll
         for (int pb = 0; pb < kBP / 16; ++pb)
@@ -277,24 +294,58 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, ch
         }
         __syncthreads();
     }
-    if (kRev && a.dh_init) {
+    if (end) {
 #pragma unroll
         for (int pb = 0; pb < kBP / 16; ++pb)
-            *reinterpret_cast<float4*>(a.dh_init + bh * kBP * kBN + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
+            *reinterpret_cast<float4*>(end + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
                 make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
     }
+    if (!kChunks && mult && threadIdx.x == 0) *mult = prod;
 }
 
-// Both walks in one launch (they are independent): workgroups [0, b*H) walk
-// forward over (row, head) = blockIdx.x, the next b*H walk backwards.
+// Segment ends of the walks (nseg > 1): workgroup w is (direction, row x
+// head, segment s < nseg - 1), direction slowest; each segment from a zero
+// state.
+__global__ __launch_bounds__(kBThreads) void bwd_seg_ends_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];
+    __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];
+    __shared__ __attribute__((aligned(16))) float sW[kBQ];
+    const int64_t nbh = static_cast<int64_t>(a.batch) * a.H;
+    const int64_t per_dir = nbh * (a.nseg - 1);
+    const int64_t w = blockIdx.x;
+    const int dir = static_cast<int>(w / per_dir);
+    const int64_t bh = (w % per_dir) / (a.nseg - 1);
+    const int seg = static_cast<int>((w % per_dir) % (a.nseg - 1));
+    const int k0 = seg * a.cps, k1 = min(k0 + a.cps, a.nc);
+    const int64_t slot = (dir * nbh + bh) * a.nseg + seg;
+    float* end = a.seg_end + slot * kBP * kBN;
+    float* mult = a.seg_mult + slot;
+    if (dir == 0) bwd_states_walk<false, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
+    else bwd_states_walk<true, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
+}
+
+// Both walks in one launch (they are independent): workgroup w is
+// (direction, row x head, segment), direction slowest.  A segment starts
+// from its incoming state (after the pass over segment ends), the first from
+// h_init (forward) or d(final states) (backward); the backward walk's last
+// segment ends in d(h_init).
 __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];   // x or dy rows
     __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];   // B or C rows
     __shared__ __attribute__((aligned(16))) float sW[kBQ];            // per-token weights
     const int64_t nbh = static_cast<int64_t>(a.batch) * a.H;
+    const int64_t per_dir = nbh * a.nseg;
     const int64_t w = blockIdx.x;
-    if (w < nbh) bwd_states_walk<false>(a, w, sV, sK, sW);
-    else bwd_states_walk<true>(a, w - nbh, sV, sK, sW);
+    const int dir = static_cast<int>(w / per_dir);
+    const int64_t bh = (w % per_dir) / a.nseg;
+    const int seg = static_cast<int>((w % per_dir) % a.nseg);
+    const int k0 = seg * a.cps, k1 = min(k0 + a.cps, a.nc);
+    const float* first = dir == 0 ? a.h_init : a.dh_final;
+    const float* init = a.nseg > 1 ? a.seg_end + ((dir * nbh + bh) * a.nseg + seg) * kBP * kBN
+                                   : (first ? first + bh * kBP * kBN : nullptr);
+    float* dh0 = dir == 1 && seg == a.nseg - 1 && a.dh_init ? a.dh_init + bh * kBP * kBN : nullptr;
+    if (dir == 0) bwd_states_walk<false, true>(a, bh, k0, k1, init, nullptr, nullptr, sV, sK, sW);
+    else bwd_states_walk<true, true>(a, bh, k0, k1, init, dh0, nullptr, sV, sK, sW);
 }
 
 // --------------------------------------------------------- per-chunk gradients
@@ -417,14 +468,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         RowPieces<kRowX, kBQ> px, pdy;
         load_rows(px, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
         load_rows(pdy, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
-        const float* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
-        const float* hsrc = a.states + (bh * a.nc + c) * kBP * kBN;
-        float4 gq[4];
+        const uint16_t* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
+        const uint16_t* hsrc = a.states + (bh * a.nc + c) * kBP * kBN;
+        uint4 gq[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;  // 16-byte bf16 piece
-            gq[2 * k] = *reinterpret_cast<const float4*>(gsrc + (q / 16) * kBN + 8 * (q % 16));
-            gq[2 * k + 1] = *reinterpret_cast<const float4*>(gsrc + (q / 16) * kBN + 8 * (q % 16) + 4);
+            gq[k] = *reinterpret_cast<const uint4*>(gsrc + (q / 16) * kBN + 8 * (q % 16));
         }
         const int tt = static_cast<int>(threadIdx.x);
         float m_cs = 0.0f, m_dt = 0.0f, m_raw = 0.0f;
@@ -443,14 +493,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
             sOm[tt] = in && sSeq[tt] == seq_last ? decay_exp(cs_last - m_cs) : 0.0f;
             sKa[tt] = in && sSeq[tt] == seq_prev ? decay_exp(m_cs) : 0.0f;
         }
-        // g_out as the bf16 operand copy
+        // g_out as the bf16 operand
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            const float4 v0 = gq[2 * k], v1 = gq[2 * k + 1];
-            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)),
-                          make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
-                                     pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w)));
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)), gq[k]);
         }
         __syncthreads();
 
@@ -603,31 +650,27 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);  // one n block's operands live at a time
             }
         }
-        // <g_out, h_in> (fp32, g_out read again); then h_in replaces g_out as
-        // the bf16 operand
+        // <g_out, h_in> over their bf16 values (fp32 sums; g_out from its LDS
+        // operand); then h_in replaces g_out as the bf16 operand
         float ghp = 0.0f;
-        float hv[16];
+        uint4 hq[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
             const int p = q / 16, slot = q % 16;
-            const float4 v0 = *reinterpret_cast<const float4*>(hsrc + p * kBN + 8 * slot);
-            const float4 v1 = *reinterpret_cast<const float4*>(hsrc + p * kBN + 8 * slot + 4);
-            const float4 g0 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot);
-            const float4 g1 = *reinterpret_cast<const float4*>(gsrc + p * kBN + 8 * slot + 4);
-            hv[8 * k + 0] = v0.x; hv[8 * k + 1] = v0.y; hv[8 * k + 2] = v0.z; hv[8 * k + 3] = v0.w;
-            hv[8 * k + 4] = v1.x; hv[8 * k + 5] = v1.y; hv[8 * k + 6] = v1.z; hv[8 * k + 7] = v1.w;
-            ghp += g0.x * v0.x + g0.y * v0.y + g0.z * v0.z + g0.w * v0.w;
-            ghp += g1.x * v1.x + g1.y * v1.y + g1.z * v1.z + g1.w * v1.w;
+            hq[k] = *reinterpret_cast<const uint4*>(hsrc + p * kBN + 8 * slot);
+            const uint4 gv = lds_ld<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot));
+            const uint32_t hw[4] = {hq[k].x, hq[k].y, hq[k].z, hq[k].w};
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ghp += bf_lo(gw[e]) * bf_lo(hw[e]) + bf_hi(gw[e]) * bf_hi(hw[e]);
         }
         const float gh = block_sum(ghp, sRed);  // its barriers also end P3's reads of g_out
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            const int p = q / 16, slot = q % 16;
-            lds_st<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot),
-                          make_uint4(pack_bf16x2(hv[8 * k], hv[8 * k + 1]), pack_bf16x2(hv[8 * k + 2], hv[8 * k + 3]),
-                                     pack_bf16x2(hv[8 * k + 4], hv[8 * k + 5]), pack_bf16x2(hv[8 * k + 6], hv[8 * k + 7])));
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)), hq[k]);
         }
         __syncthreads();
 
@@ -783,8 +826,13 @@ hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st) {
                     nstate);
 }
 
+hipError_t launch_bwd_seg_ends(const BwdArgs& a, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(2 * static_cast<int64_t>(a.batch) * a.H * (a.nseg - 1)));
+    return dispatch(bwd_seg_ends_kernel, grid, dim3(kBThreads), st, a);
+}
+
 hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(2 * static_cast<int64_t>(a.batch) * a.H));
+    const dim3 grid(static_cast<unsigned>(2 * static_cast<int64_t>(a.batch) * a.H * a.nseg));
     return dispatch(bwd_states_kernel, grid, dim3(kBThreads), st, a);
 }
 

@@ -113,8 +113,11 @@ struct BwdArgs {
     const float* h_init;    // (b, H, P, N) or null
     const float* dh_final;  // (b, H, P, N) or null (zero)
     const float* cs;        // chunk_prep_kernel's metadata blocks (as ScanArgs::cs)
-    float* states;          // (b, H, nc, P, N) workspace: state before each chunk
-    float* gstates;         // (b, H, nc, P, N) workspace: gradient after each chunk
+    // (b, H, nc, P, N) bf16 workspace: the state before each chunk and the
+    // gradient after it, rounded once to the bf16 the gradient products take
+    // them in (the walks themselves carry them in fp32)
+    uint16_t* states;
+    uint16_t* gstates;
     float* partials;        // (b, nc, H, 3) workspace: dA, dD, d(dt_bias) per chunk
     void* dx;               // (b, L, H, P)
     float* ddt;             // (b, L, H): gradient with respect to dt_raw
@@ -124,6 +127,14 @@ struct BwdArgs {
     float* dD;              // (H) or null
     float* ddt_bias;        // (H) or null
     float* dh_init;         // (b, H, P, N) or null
+    // Segmented state walks (nseg > 1): the walk of every (direction, row,
+    // head) is cut into nseg segments of cps chunks (in walk order).
+    // seg_end (2, b*H, nseg, P*N) [p][n]: each segment's end state from a zero
+    // start, then (after a pass over segments) its incoming state; seg_mult
+    // (2, b*H, nseg): the product of the segment's chunk decays.
+    float* seg_end;
+    float* seg_mult;
+    int nseg, cps;
     int64_t L;
     int batch, H, G, nc;
 };
@@ -235,6 +246,7 @@ hipError_t launch_chunk_meta_bf16_64_128_128(const ScanArgs& a, int64_t nblocks,
 // (forward: before each chunk; reverse: gradient after each chunk, then
 // d(h_init); one launch), the per-(row, chunk, group) gradients, the per-head
 // sums.
+hipError_t launch_bwd_seg_ends(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st);
