@@ -597,7 +597,7 @@ def scan_workload_measure(ssd, lib, hip, torch, w, reps):
            "value": round(b * Lp / wall, 1), "unit": "tokens/s", "calls": reps,
            "ms_per_call": round(1e3 * wall, 4), "kernels_us": [round(u, 2) for u in kus],
            "call_kernel_us": round(ksum, 2), "compulsory_bytes": nbytes,
-           "roofline": roofline_entry(nbytes, ksum),
+           "roofline": roofline_entry(nbytes, ksum, counter_traffic(w.name)),
            "mfma_frac": round(scan_flops(b, Lp, H, P, N, G, Q) / (ksum * 1e-6) / 1e12
                               / MFMA_BF16_PEAK_TFLOPS, 4)}
     if w.decode_steps:
