@@ -303,19 +303,40 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, in
     if (!kChunks && mult && threadIdx.x == 0) *mult = prod;
 }
 
-// Segment ends of the walks (nseg > 1): workgroup w is (direction, row x
-// head, segment s < nseg - 1), direction slowest; each segment from a zero
-// state.
+// Work item of a walk workgroup: (direction, row, head, segment) with the
+// heads of a B/C group fastest, then the group, the segment, the row and the
+// direction; the XCD-aware order then gives the workgroups that share a
+// group's B (or C) rows the same L2.
+struct WalkItem {
+    int dir, seg;
+    int64_t bh;
+};
+__device__ __forceinline__ WalkItem walk_item(const BwdArgs& a, int nseg_grid) {
+    uint32_t w = static_cast<uint32_t>(xcd_work_index(blockIdx.x, gridDim.x));
+    const uint32_t hpg = static_cast<uint32_t>(a.H / a.G);
+    const uint32_t hh = w % hpg;
+    w /= hpg;
+    const uint32_t g = w % static_cast<uint32_t>(a.G);
+    w /= static_cast<uint32_t>(a.G);
+    WalkItem it;
+    it.seg = static_cast<int>(w % static_cast<uint32_t>(nseg_grid));
+    w /= static_cast<uint32_t>(nseg_grid);
+    const int64_t b = w % static_cast<uint32_t>(a.batch);
+    it.dir = static_cast<int>(w / static_cast<uint32_t>(a.batch));
+    it.bh = b * a.H + g * hpg + hh;
+    return it;
+}
+
+// Segment ends of the walks (nseg > 1): one workgroup per (direction, row,
+// head, segment s < nseg - 1); each segment from a zero state.
 __global__ __launch_bounds__(kBThreads) void bwd_seg_ends_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];
     __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];
     __shared__ __attribute__((aligned(16))) float sW[kBQ];
     const int64_t nbh = static_cast<int64_t>(a.batch) * a.H;
-    const int64_t per_dir = nbh * (a.nseg - 1);
-    const int64_t w = blockIdx.x;
-    const int dir = static_cast<int>(w / per_dir);
-    const int64_t bh = (w % per_dir) / (a.nseg - 1);
-    const int seg = static_cast<int>((w % per_dir) % (a.nseg - 1));
+    const WalkItem it = walk_item(a, a.nseg - 1);
+    const int dir = it.dir, seg = it.seg;
+    const int64_t bh = it.bh;
     const int k0 = seg * a.cps, k1 = min(k0 + a.cps, a.nc);
     const int64_t slot = (dir * nbh + bh) * a.nseg + seg;
     float* end = a.seg_end + slot * kBP * kBN;
@@ -324,8 +345,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_seg_ends_kernel(BwdArgs a) {
     else bwd_states_walk<true, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
 }
 
-// Both walks in one launch (they are independent): workgroup w is
-// (direction, row x head, segment), direction slowest.  A segment starts
+// Both walks in one launch (they are independent): one workgroup per
+// (direction, row, head, segment), ordered as walk_item says.  A segment starts
 // from its incoming state (after the pass over segment ends), the first from
 // h_init (forward) or d(final states) (backward); the backward walk's last
 // segment ends in d(h_init).
@@ -334,11 +355,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];   // B or C rows
     __shared__ __attribute__((aligned(16))) float sW[kBQ];            // per-token weights
     const int64_t nbh = static_cast<int64_t>(a.batch) * a.H;
-    const int64_t per_dir = nbh * a.nseg;
-    const int64_t w = blockIdx.x;
-    const int dir = static_cast<int>(w / per_dir);
-    const int64_t bh = (w % per_dir) / a.nseg;
-    const int seg = static_cast<int>((w % per_dir) % a.nseg);
+    const WalkItem it = walk_item(a, a.nseg);
+    const int dir = it.dir, seg = it.seg;
+    const int64_t bh = it.bh;
     const int k0 = seg * a.cps, k1 = min(k0 + a.cps, a.nc);
     const float* first = dir == 0 ? a.h_init : a.dh_final;
     const float* init = a.nseg > 1 ? a.seg_end + ((dir * nbh + bh) * a.nseg + seg) * kBP * kBN
