@@ -399,6 +399,15 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
+// One head's inputs of the gradient kernel, held in registers from their
+// loads to their LDS stores: x and dy rows, g_out (bf16), and this thread's
+// token of the metadata and of dt_raw.
+struct HeadInputs {
+    RowPieces<kRowX, kBQ> px, pdy;
+    uint4 gq[2];
+    float m_cs, m_dt, m_raw;
+};
+
 __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char sB[kBQ * kRowB];
     __shared__ __attribute__((aligned(1024))) char sC[kBQ * kRowB];
@@ -454,6 +463,33 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         dCacc[nb] = acc_zero();
     }
 
+    // loads of head hh's inputs, issued during the previous head's last
+    // phases (an earlier issue keeps them in registers through the heaviest
+    // phases, which then spill)
+    auto load_head = [&](int hh, HeadInputs& in) {
+        const int h = grp * hpg + hh;
+        const int64_t bh = b * a.H + h;
+        const int64_t xstride = static_cast<int64_t>(a.H) * kRowX;
+        load_rows(in.px, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
+        load_rows(in.pdy, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
+        const uint16_t* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;  // 16-byte bf16 piece
+            in.gq[k] = *reinterpret_cast<const uint4*>(gsrc + (q / 16) * kBN + 8 * (q % 16));
+        }
+        const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
+        const int tt = static_cast<int>(threadIdx.x);
+        in.m_cs = in.m_dt = in.m_raw = 0.0f;
+        if (tt < kBQ) {
+            in.m_cs = meta[tt];
+            in.m_dt = meta[kBQ + tt];
+            if (tt < valid) in.m_raw = a.dt_raw[(srow + t0 + tt) * a.H + h];
+        }
+    };
+    HeadInputs nx;
+    load_head(0, nx);
+
     for (int hh = 0; hh < hpg; ++hh) {
         // lane bases of this head's accesses (opaque: formed again per head)
         const uint32_t bsT = lds_keep(lds_addr(sT)), bsH = lds_keep(lds_addr(sH));
@@ -482,32 +518,16 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
         const float cs_last = meta[valid - 1];
         const float e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
-        // ---- head inputs: every load issued before any is used (one round trip)
-        const int64_t xstride = static_cast<int64_t>(a.H) * kRowX;
-        RowPieces<kRowX, kBQ> px, pdy;
-        load_rows(px, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
-        load_rows(pdy, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
-        const uint16_t* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
+        // ---- head inputs (loaded during the previous head)
         const uint16_t* hsrc = a.states + (bh * a.nc + c) * kBP * kBN;
-        uint4 gq[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;  // 16-byte bf16 piece
-            gq[k] = *reinterpret_cast<const uint4*>(gsrc + (q / 16) * kBN + 8 * (q % 16));
-        }
         const int tt = static_cast<int>(threadIdx.x);
-        float m_cs = 0.0f, m_dt = 0.0f, m_raw = 0.0f;
-        if (tt < kBQ) {
-            m_cs = meta[tt];
-            m_dt = meta[kBQ + tt];
-            if (tt < valid) m_raw = a.dt_raw[(srow + t0 + tt) * a.H + h];
-        }
-        store_rows(sX, px);
-        store_rows(sDY, pdy);
+        const float m_cs = nx.m_cs;
+        store_rows(sX, nx.px);
+        store_rows(sDY, nx.pdy);
         if (tt < kBQ) {
             sCs[tt] = m_cs;
-            sDt[tt] = m_dt;
-            sRaw[tt] = m_raw;
+            sDt[tt] = nx.m_dt;
+            sRaw[tt] = nx.m_raw;
             const bool in = tt < valid;
             sOm[tt] = in && sSeq[tt] == seq_last ? decay_exp(cs_last - m_cs) : 0.0f;
             sKa[tt] = in && sSeq[tt] == seq_prev ? decay_exp(m_cs) : 0.0f;
@@ -516,7 +536,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)), gq[k]);
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)), nx.gq[k]);
         }
         __syncthreads();
 
@@ -650,6 +670,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         }
         __syncthreads();
 
+        // h_in's loads, in flight during P3 (its first use is after P3)
+        uint4 hq[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
+            hq[k] = *reinterpret_cast<const uint4*>(hsrc + (q / 16) * kBN + 8 * (q % 16));
+        }
         // ---- P3: dB^T += C^T W' + dt_j omega_j g_out^T X^T, columns j of block J = wave
         {
             const int J = wave;
@@ -672,12 +699,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         // <g_out, h_in> over their bf16 values (fp32 sums; g_out from its LDS
         // operand); then h_in replaces g_out as the bf16 operand
         float ghp = 0.0f;
-        uint4 hq[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
             const int p = q / 16, slot = q % 16;
-            hq[k] = *reinterpret_cast<const uint4*>(hsrc + p * kBN + 8 * slot);
             const uint4 gv = lds_ld<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot));
             const uint32_t hw[4] = {hq[k].x, hq[k].y, hq[k].z, hq[k].w};
             const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -693,6 +718,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         }
         __syncthreads();
 
+        // the next head's inputs, in flight during P4 and the dcs pass
+        if (hh + 1 < hpg) load_head(hh + 1, nx);
         // ---- P4: dC^T += B^T W'^T + kappa_i h_in^T dY^T, columns i of block I = wave
         {
             const int i = 16 * I + r16;
