@@ -180,9 +180,11 @@ struct BwdPlan {
            off_mult = 0, total = 0;
 };
 
-// Workgroups the gradient path's state walks aim for (two per CU: both
-// directions of every row x head, cut into segments when there are few).
-constexpr int64_t kBwdWalkWorkgroups = 512;
+// Chunks per segment of the gradient path's state walks.  Fixed in chunks
+// (not chosen from rows x heads as the forward's segments are), so that a
+// row's gradients are bitwise the same whatever batch it is in: at 8K, 4
+// segments and 512 walk workgroups.
+constexpr int64_t kBwdWalkChunks = 16;
 
 // Workspace of the gradient path: the metadata blocks of chunk_prep_kernel,
 // the bf16 state before and the gradient after every chunk, per-chunk sums,
@@ -191,11 +193,7 @@ BwdPlan make_bwd_plan(const ssd_dims& d) {
     BwdPlan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
     p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
-    const int64_t walks = 2 * d.batch * d.nheads;
-    int64_t nseg = (kBwdWalkWorkgroups + walks - 1) / walks;
-    if (nseg > p.nc) nseg = p.nc;
-    if (nseg < 1) nseg = 1;
-    p.cps = (p.nc + nseg - 1) / nseg;
+    p.cps = p.nc < kBwdWalkChunks ? p.nc : kBwdWalkChunks;
     p.nseg = (p.nc + p.cps - 1) / p.cps;
     const size_t bhc = static_cast<size_t>(d.batch * d.nheads * p.nc);
     size_t off = 0;

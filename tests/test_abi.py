@@ -325,12 +325,14 @@ def test_bwd_workspace_bytes(lib):
     meta = b * H * nc * 128 * 3 * 4
     states = b * H * nc * 64 * 128 * 2
     parts = 256 * math.ceil(b * H * nc * 3 * 4 / 256)
-    # 2 x 64 walks, cut into 4 segments: end states (fp32 P x N) and decay products
+    # 2 x 64 walks, cut into segments of 16 chunks: end states (fp32 P x N) and decay products
     segs = 2 * b * H * 4
     seg = segs * 64 * 128 * 4 + 256 * math.ceil(segs * 4 / 256)
     assert ssd.bwd_workspace_bytes(b, L, H, 64, 128, G, 128) == meta + 2 * states + parts + seg
-    # enough rows x heads: one segment
-    assert ssd.bwd_workspace_bytes(4, L, H, 64, 128, G, 128) == 4 * (meta + 2 * states + parts)
+    # segments fixed in chunks, whatever the batch: four rows, four times the bytes
+    assert ssd.bwd_workspace_bytes(4, L, H, 64, 128, G, 128) == 4 * (meta + 2 * states + parts + seg)
+    # up to 16 chunks: one segment, no segment scratch
+    assert ssd.bwd_workspace_bytes(1, 2048, H, 64, 128, G, 128) == (meta + 2 * states + parts) // 4
     assert ssd.bwd_workspace_bytes(1, 0, H, 64, 128, G, 128) == 0
     assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 64, io=ssd.BF16) == 0   # Q 64: not built
     assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 128, io=ssd.F32) == 0   # fp32: not built

@@ -116,6 +116,25 @@ def test_bwd_deterministic():
             assert np.array_equal(g1[k], g2[k]), k
 
 
+def test_bwd_batch_invariant():
+    """A row's gradients (dx, d(dt_raw), dB, dC, d(initial_states)) are
+    bitwise the same computed alone and inside a batch of three (RFC section
+    4.1: batch invariance, forward and backward).  2500 tokens: 20 chunks, so
+    the state walks run in two segments.  dA, dD and d(dt_bias) sum over the
+    batch and are not per-row quantities."""
+    b, L, H, G = 3, 2500, 4, 2
+    p = _problem(19, b, L, H, G, init=True, dfinal=True)
+    whole = _run(p)
+    for r in range(b):
+        q = {k: (v[r:r + 1] if k in ("x", "dt_raw", "B", "C", "dy", "h_init", "dfinal") and v is not None
+                 else v) for k, v in p.items()}
+        alone = _run(q)
+        for k in ("dx", "ddt", "dB", "dC", "d_initial_states"):
+            assert np.array_equal(whole[k][r:r + 1], alone[k]), (r, k)
+    # and the gradients themselves are right
+    _compare(whole, _reference(p), p)
+
+
 def test_bwd_rejects_unsupported():
     """Outside the compiled set the call fails closed before any launch."""
     import torch
