@@ -312,9 +312,12 @@ size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* dims, ssd_dtype io);
  *
  * No output may overlap an input, another output or the workspace
  * (SSD_ERR_ALIAS).  Supported set: io = SSD_BF16, headdim 64, dstate 128,
- * chunk_size 128 (else SSD_ERR_UNSUPPORTED); any b, L (L = 0 gives zero sums
- * and d_initial_states = d_final_states), H % G == 0.  Deterministic: every
- * sum is taken in a fixed order, without atomics.
+ * chunk_size 64, 128 or 256 (else SSD_ERR_UNSUPPORTED; the gradients are those
+ * of the recurrence whatever the chunk size, and the kernels run 128-token
+ * chunks); any b, L (L = 0 gives zero sums and d_initial_states =
+ * d_final_states), H % G == 0.  Deterministic: every sum is taken in a fixed
+ * order, without atomics.  A row's dx, ddt, dB, dC and d_initial_states are
+ * bitwise the same in any batch (dA, dD and ddt_bias sum over the batch).
  */
 ssd_status ssd_chunk_scan_bwd(const ssd_dims* dims, ssd_dtype io, const void* x,
                               const float* dt, const float* dt_bias, int dt_softplus,

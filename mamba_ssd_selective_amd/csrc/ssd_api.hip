@@ -155,7 +155,11 @@ ssd_status check_scan_dims(const ssd_dims* d, ssd_dtype io) {
     return SSD_OK;
 }
 
-// The gradient path's compiled set: bf16, P = 64, N = 128, chunk 128.
+// Chunk size the gradient kernels run with.
+constexpr int64_t kBwdChunk = 128;
+
+// The gradient path's compiled set: bf16, P = 64, N = 128, and the forward's
+// chunk sizes of that shape (64, 128, 256), all run as 128-token chunks.
 ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
     if (!d) return SSD_ERR_NULL_ARG;
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
@@ -165,10 +169,14 @@ ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
     if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
     if (d->batch > 65535 || d->nheads > 65535 || d->seqlen >= (int64_t(1) << 31))
         return SSD_ERR_BAD_SHAPE;
-    if (io != SSD_BF16 || d->headdim != 64 || d->dstate != 128 || d->chunk_size != 128)
+    // the gradients of the scan are those of the recurrence whatever the
+    // chunk size, so the caller's chunk grid (the forward's compiled chunks)
+    // is served by the 128-token kernels
+    if (io != SSD_BF16 || d->headdim != 64 || d->dstate != 128 ||
+        (d->chunk_size != 64 && d->chunk_size != 128 && d->chunk_size != 256))
         return SSD_ERR_UNSUPPORTED;
     // grids: (row, chunk, group) and (row, head) workgroups below 2^31
-    const int64_t nc = (d->seqlen + d->chunk_size - 1) / d->chunk_size;
+    const int64_t nc = (d->seqlen + kBwdChunk - 1) / kBwdChunk;
     if (d->batch * nc * d->ngroups >= (int64_t(1) << 31) || d->batch * d->nheads >= (int64_t(1) << 31))
         return SSD_ERR_BAD_SHAPE;
     return SSD_OK;
@@ -192,13 +200,13 @@ constexpr int64_t kBwdWalkChunks = 16;
 BwdPlan make_bwd_plan(const ssd_dims& d) {
     BwdPlan p;
     if (d.seqlen <= 0 || d.batch <= 0) return p;
-    p.nc = (d.seqlen + d.chunk_size - 1) / d.chunk_size;
+    p.nc = (d.seqlen + kBwdChunk - 1) / kBwdChunk;
     p.cps = p.nc < kBwdWalkChunks ? p.nc : kBwdWalkChunks;
     p.nseg = (p.nc + p.cps - 1) / p.cps;
     const size_t bhc = static_cast<size_t>(d.batch * d.nheads * p.nc);
     size_t off = 0;
     p.off_meta = off;
-    off = align_up(off + bhc * static_cast<size_t>(d.chunk_size) * 3 * sizeof(float));
+    off = align_up(off + bhc * static_cast<size_t>(kBwdChunk) * 3 * sizeof(float));
     p.off_states = off;
     off = align_up(off + bhc * static_cast<size_t>(d.headdim * d.dstate) * sizeof(uint16_t));
     p.off_gstates = off;
@@ -903,8 +911,8 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     sa.dt_max = dt_max;
     sa.seq_idx = seq_idx;
     sa.cs = meta;
-    sa.dtv = meta + d->chunk_size;
-    sa.wgt = meta + 2 * d->chunk_size;
+    sa.dtv = meta + kBwdChunk;
+    sa.wgt = meta + 2 * kBwdChunk;
     sa.L = L;
     sa.H = ba.H;
     sa.G = ba.G;

@@ -334,7 +334,10 @@ def test_bwd_workspace_bytes(lib):
     # up to 16 chunks: one segment, no segment scratch
     assert ssd.bwd_workspace_bytes(1, 2048, H, 64, 128, G, 128) == (meta + 2 * states + parts) // 4
     assert ssd.bwd_workspace_bytes(1, 0, H, 64, 128, G, 128) == 0
-    assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 64, io=ssd.BF16) == 0   # Q 64: not built
+    # chunk 64 and 256 run as 128-token chunks: the same workspace
+    assert ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 64) == ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 128)
+    assert ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 256) == ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 128)
+    assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 32) == 0   # not a compiled chunk
     assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 128, io=ssd.F32) == 0   # fp32: not built
 
 
@@ -356,6 +359,7 @@ def _bwd_call(lib, dims=(1, 256, 4, 64, 128, 1, 128), io=ssd.BF16, **over):
 def test_bwd_rejects_bad_arguments(lib):
     assert _bwd_call(lib, io=ssd.F32) == UNSUPPORTED
     assert _bwd_call(lib, dims=(1, 256, 4, 64, 64, 1, 128)) == UNSUPPORTED
+    assert _bwd_call(lib, dims=(1, 256, 4, 64, 128, 1, 32)) == UNSUPPORTED
     assert _bwd_call(lib, dims=(1, 256, 6, 64, 128, 4, 128)) == BAD_SHAPE   # H % G
     assert _bwd_call(lib, dy=None) == NULL_ARG
     assert _bwd_call(lib, dA=None) == NULL_ARG

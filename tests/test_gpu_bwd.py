@@ -144,7 +144,24 @@ def test_bwd_rejects_unsupported():
     with pytest.raises(ssd.SSDError):
         ssd.chunk_scan_bwd(to_dev(p["x"], bf), to_dev(p["dt_raw"]), to_dev(p["A"]),
                            to_dev(p["B"], bf), to_dev(p["C"], bf), to_dev(p["dy"], bf),
-                           chunk_size=64)
+                           chunk_size=32)
+
+
+@pytest.mark.parametrize("Q", [64, 256])
+def test_bwd_other_chunk_sizes(Q):
+    """The forward's other chunk sizes of this shape: the gradients of the
+    same recurrence (run as 128-token chunks), against the oracle."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    p = _problem(23, 2, 600, 4, 2, init=True, dfinal=True)
+    bf = torch.bfloat16
+    t = lambda k, dtype=None: to_dev(p[k], dtype)
+    g = ssd.chunk_scan_bwd(t("x", bf), t("dt_raw"), t("A"), t("B", bf), t("C", bf), t("dy", bf),
+                           chunk_size=Q, D=t("D"), dt_bias=t("dt_bias"), initial_states=t("h_init"),
+                           d_final_states=t("dfinal"))
+    torch.cuda.synchronize()
+    got = {k: (None if v is None else v.float().cpu().numpy()) for k, v in g.items()}
+    _compare(got, _reference(p), p)
 
 
 def test_bwd_prefill_8k_one_group():
