@@ -311,7 +311,7 @@ size_t ssd_chunk_scan_bwd_workspace_bytes(const ssd_dims* dims, ssd_dtype io);
  *   stream                 hipStream_t
  *
  * No output may overlap an input, another output or the workspace
- * (SSD_ERR_ALIAS).  Supported set: io = SSD_BF16, headdim 64, dstate 128,
+ * (SSD_ERR_ALIAS).  Supported set: io = SSD_BF16, headdim 64, dstate 128 or 64,
  * chunk_size 64, 128 or 256 (else SSD_ERR_UNSUPPORTED; the gradients are those
  * of the recurrence whatever the chunk size, and the kernels run 128-token
  * chunks); any b, L (L = 0 gives zero sums and d_initial_states =

@@ -158,8 +158,8 @@ ssd_status check_scan_dims(const ssd_dims* d, ssd_dtype io) {
 // Chunk size the gradient kernels run with.
 constexpr int64_t kBwdChunk = 128;
 
-// The gradient path's compiled set: bf16, P = 64, N = 128, and the forward's
-// chunk sizes of that shape (64, 128, 256), all run as 128-token chunks.
+// The gradient path's compiled set: bf16, P = 64, N = 128 or 64, and chunk
+// sizes 64, 128 and 256, all run as 128-token chunks.
 ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
     if (!d) return SSD_ERR_NULL_ARG;
     if (io != SSD_F32 && io != SSD_BF16) return SSD_ERR_BAD_DTYPE;
@@ -172,7 +172,7 @@ ssd_status check_bwd_dims(const ssd_dims* d, ssd_dtype io) {
     // the gradients of the scan are those of the recurrence whatever the
     // chunk size, so the caller's chunk grid (the forward's compiled chunks)
     // is served by the 128-token kernels
-    if (io != SSD_BF16 || d->headdim != 64 || d->dstate != 128 ||
+    if (io != SSD_BF16 || d->headdim != 64 || (d->dstate != 128 && d->dstate != 64) ||
         (d->chunk_size != 64 && d->chunk_size != 128 && d->chunk_size != 256))
         return SSD_ERR_UNSUPPORTED;
     // grids: (row, chunk, group) and (row, head) workgroups below 2^31
@@ -884,6 +884,7 @@ ssd_status ssd_chunk_scan_bwd(const ssd_dims* d, ssd_dtype io, const void* x, co
     ba.nc = static_cast<int>(plan.nc);
     ba.nseg = static_cast<int>(plan.nseg);
     ba.cps = static_cast<int>(plan.cps);
+    ba.N = static_cast<int>(N);
     if (!work) {
         if (timed_launch(k, hs, [&] { return ssd::launch_bwd_empty(ba, b * H * P * N, hs); }) !=
             hipSuccess)

@@ -61,12 +61,23 @@
 namespace ssd {
 namespace {
 
-constexpr int kBP = 64, kBN = 128, kBQ = 128;  // compiled shape
+// Compiled shapes: P = 64, Q = 128, N (the state size) a template parameter
+// of the kernels, 128 or 64.
+constexpr int kBP = 64, kBQ = 128;
 constexpr int kBWaves = 8;
 constexpr int kBThreads = kBWaves * kWave;
 constexpr int kRowX = 2 * kBP;   // bytes of a token row of an x / dy tile
-constexpr int kRowB = 2 * kBN;   // bytes of a token row of a B / C tile, of a state row
 constexpr int kRowT = 2 * kBQ;   // bytes of a row of a Q x Q matrix
+// bytes of a token row of a B / C tile, and of a state row, for state size N
+template <int N>
+struct BwdN {
+    static_assert(N == 64 || N == 128, "compiled state sizes");
+    static constexpr int RB = 2 * N;
+    static constexpr int NNB = N / 16;        // 16-wide n blocks
+    static constexpr int SP = N / 8;          // 16-byte pieces of a state row
+    static constexpr int GP = kBP * SP / kBThreads;  // a state's pieces per thread
+    static_assert(kBP * SP % kBThreads == 0, "whole rounds");
+};
 
 // ------------------------------------------------------------------ helpers
 
@@ -198,7 +209,8 @@ __device__ __forceinline__ int seq_at(const int32_t* seq, int64_t row_base, int6
 // The state before every chunk (forward: h_in, chunk order) or the gradient
 // after every chunk (backward: g_out, reverse chunk order), fp32 [p][n] in
 // `states` at (row, head, chunk).  Wave w owns state rows n = 16w + 4g + r,
-// column p = 16pb + r16 (the MFMA accumulator layout).
+// column p = 16pb + r16 (the MFMA accumulator layout); with N = 64 waves
+// 4-7 own no n block and only help with the copies.
 // One walk covers the chunks k in [k_begin, k_end) of the walk order (chunk
 // k, or nc - 1 - k backwards), starting from `init` (P x N, or zero):
 //  kChunks = true:  the state before each of them is written to `states`;
@@ -206,13 +218,15 @@ __device__ __forceinline__ int seq_at(const int32_t* seq, int64_t row_base, int6
 //  kChunks = false: only the state at the end is written, to `end`, and the
 //                   product of the chunks' decays to *mult (a segment's part
 //                   of the chain, for a pass over segments).
-template <bool kRev, bool kChunks>
+template <int N, bool kRev, bool kChunks>
 __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, int k_begin, int k_end,
                                                 const float* init, float* end, float* mult,
                                                 char* sV, char* sK, float* sW) {
+    constexpr int kRowB = BwdN<N>::RB;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
     const int r16 = lane & 15, g = lane >> 4;
+    const bool owner = wave < BwdN<N>::NNB;  // owns n block `wave`
     const int64_t b = bh / a.H;
     const int h = static_cast<int>(bh % a.H);
     const int grp = h / (a.H / a.G);
@@ -223,8 +237,8 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, in
 #pragma unroll
     for (int pb = 0; pb < kBP / 16; ++pb) {
         st[pb] = acc_zero();
-        if (init) {
-            const float4 v = *reinterpret_cast<const float4*>(init + (16 * pb + r16) * kBN +
+        if (init && owner) {
+            const float4 v = *reinterpret_cast<const float4*>(init + (16 * pb + r16) * N +
                                                               16 * wave + 4 * g);
             st[pb] = f32x4_t{v.x, v.y, v.z, v.w};
         }
@@ -266,12 +280,12 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, in
     if (k_begin < k_end) fetch(k_begin, nx);
     for (int k = k_begin; k < k_end; ++k) {
         const int c = kRev ? a.nc - 1 - k : k;
-        if constexpr (kChunks) {
+        if (kChunks && owner) {
             // the state before this chunk's update, as bf16 [p][n]
-            uint16_t* dst = (kRev ? a.gstates : a.states) + (bh * a.nc + c) * kBP * kBN;
+            uint16_t* dst = (kRev ? a.gstates : a.states) + (bh * a.nc + c) * kBP * N;
 #pragma unroll
             for (int pb = 0; pb < kBP / 16; ++pb)
-                *reinterpret_cast<uint2*>(dst + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
+                *reinterpret_cast<uint2*>(dst + (16 * pb + r16) * N + 16 * wave + 4 * g) =
                     make_uint2(pack_bf16x2(st[pb][0], st[pb][1]), pack_bf16x2(st[pb][2], st[pb][3]));
         }
         store_rows(sV, nx.v);
@@ -282,22 +296,24 @@ __device__ __forceinline__ void bwd_states_walk(const BwdArgs& a, int64_t bh, in
         __syncthreads();
         if (k + 1 < k_end) fetch(k + 1, nx);  // in flight during this chunk's products
         const uint32_t bsK = lds_keep(lds_addr(sK)), bsV = lds_keep(lds_addr(sV));
+        if (owner) {
 #pragma unroll
-        for (int pb = 0; pb < kBP / 16; ++pb)
+            for (int pb = 0; pb < kBP / 16; ++pb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[pb][r] *= e;
+                for (int r = 0; r < 4; ++r) st[pb][r] *= e;
 #pragma unroll
-        for (int s = 0; s < kBQ / 32; ++s) {
-            const Frag<uint16_t> kf = scale_tk(col_frag<kRowB>(sK, bsK, wave, s, lane), sW, s, g);
+            for (int s = 0; s < kBQ / 32; ++s) {
+                const Frag<uint16_t> kf = scale_tk(col_frag<kRowB>(sK, bsK, wave, s, lane), sW, s, g);
 #pragma unroll
-            for (int pb = 0; pb < kBP / 16; ++pb) mma(st[pb], kf, col_frag<kRowX>(sV, bsV, pb, s, lane));
+                for (int pb = 0; pb < kBP / 16; ++pb) mma(st[pb], kf, col_frag<kRowX>(sV, bsV, pb, s, lane));
+            }
         }
         __syncthreads();
     }
-    if (end) {
+    if (end && owner) {
 #pragma unroll
         for (int pb = 0; pb < kBP / 16; ++pb)
-            *reinterpret_cast<float4*>(end + (16 * pb + r16) * kBN + 16 * wave + 4 * g) =
+            *reinterpret_cast<float4*>(end + (16 * pb + r16) * N + 16 * wave + 4 * g) =
                 make_float4(st[pb][0], st[pb][1], st[pb][2], st[pb][3]);
     }
     if (!kChunks && mult && threadIdx.x == 0) *mult = prod;
@@ -329,7 +345,9 @@ __device__ __forceinline__ WalkItem walk_item(const BwdArgs& a, int nseg_grid) {
 
 // Segment ends of the walks (nseg > 1): one workgroup per (direction, row,
 // head, segment s < nseg - 1); each segment from a zero state.
+template <int N>
 __global__ __launch_bounds__(kBThreads) void bwd_seg_ends_kernel(BwdArgs a) {
+    constexpr int kRowB = BwdN<N>::RB;
     __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];
     __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];
     __shared__ __attribute__((aligned(16))) float sW[kBQ];
@@ -339,10 +357,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_seg_ends_kernel(BwdArgs a) {
     const int64_t bh = it.bh;
     const int k0 = seg * a.cps, k1 = min(k0 + a.cps, a.nc);
     const int64_t slot = (dir * nbh + bh) * a.nseg + seg;
-    float* end = a.seg_end + slot * kBP * kBN;
+    float* end = a.seg_end + slot * kBP * N;
     float* mult = a.seg_mult + slot;
-    if (dir == 0) bwd_states_walk<false, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
-    else bwd_states_walk<true, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
+    if (dir == 0) bwd_states_walk<N, false, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
+    else bwd_states_walk<N, true, false>(a, bh, k0, k1, nullptr, end, mult, sV, sK, sW);
 }
 
 // Both walks in one launch (they are independent): one workgroup per
@@ -350,7 +368,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_seg_ends_kernel(BwdArgs a) {
 // from its incoming state (after the pass over segment ends), the first from
 // h_init (forward) or d(final states) (backward); the backward walk's last
 // segment ends in d(h_init).
+template <int N>
 __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
+    constexpr int kRowB = BwdN<N>::RB;
     __shared__ __attribute__((aligned(1024))) char sV[kBQ * kRowX];   // x or dy rows
     __shared__ __attribute__((aligned(1024))) char sK[kBQ * kRowB];   // B or C rows
     __shared__ __attribute__((aligned(16))) float sW[kBQ];            // per-token weights
@@ -360,11 +380,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
     const int64_t bh = it.bh;
     const int k0 = seg * a.cps, k1 = min(k0 + a.cps, a.nc);
     const float* first = dir == 0 ? a.h_init : a.dh_final;
-    const float* init = a.nseg > 1 ? a.seg_end + ((dir * nbh + bh) * a.nseg + seg) * kBP * kBN
-                                   : (first ? first + bh * kBP * kBN : nullptr);
-    float* dh0 = dir == 1 && seg == a.nseg - 1 && a.dh_init ? a.dh_init + bh * kBP * kBN : nullptr;
-    if (dir == 0) bwd_states_walk<false, true>(a, bh, k0, k1, init, nullptr, nullptr, sV, sK, sW);
-    else bwd_states_walk<true, true>(a, bh, k0, k1, init, dh0, nullptr, sV, sK, sW);
+    const float* init = a.nseg > 1 ? a.seg_end + ((dir * nbh + bh) * a.nseg + seg) * kBP * N
+                                   : (first ? first + bh * kBP * N : nullptr);
+    float* dh0 = dir == 1 && seg == a.nseg - 1 && a.dh_init ? a.dh_init + bh * kBP * N : nullptr;
+    if (dir == 0) bwd_states_walk<N, false, true>(a, bh, k0, k1, init, nullptr, nullptr, sV, sK, sW);
+    else bwd_states_walk<N, true, true>(a, bh, k0, k1, init, dh0, nullptr, sV, sK, sW);
 }
 
 // --------------------------------------------------------- per-chunk gradients
@@ -402,13 +422,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // One head's inputs of the gradient kernel, held in registers from their
 // loads to their LDS stores: x and dy rows, g_out (bf16), and this thread's
 // token of the metadata and of dt_raw.
+template <int N>
 struct HeadInputs {
     RowPieces<kRowX, kBQ> px, pdy;
-    uint4 gq[2];
+    uint4 gq[BwdN<N>::GP];
     float m_cs, m_dt, m_raw;
 };
 
+template <int N>
 __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
+    constexpr int kRowB = BwdN<N>::RB;
+    constexpr int NNB = BwdN<N>::NNB;  // n blocks of dB, dC and the states
+    constexpr int SP = BwdN<N>::SP;    // 16-byte pieces of a state row
+    constexpr int GP = BwdN<N>::GP;    // a state's pieces per thread
     __shared__ __attribute__((aligned(1024))) char sB[kBQ * kRowB];
     __shared__ __attribute__((aligned(1024))) char sC[kBQ * kRowB];
     __shared__ __attribute__((aligned(1024))) char sX[kBQ * kRowX];
@@ -456,9 +482,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
     for (int t = static_cast<int>(threadIdx.x); t < kBQ; t += kBThreads)
         sSeq[t] = seq_at(a.seq_idx, srow, t0 + t, L);
     __syncthreads();
-    f32x4_t dBacc[8], dCacc[8];  // dB^T tiles (nb, J = wave), dC^T tiles (nb, I = wave)
+    f32x4_t dBacc[NNB], dCacc[NNB];  // dB^T tiles (nb, J = wave), dC^T tiles (nb, I = wave)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+    for (int nb = 0; nb < NNB; ++nb) {
         dBacc[nb] = acc_zero();
         dCacc[nb] = acc_zero();
     }
@@ -466,17 +492,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
     // loads of head hh's inputs, issued during the previous head's last
     // phases (an earlier issue keeps them in registers through the heaviest
     // phases, which then spill)
-    auto load_head = [&](int hh, HeadInputs& in) {
+    auto load_head = [&](int hh, HeadInputs<N>& in) {
         const int h = grp * hpg + hh;
         const int64_t bh = b * a.H + h;
         const int64_t xstride = static_cast<int64_t>(a.H) * kRowX;
         load_rows(in.px, static_cast<const char*>(a.x) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
         load_rows(in.pdy, static_cast<const char*>(a.dy) + ((srow + t0) * a.H + h) * kRowX, xstride, valid);
-        const uint16_t* gsrc = a.gstates + (bh * a.nc + c) * kBP * kBN;
+        const uint16_t* gsrc = a.gstates + (bh * a.nc + c) * kBP * N;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < GP; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;  // 16-byte bf16 piece
-            in.gq[k] = *reinterpret_cast<const uint4*>(gsrc + (q / 16) * kBN + 8 * (q % 16));
+            in.gq[k] = *reinterpret_cast<const uint4*>(gsrc + (q / SP) * N + 8 * (q % SP));
         }
         const float* meta = a.cs + meta_offset_bwd(a, b, h, c);
         const int tt = static_cast<int>(threadIdx.x);
@@ -487,7 +513,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
             if (tt < valid) in.m_raw = a.dt_raw[(srow + t0 + tt) * a.H + h];
         }
     };
-    HeadInputs nx;
+    HeadInputs<N> nx;
     load_head(0, nx);
 
     for (int hh = 0; hh < hpg; ++hh) {
@@ -519,7 +545,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         const float cs_last = meta[valid - 1];
         const float e = seq_last == seq_prev ? decay_exp(cs_last) : 0.0f;
         // ---- head inputs (loaded during the previous head)
-        const uint16_t* hsrc = a.states + (bh * a.nc + c) * kBP * kBN;
+        const uint16_t* hsrc = a.states + (bh * a.nc + c) * kBP * N;
         const int tt = static_cast<int>(threadIdx.x);
         const float m_cs = nx.m_cs;
         store_rows(sX, nx.px);
@@ -534,9 +560,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         }
         // g_out as the bf16 operand
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < GP; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)), nx.gq[k]);
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / SP, 16 * (q % SP)), nx.gq[k]);
         }
         __syncthreads();
 
@@ -569,7 +595,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                 const f32x4_t m1 = m1_tile(J);
                 f32x4_t cbt = acc_zero();
 #pragma unroll
-                for (int ks = 0; ks < kBN / 32; ++ks)
+                for (int ks = 0; ks < N / 32; ++ks)
                     mma(cbt, row_at<kRowB>(sC, rbC, I, ks), row_at<kRowB>(sB, rbB, J, ks));
                 const float dt_j = sDt[16 * J + r16];
 #pragma unroll
@@ -611,7 +637,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
                 }
             }
 #pragma unroll
-            for (int ks = 0; ks < kBN / 32; ++ks) {
+            for (int ks = 0; ks < N / 32; ++ks) {
                 const Frag<uint16_t> bf = row_at<kRowB>(sB, rbB, J, ks);
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) mma(vt[pb], row_at<kRowB>(sH, rbH, pb, ks), bf);
@@ -671,11 +697,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         __syncthreads();
 
         // h_in's loads, in flight during P3 (its first use is after P3)
-        uint4 hq[2];
+        uint4 hq[GP];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < GP; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            hq[k] = *reinterpret_cast<const uint4*>(hsrc + (q / 16) * kBN + 8 * (q % 16));
+            hq[k] = *reinterpret_cast<const uint4*>(hsrc + (q / SP) * N + 8 * (q % SP));
         }
         // ---- P3: dB^T += C^T W' + dt_j omega_j g_out^T X^T, columns j of block J = wave
         {
@@ -683,7 +709,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
             const int j = 16 * J + r16;
             const float dt_j = sDt[j], om_j = sOm[j];
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
+            for (int nb = 0; nb < NNB; ++nb) {
                 f32x4_t a1 = acc_zero(), a2 = acc_zero();
 #pragma unroll
                 for (int ks = 0; ks < kBQ / 32; ++ks)
@@ -700,9 +726,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         // operand); then h_in replaces g_out as the bf16 operand
         float ghp = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < GP; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            const int p = q / 16, slot = q % 16;
+            const int p = q / SP, slot = q % SP;
             const uint4 gv = lds_ld<uint4>(sH, bsH + tr_off<kRowB>(p, 16 * slot));
             const uint32_t hw[4] = {hq[k].x, hq[k].y, hq[k].z, hq[k].w};
             const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -712,9 +738,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
         }
         const float gh = block_sum(ghp, sRed);  // its barriers also end P3's reads of g_out
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < GP; ++k) {
             const int q = static_cast<int>(threadIdx.x) + kBThreads * k;
-            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / 16, 16 * (q % 16)), hq[k]);
+            lds_st<uint4>(sH, bsH + tr_off<kRowB>(q / SP, 16 * (q % SP)), hq[k]);
         }
         __syncthreads();
 
@@ -726,7 +752,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
             const float ka_i = sKa[i];
             float car = 0.0f;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
+            for (int nb = 0; nb < NNB; ++nb) {
                 f32x4_t cw = acc_zero(), cc = acc_zero();
 #pragma unroll
                 for (int ks = 0; ks < kBQ / 32; ++ks)
@@ -814,10 +840,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdArgs a) {
     // ---- dB, dC of the group: lane holds n = 16nb + 4g .. +3 of row 16 * wave + r16
     const int jr = 16 * wave + r16;
     if (jr < valid) {
-        uint16_t* dbp = static_cast<uint16_t*>(a.dB) + ((srow + t0 + jr) * a.G + grp) * kBN + 4 * g;
-        uint16_t* dcp = static_cast<uint16_t*>(a.dC) + ((srow + t0 + jr) * a.G + grp) * kBN + 4 * g;
+        uint16_t* dbp = static_cast<uint16_t*>(a.dB) + ((srow + t0 + jr) * a.G + grp) * N + 4 * g;
+        uint16_t* dcp = static_cast<uint16_t*>(a.dC) + ((srow + t0 + jr) * a.G + grp) * N + 4 * g;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
+        for (int nb = 0; nb < NNB; ++nb) {
             *reinterpret_cast<uint2*>(dbp + 16 * nb) = pack4(dBacc[nb]);
             *reinterpret_cast<uint2*>(dcp + 16 * nb) = pack4(dCacc[nb]);
         }
@@ -874,17 +900,20 @@ hipError_t launch_bwd_empty(const BwdArgs& a, int64_t nstate, hipStream_t st) {
 
 hipError_t launch_bwd_seg_ends(const BwdArgs& a, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(2 * static_cast<int64_t>(a.batch) * a.H * (a.nseg - 1)));
-    return dispatch(bwd_seg_ends_kernel, grid, dim3(kBThreads), st, a);
+    if (a.N == 64) return dispatch(bwd_seg_ends_kernel<64>, grid, dim3(kBThreads), st, a);
+    return dispatch(bwd_seg_ends_kernel<128>, grid, dim3(kBThreads), st, a);
 }
 
 hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(2 * static_cast<int64_t>(a.batch) * a.H * a.nseg));
-    return dispatch(bwd_states_kernel, grid, dim3(kBThreads), st, a);
+    if (a.N == 64) return dispatch(bwd_states_kernel<64>, grid, dim3(kBThreads), st, a);
+    return dispatch(bwd_states_kernel<128>, grid, dim3(kBThreads), st, a);
 }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.nc * a.G));
-    return dispatch(bwd_chunk_kernel, grid, dim3(kBThreads), st, a);
+    if (a.N == 64) return dispatch(bwd_chunk_kernel<64>, grid, dim3(kBThreads), st, a);
+    return dispatch(bwd_chunk_kernel<128>, grid, dim3(kBThreads), st, a);
 }
 
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st) {

@@ -137,6 +137,7 @@ struct BwdArgs {
     int nseg, cps;
     int64_t L;
     int batch, H, G, nc;
+    int N;                  // state size: 128 or 64
 };
 
 // Mixer steps beside the scan (ssd_mixer.hip).

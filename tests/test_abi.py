@@ -338,6 +338,8 @@ def test_bwd_workspace_bytes(lib):
     assert ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 64) == ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 128)
     assert ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 256) == ssd.bwd_workspace_bytes(1, 8192, H, 64, 128, G, 128)
     assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 32) == 0   # not a compiled chunk
+    assert ssd.bwd_workspace_bytes(1, 128, H, 64, 64, G, 64) > 0     # N 64
+    assert ssd.bwd_workspace_bytes(1, 128, H, 64, 32, G, 64) == 0    # N 32: not built
     assert ssd.bwd_workspace_bytes(1, 128, H, 64, 128, G, 128, io=ssd.F32) == 0   # fp32: not built
 
 
@@ -358,7 +360,7 @@ def _bwd_call(lib, dims=(1, 256, 4, 64, 128, 1, 128), io=ssd.BF16, **over):
 
 def test_bwd_rejects_bad_arguments(lib):
     assert _bwd_call(lib, io=ssd.F32) == UNSUPPORTED
-    assert _bwd_call(lib, dims=(1, 256, 4, 64, 64, 1, 128)) == UNSUPPORTED
+    assert _bwd_call(lib, dims=(1, 256, 4, 64, 32, 1, 128)) == UNSUPPORTED
     assert _bwd_call(lib, dims=(1, 256, 4, 64, 128, 1, 32)) == UNSUPPORTED
     assert _bwd_call(lib, dims=(1, 256, 6, 64, 128, 4, 128)) == BAD_SHAPE   # H % G
     assert _bwd_call(lib, dy=None) == NULL_ARG

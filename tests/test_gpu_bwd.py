@@ -23,12 +23,13 @@ NAMES = {"dx": "dx", "ddt": "ddt_raw", "dA": "dA", "dB": "dB", "dC": "dC", "dD":
          "ddt_bias": "ddt_bias", "d_initial_states": "dh_init"}
 
 
-def _problem(seed, b, L, H, G, *, init=False, seq=None, dfinal=False, no_D=False, no_bias=False):
+def _problem(seed, b, L, H, G, *, init=False, seq=None, dfinal=False, no_D=False, no_bias=False,
+             n=N):
     rng = np.random.default_rng(seed)
-    p = workloads.random_problem(rng, b, L, H, P, N, G, io="bf16", init=init)
+    p = workloads.random_problem(rng, b, L, H, P, n, G, io="bf16", init=init)
     p["seq_idx"] = seq
     p["dy"] = workloads.round_bf16(rng.standard_normal((b, L, H, P), dtype=np.float32))
-    p["dfinal"] = (rng.standard_normal((b, H, P, N)).astype(np.float32) if dfinal else None)
+    p["dfinal"] = (rng.standard_normal((b, H, P, n)).astype(np.float32) if dfinal else None)
     if no_D:
         p["D"] = None
     if no_bias:
@@ -145,6 +146,28 @@ def test_bwd_rejects_unsupported():
         ssd.chunk_scan_bwd(to_dev(p["x"], bf), to_dev(p["dt_raw"]), to_dev(p["A"]),
                            to_dev(p["B"], bf), to_dev(p["C"], bf), to_dev(p["dy"], bf),
                            chunk_size=32)
+
+
+@pytest.mark.parametrize("Q", [64, 128])
+def test_bwd_state_size_64(Q):
+    """State size N = 64 (with P = 64, chunk 64: the JAX page's Configuration
+    defaults), on a ragged length with an initial state, a final-state
+    gradient and packed sequences, against the oracle."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    b, L, H, G = 2, 700, 4, 2
+    seq = np.zeros((b, L), dtype=np.int32)
+    seq[:, 300:] = 1
+    seq[1, 517:] = 2
+    p = _problem(29, b, L, H, G, init=True, dfinal=True, seq=seq, n=64)
+    bf = torch.bfloat16
+    t = lambda k, dtype=None: to_dev(p[k], dtype)
+    g = ssd.chunk_scan_bwd(t("x", bf), t("dt_raw"), t("A"), t("B", bf), t("C", bf), t("dy", bf),
+                           chunk_size=Q, D=t("D"), dt_bias=t("dt_bias"), initial_states=t("h_init"),
+                           seq_idx=t("seq_idx"), d_final_states=t("dfinal"))
+    torch.cuda.synchronize()
+    got = {k: (None if v is None else v.float().cpu().numpy()) for k, v in g.items()}
+    _compare(got, _reference(p), p)
 
 
 @pytest.mark.parametrize("Q", [64, 256])
