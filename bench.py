@@ -527,7 +527,8 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
         A.data_ptr(), eB.data_ptr(), eC.data_ptr(), D.data_ptr(), ecache.data_ptr(),
         ech[0].data_ptr(), ech[1].data_ptr(), ech[2].data_ptr(), ech[3].data_ptr(), eslots,
         eidx.data_ptr(), eposd.data_ptr(), ey.data_ptr(), ews.data_ptr(), eneed, stream())
-    enames = ["stage", "chunk_prep", "chunk_output"]
+    # the output kernel in two passes: rows whose chunk does not complete, then the others
+    enames = ["stage", "chunk_prep", "chunk_output", "chunk_output_commit"]
     eus, ewall = timed(emu, len(enames), max(steps // 2, 10))
     res["strict_decode"] = {"rows": er, "slots": eslots, "offset_in_chunk": epos,
                             "kernels_us": {n: round(u, 2) for n, u in zip(enames, eus)},

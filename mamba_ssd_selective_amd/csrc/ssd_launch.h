@@ -40,6 +40,9 @@ struct ScanArgs {
     // its final state only when it holds a whole chunk (len = L), so that its
     // slot's state moves on at chunk ends only.  Single-segment calls only.
     void* y_last;
+    // decode output on the transposing-read kernels: 0 = all rows in one
+    // launch; 1 = the rows whose chunk does not complete; 2 = the others
+    int dec_pass;
     // 1: every chunk takes the per-element exp(cs_i - cs_j) form of the
     // intra-chunk decay (no factoring), so that a token's output does not
     // depend on the tokens after it in its chunk (the strict mode)

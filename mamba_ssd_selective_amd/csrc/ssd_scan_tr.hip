@@ -41,14 +41,20 @@ namespace {
 // 12: waves 0-7 own one output row block each, waves 8-11 two state n-blocks
 // each, so that the state chain and the output products of a chunk proceed on
 // different waves of each SIMD (three waves per SIMD).
-// The decode-output form (kDec: rows of one chunk, one output row block per
-// row) runs 5: wave 0 computes the row block of the row's last token, waves
-// 1-4 own two state n-blocks each; with single buffers its LDS and waves
-// leave room for two workgroups per CU.
+// Decode-output forms (kDec: rows of one chunk, one output row block per
+// row, single buffers):
+//  kDec = 1: 5 waves.  Wave 0 computes the row block of the row's last token,
+//            waves 1-4 own two state n-blocks each (the chunk's state update,
+//            when the chunk completes); 70 KB of LDS, two workgroups per CU.
+//  kDec = 2: 1 wave, the output wave alone, for rows whose chunk does not
+//            complete: it reads the chunk-start state straight into the bf16
+//            operand registers of the carried-state term (the values the
+//            state waves would have written to LDS) and needs no B tile, so
+//            up to eight workgroups share a CU.
 constexpr int kTrWaves = 8;
-template <bool kOut, bool kDec = false>
+template <bool kOut, int kDec = 0>
 struct TrWaves {
-    static constexpr int W = kDec ? 5 : (kOut ? 12 : 8);
+    static constexpr int W = kDec == 2 ? 1 : (kDec ? 5 : (kOut ? 12 : 8));
     static constexpr int kThreads = W * kWave;
     static constexpr int NBW = kOut ? 2 : 1;  // state n-blocks per state wave
     static constexpr int first_state = kDec ? 1 : (kOut ? 8 : 0);
@@ -128,7 +134,7 @@ __device__ __forceinline__ int tr_row_block(int wave) {
     else return wave;
 }
 
-template <int P, int N, int Q, bool kOut, bool kSeq, bool kDec = false>
+template <int P, int N, int Q, bool kOut, bool kSeq, int kDec = 0>
 struct TrScan {
     using G_ = TrGeo<P, N, Q>;
     static constexpr int W = TrWaves<kOut, kDec>::W;
@@ -188,6 +194,8 @@ struct TrScan {
     f32x4_t h[NBW][G_::PB];     // state rows n = 16 (nb + t) + 4g + r, column p = 16pb + r16
     uint4 cr[G_::KN];           // C rows of a chunk (k over n), loaded a chunk ahead
     uint4 cb[G_::NCB];          // C.B^T tile pairs of a chunk, loaded a chunk ahead
+    // kDec = 2: the state operand of the carried-state term, fragment (s, pb)
+    uint4 hreg[kDec == 2 ? G_::KN : 1][G_::PB];
 
     __device__ __forceinline__ TrScan(const ScanArgs& args) : a(args) {}
 
@@ -262,8 +270,27 @@ struct TrScan {
     }
     __device__ __forceinline__ void dma_all(char* sX, char* sB, TrMeta<Q>* sM, int c) const {
         dma_x(sX, c);
-        dma_b(sB, c, 0, BI);
+        if constexpr (kDec != 2) dma_b(sB, c, 0, BI);  // the one-wave form has no state update
         dma_meta(sM, c);
+    }
+
+    // kDec = 2: the chunk-start state, row p = 16 pb + r16, n = 32 s + 8 g .. +7,
+    // as the bf16 pairs the state waves' operand copy holds
+    __device__ __forceinline__ void load_state_operand(const float* __restrict__ src) {
+#pragma unroll
+        for (int s = 0; s < G_::KN; ++s)
+#pragma unroll
+            for (int pb = 0; pb < G_::PB; ++pb) {
+                if (src) {
+                    const float* q = src + (16 * pb + r16) * N + 32 * s + 8 * g;
+                    const float4 v0 = *reinterpret_cast<const float4*>(q);
+                    const float4 v1 = *reinterpret_cast<const float4*>(q + 4);
+                    hreg[s][pb] = make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
+                                             pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w));
+                } else {
+                    hreg[s][pb] = make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
     }
 
     // Factors of the G^T fragment of k step u (tiles J = 2u, 2u+1; element e
@@ -528,8 +555,10 @@ struct TrScan {
         for (int s = 0; s < G_::KN; ++s) {
             Frag<uint16_t> hf[G_::PB];
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb)
-                hf[pb] = frag_of(lds_ld<uint4>(H, (ha[K] ^ (s << 6)) + 16 * pb * G_::HROW));
+            for (int pb = 0; pb < G_::PB; ++pb) {
+                if constexpr (kDec == 2) hf[pb] = frag_of(hreg[s][pb]);
+                else hf[pb] = frag_of(lds_ld<uint4>(H, (ha[K] ^ (s << 6)) + 16 * pb * G_::HROW));
+            }
             __builtin_amdgcn_sched_barrier(0);
             const Frag<uint16_t> cf = frag_of(cr[s]);
 #pragma unroll
@@ -808,7 +837,7 @@ struct TrLds {
 };
 
 // One (row, head, segment) from set-up to the final stores.
-template <int P, int N, int Q, bool kOut, bool kSeq, bool kDec>
+template <int P, int N, int Q, bool kOut, bool kSeq, int kDec>
 __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s) {
     using G_ = TrGeo<P, N, Q>;
     using S_ = TrScan<P, N, Q, kOut, kSeq, kDec>;
@@ -828,6 +857,13 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     // no chunks when the row ends before this segment
     k.c_end = min(k.c_begin + a.cps, static_cast<int>((rs.len + Q - 1) / Q));
     const bool any = k.c_begin < k.c_end;
+    // decode output in two passes: the one-wave form takes the rows whose
+    // chunk does not complete, the five-wave form those whose chunk does
+    if constexpr (kDec == 2) {
+        if (!any || rs.len == a.L) return;
+    } else if constexpr (kDec == 1) {
+        if (a.dec_pass == 2 && rs.len != a.L) return;
+    }
     // (decode output: a slot's state moves on at chunk ends only)
     k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr && rs.live &&
                    (a.y_last == nullptr || rs.len == a.L);
@@ -900,6 +936,8 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
             k.load_cb(k.c_begin);
             k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
         }
+        if constexpr (kDec == 2)
+            k.load_state_operand(a.init && rs.live ? a.init + (rs.state * a.H + it.h) * P * N : nullptr);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         for (int c = k.c_begin; c < k.c_end; c += 2) {
@@ -950,17 +988,17 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
 //                 states from the last segment.
 // kDec: the decode-output form (one chunk per row, so the second buffers are
 // never used and take no LDS; one column-factor row).
-template <int P, int N, int Q, bool kOut, bool kSeq, bool kDec>
+template <int P, int N, int Q, bool kOut, bool kSeq, int kDec>
 __global__ __launch_bounds__((TrWaves<kOut, kDec>::kThreads)) void scan_tr_kernel(ScanArgs a) {
     using G_ = TrGeo<P, N, Q>;
     constexpr int kSecond = kDec ? 16 : 1;  // bytes of a second buffer: all, or a stub
     __shared__ __attribute__((aligned(1024))) char sX0[G_::XBYTES];
     __shared__ __attribute__((aligned(1024))) char sX1[kDec ? kSecond : G_::XBYTES];
-    __shared__ __attribute__((aligned(1024))) char sB0[G_::BBYTES];
+    __shared__ __attribute__((aligned(1024))) char sB0[kDec == 2 ? 16 : G_::BBYTES];
     __shared__ __attribute__((aligned(1024))) char sB1[kDec ? kSecond : G_::BBYTES];
     __shared__ __attribute__((aligned(16))) TrMeta<Q> sM0;
     __shared__ __attribute__((aligned(16))) char sM1[kDec ? kSecond : sizeof(TrMeta<Q>)];
-    __shared__ __attribute__((aligned(1024))) char sH0[kOut ? G_::HBYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sH0[kOut && kDec != 2 ? G_::HBYTES : 16];
     __shared__ __attribute__((aligned(1024))) char sH1[kOut && !kDec ? G_::HBYTES : 16];
     __shared__ __attribute__((aligned(16))) float sCj[kDec ? Q : (kOut ? kTrWaves * Q : 4)];
     const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1},
@@ -973,14 +1011,20 @@ template <int P, int N, int Q, bool kOut>
 hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(nblocks));
     if constexpr (kOut) {
-        // decode output (rows of one chunk, no seq_idx): the 5-wave form
-        if (a.y_last && !a.seq_idx)
-            return dispatch(scan_tr_kernel<P, N, Q, true, false, true>, grid,
-                            dim3(TrWaves<true, true>::kThreads), st, a);
+        // decode output (rows of one chunk, no seq_idx): pass 1, rows whose
+        // chunk does not complete, on the one-wave form; pass 2 (or all rows,
+        // dec_pass 0), the five-wave form
+        if (a.y_last && !a.seq_idx) {
+            if (a.dec_pass == 1)
+                return dispatch(scan_tr_kernel<P, N, Q, true, false, 2>, grid,
+                                dim3(TrWaves<true, 2>::kThreads), st, a);
+            return dispatch(scan_tr_kernel<P, N, Q, true, false, 1>, grid,
+                            dim3(TrWaves<true, 1>::kThreads), st, a);
+        }
     }
     const dim3 block(TrWaves<kOut>::kThreads);
-    if (a.seq_idx) return dispatch(scan_tr_kernel<P, N, Q, kOut, true, false>, grid, block, st, a);
-    return dispatch(scan_tr_kernel<P, N, Q, kOut, false, false>, grid, block, st, a);
+    if (a.seq_idx) return dispatch(scan_tr_kernel<P, N, Q, kOut, true, 0>, grid, block, st, a);
+    return dispatch(scan_tr_kernel<P, N, Q, kOut, false, 0>, grid, block, st, a);
 }
 
 }  // namespace
