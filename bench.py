@@ -410,16 +410,21 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
             if fn() != 0:
                 raise RuntimeError("cache call failed")
         torch.cuda.synchronize()
+        # wall time per call, back to back, with no events between the dispatches
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n
+        # each dispatch's duration from events bound to it
         evs = hip.events(2 * nk * n)
         launched = ctypes.c_int(0)
-        t0 = time.perf_counter()
         for i in range(n):
             lib.ssd_set_timing_events(ev_slice_of(evs, 2 * nk * i, 2 * nk, vp), 2 * nk,
                                       ctypes.byref(launched))
             fn()
         lib.ssd_set_timing_events(None, 0, None)
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / n
         if launched.value != nk:
             raise RuntimeError("expected %d dispatches, got %d" % (nk, launched.value))
         us = [1e3 * float(np.mean([hip.elapsed_ms(evs[2 * (nk * i + k)], evs[2 * (nk * i + k) + 1])
@@ -528,13 +533,23 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
         ech[0].data_ptr(), ech[1].data_ptr(), ech[2].data_ptr(), ech[3].data_ptr(), eslots,
         eidx.data_ptr(), eposd.data_ptr(), ey.data_ptr(), ews.data_ptr(), eneed, stream())
     # the output kernel in two passes: rows whose chunk does not complete, then the others
-    enames = ["stage", "chunk_prep", "chunk_output", "chunk_output_commit"]
+    enames = ["chunk_prep", "chunk_output", "chunk_output_commit"]
     eus, ewall = timed(emu, len(enames), max(steps // 2, 10))
     res["strict_decode"] = {"rows": er, "slots": eslots, "offset_in_chunk": epos,
                             "kernels_us": {n: round(u, 2) for n, u in zip(enames, eus)},
                             "kernels_total_us": round(sum(eus), 2),
                             "ms_per_call": round(1e3 * ewall, 4),
                             "tokens_per_s": round(er / ewall, 1)}
+    # the step at the end of every row's chunk (offset Q - 1): every row also
+    # replaces its slot's chunk-start state (the repeated calls rewrite the
+    # same slots from the states they left; the work per call is the same)
+    eposd.fill_(Q - 1)
+    cus, cwall = timed(emu, len(enames), max(steps // 2, 10))
+    res["strict_decode_chunk_end"] = {"rows": er, "slots": eslots, "offset_in_chunk": Q - 1,
+                                      "kernels_us": {n: round(u, 2) for n, u in zip(enames, cus)},
+                                      "kernels_total_us": round(sum(cus), 2),
+                                      "ms_per_call": round(1e3 * cwall, 4),
+                                      "tokens_per_s": round(er / cwall, 1)}
     res["cpu_baseline"] = None
     if cpu_seconds > 0:
         import oracle

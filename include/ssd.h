@@ -241,9 +241,11 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
  * 16-byte aligned) and computes only the 16-token row block that holds the
  * new token (the chunk's state only when it completes).  The workspace
  * (ssd_decode_emulated_workspace_bytes, 256-byte aligned) holds the chunk's
- * scan data and the rows' lengths.  This is the strict decode, not the fast
- * one (ssd_state_update).  Dispatch order: the new tokens' copy into their
- * slots, then the scan's kernels (chunk_prep, chunk_output).
+ * scan data.  This is the strict decode, not the fast one (ssd_state_update).
+ * Dispatch order: chunk_prep (which also copies the new tokens into their
+ * slots' chunk buffers), chunk_output for the rows whose chunk does not
+ * complete, chunk_output for the others (a launch of at most as many
+ * workgroups as the device runs at once, each taking several rows' heads).
  */
 size_t ssd_decode_emulated_workspace_bytes(const ssd_dims* d, ssd_dtype io);
 ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,

@@ -8,8 +8,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_scan_tr.hip", "ssd_bwd.hip", "ssd_mixer.hip",
-           "ssd_strict.hip"]
+SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_scan_tr.hip", "ssd_bwd.hip", "ssd_mixer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -318,6 +318,12 @@ struct RowLayout {
     const int32_t* slot = nullptr;
     int64_t slots = 0;
     void* y_last = nullptr;
+    // emulated decode: new-token offsets and arrays (ScanArgs::pos, tok_*)
+    const int32_t* pos = nullptr;
+    const void* tok_x = nullptr;
+    const float* tok_dt = nullptr;
+    const void* tok_B = nullptr;
+    const void* tok_C = nullptr;
 };
 
 // The forward scan over rows laid out as `rl` says.  k counts the dispatches
@@ -411,6 +417,11 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     sa.slot = rl.slot;
     sa.slots = rl.slots;
     sa.y_last = rl.y_last;
+    sa.pos = rl.pos;
+    sa.tok_x = rl.tok_x;
+    sa.tok_dt = rl.tok_dt;
+    sa.tok_B = rl.tok_B;
+    sa.tok_C = rl.tok_C;
     sa.exact_decay = one_segment ? 1 : 0;
     sa.D = D;
     sa.init = initial_states;
@@ -647,17 +658,23 @@ ssd_status ssd_chunk_scan_fwd_cached(const ssd_dims* d, ssd_dtype io, const void
 
 namespace {
 
-// Workspace of the chunk-emulating decode: the scan's (rows of one chunk,
-// strict), then the rows' lengths.
-struct EmulPlan {
-    size_t rl = 0, total = 0;
-};
-
-EmulPlan make_emul_plan(const ssd_dims& d, ssd_dtype io) {
-    EmulPlan e;
-    e.rl = align_up(make_plan(d, io, true).total);
-    e.total = align_up(e.rl + static_cast<size_t>(d.batch) * 4);
-    return e;
+// Chunk-emulating decode (RL-Kernel RFC "Nemotron-3-Nano-30B-A3B", section
+// 1, operator family 1, and section 3, Figure 2, box [F2]: the SSD scan runs
+// train, prefill and decode with one arithmetic, so that how a sequence is
+// split into prefill and decode steps does not change a bit of its outputs).
+// A decode token at offset i of its chunk is not folded into a running state.
+// Each slot keeps the state at its current chunk's start and that chunk's
+// tokens so far.  A step runs the strict chunked scan on the slots in place,
+// each row of length i + 1, in its decode-output form: chunk_prep takes the
+// new token from the inputs and appends it to the slot's chunk buffers, and
+// the output kernels compute only the row block of offset i and store only
+// y at offset i, the value the chunked prefill computes for that token.  When
+// the chunk is complete (i = Q - 1) the scan's state at its end replaces the
+// slot's chunk-start state.
+//
+// Its workspace: the scan's (rows of one chunk, strict).
+size_t emul_workspace(const ssd_dims& d, ssd_dtype io) {
+    return align_up(make_plan(d, io, true).total);
 }
 
 ssd_status check_emul_dims(const ssd_dims* d, ssd_dtype io) {
@@ -667,7 +684,6 @@ ssd_status check_emul_dims(const ssd_dims* d, ssd_dtype io) {
     const int64_t es = static_cast<int64_t>(io_size(io));
     if ((d->nheads * d->headdim * es) % 4 != 0 || (d->ngroups * d->dstate * es) % 4 != 0)
         return SSD_ERR_UNSUPPORTED;
-    if (d->batch > 65535) return SSD_ERR_BAD_SHAPE;
     return SSD_OK;
 }
 
@@ -677,7 +693,7 @@ extern "C" {
 
 size_t ssd_decode_emulated_workspace_bytes(const ssd_dims* d, ssd_dtype io) {
     if (check_emul_dims(d, io) != SSD_OK || d->batch == 0) return 0;
-    return make_emul_plan(*d, io).total;
+    return emul_workspace(*d, io);
 }
 
 ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, const float* dt,
@@ -703,8 +719,8 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
     const void* word_bufs[] = {x, dt, B, C, y, x_chunks, dt_chunks, b_chunks, c_chunks};
     for (const void* p : word_bufs)
         if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return SSD_ERR_BAD_ARG;
-    const EmulPlan e = make_emul_plan(*d, io);
-    if (!workspace || workspace_bytes < e.total ||
+    const size_t ws_need = emul_workspace(*d, io);
+    if (!workspace || workspace_bytes < ws_need ||
         (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return SSD_ERR_WORKSPACE;
     const size_t es = io_size(io);
@@ -718,7 +734,7 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
                            span(C, b * G * N * es), span(A, H * 4),
                            span(dt_bias, dt_bias ? H * 4 : 0), span(D, D ? H * 4 : 0),
                            span(state_indices, b * 4), span(positions, b * 4),
-                           span(y, b * H * P * es), span(workspace, e.total)};
+                           span(y, b * H * P * es), span(workspace, ws_need)};
     for (size_t i = 0; i < 5; ++i) {
         for (const Span& o : others)
             if (overlap(caches[i], o)) return SSD_ERR_ALIAS;
@@ -729,56 +745,29 @@ ssd_status ssd_decode_emulated(const ssd_dims* d, ssd_dtype io, const void* x, c
     const Span ins[] = {span(x, b * H * P * es), span(dt, b * H * 4), span(B, b * G * N * es),
                         span(C, b * G * N * es), span(A, H * 4), span(dt_bias, dt_bias ? H * 4 : 0),
                         span(D, D ? H * 4 : 0), span(state_indices, b * 4), span(positions, b * 4),
-                        span(workspace, e.total)};
+                        span(workspace, ws_need)};
     for (const Span& o : ins)
         if (overlap(ys, o)) return SSD_ERR_ALIAS;
 
-    char* wsb = static_cast<char*>(workspace);
-    ssd::EmulArgs ea{};
-    ea.x = x;
-    ea.dt = dt;
-    ea.B = B;
-    ea.C = C;
-    ea.x_buf = x_chunks;
-    ea.dt_buf = dt_chunks;
-    ea.b_buf = b_chunks;
-    ea.c_buf = c_chunks;
-    ea.state_idx = state_indices;
-    ea.pos = positions;
-    ea.cache_rows = cache_rows;
-    ea.row_len = reinterpret_cast<int32_t*>(wsb + e.rl);
-    ea.Q = static_cast<int>(Q);
-    ea.wx = H * P * static_cast<int64_t>(es) / 4;
-    ea.wd = H;
-    ea.wb = G * N * static_cast<int64_t>(es) / 4;
-    // the new tokens in 16-byte words when every width and buffer allows
-    const int64_t xb = H * P * static_cast<int64_t>(es), gb = G * N * static_cast<int64_t>(es);
-    const void* stage_bufs[] = {x, dt, B, C, x_chunks, dt_chunks, b_chunks, c_chunks};
-    bool wide = xb % 16 == 0 && gb % 16 == 0 && (H * 4) % 16 == 0;
-    for (const void* p : stage_bufs) wide = wide && aligned16(p);
-    if (wide) {
-        ea.wx = xb / 16;
-        ea.wd = H * 4 / 16;
-        ea.wb = gb / 16;
-    }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int k = 0;
     if (g_hooks.launched) *g_hooks.launched = 0;
     // the scan of each slot's chunk in place: its chunk buffers and its
     // chunk-start state, decode output (y of the new token; the slot's state
-    // replaced only when the chunk is complete)
+    // replaced only when the chunk is complete).  chunk_prep reads the new
+    // tokens from x, dt, B, C and appends them to the slots' chunk buffers.
     RowLayout rl;
-    rl.row_len = ea.row_len;
     rl.slot = state_indices;
     rl.slots = cache_rows;
     rl.y_last = y;
+    rl.pos = positions;
+    rl.tok_x = x;
+    rl.tok_dt = dt;
+    rl.tok_B = B;
+    rl.tok_C = C;
     return scan_fwd_impl(d, io, x_chunks, dt_chunks, dt_bias, dt_softplus, dt_min, dt_max, A,
                          b_chunks, c_chunks, D, state_cache, nullptr, rl, nullptr, state_cache,
-                         wsb, e.rl, hs, k, [&] {
-                             return timed_launch(k, hs, [&] {
-                                 return ssd::launch_emul_stage(ea, wide, b, hs);
-                             });
-                         }, true);
+                         workspace, ws_need, hs, k, [] { return hipSuccess; }, true);
 }
 
 size_t ssd_chunk_scan_varlen_workspace_bytes(const ssd_dims* d, ssd_dtype io) {

@@ -123,6 +123,11 @@ __device__ __forceinline__ void store4(T* p, const Vec4<T>& v) {
 __device__ __forceinline__ uint4 ld_raw16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
+// the same 16 bytes from a 4-byte aligned address
+__device__ __forceinline__ uint4 ld_words16(const void* p) {
+    const uint32_t* w = static_cast<const uint32_t*>(p);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
 __device__ __forceinline__ uint4 raw_keep(bool keep, const uint4& v) {
     return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }

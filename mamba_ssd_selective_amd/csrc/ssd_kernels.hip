@@ -111,6 +111,11 @@ struct StateRegs {
 //     B_{16J+4q+r}, r = 0..3, exactly the operand fragment the output kernel
 //     needs (k = j), so that kernel reads contiguous bytes per tile.
 // kTiles = false: step 1 only (the gradient kernels need the metadata alone).
+// Emulated decode (a.pos): the row's last token is read from the new-token
+// arrays, and the workgroup of its chunk copies the group's share of that
+// token (x and dt of its heads, its B and C rows) into the slot's chunk
+// buffers, where the output kernel reads it.  No workgroup of this launch
+// reads a token there that another one writes.
 template <typename T, int P, int N, int Q, bool kTiles>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     using C_ = Cfg<T, P, N, Q>;
@@ -133,6 +138,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     const int64_t r0 = rs.t0;
     const T* __restrict__ Bp = static_cast<const T*>(a.B);
     const T* __restrict__ Cp = static_cast<const T*>(a.C);
+    const bool emul = a.pos != nullptr;
+    // raw dt of head h at token t of the row
+    auto dt_at = [&](int64_t t, int h) {
+        return emul && t == tl ? a.tok_dt[b * a.H + h] : a.dt_raw[(r0 + t) * a.H + h];
+    };
 
     // ---- the sequence ids and the first head's dt first: loads return in
     // order, and the dt scan should not wait behind the B / C rows
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         for (int k = 0; k < E; ++k) {
             int64_t tt = t0 + lane * E + k;
             tt = tt < tl ? tt : tl;
-            raw0[k] = a.dt_raw[(r0 + tt) * a.H + h];
+            raw0[k] = dt_at(tt, h);
         }
     }
 
@@ -170,8 +180,29 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         n0 = n0 < N ? n0 : N - kV;
         int64_t t = t0 + j;
         t = t < tl ? t : tl;
-        rb[k] = ld_raw16(Bp + ((r0 + t) * a.G + g) * N + n0);
-        rc[k] = ld_raw16(Cp + ((r0 + t) * a.G + g) * N + n0);
+        if (emul && t == tl) {
+            const int64_t o = (b * a.G + g) * N + n0;
+            rb[k] = ld_words16(static_cast<const T*>(a.tok_B) + o);
+            rc[k] = ld_words16(static_cast<const T*>(a.tok_C) + o);
+        } else {
+            rb[k] = ld_raw16(Bp + ((r0 + t) * a.G + g) * N + n0);
+            rc[k] = ld_raw16(Cp + ((r0 + t) * a.G + g) * N + n0);
+        }
+    }
+    if (emul && tl < t0 + Q) {
+        // the new token into the slot's chunk buffers: this group's heads
+        // (x, dt) and its B / C rows
+        const int64_t dst = r0 + tl, h0 = static_cast<int64_t>(g) * hpg;
+        T* xd = const_cast<T*>(static_cast<const T*>(a.x)) + (dst * a.H + h0) * P;
+        const T* xs = static_cast<const T*>(a.tok_x) + (b * a.H + h0) * P;
+        for (int e = threadIdx.x; e < hpg * P; e += kThreads) xd[e] = xs[e];
+        float* dd = const_cast<float*>(a.dt_raw) + dst * a.H + h0;
+        for (int e = threadIdx.x; e < hpg; e += kThreads) dd[e] = a.tok_dt[b * a.H + h0 + e];
+        const int64_t gd = (dst * a.G + g) * N, gs = (b * a.G + g) * N;
+        for (int e = threadIdx.x; e < 2 * N; e += kThreads) {
+            if (e < N) const_cast<T*>(Bp)[gd + e] = static_cast<const T*>(a.tok_B)[gs + e];
+            else const_cast<T*>(Cp)[gd + e - N] = static_cast<const T*>(a.tok_C)[gs + e - N];
+        }
     }
 
     // ---- per-head chunk metadata
@@ -238,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         for (int k = 0; k < E; ++k) {
             int64_t tt = t0 + lane * E + k;
             tt = tt < tl ? tt : tl;
-            raw[k] = a.dt_raw[(r0 + tt) * a.H + g * hpg + hh];
+            raw[k] = dt_at(tt, g * hpg + hh);
         }
         head_meta(hh, raw);
     }

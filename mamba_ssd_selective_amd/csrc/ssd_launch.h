@@ -35,14 +35,28 @@ struct ScanArgs {
     // computed: nothing of it is read or written.  Single-segment calls only.
     const int32_t* slot;
     int64_t slots;
+    // emulated decode (slot rows only), or null.  pos (b): row b's length is
+    // pos[b] + 1 (0 when pos[b] is outside [0, L)), in place of row_len.  Its
+    // last token is the new one: chunk_prep reads it from tok_x (b, H, P),
+    // tok_dt (b, H), tok_B and tok_C (b, G, N) (4-byte aligned) and writes
+    // it into x, dt_raw, B and C (the slot's chunk buffers, writable here)
+    // for the kernels after it.
+    const int32_t* pos;
+    const void* tok_x;
+    const float* tok_dt;
+    const void* tok_B;
+    const void* tok_C;
     // (b, H, P) or null: decode output.  Only each row's last token (token
     // len - 1) is output, into y_last[b], and y is not written; a row writes
     // its final state only when it holds a whole chunk (len = L), so that its
     // slot's state moves on at chunk ends only.  Single-segment calls only.
     void* y_last;
-    // decode output on the transposing-read kernels: 0 = all rows in one
-    // launch; 1 = the rows whose chunk does not complete; 2 = the others
+    // decode output on the transposing-read kernels, in two launches: 1 = the
+    // rows whose chunk does not complete; 2 = the others, on a grid of fewer
+    // workgroups than work items (set by the launcher: dec_items work items,
+    // workgroup k takes items k, k + gridDim.x, ...)
     int dec_pass;
+    int64_t dec_items;
     // 1: every chunk takes the per-element exp(cs_i - cs_j) form of the
     // intra-chunk decay (no factoring), so that a token's output does not
     // depend on the tokens after it in its chunk (the strict mode)
@@ -265,25 +279,6 @@ hipError_t launch_state_pass(const PassArgs& a, int64_t bh, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, int64_t n, hipStream_t st);
 // Chunk-emulating decode: the copies around the scan (widths in 4-byte words:
 // wx = H*P*io/4, wd = H, wb = G*N*io/4; hpn = H*P*N).
-struct EmulArgs {
-    const void* x;            // (b, H, P) io: the new tokens
-    const float* dt;          // (b, H)
-    const void* B;            // (b, G, N) io
-    const void* C;            // (b, G, N) io
-    void* x_buf;              // (slots, Q, H, P) io: each slot's current chunk
-    float* dt_buf;            // (slots, Q, H)
-    void* b_buf;              // (slots, Q, G, N) io
-    void* c_buf;              // (slots, Q, G, N) io
-    const int32_t* state_idx; // (b) slot of each row
-    const int32_t* pos;       // (b) offset of the new token in its chunk
-    int64_t cache_rows;
-    int32_t* row_len;         // (b): tokens of the row's chunk so far (0: padding row)
-    int Q;
-    int64_t wx, wd, wb;
-};
-// wide: the stage copies 16-byte words (widths wx, wd, wb given in them)
-hipError_t launch_emul_stage(const EmulArgs& a, bool wide, int64_t b, hipStream_t st);
-
 // Cache slots <-> a (b, per_row) buffer: gather row r from slot idx[r] (zeros
 // for an index outside [0, rows) or when cache is null); scatter row r to slot
 // idx[r] (rows whose index is outside are skipped).  per_row % 4 == 0.

@@ -28,6 +28,8 @@
 //    element e >= 4 is token 32s + 16 + 4g + (e - 4).  The C.B^T tiles written
 //    by chunk_prep_kernel use the same token order.
 //  * k over n (state operand, C rows): element e is n = 32s + 8g + e.
+#include <atomic>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 #include "ssd_lds.h"
@@ -46,18 +48,19 @@ namespace {
 //  kDec = 1: 5 waves.  Wave 0 computes the row block of the row's last token,
 //            waves 1-4 own two state n-blocks each (the chunk's state update,
 //            when the chunk completes); 70 KB of LDS, two workgroups per CU.
-//  kDec = 2: 1 wave, the output wave alone, for rows whose chunk does not
-//            complete: it reads the chunk-start state straight into the bf16
-//            operand registers of the carried-state term (the values the
-//            state waves would have written to LDS) and needs no B tile, so
-//            up to eight workgroups share a CU.
+//  kDec = 2: 4 output waves, one 16-wide p block each, for rows whose chunk
+//            does not complete: each reads its rows of the chunk-start state
+//            straight into the bf16 operand registers of the carried-state
+//            term (the values the state waves would have written to LDS), and
+//            there is no B tile.  Every output element takes the same products
+//            in the same order as in the other forms.
 constexpr int kTrWaves = 8;
 template <bool kOut, int kDec = 0>
 struct TrWaves {
-    static constexpr int W = kDec == 2 ? 1 : (kDec ? 5 : (kOut ? 12 : 8));
+    static constexpr int W = kDec == 2 ? 4 : (kDec ? 5 : (kOut ? 12 : 8));
     static constexpr int kThreads = W * kWave;
     static constexpr int NBW = kOut ? 2 : 1;  // state n-blocks per state wave
-    static constexpr int first_state = kDec ? 1 : (kOut ? 8 : 0);
+    static constexpr int first_state = kDec == 2 ? W : (kDec ? 1 : (kOut ? 8 : 0));
 };
 template <int P, int N, int Q>
 struct TrGeo {
@@ -143,6 +146,9 @@ struct TrScan {
     static constexpr int NBI = G_::BBYTES / 1024;   // ... of a B tile
     static constexpr int XI = (NXI + W - 1) / W;    // per wave (the last round may be partial)
     static constexpr int BI = (NBI + W - 1) / W;
+    // p blocks of an output wave: all of them, or (kDec = 2) the wave's own
+    static constexpr int OPB = kDec == 2 ? 1 : G_::PB;
+    static_assert(kDec != 2 || W == G_::PB, "one p block per wave");
     static_assert(G_::XBYTES % 1024 == 0 && G_::BBYTES % 1024 == 0, "whole copy instructions");
     // A row block's intra-chunk decays are factored when the decay across its
     // 16 tokens is at most this (the column factors then stay below e^64).
@@ -158,6 +164,8 @@ struct TrScan {
     __device__ __forceinline__ bool ow() const { return kOut && out_wave_; }
     int I;                  // output row block of an output wave
     int nb;                 // first state n-block of a state wave (it owns NBW)
+    int pb0;                // kDec = 2: this wave's p block
+    __device__ __forceinline__ int pbase() const { return kDec == 2 ? pb0 : 0; }
     float Dh, Ah;           // D[h], A[h]
     int seq_prev;           // sequence id of the token before the current chunk
     float mult;             // decay of the segment (chunk-state kernel)
@@ -194,8 +202,8 @@ struct TrScan {
     f32x4_t h[NBW][G_::PB];     // state rows n = 16 (nb + t) + 4g + r, column p = 16pb + r16
     uint4 cr[G_::KN];           // C rows of a chunk (k over n), loaded a chunk ahead
     uint4 cb[G_::NCB];          // C.B^T tile pairs of a chunk, loaded a chunk ahead
-    // kDec = 2: the state operand of the carried-state term, fragment (s, pb)
-    uint4 hreg[kDec == 2 ? G_::KN : 1][G_::PB];
+    // kDec = 2: the state operand of the carried-state term, fragment (s, pb0)
+    uint4 hreg[kDec == 2 ? G_::KN : 1];
 
     __device__ __forceinline__ TrScan(const ScanArgs& args) : a(args) {}
 
@@ -274,23 +282,21 @@ struct TrScan {
         dma_meta(sM, c);
     }
 
-    // kDec = 2: the chunk-start state, row p = 16 pb + r16, n = 32 s + 8 g .. +7,
+    // kDec = 2: the chunk-start state, row p = 16 pb0 + r16, n = 32 s + 8 g .. +7,
     // as the bf16 pairs the state waves' operand copy holds
     __device__ __forceinline__ void load_state_operand(const float* __restrict__ src) {
 #pragma unroll
-        for (int s = 0; s < G_::KN; ++s)
-#pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) {
-                if (src) {
-                    const float* q = src + (16 * pb + r16) * N + 32 * s + 8 * g;
-                    const float4 v0 = *reinterpret_cast<const float4*>(q);
-                    const float4 v1 = *reinterpret_cast<const float4*>(q + 4);
-                    hreg[s][pb] = make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
-                                             pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w));
-                } else {
-                    hreg[s][pb] = make_uint4(0u, 0u, 0u, 0u);
-                }
+        for (int s = 0; s < G_::KN; ++s) {
+            if (src) {
+                const float* q = src + (16 * pb0 + r16) * N + 32 * s + 8 * g;
+                const float4 v0 = *reinterpret_cast<const float4*>(q);
+                const float4 v1 = *reinterpret_cast<const float4*>(q + 4);
+                hreg[s] = make_uint4(pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w),
+                                     pack_bf16x2(v1.x, v1.y), pack_bf16x2(v1.z, v1.w));
+            } else {
+                hreg[s] = make_uint4(0u, 0u, 0u, 0u);
             }
+        }
     }
 
     // Factors of the G^T fragment of k step u (tiles J = 2u, 2u+1; element e
@@ -412,7 +418,20 @@ struct TrScan {
     // of 16 rows.  y is not read again, so the stores are non-temporal.  All
     // lanes take part in the swap; only rows inside the sequence are stored.
     static constexpr int kYStores = G_::PB / 2;  // store instructions per row block
-    __device__ __forceinline__ void store_y(const f32x4_t (&y)[G_::PB], float fin, int c, int i, int valid) const {
+    __device__ __forceinline__ void store_y(const f32x4_t (&y)[OPB], float fin, int c, int i, int valid) const {
+        if constexpr (kDec == 2) {
+            // the row's last token: the lanes of column i = valid - 1 hold
+            // p = 16 pb0 + 4 g + r
+            if (i == valid - 1)
+                *reinterpret_cast<uint2*>(ylg + 16 * pb0 + 4 * g) =
+                    make_uint2(pack_bf16x2(y[0][0] * fin, y[0][1] * fin),
+                               pack_bf16x2(y[0][2] * fin, y[0][3] * fin));
+        } else {
+            store_rows(y, fin, c, i, valid);
+        }
+    }
+    __device__ __forceinline__ void store_rows(const f32x4_t (&y)[G_::PB], float fin, int c, int i,
+                                               int valid) const {
         static_assert(G_::PB == 4, "two swapped block pairs");
         typedef unsigned int u4 __attribute__((ext_vector_type(4)));
         uint32_t yw[G_::PB][2];
@@ -470,9 +489,10 @@ struct TrScan {
     // added to its rows with a select.  Rare: only where a sequence boundary
     // falls inside a 16-row block.
     template <int K>
-    __device__ __forceinline__ void span_passes(f32x4_t (&y)[G_::PB], int c, int valid, int i,
+    __device__ __forceinline__ void span_passes(f32x4_t (&y)[OPB], int c, int valid, int i,
                                                          int sd, float cs_i, int seq_i, int seq_m,
                                                          float dr) const {
+        static_assert(OPB == G_::PB, "packed sequences take forms with every p block per wave");
         const TrMeta<Q>* M = mo[K];
         const char* X = xo[K];
 #pragma unroll
@@ -548,21 +568,21 @@ struct TrScan {
         }
         // carried-state term y^T[p][i] = h . C_i, scaled below; each k step's
         // operand reads are issued before its products
-        f32x4_t y[G_::PB];
+        f32x4_t y[OPB];
 #pragma unroll
-        for (int pb = 0; pb < G_::PB; ++pb) y[pb] = acc_zero();
+        for (int q = 0; q < OPB; ++q) y[q] = acc_zero();
 #pragma unroll
         for (int s = 0; s < G_::KN; ++s) {
-            Frag<uint16_t> hf[G_::PB];
+            Frag<uint16_t> hf[OPB];
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) {
-                if constexpr (kDec == 2) hf[pb] = frag_of(hreg[s][pb]);
-                else hf[pb] = frag_of(lds_ld<uint4>(H, (ha[K] ^ (s << 6)) + 16 * pb * G_::HROW));
+            for (int q = 0; q < OPB; ++q) {
+                if constexpr (kDec == 2) hf[q] = frag_of(hreg[s]);
+                else hf[q] = frag_of(lds_ld<uint4>(H, (ha[K] ^ (s << 6)) + 16 * q * G_::HROW));
             }
             __builtin_amdgcn_sched_barrier(0);
             const Frag<uint16_t> cf = frag_of(cr[s]);
 #pragma unroll
-            for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], hf[pb], cf);
+            for (int q = 0; q < OPB; ++q) mma(y[q], hf[q], cf);
         }
         // column factors c_j = [seq_j = seq_m] exp(cs_m - cs_j) dt_j of the
         // tokens j < m0 + 16, and whether any of them has dt_j * A > 0
@@ -601,9 +621,9 @@ struct TrScan {
             if constexpr (kSeq) carry = seq_i == seq_prev;
         }
 #pragma unroll
-        for (int pb = 0; pb < G_::PB; ++pb)
+        for (int q = 0; q < OPB; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[pb][r] = carry ? y[pb][r] * sc : 0.0f;
+            for (int r = 0; r < 4; ++r) y[q][r] = carry ? y[q][r] * sc : 0.0f;
         if (has_next) load_c(c + 1);  // this chunk's C rows are consumed
 
         // intra-chunk outputs y^T += x^T G^T over the k steps up to the
@@ -615,10 +635,10 @@ struct TrScan {
 #pragma unroll
         for (int s = 0; s < G_::KQ; ++s) {
             if (s <= sd) {
-                Frag<uint16_t> xf[G_::PB];
+                Frag<uint16_t> xf[OPB];
                 float f[8];
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = tr_frag<G_::XROW>(X, xa[K] ^ (32 * pb), s);
+                for (int q = 0; q < OPB; ++q) xf[q] = tr_frag<G_::XROW>(X, xa[K] ^ (32 * (pbase() + q)), s);
                 if (wfast) {
                     const float4 c0 = lds_ld<float4>(cjo, cja + 128 * s);
                     const float4 c1 = lds_ld<float4>(cjo, cja + 128 * s + 64);
@@ -630,16 +650,18 @@ struct TrScan {
                 if (kSeq && mixed) {
                     const uint4 km = seq_keep_mask(M, ma[K], s, seq_m);
 #pragma unroll
-                    for (int pb = 0; pb < G_::PB; ++pb) xf[pb] = frag_and(xf[pb], km);
+                    for (int q = 0; q < OPB; ++q) xf[q] = frag_and(xf[q], km);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const Frag<uint16_t> gf = g_apply(cb[s], f, s == sd, dr, kSeq && mixed);
 #pragma unroll
-                for (int pb = 0; pb < G_::PB; ++pb) mma(y[pb], xf[pb], gf);
+                for (int q = 0; q < OPB; ++q) mma(y[q], xf[q], gf);
             }
             if (has_next) copies(s, c, Xn, Bn, Mn);
         }
-        if (kSeq && spanning) span_passes<K>(y, c, valid, i, sd, cs_i, seq_i, seq_m, dr);
+        if constexpr (kSeq) {
+            if (spanning) span_passes<K>(y, c, valid, i, sd, cs_i, seq_i, seq_m, dr);
+        }
         if (has_next) load_cb(c + 1);  // after the last use
         store_y(y, fin, c, i, valid);
         if constexpr (kSeq) seq_prev = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (Q - 1));
@@ -838,11 +860,11 @@ struct TrLds {
 
 // One (row, head, segment) from set-up to the final stores.
 template <int P, int N, int Q, bool kOut, bool kSeq, int kDec>
-__device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s) {
+__device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N, Q, kOut>& s, uint32_t widx) {
     using G_ = TrGeo<P, N, Q>;
     using S_ = TrScan<P, N, Q, kOut, kSeq, kDec>;
     S_ k(a);
-    const WorkItem it = decode_work(a, kOut ? a.nseg : a.nseg - 1);
+    const WorkItem it = decode_work_at(a, kOut ? a.nseg : a.nseg - 1, widx);
     k.wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     k.lane = static_cast<int>(threadIdx.x) % kWave;
     k.r16 = k.lane & 15;
@@ -857,17 +879,18 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     // no chunks when the row ends before this segment
     k.c_end = min(k.c_begin + a.cps, static_cast<int>((rs.len + Q - 1) / Q));
     const bool any = k.c_begin < k.c_end;
-    // decode output in two passes: the one-wave form takes the rows whose
+    // decode output in two passes: the four-wave form takes the rows whose
     // chunk does not complete, the five-wave form those whose chunk does
     if constexpr (kDec == 2) {
         if (!any || rs.len == a.L) return;
     } else if constexpr (kDec == 1) {
-        if (a.dec_pass == 2 && rs.len != a.L) return;
+        if (rs.len != a.L) return;
     }
     // (decode output: a slot's state moves on at chunk ends only)
     k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr && rs.live &&
                    (a.y_last == nullptr || rs.len == a.L);
-    k.out_wave_ = kDec ? k.wave == 0 : kOut && k.wave < G_::NB;
+    k.out_wave_ = kDec == 2 || (kDec ? k.wave == 0 : kOut && k.wave < G_::NB);
+    k.pb0 = kDec == 2 ? k.wave : 0;
     if constexpr (kDec) {
         // the row block of the row's last token (rows of one chunk)
         k.I = rs.len > 0 ? static_cast<int>((rs.len - 1) >> 4) : 0;
@@ -991,20 +1014,60 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
 template <int P, int N, int Q, bool kOut, bool kSeq, int kDec>
 __global__ __launch_bounds__((TrWaves<kOut, kDec>::kThreads)) void scan_tr_kernel(ScanArgs a) {
     using G_ = TrGeo<P, N, Q>;
-    constexpr int kSecond = kDec ? 16 : 1;  // bytes of a second buffer: all, or a stub
+    // sizes and alignments of the tiles, or of 16-byte stubs where a form has
+    // no such tile (kDec: no second buffers; kDec = 2: no B tile or state
+    // operand)
+    constexpr bool kB = kDec != 2, kX1 = !kDec, kH0 = kOut && kDec != 2, kH1 = kOut && !kDec;
     __shared__ __attribute__((aligned(1024))) char sX0[G_::XBYTES];
-    __shared__ __attribute__((aligned(1024))) char sX1[kDec ? kSecond : G_::XBYTES];
-    __shared__ __attribute__((aligned(1024))) char sB0[kDec == 2 ? 16 : G_::BBYTES];
-    __shared__ __attribute__((aligned(1024))) char sB1[kDec ? kSecond : G_::BBYTES];
+    __shared__ __attribute__((aligned(kX1 ? 1024 : 16))) char sX1[kX1 ? G_::XBYTES : 16];
+    __shared__ __attribute__((aligned(kB ? 1024 : 16))) char sB0[kB ? G_::BBYTES : 16];
+    __shared__ __attribute__((aligned(kX1 ? 1024 : 16))) char sB1[kX1 ? G_::BBYTES : 16];
     __shared__ __attribute__((aligned(16))) TrMeta<Q> sM0;
-    __shared__ __attribute__((aligned(16))) char sM1[kDec ? kSecond : sizeof(TrMeta<Q>)];
-    __shared__ __attribute__((aligned(1024))) char sH0[kOut && kDec != 2 ? G_::HBYTES : 16];
-    __shared__ __attribute__((aligned(1024))) char sH1[kOut && !kDec ? G_::HBYTES : 16];
-    __shared__ __attribute__((aligned(16))) float sCj[kDec ? Q : (kOut ? kTrWaves * Q : 4)];
+    __shared__ __attribute__((aligned(16))) char sM1[kX1 ? sizeof(TrMeta<Q>) : 16];
+    __shared__ __attribute__((aligned(kH0 ? 1024 : 16))) char sH0[kH0 ? G_::HBYTES : 16];
+    __shared__ __attribute__((aligned(kH1 ? 1024 : 16))) char sH1[kH1 ? G_::HBYTES : 16];
+    // column factors: one row per output wave
+    constexpr int kCj = kDec == 2 ? G_::PB * Q : (kDec ? Q : (kOut ? kTrWaves * Q : 4));
+    __shared__ __attribute__((aligned(16))) float sCj[kCj];
     const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1},
                                    {&sM0, reinterpret_cast<TrMeta<Q>*>(sM1)}, {sH0, sH1}, sCj};
 
-    scan_tr_run<P, N, Q, kOut, kSeq, kDec>(a, lds);
+    if constexpr (kDec == 1) {
+        // rows whose chunk completes, among this workgroup's work items
+        // blockIdx.x + k gridDim.x: every wave checks 64 of them at a time
+        // (one per lane) and the workgroup runs the ones that qualify
+        const uint32_t n = static_cast<uint32_t>(a.dec_items), step = gridDim.x;
+        const uint32_t lane = threadIdx.x % kWave;
+        for (uint32_t k0 = 0; blockIdx.x + k0 * step < n; k0 += kWave) {
+            const uint32_t w = blockIdx.x + (k0 + lane) * step;
+            const bool run = w < n && row_span(a, decode_work_at(a, a.nseg, w).b).len == a.L;
+            uint64_t m = __builtin_amdgcn_ballot_w64(run);
+            while (m != 0) {
+                const uint32_t j = static_cast<uint32_t>(__builtin_ctzll(m));
+                m &= m - 1;
+                scan_tr_run<P, N, Q, kOut, kSeq, kDec>(a, lds, blockIdx.x + (k0 + j) * step);
+                __syncthreads();  // the next item's copies overwrite the tiles
+            }
+        }
+    } else {
+        scan_tr_run<P, N, Q, kOut, kSeq, kDec>(
+            a, lds, static_cast<uint32_t>(xcd_work_index(blockIdx.x, gridDim.x)));
+    }
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cus[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 1;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            return 1;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 template <int P, int N, int Q, bool kOut>
@@ -1012,14 +1075,28 @@ hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(nblocks));
     if constexpr (kOut) {
         // decode output (rows of one chunk, no seq_idx): pass 1, rows whose
-        // chunk does not complete, on the one-wave form; pass 2 (or all rows,
-        // dec_pass 0), the five-wave form
+        // chunk does not complete, on the four-wave form; pass 2, the others,
+        // on the five-wave form, with as many workgroups as the device holds
+        // at once (an empty pass then costs one round of them)
         if (a.y_last && !a.seq_idx) {
             if (a.dec_pass == 1)
                 return dispatch(scan_tr_kernel<P, N, Q, true, false, 2>, grid,
                                 dim3(TrWaves<true, 2>::kThreads), st, a);
-            return dispatch(scan_tr_kernel<P, N, Q, true, false, 1>, grid,
-                            dim3(TrWaves<true, 1>::kThreads), st, a);
+            if (a.dec_pass != 2) return hipErrorInvalidValue;
+            constexpr int kThreads = TrWaves<true, 1>::kThreads;
+            static const int per_cu = [] {
+                int n = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n, scan_tr_kernel<P, N, Q, true, false, 1>, kThreads, 0) != hipSuccess)
+                    n = 1;
+                return n < 1 ? 1 : n;
+            }();
+            ScanArgs c = a;
+            c.dec_items = nblocks;
+            const int64_t cap = static_cast<int64_t>(per_cu) * device_cus();
+            return dispatch(scan_tr_kernel<P, N, Q, true, false, 1>,
+                            dim3(static_cast<unsigned>(nblocks < cap ? nblocks : cap)),
+                            dim3(kThreads), st, c);
         }
     }
     const dim3 block(TrWaves<kOut>::kThreads);

@@ -21,10 +21,9 @@ struct WorkItem {
     int seg, h, g;
 };
 
-// Work order (fastest first): head within its group, group, segment, row.
-// Grids stay below 2^31 workgroups, so the index arithmetic is 32-bit.
-__device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
-    uint32_t w = static_cast<uint32_t>(xcd_work_index(blockIdx.x, gridDim.x));
+// Work item w in the order (fastest first): head within its group, group,
+// segment, row.  Work counts stay below 2^31, so the arithmetic is 32-bit.
+__device__ __forceinline__ WorkItem decode_work_at(const ScanArgs& a, int nseg_grid, uint32_t w) {
     const uint32_t hpg = static_cast<uint32_t>(a.H / a.G);
     WorkItem it;
     const int hh = static_cast<int>(w % hpg);
@@ -35,6 +34,10 @@ __device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid
     it.b = static_cast<int64_t>(w / static_cast<uint32_t>(nseg_grid));
     it.h = it.g * static_cast<int>(hpg) + hh;
     return it;
+}
+// The work item of this workgroup (one per workgroup, XCD-aware order).
+__device__ __forceinline__ WorkItem decode_work(const ScanArgs& a, int nseg_grid) {
+    return decode_work_at(a, nseg_grid, static_cast<uint32_t>(xcd_work_index(blockIdx.x, gridDim.x)));
 }
 
 // The tokens of row b: the first one's index in x, dt, B, C, y and seq_idx
@@ -59,7 +62,10 @@ __device__ __forceinline__ RowSpan row_span(const ScanArgs& a, int64_t b) {
         r.len = 0;
         if (r.live) {
             r.len = a.L;
-            if (a.row_len) {
+            if (a.pos) {
+                const int64_t i = a.pos[b];
+                r.len = i >= 0 && i < a.L ? i + 1 : 0;
+            } else if (a.row_len) {
                 const int64_t rl = a.row_len[b];
                 r.len = rl < 0 ? 0 : (rl < a.L ? rl : a.L);
             }

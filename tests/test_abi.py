@@ -248,10 +248,10 @@ def test_cached_prefill_workspace_and_rejections(lib):
 def test_emulated_decode_workspace_and_rejections(lib):
     d = (4, 128, 64, 64, 128, 8, 128)
     need = ssd.library().ssd_decode_emulated_workspace_bytes(ctypes.byref(ssd._Dims(*d)), ssd.BF16)
-    # the one-chunk scan's workspace, then the row lengths (the slots are read in place)
+    # the one-chunk scan's workspace (the slots and new tokens are read in place)
     scan = ssd.workspace_bytes(*d)
     al = lambda v: (v + 255) // 256 * 256
-    assert need == al(scan) + al(4 * 4)
+    assert need == al(scan)
     buf = _Buf()
 
     def call(dims=d, rows=8, **over):
