@@ -10,10 +10,13 @@ import pytest
 
 import oracle
 import workloads
+from gpu_util import tol
 
 pytestmark = pytest.mark.gpu
 
 H, P, N, G, Q = 64, 64, 128, 8, 128
+# the shape of the tests below unless one says otherwise
+SH = dict(H=H, P=P, N=N, G=G, Q=Q, io="bf16")
 
 
 def _dev(a, dtype=None):
@@ -26,37 +29,43 @@ def _host(t):
     return t.float().cpu().numpy()
 
 
+def _io(sh):
+    import torch
+    return torch.bfloat16 if sh["io"] == "bf16" else torch.float32
+
+
 class _Slots:
-    def __init__(self, rows):
+    def __init__(self, rows, sh=SH):
         import torch
-        dev, bf = torch.device("cuda:0"), torch.bfloat16
-        self.state = torch.zeros((rows, H, P, N), dtype=torch.float32, device=dev)
-        self.chunks = (torch.zeros((rows, Q, H, P), dtype=bf, device=dev),
-                       torch.zeros((rows, Q, H), dtype=torch.float32, device=dev),
-                       torch.zeros((rows, Q, G, N), dtype=bf, device=dev),
-                       torch.zeros((rows, Q, G, N), dtype=bf, device=dev))
+        dev, io = torch.device("cuda:0"), _io(sh)
+        h, p, n, g, q = sh["H"], sh["P"], sh["N"], sh["G"], sh["Q"]
+        self.state = torch.zeros((rows, h, p, n), dtype=torch.float32, device=dev)
+        self.chunks = (torch.zeros((rows, q, h, p), dtype=io, device=dev),
+                       torch.zeros((rows, q, h), dtype=torch.float32, device=dev),
+                       torch.zeros((rows, q, g, n), dtype=io, device=dev),
+                       torch.zeros((rows, q, g, n), dtype=io, device=dev))
 
 
-def _full_prefill(p, L):
+def _full_prefill(p, L, sh=SH):
     """The strict prefill of every row's first L tokens: (y, final states)."""
     b = p["x"].shape[0]
-    s = _Slots(b)
-    y = _cached(p, list(range(b)), L, s, list(range(b)), True)
+    s = _Slots(b, sh)
+    y = _cached(p, list(range(b)), L, s, list(range(b)), True, sh=sh)
     return y, _host(s.state)
 
 
-def _step(p, slots, toks, idx, pos):
+def _step(p, slots, toks, idx, pos, sh=SH):
     """One emulated decode step; toks[r] = the token index of row r (ignored
     for padding rows)."""
     import torch
     import mamba_ssd_selective_amd as ssd
-    bf = torch.bfloat16
+    io = _io(sh)
     pick = lambda a: np.stack([a[r, max(t, 0)] for r, t in enumerate(toks)])
-    y = torch.full((len(toks), H, P), 7.0, dtype=bf, device=torch.device("cuda:0"))
-    ssd.decode_emulated(_dev(pick(p["x"]), bf), _dev(pick(p["dt_raw"])), _dev(p["A"]),
-                        _dev(pick(p["B"]), bf), _dev(pick(p["C"]), bf), slots.state, slots.chunks,
+    y = torch.full((len(toks), sh["H"], sh["P"]), 7.0, dtype=io, device=torch.device("cuda:0"))
+    ssd.decode_emulated(_dev(pick(p["x"]), io), _dev(pick(p["dt_raw"])), _dev(p["A"]),
+                        _dev(pick(p["B"]), io), _dev(pick(p["C"]), io), slots.state, slots.chunks,
                         _dev(np.asarray(idx, dtype=np.int32)), _dev(np.asarray(pos, dtype=np.int32)),
-                        chunk_size=Q, D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]), out=y)
+                        chunk_size=sh["Q"], D=_dev(p["D"]), dt_bias=_dev(p["dt_bias"]), out=y)
     return y
 
 
@@ -144,14 +153,14 @@ def test_emulated_decode_staggered_rows_and_padding():
             assert np.array_equal(yv, y_full[r, t]), (r, t)
 
 
-def _cached(p, rows_sel, L, slots, idx, strict, lens=None):
+def _cached(p, rows_sel, L, slots, idx, strict, lens=None, sh=SH):
     import torch
     import mamba_ssd_selective_amd as ssd
-    bf = torch.bfloat16
+    io = _io(sh)
     sel = lambda k: p[k][rows_sel, :L]
-    y = ssd.chunk_scan_fwd_cached(_dev(sel("x"), bf), _dev(sel("dt_raw")), _dev(p["A"]),
-                                  _dev(sel("B"), bf), _dev(sel("C"), bf), slots.state,
-                                  _dev(np.asarray(idx, dtype=np.int32)), chunk_size=Q,
+    y = ssd.chunk_scan_fwd_cached(_dev(sel("x"), io), _dev(sel("dt_raw")), _dev(p["A"]),
+                                  _dev(sel("B"), io), _dev(sel("C"), io), slots.state,
+                                  _dev(np.asarray(idx, dtype=np.int32)), chunk_size=sh["Q"],
                                   seq_lens=None if lens is None else _dev(lens),
                                   init_from_cache=False, strict=strict, D=_dev(p["D"]),
                                   dt_bias=_dev(p["dt_bias"]))
@@ -221,3 +230,48 @@ def test_strict_states_and_outputs_against_the_oracle():
     ec = oracle.rel_l2(committed, h2)
     print("emulated decode D=0: y %.3e, committed chunk-start state %.3e" % (ed, ec), flush=True)
     assert ed < 2e-2 and ec < 2e-2
+
+
+@pytest.mark.parametrize("n,q,io", [(64, 64, "bf16"), (128, 64, "bf16"), (64, 128, "bf16"),
+                                    (128, 256, "bf16"), (128, 128, "f32")])
+def test_emulated_decode_other_shapes(n, q, io):
+    """The decode forms of the other compiled shapes and of fp32: two rows,
+    one after a Q-token prompt and one from an empty slot that starts seven
+    steps later (a padding row until then), decoded across a chunk boundary
+    each.  Bitwise the strict prefill's outputs and, at the boundary, its
+    states; the values against the oracle."""
+    import torch
+    sh = dict(H=16, P=64, N=n, G=2, Q=q, io=io)
+    rng = np.random.default_rng(41)
+    T = 2 * q + 30
+    p = workloads.random_problem(rng, 2, T, sh["H"], sh["P"], n, sh["G"], io=io, init=False)
+    y_full, _ = _full_prefill(p, T, sh)
+    _, fs2 = _full_prefill(p, 2 * q, sh)
+    lens = np.array([q, 0], dtype=np.int32)
+    start = [0, 7]
+    idx = [1, 0]
+    slots = _Slots(2, sh)
+    _cached({k: (v[:, :q] if k in ("x", "dt_raw", "B", "C") else v) for k, v in p.items()},
+            [0, 1], q, slots, idx, True, lens=lens, sh=sh)
+    got = {0: [], 1: []}
+    for k in range(q + 30):
+        toks = [int(lens[r]) + k - start[r] if k >= start[r] else -1 for r in range(2)]
+        toks = [t if t < T else -1 for t in toks]
+        ii = [idx[r] if toks[r] >= 0 else -1 for r in range(2)]
+        pp = [toks[r] % q if toks[r] >= 0 else 0 for r in range(2)]
+        y = _host(_step(p, slots, toks, ii, pp, sh))
+        for r in range(2):
+            if toks[r] >= 0:
+                got[r].append((toks[r], y[r]))
+            else:
+                assert np.all(y[r] == 7.0)
+        if toks[0] == 2 * q - 1:
+            torch.cuda.synchronize()
+            assert np.array_equal(_host(slots.state)[idx[0]], fs2[0])
+    torch.cuda.synchronize()
+    for r in range(2):
+        bad = [t for t, yv in got[r] if not np.array_equal(yv, y_full[r, t])]
+        assert not bad, (r, bad[:5])
+    yr, _ = oracle.scan(p["x"], p["dt_raw"], p["A"], p["B"], p["C"], dt_bias=p["dt_bias"], D=p["D"])
+    err = oracle.rel_l2(np.stack([yv for _, yv in got[0]]), yr[0, [t for t, _ in got[0]]])
+    assert err < tol(io), err
