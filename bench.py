@@ -72,19 +72,24 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload):
-    """HBM bytes per ssd_chunk_scan_fwd call (all its dispatches) from the
-    committed rocprofv3 counter summary, if it was taken on the current
-    sources; else None."""
-    path = os.path.join(ROOT, "profiles", "scan_%s_counters.md" % workload)
+def profile_bytes(fname, key="hbm_bytes_per_call"):
+    """HBM bytes per call (all its dispatches) that a committed rocprofv3
+    counter summary under profiles/ gives for `key`, if the summary was taken
+    on the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def counter_traffic(workload):
+    """HBM bytes per ssd_chunk_scan_fwd call of a scan workload (see profile_bytes)."""
+    return profile_bytes("scan_%s_counters.md" % workload)
 
 
 def compulsory_bytes(b, L, H, P, N, G, *, es=2, seq_idx=False, init=False, final=True):
@@ -276,7 +281,7 @@ def backward_measure(ssd, lib, hip, torch, base, A, D, bias, w, steps, cpu_secon
            "grad_kernel_us": round(grad_us, 2), "kernels_us": kus,
            "call_kernel_us": round(call_us, 2), "compulsory_bytes": bwd_bytes,
            # the whole backward call: its compulsory bytes over the sum of its dispatches
-           "roofline": roofline_entry(bwd_bytes, call_us),
+           "roofline": roofline_entry(bwd_bytes, call_us, profile_bytes("bwd_prefill_8k_counters.md")),
            "grad_kernel_roofline_frac": round(bwd_bytes / (grad_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "cpu_baseline": None}
     if cpu_seconds > 0:
@@ -451,9 +456,8 @@ def cache_measure(ssd, lib, hip, torch, w, steps, cpu_seconds):
     ach = nbytes / (us * 1e-6) / 1e9
     res["decode"] = {"rows": rows, "slots": slots, "us": round(us, 2),
                      "tokens_per_s": round(rows / (us * 1e-6), 1),
-                     "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                                  "traffic": None}}
+                     "roofline": roofline_entry(nbytes, us, profile_bytes(
+                         "cache_kernels_counters.md", "hbm_bytes_per_call[cache decode]"))}
 
     # ---- prefill: 8 prompts of 512..2048 tokens into a 16-slot cache
     b, L, pslots = 8, 2048, 16
@@ -643,7 +647,8 @@ def scan_workload_measure(ssd, lib, hip, torch, w, reps):
         res["decode"] = {"rows": b, "steps": steps, "value": round(b / dwall, 1),
                          "unit": "decode tokens/s", "ms_per_step": round(1e3 * dwall, 4),
                          "kernel_us": round(dus, 2), "compulsory_bytes": dbytes,
-                         "roofline": roofline_entry(dbytes, dus)}
+                         "roofline": roofline_entry(dbytes, dus, profile_bytes(
+                             "scan_prefill_decode_counters.md", "hbm_bytes_per_decode_step"))}
     del inp, x, dt, B, C, y, ws
     torch.cuda.empty_cache()
     return res
