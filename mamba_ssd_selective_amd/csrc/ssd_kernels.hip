@@ -1178,6 +1178,19 @@ static const ScanVariant kScanVariants[] = {
     SSD_SCAN_VARIANT_TR(64, 128, 128)
     SSD_SCAN_VARIANT_TR_BLOCKED(64, 128, 256, 128)
     SSD_SCAN_VARIANT(1, uint16_t, 64, 128, 256)
+    // further shapes of the generic kernel: state size 256, head dims 32 and
+    // 128, chunk 32, state size 32 (bf16); state size 64, head dim 128 and
+    // state size 256 at chunk 64 (fp32, whose wider tiles fit the LDS only so)
+    SSD_SCAN_VARIANT(1, uint16_t, 64, 256, 64)
+    SSD_SCAN_VARIANT(1, uint16_t, 64, 256, 128)
+    SSD_SCAN_VARIANT(1, uint16_t, 128, 128, 128)
+    SSD_SCAN_VARIANT(1, uint16_t, 32, 128, 128)
+    SSD_SCAN_VARIANT(1, uint16_t, 64, 128, 32)
+    SSD_SCAN_VARIANT(1, uint16_t, 64, 32, 64)
+    SSD_SCAN_VARIANT(0, float, 64, 64, 64)
+    SSD_SCAN_VARIANT(0, float, 64, 64, 128)
+    SSD_SCAN_VARIANT(0, float, 128, 128, 64)
+    SSD_SCAN_VARIANT(0, float, 64, 256, 64)
 };
 
 const ScanVariant* find_scan_variant(int io, int64_t P, int64_t N, int64_t Q, bool strict) {

@@ -278,7 +278,7 @@ struct TrScan {
     }
     __device__ __forceinline__ void dma_all(char* sX, char* sB, TrMeta<Q>* sM, int c) const {
         dma_x(sX, c);
-        if constexpr (kDec != 2) dma_b(sB, c, 0, BI);  // the one-wave form has no state update
+        if constexpr (kDec != 2) dma_b(sB, c, 0, BI);  // the four-wave form has no state update
         dma_meta(sM, c);
     }
 

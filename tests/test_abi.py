@@ -46,6 +46,12 @@ def test_supported_set(lib):
     assert ssd.supported(ssd.BF16, 64, 128, 128)
     assert ssd.supported(ssd.BF16, 64, 128, 256)
     assert ssd.supported(ssd.F32, 16, 16, 64)
+    for io, P, N, Q in ((ssd.BF16, 64, 256, 64), (ssd.BF16, 64, 256, 128), (ssd.BF16, 128, 128, 128),
+                        (ssd.BF16, 32, 128, 128), (ssd.BF16, 64, 128, 32), (ssd.BF16, 64, 32, 64),
+                        (ssd.F32, 64, 64, 64), (ssd.F32, 64, 64, 128), (ssd.F32, 128, 128, 64),
+                        (ssd.F32, 64, 256, 64)):
+        assert ssd.supported(io, P, N, Q), (io, P, N, Q)
+    assert not ssd.supported(ssd.F32, 128, 128, 128)   # its tiles do not fit the LDS
     assert not ssd.supported(ssd.BF16, 48, 128, 128)
     assert not ssd.supported(ssd.BF16, 64, 128, 100)
     assert not ssd.supported(5, 64, 128, 128)

@@ -64,6 +64,11 @@ FP32_CASES = [
     (2, 500, 4, 16, 16, 4, 128, True, True),
     # chunk 256 run as two 128-token blocks by the chunk-128 kernels
     (1, 700, 4, 64, 128, 2, 256, True, True),
+    # state size 64, head dim 128, state size 256
+    (2, 300, 4, 64, 64, 2, 64, True, True),
+    (1, 400, 4, 64, 64, 1, 128, True, False),
+    (1, 300, 4, 128, 128, 2, 64, True, True),
+    (2, 200, 4, 64, 256, 2, 64, False, True),
 ]
 
 
@@ -89,6 +94,14 @@ BF16_CASES = [
     (1, 1000, 64, 64, 64, 8, 64, True, False),
     # chunk 256 at N = 64, run as two 128-token blocks
     (1, 900, 8, 64, 64, 2, 256, True, True),
+    # the generic kernel's other shapes: state size 256, head dims 128 and 32,
+    # chunk 32, state size 32
+    (1, 300, 4, 64, 256, 1, 64, True, True),
+    (2, 333, 4, 64, 256, 2, 128, True, False),
+    (1, 400, 4, 128, 128, 2, 128, True, True),
+    (2, 300, 4, 32, 128, 2, 128, False, True),
+    (2, 200, 4, 64, 128, 2, 32, True, True),
+    (2, 150, 4, 64, 32, 1, 64, True, False),
 ]
 
 

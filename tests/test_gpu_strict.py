@@ -233,7 +233,7 @@ def test_strict_states_and_outputs_against_the_oracle():
 
 
 @pytest.mark.parametrize("n,q,io", [(64, 64, "bf16"), (128, 64, "bf16"), (64, 128, "bf16"),
-                                    (128, 256, "bf16"), (128, 128, "f32")])
+                                    (128, 256, "bf16"), (128, 128, "f32"), (256, 64, "bf16")])
 def test_emulated_decode_other_shapes(n, q, io):
     """The decode forms of the other compiled shapes and of fp32: two rows,
     one after a Q-token prompt and one from an empty slot that starts seven
