@@ -47,7 +47,9 @@ namespace {
 // row, single buffers):
 //  kDec = 1: 5 waves.  Wave 0 computes the row block of the row's last token,
 //            waves 1-4 own two state n-blocks each (the chunk's state update,
-//            when the chunk completes); 70 KB of LDS, two workgroups per CU.
+//            when the chunk completes); 68 KB of LDS.  Launched for the rows
+//            whose chunk completes, each workgroup walking several work
+//            items (scan_tr_kernel).
 //  kDec = 2: 4 output waves, one 16-wide p block each, for rows whose chunk
 //            does not complete: each reads its rows of the chunk-start state
 //            straight into the bf16 operand registers of the carried-state
@@ -1009,8 +1011,8 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
 //                 their decay multipliers, written to the workspace;
 //   kOut = true:  outputs of every segment from its incoming state; final
 //                 states from the last segment.
-// kDec: the decode-output form (one chunk per row, so the second buffers are
-// never used and take no LDS; one column-factor row).
+// kDec: the decode-output forms (one chunk per row, so the second buffers are
+// never used and take no LDS; one column-factor row per output wave).
 template <int P, int N, int Q, bool kOut, bool kSeq, int kDec>
 __global__ __launch_bounds__((TrWaves<kOut, kDec>::kThreads)) void scan_tr_kernel(ScanArgs a) {
     using G_ = TrGeo<P, N, Q>;
