@@ -275,3 +275,57 @@ def test_emulated_decode_other_shapes(n, q, io):
     yr, _ = oracle.scan(p["x"], p["dt_raw"], p["A"], p["B"], p["C"], dt_bias=p["dt_bias"], D=p["D"])
     err = oracle.rel_l2(np.stack([yv for _, yv in got[0]]), yr[0, [t for t, _ in got[0]]])
     assert err < tol(io), err
+
+
+def test_emulated_decode_graph_replay_matches_eager_bitwise():
+    """One emulated decode step captured into a HIP graph and replayed for 130
+    tokens (across a chunk boundary, so the commit pass runs inside the
+    graph), with the next token's inputs and offsets copied into the
+    captured buffers between replays: every replay's y, and the slots at the
+    end, equal those of the same steps launched eagerly on a copy of the
+    slots, bit for bit."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    rng = np.random.default_rng(23)
+    b, T = 3, 2 * Q + 2
+    p = workloads.random_problem(rng, b, T, H, P, N, G, io="bf16", init=False)
+    bf = torch.bfloat16
+    idx = [2, 0, 1]
+    ga, eg = _Slots(3), _Slots(3)
+    for s in (ga, eg):
+        _cached(p, list(range(b)), Q, s, idx, True)
+    dev_idx = _dev(np.asarray(idx, dtype=np.int32))
+    # the captured step's inputs, refilled before every replay
+    xs = _dev(p["x"][:, Q], bf)
+    dts, Bs, Cs = _dev(p["dt_raw"][:, Q]), _dev(p["B"][:, Q], bf), _dev(p["C"][:, Q], bf)
+    pos = _dev(np.zeros(b, dtype=np.int32))
+    y = torch.empty((b, H, P), dtype=bf, device=xs.device)
+    A, D, bias = _dev(p["A"]), _dev(p["D"]), _dev(p["dt_bias"])
+
+    def step(slots, x, dt, Bt, Ct, ps, out):
+        ssd.decode_emulated(x, dt, A, Bt, Ct, slots.state, slots.chunks, dev_idx, ps,
+                            chunk_size=Q, D=D, dt_bias=bias, out=out)
+
+    # warm-up outside the capture, on scratch slots
+    warm = _Slots(3)
+    step(warm, xs, dts, Bs, Cs, pos, y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(ga, xs, dts, Bs, Cs, pos, y)
+    for t in range(Q, T):
+        xs.copy_(_dev(p["x"][:, t], bf))
+        dts.copy_(_dev(p["dt_raw"][:, t]))
+        Bs.copy_(_dev(p["B"][:, t], bf))
+        Cs.copy_(_dev(p["C"][:, t], bf))
+        pos.fill_(t % Q)
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        ye = torch.empty_like(y)
+        step(eg, xs, dts, Bs, Cs, pos, ye)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ye), t
+    assert torch.equal(ga.state, eg.state)
+    for a, e in zip(ga.chunks, eg.chunks):
+        assert torch.equal(a, e)
