@@ -466,7 +466,7 @@ ssd_status scan_fwd_impl(const ssd_dims* d, ssd_dtype io, const void* x, const f
     }
     if (rl.y_last && var->output_combines_segments) {
         // decode output on the transposing-read kernels: the rows whose chunk
-        // does not complete (the four-wave form), then those whose chunk does
+        // does not complete, then those whose chunk does
         for (int pass = 1; pass <= 2; ++pass) {
             sa.dec_pass = pass;
             if (timed_launch(k, hs, [&] { return var->chunk_output(sa, b * plan.nseg * H, hs); }) !=

@@ -44,25 +44,22 @@ namespace {
 // each, so that the state chain and the output products of a chunk proceed on
 // different waves of each SIMD (three waves per SIMD).
 // Decode-output forms (kDec: rows of one chunk, one output row block per
-// row, single buffers):
-//  kDec = 1: 5 waves.  Wave 0 computes the row block of the row's last token,
-//            waves 1-4 own two state n-blocks each (the chunk's state update,
-//            when the chunk completes); 68 KB of LDS.  Launched for the rows
-//            whose chunk completes, each workgroup walking several work
-//            items (scan_tr_kernel).
-//  kDec = 2: 4 output waves, one 16-wide p block each, for rows whose chunk
-//            does not complete: each reads its rows of the chunk-start state
-//            straight into the bf16 operand registers of the carried-state
-//            term (the values the state waves would have written to LDS), and
-//            there is no B tile.  Every output element takes the same products
-//            in the same order as in the other forms.
+// row, single buffers), 4 waves, each computing one 16-wide p block of that
+// row block.  Each wave reads its rows of the chunk-start state straight
+// into the bf16 operand registers of the carried-state term (the values the
+// state waves would have written to LDS); every output element takes the
+// same products in the same order as in the prefill forms.
+//  kDec = 1: for rows whose chunk does not complete (no B tile).
+//  kDec = 2: for rows whose chunk completes: each wave also updates its 16
+//            rows of the chunk's state from the fp32 chunk-start state, in
+//            the products and order of the prefill forms' state waves.
 constexpr int kTrWaves = 8;
 template <bool kOut, int kDec = 0>
 struct TrWaves {
-    static constexpr int W = kDec == 2 ? 4 : (kDec ? 5 : (kOut ? 12 : 8));
+    static constexpr int W = kDec ? 4 : (kOut ? 12 : 8);
     static constexpr int kThreads = W * kWave;
     static constexpr int NBW = kOut ? 2 : 1;  // state n-blocks per state wave
-    static constexpr int first_state = kDec == 2 ? W : (kDec ? 1 : (kOut ? 8 : 0));
+    static constexpr int first_state = kDec ? W : (kOut ? 8 : 0);
 };
 template <int P, int N, int Q>
 struct TrGeo {
@@ -148,9 +145,9 @@ struct TrScan {
     static constexpr int NBI = G_::BBYTES / 1024;   // ... of a B tile
     static constexpr int XI = (NXI + W - 1) / W;    // per wave (the last round may be partial)
     static constexpr int BI = (NBI + W - 1) / W;
-    // p blocks of an output wave: all of them, or (kDec = 2) the wave's own
-    static constexpr int OPB = kDec == 2 ? 1 : G_::PB;
-    static_assert(kDec != 2 || W == G_::PB, "one p block per wave");
+    // p blocks of an output wave: all of them, or (kDec) the wave's own
+    static constexpr int OPB = kDec ? 1 : G_::PB;
+    static_assert(!kDec || W == G_::PB, "one p block per wave");
     static_assert(G_::XBYTES % 1024 == 0 && G_::BBYTES % 1024 == 0, "whole copy instructions");
     // A row block's intra-chunk decays are factored when the decay across its
     // 16 tokens is at most this (the column factors then stay below e^64).
@@ -166,8 +163,11 @@ struct TrScan {
     __device__ __forceinline__ bool ow() const { return kOut && out_wave_; }
     int I;                  // output row block of an output wave
     int nb;                 // first state n-block of a state wave (it owns NBW)
-    int pb0;                // kDec = 2: this wave's p block
-    __device__ __forceinline__ int pbase() const { return kDec == 2 ? pb0 : 0; }
+    int pb0;                // kDec: this wave's p block
+    bool commit_;           // kDec = 2: the row's chunk completes (its state is updated)
+    int64_t row_state_;     // the row's state index (row, or slot)
+    int head_;
+    __device__ __forceinline__ int pbase() const { return kDec ? pb0 : 0; }
     float Dh, Ah;           // D[h], A[h]
     int seq_prev;           // sequence id of the token before the current chunk
     float mult;             // decay of the segment (chunk-state kernel)
@@ -204,8 +204,10 @@ struct TrScan {
     f32x4_t h[NBW][G_::PB];     // state rows n = 16 (nb + t) + 4g + r, column p = 16pb + r16
     uint4 cr[G_::KN];           // C rows of a chunk (k over n), loaded a chunk ahead
     uint4 cb[G_::NCB];          // C.B^T tile pairs of a chunk, loaded a chunk ahead
-    // kDec = 2: the state operand of the carried-state term, fragment (s, pb0)
-    uint4 hreg[kDec == 2 ? G_::KN : 1];
+    // kDec: the state operand of the carried-state term, fragment (s, pb0)
+    uint4 hreg[kDec ? G_::KN : 1];
+    // kDec = 2: the fp32 state rows p = 16 pb0 + r16 of n-block nb, n = 16 nb + 4g + r
+    f32x4_t hs[kDec == 2 ? G_::NNB : 1];
 
     __device__ __forceinline__ TrScan(const ScanArgs& args) : a(args) {}
 
@@ -280,11 +282,58 @@ struct TrScan {
     }
     __device__ __forceinline__ void dma_all(char* sX, char* sB, TrMeta<Q>* sM, int c) const {
         dma_x(sX, c);
-        if constexpr (kDec != 2) dma_b(sB, c, 0, BI);  // the four-wave form has no state update
+        // the decode forms update a state only when the row's chunk completes
+        if constexpr (!kDec) dma_b(sB, c, 0, BI);
+        else if constexpr (kDec == 2) {
+            if (commit_) dma_b(sB, c, 0, BI);
+        }
         dma_meta(sM, c);
     }
 
-    // kDec = 2: the chunk-start state, row p = 16 pb0 + r16, n = 32 s + 8 g .. +7,
+    // kDec = 2: the fp32 chunk-start state rows of this wave (accumulator layout)
+    __device__ __forceinline__ void load_state_f32(const float* __restrict__ src) {
+#pragma unroll
+        for (int nbk = 0; nbk < G_::NNB; ++nbk) {
+            if (src) {
+                const float4 v = *reinterpret_cast<const float4*>(src + (16 * pb0 + r16) * N + 16 * nbk + 4 * g);
+                hs[nbk] = f32x4_t{v.x, v.y, v.z, v.w};
+            } else {
+                hs[nbk] = acc_zero();
+            }
+        }
+    }
+
+    // kDec = 2: the state update of a completed chunk for this wave's rows,
+    // h = exp(cs_last) h + (B w)^T x, stored as [p][n]
+    template <int K>
+    __device__ __forceinline__ void commit_state(float* __restrict__ dst) {
+        const TrMeta<Q>* M = mo[K];
+        const char* X = xo[K];
+        const char* Bt = bo[K];
+        const float e = decay_exp(lds_ld<float>(M, mbase[K] + offsetof(TrMeta<Q>, cs) + 4 * (Q - 1)));
+#pragma unroll
+        for (int nbk = 0; nbk < G_::NNB; ++nbk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hs[nbk][r] *= e;
+#pragma unroll
+        for (int s = 0; s < G_::KQ; ++s) {
+            const Frag<uint16_t> xf = tr_frag<G_::XROW>(X, xa[K] ^ (32 * pb0), s);
+            const float4 w0 = lds_ld<float4>(M, ma[K] + offsetof(TrMeta<Q>, w) + 128 * s);
+            const float4 w1 = lds_ld<float4>(M, ma[K] + offsetof(TrMeta<Q>, w) + 128 * s + 64);
+#pragma unroll
+            for (int nbk = 0; nbk < G_::NNB; ++nbk) {
+                // (n-block nbk's lane base: that of block 0 with its 32-byte unit moved)
+                const Frag<uint16_t> braw = tr_frag<G_::BROW>(Bt, ba[K][0] ^ static_cast<uint32_t>(nbk << 5), s);
+                mma(hs[nbk], scale_frag(braw, w0, w1), xf);
+            }
+        }
+#pragma unroll
+        for (int nbk = 0; nbk < G_::NNB; ++nbk)
+            *reinterpret_cast<float4*>(dst + (16 * pb0 + r16) * N + 16 * nbk + 4 * g) =
+                make_float4(hs[nbk][0], hs[nbk][1], hs[nbk][2], hs[nbk][3]);
+    }
+
+    // kDec: the chunk-start state, row p = 16 pb0 + r16, n = 32 s + 8 g .. +7,
     // as the bf16 pairs the state waves' operand copy holds
     __device__ __forceinline__ void load_state_operand(const float* __restrict__ src) {
 #pragma unroll
@@ -421,7 +470,7 @@ struct TrScan {
     // lanes take part in the swap; only rows inside the sequence are stored.
     static constexpr int kYStores = G_::PB / 2;  // store instructions per row block
     __device__ __forceinline__ void store_y(const f32x4_t (&y)[OPB], float fin, int c, int i, int valid) const {
-        if constexpr (kDec == 2) {
+        if constexpr (kDec) {
             // the row's last token: the lanes of column i = valid - 1 hold
             // p = 16 pb0 + 4 g + r
             if (i == valid - 1)
@@ -578,7 +627,7 @@ struct TrScan {
             Frag<uint16_t> hf[OPB];
 #pragma unroll
             for (int q = 0; q < OPB; ++q) {
-                if constexpr (kDec == 2) hf[q] = frag_of(hreg[s]);
+                if constexpr (kDec) hf[q] = frag_of(hreg[s]);
                 else hf[q] = frag_of(lds_ld<uint4>(H, (ha[K] ^ (s << 6)) + 16 * q * G_::HROW));
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -666,6 +715,9 @@ struct TrScan {
         }
         if (has_next) load_cb(c + 1);  // after the last use
         store_y(y, fin, c, i, valid);
+        if constexpr (kDec == 2) {
+            if (commit_) commit_state<K>(a.final_states + (row_state_ * a.H + head_) * P * N);
+        }
         if constexpr (kSeq) seq_prev = lds_ld<int>(M, mb + offsetof(TrMeta<Q>, seq) + 4 * (Q - 1));
         // this wave's copies of chunk c+1 have landed; the C.B^T tiles and y
         // stores issued after them may still be in flight (the first use of the
@@ -881,18 +933,21 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
     // no chunks when the row ends before this segment
     k.c_end = min(k.c_begin + a.cps, static_cast<int>((rs.len + Q - 1) / Q));
     const bool any = k.c_begin < k.c_end;
-    // decode output in two passes: the four-wave form takes the rows whose
-    // chunk does not complete, the five-wave form those whose chunk does
-    if constexpr (kDec == 2) {
+    // decode output in two passes: kDec = 1 takes the rows whose chunk does
+    // not complete, kDec = 2 those whose chunk does
+    if constexpr (kDec == 1) {
         if (!any || rs.len == a.L) return;
-    } else if constexpr (kDec == 1) {
+    } else if constexpr (kDec == 2) {
         if (rs.len != a.L) return;
     }
     // (decode output: a slot's state moves on at chunk ends only)
     k.want_final = kOut && it.seg == a.nseg - 1 && a.final_states != nullptr && rs.live &&
                    (a.y_last == nullptr || rs.len == a.L);
-    k.out_wave_ = kDec == 2 || (kDec ? k.wave == 0 : kOut && k.wave < G_::NB);
-    k.pb0 = kDec == 2 ? k.wave : 0;
+    k.out_wave_ = kDec || (kOut && k.wave < G_::NB);
+    k.pb0 = kDec ? k.wave : 0;
+    k.commit_ = kDec == 2 && k.want_final;
+    k.row_state_ = rs.state;
+    k.head_ = it.h;
     if constexpr (kDec) {
         // the row block of the row's last token (rows of one chunk)
         k.I = rs.len > 0 ? static_cast<int>((rs.len - 1) >> 4) : 0;
@@ -961,8 +1016,11 @@ __device__ __forceinline__ void scan_tr_run(const ScanArgs& a, const TrLds<P, N,
             k.load_cb(k.c_begin);
             k.dma_all(s.x[0], s.b[0], s.m[0], k.c_begin);
         }
-        if constexpr (kDec == 2)
+        if constexpr (kDec)
             k.load_state_operand(a.init && rs.live ? a.init + (rs.state * a.H + it.h) * P * N : nullptr);
+        if constexpr (kDec == 2) {
+            if (k.commit_) k.load_state_f32(a.init && rs.live ? a.init + (rs.state * a.H + it.h) * P * N : nullptr);
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         for (int c = k.c_begin; c < k.c_end; c += 2) {
@@ -1017,9 +1075,9 @@ template <int P, int N, int Q, bool kOut, bool kSeq, int kDec>
 __global__ __launch_bounds__((TrWaves<kOut, kDec>::kThreads)) void scan_tr_kernel(ScanArgs a) {
     using G_ = TrGeo<P, N, Q>;
     // sizes and alignments of the tiles, or of 16-byte stubs where a form has
-    // no such tile (kDec: no second buffers; kDec = 2: no B tile or state
-    // operand)
-    constexpr bool kB = kDec != 2, kX1 = !kDec, kH0 = kOut && kDec != 2, kH1 = kOut && !kDec;
+    // no such tile (kDec: no second buffers and no state operand; kDec = 1:
+    // no B tile)
+    constexpr bool kB = kDec != 1, kX1 = !kDec, kH0 = kOut && !kDec, kH1 = kOut && !kDec;
     __shared__ __attribute__((aligned(1024))) char sX0[G_::XBYTES];
     __shared__ __attribute__((aligned(kX1 ? 1024 : 16))) char sX1[kX1 ? G_::XBYTES : 16];
     __shared__ __attribute__((aligned(kB ? 1024 : 16))) char sB0[kB ? G_::BBYTES : 16];
@@ -1029,12 +1087,12 @@ __global__ __launch_bounds__((TrWaves<kOut, kDec>::kThreads)) void scan_tr_kerne
     __shared__ __attribute__((aligned(kH0 ? 1024 : 16))) char sH0[kH0 ? G_::HBYTES : 16];
     __shared__ __attribute__((aligned(kH1 ? 1024 : 16))) char sH1[kH1 ? G_::HBYTES : 16];
     // column factors: one row per output wave
-    constexpr int kCj = kDec == 2 ? G_::PB * Q : (kDec ? Q : (kOut ? kTrWaves * Q : 4));
+    constexpr int kCj = kDec ? G_::PB * Q : (kOut ? kTrWaves * Q : 4);
     __shared__ __attribute__((aligned(16))) float sCj[kCj];
     const TrLds<P, N, Q, kOut> lds{{sX0, sX1}, {sB0, sB1},
                                    {&sM0, reinterpret_cast<TrMeta<Q>*>(sM1)}, {sH0, sH1}, sCj};
 
-    if constexpr (kDec == 1) {
+    if constexpr (kDec == 2) {
         // rows whose chunk completes, among this workgroup's work items
         // blockIdx.x + k gridDim.x: every wave checks 64 of them at a time
         // (one per lane) and the workgroup runs the ones that qualify
@@ -1076,27 +1134,28 @@ template <int P, int N, int Q, bool kOut>
 hipError_t launch_scan_tr(const ScanArgs& a, int64_t nblocks, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(nblocks));
     if constexpr (kOut) {
-        // decode output (rows of one chunk, no seq_idx): pass 1, rows whose
-        // chunk does not complete, on the four-wave form; pass 2, the others,
-        // on the five-wave form, with as many workgroups as the device holds
-        // at once (an empty pass then costs one round of them)
+        // decode output (rows of one chunk, no seq_idx): pass 1, the rows
+        // whose chunk does not complete (kDec = 1, one workgroup each); pass
+        // 2, the others (kDec = 2) on as many workgroups as the device holds
+        // at once, each walking its share of the work items (so that a pass
+        // with no such row costs one round of workgroups)
         if (a.y_last && !a.seq_idx) {
             if (a.dec_pass == 1)
-                return dispatch(scan_tr_kernel<P, N, Q, true, false, 2>, grid,
-                                dim3(TrWaves<true, 2>::kThreads), st, a);
+                return dispatch(scan_tr_kernel<P, N, Q, true, false, 1>, grid,
+                                dim3(TrWaves<true, 1>::kThreads), st, a);
             if (a.dec_pass != 2) return hipErrorInvalidValue;
-            constexpr int kThreads = TrWaves<true, 1>::kThreads;
+            constexpr int kThreads = TrWaves<true, 2>::kThreads;
             static const int per_cu = [] {
                 int n = 0;
                 if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &n, scan_tr_kernel<P, N, Q, true, false, 1>, kThreads, 0) != hipSuccess)
+                        &n, scan_tr_kernel<P, N, Q, true, false, 2>, kThreads, 0) != hipSuccess)
                     n = 1;
                 return n < 1 ? 1 : n;
             }();
             ScanArgs c = a;
             c.dec_items = nblocks;
             const int64_t cap = static_cast<int64_t>(per_cu) * device_cus();
-            return dispatch(scan_tr_kernel<P, N, Q, true, false, 1>,
+            return dispatch(scan_tr_kernel<P, N, Q, true, false, 2>,
                             dim3(static_cast<unsigned>(nblocks < cap ? nblocks : cap)),
                             dim3(kThreads), st, c);
         }
