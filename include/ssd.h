@@ -22,6 +22,10 @@
  *    The caller owns all of them; the library allocates nothing and keeps no
  *    global buffers, so calls are re-entrant.  (One exception, on purpose:
  *    ssd_chunk_scan_fwd_noalloc takes its scratch from a static device array.)
+ *    The other state the library keeps: the diagnostic timing hooks
+ *    (ssd_set_timing_events), per host thread and off unless a caller sets
+ *    them, and per-device launch sizes it queries once (compute units,
+ *    workgroups per CU); no call's results depend on an earlier call.
  *  - Arguments are validated on the host before anything is launched.  Any
  *    failure returns a non-zero ssd_status and leaves every output untouched
  *    (fail closed, RFC section 4.1 and section 7 "Fail closed"); there is no
