@@ -329,3 +329,46 @@ def test_emulated_decode_graph_replay_matches_eager_bitwise():
     assert torch.equal(ga.state, eg.state)
     for a, e in zip(ga.chunks, eg.chunks):
         assert torch.equal(a, e)
+
+
+def test_emulated_decode_many_rows_bitwise():
+    """520 rows x 64 heads (33,280 work items), decoded from empty slots for
+    130 tokens in lockstep, so that every row completes its chunk in the same
+    step: the pass for completing rows then walks up to 65 items per
+    workgroup (two rounds of 64 candidates).  Every step's outputs equal the
+    strict prefill's bit for bit, and after the chunk end every slot holds
+    the strict prefill's state after Q tokens."""
+    import torch
+    import mamba_ssd_selective_amd as ssd
+    dev, bf = torch.device("cuda:0"), torch.bfloat16
+    b, T = 520, Q + 2
+    gen = torch.Generator(device=dev).manual_seed(77)
+    x = torch.randn((b, T, H, P), generator=gen, device=dev).to(bf)
+    dt = torch.randn((b, T, H), generator=gen, device=dev)
+    Bm = (torch.randn((b, T, G, N), generator=gen, device=dev) / N ** 0.5).to(bf)
+    Cm = (torch.randn((b, T, G, N), generator=gen, device=dev) / N ** 0.5).to(bf)
+    A = -torch.exp(torch.rand(H, generator=gen, device=dev) * 2.7)
+    D = torch.randn(H, generator=gen, device=dev)
+    bias = -2.0 - 2.0 * torch.rand(H, generator=gen, device=dev)
+    idx = torch.randperm(b, generator=gen, device=dev).to(torch.int32)
+
+    def prefill(L):
+        st = torch.zeros((b, H, P, N), device=dev)
+        y = ssd.chunk_scan_fwd_cached(x[:, :L].contiguous(), dt[:, :L].contiguous(), A,
+                                      Bm[:, :L].contiguous(), Cm[:, :L].contiguous(), st,
+                                      torch.arange(b, dtype=torch.int32, device=dev), chunk_size=Q,
+                                      init_from_cache=False, strict=True, D=D, dt_bias=bias)
+        return y, st
+
+    y_full, _ = prefill(T)
+    _, st_q = prefill(Q)
+    slots = _Slots(b)
+    for t in range(T):
+        pos = torch.full((b,), t % Q, dtype=torch.int32, device=dev)
+        y = ssd.decode_emulated(x[:, t].contiguous(), dt[:, t].contiguous(), A, Bm[:, t].contiguous(),
+                                Cm[:, t].contiguous(), slots.state, slots.chunks, idx, pos,
+                                chunk_size=Q, D=D, dt_bias=bias)
+        assert torch.equal(y, y_full[:, t]), t
+        if t == Q - 1:
+            assert torch.equal(slots.state[idx.long()], st_q)
+    torch.cuda.synchronize()
