@@ -6,8 +6,6 @@ Tolerance (relative L2 over all elements): 1e-4 for fp32 inputs, 2e-2 for bf16
 inputs with fp32 state.  Because D*x dominates y for these input distributions,
 every case is also checked with D = 0, where y is the state-space part alone.
 """
-import math
-
 import numpy as np
 import pytest
 
