@@ -170,6 +170,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     constexpr int CPR = C_::NP / kV;       // 16-byte pieces per padded row
     constexpr int PIECES = Q * CPR;
     constexpr int PPT = (PIECES + kThreads - 1) / kThreads;
+    // decode output: the output kernels read the tiles and C rows of the row
+    // block of the row's last token only, which need the B rows up to that
+    // block's end and the C rows of that block
+    const int I_only = a.y_last ? static_cast<int>((rs.len - 1 - t0) >> 4) : -1;
+    auto needed = [&](int j, bool isB) {
+        return I_only < 0 || (j < 16 * I_only + 16 && (isB || j >= 16 * I_only));
+    };
     uint4 rb[PPT], rc[PPT];
 #pragma unroll
     for (int k = 0; k < (kTiles ? PPT : 0); ++k) {
@@ -180,13 +187,16 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
         n0 = n0 < N ? n0 : N - kV;
         int64_t t = t0 + j;
         t = t < tl ? t : tl;
+        rb[k] = rc[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (!needed(j, true)) continue;  // (the C rows needed lie inside the B rows needed)
+        const bool wantC = needed(j, false);
         if (emul && t == tl) {
             const int64_t o = (b * a.G + g) * N + n0;
             rb[k] = ld_words16(static_cast<const T*>(a.tok_B) + o);
-            rc[k] = ld_words16(static_cast<const T*>(a.tok_C) + o);
+            if (wantC) rc[k] = ld_words16(static_cast<const T*>(a.tok_C) + o);
         } else {
             rb[k] = ld_raw16(Bp + ((r0 + t) * a.G + g) * N + n0);
-            rc[k] = ld_raw16(Cp + ((r0 + t) * a.G + g) * N + n0);
+            if (wantC) rc[k] = ld_raw16(Cp + ((r0 + t) * a.G + g) * N + n0);
         }
     }
     if (emul && tl < t0 + Q) {
@@ -275,10 +285,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
     }
 
     if constexpr (kTiles) {
-        // decode output: the output kernels read the tiles and C rows of the
-        // row block of the row's last token only
-        const int I_only = a.y_last ? static_cast<int>((rs.len - 1 - t0) >> 4) : -1;
-        // ---- stage B and C rows (tokens past L and columns past N are zero)
+        // ---- stage B and C rows (tokens past L and columns past N are zero;
+        // decode output: the needed rows only, the others are never read)
         const int64_t valid = rs.len - t0;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
@@ -286,8 +294,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ScanArgs a) {
             if (li < PIECES) {
                 const int j = li / CPR, n0 = (li % CPR) * kV;
                 const bool keep = j < valid && n0 < N;
-                *reinterpret_cast<uint4*>(sB + j * C_::SB + n0) = raw_keep(keep, rb[k]);
-                *reinterpret_cast<uint4*>(sC + j * C_::SB + n0) = raw_keep(keep, rc[k]);
+                if (needed(j, true)) *reinterpret_cast<uint4*>(sB + j * C_::SB + n0) = raw_keep(keep, rb[k]);
+                if (needed(j, false)) *reinterpret_cast<uint4*>(sC + j * C_::SB + n0) = raw_keep(keep, rc[k]);
             }
         }
         __syncthreads();
