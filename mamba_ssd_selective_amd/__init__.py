@@ -57,6 +57,11 @@ def library():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("libssd.so not found at %s: build it with "
                                "mamba_ssd_selective_amd._build.build()" % _LIB_PATH)
+        # torch's HIP runtime first: the library then binds that same copy
+        # (both carry the soname libamdhip64.so.7).  Loaded before torch, it
+        # would bind the system copy and torch would add its own, two HIP
+        # runtimes in one process, where the library's launches have failed.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(_LIB_PATH)
         vp, f, i64, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int64, ctypes.c_int
         dims_p = ctypes.POINTER(_Dims)

@@ -35,6 +35,20 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(raw, n), "libssd.so does not export %s" % n
 
 
+def test_one_hip_runtime_when_the_library_loads_first():
+    # the binding loads torch's HIP runtime ahead of the library, so that the
+    # library binds that copy (same soname) and not the system one beside it
+    import subprocess
+    import sys
+    code = ("import mamba_ssd_selective_amd as s; s.library(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    env = dict(os.environ, PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                         cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"
+
+
 def test_version_and_status_strings(lib):
     assert lib.ssd_abi_version() == 1
     for s in range(11):
