@@ -390,22 +390,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdArgs a) {
 // --------------------------------------------------------- per-chunk gradients
 
 // Sum over the 16 lanes of a 16-lane row (same g).
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
+__device__ __forceinline__ float sum16(float v) { return row16_sum(v); }
 // Sum over the 4 lane groups g with the same r16.
-__device__ __forceinline__ float sum_g(float v) {
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    return v;
-}
-__device__ __forceinline__ float sum64(float v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
+__device__ __forceinline__ float sum_g(float v) { return add_lane_xor32(add_lane_xor16(v)); }
+__device__ __forceinline__ float sum64(float v) { return wave_sum(v); }
 // Workgroup sum (fixed order); every thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float* red) {
     v = sum64(v);

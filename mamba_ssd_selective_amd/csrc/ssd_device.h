@@ -305,6 +305,56 @@ __device__ __forceinline__ f32x4_t acc_zero() { return f32x4_t{0.0f, 0.0f, 0.0f,
 
 // ----------------------------------------------------------- wave primitives
 
+// Cross-lane sums on VALU moves: DPP within a 16-lane row, the permlane swaps
+// across rows, in place of LDS permutes (ds_bpermute, one trip through the LDS
+// unit per step).  Each step adds to every lane the value of a partner; where
+// that partner is not the xor butterfly's, the two hold the same value at that
+// step, so the sums are the butterfly's, bit for bit.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+// v + v of lane ^ 16 (rows 0/1 and 2/3 trade places), then the same with ^ 32
+__device__ __forceinline__ float add_lane_xor16(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float add_lane_xor32(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// Sum over each 16-lane row, the butterfly over offsets 1, 2, 4, 8.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_f32<0x141>(v);  // row_half_mirror: a lane of the other quad of the half row
+    v += dpp_f32<0x140>(v);  // row_mirror: a lane of the other half of the row
+    return v;
+}
+// Sum over the wave, the butterfly over offsets 1, 2, ..., 32.
+__device__ __forceinline__ float wave_sum(float v) {
+    return add_lane_xor32(add_lane_xor16(row16_sum(v)));
+}
+// Sum over aligned groups of kG lanes (a power of two, 2..64), the butterfly
+// from the widest offset down: kG / 2, ..., 2, 1.
+template <int kG>
+__device__ __forceinline__ float group_sum_wide_first(float v) {
+    static_assert(kG >= 2 && kG <= 64 && (kG & (kG - 1)) == 0, "group size");
+    if constexpr (kG >= 64) v = add_lane_xor32(v);
+    if constexpr (kG >= 32) v = add_lane_xor16(v);
+    if constexpr (kG >= 16) {
+        v += dpp_f32<0x128>(v);  // row_ror:8: lane ^ 8
+        v += dpp_f32<0x124>(v);  // row_ror:4: a lane equal to lane ^ 4 after the step above
+    } else if constexpr (kG == 8) {
+        v += __shfl_xor(v, 4, kWave);  // the first step: no DPP move gives lane ^ 4
+    }
+    if constexpr (kG >= 4) v += dpp_f32<0x4E>(v);  // lane ^ 2
+    v += dpp_f32<0xB1>(v);                          // lane ^ 1
+    return v;
+}
+
 // Inclusive segmented scan over the 64 lanes: a set `head` flag starts a new
 // segment at that lane.  Fixed tree order (deterministic).
 __device__ __forceinline__ float wave_segmented_scan(float v, int head) {

@@ -1088,8 +1088,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
                 }
                 part = s.x * cv[0] + s.y * cv[1] + s.z * cv[2] + s.w * cv[3];
             }
-#pragma unroll
-            for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+            part = group_sum_wide_first<TPR>(part);
             if (p < p_end && cc == 0) y[bh * a.P + p] = Io<T>::from_f32(part + Dh * xv[u]);
         }
     }

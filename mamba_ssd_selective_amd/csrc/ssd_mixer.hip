@@ -284,8 +284,7 @@ __global__ __launch_bounds__(kMixThreads) void gated_rmsnorm_kernel(NormArgs a) 
             }
         }
     }
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) ss += __shfl_xor(ss, d, kWave);
+    ss = wave_sum(ss);
     const float rstd = rsqrtf(ss / static_cast<float>(a.group) + a.eps);
 #pragma unroll
     for (int q = 0; q < kMaxPass; ++q) {
