@@ -22,8 +22,8 @@ namespace ssd {
 namespace {
 
 constexpr int kConvW = 4;        // taps (the pages' mamba_d_conv)
-constexpr int kConvTile = 16;    // tokens per thread of the prefill kernel
-constexpr int kConvStep = 4;     // tokens whose loads are in flight together
+constexpr int kConvTile = 32;    // tokens per thread of the prefill kernel
+constexpr int kConvStep = 8;     // tokens whose loads are in flight together
 constexpr int kMixThreads = 256;
 
 template <typename T> struct V8;
