@@ -256,6 +256,53 @@ __global__ __launch_bounds__(kMixThreads) void conv1d_update_kernel(ConvArgs a) 
     ov.store(conv_dst<T>(a, b, c0));
 }
 
+// Groups of 512 channels: one wave per kNormUnits consecutive (row, group)
+// units, all their loads issued before any arithmetic; each unit as below.
+constexpr int kNormUnits = 2;
+template <typename T>
+__global__ __launch_bounds__(kMixThreads) void gated_rmsnorm512_kernel(NormArgs a) {
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const int64_t groups = a.dim / 512;
+    const int64_t total = a.rows * groups;
+    const int64_t unit0 = (static_cast<int64_t>(blockIdx.x) * (kMixThreads / kWave) +
+                           static_cast<int64_t>(threadIdx.x) / kWave) * kNormUnits;
+    if (unit0 >= total) return;
+    V8<T> y[kNormUnits], z[kNormUnits];
+#pragma unroll
+    for (int u = 0; u < kNormUnits; ++u) {
+        const int64_t unit = unit0 + u < total ? unit0 + u : total - 1;
+        const int64_t base = (unit / groups) * a.dim + (unit % groups) * 512 + 8 * lane;
+        y[u].load(static_cast<const T*>(a.y) + base);
+        z[u].load(static_cast<const T*>(a.z) + base);
+    }
+#pragma unroll
+    for (int u = 0; u < kNormUnits; ++u) {
+        const int64_t unit = unit0 + u;
+        if (unit >= total) break;
+        const int gq = static_cast<int>(unit % groups);
+        const int64_t base = (unit / groups) * a.dim + static_cast<int64_t>(gq) * 512 + 8 * lane;
+        float v[8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[e] = y[u].get(e) * silu_f32(z[u].get(e));
+            ss += v[e] * v[e];
+        }
+        ss = wave_sum(ss);
+        const float rstd = rsqrtf(ss / 512.0f + a.eps);
+        const int64_t ch = static_cast<int64_t>(gq) * 512 + 8 * lane;
+        const float4 w0 = *reinterpret_cast<const float4*>(a.weight + ch);
+        const float4 w1 = *reinterpret_cast<const float4*>(a.weight + ch + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[e] * rstd * wv[e];
+        V8<T> ov;
+        ov.set(o);
+        ov.store(static_cast<T*>(a.out) + base);
+    }
+}
+
 // One wave per (row, group of channels); a lane holds 8 channels per 512.
 template <typename T>
 __global__ __launch_bounds__(kMixThreads) void gated_rmsnorm_kernel(NormArgs a) {
@@ -327,6 +374,12 @@ hipError_t launch_conv1d_update(int io, const ConvArgs& a, hipStream_t st) {
 hipError_t launch_gated_rmsnorm(int io, const NormArgs& a, hipStream_t st) {
     const int64_t units = a.rows * (a.dim / a.group);
     const int per_block = kMixThreads / kWave;
+    if (a.group == 512) {
+        const int64_t per = static_cast<int64_t>(per_block) * kNormUnits;
+        const dim3 g512(static_cast<unsigned>((units + per - 1) / per));
+        if (io == 1) return dispatch(gated_rmsnorm512_kernel<uint16_t>, g512, dim3(kMixThreads), st, a);
+        return dispatch(gated_rmsnorm512_kernel<float>, g512, dim3(kMixThreads), st, a);
+    }
     const dim3 grid(static_cast<unsigned>((units + per_block - 1) / per_block));
     if (io == 1) return dispatch(gated_rmsnorm_kernel<uint16_t>, grid, dim3(kMixThreads), st, a);
     return dispatch(gated_rmsnorm_kernel<float>, grid, dim3(kMixThreads), st, a);

@@ -124,7 +124,9 @@ def test_conv1d_full_30b_shape():
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("rows,dim,group", [(8192, 4096, 512), (33, 1000, 200), (5, 4096, 4096),
-                                            (7, 512, 64), (1, 8, 8)])
+                                            (7, 512, 64), (1, 8, 8),
+                                            # groups of 512 (two per wave): ragged and single units
+                                            (7, 1536, 512), (1, 512, 512)])
 def test_gated_rmsnorm_parity(io, rows, dim, group):
     import torch
     import mamba_ssd_selective_amd as ssd
